@@ -1,0 +1,63 @@
+"""The closed-form byte/FLOP calculator against the numbers the pages print."""
+
+import json
+import os
+
+import pytest
+
+import synth
+from int4_weight_streaming_decode_amd import roofline
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_closed_forms.json")
+
+
+@pytest.fixture(scope="module")
+def pages():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_roofline_reply_27b_intensity(pages):
+    g = pages["roofline_reply_section_2"]
+    flops = 2 * g["params"]
+    byts = g["params"] * g["bytes_per_param"]
+    assert flops == g["flops_per_token"] and byts == g["bytes_per_token"]
+    assert flops / byts == g["intensity"]
+    assert 100.0 / g["ridge"] == pytest.approx(g["utilisation_pct"], abs=0.01)
+
+
+def test_primer_7b_decode_bound(pages):
+    g = pages["primer_section_1_2"]
+    t = roofline.decode_latency_bound_s(g["weight_bytes"], g["bandwidth"])
+    assert t * 1e3 == pytest.approx(g["ms_per_token"], abs=0.05)
+    assert 1.0 / t == pytest.approx(g["tokens_per_s"], rel=0.03)   # the page rounds 214 to "about 210"
+
+
+def test_primer_memory_bill(pages):
+    g = pages["primer_section_1_4"]
+    m = roofline.estimate_mem(**g["args"])
+    p = g["printed_GB"]
+    assert m["weights"] / 1e9 == pytest.approx(p["weights"])
+    assert m["adam"] / 1e9 == pytest.approx(p["adam"])
+    assert m["act"] / 1e9 == pytest.approx(p["act"], abs=0.5)
+    # the page prints 0.6 GB for KV; its own formula gives 2.68 GB (recorded contradiction)
+    assert m["kv"] / 1e9 == pytest.approx(g["formula_kv_GB"], abs=0.01)
+    assert m["kv"] / 1e9 != pytest.approx(p["kv"], abs=0.1)
+
+
+def test_primer_70b_flop_sum(pages):
+    g = pages["primer_section_1_1"]
+    s = g["L"] * (4 * g["D"] ** 2 + 2 * g["D"] * g["d_ff"])
+    assert s == pytest.approx(g["formula_value"], rel=1e-3)
+
+
+def test_int4_bytes_per_weight_and_27b_step():
+    # g = 128 with bf16 scales: 0.5 + 2/128 = 0.515625 bytes per weight
+    assert roofline.matrix_bytes(128, 1024, 128) / (128 * 1024) == 0.515625
+    s = synth.SHAPES["27b"]
+    b = roofline.step_bytes(s, 1, s.kv_len + 1)
+    # 64 layers x (186.5 MB weights + 33.6 MB KV read + 4 KB write)
+    assert b / 1e9 == pytest.approx(14.087, abs=0.002)
+    assert roofline.step_bytes(s, 1, s.kv_len + 1, "bf16") / 1e9 == pytest.approx(48.454, abs=0.002)
+    lm = synth.SHAPES["27b_lm"]
+    assert roofline.step_bytes(lm, 1, lm.kv_len + 1, lm_head=True) / 1e9 == pytest.approx(14.489, abs=0.002)

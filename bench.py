@@ -1,0 +1,212 @@
+"""Decode benchmark: one step = the whole int4 weight-streaming decode path.
+
+Default workload (the headline metric): the 27B-shaped int4 decoder stack
+(64 layers, D 5120, 64 query / 8 KV heads, head_dim 128, d_ff 17408, groups of
+128) plus the 152064 x 5120 int4 LM head swept in chunks of 8192 rows, batch 1,
+8192 cached tokens at the first timed step (the position advances by one per
+step).  Inputs are synthetic (seeded, generated on the GPU, resident in HBM
+before timing).  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--batch B] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from int4_weight_streaming_decode_amd import roofline  # noqa: E402
+
+METRIC = "decode tokens/s at batch 1 and achieved HBM GB/s (% of peak), 27B-shaped int4"
+
+WORKLOADS = {
+    # name: (shape, weight dtype, LM head)
+    "27b_lm": ("27b_lm", "int4", True),
+    "27b": ("27b", "int4", False),
+    "27b_bf16": ("27b", "bf16", False),
+    "7b": ("7b", "int4", False),
+    "70b": ("70b", "int4", False),
+}
+
+
+def describe(shape, dtype, lm, batch):
+    s = (f"{shape.name}-shaped {dtype} decoder stack: {shape.n_layers} layers, D={shape.d_model}, "
+         f"{shape.n_q_heads}/{shape.n_kv_heads} heads, head_dim {shape.head_dim}, d_ff {shape.d_ff}, "
+         f"group {shape.group}; KV {shape.kv_len} cached tokens; batch {batch}")
+    if lm:
+        s += f"; int4 LM head {shape.vocab} x {shape.d_model}, chunks of {shape.lm_chunk} rows, greedy argmax"
+    return s
+
+
+def cpu_baseline(shape, dtype, lm):
+    """The CPU oracle as it stands, on a bounded sample of the same workload,
+    scaled to one full step."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cap = ((shape.kv_len + 1 + 7) // 8) * 8
+    layer = synth.make_layer(shape, 17, 0, dtype)
+    kc, vc = synth.make_kv(shape, 17, 0, 1, [shape.kv_len], cap)
+    x = synth.make_x(shape, 17, 1).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.decode_layer(shape, layer, x, kc, vc, [shape.kv_len])
+    t_layer = time.perf_counter() - t0
+    step = shape.n_layers * t_layer
+    sample = f"1 of {shape.n_layers} layers at KV {shape.kv_len} ({t_layer:.2f} s)"
+    if lm:
+        w = synth.make_lm_head(shape.lm_chunk, shape.d_model, shape.group, 18)
+        h = synth.make_hidden(shape.d_model, 19, 1).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.lm_head_chunked_argmax(w, h, shape.lm_chunk)
+        t_chunk = time.perf_counter() - t0
+        step += t_chunk * shape.vocab / shape.lm_chunk
+        sample += f" + 1 LM-head chunk of {shape.lm_chunk} rows ({t_chunk:.2f} s), scaled to the full step"
+    return {"value": 1.0 / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "sample": sample,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="27b_lm", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--exec-mode", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design note, "
+              "not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from int4_weight_streaming_decode_amd import binding as B
+    from synth import gpu as G
+
+    shape_name, wdtype, lm = WORKLOADS[args.workload]
+    shape = synth.SHAPES[shape_name]
+    batch = args.batch
+    torch.cuda.set_device(0)
+    torch.manual_seed(0)
+
+    n_total = args.warmup + args.steps
+    cap = ((shape.kv_len + n_total + 1 + 7) // 8) * 8
+    t_gen = time.perf_counter()
+    keep = []
+    layers, kvs = [], []
+    for l in range(shape.n_layers):
+        p = G.make_layer_gpu(shape, 1, l, wdtype)
+        mats = {}
+        for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            m = p[n]
+            if wdtype == "int4":
+                mats[n] = B.make_mat(m["codes"], m["scales"], m["n"], m["k"], m["group"], B.WEIGHT_INT4)
+            else:
+                mats[n] = B.make_mat(m["bf16"], None, m["n"], m["k"], 0, B.WEIGHT_BF16)
+        layers.append(B.make_layer(p["attn_norm"], p["ffn_norm"], mats))
+        k, v = G.make_kv_gpu(shape, 1, l, batch, cap)
+        kvs.append(B.make_kv(k, v, cap))
+        keep.append((p, k, v))
+    lm_mat = None
+    if lm:
+        W = G.make_lm_head_gpu(shape.vocab, shape.d_model, shape.group, 2)
+        keep.append(W)
+        lm_mat = B.make_mat(W["codes"], W["scales"], W["n"], W["k"], W["group"], B.WEIGHT_INT4)
+    layers = (B.I4dLayer * len(layers))(*layers)      # host arrays built once
+    kvs = (B.I4dKv * len(kvs))(*kvs)
+    x = G.make_x_gpu(shape, 3, batch)
+    out = torch.empty_like(x)
+    tok = torch.empty(batch, dtype=torch.int32, device="cuda")
+    mx = torch.empty(batch, dtype=torch.float32, device="cuda")
+    pos = torch.full((batch,), shape.kv_len, dtype=torch.int32, device="cuda")
+    cfg = B.make_config(shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
+                        shape.rms_eps, shape.rope_base, args.exec_mode)
+    ws = torch.zeros(B.workspace_size(cfg, batch, cap - 1, shape.vocab), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(i, events=None):
+        max_pos = shape.kv_len + i
+        if events:
+            events[0].record()
+        B.decode_stack(cfg, layers, batch, x, out, kvs, pos, max_pos, ws)
+        if events:
+            events[1].record()
+        if lm:
+            B.lm_head_chunked(lm_mat, batch, out, shape.lm_chunk, tok, mx, ws)
+        if events:
+            events[2].record()
+        pos.add_(1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    lm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if lm else 0.0
+    status = B.read_device_status(ws)
+
+    ms_per_step = total_ms / args.steps
+    keys_avg = shape.kv_len + args.warmup + (args.steps - 1) / 2.0 + 1
+    stack_bytes = roofline.step_bytes(shape, batch, keys_avg, wdtype)
+    lm_bytes = roofline.lm_head_bytes(shape.vocab, shape.d_model, shape.group) if lm else 0
+    step_bytes = stack_bytes + lm_bytes
+    hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    stack_gbps = stack_bytes / (stack_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": batch * 1000.0 / ms_per_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights, f16 x f16 -> f32 dot; bf16 MFMA attention" if wdtype == "int4" else "bf16 weights, f32 FMA",
+        "data": "synthetic",
+        "config": {"workload": describe(shape, wdtype, lm, batch), "batch": batch, "kv_len": shape.kv_len,
+                   "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode},
+        "hbm_gbps": hbm_gbps,
+        "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": "i4d_decode_stack (all layers of one step)",
+                     "achieved": stack_gbps, "peak": 8000.0, "unit": "GB/s", "frac": stack_gbps / 8000.0,
+                     "traffic": None, "avg_launch_ms": stack_ms, "bytes_per_launch": stack_bytes},
+        "lm_head_ms": lm_ms,
+        "device_status": status,
+        "input_generation_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, wdtype, lm)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

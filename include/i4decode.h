@@ -1,0 +1,191 @@
+/*
+ * i4decode -- int4 weight-streaming decode for MI355X (gfx950).
+ *
+ * One decode step of a dense grouped-query-attention decoder stack whose
+ * weights are int4 codes plus bf16 group scales (the batch-1 path the pages
+ * build their roofline argument on).  Per layer the library computes
+ *
+ *   h   = RMSNorm(x) * g1                          (Primer 1.1)
+ *   q,k,v = Wq h, Wk h, Wv h                       (Primer 1.1; int4 expanded
+ *                                                   in registers: Unsloth
+ *                                                   article 二.3)
+ *   q,k = RoPE(q, k; pos)                          (Roofline reply 五)
+ *   cache[pos] = bf16(k), bf16(v)                  (Primer 1.2: append)
+ *   o   = softmax(q K^T / sqrt(hd)) V over 0..pos  (Primer 1.1, 1.2; query head
+ *                                                   h reads KV head h / (Hq/Hkv):
+ *                                                   Unsloth article 二.2)
+ *   y   = x + Wo o
+ *   act = SiLU(Wg RMSNorm(y) g2) * (Wu RMSNorm(y) g2)   (Unsloth article 二.1)
+ *   z   = y + Wd act
+ *
+ * and, for the LM head, the greedy token argmax_v (W_lm h)_v computed over the
+ * vocabulary in chunks without materialising the logits (Unsloth article 三;
+ * Primer 1.2).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless the comment says "host".  Every
+ *    buffer is allocated, owned and freed by the caller; the library never
+ *    allocates, frees, synchronises or keeps state between calls.
+ *  - bf16 values are carried as uint16_t bit patterns.  Activations are fp32.
+ *  - `stream` is a hipStream_t passed as void*; all device work is enqueued on
+ *    it, in order.
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    negative return code means nothing was enqueued.  Faults inside kernels
+ *    (a position outside the cache, a grid barrier that timed out) cannot be
+ *    returned synchronously: they set a status word in the workspace that
+ *    i4d_read_device_status() reports, and the kernels skip the offending work
+ *    instead of touching memory out of bounds.
+ *  - The workspace is caller-allocated device memory of at least
+ *    i4d_workspace_size() bytes (never less than I4D_WS_MIN_BYTES), 256-byte
+ *    aligned, initialised once with i4d_workspace_init() before first use (it
+ *    clears the status word).  It is scratch between calls: no call reads what
+ *    an earlier call left there.  Calls that share a workspace must be ordered
+ *    on one stream.
+ */
+#ifndef I4DECODE_H
+#define I4DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define I4D_OK            0
+#define I4D_EINVAL       -1   /* null pointer, bad shape or group, Hq % Hkv != 0, ... */
+#define I4D_EALIGN       -2   /* a pointer or pitch misses its required alignment */
+#define I4D_EWORKSPACE   -3   /* workspace missing or smaller than i4d_workspace_size() */
+#define I4D_ERANGE       -4   /* max_pos >= capacity, chunk_rows <= 0, batch out of range */
+#define I4D_EHIP         -5   /* a HIP launch failed (hipGetLastError) */
+#define I4D_EUNSUPPORTED -6   /* valid request this build does not implement */
+
+/* smallest workspace any entry point accepts (header + LM-head argmax keys) */
+#define I4D_WS_MIN_BYTES (512 + 4096 * 8 * 8)
+
+/* device status word bits (i4d_read_device_status) */
+#define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
+#define I4D_DEV_BARRIER_TIMEOUT 2 /* a grid barrier of the persistent kernel gave up waiting */
+
+/* ---- weight matrices ---- */
+#define I4D_WEIGHT_INT4 0
+#define I4D_WEIGHT_BF16 1
+
+/* A weight matrix W of n output rows and k inputs, applied as y = W x.
+ *  I4D_WEIGHT_INT4: data   = uint8  codes  [n][k/2], row-major, two 4-bit
+ *                            codes per byte, input index 2i in the low nibble;
+ *                   scales = bf16   [n][ceil(k/group)], row-major; input i of
+ *                            row r stands for (code - 8) * scales[r][i/group].
+ *                   k % 8 == 0, group % 8 == 0, data 16-byte aligned.
+ *  I4D_WEIGHT_BF16: data   = bf16 [n][k] row-major, scales = NULL, group
+ *                   ignored, k % 8 == 0, data 16-byte aligned.              */
+typedef struct i4d_mat {
+    const void* data;
+    const void* scales;
+    int32_t n, k, group, dtype;
+} i4d_mat;
+
+/* One decoder layer (host struct of device pointers).  Shapes, with
+ * qw = n_q_heads*head_dim, kvw = n_kv_heads*head_dim, D = d_model, F = d_ff:
+ *   wq [qw][D], wk [kvw][D], wv [kvw][D], wo [D][qw], wg [F][D], wu [F][D],
+ *   wd [D][F]; attn_norm, ffn_norm: bf16 [D].  All seven matrices share one
+ *   dtype (and one group for int4).                                         */
+typedef struct i4d_layer {
+    const uint16_t* attn_norm;
+    i4d_mat wq, wk, wv, wo;
+    const uint16_t* ffn_norm;
+    i4d_mat wg, wu, wd;
+} i4d_layer;
+
+/* Model shape.  head_dim must be 64 or 128; n_q_heads / n_kv_heads <= 16.
+ * exec_mode selects how decode_layer/decode_stack run their phases:
+ *   0 = auto (persistent kernel when supported, else one launch per phase),
+ *   1 = one kernel launch per phase,
+ *   2 = one persistent cooperative kernel per call with grid barriers.     */
+typedef struct i4d_config {
+    int32_t d_model, n_q_heads, n_kv_heads, head_dim, d_ff;
+    float   rms_eps;
+    double  rope_base;
+    int32_t exec_mode;
+} i4d_config;
+
+/* KV cache of one layer.
+ *   k: bf16 [B][n_kv_heads][capacity][head_dim]  (keys, after RoPE)
+ *   v: bf16 [B][n_kv_heads][head_dim][capacity]  (values, stored transposed so
+ *      that the attention kernel reads a run of positions per dimension)
+ * capacity % 8 == 0.  Slot t of sequence b holds the token at position t.    */
+typedef struct i4d_kv {
+    uint16_t* k;
+    uint16_t* v;
+    int32_t capacity;
+} i4d_kv;
+
+/* Bytes of workspace needed for this shape, batch, largest position and
+ * vocabulary (0 if no LM head is used).  Pure host arithmetic.              */
+size_t i4d_workspace_size(const i4d_config* cfg, int32_t batch, int32_t max_pos, int32_t vocab);
+
+/* Zero a fresh workspace, status word included (a fill kernel, no
+ * hipMemset).  Needed once per workspace.                                   */
+int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* One decoder layer for `batch` sequences (1 <= batch <= 8).
+ *   x_in  [B][D] fp32: hidden state of each sequence's new token.
+ *   x_out [B][D] fp32: layer output z; must not alias x_in.
+ *   pos   [B] int32 (device): number of cached tokens = position of the new
+ *         token; attention covers slots 0..pos[b].  Slot pos[b] of every KV
+ *         head is written (K after RoPE, V), no other slot is touched.
+ *   max_pos (host): an upper bound on pos[b], < kv->capacity; it sizes the
+ *         split of the key axis.                                            */
+int i4d_decode_layer(const i4d_config* cfg, const i4d_layer* layer, int32_t batch,
+                     const float* x_in, float* x_out, const i4d_kv* kv,
+                     const int32_t* pos, int32_t max_pos,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* n_layers decoder layers applied in order (Primer 1.2's decode loop), each
+ * layer's output feeding the next.  `layers` and `kv` are HOST arrays of
+ * n_layers entries.  Same contract as i4d_decode_layer otherwise.           */
+int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch,
+                     const float* x_in, float* x_out, const i4d_kv* kv,
+                     const int32_t* pos, int32_t max_pos,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy LM head (Unsloth article 三; Primer 1.2): for each of `batch` hidden
+ * states h [B][D] fp32, token_out[b] = lowest v maximising (W_lm h_b)_v and
+ * max_logit_out[b] = that logit (fp32).  w_lm is int4 [V][D].  The vocabulary
+ * is swept in passes of chunk_rows rows (chunk_rows > 0) with a running
+ * argmax; the full logit vector is never stored.  1 <= batch <= 8.
+ * ws_bytes >= I4D_WS_MIN_BYTES.                                              */
+int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
+                        int32_t* token_out, float* max_logit_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Expand an int4 matrix to fp32 out [n][k]: out = (code - 8) * scale, exact
+ * (Unsloth article 二.3).  A test hook for the int4 format.                 */
+int i4d_dequant_int4(const i4d_mat* w, float* out, void* stream);
+
+/* Plain y[b] = W x[b] through the streaming matrix-vector core (x [B][k],
+ * y [B][n] fp32, 1 <= batch <= 8).  A test hook for the core every
+ * projection of the layer uses.                                             */
+int i4d_gemv(const i4d_mat* w, int32_t batch, const float* x, float* y,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* Decode attention alone (Primer 1.1; Unsloth article 二.2; Roofline reply
+ * 四): q [B][n_q_heads][head_dim] fp32 (already rotated), the cache of one
+ * layer holding slots 0..pos[b], o [B][n_q_heads][head_dim] fp32.  Reads no
+ * slot beyond pos[b].                                                        */
+int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4d_kv* kv,
+                  const int32_t* pos, int32_t max_pos, float* o,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Copy the workspace's device status word to *status_out (host) after the
+ * stream's prior work; blocks until it is available.                       */
+int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream);
+
+/* Static text for a status code. */
+const char* i4d_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* I4DECODE_H */

@@ -1,0 +1,183 @@
+"""ctypes binding of libi4decode.so (include/i4decode.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of the library.  Tensors are torch device tensors; their data pointers
+and torch's current HIP stream are handed to the C entry points, which return a
+status code that is turned into an exception here.  The library is loaded on
+first use; if it has not been built, loading raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libi4decode.so")
+
+I4D_OK = 0
+I4D_EINVAL = -1
+I4D_EALIGN = -2
+I4D_EWORKSPACE = -3
+I4D_ERANGE = -4
+I4D_EHIP = -5
+I4D_EUNSUPPORTED = -6
+WS_MIN_BYTES = 512 + 4096 * 8 * 8     # I4D_WS_MIN_BYTES
+I4D_DEV_BAD_POS = 1
+I4D_DEV_BARRIER_TIMEOUT = 2
+
+WEIGHT_INT4 = 0
+WEIGHT_BF16 = 1
+
+EXEC_AUTO = 0
+EXEC_PHASES = 1
+EXEC_PERSISTENT = 2
+
+
+class I4dMat(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("n", ctypes.c_int32), ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class I4dLayer(ctypes.Structure):
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("wq", I4dMat), ("wk", I4dMat), ("wv", I4dMat), ("wo", I4dMat),
+                ("ffn_norm", ctypes.c_void_p), ("wg", I4dMat), ("wu", I4dMat), ("wd", I4dMat)]
+
+
+class I4dConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_base", ctypes.c_double), ("exec_mode", ctypes.c_int32)]
+
+
+class I4dKv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
+
+
+class I4DError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: status {code} ({status_string(code)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if libi4decode.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() (hipcc for gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.i4d_workspace_size.argtypes = [ctypes.POINTER(I4dConfig), I, I, I]
+        L.i4d_workspace_size.restype = Z
+        L.i4d_workspace_init.argtypes = [P, Z, P]
+        L.i4d_decode_layer.argtypes = [ctypes.POINTER(I4dConfig), ctypes.POINTER(I4dLayer), I, P, P,
+                                       ctypes.POINTER(I4dKv), P, I, P, Z, P]
+        L.i4d_decode_stack.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
+                                       ctypes.POINTER(I4dKv), P, I, P, Z, P]
+        L.i4d_lm_head_chunked.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P, Z, P]
+        L.i4d_dequant_int4.argtypes = [ctypes.POINTER(I4dMat), P, P]
+        L.i4d_gemv.argtypes = [ctypes.POINTER(I4dMat), I, P, P, P, Z, P]
+        L.i4d_attention.argtypes = [ctypes.POINTER(I4dConfig), I, P, ctypes.POINTER(I4dKv), P, I, P, P, Z, P]
+        L.i4d_read_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
+        L.i4d_status_string.argtypes = [ctypes.c_int]
+        L.i4d_status_string.restype = ctypes.c_char_p
+        for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked",
+                     "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().i4d_status_string(int(code)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != I4D_OK:
+        raise I4DError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ------------------------------------------------------------------ struct builders
+
+def make_config(d_model, n_q_heads, n_kv_heads, head_dim, d_ff, rms_eps, rope_base, exec_mode=EXEC_AUTO) -> I4dConfig:
+    return I4dConfig(d_model, n_q_heads, n_kv_heads, head_dim, d_ff, rms_eps, rope_base, exec_mode)
+
+
+def make_mat(data, scales, n, k, group, dtype=WEIGHT_INT4) -> I4dMat:
+    """data/scales: torch tensors (scales None for bf16)."""
+    return I4dMat(data.data_ptr(), scales.data_ptr() if scales is not None else None, n, k, group, dtype)
+
+
+def make_layer(attn_norm, ffn_norm, mats: dict) -> I4dLayer:
+    """mats: name -> I4dMat for wq, wk, wv, wo, wg, wu, wd."""
+    return I4dLayer(attn_norm.data_ptr(), mats["wq"], mats["wk"], mats["wv"], mats["wo"],
+                    ffn_norm.data_ptr(), mats["wg"], mats["wu"], mats["wd"])
+
+
+def make_kv(k_cache, v_cache, capacity) -> I4dKv:
+    return I4dKv(k_cache.data_ptr(), v_cache.data_ptr(), capacity)
+
+
+# ------------------------------------------------------------------ entry points (same names as the C ABI)
+
+def workspace_size(cfg: I4dConfig, batch: int, max_pos: int, vocab: int = 0) -> int:
+    return int(lib().i4d_workspace_size(ctypes.byref(cfg), batch, max_pos, vocab))
+
+
+def workspace_init(ws, stream=None):
+    _check(lib().i4d_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_workspace_init")
+
+
+def decode_layer(cfg, layer: I4dLayer, batch, x_in, x_out, kv: I4dKv, pos, max_pos, ws, stream=None):
+    _check(lib().i4d_decode_layer(ctypes.byref(cfg), ctypes.byref(layer), batch, _ptr(x_in), _ptr(x_out),
+                                  ctypes.byref(kv), _ptr(pos), max_pos, _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "i4d_decode_layer")
+
+
+def decode_stack(cfg, layers, batch, x_in, x_out, kvs, pos, max_pos, ws, stream=None):
+    """layers: sequence (or prebuilt ctypes array) of I4dLayer; kvs: likewise of I4dKv."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_decode_stack(ctypes.byref(cfg), n, larr, batch, _ptr(x_in), _ptr(x_out), karr, _ptr(pos),
+                                  max_pos, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "i4d_decode_stack")
+
+
+def lm_head_chunked(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out, ws, stream=None):
+    _check(lib().i4d_lm_head_chunked(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, _ptr(token_out),
+                                     _ptr(max_logit_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "i4d_lm_head_chunked")
+
+
+def dequant_int4(w: I4dMat, out, stream=None):
+    _check(lib().i4d_dequant_int4(ctypes.byref(w), _ptr(out), _stream(stream)), "i4d_dequant_int4")
+
+
+def gemv(w: I4dMat, batch, x, y, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().i4d_gemv(ctypes.byref(w), batch, _ptr(x), _ptr(y), _ptr(ws), nbytes, _stream(stream)), "i4d_gemv")
+
+
+def attention(cfg, batch, q, kv: I4dKv, pos, max_pos, o, ws, stream=None):
+    _check(lib().i4d_attention(ctypes.byref(cfg), batch, _ptr(q), ctypes.byref(kv), _ptr(pos), max_pos, _ptr(o),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_attention")
+
+
+def read_device_status(ws, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    _check(lib().i4d_read_device_status(_ptr(ws), ctypes.byref(out), _stream(stream)), "i4d_read_device_status")
+    return int(out.value)

@@ -1,0 +1,54 @@
+// Device helpers shared by the decode kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+#define I4D_DEVINL __device__ __forceinline__
+
+// ---------------------------------------------------------------- bf16
+I4D_DEVINL float bf16_to_f32(uint16_t b) { return __uint_as_float((u32)b << 16); }
+
+// round-to-nearest-even to bf16 (finite inputs)
+I4D_DEVINL uint16_t f32_to_bf16(float f) {
+    u32 u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- cross-lane
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total
+// (rotations within the row; the same fixed schedule on every call).
+I4D_DEVINL float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+    return v;
+}
+
+I4D_DEVINL float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+I4D_DEVINL float shfl_f(float v, int lane) { return __shfl(v, lane, 64); }
+
+// ---------------------------------------------------------------- ordered argmax keys
+// Larger float -> larger unsigned key; lower index wins ties via the inverted
+// index in the low word, so one unsigned max gives (max logit, lowest id).
+I4D_DEVINL u32 float_order_key(float f) {
+    u32 u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+I4D_DEVINL float float_from_order_key(u32 k) {
+    u32 u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+I4D_DEVINL u64 argmax_key(float logit, u32 idx) { return ((u64)float_order_key(logit) << 32) | (u64)(0xFFFFFFFFu - idx); }
+
+// ---------------------------------------------------------------- status word
+I4D_DEVINL void raise_status(int* status, int bit) { atomicOr(status, bit); }

@@ -1,0 +1,747 @@
+// libi4decode: kernels and the C ABI of include/i4decode.h (gfx950).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <algorithm>
+#include <string.h>
+
+#include "../../include/i4decode.h"
+#include "attention.h"
+#include "common.h"
+#include "gemv.h"
+
+namespace {
+
+#ifndef I4D_GEMV_NT
+#define I4D_GEMV_NT 512
+#endif
+#ifndef I4D_GEMV_D
+#define I4D_GEMV_D 6
+#endif
+#ifndef I4D_ATTN_NT
+#define I4D_ATTN_NT 512
+#endif
+#ifndef I4D_WG_PER_CU
+#define I4D_WG_PER_CU 1
+#endif
+constexpr int GEMV_NT = I4D_GEMV_NT;       // threads per GEMV workgroup
+constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
+constexpr int ATTN_NT = I4D_ATTN_NT;       // threads per attention workgroup
+constexpr int WG_PER_CU = I4D_WG_PER_CU;   // GEMV workgroups per compute unit
+constexpr int NSPLIT_MAX = 128;    // key-axis splits per (sequence, KV head)
+constexpr int MAX_BATCH = 8;
+
+template <int NB> struct MaxJ { static constexpr int v = NB <= 2 ? 8 : 4; };
+
+// ============================================================== epilogues and staging functors
+
+// Stage `src` (optionally RMS-normalised with `gain`) into LDS.
+template <int FMT, int NB, int PREC>
+struct StageFn {
+    char* act; const float* src; int stride; int K; int nb; const uint16_t* gain; float eps; float* red;
+    __device__ void issue(StagePre<FMT>& pre) { stage_issue<FMT, NB, GEMV_NT>(pre, src, stride, K, nb, gain); }
+    __device__ void finish(const StagePre<FMT>& pre) {
+        stage_finish<FMT, NB, GEMV_NT, PREC>(pre, act, src, stride, K, nb, gain, eps, red);
+    }
+};
+
+// Activation precision of the int4 dot products: one fp16 plane (about 2^-12
+// relative per input), or fp16 value + fp16 remainder (about 2^-22) for the
+// q/k/v projection, whose k and v are rounded to bf16 into the cache.
+constexpr int PREC_STD = 1, PREC_QKV = 2;
+
+// y[b][row] = (resid ? resid[b][row] : 0) + W x   for rows 2p, 2p+1
+struct EpiRows {
+    float* y; const float* resid; int n; int nb;
+    __device__ void operator()(int, int pair, int b, float va, float vb) {
+        if (b >= nb) return;
+        const int r = 2 * pair;
+        float* yr = y + (size_t)b * n;
+        const float* rr = resid ? resid + (size_t)b * n : nullptr;
+        yr[r] = (rr ? rr[r] : 0.f) + va;
+        if (r + 1 < n) yr[r + 1] = (rr ? rr[r + 1] : 0.f) + vb;
+    }
+    __device__ void end_pass(int, int, int) {}
+};
+
+// act[b][i] = SiLU(gate_i) * up_i
+struct EpiSwiGLU {
+    float* act; int F; int nb;
+    __device__ void operator()(int, int pair, int b, float g, float u) {
+        if (b >= nb) return;
+        act[(size_t)b * F + pair] = g / (1.0f + expf(-g)) * u;
+    }
+    __device__ void end_pass(int, int, int) {}
+};
+
+// RoPE on q and k pairs, q to the fp32 buffer, bf16 k/v appended at slot pos[b].
+struct EpiQKV {
+    float* q; uint16_t* kc; uint16_t* vc; const int* pos_lds;
+    int cap, hq, hkv, hd, nb; double base;
+    __device__ void operator()(int, int pair, int b, float va, float vb) {
+        if (b >= nb) return;
+        const int half = hd >> 1;
+        const int npq = hq * half, npk = hkv * half;
+        int lp = pair, mat = 0;
+        if (lp >= npq) { lp -= npq; mat = 1; if (lp >= npk) { lp -= npk; mat = 2; } }
+        const int head = lp / half, i = lp - head * half;
+        const int p = pos_lds[b];                      // -1: invalid position, nothing appended
+        float ra = va, rb = vb;
+        if (mat < 2) {
+            const double theta = pow(base, -2.0 * (double)i / (double)hd);
+            const double phi = (double)max(p, 0) * theta;
+            const float c = (float)cos(phi), s = (float)sin(phi);
+            ra = va * c - vb * s;
+            rb = va * s + vb * c;
+        }
+        if (mat == 0) {
+            float* qr = q + ((size_t)b * hq + head) * hd;
+            qr[i] = ra; qr[i + half] = rb;
+        } else if (p >= 0) {
+            if (mat == 1) {
+                uint16_t* kr = kc + (((size_t)b * hkv + head) * cap + p) * hd;
+                kr[i] = f32_to_bf16(ra); kr[i + half] = f32_to_bf16(rb);
+            } else {
+                uint16_t* vr = vc + ((size_t)b * hkv + head) * hd * cap;
+                vr[(size_t)i * cap + p] = f32_to_bf16(ra);
+                vr[(size_t)(i + half) * cap + p] = f32_to_bf16(rb);
+            }
+        }
+    }
+    __device__ void end_pass(int, int, int) {}
+};
+
+// greedy argmax over rows 2p, 2p+1: per-thread running best key of batch slot
+// `bslot` (a thread always serves the same slot: the epilogue's thread-to-slot
+// assignment repeats every pass)
+struct EpiArgmax {
+    int n; int nb; u64 best; int bslot;
+    __device__ void operator()(int, int pair, int b, float va, float vb) {
+        if (b >= nb) return;
+        const int r = 2 * pair;
+        u64 k = argmax_key(va, (u32)r);
+        if (r + 1 < n) { const u64 k2 = argmax_key(vb, (u32)(r + 1)); k = k2 > k ? k2 : k; }
+        best = k > best ? k : best;
+        bslot = b;
+    }
+    __device__ void end_pass(int, int, int) {}
+};
+
+// ============================================================== LDS carve-up for GEMV kernels
+template <int FMT, int NB>
+__host__ __device__ constexpr int gemv_part_bytes() { return (GEMV_NT / 16) * (MaxJ<NB>::v * NB * 2 + 2) * 4; }
+
+template <int FMT, int NB, int PREC>
+__host__ inline size_t gemv_lds_bytes(int K) {
+    return (size_t)act_lds_bytes<FMT, NB, PREC>(K) + gemv_part_bytes<FMT, NB>() + (GEMV_NT / 64) * NB * 4 + 256;
+}
+
+struct GemvLds { char* act; float* part; float* red; char* extra; };
+
+template <int FMT, int NB, int PREC>
+__device__ inline GemvLds carve(char* lds, int K) {
+    GemvLds l;
+    l.act = lds;
+    l.part = (float*)(lds + act_lds_bytes<FMT, NB, PREC>(K));
+    l.red = l.part + gemv_part_bytes<FMT, NB>() / 4;
+    l.extra = (char*)(l.red + (GEMV_NT / 64) * NB);
+    return l;
+}
+
+// ============================================================== kernels
+__global__ void k_fill_zero(int* p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ void k_dequant(const uint8_t* codes, const uint16_t* scales, int n, int k, int group, int ngroups, float* out) {
+    const size_t total = (size_t)n * k;
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = idx / k;
+        const int i = (int)(idx - r * k);
+        const uint8_t byte = codes[r * (size_t)(k >> 1) + (i >> 1)];
+        const int c = (i & 1) ? (byte >> 4) : (byte & 15);
+        out[idx] = (float)(c - 8) * bf16_to_f32(scales[r * ngroups + i / group]);
+    }
+}
+
+template <int FMT, int NB>
+__global__ void __launch_bounds__(GEMV_NT) k_gemv_rows(GemvTask t, const float* x, int x_stride, int nb,
+                                                        const uint16_t* gain, float eps, float* y, const float* resid) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
+    StageFn<FMT, NB, PREC_STD> st{L.act, x, x_stride, t.k, nb, gain, eps, L.red};
+    EpiRows ep{y, resid, t.a.n, nb};
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+}
+
+template <int FMT, int NB>
+__global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float* x, int nb, const uint16_t* gain, float eps, float* act) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
+    StageFn<FMT, NB, PREC_STD> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
+    EpiSwiGLU ep{act, t.a.n, nb};
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+}
+
+template <int FMT, int NB>
+__global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x, int nb, const uint16_t* gain, float eps,
+                                                       const int* pos, int max_pos, float* q, uint16_t* kc, uint16_t* vc,
+                                                       int cap, int hq, int hkv, double base, int* status) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
+    int* pos_lds = (int*)L.extra;
+    if (threadIdx.x < NB) {
+        int p = -1;
+        if ((int)threadIdx.x < nb) {
+            p = pos[threadIdx.x];
+            if (p < 0 || p > max_pos || p >= cap) {
+                if (blockIdx.x == 0) raise_status(status, I4D_DEV_BAD_POS);
+                p = -1;
+            }
+        }
+        pos_lds[threadIdx.x] = p;
+    }
+    StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
+    EpiQKV ep{q, kc, vc, pos_lds, cap, hq, hkv, t.head_dim, nb, base};
+    gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+}
+
+template <int FMT, int NB>
+__global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h, int nb, u64* wg_keys) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
+    StageFn<FMT, NB, PREC_STD> st{L.act, h, t.k, t.k, nb, nullptr, 0.f, L.red};
+    EpiArgmax ep{t.a.n, nb, 0ull, -1};
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+    // workgroup best per batch slot -> this workgroup's key slots
+    u64* kl = (u64*)(L.extra + 256);
+    int* ks = (int*)(kl + GEMV_NT);
+    kl[threadIdx.x] = ep.best;
+    ks[threadIdx.x] = ep.bslot;
+    __syncthreads();
+    if ((int)threadIdx.x < MAX_BATCH) {
+        u64 best = 0;
+        for (int i = 0; i < GEMV_NT; ++i)
+            if (ks[i] == (int)threadIdx.x) best = kl[i] > best ? kl[i] : best;
+        wg_keys[(size_t)blockIdx.x * MAX_BATCH + threadIdx.x] = best;
+    }
+}
+
+// Reduce the per-workgroup argmax keys: token = lowest id of the largest logit.
+__global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg, int nb, int32_t* token_out, float* max_out) {
+    __shared__ u64 red[256];
+    for (int b = 0; b < nb; ++b) {
+        u64 best = 0;
+        for (int w = threadIdx.x; w < nwg; w += 256) {
+            const u64 k = wg_keys[(size_t)w * MAX_BATCH + b];
+            best = k > best ? k : best;
+        }
+        red[threadIdx.x] = best;
+        __syncthreads();
+        for (int s2 = 128; s2 > 0; s2 >>= 1) {
+            if ((int)threadIdx.x < s2) red[threadIdx.x] = red[threadIdx.x + s2] > red[threadIdx.x] ? red[threadIdx.x + s2] : red[threadIdx.x];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            const u64 k = red[0];
+            token_out[b] = (int32_t)(0xFFFFFFFFu - (u32)(k & 0xFFFFFFFFull));
+            max_out[b] = float_from_order_key((u32)(k >> 32));
+        }
+        __syncthreads();
+    }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int items = a.batch * a.hkv * a.nsplit;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT>(a, it, lds);
+}
+
+template <int HD>
+__global__ void __launch_bounds__(HD) k_attention_merge(AttnArgs a) {
+    __shared__ float lds[2 * NSPLIT_MAX];
+    attn_merge_head<HD>(a, blockIdx.x, lds);
+}
+
+// ============================================================== host helpers
+int g_num_cus[64];
+
+int num_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (g_num_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_num_cus[dev] = n;
+    }
+    return g_num_cus[dev];
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: a 512-byte header (the status word), then the fp32 buffers of
+// the layer.  The LM head uses the bytes after the header for its
+// per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer buffers:
+// calls on one stream never use both at once.
+constexpr size_t WS_STATUS = 0, WS_HEADER = 512;
+constexpr int LM_MAX_WG = 4096;
+constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH * 8;
+
+struct WsLayout {
+    size_t q, pm, pl, po, o, y, act, ping0, ping1, total;
+};
+
+WsLayout ws_layout(const i4d_config* c, int B) {
+    WsLayout w;
+    size_t off = WS_HEADER;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    const size_t hq = c->n_q_heads, hd = c->head_dim;
+    w.q = take((size_t)B * hq * hd * 4);
+    w.pm = take((size_t)B * hq * NSPLIT_MAX * 4);
+    w.pl = take((size_t)B * hq * NSPLIT_MAX * 4);
+    w.po = take((size_t)B * hq * NSPLIT_MAX * hd * 4);
+    w.o = take((size_t)B * hq * hd * 4);
+    w.y = take((size_t)B * c->d_model * 4);
+    w.act = take((size_t)B * c->d_ff * 4);
+    w.ping0 = take((size_t)B * c->d_model * 4);
+    w.ping1 = take((size_t)B * c->d_model * 4);
+    w.total = std::max(off, WS_LM_KEYS + WS_LM_BYTES);
+    return w;
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int v) { int l = 0; while ((1 << l) < v) ++l; return l; }
+
+int validate_mat(const i4d_mat* m, int n, int k, int dtype, int group) {
+    if (!m || !m->data) return I4D_EINVAL;
+    if (m->n != n || m->k != k || m->dtype != dtype) return I4D_EINVAL;
+    if (!aligned(m->data, 16)) return I4D_EALIGN;
+    if (dtype == I4D_WEIGHT_INT4) {
+        if (!m->scales || m->group != group || group <= 0 || group % 8 != 0 || k % 8 != 0) return I4D_EINVAL;
+        if (!aligned(m->scales, 2)) return I4D_EALIGN;
+    } else if (dtype == I4D_WEIGHT_BF16) {
+        if (k % 8 != 0) return I4D_EINVAL;
+    } else {
+        return I4D_EINVAL;
+    }
+    return I4D_OK;
+}
+
+int validate_cfg(const i4d_config* c) {
+    if (!c) return I4D_EINVAL;
+    if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->d_ff <= 0) return I4D_EINVAL;
+    if (c->head_dim != 64 && c->head_dim != 128) return I4D_EINVAL;
+    if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 16) return I4D_EINVAL;
+    if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.0)) return I4D_EINVAL;
+    if (c->exec_mode < 0 || c->exec_mode > 2) return I4D_EINVAL;
+    return I4D_OK;
+}
+
+int validate_layer(const i4d_config* c, const i4d_layer* L) {
+    if (!L || !L->attn_norm || !L->ffn_norm) return I4D_EINVAL;
+    if (!aligned(L->attn_norm, 2) || !aligned(L->ffn_norm, 2)) return I4D_EALIGN;
+    const int D = c->d_model, qw = c->n_q_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim, F = c->d_ff;
+    const int dt = L->wq.dtype, g = L->wq.group;
+    int rc;
+    if ((rc = validate_mat(&L->wq, qw, D, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wk, kvw, D, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wv, kvw, D, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wo, D, qw, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wg, F, D, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wu, F, D, dt, g))) return rc;
+    if ((rc = validate_mat(&L->wd, D, F, dt, g))) return rc;
+    return I4D_OK;
+}
+
+int validate_kv(const i4d_config* c, const i4d_kv* kv, int max_pos) {
+    (void)c;
+    if (!kv || !kv->k || !kv->v) return I4D_EINVAL;
+    if (kv->capacity <= 0 || kv->capacity % 8 != 0) return I4D_EINVAL;
+    if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return I4D_EALIGN;
+    if (max_pos < 0 || max_pos >= kv->capacity) return I4D_ERANGE;
+    return I4D_OK;
+}
+
+int validate_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (!ws) return I4D_EWORKSPACE;
+    if (!aligned(ws, 256)) return I4D_EALIGN;
+    if (ws_bytes < need) return I4D_EWORKSPACE;
+    return I4D_OK;
+}
+
+DevMat dev_mat(const i4d_mat& m) {
+    DevMat d;
+    d.data = (const uint8_t*)m.data;
+    d.scales = (const uint16_t*)m.scales;
+    d.n = m.n; d.k = m.k; d.group = m.group;
+    d.ngroups = (m.dtype == I4D_WEIGHT_INT4) ? (m.k + m.group - 1) / m.group : 0;
+    return d;
+}
+
+int pick_fmt(const i4d_mat& m) {
+    if (m.dtype == I4D_WEIGHT_INT4)
+        return (m.k % 512 == 0 && is_pow2(m.group) && m.group >= 32) ? FMT_INT4_FAST : FMT_INT4_GEN;
+    return (m.k % 128 == 0) ? FMT_BF16_FAST : FMT_BF16_GEN;
+}
+
+int unit_w(int fmt) {
+    switch (fmt) {
+        case FMT_INT4_FAST: return FmtT<FMT_INT4_FAST>::UNIT_W;
+        case FMT_INT4_GEN: return FmtT<FMT_INT4_GEN>::UNIT_W;
+        case FMT_BF16_FAST: return FmtT<FMT_BF16_FAST>::UNIT_W;
+        default: return FmtT<FMT_BF16_GEN>::UNIT_W;
+    }
+}
+
+int nb_slot(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
+int maxj_of(int nb) { return nb <= 2 ? MaxJ<1>::v : MaxJ<4>::v; }
+
+// Fill pass geometry: at most `cap_pairs` pairs per pass (0: no cap), and never
+// more pairs per workgroup than keeps every slot within MAXJ runs.
+void plan_passes(GemvTask& t, int fmt, int nb, int nwg, int cap_pairs) {
+    const int S = (t.k + unit_w(fmt) - 1) / unit_w(fmt);
+    const int maxj = maxj_of(nb);
+    int ppw = (t.total_pairs + nwg - 1) / nwg;
+    while (ppw > 1 && gemv_max_runs(ppw, S, GEMV_NT / 64) > maxj) --ppw;
+    long long pp = (long long)ppw * nwg;
+    if (cap_pairs > 0 && pp > cap_pairs) pp = cap_pairs;
+    if (pp > t.total_pairs) pp = t.total_pairs;
+    if (pp < 1) pp = 1;
+    // with pp pairs per pass a workgroup gets at most ceil(pp / nwg) <= ppw pairs
+    t.pass_pairs = (int)pp;
+    t.npasses = (t.total_pairs + t.pass_pairs - 1) / t.pass_pairs;
+}
+
+GemvTask make_task(int kind, const i4d_mat* a, const i4d_mat* b, const i4d_mat* c, int head_dim) {
+    GemvTask t;
+    memset(&t, 0, sizeof(t));
+    t.kind = kind;
+    t.a = dev_mat(*a);
+    t.b = b ? dev_mat(*b) : t.a;
+    t.c = c ? dev_mat(*c) : t.a;
+    t.k = a->k;
+    t.log2_group = (a->dtype == I4D_WEIGHT_INT4) ? ilog2(a->group) : 0;
+    t.head_dim = head_dim;
+    if (kind == KIND_ADJ) t.total_pairs = (a->n + 1) / 2;
+    else if (kind == KIND_TWO) t.total_pairs = a->n;
+    else t.total_pairs = (a->n + b->n + c->n) / 2;
+    return t;
+}
+
+// Raise a kernel's dynamic-LDS limit once per process and device (a host-side
+// cache keyed by the kernel; the attribute only ever grows).
+struct LdsAttr { const void* fn; int dev; size_t bytes; };
+LdsAttr g_lds_attr[256];
+int g_lds_attr_n = 0;
+
+template <class K>
+hipError_t set_lds(K kernel, size_t bytes) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const void* fn = (const void*)kernel;
+    for (int i = 0; i < g_lds_attr_n; ++i)
+        if (g_lds_attr[i].fn == fn && g_lds_attr[i].dev == dev) {
+            if (g_lds_attr[i].bytes >= bytes) return hipSuccess;
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+            if (e == hipSuccess) g_lds_attr[i].bytes = bytes;
+            return e;
+        }
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && g_lds_attr_n < 256) g_lds_attr[g_lds_attr_n++] = LdsAttr{fn, dev, bytes};
+    return e;
+}
+
+constexpr size_t LDS_LIMIT = 160 * 1024;
+
+// ---------------------------------------------------------------- typed launchers
+#define I4D_DISPATCH(FMTV, NBV, CALL)                                                         \
+    switch (FMTV) {                                                                           \
+        case FMT_INT4_FAST: switch (NBV) { case 1: CALL(FMT_INT4_FAST, 1); case 2: CALL(FMT_INT4_FAST, 2); \
+                                           case 4: CALL(FMT_INT4_FAST, 4); default: CALL(FMT_INT4_FAST, 8); } \
+        case FMT_INT4_GEN: switch (NBV) { case 1: CALL(FMT_INT4_GEN, 1); case 2: CALL(FMT_INT4_GEN, 2); \
+                                          case 4: CALL(FMT_INT4_GEN, 4); default: CALL(FMT_INT4_GEN, 8); } \
+        case FMT_BF16_FAST: switch (NBV) { case 1: CALL(FMT_BF16_FAST, 1); case 2: CALL(FMT_BF16_FAST, 2); \
+                                           case 4: CALL(FMT_BF16_FAST, 4); default: CALL(FMT_BF16_FAST, 8); } \
+        default: switch (NBV) { case 1: CALL(FMT_BF16_GEN, 1); case 2: CALL(FMT_BF16_GEN, 2);     \
+                                case 4: CALL(FMT_BF16_GEN, 4); default: CALL(FMT_BF16_GEN, 8); } \
+    }
+
+template <int FMT, int NB>
+int launch_rows_t(const GemvTask& t, int nwg, const float* x, int x_stride, int nb, const uint16_t* gain, float eps,
+                  float* y, const float* resid, hipStream_t s) {
+    const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (set_lds(k_gemv_rows<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    hipLaunchKernelGGL((k_gemv_rows<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, x_stride, nb, gain, eps, y, resid);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+template <int FMT, int NB>
+int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, float* act, hipStream_t s) {
+    const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (set_lds(k_gemv_swiglu<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    hipLaunchKernelGGL((k_gemv_swiglu<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, act);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+template <int FMT, int NB>
+int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, const int* pos, int max_pos,
+                 float* q, const i4d_kv* kv, int hq, int hkv, double base, int* status, hipStream_t s) {
+    const size_t lds = gemv_lds_bytes<FMT, NB, PREC_QKV>(t.k);
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    hipLaunchKernelGGL((k_gemv_qkv<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
+                       kv->k, kv->v, kv->capacity, hq, hkv, base, status);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+template <int FMT, int NB>
+int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys, int32_t* tok, float* mx, hipStream_t s) {
+    if constexpr (!FmtT<FMT>::INT4) {
+        return I4D_EUNSUPPORTED;
+    } else {
+        const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k) + (size_t)GEMV_NT * 12;
+        if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+        if (set_lds(k_lm_head<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+        hipLaunchKernelGGL((k_lm_head<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys);
+        hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, nb, tok, mx);
+        return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+    }
+}
+
+int launch_rows(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int x_stride, int bn, const uint16_t* gain,
+                float eps, float* y, const float* resid, hipStream_t s) {
+#define CALL(F, N) return launch_rows_t<F, N>(t, nwg, x, x_stride, bn, gain, eps, y, resid, s)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+int launch_swiglu(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int bn, const uint16_t* gain, float eps, float* act,
+                  hipStream_t s) {
+#define CALL(F, N) return launch_swiglu_t<F, N>(t, nwg, x, bn, gain, eps, act, s)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+int launch_qkv(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int bn, const uint16_t* gain, float eps,
+               const int* pos, int max_pos, float* q, const i4d_kv* kv, int hq, int hkv, double base, int* status, hipStream_t s) {
+#define CALL(F, N) return launch_qkv_t<F, N>(t, nwg, x, bn, gain, eps, pos, max_pos, q, kv, hq, hkv, base, status, s)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+int launch_lm(int fmt, int nb, const GemvTask& t, int nwg, const float* h, int bn, u64* keys, int32_t* tok, float* mx,
+              hipStream_t s) {
+#define CALL(F, N) return launch_lm_t<F, N>(t, nwg, h, bn, keys, tok, mx, s)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+
+// attention split plan
+void plan_attention(const i4d_config* c, int B, int max_pos, int& nsplit, int& T) {
+    const int nk = max_pos + 1;
+    int want = (num_cus() + B * c->n_kv_heads - 1) / (B * c->n_kv_heads);
+    want = std::max(1, std::min(want, NSPLIT_MAX));
+    T = (nk + want - 1) / want;
+    T = std::max(16, ((T + 3) / 4) * 4);
+    nsplit = (nk + T - 1) / T;
+    if (nsplit > NSPLIT_MAX) {   // not reachable with T >= nk / NSPLIT_MAX, kept as a guard
+        T = ((nk + NSPLIT_MAX - 1) / NSPLIT_MAX + 3) / 4 * 4;
+        nsplit = (nk + T - 1) / T;
+    }
+}
+
+int launch_attention(const i4d_config* c, int B, const float* q, const i4d_kv* kv, const int* pos, int max_pos, float* o,
+                     char* ws, const WsLayout& W, hipStream_t s) {
+    AttnArgs a;
+    a.q = q; a.kc = kv->k; a.vc = kv->v; a.pos = pos;
+    a.cap = kv->capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B; a.max_pos = max_pos;
+    plan_attention(c, B, max_pos, a.nsplit, a.T);
+    a.nsplit_max = NSPLIT_MAX;
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
+    a.pm = (float*)(ws + W.pm); a.pl = (float*)(ws + W.pl); a.po = (float*)(ws + W.po);
+    a.o = o;
+    const int items = B * c->n_kv_heads * a.nsplit;
+    const int heads = B * c->n_q_heads;
+    if (c->head_dim == 128) {
+        const size_t lds = attn_lds_bytes<128, ATTN_NT>();
+        if (set_lds(k_attention<128>, lds) != hipSuccess) return I4D_EHIP;
+        hipLaunchKernelGGL(k_attention<128>, dim3(items), dim3(ATTN_NT), lds, s, a);
+        hipLaunchKernelGGL(k_attention_merge<128>, dim3(heads), dim3(128), 0, s, a);
+    } else {
+        const size_t lds = attn_lds_bytes<64, ATTN_NT>();
+        if (set_lds(k_attention<64>, lds) != hipSuccess) return I4D_EHIP;
+        hipLaunchKernelGGL(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
+        hipLaunchKernelGGL(k_attention_merge<64>, dim3(heads), dim3(64), 0, s, a);
+    }
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// One layer as five phase launches.
+int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
+                     const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
+    const int nb = nb_slot(B), nwg = num_cus() * WG_PER_CU;
+    const int hd = c->head_dim;
+    int* status = (int*)(ws + WS_STATUS);
+    float* q = (float*)(ws + W.q);
+    float* o = (float*)(ws + W.o);
+    float* y = (float*)(ws + W.y);
+    float* act = (float*)(ws + W.act);
+    int rc;
+
+    GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
+    const int fq = pick_fmt(L->wq);
+    plan_passes(tq, fq, nb, nwg, 0);
+    if ((rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, c->n_q_heads,
+                         c->n_kv_heads, c->rope_base, status, s))) return rc;
+
+    if ((rc = launch_attention(c, B, q, kv, pos, max_pos, o, ws, W, s))) return rc;
+
+    GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
+    const int fo = pick_fmt(L->wo);
+    plan_passes(to, fo, nb, nwg, 0);
+    if ((rc = launch_rows(fo, nb, to, nwg, o, c->n_q_heads * hd, B, nullptr, 0.f, y, x_in, s))) return rc;
+
+    GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
+    const int fg = pick_fmt(L->wg);
+    plan_passes(tg, fg, nb, nwg, 0);
+    if ((rc = launch_swiglu(fg, nb, tg, nwg, y, B, L->ffn_norm, c->rms_eps, act, s))) return rc;
+
+    GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
+    const int fd = pick_fmt(L->wd);
+    plan_passes(td, fd, nb, nwg, 0);
+    return launch_rows(fd, nb, td, nwg, act, c->d_ff, B, nullptr, 0.f, x_out, y, s);
+}
+
+}  // namespace
+
+// ============================================================== C ABI
+extern "C" {
+
+size_t i4d_workspace_size(const i4d_config* cfg, int32_t batch, int32_t max_pos, int32_t vocab) {
+    if (validate_cfg(cfg) || batch < 1 || batch > MAX_BATCH || max_pos < 0) return 0;
+    (void)vocab;
+    return ws_layout(cfg, batch).total;
+}
+
+int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return I4D_EWORKSPACE;
+    if (!aligned(ws, 256)) return I4D_EALIGN;
+    if (ws_bytes < WS_HEADER) return I4D_EWORKSPACE;
+    // the status word lives in the header; zero the whole workspace
+    hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(256), 0, (hipStream_t)stream, (int*)ws, ws_bytes / 4);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int i4d_decode_layer(const i4d_config* cfg, const i4d_layer* layer, int32_t batch, const float* x_in, float* x_out,
+                     const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes, void* stream) {
+    return i4d_decode_stack(cfg, 1, layer, batch, x_in, x_out, kv, pos, max_pos, ws, ws_bytes, stream);
+}
+
+int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch, const float* x_in,
+                     float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int rc;
+    if ((rc = validate_cfg(cfg))) return rc;
+    if (n_layers < 1 || !layers || !kv) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (!x_in || !x_out || !pos || x_in == x_out) return I4D_EINVAL;
+    if (!aligned(x_in, 16) || !aligned(x_out, 16) || !aligned(pos, 4)) return I4D_EALIGN;
+    if (cfg->d_model % 8 != 0 || cfg->d_ff % 8 != 0) return I4D_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((rc = validate_layer(cfg, &layers[l]))) return rc;
+        if (layers[l].wq.dtype != layers[0].wq.dtype) return I4D_EINVAL;
+        if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
+    }
+    const WsLayout W = ws_layout(cfg, batch);
+    if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
+    if (cfg->exec_mode == 2) return I4D_EUNSUPPORTED;
+    char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    float* ping[2] = {(float*)(w + W.ping0), (float*)(w + W.ping1)};
+    for (int l = 0; l < n_layers; ++l) {
+        const float* in = (l == 0) ? x_in : ping[(l - 1) & 1];
+        float* out = (l == n_layers - 1) ? x_out : ping[l & 1];
+        if ((rc = run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, s))) return rc;
+    }
+    return I4D_OK;
+}
+
+int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
+                        float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!w_lm || w_lm->dtype != I4D_WEIGHT_INT4) return I4D_EINVAL;
+    int rc;
+    if ((rc = validate_mat(w_lm, w_lm->n, w_lm->k, I4D_WEIGHT_INT4, w_lm->group))) return rc;
+    if (w_lm->n < 1 || w_lm->k < 8) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH || chunk_rows <= 0) return I4D_ERANGE;
+    if (!h || !token_out || !max_logit_out) return I4D_EINVAL;
+    if (!aligned(h, 16)) return I4D_EALIGN;
+    if ((rc = validate_ws(ws, ws_bytes, WS_LM_KEYS + WS_LM_BYTES))) return rc;
+    char* w = (char*)ws;
+    const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
+    GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
+    const int fmt = pick_fmt(*w_lm);
+    plan_passes(t, fmt, nb, nwg, (chunk_rows + 1) / 2);
+    if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
+    return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, (hipStream_t)stream);
+}
+
+int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {
+    if (!wm || !out) return I4D_EINVAL;
+    int rc;
+    if ((rc = validate_mat(wm, wm->n, wm->k, I4D_WEIGHT_INT4, wm->group))) return rc;
+    const int ng = (wm->k + wm->group - 1) / wm->group;
+    hipLaunchKernelGGL(k_dequant, dim3(1024), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)wm->data,
+                       (const uint16_t*)wm->scales, wm->n, wm->k, wm->group, ng, out);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int i4d_gemv(const i4d_mat* wm, int32_t batch, const float* x, float* y, void* ws, size_t ws_bytes, void* stream) {
+    if (!wm || !x || !y) return I4D_EINVAL;
+    int rc;
+    if ((rc = validate_mat(wm, wm->n, wm->k, wm->dtype, wm->group))) return rc;
+    if (wm->n < 1) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (!aligned(x, 16) || !aligned(y, 4)) return I4D_EALIGN;
+    (void)ws; (void)ws_bytes;
+    const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
+    GemvTask t = make_task(KIND_ADJ, wm, nullptr, nullptr, 64);
+    const int fmt = pick_fmt(*wm);
+    plan_passes(t, fmt, nb, nwg, 0);
+    return launch_rows(fmt, nb, t, nwg, x, wm->k, batch, nullptr, 0.f, y, nullptr, (hipStream_t)stream);
+}
+
+int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4d_kv* kv, const int32_t* pos, int32_t max_pos,
+                  float* o, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = validate_cfg(cfg))) return rc;
+    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (!q || !o || !pos) return I4D_EINVAL;
+    if ((rc = validate_kv(cfg, kv, max_pos))) return rc;
+    const WsLayout W = ws_layout(cfg, batch);
+    if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
+    return launch_attention(cfg, batch, q, kv, pos, max_pos, o, (char*)ws, W, (hipStream_t)stream);
+}
+
+int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream) {
+    if (!ws || !status_out) return I4D_EINVAL;
+    if (hipMemcpyAsync(status_out, ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return I4D_EHIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return I4D_EHIP;
+    return I4D_OK;
+}
+
+const char* i4d_status_string(int status) {
+    switch (status) {
+        case I4D_OK: return "ok";
+        case I4D_EINVAL: return "invalid argument (null pointer, shape, group or head layout)";
+        case I4D_EALIGN: return "misaligned pointer";
+        case I4D_EWORKSPACE: return "workspace missing or too small";
+        case I4D_ERANGE: return "value out of range (batch, max_pos or chunk_rows)";
+        case I4D_EHIP: return "HIP launch failed";
+        case I4D_EUNSUPPORTED: return "request not supported by this build";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

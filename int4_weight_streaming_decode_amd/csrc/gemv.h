@@ -1,0 +1,612 @@
+// Weight-streaming matrix-vector core for small batches (gfx950, wave64).
+//
+// Every weight byte is read from HBM once per step (Primer 1.2: decode time is
+// the time to read the weights once; Unsloth article 二.3: int4 codes are
+// expanded only in registers).  Rows are processed in pairs (two rows that one
+// epilogue needs together: the two halves of a RoPE pair, a gate row and its
+// up row, or two adjacent rows).  A pair's K axis is cut into units of
+// 16 lanes x one 16-byte load per row, so each 16-lane DPP row streams 256
+// contiguous bytes of each of its two rows per load.
+//
+// Work split.  The pairs of a pass are split evenly over workgroups; inside a
+// workgroup the (pair, unit) grid is cut into one contiguous range per wave and
+// then one contiguous range per 16-lane slot.  A slot accumulates in registers
+// while its pair stays the same and parks the per-lane sum of a finished pair
+// ("run") in a small register array; at the end of the pass the runs are
+// summed over their 16 lanes with DPP rotations and written to LDS, and the
+// per-pair totals are formed in slot order -- a fixed order, so results are
+// bit-reproducible.
+//
+// Loads are software-pipelined: each lane keeps D units in flight in a ring of
+// registers, and the ring runs ahead across pass boundaries of a phase.
+//
+// int4 unpack: a dword holds 8 codes c0..c7 (c0 lowest nibble).  OR-ing
+// 0x6400 (fp16 1024.0) into the masked halves gives fp16 (1024 + c) for the
+// nibbles at bits 0-3 / 16-19 and (1024 + 16 c) for bits 4-7 / 20-23 (likewise
+// after one 8-bit shift), all exact.  The activations are staged in LDS as fp16
+// pairs in the matching order, the odd ones pre-divided by 16 (exact), and
+// v_dot2_f32_f16 accumulates in fp32.  The bias terms and the zero-point of 8
+// come out as one per-32-input correction computed at staging time:
+//   sum (c - 8) x = acc - (1032 * sum x_even + 1152 * sum a_odd)
+// (a_odd = the stored x_odd / 16).  The bf16 group scale multiplies the unit's
+// partial sum once.  This costs about 1.2 VALU operations per weight.
+#pragma once
+#include "common.h"
+
+enum { FMT_INT4_FAST = 0, FMT_INT4_GEN = 1, FMT_BF16_FAST = 2, FMT_BF16_GEN = 3 };
+enum { KIND_ADJ = 0, KIND_TWO = 1, KIND_QKV = 2 };
+
+struct DevMat {
+    const uint8_t* data;       // int4 codes [n][k/2] or bf16 [n][k]
+    const uint16_t* scales;    // bf16 [n][ngroups] (int4 only)
+    int n, k, group, ngroups;
+};
+
+// One matrix-vector phase.
+struct GemvTask {
+    int kind;                  // KIND_*
+    DevMat a, b, c;            // ADJ: a.  TWO: rows of a paired with rows of b.  QKV: q, k, v.
+    int k;                     // inputs per row (all matrices of the task)
+    int log2_group;            // fast int4 path: group = 1 << log2_group
+    int head_dim;              // QKV pairing
+    int total_pairs;
+    int pass_pairs;            // pairs per pass (all workgroups together)
+    int npasses;
+};
+
+template <int FMT> struct FmtT;
+template <> struct FmtT<FMT_INT4_FAST> { static constexpr int LANE_B = 16, LANE_W = 32, UNIT_W = 512; static constexpr bool INT4 = true; };
+template <> struct FmtT<FMT_INT4_GEN>  { static constexpr int LANE_B = 4,  LANE_W = 8,  UNIT_W = 128; static constexpr bool INT4 = true; };
+template <> struct FmtT<FMT_BF16_FAST> { static constexpr int LANE_B = 16, LANE_W = 8,  UNIT_W = 128; static constexpr bool INT4 = false; };
+template <> struct FmtT<FMT_BF16_GEN>  { static constexpr int LANE_B = 4,  LANE_W = 2,  UNIT_W = 32;  static constexpr bool INT4 = false; };
+
+// ---------------------------------------------------------------- LDS footprint of a staged activation
+// int4: PREC planes of fp16 pairs [NB][K/2] (4 B each; plane 0 the fp16 value,
+// plane 1 the fp16 of the remainder) + corrections [NB][K/LANE_W] fp32.
+// bf16: fp32 [NB][K].
+template <int FMT, int NB, int PREC>
+__host__ __device__ constexpr int act_lds_bytes(int K) {
+    return FmtT<FMT>::INT4 ? NB * (PREC * K * 2 + (K / FmtT<FMT>::LANE_W) * 4) : NB * K * 4;
+}
+
+// ---------------------------------------------------------------- pair -> rows
+struct RowPtrs { const uint8_t* pa; const uint8_t* pb; const uint16_t* sa; const uint16_t* sb; };
+
+template <int FMT>
+I4D_DEVINL RowPtrs resolve_pair(const GemvTask& t, int pair) {
+    // select by value (no pointer to a member of the kernel argument, which
+    // would push the task into scratch memory)
+    const uint8_t* da = t.a.data; const uint16_t* sa = t.a.scales; int ga = t.a.ngroups;
+    const uint8_t* db; const uint16_t* sb; int gb;
+    int ra, rb;
+    if (t.kind == KIND_ADJ) {
+        ra = 2 * pair;
+        rb = min(2 * pair + 1, t.a.n - 1);
+        db = da; sb = sa; gb = ga;
+    } else if (t.kind == KIND_TWO) {
+        ra = pair; rb = pair;
+        db = t.b.data; sb = t.b.scales; gb = t.b.ngroups;
+    } else {
+        const int half = t.head_dim >> 1;
+        const int npq = t.a.n >> 1, npk = t.b.n >> 1;
+        int lp = pair;
+        if (lp >= npq) {
+            lp -= npq;
+            if (lp >= npk) { lp -= npk; da = t.c.data; sa = t.c.scales; ga = t.c.ngroups; }
+            else { da = t.b.data; sa = t.b.scales; ga = t.b.ngroups; }
+        }
+        const int head = lp / half, i = lp - head * half;
+        ra = head * t.head_dim + i;
+        rb = ra + half;
+        db = da; sb = sa; gb = ga;
+    }
+    const size_t row_bytes = FmtT<FMT>::INT4 ? (size_t)(t.k >> 1) : (size_t)t.k * 2;
+    RowPtrs r;
+    r.pa = da + (size_t)ra * row_bytes;
+    r.pb = db + (size_t)rb * row_bytes;
+    r.sa = FmtT<FMT>::INT4 ? sa + (size_t)ra * ga : nullptr;
+    r.sb = FmtT<FMT>::INT4 ? sb + (size_t)rb * gb : nullptr;
+    return r;
+}
+
+// ---------------------------------------------------------------- one buffered unit
+// The registers of one unit are only written by loads: nothing is computed
+// from them until the unit is consumed, so a load never forces a wait on
+// itself and D units stay in flight.
+template <int FMT> struct Unit;
+template <> struct Unit<FMT_INT4_FAST> { u32x4 a, b; u32 sa, sb; };
+template <> struct Unit<FMT_INT4_GEN>  { u32 a, b; u32 sa, sb; };
+template <> struct Unit<FMT_BF16_FAST> { u32x4 a, b; };
+template <> struct Unit<FMT_BF16_GEN>  { u32 a, b; };
+
+template <class T> I4D_DEVINL T nt_load(const T* p) { return __builtin_nontemporal_load(p); }
+
+// Issue the loads of one unit.  `valid` = the unit exists; otherwise the
+// loads read a fixed in-bounds address (the first bytes of the task's first
+// matrix, cached after the first touch) and the unit is never consumed.  The
+// loads are unconditional so the compiler can count them exactly.
+template <int FMT>
+I4D_DEVINL void load_unit(Unit<FMT>& u, const RowPtrs& rp, int seg, int lane16, int K, int log2g, int group,
+                          bool valid, const uint8_t* dummy, const uint16_t* dummy_s) {
+    typedef FmtT<FMT> F;
+    int k0 = seg * F::UNIT_W + lane16 * F::LANE_W;          // first input of this lane's load
+    if constexpr (FMT == FMT_INT4_GEN || FMT == FMT_BF16_GEN) valid = valid && (k0 < K);
+    if constexpr (F::INT4) {
+        const size_t off = (size_t)(k0 >> 1);
+        const int gi = (FMT == FMT_INT4_FAST) ? (k0 >> log2g) : (k0 / group);
+        const uint8_t* pa = valid ? rp.pa + off : dummy;
+        const uint8_t* pb = valid ? rp.pb + off : dummy;
+        const uint16_t* qa = valid ? rp.sa + gi : dummy_s;
+        const uint16_t* qb = valid ? rp.sb + gi : dummy_s;
+        if constexpr (FMT == FMT_INT4_FAST) {
+            u.a = nt_load((const u32x4*)pa);
+            u.b = nt_load((const u32x4*)pb);
+        } else {
+            u.a = nt_load((const u32*)pa);
+            u.b = nt_load((const u32*)pb);
+        }
+        u.sa = *qa;
+        u.sb = *qb;
+    } else {
+        const size_t off = (size_t)k0 * 2;
+        const uint8_t* pa = valid ? rp.pa + off : dummy;
+        const uint8_t* pb = valid ? rp.pb + off : dummy;
+        if constexpr (FMT == FMT_BF16_FAST) {
+            u.a = nt_load((const u32x4*)pa);
+            u.b = nt_load((const u32x4*)pb);
+        } else {
+            u.a = nt_load((const u32*)pa);
+            u.b = nt_load((const u32*)pb);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dot products of one unit
+I4D_DEVINL h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
+
+// acc + sum over one dword of 8 codes, with act[4] the staged fp16 pairs.
+I4D_DEVINL float dot8_int4(u32 w, const h2* act, float acc) {
+    const u32 w8 = w >> 8;
+    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) | 0x64006400u), act[0], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) | 0x64006400u), act[1], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) | 0x64006400u), act[2], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) | 0x64006400u), act[3], acc, false);
+    return acc;
+}
+
+template <int FMT, int NB, int PREC>
+I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int seg, int lane16,
+                             float (&ra)[NB], float (&rb)[NB]) {
+    typedef FmtT<FMT> F;
+    if constexpr (F::INT4) {
+        const int nchunk = K / F::LANE_W;
+        int c = seg * 16 + lane16;                      // lane chunk index along K
+        if (FMT == FMT_INT4_GEN) c = min(c, nchunk - 1);  // masked lanes read a valid chunk, scale 0
+        const float* corr = (const float*)(act_lds + NB * PREC * K * 2);
+        // generic path: lanes past the end of K contribute nothing
+        const bool live = (FMT == FMT_INT4_FAST) || (seg * F::UNIT_W + lane16 * F::LANE_W < K);
+        const float sa = live ? bf16_to_f32((uint16_t)u.sa) : 0.f;
+        const float sb = live ? bf16_to_f32((uint16_t)u.sb) : 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float cr = corr[b * nchunk + c];
+            float acca = -cr, accb = -cr;
+#pragma unroll
+            for (int pl = 0; pl < PREC; ++pl) {
+                const h2* act = (const h2*)act_lds + (size_t)(pl * NB + b) * (K >> 1);
+                if constexpr (FMT == FMT_INT4_FAST) {
+                    const u32x4* ap = (const u32x4*)(act + c * 16);
+                    u32x4 x0 = ap[0], x1 = ap[1], x2 = ap[2], x3 = ap[3];
+                    h2 xa[16] = {as_h2(x0.x), as_h2(x0.y), as_h2(x0.z), as_h2(x0.w), as_h2(x1.x), as_h2(x1.y), as_h2(x1.z), as_h2(x1.w),
+                                 as_h2(x2.x), as_h2(x2.y), as_h2(x2.z), as_h2(x2.w), as_h2(x3.x), as_h2(x3.y), as_h2(x3.z), as_h2(x3.w)};
+                    acca = dot8_int4(u.a.x, xa + 0, acca);  accb = dot8_int4(u.b.x, xa + 0, accb);
+                    acca = dot8_int4(u.a.y, xa + 4, acca);  accb = dot8_int4(u.b.y, xa + 4, accb);
+                    acca = dot8_int4(u.a.z, xa + 8, acca);  accb = dot8_int4(u.b.z, xa + 8, accb);
+                    acca = dot8_int4(u.a.w, xa + 12, acca); accb = dot8_int4(u.b.w, xa + 12, accb);
+                } else {
+                    const u32x4 x0 = *(const u32x4*)(act + c * 4);
+                    h2 xa[4] = {as_h2(x0.x), as_h2(x0.y), as_h2(x0.z), as_h2(x0.w)};
+                    acca = dot8_int4(u.a, xa, acca);
+                    accb = dot8_int4(u.b, xa, accb);
+                }
+            }
+            ra[b] = fmaf(sa, acca, ra[b]);
+            rb[b] = fmaf(sb, accb, rb[b]);
+        }
+    } else {
+        const float* act = (const float*)act_lds;
+        int k0 = seg * F::UNIT_W + lane16 * F::LANE_W;
+        const bool live = (FMT == FMT_BF16_FAST) || (k0 < K);
+        if (FMT == FMT_BF16_GEN) k0 = min(k0, K - 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float* xp = act + (size_t)b * K + k0;
+            float acca = 0.f, accb = 0.f;
+            if constexpr (FMT == FMT_BF16_FAST) {
+                const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
+                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                const u32 wa[4] = {u.a.x, u.a.y, u.a.z, u.a.w};
+                const u32 wb[4] = {u.b.x, u.b.y, u.b.z, u.b.w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    acca = fmaf(__uint_as_float(wa[d] << 16), xv[2 * d], acca);
+                    acca = fmaf(__uint_as_float(wa[d] & 0xFFFF0000u), xv[2 * d + 1], acca);
+                    accb = fmaf(__uint_as_float(wb[d] << 16), xv[2 * d], accb);
+                    accb = fmaf(__uint_as_float(wb[d] & 0xFFFF0000u), xv[2 * d + 1], accb);
+                }
+            } else {
+                acca = fmaf(__uint_as_float(u.a << 16), xp[0], __uint_as_float(u.a & 0xFFFF0000u) * xp[1]);
+                accb = fmaf(__uint_as_float(u.b << 16), xp[0], __uint_as_float(u.b & 0xFFFF0000u) * xp[1]);
+            }
+            ra[b] += live ? acca : 0.f;
+            rb[b] += live ? accb : 0.f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- activation staging
+// Stage nb rows of `src` (fp32, row stride src_stride, K inputs) into LDS for
+// NB batch slots (missing rows are zeros), optionally RMS-normalised with a bf16
+// gain: h = x / sqrt(mean(x^2) + eps) * gain.
+//
+// Staging is split in two so that its global loads are issued before the
+// weight loads (the vector-memory counter is in order: a wait for a load also
+// waits for every load issued before it).  stage_issue() loads the first
+// PRE_CHUNKS chunks of each thread into registers; stage_finish() does the
+// rest.  `red` is NT/64*NB floats of LDS.
+constexpr int PRE_CHUNKS = 2;
+
+template <int FMT>
+struct StagePre {
+    static constexpr int NV = FmtT<FMT>::INT4 ? FmtT<FMT>::LANE_W / 4 : 2;   // float4 loads per chunk
+    f4 x[PRE_CHUNKS][NV];
+    u32x4 g[PRE_CHUNKS][FmtT<FMT>::INT4 ? NV / 2 : 1];
+};
+
+// chunk geometry: int4 chunks are LANE_W inputs; bf16 chunks are 8 inputs
+template <int FMT> I4D_DEVINL int stage_chunk_w() { return FmtT<FMT>::INT4 ? FmtT<FMT>::LANE_W : 8; }
+
+template <int FMT, int NB, int NT>
+I4D_DEVINL void stage_load_chunk(f4 (&xv)[StagePre<FMT>::NV], u32x4 (&gv)[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1],
+                                 const float* src, int src_stride, int K, int nb, const uint16_t* gain, int idx) {
+    constexpr int NV = StagePre<FMT>::NV;
+    const int cw = stage_chunk_w<FMT>();
+    const int nchunk = K / cw;
+    const int b = idx / nchunk, c = idx - b * nchunk;
+    const int k0 = c * cw;
+    const f4* xp = (const f4*)(src + (size_t)min(b, nb - 1) * src_stride + k0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) xv[i] = xp[i];
+    if (gain != nullptr) {
+        constexpr int NG = FmtT<FMT>::INT4 ? NV / 2 : 1;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) gv[i] = ((const u32x4*)(gain + k0))[i];
+    }
+}
+
+template <int FMT, int NB, int NT>
+I4D_DEVINL void stage_issue(StagePre<FMT>& pre, const float* src, int src_stride, int K, int nb, const uint16_t* gain) {
+    const int nidx = NB * (K / stage_chunk_w<FMT>());
+#pragma unroll
+    for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+        const int idx = min((int)threadIdx.x + pc * NT, nidx - 1);     // clamped: loads are unconditional
+        stage_load_chunk<FMT, NB, NT>(pre.x[pc], pre.g[pc], src, src_stride, K, nb, gain, idx);
+    }
+}
+
+// Write one chunk (already in registers) to LDS.
+template <int FMT, int NB, int PREC>
+I4D_DEVINL void stage_write_chunk(char* act_lds, const f4 (&xv)[StagePre<FMT>::NV],
+                                  const u32x4 (&gv)[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1],
+                                  int K, int nb, bool has_gain, const float (&rs)[NB], int idx) {
+    typedef FmtT<FMT> F;
+    const int cw = stage_chunk_w<FMT>();
+    const int nchunk = K / cw;
+    const int b = idx / nchunk, c = idx - b * nchunk;
+    const int k0 = c * cw;
+    float scale = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) if (bb == b && b < nb) scale = rs[bb];
+    if constexpr (F::INT4) {
+        h2* act = (h2*)act_lds;
+        float* corr = (float*)(act_lds + NB * PREC * K * 2);
+        double ce = 0.0;
+#pragma unroll
+        for (int d = 0; d < F::LANE_W / 8; ++d) {
+            // a[e]: staged value (odd positions pre-divided by 16, exact);
+            // hi = fp16(a), lo = fp16(a - hi) when two planes are used
+            _Float16 hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = d * 8 + e;
+                float v = xv[q >> 2][q & 3] * scale;
+                if (has_gain) {
+                    const u32 gw = gv[q >> 3][(q >> 1) & 3];
+                    v *= __uint_as_float((q & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+                }
+                const float a = (e & 1) ? v * 0.0625f : v;
+                hi[e] = (_Float16)a;
+                lo[e] = (_Float16)(a - (float)hi[e]);
+                const double w = (e & 1) ? 1152.0 : 1032.0;
+                ce += w * ((double)hi[e] + (PREC > 1 ? (double)lo[e] : 0.0));
+            }
+            h2* dst = act + (size_t)b * (K >> 1) + (size_t)((k0 >> 1) + 4 * d);
+            dst[0] = h2{hi[0], hi[4]};
+            dst[1] = h2{hi[1], hi[5]};
+            dst[2] = h2{hi[2], hi[6]};
+            dst[3] = h2{hi[3], hi[7]};
+            if (PREC > 1) {
+                h2* dl = dst + (size_t)NB * (K >> 1);
+                dl[0] = h2{lo[0], lo[4]};
+                dl[1] = h2{lo[1], lo[5]};
+                dl[2] = h2{lo[2], lo[6]};
+                dl[3] = h2{lo[3], lo[7]};
+            }
+        }
+        corr[b * nchunk + c] = (float)ce;
+    } else {
+        float* act = (float*)act_lds + (size_t)b * K + k0;
+        const u32x4 gw = gv[0];
+        const u32 gws[4] = {gw.x, gw.y, gw.z, gw.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            float v = xv[q >> 2][q & 3] * scale;
+            if (has_gain) v *= __uint_as_float((q & 1) ? (gws[q >> 1] & 0xFFFF0000u) : (gws[q >> 1] << 16));
+            act[q] = v;
+        }
+    }
+}
+
+template <int FMT, int NB, int NT, int PREC>
+__device__ void stage_finish(const StagePre<FMT>& pre, char* act_lds, const float* src, int src_stride, int K, int nb,
+                             const uint16_t* gain, float eps, float* red) {
+    const int tid = threadIdx.x;
+    const int nidx = NB * (K / stage_chunk_w<FMT>());
+    float rs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rs[b] = 1.0f;
+    if (gain != nullptr) {
+        // sum of squares per batch row: prefetched chunks from registers, the rest from memory
+        float ss[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+        const int nchunk = K / stage_chunk_w<FMT>();
+#pragma unroll
+        for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+            const int idx = tid + pc * NT;
+            if (idx < nidx) {
+                f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < StagePre<FMT>::NV; ++i) acc += pre.x[pc][i] * pre.x[pc][i];
+                const float v = (acc.x + acc.y) + (acc.z + acc.w);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) if (b == idx / nchunk) ss[b] += v;
+            }
+        }
+        for (int idx = tid + PRE_CHUNKS * NT; idx < nidx; idx += NT) {
+            f4 xv[StagePre<FMT>::NV];
+            u32x4 gv[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1];
+            stage_load_chunk<FMT, NB, NT>(xv, gv, src, src_stride, K, nb, nullptr, idx);
+            f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < StagePre<FMT>::NV; ++i) acc += xv[i] * xv[i];
+            const float v = (acc.x + acc.y) + (acc.z + acc.w);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) if (b == idx / nchunk) ss[b] += v;
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            for (int m = 32; m >= 1; m >>= 1) ss[b] += shfl_xor_f(ss[b], m);
+        const int wave = tid >> 6;
+        if ((tid & 63) == 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) red[wave * NB + b] = ss[b];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = 0.f;
+            for (int w = 0; w < NT / 64; ++w) t += red[w * NB + b];
+            rs[b] = 1.0f / sqrtf(t / (float)K + eps);
+        }
+        __syncthreads();   // red may be reused by the caller
+    }
+#pragma unroll
+    for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+        const int idx = tid + pc * NT;
+        if (idx < nidx) stage_write_chunk<FMT, NB, PREC>(act_lds, pre.x[pc], pre.g[pc], K, nb, gain != nullptr, rs, idx);
+    }
+    for (int idx = tid + PRE_CHUNKS * NT; idx < nidx; idx += NT) {
+        f4 xv[StagePre<FMT>::NV];
+        u32x4 gv[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1];
+        stage_load_chunk<FMT, NB, NT>(xv, gv, src, src_stride, K, nb, gain, idx);
+        stage_write_chunk<FMT, NB, PREC>(act_lds, xv, gv, K, nb, gain != nullptr, rs, idx);
+    }
+}
+
+// ---------------------------------------------------------------- schedule arithmetic
+// Pairs of pass p owned by workgroup w (32-bit: pairs * workgroups < 2^31).
+I4D_DEVINL void pass_pairs_of(const GemvTask& t, int pass, int w, int nwg, int& q0, int& q1) {
+    const int pb = pass * t.pass_pairs;
+    const int np = min(t.total_pairs, pb + t.pass_pairs) - pb;
+    q0 = pb + (w * np) / nwg;
+    q1 = pb + ((w + 1) * np) / nwg;
+}
+
+// Unit range of 16-lane slot s (wave s/4, slot s%4) among U units of a workgroup;
+// n_it = iterations every slot of that wave runs (the longest slot's count).
+template <int NW>
+I4D_DEVINL void slot_range(int U, int s, int& u0, int& u1, int& n_it) {
+    const int w = s >> 2, t = s & 3;
+    const int wu0 = (w * U) / NW, wu1 = ((w + 1) * U) / NW;
+    const int n = wu1 - wu0;
+    u0 = wu0 + (t * n) / 4;
+    u1 = wu0 + ((t + 1) * n) / 4;
+    n_it = (n + 3) / 4;
+}
+
+// Per-lane position of the loader inside one pass.
+struct LoadCursor {
+    int u, u1;         // next unit to load, end of the slot's range
+    int pair, seg;     // of unit u
+    RowPtrs rp;
+};
+
+template <int FMT>
+I4D_DEVINL void cursor_begin(LoadCursor& lc, const GemvTask& t, int q0, int u0, int u1, int S) {
+    lc.u = u0; lc.u1 = u1;
+    const int ql = u0 / S;
+    lc.pair = q0 + ql;
+    lc.seg = u0 - ql * S;
+    lc.rp = resolve_pair<FMT>(t, u0 < u1 ? lc.pair : 0);
+}
+
+// Load the slot's next unit into dst (if any) and advance.
+template <int FMT>
+I4D_DEVINL void cursor_load(LoadCursor& lc, Unit<FMT>& dst, const GemvTask& t, int S, int lane16) {
+    const bool valid = lc.u < lc.u1;
+    load_unit<FMT>(dst, lc.rp, lc.seg, lane16, t.k, t.log2_group, t.a.group, valid, t.a.data, t.a.scales);
+    if (valid) {
+        ++lc.u;
+        if (++lc.seg == S) {
+            lc.seg = 0;
+            ++lc.pair;
+            if (lc.u < lc.u1) lc.rp = resolve_pair<FMT>(t, lc.pair);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- the pass loop
+// Run every pass of task `t` for workgroup w.  The activations are staged once:
+//   stage.issue(pre), stage.finish(pre) -- see stage_issue / stage_finish
+// and for each pass:
+//   epi(pass, pair, b, va, vb)   -- per (pair, batch slot) results, pair in [q0, q1)
+//   epi.end_pass(pass, q0, q1)   -- after all epilogue calls of the pass
+// Each lane keeps D units in flight; the first D units of the next pass are
+// issued before the current pass's reduction and epilogue.
+// LDS: act_lds (staged activations), part_lds (NS*MAXJ*NB*2 floats + 2*NS ints).
+template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Stage, class Epi>
+__device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
+    constexpr int NW = NT / 64, NS = NT / 16;
+    typedef FmtT<FMT> F;
+    const int tid = threadIdx.x;
+    const int slot = tid >> 4, lane16 = tid & 15;
+    const int S = (t.k + F::UNIT_W - 1) / F::UNIT_W;
+    int* slot_info = (int*)(part_lds + NS * MAXJ * NB * 2);     // [NS][2]: first local pair, runs
+
+    StagePre<FMT> pre;
+    stage.issue(pre);                    // activation loads first ...
+
+    Unit<FMT> ring[D];
+    LoadCursor lc;
+    int q0, q1, u0, u1, n_it;
+    pass_pairs_of(t, 0, w, nwg, q0, q1);
+    slot_range<NW>((q1 - q0) * S, slot, u0, u1, n_it);
+    cursor_begin<FMT>(lc, t, q0, u0, u1, S);
+#pragma unroll
+    for (int i = 0; i < D; ++i) cursor_load<FMT>(lc, ring[i], t, S, lane16);   // ... then the weight ring
+
+    stage.finish(pre);                   // waits only for the activation loads
+    __syncthreads();
+
+    for (int pass = 0; pass < t.npasses; ++pass) {
+        const int n_itp = ((n_it + D - 1) / D) * D;
+
+        float ra[NB], rb[NB], da[MAXJ][NB], db[MAXJ][NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { ra[b] = 0.f; rb[b] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < MAXJ; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) { da[j][b] = 0.f; db[j][b] = 0.f; }
+        int run = 0;
+        const int first_local = u0 / S;
+        int seg = u0 - first_local * S;
+        int u = u0;
+
+        for (int itb = 0; itb < n_itp; itb += D) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                if (u < u1) {
+                    consume_unit<FMT, NB, PREC>(ring[i], act_lds, t.k, seg, lane16, ra, rb);
+                    ++u;
+                    if (++seg == S) {   // this pair's run is complete: park it
+                        seg = 0;
+#pragma unroll
+                        for (int j = 0; j < MAXJ; ++j)
+                            if (j == run)
+#pragma unroll
+                                for (int b = 0; b < NB; ++b) { da[j][b] = ra[b]; db[j][b] = rb[b]; }
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) { ra[b] = 0.f; rb[b] = 0.f; }
+                        ++run;
+                    }
+                }
+                cursor_load<FMT>(lc, ring[i], t, S, lane16);
+            }
+        }
+        if (seg != 0) {      // a partially covered last pair
+#pragma unroll
+            for (int j = 0; j < MAXJ; ++j)
+                if (j == run)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) { da[j][b] = ra[b]; db[j][b] = rb[b]; }
+            ++run;
+        }
+        const int this_q0 = q0, this_q1 = q1;
+        // next pass: geometry, and its first D units in flight during this epilogue
+        if (pass + 1 < t.npasses) {
+            pass_pairs_of(t, pass + 1, w, nwg, q0, q1);
+            slot_range<NW>((q1 - q0) * S, slot, u0, u1, n_it);
+            cursor_begin<FMT>(lc, t, q0, u0, u1, S);
+#pragma unroll
+            for (int i = 0; i < D; ++i) cursor_load<FMT>(lc, ring[i], t, S, lane16);
+        }
+        // 16-lane sums of every run, written by lane 0 of the slot
+#pragma unroll
+        for (int j = 0; j < MAXJ; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float sa = row16_sum(da[j][b]);
+                const float sb = row16_sum(db[j][b]);
+                if (lane16 == 0 && j < run) {
+                    float* p = part_lds + ((slot * MAXJ + j) * NB + b) * 2;
+                    p[0] = sa; p[1] = sb;
+                }
+            }
+        if (lane16 == 0) { slot_info[2 * slot] = first_local; slot_info[2 * slot + 1] = min(run, MAXJ); }
+        __syncthreads();
+        // per-pair totals: 32 lanes per (pair, batch slot), lane i reading the
+        // slots i, i+32, ..; a fixed shuffle tree sums them (deterministic)
+        const int npairs = this_q1 - this_q0;
+        const int grp = tid >> 5, l32 = tid & 31;
+        for (int base = 0; base < npairs * NB; base += NT / 32) {
+            const int idx = base + grp;
+            const int ql = idx / NB, b = idx - ql * NB;
+            float va = 0.f, vb = 0.f;
+            if (idx < npairs * NB) {
+                for (int s2 = l32; s2 < NS; s2 += 32) {
+                    const int j = ql - slot_info[2 * s2];
+                    if (j >= 0 && j < slot_info[2 * s2 + 1]) {
+                        const float* p = part_lds + ((s2 * MAXJ + j) * NB + b) * 2;
+                        va += p[0]; vb += p[1];
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) { va += shfl_xor_f(va, m); vb += shfl_xor_f(vb, m); }
+            if (l32 == 0 && idx < npairs * NB) epi(pass, this_q0 + ql, b, va, vb);
+        }
+        epi.end_pass(pass, this_q0, this_q1);
+        __syncthreads();
+    }
+}
+
+// Largest number of runs any slot can see in a pass of `pairs_per_wg` pairs
+// with S units per pair (host-side sizing of passes).
+__host__ inline int gemv_max_runs(int pairs_per_wg, int S, int nw) {
+    const long long U = (long long)pairs_per_wg * S;
+    const long long wave_units = (U + nw - 1) / nw;
+    const long long slot_units = (wave_units + 3) / 4;
+    return (int)((slot_units + S - 1) / S) + 1;
+}

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, and rejects bad arguments before enqueuing any GPU work.
+
+No call here reaches a HIP API (validation happens first), so these run on a
+machine without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from int4_weight_streaming_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i4decode.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(i4d_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libi4decode.so not built: run __graft_entry__.build()")
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert B.status_string(code)
+    assert B.status_string(-99) == "unknown status"
+
+
+def _cfg(**kw):
+    base = dict(d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ff=688, rms_eps=1e-6, rope_base=1e4)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def test_workspace_size_is_pure_and_validates(lib):
+    assert B.workspace_size(_cfg(), 1, 127) > 0
+    assert B.workspace_size(_cfg(), 8, 32767) > B.workspace_size(_cfg(), 1, 32767)
+    assert B.workspace_size(_cfg(head_dim=96), 1, 127) == 0          # unsupported head_dim
+    assert B.workspace_size(_cfg(n_q_heads=6, n_kv_heads=4), 1, 127) == 0  # Hq % Hkv != 0
+    assert B.workspace_size(_cfg(), 9, 127) == 0                     # batch > 8
+    assert B.workspace_size(_cfg(), 0, 127) == 0
+
+
+class _FakeDev:
+    """An address stand-in: validation never dereferences pointers."""
+
+    def __init__(self, addr, nbytes=1 << 30):
+        self.addr, self.n = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def _mat(n, k, group=64, addr=0x10000, dtype=B.WEIGHT_INT4):
+    return B.I4dMat(addr, addr + 0x8000000, n, k, group, dtype)
+
+
+def _layer(cfg, group=64, **override):
+    D, qw, kvw, F = cfg.d_model, cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.d_ff
+    mats = {"wq": _mat(qw, D, group), "wk": _mat(kvw, D, group), "wv": _mat(kvw, D, group),
+            "wo": _mat(D, qw, group), "wg": _mat(F, D, group), "wu": _mat(F, D, group), "wd": _mat(D, F, group)}
+    mats.update(override)
+    return B.I4dLayer(0x20000, mats["wq"], mats["wk"], mats["wv"], mats["wo"], 0x30000, mats["wg"], mats["wu"], mats["wd"])
+
+
+def _call_layer(cfg, layer, batch=1, x_in=0x100000, x_out=0x200000, cap=256, max_pos=127, ws=0x400000, ws_bytes=1 << 30):
+    kv = B.I4dKv(0x500000, 0x600000, cap)
+    return B.lib().i4d_decode_layer(ctypes.byref(cfg), ctypes.byref(layer), batch, ctypes.c_void_p(x_in),
+                                    ctypes.c_void_p(x_out), ctypes.byref(kv), ctypes.c_void_p(0x700000), max_pos,
+                                    ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_decode_layer_argument_validation(lib):
+    cfg = _cfg()
+    L = _layer(cfg)
+    assert lib.i4d_decode_layer(None, ctypes.byref(L), 1, None, None, None, None, 0, None, 0, None) == B.I4D_EINVAL
+    assert _call_layer(cfg, L, batch=0) == B.I4D_ERANGE
+    assert _call_layer(cfg, L, batch=9) == B.I4D_ERANGE
+    assert _call_layer(cfg, L, x_out=0x100000) == B.I4D_EINVAL           # x_out aliases x_in
+    assert _call_layer(cfg, L, x_in=0x100004) == B.I4D_EALIGN
+    assert _call_layer(cfg, L, max_pos=256) == B.I4D_ERANGE                # max_pos >= capacity
+    assert _call_layer(cfg, L, cap=250) == B.I4D_EINVAL                    # capacity % 8 != 0
+    assert _call_layer(cfg, L, ws_bytes=100) == B.I4D_EWORKSPACE
+    assert _call_layer(cfg, L, ws=0x400010) == B.I4D_EALIGN
+    assert _call_layer(cfg, _layer(cfg, wq=_mat(255, 256))) == B.I4D_EINVAL   # wrong row count
+    assert _call_layer(cfg, _layer(cfg, wo=_mat(256, 256, addr=0x10008))) == B.I4D_EALIGN
+    assert _call_layer(cfg, _layer(cfg, group=12)) == B.I4D_EINVAL             # group % 8 != 0
+    assert _call_layer(_cfg(head_dim=80), L) == B.I4D_EINVAL
+    mixed = _layer(cfg, wd=_mat(256, 688, dtype=B.WEIGHT_BF16))
+    assert _call_layer(cfg, mixed) == B.I4D_EINVAL
+
+
+def test_lm_head_and_gemv_validation(lib):
+    w = _mat(1000, 256)
+    h = ctypes.c_void_p(0x100000)
+    out = ctypes.c_void_p(0x200000)
+    ws = ctypes.c_void_p(0x400000)
+    assert lib.i4d_lm_head_chunked(ctypes.byref(w), 1, h, 0, out, out, ws, 1 << 20, None) == B.I4D_ERANGE
+    assert lib.i4d_lm_head_chunked(ctypes.byref(w), 0, h, 64, out, out, ws, 1 << 20, None) == B.I4D_ERANGE
+    assert lib.i4d_lm_head_chunked(ctypes.byref(w), 1, h, 64, out, out, ws, 16, None) == B.I4D_EWORKSPACE
+    wb = _mat(1000, 256, dtype=B.WEIGHT_BF16)
+    assert lib.i4d_lm_head_chunked(ctypes.byref(wb), 1, h, 64, out, out, ws, 1 << 20, None) == B.I4D_EINVAL
+    assert lib.i4d_gemv(ctypes.byref(_mat(10, 12)), 1, h, out, None, 0, None) == B.I4D_EINVAL   # k % 8 != 0
+    assert lib.i4d_gemv(ctypes.byref(w), 9, h, out, None, 0, None) == B.I4D_ERANGE
+    assert lib.i4d_dequant_int4(None, out, None) == B.I4D_EINVAL
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(B.I4DError) as e:
+        B._check(B.I4D_EALIGN, "x")
+    assert e.value.code == B.I4D_EALIGN

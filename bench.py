@@ -135,7 +135,7 @@ def main():
     pos = torch.full((batch,), shape.kv_len, dtype=torch.int32, device="cuda")
     cfg = B.make_config(shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
                         shape.rms_eps, shape.rope_base, args.exec_mode)
-    ws = torch.zeros(B.workspace_size(cfg, batch, cap - 1, shape.vocab), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(B.workspace_size(cfg, shape.n_layers, batch, cap - 1, shape.vocab), dtype=torch.uint8, device="cuda")
     B.workspace_init(ws)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen

@@ -62,7 +62,7 @@ extern "C" {
 #define I4D_EUNSUPPORTED -6   /* valid request this build does not implement */
 
 /* smallest workspace any entry point accepts (header + LM-head argmax keys) */
-#define I4D_WS_MIN_BYTES (512 + 4096 * 8 * 8)
+#define I4D_WS_MIN_BYTES (8192 + 4096 * 8 * 8)
 
 /* device status word bits (i4d_read_device_status) */
 #define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
@@ -121,9 +121,10 @@ typedef struct i4d_kv {
     int32_t capacity;
 } i4d_kv;
 
-/* Bytes of workspace needed for this shape, batch, largest position and
- * vocabulary (0 if no LM head is used).  Pure host arithmetic.              */
-size_t i4d_workspace_size(const i4d_config* cfg, int32_t batch, int32_t max_pos, int32_t vocab);
+/* Bytes of workspace needed to run up to n_layers layers per call for this
+ * shape, batch, largest position and vocabulary (0 if no LM head is used).
+ * Pure host arithmetic; 0 for invalid arguments.                            */
+size_t i4d_workspace_size(const i4d_config* cfg, int32_t n_layers, int32_t batch, int32_t max_pos, int32_t vocab);
 
 /* Zero a fresh workspace, status word included (a fill kernel, no
  * hipMemset).  Needed once per workspace.                                   */

@@ -20,7 +20,7 @@ I4D_EWORKSPACE = -3
 I4D_ERANGE = -4
 I4D_EHIP = -5
 I4D_EUNSUPPORTED = -6
-WS_MIN_BYTES = 512 + 4096 * 8 * 8     # I4D_WS_MIN_BYTES
+WS_MIN_BYTES = 8192 + 4096 * 8 * 8    # I4D_WS_MIN_BYTES
 I4D_DEV_BAD_POS = 1
 I4D_DEV_BARRIER_TIMEOUT = 2
 
@@ -69,7 +69,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() (hipcc for gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        L.i4d_workspace_size.argtypes = [ctypes.POINTER(I4dConfig), I, I, I]
+        L.i4d_workspace_size.argtypes = [ctypes.POINTER(I4dConfig), I, I, I, I]
         L.i4d_workspace_size.restype = Z
         L.i4d_workspace_init.argtypes = [P, Z, P]
         L.i4d_decode_layer.argtypes = [ctypes.POINTER(I4dConfig), ctypes.POINTER(I4dLayer), I, P, P,
@@ -133,8 +133,8 @@ def make_kv(k_cache, v_cache, capacity) -> I4dKv:
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)
 
-def workspace_size(cfg: I4dConfig, batch: int, max_pos: int, vocab: int = 0) -> int:
-    return int(lib().i4d_workspace_size(ctypes.byref(cfg), batch, max_pos, vocab))
+def workspace_size(cfg: I4dConfig, n_layers: int, batch: int, max_pos: int, vocab: int = 0) -> int:
+    return int(lib().i4d_workspace_size(ctypes.byref(cfg), n_layers, batch, max_pos, vocab))
 
 
 def workspace_init(ws, stream=None):

@@ -59,7 +59,7 @@ I4D_DEVINL int keys_of(const AttnArgs& a, int b) {
 
 // LDS bytes used by attn_item with NT threads.
 template <int HD, int NT>
-__host__ __device__ constexpr int attn_lds_bytes() { return (NT / 64) * (16 * HD + 32) * 4 + 16; }
+__host__ __device__ constexpr int attn_lds_bytes() { return (NT / 64) * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8; }
 
 template <int HD, int NT>
 __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
@@ -75,14 +75,16 @@ __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
     const int t_e = min(t_s + a.T, nk);
     const int nsub = (t_e > t_s) ? (t_e - t_s + 15) / 16 : 0;
 
-    // q^T operand (hi, lo) for head r of this group, dims DPL*g + 4kb + i
-    // (vector loads from a clamped head, then zeroed for padding heads r >= G)
-    s4 qh[NKB], ql[NKB];
-    {
+    // q^T operand (hi, lo) for head r of this group, dims DPL*g + 4kb + i, kept
+    // in LDS (every wave of the workgroup uses the same operands): [kb][lane]
+    // s4 pairs after the per-wave areas.  Vector loads from a clamped head,
+    // zeroed for padding heads r >= G.
+    s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
+    if (wave == 0) {
         const f4* qp = (const f4*)(a.q + ((size_t)(b * a.hq + j * G + min(r, G - 1)) * HD) + DPL * g);
         f4 qv[NKB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qv[kb] = qp[kb];
+        for (int kb = 0; kb < NKB; ++kb) qv[kb] = qp[kb];    // this layer's q, first read after it was written
         const float qs = (r < G) ? a.qscale : 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -93,10 +95,11 @@ __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
                 hv[i] = f32_to_bf16(v);
                 lv[i] = f32_to_bf16(v - bf16_to_f32(hv[i]));
             }
-            qh[kb] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-            ql[kb] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
+            qop[(2 * kb) * 64 + lane] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+            qop[(2 * kb + 1) * 64 + lane] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
         }
     }
+    __syncthreads();
 
     const uint16_t* kbase = a.kc + (size_t)(b * a.hkv + j) * a.cap * HD;
     const uint16_t* vbase = a.vc + (size_t)(b * a.hkv + j) * HD * a.cap;
@@ -133,8 +136,8 @@ __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
             u32x4 w = kr[kb >> 1];
             if (!kvalid) w = u32x4{0, 0, 0, 0};
             const s4 kop = (kb & 1) ? dwords_to_s4(w.z, w.w) : dwords_to_s4(w.x, w.y);
-            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qh[kb], sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, ql[kb], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb) * 64 + lane], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb + 1) * 64 + lane], sc, 0, 0, 0);
         }
         float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
 #pragma unroll
@@ -224,36 +227,45 @@ __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
             }
         }
         const size_t pidx = (hrow0 + h) * a.nsplit_max + s;
-        a.po[pidx * HD + d] = acc;
-        if (d == 0) { a.pm[pidx] = M; a.pl[pidx] = L; }
+        st_dev(a.po + pidx * HD + d, acc);
+        if (d == 0) { st_dev(a.pm + pidx, M); st_dev(a.pl + pidx, L); }
     }
     __syncthreads();       // the wave area of LDS is reused by the next item
 }
 
-// Merge the splits of one query head (b, h): o = sum_s w_s O_s / sum_s w_s l_s
-// with w_s = 2^(m_s - max m), in split order.  One workgroup of HD threads per
-// head; LDS: 2 * nsplit floats.
-template <int HD>
-__device__ void attn_merge_head(const AttnArgs& a, int bh, float* lds) {
-    const int tid = threadIdx.x;
+// Merge the splits of query heads: o = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = 2^(m_s - max m), in split order.  Each group of HD threads of the
+// workgroup merges head bh0 + group (if < nheads); every thread of the
+// workgroup must call this (it synchronises).  LDS: (NT/HD) * 2 * nsplit floats.
+template <int HD, int NT>
+__device__ void attn_merge_heads(const AttnArgs& a, int bh0, int nheads, float* lds) {
+    const int g = threadIdx.x / HD, lt = threadIdx.x - g * HD;
+    const int bh = bh0 + g;
+    const bool valid = (g < NT / HD) && (bh < nheads);
     const int ns = a.nsplit;
     const size_t prow = (size_t)bh * a.nsplit_max;
-    float* sm = lds;              // [ns] split maxima, then weights
-    float* sl = lds + ns;         // [ns] split sums
-    for (int ss = tid; ss < ns; ss += HD) { sm[ss] = a.pm[prow + ss]; sl[ss] = a.pl[prow + ss]; }
+    float* sm = lds + g * 2 * ns;      // split maxima, then weights
+    float* sl = sm + ns;               // split sums
+    if (valid)
+        for (int ss = lt; ss < ns; ss += HD) { sm[ss] = ld_dev(a.pm + prow + ss); sl[ss] = ld_dev(a.pl + prow + ss); }
     __syncthreads();
-    float M = -INFINITY;
-    for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, sm[ss]);
-    float L = 0.f;
-    if (M != -INFINITY)
-        for (int ss = 0; ss < ns; ++ss) L = fmaf(sl[ss], exp2f(sm[ss] - M), L);
+    float M = -INFINITY, L = 0.f;
+    if (valid) {
+        for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, sm[ss]);
+        if (M != -INFINITY)
+            for (int ss = 0; ss < ns; ++ss) L = fmaf(sl[ss], exp2f(sm[ss] - M), L);
+    }
     const float inv = (L > 0.f) ? 1.0f / L : 0.f;
     __syncthreads();
-    for (int ss = tid; ss < ns; ss += HD) sm[ss] = (M != -INFINITY) ? exp2f(sm[ss] - M) * inv : 0.f;
+    if (valid)
+        for (int ss = lt; ss < ns; ss += HD) sm[ss] = (M != -INFINITY) ? exp2f(sm[ss] - M) * inv : 0.f;
     __syncthreads();
-    const float* src = a.po + prow * HD + tid;
-    float acc = 0.f;
+    if (valid) {
+        const float* src = a.po + prow * HD + lt;
+        float acc = 0.f;
 #pragma unroll 16
-    for (int ss = 0; ss < ns; ++ss) acc = fmaf(sm[ss], src[(size_t)ss * HD], acc);
-    a.o[(size_t)bh * HD + tid] = acc;
+        for (int ss = 0; ss < ns; ++ss) acc = fmaf(sm[ss], ld_dev(src + (size_t)ss * HD), acc);
+        st_dev(a.o + (size_t)bh * HD + lt, acc);
+    }
+    __syncthreads();
 }

@@ -50,5 +50,27 @@ I4D_DEVINL float float_from_order_key(u32 k) {
 }
 I4D_DEVINL u64 argmax_key(float logit, u32 idx) { return ((u64)float_order_key(logit) << 32) | (u64)(0xFFFFFFFFu - idx); }
 
+// ---------------------------------------------------------------- device-coherent accesses
+// Values one workgroup writes and another reads within the same kernel (the
+// persistent decode kernel passes activations, q, attention partials and the
+// appended K/V between phases) use device-scope accesses: the store writes
+// through to memory and the load does not use a possibly stale line of its
+// own XCD's L2.  A writer makes its stores visible by waiting for their
+// completion (wait_stores) before it raises its barrier flag; no L2 writeback
+// fence is needed because none of the exchanged data sits dirty in an L2.
+I4D_DEVINL void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL void st_dev(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL void st_dev(uint16_t* p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL void st_dev(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL float ld_dev(const float* p) { return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL int ld_dev(const int* p) { return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL u64 ld_dev(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL f4 ld_dev4(const float* p) { return f4{ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3)}; }
+// wait until every vector-memory access of this thread (stores included) has completed
+I4D_DEVINL void wait_stores() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- status word
 I4D_DEVINL void raise_status(int* status, int bit) { atomicOr(status, bit); }

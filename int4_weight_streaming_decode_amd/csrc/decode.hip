@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <vector>
 #include <string.h>
 
 #include "../../include/i4decode.h"
@@ -33,6 +34,11 @@ constexpr int MAX_BATCH = 8;
 
 template <int NB> struct MaxJ { static constexpr int v = NB <= 2 ? 8 : 4; };
 
+// LDS beyond the staged activations: per-slot partials, a reduction scratch
+// and an "extra" area (positions: 64 B; RoPE cos/sin table: NB * 64 float2).
+constexpr int GEMV_EXTRA = 64 + MAX_BATCH * 64 * 8;
+
+
 // ============================================================== epilogues and staging functors
 
 // Stage `src` (optionally RMS-normalised with `gain`) into LDS.
@@ -58,8 +64,8 @@ struct EpiRows {
         const int r = 2 * pair;
         float* yr = y + (size_t)b * n;
         const float* rr = resid ? resid + (size_t)b * n : nullptr;
-        yr[r] = (rr ? rr[r] : 0.f) + va;
-        if (r + 1 < n) yr[r + 1] = (rr ? rr[r + 1] : 0.f) + vb;
+        st_dev(yr + r, (rr ? rr[r] : 0.f) + va);
+        if (r + 1 < n) st_dev(yr + r + 1, (rr ? rr[r + 1] : 0.f) + vb);
     }
     __device__ void end_pass(int, int, int) {}
 };
@@ -69,15 +75,30 @@ struct EpiSwiGLU {
     float* act; int F; int nb;
     __device__ void operator()(int, int pair, int b, float g, float u) {
         if (b >= nb) return;
-        act[(size_t)b * F + pair] = g / (1.0f + expf(-g)) * u;
+        st_dev(act + (size_t)b * F + pair, g / (1.0f + expf(-g)) * u);
     }
     __device__ void end_pass(int, int, int) {}
 };
 
+// cos/sin of the RoPE angles pos[b] * base^(-2i/hd) for every batch slot and
+// pair index i < hd/2, computed once per launch in float64 (the angle reaches
+// 3e4 rad at long positions, beyond what float32 can reduce accurately) and
+// kept in LDS as float2 [NB][hd/2].  pos_lds[b] = -1 (invalid) uses angle 0.
+template <int NB>
+I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) {
+    const int half = hd >> 1;
+    for (int idx = threadIdx.x; idx < NB * half; idx += blockDim.x) {
+        const int b = idx / half, i = idx - b * half;
+        const double theta = pow(base, -2.0 * (double)i / (double)hd);
+        const double phi = (double)max(pos_lds[b], 0) * theta;
+        cs[idx] = float2{(float)cos(phi), (float)sin(phi)};
+    }
+}
+
 // RoPE on q and k pairs, q to the fp32 buffer, bf16 k/v appended at slot pos[b].
 struct EpiQKV {
-    float* q; uint16_t* kc; uint16_t* vc; const int* pos_lds;
-    int cap, hq, hkv, hd, nb; double base;
+    float* q; uint16_t* kc; uint16_t* vc; const int* pos_lds; const float2* cs;
+    int cap, hq, hkv, hd, nb;
     __device__ void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int half = hd >> 1;
@@ -88,23 +109,21 @@ struct EpiQKV {
         const int p = pos_lds[b];                      // -1: invalid position, nothing appended
         float ra = va, rb = vb;
         if (mat < 2) {
-            const double theta = pow(base, -2.0 * (double)i / (double)hd);
-            const double phi = (double)max(p, 0) * theta;
-            const float c = (float)cos(phi), s = (float)sin(phi);
-            ra = va * c - vb * s;
-            rb = va * s + vb * c;
+            const float2 r = cs[b * half + i];
+            ra = va * r.x - vb * r.y;
+            rb = va * r.y + vb * r.x;
         }
         if (mat == 0) {
             float* qr = q + ((size_t)b * hq + head) * hd;
-            qr[i] = ra; qr[i + half] = rb;
+            st_dev(qr + i, ra); st_dev(qr + i + half, rb);
         } else if (p >= 0) {
             if (mat == 1) {
                 uint16_t* kr = kc + (((size_t)b * hkv + head) * cap + p) * hd;
-                kr[i] = f32_to_bf16(ra); kr[i + half] = f32_to_bf16(rb);
+                st_dev(kr + i, f32_to_bf16(ra)); st_dev(kr + i + half, f32_to_bf16(rb));
             } else {
                 uint16_t* vr = vc + ((size_t)b * hkv + head) * hd * cap;
-                vr[(size_t)i * cap + p] = f32_to_bf16(ra);
-                vr[(size_t)(i + half) * cap + p] = f32_to_bf16(rb);
+                st_dev(vr + (size_t)i * cap + p, f32_to_bf16(ra));
+                st_dev(vr + (size_t)(i + half) * cap + p, f32_to_bf16(rb));
             }
         }
     }
@@ -133,7 +152,7 @@ __host__ __device__ constexpr int gemv_part_bytes() { return (GEMV_NT / 16) * (M
 
 template <int FMT, int NB, int PREC>
 __host__ inline size_t gemv_lds_bytes(int K) {
-    return (size_t)act_lds_bytes<FMT, NB, PREC>(K) + gemv_part_bytes<FMT, NB>() + (GEMV_NT / 64) * NB * 4 + 256;
+    return (size_t)act_lds_bytes<FMT, NB, PREC>(K) + gemv_part_bytes<FMT, NB>() + (GEMV_NT / 64) * NB * 4 + GEMV_EXTRA;
 }
 
 struct GemvLds { char* act; float* part; float* red; char* extra; };
@@ -201,8 +220,11 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
         }
         pos_lds[threadIdx.x] = p;
     }
+    __syncthreads();
+    float2* cs = (float2*)(L.extra + 64);
+    rope_table<NB>(cs, pos_lds, t.head_dim, base);
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiQKV ep{q, kc, vc, pos_lds, cap, hq, hkv, t.head_dim, nb, base};
+    EpiQKV ep{q, kc, vc, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
     gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -214,7 +236,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h,
     EpiArgmax ep{t.a.n, nb, 0ull, -1};
     gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
     // workgroup best per batch slot -> this workgroup's key slots
-    u64* kl = (u64*)(L.extra + 256);
+    u64* kl = (u64*)(L.extra + GEMV_EXTRA);
     int* ks = (int*)(kl + GEMV_NT);
     kl[threadIdx.x] = ep.best;
     ks[threadIdx.x] = ep.bslot;
@@ -261,7 +283,193 @@ __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
 template <int HD>
 __global__ void __launch_bounds__(HD) k_attention_merge(AttnArgs a) {
     __shared__ float lds[2 * NSPLIT_MAX];
-    attn_merge_head<HD>(a, blockIdx.x, lds);
+    attn_merge_heads<HD, HD>(a, blockIdx.x, a.batch * a.hq, lds);
+}
+
+// Workspace: an 8 KB header (status word, grid-barrier epoch and flags), the
+// persistent kernel's layer table, then the fp32 buffers of the layer.  The LM head uses the bytes after the header for its
+// per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer buffers:
+// calls on one stream never use both at once.
+constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_FLAGS = 4096, WS_HEADER = 8192;
+constexpr int PERS_MAX_WG = 1024;                    // flags: one int per workgroup of the persistent kernel
+constexpr int PERS_MAX_LAYERS = 256;
+constexpr int LM_MAX_WG = 4096;
+constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH * 8;
+
+// ============================================================== persistent decode kernel
+// One cooperative launch runs every layer of the step: 256 workgroups (one per
+// compute unit) walk through the six phases of each layer, separated by grid
+// barriers.  Before a barrier each workgroup already issues the weight loads
+// of the next matrix-vector phase (weights do not depend on activations), so
+// HBM keeps streaming while the barrier completes.
+
+struct PLayer {
+    GemvTask qkv, wo, gu, down;
+    const uint16_t* attn_norm;
+    const uint16_t* ffn_norm;
+    uint16_t* kc;
+    uint16_t* vc;
+    float* q; float* o; float* y; float* act; float* xout;   // this layer's buffers
+};
+constexpr size_t PERS_TABLE_BYTES = (size_t)PERS_MAX_LAYERS * sizeof(PLayer);
+
+struct PArgs {
+    const PLayer* layers;
+    int n_layers, batch;
+    const float* x_in;
+    AttnArgs attn;               // per-layer q, o, kc, vc filled in by the kernel
+    const int* pos;
+    int max_pos, cap, hq, hkv, hd, d_model, d_ff;
+    double base;
+    float eps;
+    int act_bytes;               // LDS bytes reserved for staged activations
+    int pos_off;                 // LDS offset of the per-sequence positions (past every phase's use)
+    int* status; int* flags; int* epoch;
+};
+
+constexpr int PERS_NT = 512;
+constexpr long long BAR_SPIN_LIMIT = 1 << 20;
+
+// Grid barrier on per-workgroup epoch flags.  A workgroup publishes epoch
+// base + k once every thread's stores have completed, then one wave polls all
+// flags with device-scope loads.  The spin is bounded: on timeout the status
+// word gets I4D_DEV_BARRIER_TIMEOUT and, that bit being sticky, no later
+// barrier of any workgroup waits again -- every wave always reaches the end.
+struct GridSync {
+    int* flags; int* status; int base; int nwg;
+    __device__ void wait(int k) const {
+        const int target = base + k;
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) st_dev(flags + blockIdx.x, target);
+        if (threadIdx.x < 64) {
+            if ((ld_dev(status) & I4D_DEV_BARRIER_TIMEOUT) == 0) {
+                long long spins = 0;
+                for (;;) {
+                    bool ok = true;
+                    for (int i = threadIdx.x; i < nwg; i += 64) ok = ok && (ld_dev(flags + i) - target >= 0);
+                    if (__all(ok)) break;
+                    if (++spins > BAR_SPIN_LIMIT) {
+                        if (threadIdx.x == 0) raise_status(status, I4D_DEV_BARRIER_TIMEOUT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+        }
+        __syncthreads();
+    }
+};
+
+template <int NB, class Nx>
+struct PrimeNext {
+    GemvPipe<FMT_INT4_FAST, GEMV_D>* P; const GemvTask* t; int w, nwg; bool on;
+    __device__ void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, GEMV_D>(*P, *t, w, nwg); }
+};
+
+template <int NB>
+__global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
+    constexpr int FMT = FMT_INT4_FAST;
+    constexpr int MJ = MaxJ<NB>::v;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int w = blockIdx.x, nwg = gridDim.x;
+    GemvLds L;
+    L.act = lds;
+    L.part = (float*)(lds + A.act_bytes);
+    L.red = L.part + gemv_part_bytes<FMT, NB>() / 4;
+    L.extra = (char*)(L.red + (PERS_NT / 64) * NB);
+    int* pos_lds = (int*)(lds + A.pos_off);
+    float2* cs = (float2*)(lds + A.pos_off + 64);
+    if (threadIdx.x < NB) {
+        int p = -1;
+        if ((int)threadIdx.x < A.batch) {
+            p = A.pos[threadIdx.x];
+            if (p < 0 || p > A.max_pos || p >= A.cap) {
+                if (w == 0) raise_status(A.status, I4D_DEV_BAD_POS);
+                p = -1;
+            }
+        }
+        pos_lds[threadIdx.x] = p;
+    }
+    __syncthreads();
+    rope_table<NB>(cs, pos_lds, A.hd, A.base);
+    GridSync gs{A.flags, A.status, ld_dev(A.epoch), nwg};
+    int bar = 0;
+    const int items = A.batch * A.hkv * A.attn.nsplit;
+    const int heads = A.batch * A.hq;
+    constexpr int HPW = PERS_NT / 128;              // heads merged per workgroup per round
+
+    GemvPipe<FMT, GEMV_D> P;
+    gemv_prime<FMT, PERS_NT, GEMV_D>(P, A.layers[0].qkv, w, nwg);
+    for (int l = 0; l < A.n_layers; ++l) {
+        const PLayer& Ly = A.layers[l];
+        const float* xin = (l == 0) ? A.x_in : A.layers[l - 1].xout;
+        float* xout = Ly.xout;
+
+        // ---- q/k/v projection, RoPE, KV append
+        {
+            StagePre<FMT> pre;
+            stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, Ly.attn_norm);
+            stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, Ly.attn_norm, A.eps, L.red);
+            __syncthreads();
+            EpiQKV ep{Ly.q, Ly.kc, Ly.vc, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
+            NoNext nn;
+            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, GEMV_D, MJ>(P, Ly.qkv, w, nwg, L.act, L.part, ep, nn);
+        }
+        gs.wait(++bar);
+        // ---- attention partials (then the Wo weights start streaming)
+        {
+            AttnArgs a = A.attn;
+            a.kc = Ly.kc; a.vc = Ly.vc; a.q = Ly.q;
+            for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT>(a, it, lds);
+            gemv_prime<FMT, PERS_NT, GEMV_D>(P, Ly.wo, w, nwg);
+        }
+        gs.wait(++bar);
+        // ---- merge of the splits
+        {
+            AttnArgs a = A.attn;
+            a.o = Ly.o;
+            for (int bh0 = w * HPW; bh0 < heads; bh0 += nwg * HPW) attn_merge_heads<128, PERS_NT>(a, bh0, heads, (float*)lds);
+        }
+        gs.wait(++bar);
+        // ---- output projection + residual
+        {
+            StagePre<FMT> pre;
+            stage_issue<FMT, NB, PERS_NT>(pre, Ly.o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
+            __syncthreads();
+            EpiRows ep{Ly.y, xin, A.d_model, A.batch};
+            PrimeNext<NB, void> nx{&P, &Ly.gu, w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.wo, w, nwg, L.act, L.part, ep, nx);
+        }
+        gs.wait(++bar);
+        // ---- gate/up projection + SwiGLU
+        {
+            StagePre<FMT> pre;
+            stage_issue<FMT, NB, PERS_NT>(pre, Ly.y, A.d_model, A.d_model, A.batch, Ly.ffn_norm);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.y, A.d_model, A.d_model, A.batch, Ly.ffn_norm, A.eps, L.red);
+            __syncthreads();
+            EpiSwiGLU ep{Ly.act, A.d_ff, A.batch};
+            PrimeNext<NB, void> nx{&P, &Ly.down, w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.gu, w, nwg, L.act, L.part, ep, nx);
+        }
+        gs.wait(++bar);
+        // ---- down projection + residual (then the next layer's q/k/v weights start streaming)
+        {
+            StagePre<FMT> pre;
+            stage_issue<FMT, NB, PERS_NT>(pre, Ly.act, A.d_ff, A.d_ff, A.batch, nullptr);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.act, A.d_ff, A.d_ff, A.batch, nullptr, 0.f, L.red);
+            __syncthreads();
+            EpiRows ep{xout, Ly.y, A.d_model, A.batch};
+            const bool more = l + 1 < A.n_layers;
+            PrimeNext<NB, void> nx{&P, more ? &A.layers[l + 1].qkv : &Ly.qkv, w, nwg, more};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.down, w, nwg, L.act, L.part, ep, nx);
+        }
+        if (l + 1 < A.n_layers) gs.wait(++bar);
+    }
+    // every workgroup read the epoch at its start before any passed the first
+    // barrier, so the next launch's epoch can be published now
+    if (w == 0 && threadIdx.x == 0) st_dev(A.epoch, gs.base + bar);
 }
 
 // ============================================================== host helpers
@@ -280,32 +488,38 @@ int num_cus() {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: a 512-byte header (the status word), then the fp32 buffers of
-// the layer.  The LM head uses the bytes after the header for its
-// per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer buffers:
-// calls on one stream never use both at once.
-constexpr size_t WS_STATUS = 0, WS_HEADER = 512;
-constexpr int LM_MAX_WG = 4096;
-constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH * 8;
-
 struct WsLayout {
-    size_t q, pm, pl, po, o, y, act, ping0, ping1, total;
+    size_t table, pm, pl, po, ping0, ping1;
+    size_t layer0, layer_stride;          // per-layer activation regions
+    size_t q, o, y, act, x;               // offsets inside a layer region
+    size_t total;
 };
 
-WsLayout ws_layout(const i4d_config* c, int B) {
+// Layer l's region holds its q, merged attention output o, residual y, SwiGLU
+// activations and output x.  Per-phase launches use region 0 only; the
+// persistent kernel gives every layer its own region so that no buffer is read
+// in a launch before it has been written there.
+WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     WsLayout w;
     size_t off = WS_HEADER;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    w.table = take(PERS_TABLE_BYTES);
     const size_t hq = c->n_q_heads, hd = c->head_dim;
-    w.q = take((size_t)B * hq * hd * 4);
     w.pm = take((size_t)B * hq * NSPLIT_MAX * 4);
     w.pl = take((size_t)B * hq * NSPLIT_MAX * 4);
     w.po = take((size_t)B * hq * NSPLIT_MAX * hd * 4);
-    w.o = take((size_t)B * hq * hd * 4);
-    w.y = take((size_t)B * c->d_model * 4);
-    w.act = take((size_t)B * c->d_ff * 4);
     w.ping0 = take((size_t)B * c->d_model * 4);
     w.ping1 = take((size_t)B * c->d_model * 4);
+    size_t lo = 0;
+    auto ltake = [&](size_t bytes) { size_t o = lo; lo = align256(lo + bytes); return o; };
+    w.q = ltake((size_t)B * hq * hd * 4);
+    w.o = ltake((size_t)B * hq * hd * 4);
+    w.y = ltake((size_t)B * c->d_model * 4);
+    w.act = ltake((size_t)B * c->d_ff * 4);
+    w.x = ltake((size_t)B * c->d_model * 4);
+    w.layer_stride = lo;
+    w.layer0 = off;
+    off += (size_t)std::max(n_layers, 1) * lo;
     w.total = std::max(off, WS_LM_KEYS + WS_LM_BYTES);
     return w;
 }
@@ -578,16 +792,130 @@ int launch_attention(const i4d_config* c, int B, const float* q, const i4d_kv* k
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
+// ---------------------------------------------------------------- persistent launch
+template <int NB>
+size_t persistent_lds(const i4d_config* c, int nsplit) {
+    constexpr int FMT = FMT_INT4_FAST;
+    const int D = c->d_model, qw = c->n_q_heads * c->head_dim, F = c->d_ff;
+    const int act = std::max(std::max(act_lds_bytes<FMT, NB, PREC_QKV>(D), act_lds_bytes<FMT, NB, PREC_STD>(qw)),
+                             act_lds_bytes<FMT, NB, PREC_STD>(F));
+    const size_t gemv = (size_t)act + gemv_part_bytes<FMT, NB>() + (PERS_NT / 64) * NB * 4 + 256;
+    const size_t attn = attn_lds_bytes<128, PERS_NT>();
+    const size_t merge = (size_t)(PERS_NT / 128) * 2 * nsplit * 4;
+    return align256(std::max(std::max(gemv, attn), merge)) + GEMV_EXTRA;
+}
+
+bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int B) {
+    if (c->head_dim != 128 || B > 4 || n_layers > PERS_MAX_LAYERS) return false;
+    const int nwg = num_cus();
+    if (nwg > PERS_MAX_WG || GEMV_NT != PERS_NT) return false;
+    for (int l = 0; l < n_layers; ++l) {
+        const i4d_layer& L = layers[l];
+        const i4d_mat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+        for (int i = 0; i < 7; ++i)
+            if (m[i]->dtype != I4D_WEIGHT_INT4 || pick_fmt(*m[i]) != FMT_INT4_FAST) return false;
+        if (kv[l].capacity != kv[0].capacity) return false;
+    }
+    return true;
+}
+
+template <int NB>
+int launch_persistent_t(PArgs& A, int nwg, size_t lds, hipStream_t s) {
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (set_lds(k_decode_persistent<NB>, lds) != hipSuccess) return I4D_EHIP;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_persistent<NB>, PERS_NT, lds) != hipSuccess)
+        return I4D_EHIP;
+    if (per_cu < 1) return I4D_EUNSUPPORTED;
+    void* args[] = {&A};
+    if (hipLaunchCooperativeKernel((const void*)k_decode_persistent<NB>, dim3(nwg), dim3(PERS_NT), args, (unsigned)lds, s) != hipSuccess)
+        return I4D_EHIP;
+    return I4D_OK;
+}
+
+int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* layers, int B, const float* x_in, float* x_out,
+                         const i4d_kv* kv, const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
+    const int nb = nb_slot(B), nwg = num_cus();
+    const int hd = c->head_dim;
+    std::vector<PLayer> tab((size_t)n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+        const i4d_layer& Ls = layers[l];
+        PLayer& P = tab[(size_t)l];
+        P.qkv = make_task(KIND_QKV, &Ls.wq, &Ls.wk, &Ls.wv, hd);
+        P.wo = make_task(KIND_ADJ, &Ls.wo, nullptr, nullptr, hd);
+        P.gu = make_task(KIND_TWO, &Ls.wg, &Ls.wu, nullptr, hd);
+        P.down = make_task(KIND_ADJ, &Ls.wd, nullptr, nullptr, hd);
+        plan_passes(P.qkv, FMT_INT4_FAST, nb, nwg, 0);
+        plan_passes(P.wo, FMT_INT4_FAST, nb, nwg, 0);
+        plan_passes(P.gu, FMT_INT4_FAST, nb, nwg, 0);
+        plan_passes(P.down, FMT_INT4_FAST, nb, nwg, 0);
+        P.attn_norm = Ls.attn_norm;
+        P.ffn_norm = Ls.ffn_norm;
+        P.kc = kv[l].k;
+        P.vc = kv[l].v;
+        char* R = ws + W.layer0 + (size_t)l * W.layer_stride;
+        P.q = (float*)(R + W.q); P.o = (float*)(R + W.o); P.y = (float*)(R + W.y); P.act = (float*)(R + W.act);
+        P.xout = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
+    }
+    // pageable source: the copy is staged before hipMemcpyAsync returns
+    if (hipMemcpyAsync(ws + W.table, tab.data(), tab.size() * sizeof(PLayer), hipMemcpyHostToDevice, s) != hipSuccess)
+        return I4D_EHIP;
+
+    PArgs A;
+    memset(&A, 0, sizeof(A));
+    A.layers = (const PLayer*)(ws + W.table);
+    A.n_layers = n_layers;
+    A.batch = B;
+    A.x_in = x_in;
+    AttnArgs& a = A.attn;
+    a.q = nullptr; a.pos = pos; a.cap = kv[0].capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B;
+    a.max_pos = max_pos;
+    plan_attention(c, B, max_pos, a.nsplit, a.T);
+    a.nsplit_max = NSPLIT_MAX;
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)hd));
+    a.pm = (float*)(ws + W.pm); a.pl = (float*)(ws + W.pl); a.po = (float*)(ws + W.po);
+    a.o = nullptr;
+    A.pos = pos; A.max_pos = max_pos; A.cap = kv[0].capacity;
+    A.hq = c->n_q_heads; A.hkv = c->n_kv_heads; A.hd = hd; A.d_model = c->d_model; A.d_ff = c->d_ff;
+    A.base = c->rope_base; A.eps = c->rms_eps;
+    A.status = (int*)(ws + WS_STATUS); A.flags = (int*)(ws + WS_FLAGS); A.epoch = (int*)(ws + WS_EPOCH);
+    const int D = c->d_model, qw = c->n_q_heads * hd, F = c->d_ff;
+    switch (nb) {
+        case 1: {
+            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 1, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 1, PREC_STD>(qw)),
+                                   act_lds_bytes<FMT_INT4_FAST, 1, PREC_STD>(F));
+            const size_t lds = persistent_lds<1>(c, a.nsplit);
+            A.pos_off = (int)lds - GEMV_EXTRA;
+            return launch_persistent_t<1>(A, nwg, lds, s);
+        }
+        case 2: {
+            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 2, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 2, PREC_STD>(qw)),
+                                   act_lds_bytes<FMT_INT4_FAST, 2, PREC_STD>(F));
+            const size_t lds = persistent_lds<2>(c, a.nsplit);
+            A.pos_off = (int)lds - GEMV_EXTRA;
+            return launch_persistent_t<2>(A, nwg, lds, s);
+        }
+        default: {
+            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 4, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 4, PREC_STD>(qw)),
+                                   act_lds_bytes<FMT_INT4_FAST, 4, PREC_STD>(F));
+            const size_t lds = persistent_lds<4>(c, a.nsplit);
+            A.pos_off = (int)lds - GEMV_EXTRA;
+            return launch_persistent_t<4>(A, nwg, lds, s);
+        }
+    }
+}
+
 // One layer as five phase launches.
 int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
                      const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
     const int nb = nb_slot(B), nwg = num_cus() * WG_PER_CU;
     const int hd = c->head_dim;
     int* status = (int*)(ws + WS_STATUS);
-    float* q = (float*)(ws + W.q);
-    float* o = (float*)(ws + W.o);
-    float* y = (float*)(ws + W.y);
-    float* act = (float*)(ws + W.act);
+    char* R = ws + W.layer0;
+    float* q = (float*)(R + W.q);
+    float* o = (float*)(R + W.o);
+    float* y = (float*)(R + W.y);
+    float* act = (float*)(R + W.act);
     int rc;
 
     GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
@@ -619,10 +947,10 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 // ============================================================== C ABI
 extern "C" {
 
-size_t i4d_workspace_size(const i4d_config* cfg, int32_t batch, int32_t max_pos, int32_t vocab) {
-    if (validate_cfg(cfg) || batch < 1 || batch > MAX_BATCH || max_pos < 0) return 0;
+size_t i4d_workspace_size(const i4d_config* cfg, int32_t n_layers, int32_t batch, int32_t max_pos, int32_t vocab) {
+    if (validate_cfg(cfg) || n_layers < 1 || batch < 1 || batch > MAX_BATCH || max_pos < 0) return 0;
     (void)vocab;
-    return ws_layout(cfg, batch).total;
+    return ws_layout(cfg, n_layers, batch).total;
 }
 
 int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -654,11 +982,14 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if (layers[l].wq.dtype != layers[0].wq.dtype) return I4D_EINVAL;
         if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
     }
-    const WsLayout W = ws_layout(cfg, batch);
+    const WsLayout W = ws_layout(cfg, n_layers, batch);
     if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
-    if (cfg->exec_mode == 2) return I4D_EUNSUPPORTED;
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
+    if (cfg->exec_mode == 2) {
+        if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
+        return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
+    }
     float* ping[2] = {(float*)(w + W.ping0), (float*)(w + W.ping1)};
     for (int l = 0; l < n_layers; ++l) {
         const float* in = (l == 0) ? x_in : ping[(l - 1) & 1];
@@ -719,7 +1050,7 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
     if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
     if (!q || !o || !pos) return I4D_EINVAL;
     if ((rc = validate_kv(cfg, kv, max_pos))) return rc;
-    const WsLayout W = ws_layout(cfg, batch);
+    const WsLayout W = ws_layout(cfg, 1, batch);
     if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
     return launch_attention(cfg, batch, q, kv, pos, max_pos, o, (char*)ws, W, (hipStream_t)stream);
 }

@@ -254,7 +254,7 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
 // waits for every load issued before it).  stage_issue() loads the first
 // PRE_CHUNKS chunks of each thread into registers; stage_finish() does the
 // rest.  `red` is NT/64*NB floats of LDS.
-constexpr int PRE_CHUNKS = 2;
+constexpr int PRE_CHUNKS = 1;
 
 template <int FMT>
 struct StagePre {
@@ -274,6 +274,9 @@ I4D_DEVINL void stage_load_chunk(f4 (&xv)[StagePre<FMT>::NV], u32x4 (&gv)[FmtT<F
     const int nchunk = K / cw;
     const int b = idx / nchunk, c = idx - b * nchunk;
     const int k0 = c * cw;
+    // written by an earlier phase: either an earlier kernel, or -- in the
+    // persistent kernel -- a buffer of this layer that no workgroup read
+    // before it was written (so no L2 holds a stale copy of it)
     const f4* xp = (const f4*)(src + (size_t)min(b, nb - 1) * src_stride + k0);
 #pragma unroll
     for (int i = 0; i < NV; ++i) xv[i] = xp[i];
@@ -477,16 +480,42 @@ I4D_DEVINL void cursor_load(LoadCursor& lc, Unit<FMT>& dst, const GemvTask& t, i
 }
 
 // ---------------------------------------------------------------- the pass loop
-// Run every pass of task `t` for workgroup w.  The activations are staged once:
-//   stage.issue(pre), stage.finish(pre) -- see stage_issue / stage_finish
-// and for each pass:
+// The load ring of one workgroup lane plus the geometry of the pass it is
+// loading.  A ring can be primed for a phase (gemv_prime) long before the
+// phase runs -- e.g. before the grid barrier that precedes it -- because
+// weights do not depend on the previous phase.
+template <int FMT, int D>
+struct GemvPipe {
+    Unit<FMT> ring[D];
+    LoadCursor lc;
+    int q0, q1, u0, u1, n_it;     // pass-0 geometry of the primed phase
+};
+
+// Issue the first D units of pass 0 of task t into the ring.
+template <int FMT, int NT, int D>
+I4D_DEVINL void gemv_prime(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg) {
+    constexpr int NW = NT / 64;
+    const int slot = threadIdx.x >> 4, lane16 = threadIdx.x & 15;
+    const int S = (t.k + FmtT<FMT>::UNIT_W - 1) / FmtT<FMT>::UNIT_W;
+    pass_pairs_of(t, 0, w, nwg, P.q0, P.q1);
+    slot_range<NW>((P.q1 - P.q0) * S, slot, P.u0, P.u1, P.n_it);
+    cursor_begin<FMT>(P.lc, t, P.q0, P.u0, P.u1, S);
+#pragma unroll
+    for (int i = 0; i < D; ++i) cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+}
+
+struct NoNext { __device__ void operator()() {} };
+
+// Run every pass of task `t` for workgroup w, the ring P already primed
+// for t.  Activations must already be staged in act_lds.  For each pass:
 //   epi(pass, pair, b, va, vb)   -- per (pair, batch slot) results, pair in [q0, q1)
 //   epi.end_pass(pass, q0, q1)   -- after all epilogue calls of the pass
-// Each lane keeps D units in flight; the first D units of the next pass are
-// issued before the current pass's reduction and epilogue.
+// After the last pass's loads are consumed, next() may prime the ring for the
+// following phase; its loads are then in flight during this epilogue.
 // LDS: act_lds (staged activations), part_lds (NS*MAXJ*NB*2 floats + 2*NS ints).
-template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Stage, class Epi>
-__device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
+template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Epi, class Next>
+__device__ void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg, const char* act_lds, float* part_lds,
+                            Epi& epi, Next& next) {
     constexpr int NW = NT / 64, NS = NT / 16;
     typedef FmtT<FMT> F;
     const int tid = threadIdx.x;
@@ -494,24 +523,8 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
     const int S = (t.k + F::UNIT_W - 1) / F::UNIT_W;
     int* slot_info = (int*)(part_lds + NS * MAXJ * NB * 2);     // [NS][2]: first local pair, runs
 
-    StagePre<FMT> pre;
-    stage.issue(pre);                    // activation loads first ...
-
-    Unit<FMT> ring[D];
-    LoadCursor lc;
-    int q0, q1, u0, u1, n_it;
-    pass_pairs_of(t, 0, w, nwg, q0, q1);
-    slot_range<NW>((q1 - q0) * S, slot, u0, u1, n_it);
-    cursor_begin<FMT>(lc, t, q0, u0, u1, S);
-#pragma unroll
-    for (int i = 0; i < D; ++i) cursor_load<FMT>(lc, ring[i], t, S, lane16);   // ... then the weight ring
-
-    stage.finish(pre);                   // waits only for the activation loads
-    __syncthreads();
-
     for (int pass = 0; pass < t.npasses; ++pass) {
-        const int n_itp = ((n_it + D - 1) / D) * D;
-
+        const int n_itp = ((P.n_it + D - 1) / D) * D;
         float ra[NB], rb[NB], da[MAXJ][NB], db[MAXJ][NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) { ra[b] = 0.f; rb[b] = 0.f; }
@@ -520,15 +533,16 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
 #pragma unroll
             for (int b = 0; b < NB; ++b) { da[j][b] = 0.f; db[j][b] = 0.f; }
         int run = 0;
-        const int first_local = u0 / S;
-        int seg = u0 - first_local * S;
-        int u = u0;
+        const int first_local = P.u0 / S;
+        int seg = P.u0 - first_local * S;
+        int u = P.u0;
+        const int u1 = P.u1;
 
         for (int itb = 0; itb < n_itp; itb += D) {
 #pragma unroll
             for (int i = 0; i < D; ++i) {
                 if (u < u1) {
-                    consume_unit<FMT, NB, PREC>(ring[i], act_lds, t.k, seg, lane16, ra, rb);
+                    consume_unit<FMT, NB, PREC>(P.ring[i], act_lds, t.k, seg, lane16, ra, rb);
                     ++u;
                     if (++seg == S) {   // this pair's run is complete: park it
                         seg = 0;
@@ -542,7 +556,7 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
                         ++run;
                     }
                 }
-                cursor_load<FMT>(lc, ring[i], t, S, lane16);
+                cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
             }
         }
         if (seg != 0) {      // a partially covered last pair
@@ -553,14 +567,16 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
                     for (int b = 0; b < NB; ++b) { da[j][b] = ra[b]; db[j][b] = rb[b]; }
             ++run;
         }
-        const int this_q0 = q0, this_q1 = q1;
-        // next pass: geometry, and its first D units in flight during this epilogue
+        const int this_q0 = P.q0, this_q1 = P.q1;
+        // next pass (or next phase): its first D units fly during this epilogue
         if (pass + 1 < t.npasses) {
-            pass_pairs_of(t, pass + 1, w, nwg, q0, q1);
-            slot_range<NW>((q1 - q0) * S, slot, u0, u1, n_it);
-            cursor_begin<FMT>(lc, t, q0, u0, u1, S);
+            pass_pairs_of(t, pass + 1, w, nwg, P.q0, P.q1);
+            slot_range<NW>((P.q1 - P.q0) * S, slot, P.u0, P.u1, P.n_it);
+            cursor_begin<FMT>(P.lc, t, P.q0, P.u0, P.u1, S);
 #pragma unroll
-            for (int i = 0; i < D; ++i) cursor_load<FMT>(lc, ring[i], t, S, lane16);
+            for (int i = 0; i < D; ++i) cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+        } else {
+            next();
         }
         // 16-lane sums of every run, written by lane 0 of the slot
 #pragma unroll
@@ -576,16 +592,16 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
             }
         if (lane16 == 0) { slot_info[2 * slot] = first_local; slot_info[2 * slot + 1] = min(run, MAXJ); }
         __syncthreads();
-        // per-pair totals: 32 lanes per (pair, batch slot), lane i reading the
-        // slots i, i+32, ..; a fixed shuffle tree sums them (deterministic)
+        // per-pair totals: one 16-lane DPP row per (pair, batch slot), lane i
+        // reading the slots i, i+16, ..; a fixed rotation tree sums them
         const int npairs = this_q1 - this_q0;
-        const int grp = tid >> 5, l32 = tid & 31;
-        for (int base = 0; base < npairs * NB; base += NT / 32) {
+        const int grp = tid >> 4;
+        for (int base = 0; base < npairs * NB; base += NT / 16) {
             const int idx = base + grp;
             const int ql = idx / NB, b = idx - ql * NB;
             float va = 0.f, vb = 0.f;
             if (idx < npairs * NB) {
-                for (int s2 = l32; s2 < NS; s2 += 32) {
+                for (int s2 = lane16; s2 < NS; s2 += 16) {
                     const int j = ql - slot_info[2 * s2];
                     if (j >= 0 && j < slot_info[2 * s2 + 1]) {
                         const float* p = part_lds + ((s2 * MAXJ + j) * NB + b) * 2;
@@ -593,13 +609,28 @@ __device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float
                     }
                 }
             }
-#pragma unroll
-            for (int m = 16; m >= 1; m >>= 1) { va += shfl_xor_f(va, m); vb += shfl_xor_f(vb, m); }
-            if (l32 == 0 && idx < npairs * NB) epi(pass, this_q0 + ql, b, va, vb);
+            va = row16_sum(va);
+            vb = row16_sum(vb);
+            if (lane16 == 0 && idx < npairs * NB) epi(pass, this_q0 + ql, b, va, vb);
         }
         epi.end_pass(pass, this_q0, this_q1);
         __syncthreads();
     }
+}
+
+// One whole phase in a single kernel: activation loads are issued first, then
+// the weight ring, then the activations are staged (waiting only for their own
+// loads), then every pass runs.
+template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Stage, class Epi>
+__device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
+    StagePre<FMT> pre;
+    stage.issue(pre);
+    GemvPipe<FMT, D> P;
+    gemv_prime<FMT, NT, D>(P, t, w, nwg);
+    stage.finish(pre);
+    __syncthreads();
+    NoNext nn;
+    gemv_passes<FMT, NB, PREC, NT, D, MAXJ>(P, t, w, nwg, act_lds, part_lds, epi, nn);
 }
 
 // Largest number of runs any slot can see in a pass of `pairs_per_wg` pairs

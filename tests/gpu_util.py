@@ -63,8 +63,8 @@ def config_of(shape, exec_mode=B.EXEC_AUTO):
                          shape.rms_eps, shape.rope_base, exec_mode)
 
 
-def workspace(cfg, batch, max_pos, vocab=0):
-    n = B.workspace_size(cfg, batch, max_pos, vocab)
+def workspace(cfg, batch, max_pos, vocab=0, n_layers=1):
+    n = B.workspace_size(cfg, n_layers, batch, max_pos, vocab)
     assert n > 0
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     B.workspace_init(ws)

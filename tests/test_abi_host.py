@@ -50,12 +50,15 @@ def _cfg(**kw):
 
 
 def test_workspace_size_is_pure_and_validates(lib):
-    assert B.workspace_size(_cfg(), 1, 127) > 0
-    assert B.workspace_size(_cfg(), 8, 32767) > B.workspace_size(_cfg(), 1, 32767)
-    assert B.workspace_size(_cfg(head_dim=96), 1, 127) == 0          # unsupported head_dim
-    assert B.workspace_size(_cfg(n_q_heads=6, n_kv_heads=4), 1, 127) == 0  # Hq % Hkv != 0
-    assert B.workspace_size(_cfg(), 9, 127) == 0                     # batch > 8
-    assert B.workspace_size(_cfg(), 0, 127) == 0
+    assert B.workspace_size(_cfg(), 1, 1, 127) > 0
+    assert B.workspace_size(_cfg(), 1, 8, 32767) > B.workspace_size(_cfg(), 1, 1, 32767)
+    assert B.workspace_size(_cfg(), 64, 1, 127) > B.workspace_size(_cfg(), 1, 1, 127)
+    assert B.workspace_size(_cfg(), 1, 1, 127) >= B.WS_MIN_BYTES
+    assert B.workspace_size(_cfg(head_dim=96), 1, 1, 127) == 0          # unsupported head_dim
+    assert B.workspace_size(_cfg(n_q_heads=6, n_kv_heads=4), 1, 1, 127) == 0  # Hq % Hkv != 0
+    assert B.workspace_size(_cfg(), 1, 9, 127) == 0                     # batch > 8
+    assert B.workspace_size(_cfg(), 1, 0, 127) == 0
+    assert B.workspace_size(_cfg(), 0, 1, 127) == 0                     # no layers
 
 
 class _FakeDev:
@@ -132,3 +135,11 @@ def test_binding_raises_with_status():
     with pytest.raises(B.I4DError) as e:
         B._check(B.I4D_EALIGN, "x")
     assert e.value.code == B.I4D_EALIGN
+
+
+def test_ws_min_bytes_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define I4D_WS_MIN_BYTES \((\d+) \+ (\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "I4D_WS_MIN_BYTES not found"
+    a, b, c, d = map(int, m.groups())
+    assert B.WS_MIN_BYTES == a + b * c * d

@@ -164,7 +164,7 @@ def test_decode_stack_matches_oracle_and_is_deterministic():
     ref = oracle.decode_stack(shape, layers, x.astype(np.float64), caches, pos)
     Ls = [DevLayer(l) for l in layers]
     cfg = config_of(shape)
-    ws = workspace(cfg, 1, 127)
+    ws = workspace(cfg, 1, 127, n_layers=3)
     outs = []
     for rep in range(2):
         kvs = [DevKV(*c) for c in caches]
@@ -237,3 +237,74 @@ def test_gpu_quantiser_matches_numpy_quantiser():
     c2, s2 = quantize_int4_torch(torch.from_numpy(w).cuda(), 64)
     assert np.array_equal(c2.cpu().numpy(), codes)
     assert np.array_equal(s2.cpu().numpy().view(np.uint16), scales)
+
+
+# ------------------------------------------------------------------ several decode steps (KV appended, position advancing)
+
+def _multi_step(shape, n_layers, pos0, steps, exec_mode, seed=21, batch=1):
+    """Run `steps` decode steps through decode_stack; return per-step outputs
+    and the final caches (host), plus the oracle's outputs and caches."""
+    cap = ((pos0 + steps + 7) // 8) * 8 + 8
+    layers = [synth.make_layer(shape, seed, l) for l in range(n_layers)]
+    caches = [synth.make_kv(shape, seed, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    xs = [synth.make_x(shape, seed, batch, step=s) for s in range(steps)]
+    Ls = [DevLayer(l) for l in layers]
+    kvs = [DevKV(*c) for c in caches]
+    cfg = config_of(shape, exec_mode)
+    ws = workspace(cfg, batch, cap - 1, n_layers=n_layers)
+    outs = []
+    for s in range(steps):
+        out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+        pos = dev(np.full(batch, pos0 + s, dtype=np.int32))
+        B.decode_stack(cfg, [l.layer for l in Ls], batch, dev(xs[s]), out, [k.kv for k in kvs], pos, pos0 + s, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    status = B.read_device_status(ws)
+    ref_caches = caches
+    ref_outs = []
+    for s in range(steps):
+        r = oracle.decode_stack(shape, layers, xs[s].astype(np.float64), ref_caches, [pos0 + s] * batch)
+        ref_outs.append(r["z"])
+        ref_caches = r["caches"]
+    return outs, [k.host() for k in kvs], ref_outs, ref_caches, status
+
+
+FAST_SHAPE = synth.SHAPES["tiny"].with_(name="fast", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                                        d_ff=1024, group=128, rope_base=1e6)
+
+
+@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_PERSISTENT])
+def test_multi_step_decode_matches_oracle(exec_mode):
+    _print_case("multi-step decode", exec_mode)
+    outs, kv_gpu, ref_outs, ref_caches, status = _multi_step(FAST_SHAPE, 2, 120, 3, exec_mode)
+    assert status == 0, status
+    for s in range(3):
+        assert_close(outs[s], ref_outs[s], what=f"step {s}")
+    for l in range(2):
+        for s in range(3):
+            for name, g_, r_ in (("K", kv_gpu[l][0], ref_caches[l][0]), ("V", kv_gpu[l][1], ref_caches[l][1])):
+                assert_close_bf16(synth.bf16_value(g_[0, :, 120 + s]), synth.bf16_value(r_[0, :, 120 + s]),
+                                  what=f"layer {l} {name} slot {120 + s}")
+
+
+def test_persistent_kernel_is_bit_identical_to_phase_launches():
+    _print_case("persistent vs phases")
+    a = _multi_step(FAST_SHAPE, 3, 200, 3, B.EXEC_PHASES, seed=23)
+    b = _multi_step(FAST_SHAPE, 3, 200, 3, B.EXEC_PERSISTENT, seed=23)
+    assert a[4] == 0 and b[4] == 0
+    for s in range(3):
+        assert np.array_equal(a[0][s].view(np.uint32), b[0][s].view(np.uint32)), f"step {s} differs"
+    for l in range(3):
+        assert np.array_equal(a[1][l][0], b[1][l][0]) and np.array_equal(a[1][l][1], b[1][l][1])
+
+
+def test_persistent_mode_rejects_unsupported_shapes():
+    shape = synth.SHAPES["tiny"]                       # K = 256, 688: not on the 512-wide fast path
+    layers, caches, x = _layer_case(shape, 3, 1, [20], cap=64)
+    L, kvd = DevLayer(layers[0]), DevKV(*caches[0])
+    cfg = config_of(shape, B.EXEC_PERSISTENT)
+    ws = workspace(cfg, 1, 20)
+    out = torch.empty((1, shape.d_model), dtype=torch.float32, device="cuda")
+    with pytest.raises(B.I4DError) as e:
+        B.decode_layer(cfg, L.layer, 1, dev(x), out, kvd.kv, dev(np.array([20], dtype=np.int32)), 20, ws)
+    assert e.value.code == B.I4D_EUNSUPPORTED

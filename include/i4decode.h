@@ -100,9 +100,10 @@ typedef struct i4d_layer {
 
 /* Model shape.  head_dim must be 64 or 128; n_q_heads / n_kv_heads <= 16.
  * exec_mode selects how decode_layer/decode_stack run their phases:
- *   0 = auto (persistent kernel when supported, else one launch per phase),
+ *   0 = auto (currently one launch per phase),
  *   1 = one kernel launch per phase,
- *   2 = one persistent cooperative kernel per call with grid barriers.     */
+ *   2 = one persistent cooperative kernel per call with grid barriers
+ *       (switched off in this build: returns I4D_EUNSUPPORTED).            */
 typedef struct i4d_config {
     int32_t d_model, n_q_heads, n_kv_heads, head_dim, d_ff;
     float   rms_eps;

@@ -25,6 +25,9 @@ namespace {
 #ifndef I4D_WG_PER_CU
 #define I4D_WG_PER_CU 1
 #endif
+#ifndef I4D_ENABLE_PERSISTENT
+#define I4D_ENABLE_PERSISTENT 0
+#endif
 constexpr int GEMV_NT = I4D_GEMV_NT;       // threads per GEMV workgroup
 constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
 constexpr int ATTN_NT = I4D_ATTN_NT;       // threads per attention workgroup
@@ -987,6 +990,10 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
     if (cfg->exec_mode == 2) {
+        // The persistent kernel took a GPU fault on its first launch in a test
+        // process after a change to its LDS layout; it stays switched off
+        // until the cause is shown.
+        if (!I4D_ENABLE_PERSISTENT) return I4D_EUNSUPPORTED;
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
         return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
     }

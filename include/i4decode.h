@@ -103,7 +103,8 @@ typedef struct i4d_layer {
  *   0 = auto (currently one launch per phase),
  *   1 = one kernel launch per phase,
  *   2 = one persistent cooperative kernel per call with grid barriers
- *       (switched off in this build: returns I4D_EUNSUPPORTED).            */
+ *       (int4 weights with one group size, head_dim 128, batch <= 4;
+ *       I4D_EUNSUPPORTED otherwise).                                        */
 typedef struct i4d_config {
     int32_t d_model, n_q_heads, n_kv_heads, head_dim, d_ff;
     float   rms_eps;

@@ -43,8 +43,8 @@ struct AttnArgs {
     float* o;                // [B][Hq][hd] fp32 (merge kernel output)
 };
 
-I4D_DEVINL u32x4 nt_load_k(const u32x4* p) { return __builtin_nontemporal_load(p); }
-I4D_DEVINL u32x2 nt_load_v(const u32x2* p) { return __builtin_nontemporal_load(p); }
+I4D_DEVINL u32x4 nt_load_k(const u32x4* p) { return ld_g_nt(p); }
+I4D_DEVINL u32x2 nt_load_v(const u32x2* p) { return ld_g_nt(p); }
 
 I4D_DEVINL s4 pack_bf16x4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
     s4 r; r[0] = (short)a; r[1] = (short)b; r[2] = (short)c; r[3] = (short)d; return r;
@@ -62,9 +62,9 @@ template <int HD, int NT>
 __host__ __device__ constexpr int attn_lds_bytes() { return (NT / 64) * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8; }
 
 template <int HD, int NT>
-__device__ void attn_item(const AttnArgs& a, int item, char* lds) {
+I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
     constexpr int NW = NT / 64, NKB = HD / 16, DPL = HD / 4;   // DPL: dims per lane group
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int G = a.hq / a.hkv;
     const int s = item % a.nsplit;
@@ -238,8 +238,8 @@ __device__ void attn_item(const AttnArgs& a, int item, char* lds) {
 // workgroup merges head bh0 + group (if < nheads); every thread of the
 // workgroup must call this (it synchronises).  LDS: (NT/HD) * 2 * nsplit floats.
 template <int HD, int NT>
-__device__ void attn_merge_heads(const AttnArgs& a, int bh0, int nheads, float* lds) {
-    const int g = threadIdx.x / HD, lt = threadIdx.x - g * HD;
+I4D_DEVINL void attn_merge_heads(const AttnArgs& a, int bh0, int nheads, float* lds) {
+    const int g = i4d_tid() / HD, lt = i4d_tid() - g * HD;
     const int bh = bh0 + g;
     const bool valid = (g < NT / HD) && (bh < nheads);
     const int ns = a.nsplit;

@@ -13,6 +13,24 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 
 #define I4D_DEVINL __device__ __forceinline__
 
+// Thread index as an opaque value: the persistent kernel runs every phase of
+// every layer in one loop, and without this the compiler hoists each phase's
+// lane arithmetic out of the layer loop and keeps all of it live at once.
+I4D_DEVINL int i4d_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Loads and stores through global-address-space pointers.  The persistent
+// kernel reads its matrix and cache pointers from a table in device memory,
+// and for such pointers the compiler would emit flat instructions, which also
+// count against the LDS wait counter: every LDS wait would then wait for the
+// weight stream as well.
+#define I4D_GLOBAL __attribute__((address_space(1)))
+template <class T> I4D_DEVINL T ld_g(const T* p) { return *(const I4D_GLOBAL T*)p; }
+template <class T> I4D_DEVINL T ld_g_nt(const T* p) { return __builtin_nontemporal_load((const I4D_GLOBAL T*)p); }
+
 // ---------------------------------------------------------------- bf16
 I4D_DEVINL float bf16_to_f32(uint16_t b) { return __uint_as_float((u32)b << 16); }
 
@@ -58,13 +76,15 @@ I4D_DEVINL u64 argmax_key(float logit, u32 idx) { return ((u64)float_order_key(l
 // own XCD's L2.  A writer makes its stores visible by waiting for their
 // completion (wait_stores) before it raises its barrier flag; no L2 writeback
 // fence is needed because none of the exchanged data sits dirty in an L2.
-I4D_DEVINL void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL void st_dev(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL void st_dev(uint16_t* p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL void st_dev(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL float ld_dev(const float* p) { return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL int ld_dev(const int* p) { return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-I4D_DEVINL u64 ld_dev(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <class T> I4D_DEVINL void st_dev_t(T* p, T v) { __hip_atomic_store((I4D_GLOBAL T*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <class T> I4D_DEVINL T ld_dev_t(const T* p) { return __hip_atomic_load((I4D_GLOBAL T*)const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+I4D_DEVINL void st_dev(float* p, float v) { st_dev_t(p, v); }
+I4D_DEVINL void st_dev(int* p, int v) { st_dev_t(p, v); }
+I4D_DEVINL void st_dev(uint16_t* p, uint16_t v) { st_dev_t(p, v); }
+I4D_DEVINL void st_dev(u64* p, u64 v) { st_dev_t(p, v); }
+I4D_DEVINL float ld_dev(const float* p) { return ld_dev_t(p); }
+I4D_DEVINL int ld_dev(const int* p) { return ld_dev_t(p); }
+I4D_DEVINL u64 ld_dev(const u64* p) { return ld_dev_t(p); }
 I4D_DEVINL f4 ld_dev4(const float* p) { return f4{ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3)}; }
 // wait until every vector-memory access of this thread (stores included) has completed
 I4D_DEVINL void wait_stores() {

@@ -26,7 +26,7 @@ namespace {
 #define I4D_WG_PER_CU 1
 #endif
 #ifndef I4D_ENABLE_PERSISTENT
-#define I4D_ENABLE_PERSISTENT 0
+#define I4D_ENABLE_PERSISTENT 1
 #endif
 constexpr int GEMV_NT = I4D_GEMV_NT;       // threads per GEMV workgroup
 constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
@@ -48,8 +48,8 @@ constexpr int GEMV_EXTRA = 64 + MAX_BATCH * 64 * 8;
 template <int FMT, int NB, int PREC>
 struct StageFn {
     char* act; const float* src; int stride; int K; int nb; const uint16_t* gain; float eps; float* red;
-    __device__ void issue(StagePre<FMT>& pre) { stage_issue<FMT, NB, GEMV_NT>(pre, src, stride, K, nb, gain); }
-    __device__ void finish(const StagePre<FMT>& pre) {
+    I4D_DEVINL void issue(StagePre<FMT>& pre) { stage_issue<FMT, NB, GEMV_NT>(pre, src, stride, K, nb, gain); }
+    I4D_DEVINL void finish(const StagePre<FMT>& pre) {
         stage_finish<FMT, NB, GEMV_NT, PREC>(pre, act, src, stride, K, nb, gain, eps, red);
     }
 };
@@ -62,7 +62,7 @@ constexpr int PREC_STD = 1, PREC_QKV = 2;
 // y[b][row] = (resid ? resid[b][row] : 0) + W x   for rows 2p, 2p+1
 struct EpiRows {
     float* y; const float* resid; int n; int nb;
-    __device__ void operator()(int, int pair, int b, float va, float vb) {
+    I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int r = 2 * pair;
         float* yr = y + (size_t)b * n;
@@ -70,17 +70,17 @@ struct EpiRows {
         st_dev(yr + r, (rr ? rr[r] : 0.f) + va);
         if (r + 1 < n) st_dev(yr + r + 1, (rr ? rr[r + 1] : 0.f) + vb);
     }
-    __device__ void end_pass(int, int, int) {}
+    I4D_DEVINL void end_pass(int, int, int) {}
 };
 
 // act[b][i] = SiLU(gate_i) * up_i
 struct EpiSwiGLU {
     float* act; int F; int nb;
-    __device__ void operator()(int, int pair, int b, float g, float u) {
+    I4D_DEVINL void operator()(int, int pair, int b, float g, float u) {
         if (b >= nb) return;
         st_dev(act + (size_t)b * F + pair, g / (1.0f + expf(-g)) * u);
     }
-    __device__ void end_pass(int, int, int) {}
+    I4D_DEVINL void end_pass(int, int, int) {}
 };
 
 // cos/sin of the RoPE angles pos[b] * base^(-2i/hd) for every batch slot and
@@ -90,7 +90,7 @@ struct EpiSwiGLU {
 template <int NB>
 I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) {
     const int half = hd >> 1;
-    for (int idx = threadIdx.x; idx < NB * half; idx += blockDim.x) {
+    for (int idx = i4d_tid(); idx < NB * half; idx += blockDim.x) {
         const int b = idx / half, i = idx - b * half;
         const double theta = pow(base, -2.0 * (double)i / (double)hd);
         const double phi = (double)max(pos_lds[b], 0) * theta;
@@ -102,7 +102,7 @@ I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) 
 struct EpiQKV {
     float* q; uint16_t* kc; uint16_t* vc; const int* pos_lds; const float2* cs;
     int cap, hq, hkv, hd, nb;
-    __device__ void operator()(int, int pair, int b, float va, float vb) {
+    I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int half = hd >> 1;
         const int npq = hq * half, npk = hkv * half;
@@ -130,7 +130,7 @@ struct EpiQKV {
             }
         }
     }
-    __device__ void end_pass(int, int, int) {}
+    I4D_DEVINL void end_pass(int, int, int) {}
 };
 
 // greedy argmax over rows 2p, 2p+1: per-thread running best key of batch slot
@@ -138,7 +138,7 @@ struct EpiQKV {
 // assignment repeats every pass)
 struct EpiArgmax {
     int n; int nb; u64 best; int bslot;
-    __device__ void operator()(int, int pair, int b, float va, float vb) {
+    I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int r = 2 * pair;
         u64 k = argmax_key(va, (u32)r);
@@ -146,12 +146,12 @@ struct EpiArgmax {
         best = k > best ? k : best;
         bslot = b;
     }
-    __device__ void end_pass(int, int, int) {}
+    I4D_DEVINL void end_pass(int, int, int) {}
 };
 
 // ============================================================== LDS carve-up for GEMV kernels
-template <int FMT, int NB>
-__host__ __device__ constexpr int gemv_part_bytes() { return (GEMV_NT / 16) * (MaxJ<NB>::v * NB * 2 + 2) * 4; }
+template <int FMT, int NB, int NT = GEMV_NT>
+__host__ __device__ constexpr int gemv_part_bytes() { return (NT / 16) * (MaxJ<NB>::v * NB * 2 + 2) * 4; }
 
 template <int FMT, int NB, int PREC>
 __host__ inline size_t gemv_lds_bytes(int K) {
@@ -161,7 +161,7 @@ __host__ inline size_t gemv_lds_bytes(int K) {
 struct GemvLds { char* act; float* part; float* red; char* extra; };
 
 template <int FMT, int NB, int PREC>
-__device__ inline GemvLds carve(char* lds, int K) {
+I4D_DEVINL GemvLds carve(char* lds, int K) {
     GemvLds l;
     l.act = lds;
     l.part = (float*)(lds + act_lds_bytes<FMT, NB, PREC>(K));
@@ -172,12 +172,12 @@ __device__ inline GemvLds carve(char* lds, int K) {
 
 // ============================================================== kernels
 __global__ void k_fill_zero(int* p, size_t n) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + i4d_tid(); i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
 __global__ void k_dequant(const uint8_t* codes, const uint16_t* scales, int n, int k, int group, int ngroups, float* out) {
     const size_t total = (size_t)n * k;
-    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + i4d_tid(); idx < total; idx += (size_t)gridDim.x * blockDim.x) {
         const size_t r = idx / k;
         const int i = (int)(idx - r * k);
         const uint8_t byte = codes[r * (size_t)(k >> 1) + (i >> 1)];
@@ -212,16 +212,16 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
     int* pos_lds = (int*)L.extra;
-    if (threadIdx.x < NB) {
+    if (i4d_tid() < NB) {
         int p = -1;
-        if ((int)threadIdx.x < nb) {
-            p = pos[threadIdx.x];
+        if (i4d_tid() < nb) {
+            p = pos[i4d_tid()];
             if (p < 0 || p > max_pos || p >= cap) {
                 if (blockIdx.x == 0) raise_status(status, I4D_DEV_BAD_POS);
                 p = -1;
             }
         }
-        pos_lds[threadIdx.x] = p;
+        pos_lds[i4d_tid()] = p;
     }
     __syncthreads();
     float2* cs = (float2*)(L.extra + 64);
@@ -241,14 +241,14 @@ __global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h,
     // workgroup best per batch slot -> this workgroup's key slots
     u64* kl = (u64*)(L.extra + GEMV_EXTRA);
     int* ks = (int*)(kl + GEMV_NT);
-    kl[threadIdx.x] = ep.best;
-    ks[threadIdx.x] = ep.bslot;
+    kl[i4d_tid()] = ep.best;
+    ks[i4d_tid()] = ep.bslot;
     __syncthreads();
-    if ((int)threadIdx.x < MAX_BATCH) {
+    if (i4d_tid() < MAX_BATCH) {
         u64 best = 0;
         for (int i = 0; i < GEMV_NT; ++i)
-            if (ks[i] == (int)threadIdx.x) best = kl[i] > best ? kl[i] : best;
-        wg_keys[(size_t)blockIdx.x * MAX_BATCH + threadIdx.x] = best;
+            if (ks[i] == i4d_tid()) best = kl[i] > best ? kl[i] : best;
+        wg_keys[(size_t)blockIdx.x * MAX_BATCH + i4d_tid()] = best;
     }
 }
 
@@ -257,17 +257,17 @@ __global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg
     __shared__ u64 red[256];
     for (int b = 0; b < nb; ++b) {
         u64 best = 0;
-        for (int w = threadIdx.x; w < nwg; w += 256) {
+        for (int w = i4d_tid(); w < nwg; w += 256) {
             const u64 k = wg_keys[(size_t)w * MAX_BATCH + b];
             best = k > best ? k : best;
         }
-        red[threadIdx.x] = best;
+        red[i4d_tid()] = best;
         __syncthreads();
         for (int s2 = 128; s2 > 0; s2 >>= 1) {
-            if ((int)threadIdx.x < s2) red[threadIdx.x] = red[threadIdx.x + s2] > red[threadIdx.x] ? red[threadIdx.x + s2] : red[threadIdx.x];
+            if (i4d_tid() < s2) red[i4d_tid()] = red[i4d_tid() + s2] > red[i4d_tid()] ? red[i4d_tid() + s2] : red[i4d_tid()];
             __syncthreads();
         }
-        if (threadIdx.x == 0) {
+        if (i4d_tid() == 0) {
             const u64 k = red[0];
             token_out[b] = (int32_t)(0xFFFFFFFFu - (u32)(k & 0xFFFFFFFFull));
             max_out[b] = float_from_order_key((u32)(k >> 32));
@@ -306,20 +306,27 @@ constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_B
 // of the next matrix-vector phase (weights do not depend on activations), so
 // HBM keeps streaming while the barrier completes.
 
-struct PLayer {
-    GemvTask qkv, wo, gu, down;
+// Per-layer device pointers: the only per-layer data the kernel reads (the
+// schedules of the four matrix-vector phases are the same for every layer and
+// travel in the kernel arguments as templates).
+struct PDesc {
+    const uint8_t* d[7];          // codes of wq wk wv wo wg wu wd
+    const uint16_t* sc[7];        // their bf16 scales
     const uint16_t* attn_norm;
     const uint16_t* ffn_norm;
     uint16_t* kc;
     uint16_t* vc;
-    float* q; float* o; float* y; float* act; float* xout;   // this layer's buffers
 };
-constexpr size_t PERS_TABLE_BYTES = (size_t)PERS_MAX_LAYERS * sizeof(PLayer);
+constexpr size_t PERS_TABLE_BYTES = (size_t)PERS_MAX_LAYERS * sizeof(PDesc);
 
 struct PArgs {
-    const PLayer* layers;
+    const PDesc* layers;
     int n_layers, batch;
     const float* x_in;
+    float* x_out;                // output of the last layer
+    GemvTask tq, to, tg, td;     // schedules of q/k/v, Wo, gate/up, down (pointers filled per layer)
+    char* lbase;                 // per-layer workspace regions: lbase + l * lstride
+    size_t lstride, off_q, off_o, off_y, off_act, off_x;
     AttnArgs attn;               // per-layer q, o, kc, vc filled in by the kernel
     const int* pos;
     int max_pos, cap, hq, hkv, hd, d_model, d_ff;
@@ -330,7 +337,29 @@ struct PArgs {
     int* status; int* flags; int* epoch;
 };
 
-constexpr int PERS_NT = 512;
+// A phase's task: the template with layer L's matrices i0 (and i1, i2).
+I4D_DEVINL GemvTask task_of(GemvTask t, const PDesc& L, int i0, int i1, int i2) {
+    t.a.data = L.d[i0]; t.a.scales = L.sc[i0];
+    if (i1 >= 0) { t.b.data = L.d[i1]; t.b.scales = L.sc[i1]; } else { t.b.data = t.a.data; t.b.scales = t.a.scales; }
+    if (i2 >= 0) { t.c.data = L.d[i2]; t.c.scales = L.sc[i2]; } else { t.c.data = t.a.data; t.c.scales = t.a.scales; }
+    return t;
+}
+
+// Copy a chunk of layer descriptors (passed by value) into the workspace
+// table; a few of these replace a host-to-device copy of the table.
+constexpr int PDESC_PER_FILL = 24;
+struct PDescChunk { PDesc e[PDESC_PER_FILL]; PDesc* dst; int count; };
+__global__ void __launch_bounds__(64) k_fill_table(PDescChunk c) {
+    const int words = c.count * (int)(sizeof(PDesc) / 8);
+    for (int i = i4d_tid(); i < words; i += 64) ((u64*)c.dst)[i] = ((const u64*)c.e)[i];
+}
+
+// One wave per SIMD: the fused kernel's live state needs more than the 256
+// registers a wave gets at two waves per SIMD; at one wave it can also use
+// the accumulation registers and needs no scratch memory.  A deeper load ring
+// keeps as many bytes in flight per compute unit as two waves would.
+constexpr int PERS_NT = 256;
+constexpr int PERS_D = 10;
 constexpr long long BAR_SPIN_LIMIT = 1 << 20;
 
 // Grid barrier on per-workgroup epoch flags.  A workgroup publishes epoch
@@ -340,20 +369,20 @@ constexpr long long BAR_SPIN_LIMIT = 1 << 20;
 // barrier of any workgroup waits again -- every wave always reaches the end.
 struct GridSync {
     int* flags; int* status; int base; int nwg;
-    __device__ void wait(int k) const {
+    I4D_DEVINL void wait(int k) const {
         const int target = base + k;
         wait_stores();
         __syncthreads();
-        if (threadIdx.x == 0) st_dev(flags + blockIdx.x, target);
-        if (threadIdx.x < 64) {
+        if (i4d_tid() == 0) st_dev(flags + blockIdx.x, target);
+        if (i4d_tid() < 64) {
             if ((ld_dev(status) & I4D_DEV_BARRIER_TIMEOUT) == 0) {
                 long long spins = 0;
                 for (;;) {
                     bool ok = true;
-                    for (int i = threadIdx.x; i < nwg; i += 64) ok = ok && (ld_dev(flags + i) - target >= 0);
+                    for (int i = i4d_tid(); i < nwg; i += 64) ok = ok && (ld_dev(flags + i) - target >= 0);
                     if (__all(ok)) break;
                     if (++spins > BAR_SPIN_LIMIT) {
-                        if (threadIdx.x == 0) raise_status(status, I4D_DEV_BARRIER_TIMEOUT);
+                        if (i4d_tid() == 0) raise_status(status, I4D_DEV_BARRIER_TIMEOUT);
                         break;
                     }
                     __builtin_amdgcn_s_sleep(2);
@@ -366,8 +395,8 @@ struct GridSync {
 
 template <int NB, class Nx>
 struct PrimeNext {
-    GemvPipe<FMT_INT4_FAST, GEMV_D>* P; const GemvTask* t; int w, nwg; bool on;
-    __device__ void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, GEMV_D>(*P, *t, w, nwg); }
+    GemvPipe<FMT_INT4_FAST, PERS_D>& P; GemvTask t; int w, nwg; bool on;
+    I4D_DEVINL void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, PERS_D>(P, t, w, nwg); }
 };
 
 template <int NB>
@@ -375,104 +404,120 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
     constexpr int FMT = FMT_INT4_FAST;
     constexpr int MJ = MaxJ<NB>::v;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int w = blockIdx.x, nwg = gridDim.x;
+    const int w0 = blockIdx.x, nwg0 = gridDim.x;
     GemvLds L;
     L.act = lds;
     L.part = (float*)(lds + A.act_bytes);
-    L.red = L.part + gemv_part_bytes<FMT, NB>() / 4;
+    L.red = L.part + gemv_part_bytes<FMT, NB, PERS_NT>() / 4;
     L.extra = (char*)(L.red + (PERS_NT / 64) * NB);
     int* pos_lds = (int*)(lds + A.pos_off);
     float2* cs = (float2*)(lds + A.pos_off + 64);
-    if (threadIdx.x < NB) {
+    if (i4d_tid() < NB) {
         int p = -1;
-        if ((int)threadIdx.x < A.batch) {
-            p = A.pos[threadIdx.x];
+        if (i4d_tid() < A.batch) {
+            p = A.pos[i4d_tid()];
             if (p < 0 || p > A.max_pos || p >= A.cap) {
-                if (w == 0) raise_status(A.status, I4D_DEV_BAD_POS);
+                if (w0 == 0) raise_status(A.status, I4D_DEV_BAD_POS);
                 p = -1;
             }
         }
-        pos_lds[threadIdx.x] = p;
+        pos_lds[i4d_tid()] = p;
     }
     __syncthreads();
     rope_table<NB>(cs, pos_lds, A.hd, A.base);
-    GridSync gs{A.flags, A.status, ld_dev(A.epoch), nwg};
+    GridSync gs{A.flags, A.status, ld_dev(A.epoch), nwg0};
     int bar = 0;
     const int items = A.batch * A.hkv * A.attn.nsplit;
     const int heads = A.batch * A.hq;
     constexpr int HPW = PERS_NT / 128;              // heads merged per workgroup per round
 
-    GemvPipe<FMT, GEMV_D> P;
-    gemv_prime<FMT, PERS_NT, GEMV_D>(P, A.layers[0].qkv, w, nwg);
+    GemvPipe<FMT, PERS_D> P;
+    gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.tq, A.layers[0], 0, 1, 2), w0, nwg0);
     for (int l = 0; l < A.n_layers; ++l) {
-        const PLayer& Ly = A.layers[l];
-        const float* xin = (l == 0) ? A.x_in : A.layers[l - 1].xout;
-        float* xout = Ly.xout;
+        // per-layer opaque copies of the launch constants: otherwise every
+        // phase's schedule arithmetic is hoisted out of the layer loop and
+        // stays live in registers across all phases
+        int w = w0, nwg = nwg0;
+        asm volatile("" : "+s"(w), "+s"(nwg));
+        const PDesc& Ly = A.layers[l];
+        const uint16_t* attn_norm = Ly.attn_norm;
+        const uint16_t* ffn_norm = Ly.ffn_norm;
+        uint16_t* kc = Ly.kc;
+        uint16_t* vc = Ly.vc;
+        char* R = A.lbase + (size_t)l * A.lstride;
+        float* q = (float*)(R + A.off_q);
+        float* o = (float*)(R + A.off_o);
+        float* y = (float*)(R + A.off_y);
+        float* act = (float*)(R + A.off_act);
+        const float* xin = (l == 0) ? A.x_in : (const float*)(R - A.lstride + A.off_x);
+        float* xout = (l + 1 == A.n_layers) ? A.x_out : (float*)(R + A.off_x);
 
         // ---- q/k/v projection, RoPE, KV append
         {
             StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, Ly.attn_norm);
-            stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, Ly.attn_norm, A.eps, L.red);
+            stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, attn_norm);
+            stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, attn_norm, A.eps, L.red);
             __syncthreads();
-            EpiQKV ep{Ly.q, Ly.kc, Ly.vc, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
+            EpiQKV ep{q, kc, vc, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
             NoNext nn;
-            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, GEMV_D, MJ>(P, Ly.qkv, w, nwg, L.act, L.part, ep, nn);
+            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
         }
         gs.wait(++bar);
         // ---- attention partials (then the Wo weights start streaming)
         {
             AttnArgs a = A.attn;
-            a.kc = Ly.kc; a.vc = Ly.vc; a.q = Ly.q;
+            asm volatile("" : "+s"(a.nsplit), "+s"(a.T), "+s"(a.hq), "+s"(a.hkv), "+s"(a.cap));
+            a.kc = kc; a.vc = vc; a.q = q;
             for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT>(a, it, lds);
-            gemv_prime<FMT, PERS_NT, GEMV_D>(P, Ly.wo, w, nwg);
+            gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
         }
         gs.wait(++bar);
         // ---- merge of the splits
         {
             AttnArgs a = A.attn;
-            a.o = Ly.o;
+            asm volatile("" : "+s"(a.nsplit), "+s"(a.hq));
+            a.o = o;
             for (int bh0 = w * HPW; bh0 < heads; bh0 += nwg * HPW) attn_merge_heads<128, PERS_NT>(a, bh0, heads, (float*)lds);
         }
         gs.wait(++bar);
         // ---- output projection + residual
         {
             StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, Ly.o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
+            stage_issue<FMT, NB, PERS_NT>(pre, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
             __syncthreads();
-            EpiRows ep{Ly.y, xin, A.d_model, A.batch};
-            PrimeNext<NB, void> nx{&P, &Ly.gu, w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.wo, w, nwg, L.act, L.part, ep, nx);
+            EpiRows ep{y, xin, A.d_model, A.batch};
+            PrimeNext<NB, void> nx{P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg, L.act, L.part, ep, nx);
         }
         gs.wait(++bar);
         // ---- gate/up projection + SwiGLU
         {
             StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, Ly.y, A.d_model, A.d_model, A.batch, Ly.ffn_norm);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.y, A.d_model, A.d_model, A.batch, Ly.ffn_norm, A.eps, L.red);
+            stage_issue<FMT, NB, PERS_NT>(pre, y, A.d_model, A.d_model, A.batch, ffn_norm);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, y, A.d_model, A.d_model, A.batch, ffn_norm, A.eps, L.red);
             __syncthreads();
-            EpiSwiGLU ep{Ly.act, A.d_ff, A.batch};
-            PrimeNext<NB, void> nx{&P, &Ly.down, w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.gu, w, nwg, L.act, L.part, ep, nx);
+            EpiSwiGLU ep{act, A.d_ff, A.batch};
+            PrimeNext<NB, void> nx{P, task_of(A.td, Ly, 6, -1, -1), w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, L.act, L.part, ep, nx);
         }
         gs.wait(++bar);
         // ---- down projection + residual (then the next layer's q/k/v weights start streaming)
         {
             StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, Ly.act, A.d_ff, A.d_ff, A.batch, nullptr);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, Ly.act, A.d_ff, A.d_ff, A.batch, nullptr, 0.f, L.red);
+            stage_issue<FMT, NB, PERS_NT>(pre, act, A.d_ff, A.d_ff, A.batch, nullptr);
+            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, act, A.d_ff, A.d_ff, A.batch, nullptr, 0.f, L.red);
             __syncthreads();
-            EpiRows ep{xout, Ly.y, A.d_model, A.batch};
+            EpiRows ep{xout, y, A.d_model, A.batch};
             const bool more = l + 1 < A.n_layers;
-            PrimeNext<NB, void> nx{&P, more ? &A.layers[l + 1].qkv : &Ly.qkv, w, nwg, more};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, GEMV_D, MJ>(P, Ly.down, w, nwg, L.act, L.part, ep, nx);
+            PrimeNext<NB, void> nx{P, task_of(A.tq, more ? A.layers[l + 1] : Ly, 0, 1, 2), w, nwg, more};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.td, Ly, 6, -1, -1), w, nwg, L.act, L.part, ep, nx);
         }
         if (l + 1 < A.n_layers) gs.wait(++bar);
     }
     // every workgroup read the epoch at its start before any passed the first
     // barrier, so the next launch's epoch can be published now
-    if (w == 0 && threadIdx.x == 0) st_dev(A.epoch, gs.base + bar);
+    if (w0 == 0 && i4d_tid() == 0) st_dev(A.epoch, gs.base + bar);
 }
 
 // ============================================================== host helpers
@@ -618,11 +663,11 @@ int maxj_of(int nb) { return nb <= 2 ? MaxJ<1>::v : MaxJ<4>::v; }
 
 // Fill pass geometry: at most `cap_pairs` pairs per pass (0: no cap), and never
 // more pairs per workgroup than keeps every slot within MAXJ runs.
-void plan_passes(GemvTask& t, int fmt, int nb, int nwg, int cap_pairs) {
+void plan_passes(GemvTask& t, int fmt, int nb, int nwg, int cap_pairs, int nt = GEMV_NT) {
     const int S = (t.k + unit_w(fmt) - 1) / unit_w(fmt);
     const int maxj = maxj_of(nb);
     int ppw = (t.total_pairs + nwg - 1) / nwg;
-    while (ppw > 1 && gemv_max_runs(ppw, S, GEMV_NT / 64) > maxj) --ppw;
+    while (ppw > 1 && gemv_max_runs(ppw, S, nt / 64) > maxj) --ppw;
     long long pp = (long long)ppw * nwg;
     if (cap_pairs > 0 && pp > cap_pairs) pp = cap_pairs;
     if (pp > t.total_pairs) pp = t.total_pairs;
@@ -802,7 +847,7 @@ size_t persistent_lds(const i4d_config* c, int nsplit) {
     const int D = c->d_model, qw = c->n_q_heads * c->head_dim, F = c->d_ff;
     const int act = std::max(std::max(act_lds_bytes<FMT, NB, PREC_QKV>(D), act_lds_bytes<FMT, NB, PREC_STD>(qw)),
                              act_lds_bytes<FMT, NB, PREC_STD>(F));
-    const size_t gemv = (size_t)act + gemv_part_bytes<FMT, NB>() + (PERS_NT / 64) * NB * 4 + 256;
+    const size_t gemv = (size_t)act + gemv_part_bytes<FMT, NB, PERS_NT>() + (PERS_NT / 64) * NB * 4 + 256;
     const size_t attn = attn_lds_bytes<128, PERS_NT>();
     const size_t merge = (size_t)(PERS_NT / 128) * 2 * nsplit * 4;
     return align256(std::max(std::max(gemv, attn), merge)) + GEMV_EXTRA;
@@ -811,12 +856,12 @@ size_t persistent_lds(const i4d_config* c, int nsplit) {
 bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int B) {
     if (c->head_dim != 128 || B > 4 || n_layers > PERS_MAX_LAYERS) return false;
     const int nwg = num_cus();
-    if (nwg > PERS_MAX_WG || GEMV_NT != PERS_NT) return false;
+    if (nwg > PERS_MAX_WG) return false;
     for (int l = 0; l < n_layers; ++l) {
         const i4d_layer& L = layers[l];
         const i4d_mat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
         for (int i = 0; i < 7; ++i)
-            if (m[i]->dtype != I4D_WEIGHT_INT4 || pick_fmt(*m[i]) != FMT_INT4_FAST) return false;
+            if (m[i]->dtype != I4D_WEIGHT_INT4 || pick_fmt(*m[i]) != FMT_INT4_FAST || m[i]->group != layers[0].wq.group) return false;
         if (kv[l].capacity != kv[0].capacity) return false;
     }
     return true;
@@ -826,6 +871,11 @@ template <int NB>
 int launch_persistent_t(PArgs& A, int nwg, size_t lds, hipStream_t s) {
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_decode_persistent<NB>, lds) != hipSuccess) return I4D_EHIP;
+    // The cooperative kernel must run entirely in registers and LDS: a build
+    // that gives it a private (scratch) segment is not launched.
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, (const void*)k_decode_persistent<NB>) != hipSuccess) return I4D_EHIP;
+    if (fa.localSizeBytes != 0) return I4D_EUNSUPPORTED;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_persistent<NB>, PERS_NT, lds) != hipSuccess)
         return I4D_EHIP;
@@ -840,36 +890,46 @@ int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* lay
                          const i4d_kv* kv, const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
     const int nb = nb_slot(B), nwg = num_cus();
     const int hd = c->head_dim;
-    std::vector<PLayer> tab((size_t)n_layers);
-    for (int l = 0; l < n_layers; ++l) {
-        const i4d_layer& Ls = layers[l];
-        PLayer& P = tab[(size_t)l];
-        P.qkv = make_task(KIND_QKV, &Ls.wq, &Ls.wk, &Ls.wv, hd);
-        P.wo = make_task(KIND_ADJ, &Ls.wo, nullptr, nullptr, hd);
-        P.gu = make_task(KIND_TWO, &Ls.wg, &Ls.wu, nullptr, hd);
-        P.down = make_task(KIND_ADJ, &Ls.wd, nullptr, nullptr, hd);
-        plan_passes(P.qkv, FMT_INT4_FAST, nb, nwg, 0);
-        plan_passes(P.wo, FMT_INT4_FAST, nb, nwg, 0);
-        plan_passes(P.gu, FMT_INT4_FAST, nb, nwg, 0);
-        plan_passes(P.down, FMT_INT4_FAST, nb, nwg, 0);
-        P.attn_norm = Ls.attn_norm;
-        P.ffn_norm = Ls.ffn_norm;
-        P.kc = kv[l].k;
-        P.vc = kv[l].v;
-        char* R = ws + W.layer0 + (size_t)l * W.layer_stride;
-        P.q = (float*)(R + W.q); P.o = (float*)(R + W.o); P.y = (float*)(R + W.y); P.act = (float*)(R + W.act);
-        P.xout = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
+    // the layer table goes to the workspace as by-value kernel arguments of a
+    // few copy kernels (no host buffer has to outlive this call)
+    PDesc* table = (PDesc*)(ws + W.table);
+    for (int l0 = 0; l0 < n_layers; l0 += PDESC_PER_FILL) {
+        PDescChunk ch;
+        memset(&ch, 0, sizeof(ch));
+        ch.count = std::min(PDESC_PER_FILL, n_layers - l0);
+        ch.dst = table + l0;
+        for (int i = 0; i < ch.count; ++i) {
+            const i4d_layer& Ls = layers[l0 + i];
+            const i4d_mat* m[7] = {&Ls.wq, &Ls.wk, &Ls.wv, &Ls.wo, &Ls.wg, &Ls.wu, &Ls.wd};
+            PDesc& d = ch.e[i];
+            for (int k = 0; k < 7; ++k) { d.d[k] = (const uint8_t*)m[k]->data; d.sc[k] = (const uint16_t*)m[k]->scales; }
+            d.attn_norm = Ls.attn_norm;
+            d.ffn_norm = Ls.ffn_norm;
+            d.kc = kv[l0 + i].k;
+            d.vc = kv[l0 + i].v;
+        }
+        hipLaunchKernelGGL(k_fill_table, dim3(1), dim3(64), 0, s, ch);
     }
-    // pageable source: the copy is staged before hipMemcpyAsync returns
-    if (hipMemcpyAsync(ws + W.table, tab.data(), tab.size() * sizeof(PLayer), hipMemcpyHostToDevice, s) != hipSuccess)
-        return I4D_EHIP;
 
     PArgs A;
     memset(&A, 0, sizeof(A));
-    A.layers = (const PLayer*)(ws + W.table);
+    A.layers = table;
     A.n_layers = n_layers;
     A.batch = B;
     A.x_in = x_in;
+    A.x_out = x_out;
+    const i4d_layer& L0 = layers[0];
+    A.tq = make_task(KIND_QKV, &L0.wq, &L0.wk, &L0.wv, hd);
+    A.to = make_task(KIND_ADJ, &L0.wo, nullptr, nullptr, hd);
+    A.tg = make_task(KIND_TWO, &L0.wg, &L0.wu, nullptr, hd);
+    A.td = make_task(KIND_ADJ, &L0.wd, nullptr, nullptr, hd);
+    plan_passes(A.tq, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
+    plan_passes(A.to, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
+    plan_passes(A.tg, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
+    plan_passes(A.td, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
+    A.lbase = ws + W.layer0;
+    A.lstride = W.layer_stride;
+    A.off_q = W.q; A.off_o = W.o; A.off_y = W.y; A.off_act = W.act; A.off_x = W.x;
     AttnArgs& a = A.attn;
     a.q = nullptr; a.pos = pos; a.cap = kv[0].capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B;
     a.max_pos = max_pos;
@@ -990,9 +1050,6 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
     if (cfg->exec_mode == 2) {
-        // The persistent kernel took a GPU fault on its first launch in a test
-        // process after a change to its LDS layout; it stays switched off
-        // until the cause is shown.
         if (!I4D_ENABLE_PERSISTENT) return I4D_EUNSUPPORTED;
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
         return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);

@@ -119,7 +119,7 @@ template <> struct Unit<FMT_INT4_GEN>  { u32 a, b; u32 sa, sb; };
 template <> struct Unit<FMT_BF16_FAST> { u32x4 a, b; };
 template <> struct Unit<FMT_BF16_GEN>  { u32 a, b; };
 
-template <class T> I4D_DEVINL T nt_load(const T* p) { return __builtin_nontemporal_load(p); }
+template <class T> I4D_DEVINL T nt_load(const T* p) { return ld_g_nt(p); }
 
 // Issue the loads of one unit.  `valid` = the unit exists; otherwise the
 // loads read a fixed in-bounds address (the first bytes of the task's first
@@ -145,8 +145,8 @@ I4D_DEVINL void load_unit(Unit<FMT>& u, const RowPtrs& rp, int seg, int lane16, 
             u.a = nt_load((const u32*)pa);
             u.b = nt_load((const u32*)pb);
         }
-        u.sa = *qa;
-        u.sb = *qb;
+        u.sa = ld_g(qa);
+        u.sb = ld_g(qb);
     } else {
         const size_t off = (size_t)k0 * 2;
         const uint8_t* pa = valid ? rp.pa + off : dummy;
@@ -279,11 +279,11 @@ I4D_DEVINL void stage_load_chunk(f4 (&xv)[StagePre<FMT>::NV], u32x4 (&gv)[FmtT<F
     // before it was written (so no L2 holds a stale copy of it)
     const f4* xp = (const f4*)(src + (size_t)min(b, nb - 1) * src_stride + k0);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) xv[i] = xp[i];
+    for (int i = 0; i < NV; ++i) xv[i] = ld_g(xp + i);
     if (gain != nullptr) {
         constexpr int NG = FmtT<FMT>::INT4 ? NV / 2 : 1;
 #pragma unroll
-        for (int i = 0; i < NG; ++i) gv[i] = ((const u32x4*)(gain + k0))[i];
+        for (int i = 0; i < NG; ++i) gv[i] = ld_g((const u32x4*)(gain + k0) + i);
     }
 }
 
@@ -292,7 +292,7 @@ I4D_DEVINL void stage_issue(StagePre<FMT>& pre, const float* src, int src_stride
     const int nidx = NB * (K / stage_chunk_w<FMT>());
 #pragma unroll
     for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
-        const int idx = min((int)threadIdx.x + pc * NT, nidx - 1);     // clamped: loads are unconditional
+        const int idx = min(i4d_tid() + pc * NT, nidx - 1);     // clamped: loads are unconditional
         stage_load_chunk<FMT, NB, NT>(pre.x[pc], pre.g[pc], src, src_stride, K, nb, gain, idx);
     }
 }
@@ -361,9 +361,9 @@ I4D_DEVINL void stage_write_chunk(char* act_lds, const f4 (&xv)[StagePre<FMT>::N
 }
 
 template <int FMT, int NB, int NT, int PREC>
-__device__ void stage_finish(const StagePre<FMT>& pre, char* act_lds, const float* src, int src_stride, int K, int nb,
+I4D_DEVINL void stage_finish(const StagePre<FMT>& pre, char* act_lds, const float* src, int src_stride, int K, int nb,
                              const uint16_t* gain, float eps, float* red) {
-    const int tid = threadIdx.x;
+    const int tid = i4d_tid();
     const int nidx = NB * (K / stage_chunk_w<FMT>());
     float rs[NB];
 #pragma unroll
@@ -495,7 +495,7 @@ struct GemvPipe {
 template <int FMT, int NT, int D>
 I4D_DEVINL void gemv_prime(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg) {
     constexpr int NW = NT / 64;
-    const int slot = threadIdx.x >> 4, lane16 = threadIdx.x & 15;
+    const int slot = i4d_tid() >> 4, lane16 = i4d_tid() & 15;
     const int S = (t.k + FmtT<FMT>::UNIT_W - 1) / FmtT<FMT>::UNIT_W;
     pass_pairs_of(t, 0, w, nwg, P.q0, P.q1);
     slot_range<NW>((P.q1 - P.q0) * S, slot, P.u0, P.u1, P.n_it);
@@ -504,7 +504,7 @@ I4D_DEVINL void gemv_prime(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nw
     for (int i = 0; i < D; ++i) cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
 }
 
-struct NoNext { __device__ void operator()() {} };
+struct NoNext { I4D_DEVINL void operator()() {} };
 
 // Run every pass of task `t` for workgroup w, the ring P already primed
 // for t.  Activations must already be staged in act_lds.  For each pass:
@@ -514,11 +514,11 @@ struct NoNext { __device__ void operator()() {} };
 // following phase; its loads are then in flight during this epilogue.
 // LDS: act_lds (staged activations), part_lds (NS*MAXJ*NB*2 floats + 2*NS ints).
 template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Epi, class Next>
-__device__ void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg, const char* act_lds, float* part_lds,
+I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg, const char* act_lds, float* part_lds,
                             Epi& epi, Next& next) {
     constexpr int NW = NT / 64, NS = NT / 16;
     typedef FmtT<FMT> F;
-    const int tid = threadIdx.x;
+    const int tid = i4d_tid();
     const int slot = tid >> 4, lane16 = tid & 15;
     const int S = (t.k + F::UNIT_W - 1) / F::UNIT_W;
     int* slot_info = (int*)(part_lds + NS * MAXJ * NB * 2);     // [NS][2]: first local pair, runs
@@ -557,6 +557,9 @@ __device__ void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
                     }
                 }
                 cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+                // keep each unit's LDS reads next to their use: hoisting the
+                // activation reads of later units costs registers, not time
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (seg != 0) {      // a partially covered last pair
@@ -622,7 +625,7 @@ __device__ void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
 // the weight ring, then the activations are staged (waiting only for their own
 // loads), then every pass runs.
 template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Stage, class Epi>
-__device__ void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
+I4D_DEVINL void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
     StagePre<FMT> pre;
     stage.issue(pre);
     GemvPipe<FMT, D> P;

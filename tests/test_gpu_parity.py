@@ -273,12 +273,7 @@ FAST_SHAPE = synth.SHAPES["tiny"].with_(name="fast", d_model=512, n_q_heads=4, n
                                         d_ff=1024, group=128, rope_base=1e6)
 
 
-PERSISTENT_OFF = ("the persistent kernel took a GPU fault on its first launch after an LDS-layout change; "
-                  "the library returns I4D_EUNSUPPORTED for exec_mode 2 until the cause is shown")
-
-
-@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES,
-                                       pytest.param(B.EXEC_PERSISTENT, marks=pytest.mark.skip(reason=PERSISTENT_OFF))])
+@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_PERSISTENT])
 def test_multi_step_decode_matches_oracle(exec_mode):
     _print_case("multi-step decode", exec_mode)
     outs, kv_gpu, ref_outs, ref_caches, status = _multi_step(FAST_SHAPE, 2, 120, 3, exec_mode)
@@ -292,7 +287,6 @@ def test_multi_step_decode_matches_oracle(exec_mode):
                                   what=f"layer {l} {name} slot {120 + s}")
 
 
-@pytest.mark.skip(reason=PERSISTENT_OFF)
 def test_persistent_kernel_is_bit_identical_to_phase_launches():
     _print_case("persistent vs phases")
     a = _multi_step(FAST_SHAPE, 3, 200, 3, B.EXEC_PHASES, seed=23)

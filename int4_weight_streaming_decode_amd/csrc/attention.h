@@ -3,22 +3,34 @@
 // One work item = (sequence b, KV head j, split s of the key axis).  The item's
 // workgroup serves all G = Hq/Hkv query heads of KV head j from one read of the
 // K/V tiles (Unsloth article 二.2: query heads address their KV head by index,
-// never by a broadcast copy).  Keys are processed in 16-key subtiles, one
-// subtile per wave at a time, with an online softmax (Roofline reply 四:
-// FlashAttention-style tiling; the score row never reaches HBM).  Each item
-// leaves a partial (running max m, running sum l, unnormalised output O); a
-// second kernel merges the splits of each query head in split order, so the
-// result is bit-reproducible.  Workgroups never wait on or signal each other:
-// a device-scope fence per workgroup (what a last-arriver merge needs for the
-// partials to be visible across XCDs) writes back the XCD's L2 and serialises,
-// which costs far more than the kernel boundary does.
+// never by a broadcast copy).  Keys are processed in 16-key subtiles with an
+// online softmax (Roofline reply 四: FlashAttention-style tiling; the score row
+// never reaches HBM).  Subtile st of an item belongs to wave st % NW.
+//
+// Loads.  A wave issues the K/V loads of all its subtiles of a round (up to
+// NSW of them) before computing any, so an item costs about one memory round
+// trip; the persistent kernel issues round 0 before the grid barrier that
+// precedes attention, because the cached history does not depend on the q/k/v
+// phase.  The one key that does -- the new token's, at position pos[b] -- is
+// read from a small side buffer that the q/k/v epilogue writes next to the
+// cache, and patched into the registers after the barrier; cache lines loaded
+// before the barrier may hold the old contents of that slot.
+//
+// Merge.  Each item leaves a partial (running max m, running sum l,
+// unnormalised O); the last of the nsplit workgroups of (b, j) to finish
+// (an arrival counter) merges the splits in split order, so the result is
+// bit-reproducible.  Partials are written through to memory and the counter is
+// incremented only after those stores completed, so the merging workgroup sees
+// every split; no cache-writeback fence is needed.
 //
 // MFMA mapping (16x16x16 bf16, fp32 accumulate):
 //   scores^T[key][head] = K_tile[key][dims] x q^T[dims][head]  (M = 16 keys,
 //       N = 16 heads (G used), K = 16 dims per instruction).  Lane (r, g)
-//       (r = lane % 16, g = lane / 16) feeds key r, dims 32g + 4kb + i of its
-//       own 64 contiguous bytes of the K row, and receives the scores of head r
-//       for keys 4g..4g+3 -- which is exactly the A-operand layout of
+//       (r = lane % 16, g = lane / 16) feeds key r, dims 32(kb/2) + 8g +
+//       4(kb%2) + i (for each 16-byte load the four lanes of key r read 64
+//       contiguous bytes of its row; q^T uses the same dim order), and
+//       receives the scores of head r for keys 4g..4g+3 -- which is exactly the
+//       A-operand layout of
 //   O[head][dim] += P[head][key] x V[key][dim]  (M = heads, N = 16 dims, K = 16
 //       keys).  V is cached transposed ([dim][position]) so that lane (r, g)
 //       reads keys 4g..4g+3 of dimension 16nt + r as one 8-byte load.
@@ -32,15 +44,17 @@ struct AttnArgs {
     const float* q;          // [B][Hq][hd] fp32
     const uint16_t* kc;      // [B][Hkv][cap][hd]
     const uint16_t* vc;      // [B][Hkv][hd][cap]
+    const uint16_t* kvn;     // [B][Hkv][2][hd]: the new token's bf16 k (row 0) and v (row 1)
     const int* pos;          // [B]
     int cap, hq, hkv, batch, max_pos;
     int nsplit;              // splits per (b, j)
     int T;                   // keys per split (multiple of 4)
-    int nsplit_max;          // partial-buffer stride
+    int pstride;             // partial-buffer stride per head (multiple of 32 splits)
     float qscale;            // log2(e) / sqrt(hd)
-    float* pm; float* pl;    // [B][Hq][nsplit_max]
-    float* po;               // [B][Hq][nsplit_max][hd]
-    float* o;                // [B][Hq][hd] fp32 (merge kernel output)
+    float* pm; float* pl;    // [B][Hq][pstride]
+    float* po;               // [B][Hq][pstride][hd]
+    int* cnt;                // [B][Hkv] arrival counters, zero between calls
+    float* o;                // [B][Hq][hd] fp32 merged output
 };
 
 I4D_DEVINL u32x4 nt_load_k(const u32x4* p) { return ld_g_nt(p); }
@@ -57,34 +71,133 @@ I4D_DEVINL int keys_of(const AttnArgs& a, int b) {
     return (p >= 0 && p <= a.max_pos && p < a.cap) ? p + 1 : 0;
 }
 
-// LDS bytes used by attn_item with NT threads.
+// LDS bytes used by the attention of one workgroup of NT threads: per-wave
+// partial states, then the q operand (the merge reuses the per-wave area).
 template <int HD, int NT>
 __host__ __device__ constexpr int attn_lds_bytes() { return (NT / 64) * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8; }
 
-template <int HD, int NT>
-I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
-    constexpr int NW = NT / 64, NKB = HD / 16, DPL = HD / 4;   // DPL: dims per lane group
-    const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int G = a.hq / a.hkv;
-    const int s = item % a.nsplit;
-    const int j = (item / a.nsplit) % a.hkv;
-    const int b = item / (a.nsplit * a.hkv);
-    const int nk = keys_of(a, b);
-    const int t_s = s * a.T;
-    const int t_e = min(t_s + a.T, nk);
-    const int nsub = (t_e > t_s) ? (t_e - t_s + 15) / 16 : 0;
+// Subtiles a wave holds in registers per round.
+template <int NT> struct AttnNsw { static constexpr int v = NT >= 512 ? 3 : 5; };
 
-    // q^T operand (hi, lo) for head r of this group, dims DPL*g + 4kb + i, kept
-    // in LDS (every wave of the workgroup uses the same operands): [kb][lane]
-    // s4 pairs after the per-wave areas.  Vector loads from a clamped head,
-    // zeroed for padding heads r >= G.
+struct AttnGeo {
+    int b, j, s, t_s, t_e, nsub, kpos;     // kpos: the new key's position, -1 if none
+};
+
+I4D_DEVINL AttnGeo attn_geo(const AttnArgs& a, int item) {
+    AttnGeo g;
+    g.s = item % a.nsplit;
+    g.j = (item / a.nsplit) % a.hkv;
+    g.b = item / (a.nsplit * a.hkv);
+    const int nk = keys_of(a, g.b);
+    g.t_s = g.s * a.T;
+    g.t_e = min(g.t_s + a.T, nk);
+    g.nsub = (g.t_e > g.t_s) ? (g.t_e - g.t_s + 15) / 16 : 0;
+    g.kpos = nk - 1;
+    return g;
+}
+
+template <int HD, int NSW>
+struct AttnRegs {
+    u32x4 k[NSW][HD / 32];
+    u32x2 v[NSW][HD / 16];
+};
+
+// K rows (key t0 + r, dims DPL*g ..) and V^T runs (dim 16nt + r, keys t0 + 4g ..
+// t0 + 4g + 3) of subtile st.  Addresses are clamped into the cache so every
+// load is issued; keys outside the item are masked when the subtile is used.
+template <int HD>
+I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, u32x4 (&kr)[HD / 32], u32x2 (&vr)[HD / 16]) {
+    constexpr int NKB = HD / 16, DPL = HD / 4;
+    const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
+    const uint16_t* kbase = a.kc + (size_t)(g.b * a.hkv + g.j) * a.cap * HD;
+    const uint16_t* vbase = a.vc + (size_t)(g.b * a.hkv + g.j) * HD * a.cap;
+    const int t0 = g.t_s + 16 * st;
+    const int tk = min(t0 + r, a.cap - 1);
+    const uint16_t* kp = kbase + (size_t)tk * HD + 8 * gq;
+#pragma unroll
+    for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = nt_load_k((const u32x4*)(kp + 32 * mm));
+    const int tv = min(t0 + 4 * gq, a.cap - 4);
+#pragma unroll
+    for (int nt = 0; nt < NKB; ++nt) vr[nt] = nt_load_v((const u32x2*)(vbase + (size_t)(16 * nt + r) * a.cap + tv));
+}
+
+// Issue the loads of round r of this wave.  Slots past the item re-read the
+// wave's first subtile (already requested: no extra HBM traffic), so the loads
+// stay unconditional and the compiler can count them exactly.
+template <int HD, int NT, int NSW>
+I4D_DEVINL void attn_load_round(const AttnArgs& a, const AttnGeo& g, int rnd, AttnRegs<HD, NSW>& R) {
+    constexpr int NW = NT / 64;
+    const int wave = i4d_tid() >> 6;
+#pragma unroll
+    for (int i = 0; i < NSW; ++i) {
+        int st = (rnd * NSW + i) * NW + wave;
+        if (st >= g.nsub) st = (rnd * NSW) * NW + wave;
+        attn_load_sub<HD>(a, g, st, R.k[i], R.v[i]);
+    }
+}
+
+// Replace the new key's K row and V column in subtile st's registers with the
+// side-buffer values (the cached copies may predate this step's append).
+template <int HD>
+I4D_DEVINL void attn_patch_new(const AttnArgs& a, const AttnGeo& g, int st, u32x4 (&kr)[HD / 32], u32x2 (&vr)[HD / 16]) {
+    constexpr int NKB = HD / 16, DPL = HD / 4;
+    const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
+    const int t0 = g.t_s + 16 * st;
+    const uint16_t* kn = a.kvn + (size_t)(g.b * a.hkv + g.j) * 2 * HD;
+    if (t0 + r == g.kpos) {
+#pragma unroll
+        for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = ld_g((const u32x4*)(kn + 32 * mm + 8 * gq));
+    }
+    const int e = g.kpos - (t0 + 4 * gq);          // index of the new key in this lane's run of 4
+    if (e >= 0 && e < 4 && t0 + 4 * gq <= a.cap - 4) {
+#pragma unroll
+        for (int nt = 0; nt < NKB; ++nt) {
+            const u32 nv = (u32)ld_g(kn + HD + 16 * nt + r);
+            u32 lo = vr[nt].x, hi = vr[nt].y;
+            if (e == 0) lo = (lo & 0xFFFF0000u) | nv;
+            else if (e == 1) lo = (lo & 0x0000FFFFu) | (nv << 16);
+            else if (e == 2) hi = (hi & 0xFFFF0000u) | nv;
+            else hi = (hi & 0x0000FFFFu) | (nv << 16);
+            vr[nt] = u32x2{lo, hi};
+        }
+    }
+}
+
+// The whole item: optional round-0 registers already loaded (pre = true),
+// compute, per-item partial, and the merge by the last split to arrive.
+template <int HD, int NT, int NSW>
+I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, NSW>& R, bool pre) {
+    constexpr int NW = NT / 64, NKB = HD / 16, DPL = HD / 4;
+    const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+    const int G = a.hq / a.hkv;
+    const AttnGeo g = attn_geo(a, item);
+    const int nsub = g.nsub, t_e = g.t_e;
+
+    // the subtile holding the new key gets the side-buffer values in the round
+    // that loads it (whichever round: a line loaded earlier may be stale)
+    auto patch_round = [&](int rnd) {
+        if (a.kvn == nullptr || g.kpos < g.t_s || g.kpos >= t_e) return;
+        const int stp = (g.kpos - g.t_s) / 16;
+        if (stp % NW != wave || (stp / NW) / NSW != rnd) return;
+#pragma unroll
+        for (int i = 0; i < NSW; ++i)
+            if (i == (stp / NW) % NSW) attn_patch_new<HD>(a, g, stp, R.k[i], R.v[i]);
+    };
+    // q first: its loads then only wait for themselves, not for the K/V stream
+    // issued after them.  q^T operand (hi, lo) for head r of this group, dims
+    // in the K-row order above, kept in LDS after the per-wave areas (every
+    // wave uses the same operands).
+    f4 qv[NKB];
+    if (wave == 0) {
+        const float* qrow = a.q + (size_t)(g.b * a.hq + g.j * G + min(r, G - 1)) * HD + 8 * gq;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) qv[kb] = ld_g((const f4*)(qrow + 32 * (kb >> 1) + 4 * (kb & 1)));
+    }
+    if (!pre) attn_load_round<HD, NT, NSW>(a, g, 0, R);
+    patch_round(0);
     s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
     if (wave == 0) {
-        const f4* qp = (const f4*)(a.q + ((size_t)(b * a.hq + j * G + min(r, G - 1)) * HD) + DPL * g);
-        f4 qv[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qv[kb] = qp[kb];    // this layer's q, first read after it was written
         const float qs = (r < G) ? a.qscale : 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -101,35 +214,17 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
     }
     __syncthreads();
 
-    const uint16_t* kbase = a.kc + (size_t)(b * a.hkv + j) * a.cap * HD;
-    const uint16_t* vbase = a.vc + (size_t)(b * a.hkv + j) * HD * a.cap;
-
     float m = -INFINITY, lsum = 0.f;
     f4 O[NKB];
 #pragma unroll
     for (int nt = 0; nt < NKB; ++nt) O[nt] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // One 16-key subtile: K rows (key t0 + r, dims DPL*g ..) and V^T runs
-    // (dim 16nt + r, keys t0 + 4g .. t0 + 4g + 3).  Addresses are clamped into
-    // the cache so every load is issued unconditionally; keys outside
-    // [t_s, t_e) are zeroed when the subtile is consumed.
-    auto load_sub = [&](int st, u32x4 (&kr)[NKB / 2], u32x2 (&vr)[NKB]) {
-        const int t0 = t_s + 16 * st;
-        const int tk = min(t0 + r, a.cap - 1);
-        const u32x4* kp = (const u32x4*)(kbase + (size_t)tk * HD + DPL * g);
-#pragma unroll
-        for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = nt_load_k(kp + mm);
-        const int tv = min(t0 + 4 * g, a.cap - 4);
-#pragma unroll
-        for (int nt = 0; nt < NKB; ++nt) vr[nt] = nt_load_v((const u32x2*)(vbase + (size_t)(16 * nt + r) * a.cap + tv));
-    };
-
     auto compute_sub = [&](int st, const u32x4 (&kr)[NKB / 2], const u32x2 (&vr)[NKB]) {
-        const int t0 = t_s + 16 * st;
-        const int tv = t0 + 4 * g;
+        const int t0 = g.t_s + 16 * st;
+        const int tv = t0 + 4 * gq;
         const bool kvalid = t0 + r < t_e;               // this lane's K row
         const int vvalid = t_e - tv;                    // keys of this lane's V run in range
-        // scores^T for keys 4g..4g+3 of head r
+        // scores^T for keys 4gq..4gq+3 of head r
         f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -153,10 +248,10 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
         for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - mnew);
         lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
         m = mnew;
-        // rescale O rows (heads 4g + i) by their alpha
+        // rescale O rows (heads 4gq + i) by their alpha
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float ai = shfl_f(alpha, 4 * g + i);
+            const float ai = shfl_f(alpha, 4 * gq + i);
 #pragma unroll
             for (int nt = 0; nt < NKB; ++nt) O[nt][i] *= ai;
         }
@@ -178,23 +273,14 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
         }
     };
 
-    // Two subtiles in flight per wave.  Each "prefetch; compute" block issues
-    // its loads unconditionally, so the wait before a compute only covers the
-    // buffer it reads; the last subtile of the wave is computed on its own.
-    u32x4 kr0[NKB / 2], kr1[NKB / 2];
-    u32x2 vr0[NKB], vr1[NKB];
-    int st = wave;
-    if (st < nsub) {
-        load_sub(st, kr0, vr0);
-        for (;;) {
-            if (st + NW >= nsub) { compute_sub(st, kr0, vr0); break; }
-            load_sub(st + NW, kr1, vr1);
-            compute_sub(st, kr0, vr0);
-            st += NW;
-            if (st + NW >= nsub) { compute_sub(st, kr1, vr1); break; }
-            load_sub(st + NW, kr0, vr0);
-            compute_sub(st, kr1, vr1);
-            st += NW;
+    // rounds of NSW subtiles per wave: round 0 is in R already
+    const int nround = (nsub + NW * NSW - 1) / (NW * NSW);
+    for (int rnd = 0; rnd < nround; ++rnd) {
+        if (rnd > 0) { attn_load_round<HD, NT, NSW>(a, g, rnd, R); patch_round(rnd); }
+#pragma unroll
+        for (int i = 0; i < NSW; ++i) {
+            const int st = (rnd * NSW + i) * NW + wave;
+            if (st < nsub) compute_sub(st, R.k[i], R.v[i]);
         }
     }
 
@@ -203,15 +289,15 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
     float lt = lsum;
     lt += shfl_xor_f(lt, 16);
     lt += shfl_xor_f(lt, 32);
-    if (g == 0) { wbase[r] = m; wbase[16 + r] = lt; }
+    if (gq == 0) { wbase[r] = m; wbase[16 + r] = lt; }
 #pragma unroll
     for (int nt = 0; nt < NKB; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wbase[32 + (4 * g + i) * HD + 16 * nt + r] = O[nt][i];
+        for (int i = 0; i < 4; ++i) wbase[32 + (4 * gq + i) * HD + 16 * nt + r] = O[nt][i];
     __syncthreads();
 
-    // combine the waves; write this split's partial
-    const size_t hrow0 = (size_t)(b * a.hq + j * G);
+    // combine the waves; write this split's partial (through to memory)
+    const size_t hrow0 = (size_t)(g.b * a.hq + g.j * G);
     for (int idx = tid; idx < G * HD; idx += NT) {
         const int h = idx / HD, d = idx - h * HD;
         const float* lw = (const float*)lds;
@@ -226,46 +312,96 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds) {
                 L = fmaf(wb[16 + h], e, L);
             }
         }
-        const size_t pidx = (hrow0 + h) * a.nsplit_max + s;
+        const size_t pidx = (hrow0 + h) * a.pstride + g.s;
         st_dev(a.po + pidx * HD + d, acc);
         if (d == 0) { st_dev(a.pm + pidx, M); st_dev(a.pl + pidx, L); }
     }
-    __syncthreads();       // the wave area of LDS is reused by the next item
-}
+    wait_stores();
+    __syncthreads();
 
-// Merge the splits of query heads: o = sum_s w_s O_s / sum_s w_s l_s with
-// w_s = 2^(m_s - max m), in split order.  Each group of HD threads of the
-// workgroup merges head bh0 + group (if < nheads); every thread of the
-// workgroup must call this (it synchronises).  LDS: (NT/HD) * 2 * nsplit floats.
-template <int HD, int NT>
-I4D_DEVINL void attn_merge_heads(const AttnArgs& a, int bh0, int nheads, float* lds) {
-    const int g = i4d_tid() / HD, lt = i4d_tid() - g * HD;
-    const int bh = bh0 + g;
-    const bool valid = (g < NT / HD) && (bh < nheads);
-    const int ns = a.nsplit;
-    const size_t prow = (size_t)bh * a.nsplit_max;
-    float* sm = lds + g * 2 * ns;      // split maxima, then weights
-    float* sl = sm + ns;               // split sums
-    if (valid)
-        for (int ss = lt; ss < ns; ss += HD) { sm[ss] = ld_dev(a.pm + prow + ss); sl[ss] = ld_dev(a.pl + prow + ss); }
-    __syncthreads();
-    float M = -INFINITY, L = 0.f;
-    if (valid) {
-        for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, sm[ss]);
-        if (M != -INFINITY)
-            for (int ss = 0; ss < ns; ++ss) L = fmaf(sl[ss], exp2f(sm[ss] - M), L);
-    }
-    const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-    __syncthreads();
-    if (valid)
-        for (int ss = lt; ss < ns; ss += HD) sm[ss] = (M != -INFINITY) ? exp2f(sm[ss] - M) * inv : 0.f;
-    __syncthreads();
-    if (valid) {
-        const float* src = a.po + prow * HD + lt;
-        float acc = 0.f;
-#pragma unroll 16
-        for (int ss = 0; ss < ns; ++ss) acc = fmaf(sm[ss], ld_dev(src + (size_t)ss * HD), acc);
-        st_dev(a.o + (size_t)bh * HD + lt, acc);
+    // arrival: the last split of (b, j) merges
+    int* last = (int*)lds;
+    if (tid == 0) {
+        int* c = a.cnt + g.b * a.hkv + g.j;
+        const int old = __hip_atomic_fetch_add((I4D_GLOBAL int*)c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int is_last = (old == a.nsplit - 1);
+        if (is_last) st_dev(c, 0);                  // ready for the next call
+        last[0] = is_last;
     }
     __syncthreads();
+    const bool merge = last[0] != 0;
+    __syncthreads();
+    if (merge) {
+        // o[h][d] = sum_s w_s O_s[h][d] with w_s = 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+        // Threads own (head, 4 dims) slots; with more threads than slots each
+        // slot's splits are cut into contiguous chunks summed in chunk order.
+        // The first MB partial rows of every thread are requested before the
+        // maxima, so the merge costs about one memory round trip.
+        // LDS: 2*G*ns + 32 floats + NT float4 (at most 25 KB, inside the
+        // per-wave area for every supported shape).
+        constexpr int MB = NT >= 512 ? 16 : 32;
+        const int ns = a.nsplit;
+        const int slots = G * (HD / 4);
+        const int chunks = max(1, NT / slots);
+        float* sw = (float*)lds;                     // [G][ns] maxima, then weights
+        float* sl = sw + G * ns;                     // [G][ns] sums
+        float* hm = sl + G * ns;                     // [G] max, [G] 1 / L
+        f4* part = (f4*)(lds + ((2 * G * ns + 32) * 4 + 15) / 16 * 16);   // [chunks][slots]
+        const bool live = tid < slots * chunks;
+        const int slot = live ? tid % slots : 0, chunk = live ? tid / slots : 0;
+        const int h = slot / (HD / 4), d4 = slot - h * (HD / 4);
+        const f4* src = (const f4*)(a.po + (hrow0 + h) * a.pstride * HD) + d4;
+        const int per = (ns + chunks - 1) / chunks;
+        const int s_lo = min(chunk * per, ns), s_hi = min(ns, s_lo + per);
+        f4 pv[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u) pv[u] = ld_g(src + (size_t)min(s_lo + u, ns - 1) * (HD / 4));
+        for (int idx = tid; idx < G * ns; idx += NT) {
+            const int hh = idx / ns, ss = idx - hh * ns;
+            const size_t pidx = (hrow0 + hh) * a.pstride + ss;
+            sw[idx] = ld_g(a.pm + pidx);
+            sl[idx] = ld_g(a.pl + pidx);
+        }
+        __syncthreads();
+        if (tid < G) {
+            float M = -INFINITY, L = 0.f;
+            for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, sw[tid * ns + ss]);
+            if (M != -INFINITY)
+                for (int ss = 0; ss < ns; ++ss) L = fmaf(sl[tid * ns + ss], exp2f(sw[tid * ns + ss] - M), L);
+            hm[tid] = M;
+            hm[G + tid] = (L > 0.f) ? 1.0f / L : 0.f;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < G * ns; idx += NT) {
+            const int hh = idx / ns;
+            const float M = hm[hh];
+            sw[idx] = (M != -INFINITY) ? exp2f(sw[idx] - M) * hm[G + hh] : 0.f;
+        }
+        __syncthreads();
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = s_lo; s0 < s_hi; s0 += MB) {
+            if (s0 > s_lo) {
+#pragma unroll
+                for (int u = 0; u < MB; ++u) pv[u] = ld_g(src + (size_t)min(s0 + u, ns - 1) * (HD / 4));
+            }
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                if (s0 + u < s_hi) {
+                    const float ws = sw[h * ns + s0 + u];
+                    acc.x = fmaf(ws, pv[u].x, acc.x); acc.y = fmaf(ws, pv[u].y, acc.y);
+                    acc.z = fmaf(ws, pv[u].z, acc.z); acc.w = fmaf(ws, pv[u].w, acc.w);
+                }
+            }
+        }
+        if (live) part[chunk * slots + slot] = acc;
+        __syncthreads();
+        for (int sl2 = tid; sl2 < slots; sl2 += NT) {
+            f4 t = part[sl2];
+            for (int c = 1; c < chunks; ++c) t += part[c * slots + sl2];
+            const int hh = sl2 / (HD / 4), dd = sl2 - hh * (HD / 4);
+            float* dst = a.o + (hrow0 + hh) * HD + 4 * dd;
+            st_dev(dst, t.x); st_dev(dst + 1, t.y); st_dev(dst + 2, t.z); st_dev(dst + 3, t.w);
+        }
+    }
+    __syncthreads();       // LDS is reused by the next item
 }

@@ -100,7 +100,7 @@ I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) 
 
 // RoPE on q and k pairs, q to the fp32 buffer, bf16 k/v appended at slot pos[b].
 struct EpiQKV {
-    float* q; uint16_t* kc; uint16_t* vc; const int* pos_lds; const float2* cs;
+    float* q; uint16_t* kc; uint16_t* vc; uint16_t* kvn; const int* pos_lds; const float2* cs;
     int cap, hq, hkv, hd, nb;
     I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
@@ -120,13 +120,16 @@ struct EpiQKV {
             float* qr = q + ((size_t)b * hq + head) * hd;
             st_dev(qr + i, ra); st_dev(qr + i + half, rb);
         } else if (p >= 0) {
+            const uint16_t ba = f32_to_bf16(ra), bb = f32_to_bf16(rb);
+            uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
+            st_dev(nr + i, ba); st_dev(nr + i + half, bb);
             if (mat == 1) {
                 uint16_t* kr = kc + (((size_t)b * hkv + head) * cap + p) * hd;
-                st_dev(kr + i, f32_to_bf16(ra)); st_dev(kr + i + half, f32_to_bf16(rb));
+                st_dev(kr + i, ba); st_dev(kr + i + half, bb);
             } else {
                 uint16_t* vr = vc + ((size_t)b * hkv + head) * hd * cap;
-                st_dev(vr + (size_t)i * cap + p, f32_to_bf16(ra));
-                st_dev(vr + (size_t)(i + half) * cap + p, f32_to_bf16(rb));
+                st_dev(vr + (size_t)i * cap + p, ba);
+                st_dev(vr + (size_t)(i + half) * cap + p, bb);
             }
         }
     }
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float
 template <int FMT, int NB>
 __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x, int nb, const uint16_t* gain, float eps,
                                                        const int* pos, int max_pos, float* q, uint16_t* kc, uint16_t* vc,
-                                                       int cap, int hq, int hkv, double base, int* status) {
+                                                       uint16_t* kvn, int cap, int hq, int hkv, double base, int* status) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
     int* pos_lds = (int*)L.extra;
@@ -227,7 +230,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
     float2* cs = (float2*)(L.extra + 64);
     rope_table<NB>(cs, pos_lds, t.head_dim, base);
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiQKV ep{q, kc, vc, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
+    EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
     gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -279,21 +282,21 @@ __global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg
 template <int HD>
 __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int NSW = AttnNsw<ATTN_NT>::v;
     const int items = a.batch * a.hkv * a.nsplit;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT>(a, it, lds);
+    AttnRegs<HD, NSW> R;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW>(a, it, lds, R, false);
 }
 
-template <int HD>
-__global__ void __launch_bounds__(HD) k_attention_merge(AttnArgs a) {
-    __shared__ float lds[2 * NSPLIT_MAX];
-    attn_merge_heads<HD, HD>(a, blockIdx.x, a.batch * a.hq, lds);
-}
-
-// Workspace: an 8 KB header (status word, grid-barrier epoch and flags), the
-// persistent kernel's layer table, then the fp32 buffers of the layer.  The LM head uses the bytes after the header for its
-// per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer buffers:
-// calls on one stream never use both at once.
-constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_FLAGS = 4096, WS_HEADER = 8192;
+// Workspace: an 8 KB header (status word, grid-barrier epoch, the attention
+// arrival counters, barrier flags), the persistent kernel's layer table, then
+// one region of buffers per layer.  The LM head uses the bytes after the header
+// for its per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer
+// buffers: calls on one stream never use both at once.  The counters sit in
+// the header because they must read zero at the start of every attention
+// phase (each merge resets its own).
+constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_CNT = 1024, WS_FLAGS = 4096, WS_HEADER = 8192;
+constexpr int WS_MAX_CNT = (int)((WS_FLAGS - WS_CNT) / 4);     // B * Hkv arrival counters
 constexpr int PERS_MAX_WG = 1024;                    // flags: one int per workgroup of the persistent kernel
 constexpr int PERS_MAX_LAYERS = 256;
 constexpr int LM_MAX_WG = 4096;
@@ -326,7 +329,7 @@ struct PArgs {
     float* x_out;                // output of the last layer
     GemvTask tq, to, tg, td;     // schedules of q/k/v, Wo, gate/up, down (pointers filled per layer)
     char* lbase;                 // per-layer workspace regions: lbase + l * lstride
-    size_t lstride, off_q, off_o, off_y, off_act, off_x;
+    size_t lstride, off_q, off_o, off_y, off_act, off_x, off_kvn, off_pm, off_pl, off_po;
     AttnArgs attn;               // per-layer q, o, kc, vc filled in by the kernel
     const int* pos;
     int max_pos, cap, hq, hkv, hd, d_model, d_ff;
@@ -369,11 +372,15 @@ constexpr long long BAR_SPIN_LIMIT = 1 << 20;
 // barrier of any workgroup waits again -- every wave always reaches the end.
 struct GridSync {
     int* flags; int* status; int base; int nwg;
-    I4D_DEVINL void wait(int k) const {
-        const int target = base + k;
+    // publish arrival k once every store of this workgroup has completed
+    I4D_DEVINL void arrive(int k) const {
         wait_stores();
         __syncthreads();
-        if (i4d_tid() == 0) st_dev(flags + blockIdx.x, target);
+        if (i4d_tid() == 0) st_dev(flags + blockIdx.x, base + k);
+    }
+    // wait until every workgroup has arrived at k (bounded spin)
+    I4D_DEVINL void depart(int k) const {
+        const int target = base + k;
         if (i4d_tid() < 64) {
             if ((ld_dev(status) & I4D_DEV_BARRIER_TIMEOUT) == 0) {
                 long long spins = 0;
@@ -391,6 +398,7 @@ struct GridSync {
         }
         __syncthreads();
     }
+    I4D_DEVINL void wait(int k) const { arrive(k); depart(k); }
 };
 
 template <int NB, class Nx>
@@ -428,8 +436,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
     GridSync gs{A.flags, A.status, ld_dev(A.epoch), nwg0};
     int bar = 0;
     const int items = A.batch * A.hkv * A.attn.nsplit;
-    const int heads = A.batch * A.hq;
-    constexpr int HPW = PERS_NT / 128;              // heads merged per workgroup per round
+    constexpr int ANSW = AttnNsw<PERS_NT>::v;
 
     GemvPipe<FMT, PERS_D> P;
     gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.tq, A.layers[0], 0, 1, 2), w0, nwg0);
@@ -452,33 +459,32 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
         const float* xin = (l == 0) ? A.x_in : (const float*)(R - A.lstride + A.off_x);
         float* xout = (l + 1 == A.n_layers) ? A.x_out : (float*)(R + A.off_x);
 
+        uint16_t* kvn = (uint16_t*)(R + A.off_kvn);
+        AttnArgs a = A.attn;
+        asm volatile("" : "+s"(a.nsplit), "+s"(a.T), "+s"(a.hq), "+s"(a.hkv), "+s"(a.cap));
+        a.kc = kc; a.vc = vc; a.q = q; a.kvn = kvn; a.o = o;
+        a.pm = (float*)(R + A.off_pm); a.pl = (float*)(R + A.off_pl); a.po = (float*)(R + A.off_po);
+
         // ---- q/k/v projection, RoPE, KV append
         {
             StagePre<FMT> pre;
             stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, attn_norm);
             stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, attn_norm, A.eps, L.red);
             __syncthreads();
-            EpiQKV ep{q, kc, vc, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
+            EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
             NoNext nn;
             gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
         }
-        gs.wait(++bar);
-        // ---- attention partials (then the Wo weights start streaming)
-        {
-            AttnArgs a = A.attn;
-            asm volatile("" : "+s"(a.nsplit), "+s"(a.T), "+s"(a.hq), "+s"(a.hkv), "+s"(a.cap));
-            a.kc = kc; a.vc = vc; a.q = q;
-            for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT>(a, it, lds);
-            gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
-        }
-        gs.wait(++bar);
-        // ---- merge of the splits
-        {
-            AttnArgs a = A.attn;
-            asm volatile("" : "+s"(a.nsplit), "+s"(a.hq));
-            a.o = o;
-            for (int bh0 = w * HPW; bh0 < heads; bh0 += nwg * HPW) attn_merge_heads<128, PERS_NT>(a, bh0, heads, (float*)lds);
-        }
+        // ---- barrier; the cached history of this workgroup's first attention
+        // item streams in while it completes
+        AttnRegs<128, ANSW> AR;
+        gs.arrive(++bar);
+        if (w < items) attn_load_round<128, PERS_NT, ANSW>(a, attn_geo(a, w), 0, AR);
+        gs.depart(bar);
+        // ---- attention, merged by the last split of each (sequence, KV
+        // head); then the Wo weights start streaming
+        for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT, ANSW>(a, it, lds, AR, it == w);
+        gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
         gs.wait(++bar);
         // ---- output projection + residual
         {
@@ -537,27 +543,32 @@ int num_cus() {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t table, pm, pl, po, ping0, ping1;
-    size_t layer0, layer_stride;          // per-layer activation regions
-    size_t q, o, y, act, x;               // offsets inside a layer region
+    size_t table;
+    size_t layer0, layer_stride;          // per-layer regions
+    size_t q, o, y, act, x, kvn, pm, pl, po;   // offsets inside a layer region
+    int pstride;                          // attention partials per head (>= splits, multiple of 32)
     size_t total;
 };
 
+// Most key-axis splits plan_attention picks for this shape and batch.
+int attn_splits_max(const i4d_config* c, int B) {
+    const int want = (num_cus() + B * c->n_kv_heads - 1) / (B * c->n_kv_heads);
+    return std::max(1, std::min(want, NSPLIT_MAX));
+}
+
 // Layer l's region holds its q, merged attention output o, residual y, SwiGLU
-// activations and output x.  Per-phase launches use region 0 only; the
-// persistent kernel gives every layer its own region so that no buffer is read
-// in a launch before it has been written there.
+// activations, output x, the new token's k/v side copy and the attention
+// partials.  Per-phase launches use region 0 only; the persistent kernel gives
+// every layer its own region so that no buffer is read in a launch before it
+// has been written there.  Partial rows are padded to 128-byte lines so the
+// partials of different (sequence, KV head) groups never share a cache line.
 WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     WsLayout w;
     size_t off = WS_HEADER;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     w.table = take(PERS_TABLE_BYTES);
-    const size_t hq = c->n_q_heads, hd = c->head_dim;
-    w.pm = take((size_t)B * hq * NSPLIT_MAX * 4);
-    w.pl = take((size_t)B * hq * NSPLIT_MAX * 4);
-    w.po = take((size_t)B * hq * NSPLIT_MAX * hd * 4);
-    w.ping0 = take((size_t)B * c->d_model * 4);
-    w.ping1 = take((size_t)B * c->d_model * 4);
+    const size_t hq = c->n_q_heads, hkv = c->n_kv_heads, hd = c->head_dim;
+    w.pstride = (attn_splits_max(c, B) + 31) / 32 * 32;
     size_t lo = 0;
     auto ltake = [&](size_t bytes) { size_t o = lo; lo = align256(lo + bytes); return o; };
     w.q = ltake((size_t)B * hq * hd * 4);
@@ -565,6 +576,10 @@ WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     w.y = ltake((size_t)B * c->d_model * 4);
     w.act = ltake((size_t)B * c->d_ff * 4);
     w.x = ltake((size_t)B * c->d_model * 4);
+    w.kvn = ltake((size_t)B * hkv * 2 * hd * 2);
+    w.pm = ltake((size_t)B * hq * w.pstride * 4);
+    w.pl = ltake((size_t)B * hq * w.pstride * 4);
+    w.po = ltake((size_t)B * hq * w.pstride * hd * 4);
     w.layer_stride = lo;
     w.layer0 = off;
     off += (size_t)std::max(n_layers, 1) * lo;
@@ -752,12 +767,12 @@ int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const ui
 
 template <int FMT, int NB>
 int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, const int* pos, int max_pos,
-                 float* q, const i4d_kv* kv, int hq, int hkv, double base, int* status, hipStream_t s) {
+                 float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_QKV>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
     hipLaunchKernelGGL((k_gemv_qkv<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
-                       kv->k, kv->v, kv->capacity, hq, hkv, base, status);
+                       kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -788,8 +803,9 @@ int launch_swiglu(int fmt, int nb, const GemvTask& t, int nwg, const float* x, i
 #undef CALL
 }
 int launch_qkv(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int bn, const uint16_t* gain, float eps,
-               const int* pos, int max_pos, float* q, const i4d_kv* kv, int hq, int hkv, double base, int* status, hipStream_t s) {
-#define CALL(F, N) return launch_qkv_t<F, N>(t, nwg, x, bn, gain, eps, pos, max_pos, q, kv, hq, hkv, base, status, s)
+               const int* pos, int max_pos, float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status,
+               hipStream_t s) {
+#define CALL(F, N) return launch_qkv_t<F, N>(t, nwg, x, bn, gain, eps, pos, max_pos, q, kv, kvn, hq, hkv, base, status, s)
     I4D_DISPATCH(fmt, nb, CALL)
 #undef CALL
 }
@@ -814,28 +830,32 @@ void plan_attention(const i4d_config* c, int B, int max_pos, int& nsplit, int& T
     }
 }
 
-int launch_attention(const i4d_config* c, int B, const float* q, const i4d_kv* kv, const int* pos, int max_pos, float* o,
-                     char* ws, const WsLayout& W, hipStream_t s) {
+// Attention arguments for layer region R (kvn = nullptr: the cache already
+// holds every attended key, as for the attention test hook).
+AttnArgs attn_args(const i4d_config* c, int B, const float* q, const i4d_kv* kv, const uint16_t* kvn, const int* pos,
+                   int max_pos, float* o, char* ws, const WsLayout& W, const char* R) {
     AttnArgs a;
-    a.q = q; a.kc = kv->k; a.vc = kv->v; a.pos = pos;
+    a.q = q; a.kc = kv->k; a.vc = kv->v; a.kvn = kvn; a.pos = pos;
     a.cap = kv->capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B; a.max_pos = max_pos;
     plan_attention(c, B, max_pos, a.nsplit, a.T);
-    a.nsplit_max = NSPLIT_MAX;
+    a.pstride = W.pstride;
     a.qscale = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
-    a.pm = (float*)(ws + W.pm); a.pl = (float*)(ws + W.pl); a.po = (float*)(ws + W.po);
+    a.pm = (float*)(R + W.pm); a.pl = (float*)(R + W.pl); a.po = (float*)(R + W.po);
+    a.cnt = (int*)(ws + WS_CNT);
     a.o = o;
-    const int items = B * c->n_kv_heads * a.nsplit;
-    const int heads = B * c->n_q_heads;
-    if (c->head_dim == 128) {
+    return a;
+}
+
+int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
+    const int items = a.batch * a.hkv * a.nsplit;
+    if (hd == 128) {
         const size_t lds = attn_lds_bytes<128, ATTN_NT>();
         if (set_lds(k_attention<128>, lds) != hipSuccess) return I4D_EHIP;
         hipLaunchKernelGGL(k_attention<128>, dim3(items), dim3(ATTN_NT), lds, s, a);
-        hipLaunchKernelGGL(k_attention_merge<128>, dim3(heads), dim3(128), 0, s, a);
     } else {
         const size_t lds = attn_lds_bytes<64, ATTN_NT>();
         if (set_lds(k_attention<64>, lds) != hipSuccess) return I4D_EHIP;
         hipLaunchKernelGGL(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
-        hipLaunchKernelGGL(k_attention_merge<64>, dim3(heads), dim3(64), 0, s, a);
     }
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -849,8 +869,8 @@ size_t persistent_lds(const i4d_config* c, int nsplit) {
                              act_lds_bytes<FMT, NB, PREC_STD>(F));
     const size_t gemv = (size_t)act + gemv_part_bytes<FMT, NB, PERS_NT>() + (PERS_NT / 64) * NB * 4 + 256;
     const size_t attn = attn_lds_bytes<128, PERS_NT>();
-    const size_t merge = (size_t)(PERS_NT / 128) * 2 * nsplit * 4;
-    return align256(std::max(std::max(gemv, attn), merge)) + GEMV_EXTRA;
+    (void)nsplit;
+    return align256(std::max(gemv, attn)) + GEMV_EXTRA;
 }
 
 bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int B) {
@@ -930,14 +950,9 @@ int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* lay
     A.lbase = ws + W.layer0;
     A.lstride = W.layer_stride;
     A.off_q = W.q; A.off_o = W.o; A.off_y = W.y; A.off_act = W.act; A.off_x = W.x;
-    AttnArgs& a = A.attn;
-    a.q = nullptr; a.pos = pos; a.cap = kv[0].capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B;
-    a.max_pos = max_pos;
-    plan_attention(c, B, max_pos, a.nsplit, a.T);
-    a.nsplit_max = NSPLIT_MAX;
-    a.qscale = (float)(1.4426950408889634 / sqrt((double)hd));
-    a.pm = (float*)(ws + W.pm); a.pl = (float*)(ws + W.pl); a.po = (float*)(ws + W.po);
-    a.o = nullptr;
+    A.attn = attn_args(c, B, nullptr, &kv[0], nullptr, pos, max_pos, nullptr, ws, W, ws + W.layer0);  // per-layer pointers set in the kernel
+    const AttnArgs& a = A.attn;
+    A.off_kvn = W.kvn; A.off_pm = W.pm; A.off_pl = W.pl; A.off_po = W.po;
     A.pos = pos; A.max_pos = max_pos; A.cap = kv[0].capacity;
     A.hq = c->n_q_heads; A.hkv = c->n_kv_heads; A.hd = hd; A.d_model = c->d_model; A.d_ff = c->d_ff;
     A.base = c->rope_base; A.eps = c->rms_eps;
@@ -968,13 +983,14 @@ int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* lay
     }
 }
 
-// One layer as five phase launches.
+// One layer as phase launches (q/k/v, attention, Wo, gate/up, down), using
+// the workspace region R.
 int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
-                     const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
+                     const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s) {
     const int nb = nb_slot(B), nwg = num_cus() * WG_PER_CU;
     const int hd = c->head_dim;
     int* status = (int*)(ws + WS_STATUS);
-    char* R = ws + W.layer0;
+    uint16_t* kvn = (uint16_t*)(R + W.kvn);
     float* q = (float*)(R + W.q);
     float* o = (float*)(R + W.o);
     float* y = (float*)(R + W.y);
@@ -984,10 +1000,10 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
     GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
     const int fq = pick_fmt(L->wq);
     plan_passes(tq, fq, nb, nwg, 0);
-    if ((rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, c->n_q_heads,
+    if ((rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, kvn, c->n_q_heads,
                          c->n_kv_heads, c->rope_base, status, s))) return rc;
 
-    if ((rc = launch_attention(c, B, q, kv, pos, max_pos, o, ws, W, s))) return rc;
+    if ((rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s))) return rc;
 
     GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
     const int fo = pick_fmt(L->wo);
@@ -1012,6 +1028,7 @@ extern "C" {
 
 size_t i4d_workspace_size(const i4d_config* cfg, int32_t n_layers, int32_t batch, int32_t max_pos, int32_t vocab) {
     if (validate_cfg(cfg) || n_layers < 1 || batch < 1 || batch > MAX_BATCH || max_pos < 0) return 0;
+    if (batch * cfg->n_kv_heads > WS_MAX_CNT) return 0;
     (void)vocab;
     return ws_layout(cfg, n_layers, batch).total;
 }
@@ -1045,6 +1062,7 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if (layers[l].wq.dtype != layers[0].wq.dtype) return I4D_EINVAL;
         if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
     }
+    if (batch * cfg->n_kv_heads > WS_MAX_CNT) return I4D_EUNSUPPORTED;
     const WsLayout W = ws_layout(cfg, n_layers, batch);
     if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
     char* w = (char*)ws;
@@ -1054,11 +1072,11 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
         return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
     }
-    float* ping[2] = {(float*)(w + W.ping0), (float*)(w + W.ping1)};
     for (int l = 0; l < n_layers; ++l) {
-        const float* in = (l == 0) ? x_in : ping[(l - 1) & 1];
-        float* out = (l == n_layers - 1) ? x_out : ping[l & 1];
-        if ((rc = run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, s))) return rc;
+        char* R = w + W.layer0 + (size_t)l * W.layer_stride;
+        const float* in = (l == 0) ? x_in : (const float*)(R - W.layer_stride + W.x);
+        float* out = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
+        if ((rc = run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s))) return rc;
     }
     return I4D_OK;
 }
@@ -1116,7 +1134,10 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
     if ((rc = validate_kv(cfg, kv, max_pos))) return rc;
     const WsLayout W = ws_layout(cfg, 1, batch);
     if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
-    return launch_attention(cfg, batch, q, kv, pos, max_pos, o, (char*)ws, W, (hipStream_t)stream);
+    if (batch * cfg->n_kv_heads > WS_MAX_CNT) return I4D_EUNSUPPORTED;
+    char* w = (char*)ws;
+    return launch_attention(attn_args(cfg, batch, q, kv, nullptr, pos, max_pos, o, w, W, w + W.layer0), cfg->head_dim,
+                            (hipStream_t)stream);
 }
 
 int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream) {

@@ -164,13 +164,24 @@ I4D_DEVINL void load_unit(Unit<FMT>& u, const RowPtrs& rp, int seg, int lane16, 
 // ---------------------------------------------------------------- dot products of one unit
 I4D_DEVINL h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 
+// (a & m) | o in one VALU operation.  gfx9 VOP3 encodings take no literal
+// constants, so the compiler splits the expression into an AND and an OR; the
+// mask comes in through a scalar register and the OR value through a vector
+// register instead (one scalar operand per instruction is allowed).
+I4D_DEVINL u32 and_or(u32 a, u32 m, u32 o) {
+    u32 r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+    return r;
+}
+
 // acc + sum over one dword of 8 codes, with act[4] the staged fp16 pairs.
 I4D_DEVINL float dot8_int4(u32 w, const h2* act, float acc) {
     const u32 w8 = w >> 8;
-    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) | 0x64006400u), act[0], acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) | 0x64006400u), act[1], acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) | 0x64006400u), act[2], acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) | 0x64006400u), act[3], acc, false);
+    const u32 magic = 0x64006400u;
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, 0x000F000Fu, magic)), act[0], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, 0x00F000F0u, magic)), act[1], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, 0x000F000Fu, magic)), act[2], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, 0x00F000F0u, magic)), act[3], acc, false);
     return acc;
 }
 

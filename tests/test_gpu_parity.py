@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from int4_weight_streaming_decode_amd import binding as B
-from tests.gpu_util import (DevKV, DevLayer, DevMat, assert_close, assert_close_bf16, bf16_ulp_diff, config_of,
+from tests.gpu_util import (DevKV, DevLayer, DevMat, assert_close, assert_close_bf16, bf16_ulp_diff, config_of, rel_l2,
                             dev, workspace)
 
 pytestmark = pytest.mark.gpu
@@ -287,15 +287,34 @@ def test_multi_step_decode_matches_oracle(exec_mode):
                                   what=f"layer {l} {name} slot {120 + s}")
 
 
-def test_persistent_kernel_is_bit_identical_to_phase_launches():
-    _print_case("persistent vs phases")
-    a = _multi_step(FAST_SHAPE, 3, 200, 3, B.EXEC_PHASES, seed=23)
-    b = _multi_step(FAST_SHAPE, 3, 200, 3, B.EXEC_PERSISTENT, seed=23)
+@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_PERSISTENT])
+def test_decode_is_bit_reproducible(exec_mode):
+    """Fixed reduction orders: the same inputs give the same bits, run to run
+    (position 5000: several 16-key subtiles per attention split)."""
+    _print_case("bit reproducible", exec_mode)
+    a = _multi_step(FAST_SHAPE, 3, 5000, 2, exec_mode, seed=23)
+    b = _multi_step(FAST_SHAPE, 3, 5000, 2, exec_mode, seed=23)
     assert a[4] == 0 and b[4] == 0
-    for s in range(3):
+    for s in range(2):
         assert np.array_equal(a[0][s].view(np.uint32), b[0][s].view(np.uint32)), f"step {s} differs"
     for l in range(3):
         assert np.array_equal(a[1][l][0], b[1][l][0]) and np.array_equal(a[1][l][1], b[1][l][1])
+
+
+def test_persistent_kernel_agrees_with_phase_launches():
+    """The two execution modes cut the reductions differently (256 vs 512
+    threads per workgroup), so they agree to rounding, and both match the
+    oracle."""
+    _print_case("persistent vs phases")
+    a = _multi_step(FAST_SHAPE, 3, 5000, 2, B.EXEC_PHASES, seed=29)
+    b = _multi_step(FAST_SHAPE, 3, 5000, 2, B.EXEC_PERSISTENT, seed=29)
+    assert a[4] == 0 and b[4] == 0
+    for s in range(2):
+        assert rel_l2(b[0][s], a[0][s]) <= 1e-5, f"step {s}"
+        assert_close(b[0][s], a[2][s], what=f"persistent step {s} vs oracle")
+    for l in range(3):
+        for k in range(2):
+            assert bf16_ulp_diff(a[1][l][k], b[1][l][k]).max() <= 1
 
 
 def test_persistent_mode_rejects_unsupported_shapes():

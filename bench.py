@@ -55,7 +55,7 @@ def cpu_baseline(shape, dtype, lm):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    cap = ((shape.kv_len + 1 + 7) // 8) * 8
+    cap = ((shape.kv_len + 1 + 15) // 16) * 16
     layer = synth.make_layer(shape, 17, 0, dtype)
     kc, vc = synth.make_kv(shape, 17, 0, 1, [shape.kv_len], cap)
     x = synth.make_x(shape, 17, 1).astype(np.float64)
@@ -104,7 +104,7 @@ def main():
     torch.manual_seed(0)
 
     n_total = args.warmup + args.steps
-    cap = ((shape.kv_len + n_total + 1 + 7) // 8) * 8
+    cap = ((shape.kv_len + n_total + 1 + 15) // 16) * 16
     t_gen = time.perf_counter()
     keep = []
     layers, kvs = [], []

@@ -112,11 +112,13 @@ typedef struct i4d_config {
     int32_t exec_mode;
 } i4d_config;
 
-/* KV cache of one layer.
- *   k: bf16 [B][n_kv_heads][capacity][head_dim]  (keys, after RoPE)
- *   v: bf16 [B][n_kv_heads][head_dim][capacity]  (values, stored transposed so
- *      that the attention kernel reads a run of positions per dimension)
- * capacity % 8 == 0.  Slot t of sequence b holds the token at position t.    */
+/* KV cache of one layer, in tiles of 16 positions (each attention load then
+ * reads whole cache lines).  For sequence b, KV head j, position t, dim d:
+ *   k (after RoPE): bf16 element at [b][j][t / 16][d / 32][t % 16][d % 32]
+ *   v:              bf16 element at [b][j][t / 16][d][t % 16]
+ * i.e. k is [B][n_kv_heads][capacity/16][head_dim/32][16][32] and v is
+ * [B][n_kv_heads][capacity/16][head_dim][16].  capacity % 16 == 0.  Slot t of
+ * sequence b holds the token at position t.                                  */
 typedef struct i4d_kv {
     uint16_t* k;
     uint16_t* v;

@@ -32,8 +32,9 @@
 //       receives the scores of head r for keys 4g..4g+3 -- which is exactly the
 //       A-operand layout of
 //   O[head][dim] += P[head][key] x V[key][dim]  (M = heads, N = 16 dims, K = 16
-//       keys).  V is cached transposed ([dim][position]) so that lane (r, g)
-//       reads keys 4g..4g+3 of dimension 16nt + r as one 8-byte load.
+//       keys).  V is cached dim-major inside each 16-position tile so that
+//       lane (r, g) reads keys 4g..4g+3 of dimension 16nt + r as one 8-byte
+//       load.
 // q and P are split into bf16 hi + lo parts (two MFMAs each), which carries
 // them at about 16 significant bits; K and V are exact bf16, products are exact
 // in fp32.  Scores are in log2 units (q is pre-scaled by log2(e)/sqrt(hd)).
@@ -42,13 +43,13 @@
 
 struct AttnArgs {
     const float* q;          // [B][Hq][hd] fp32
-    const uint16_t* kc;      // [B][Hkv][cap][hd]
-    const uint16_t* vc;      // [B][Hkv][hd][cap]
+    const uint16_t* kc;      // [B][Hkv][cap/16][hd/32][16][32]
+    const uint16_t* vc;      // [B][Hkv][cap/16][hd][16]
     const uint16_t* kvn;     // [B][Hkv][2][hd]: the new token's bf16 k (row 0) and v (row 1)
     const int* pos;          // [B]
     int cap, hq, hkv, batch, max_pos;
     int nsplit;              // splits per (b, j)
-    int T;                   // keys per split (multiple of 4)
+    int T;                   // keys per split (multiple of 16)
     int pstride;             // partial-buffer stride per head (multiple of 32 splits)
     float qscale;            // log2(e) / sqrt(hd)
     float* pm; float* pl;    // [B][Hq][pstride]
@@ -102,37 +103,42 @@ struct AttnRegs {
     u32x2 v[NSW][HD / 16];
 };
 
-// K rows (key t0 + r, dims DPL*g ..) and V^T runs (dim 16nt + r, keys t0 + 4g ..
-// t0 + 4g + 3) of subtile st.  Addresses are clamped into the cache so every
-// load is issued; keys outside the item are masked when the subtile is used.
+// K (key t0 + r, dims 32mm + 8g .. + 8) and V (dim 16nt + r, keys t0 + 4g ..
+// t0 + 4g + 3) of subtile st, from the cache's 16-position tiles (the cache
+// layout is chosen so that every load instruction reads whole cache lines).
+// Subtiles start on tile boundaries (keys per split are a multiple of 16);
+// keys outside the item are masked when the subtile is used.
+// A slot past the item (live = false) reads one 16-byte word of the cache for
+// every lane instead: the loads stay unconditional, so the compiler can count
+// them exactly, but cost one cache line each.
 template <int HD>
-I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, u32x4 (&kr)[HD / 32], u32x2 (&vr)[HD / 16]) {
-    constexpr int NKB = HD / 16, DPL = HD / 4;
+I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool live, u32x4 (&kr)[HD / 32],
+                              u32x2 (&vr)[HD / 16]) {
+    constexpr int NKB = HD / 16;
     const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
     const uint16_t* kbase = a.kc + (size_t)(g.b * a.hkv + g.j) * a.cap * HD;
     const uint16_t* vbase = a.vc + (size_t)(g.b * a.hkv + g.j) * HD * a.cap;
-    const int t0 = g.t_s + 16 * st;
-    const int tk = min(t0 + r, a.cap - 1);
-    const uint16_t* kp = kbase + (size_t)tk * HD + 8 * gq;
+    const size_t tile = (size_t)((g.t_s >> 4) + st) * 16 * HD;     // this subtile's 16-position tile
+    // K tile [HD/32][16][32]: block mm of the four lanes of key r is 64 bytes;
+    // one instruction reads the 1 KB block [mm][0..15][0..31]
+    const uint16_t* kp = live ? kbase + tile + r * 32 + 8 * gq : kbase;
 #pragma unroll
-    for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = nt_load_k((const u32x4*)(kp + 32 * mm));
-    const int tv = min(t0 + 4 * gq, a.cap - 4);
+    for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = nt_load_k((const u32x4*)(kp + (live ? 512 * mm : 0)));
+    // V tile [HD][16]: one instruction reads dims 16nt..16nt+15, 512 contiguous bytes
+    const uint16_t* vp = live ? vbase + tile + r * 16 + 4 * gq : vbase;
 #pragma unroll
-    for (int nt = 0; nt < NKB; ++nt) vr[nt] = nt_load_v((const u32x2*)(vbase + (size_t)(16 * nt + r) * a.cap + tv));
+    for (int nt = 0; nt < NKB; ++nt) vr[nt] = nt_load_v((const u32x2*)(vp + (live ? 256 * nt : 0)));
 }
 
-// Issue the loads of round r of this wave.  Slots past the item re-read the
-// wave's first subtile (already requested: no extra HBM traffic), so the loads
-// stay unconditional and the compiler can count them exactly.
+// Issue the loads of round r of this wave.
 template <int HD, int NT, int NSW>
 I4D_DEVINL void attn_load_round(const AttnArgs& a, const AttnGeo& g, int rnd, AttnRegs<HD, NSW>& R) {
     constexpr int NW = NT / 64;
     const int wave = i4d_tid() >> 6;
 #pragma unroll
     for (int i = 0; i < NSW; ++i) {
-        int st = (rnd * NSW + i) * NW + wave;
-        if (st >= g.nsub) st = (rnd * NSW) * NW + wave;
-        attn_load_sub<HD>(a, g, st, R.k[i], R.v[i]);
+        const int st = (rnd * NSW + i) * NW + wave;
+        attn_load_sub<HD>(a, g, st, st < g.nsub, R.k[i], R.v[i]);
     }
 }
 
@@ -149,7 +155,7 @@ I4D_DEVINL void attn_patch_new(const AttnArgs& a, const AttnGeo& g, int st, u32x
         for (int mm = 0; mm < NKB / 2; ++mm) kr[mm] = ld_g((const u32x4*)(kn + 32 * mm + 8 * gq));
     }
     const int e = g.kpos - (t0 + 4 * gq);          // index of the new key in this lane's run of 4
-    if (e >= 0 && e < 4 && t0 + 4 * gq <= a.cap - 4) {
+    if (e >= 0 && e < 4) {
 #pragma unroll
         for (int nt = 0; nt < NKB; ++nt) {
             const u32 nv = (u32)ld_g(kn + HD + 16 * nt + r);
@@ -174,16 +180,10 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
     const AttnGeo g = attn_geo(a, item);
     const int nsub = g.nsub, t_e = g.t_e;
 
-    // the subtile holding the new key gets the side-buffer values in the round
-    // that loads it (whichever round: a line loaded earlier may be stale)
-    auto patch_round = [&](int rnd) {
-        if (a.kvn == nullptr || g.kpos < g.t_s || g.kpos >= t_e) return;
-        const int stp = (g.kpos - g.t_s) / 16;
-        if (stp % NW != wave || (stp / NW) / NSW != rnd) return;
-#pragma unroll
-        for (int i = 0; i < NSW; ++i)
-            if (i == (stp / NW) % NSW) attn_patch_new<HD>(a, g, stp, R.k[i], R.v[i]);
-    };
+    // the subtile holding the new key gets the side-buffer values just before
+    // it is used (in whichever round loads it: a line loaded earlier may be
+    // stale); the other subtiles' loads are not waited for by these
+    const int stp = (a.kvn != nullptr && g.kpos >= g.t_s && g.kpos < t_e) ? (g.kpos - g.t_s) / 16 : -1;
     // q first: its loads then only wait for themselves, not for the K/V stream
     // issued after them.  q^T operand (hi, lo) for head r of this group, dims
     // in the K-row order above, kept in LDS after the per-wave areas (every
@@ -195,7 +195,6 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
         for (int kb = 0; kb < NKB; ++kb) qv[kb] = ld_g((const f4*)(qrow + 32 * (kb >> 1) + 4 * (kb & 1)));
     }
     if (!pre) attn_load_round<HD, NT, NSW>(a, g, 0, R);
-    patch_round(0);
     s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
     if (wave == 0) {
         const float qs = (r < G) ? a.qscale : 0.f;
@@ -276,10 +275,11 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
     // rounds of NSW subtiles per wave: round 0 is in R already
     const int nround = (nsub + NW * NSW - 1) / (NW * NSW);
     for (int rnd = 0; rnd < nround; ++rnd) {
-        if (rnd > 0) { attn_load_round<HD, NT, NSW>(a, g, rnd, R); patch_round(rnd); }
+        if (rnd > 0) attn_load_round<HD, NT, NSW>(a, g, rnd, R);
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
             const int st = (rnd * NSW + i) * NW + wave;
+            if (st == stp) attn_patch_new<HD>(a, g, st, R.k[i], R.v[i]);
             if (st < nsub) compute_sub(st, R.k[i], R.v[i]);
         }
     }
@@ -363,13 +363,20 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
             sl[idx] = ld_g(a.pl + pidx);
         }
         __syncthreads();
-        if (tid < G) {
-            float M = -INFINITY, L = 0.f;
-            for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, sw[tid * ns + ss]);
-            if (M != -INFINITY)
-                for (int ss = 0; ss < ns; ++ss) L = fmaf(sl[tid * ns + ss], exp2f(sw[tid * ns + ss] - M), L);
-            hm[tid] = M;
-            hm[G + tid] = (L > 0.f) ? 1.0f / L : 0.f;
+        // per-head maximum and sum, 32 threads per head (uniform trip count;
+        // the shuffles stay inside each 32-lane group)
+        for (int h0 = 0; h0 < G; h0 += NT / 32) {
+            const int hh = h0 + (tid >> 5), lt = tid & 31;
+            const bool ok = hh < G;
+            float M = -INFINITY;
+            if (ok)
+                for (int ss = lt; ss < ns; ss += 32) M = fmaxf(M, sw[hh * ns + ss]);
+            for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+            float L = 0.f;
+            if (ok && M != -INFINITY)
+                for (int ss = lt; ss < ns; ss += 32) L = fmaf(sl[hh * ns + ss], exp2f(sw[hh * ns + ss] - M), L);
+            for (int o = 16; o >= 1; o >>= 1) L += shfl_xor_f(L, o);
+            if (ok && lt == 0) { hm[hh] = M; hm[G + hh] = (L > 0.f) ? 1.0f / L : 0.f; }
         }
         __syncthreads();
         for (int idx = tid; idx < G * ns; idx += NT) {

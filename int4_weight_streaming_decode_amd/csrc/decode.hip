@@ -123,13 +123,17 @@ struct EpiQKV {
             const uint16_t ba = f32_to_bf16(ra), bb = f32_to_bf16(rb);
             uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
             st_dev(nr + i, ba); st_dev(nr + i + half, bb);
+            // 16-position tiles: K [hd/32][16][32], V [hd][16]
+            const size_t tile = ((size_t)b * hkv + head) * cap * hd + (size_t)(p >> 4) * 16 * hd;
+            const int tp = p & 15;
             if (mat == 1) {
-                uint16_t* kr = kc + (((size_t)b * hkv + head) * cap + p) * hd;
-                st_dev(kr + i, ba); st_dev(kr + i + half, bb);
+                uint16_t* kt = kc + tile;
+                st_dev(kt + (i >> 5) * 512 + tp * 32 + (i & 31), ba);
+                st_dev(kt + ((i + half) >> 5) * 512 + tp * 32 + ((i + half) & 31), bb);
             } else {
-                uint16_t* vr = vc + ((size_t)b * hkv + head) * hd * cap;
-                st_dev(vr + (size_t)i * cap + p, ba);
-                st_dev(vr + (size_t)(i + half) * cap + p, bb);
+                uint16_t* vt = vc + tile;
+                st_dev(vt + (size_t)i * 16 + tp, ba);
+                st_dev(vt + (size_t)(i + half) * 16 + tp, bb);
             }
         }
     }
@@ -636,7 +640,7 @@ int validate_layer(const i4d_config* c, const i4d_layer* L) {
 int validate_kv(const i4d_config* c, const i4d_kv* kv, int max_pos) {
     (void)c;
     if (!kv || !kv->k || !kv->v) return I4D_EINVAL;
-    if (kv->capacity <= 0 || kv->capacity % 8 != 0) return I4D_EINVAL;
+    if (kv->capacity <= 0 || kv->capacity % 16 != 0) return I4D_EINVAL;
     if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return I4D_EALIGN;
     if (max_pos < 0 || max_pos >= kv->capacity) return I4D_ERANGE;
     return I4D_OK;
@@ -822,12 +826,8 @@ void plan_attention(const i4d_config* c, int B, int max_pos, int& nsplit, int& T
     int want = (num_cus() + B * c->n_kv_heads - 1) / (B * c->n_kv_heads);
     want = std::max(1, std::min(want, NSPLIT_MAX));
     T = (nk + want - 1) / want;
-    T = std::max(16, ((T + 3) / 4) * 4);
+    T = std::max(16, ((T + 15) / 16) * 16);      // whole 16-position cache tiles
     nsplit = (nk + T - 1) / T;
-    if (nsplit > NSPLIT_MAX) {   // not reachable with T >= nk / NSPLIT_MAX, kept as a guard
-        T = ((nk + NSPLIT_MAX - 1) / NSPLIT_MAX + 3) / 4 * 4;
-        nsplit = (nk + T - 1) / T;
-    }
 }
 
 // Attention arguments for layer region R (kvn = nullptr: the cache already

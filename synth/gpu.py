@@ -60,10 +60,13 @@ def make_layer_gpu(shape, seed: int, layer: int, weight_dtype: str = "int4") -> 
 
 
 def make_kv_gpu(shape, seed: int, layer: int, batch: int, capacity: int):
-    """K [B][Hkv][cap][hd] and V transposed [B][Hkv][hd][cap], bf16 N(0,1) bits as int16."""
+    """K [B][Hkv][cap/16][hd/32][16][32] and V [B][Hkv][cap/16][hd][16] (the
+    library's 16-position cache tiles), bf16 N(0,1) bits as int16.  The values
+    are i.i.d., so they are drawn directly in the tiled order."""
     H, hd = shape.n_kv_heads, shape.head_dim
-    k = _normal((batch, H, capacity, hd), seed, layer, 9).to(torch.bfloat16).view(torch.int16)
-    v = _normal((batch, H, hd, capacity), seed, layer, 10).to(torch.bfloat16).view(torch.int16)
+    assert capacity % 16 == 0 and hd % 32 == 0
+    k = _normal((batch, H, capacity // 16, hd // 32, 16, 32), seed, layer, 9).to(torch.bfloat16).view(torch.int16)
+    v = _normal((batch, H, capacity // 16, hd, 16), seed, layer, 10).to(torch.bfloat16).view(torch.int16)
     return k, v
 
 

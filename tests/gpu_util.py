@@ -1,7 +1,7 @@
 """Test glue: move synth arrays to the GPU in the library's layouts and compare results.
 
-Layout conversion only (the V cache is handed to the library transposed to
-[B][Hkv][hd][cap]); no decode arithmetic lives here.
+Layout conversion only (the K/V caches are handed to the library in its
+16-position tiles); no decode arithmetic lives here.
 """
 
 import numpy as np
@@ -43,19 +43,40 @@ class DevLayer:
         self.layer = B.make_layer(self.attn_norm, self.ffn_norm, {n: self.mats[n].mat for n in MAT_NAMES})
 
 
+def k_to_tiles(kc: np.ndarray) -> np.ndarray:
+    """[B][H][cap][hd] -> [B][H][cap/16][hd/32][16][32]."""
+    b, h, cap, hd = kc.shape
+    return np.ascontiguousarray(kc.reshape(b, h, cap // 16, 16, hd // 32, 32).transpose(0, 1, 2, 4, 3, 5))
+
+
+def v_to_tiles(vc: np.ndarray) -> np.ndarray:
+    """[B][H][cap][hd] -> [B][H][cap/16][hd][16]."""
+    b, h, cap, hd = vc.shape
+    return np.ascontiguousarray(vc.reshape(b, h, cap // 16, 16, hd).transpose(0, 1, 2, 4, 3))
+
+
+def k_from_tiles(kt: np.ndarray, shape) -> np.ndarray:
+    b, h, cap, hd = shape
+    return np.ascontiguousarray(kt.reshape(b, h, cap // 16, hd // 32, 16, 32).transpose(0, 1, 2, 4, 3, 5).reshape(shape))
+
+
+def v_from_tiles(vt: np.ndarray, shape) -> np.ndarray:
+    b, h, cap, hd = shape
+    return np.ascontiguousarray(vt.reshape(b, h, cap // 16, hd, 16).transpose(0, 1, 2, 4, 3).reshape(shape))
+
+
 class DevKV:
-    """K as [B][Hkv][cap][hd]; V transposed to [B][Hkv][hd][cap]."""
+    """K and V given as [B][Hkv][cap][hd]; held on the device in the library's tiles."""
 
     def __init__(self, kc: np.ndarray, vc: np.ndarray):
+        self.shape = kc.shape
         self.cap = kc.shape[2]
-        self.k = dev(kc)
-        self.v = dev(np.ascontiguousarray(vc.transpose(0, 1, 3, 2)))
+        self.k = dev(k_to_tiles(kc))
+        self.v = dev(v_to_tiles(vc))
         self.kv = B.make_kv(self.k, self.v, self.cap)
 
     def host(self):
-        k = host_u16(self.k)
-        v = np.ascontiguousarray(host_u16(self.v).transpose(0, 1, 3, 2))
-        return k, v
+        return k_from_tiles(host_u16(self.k), self.shape), v_from_tiles(host_u16(self.v), self.shape)
 
 
 def config_of(shape, exec_mode=B.EXEC_AUTO):

@@ -105,7 +105,8 @@ def test_decode_layer_argument_validation(lib):
     assert _call_layer(cfg, L, x_out=0x100000) == B.I4D_EINVAL           # x_out aliases x_in
     assert _call_layer(cfg, L, x_in=0x100004) == B.I4D_EALIGN
     assert _call_layer(cfg, L, max_pos=256) == B.I4D_ERANGE                # max_pos >= capacity
-    assert _call_layer(cfg, L, cap=250) == B.I4D_EINVAL                    # capacity % 8 != 0
+    assert _call_layer(cfg, L, cap=250) == B.I4D_EINVAL                    # capacity % 16 != 0
+    assert _call_layer(cfg, L, cap=248) == B.I4D_EINVAL
     assert _call_layer(cfg, L, ws_bytes=100) == B.I4D_EWORKSPACE
     assert _call_layer(cfg, L, ws=0x400010) == B.I4D_EALIGN
     assert _call_layer(cfg, _layer(cfg, wq=_mat(255, 256))) == B.I4D_EINVAL   # wrong row count

@@ -72,7 +72,7 @@ def test_gemv_matches_oracle(n, k, g, batch, dtype):
 # ------------------------------------------------------------------ attention
 
 def _attn_case(shape, batch, pos, seed):
-    cap = ((max(pos) + 1 + 7) // 8) * 8 + 8
+    cap = ((max(pos) + 1 + 15) // 16) * 16 + 16
     rng = np.random.default_rng(seed)
     kc = np.full((batch, shape.n_kv_heads, cap, shape.head_dim), 0x7FC0, dtype=np.uint16)
     vc = kc.copy()
@@ -108,7 +108,7 @@ def test_attention_matches_oracle(name, batch, pos):
 # ------------------------------------------------------------------ layer and stack
 
 def _layer_case(shape, seed, batch, pos, cap=None, weight_dtype="int4", n_layers=1):
-    cap = cap or ((max(pos) + 1 + 7) // 8) * 8 + 8
+    cap = cap or ((max(pos) + 1 + 15) // 16) * 16 + 16
     layers = [synth.make_layer(shape, seed, l, weight_dtype) for l in range(n_layers)]
     caches = [synth.make_kv(shape, seed, l, batch, pos, cap) for l in range(n_layers)]
     x = synth.make_x(shape, seed, batch)
@@ -244,7 +244,7 @@ def test_gpu_quantiser_matches_numpy_quantiser():
 def _multi_step(shape, n_layers, pos0, steps, exec_mode, seed=21, batch=1):
     """Run `steps` decode steps through decode_stack; return per-step outputs
     and the final caches (host), plus the oracle's outputs and caches."""
-    cap = ((pos0 + steps + 7) // 8) * 8 + 8
+    cap = ((pos0 + steps + 15) // 16) * 16 + 16
     layers = [synth.make_layer(shape, seed, l) for l in range(n_layers)]
     caches = [synth.make_kv(shape, seed, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
     xs = [synth.make_x(shape, seed, batch, step=s) for s in range(steps)]

@@ -5,10 +5,15 @@ Default workload (the headline metric): the 27B-shaped int4 decoder stack
 128) plus the 152064 x 5120 int4 LM head swept in chunks of 8192 rows, batch 1,
 8192 cached tokens at the first timed step (the position advances by one per
 step).  Inputs are synthetic (seeded, generated on the GPU, resident in HBM
-before timing).  Prints one JSON line.
+before timing).  Prints one JSON line: `value` from K timed steps, the
+roofline of the dominant kernel (k_gemv_swiglu) from a second region of K
+steps whose launches of that kernel carry HIP events, a per-kernel breakdown
+from a few more steps per kernel, and the CPU oracle's rate on a bounded
+sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--batch B] [--no-cpu-baseline]
+                       [--batch B] [--exec-mode M] [--roofline-kernel K]
+                       [--breakdown-steps N] [--calibrate-copy-mib MIB] [--no-cpu-baseline]
 """
 
 import argparse
@@ -33,6 +38,42 @@ WORKLOADS = {
     "7b": ("7b", "int4", False),
     "70b": ("70b", "int4", False),
 }
+
+
+# library kernel behind each timed phase
+KERNEL_NAMES = {"qkv": "k_gemv_qkv", "attention": "k_attention<128>", "wo": "k_gemv_rows (Wo)",
+                "gate_up": "k_gemv_swiglu", "down": "k_gemv_rows (W_down)", "lm_head": "k_lm_head",
+                "persistent": "k_decode_persistent"}
+
+
+# HBM traffic of the roofline kernel as hardware counters saw it, recorded in
+# this profile by two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
+# a plain copy of known size, with a hash of the kernel sources it was taken
+# on.  Reported only while the sources still hash the same.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_27b_int4_hbm_traffic.md")
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int4_weight_streaming_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """Bytes per launch from the traffic record, or None if absent or stale."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    import re
+    for line in open(TRAFFIC_RECORD):
+        m = re.match(r"traffic-record: kernel=(\S+) bytes_per_launch=(\d+) sources_sha256=([0-9a-f]{64})", line.strip())
+        if m and m.group(1) == kernel and m.group(3) == sources_sha256():
+            return int(m.group(2))
+    return None
 
 
 def describe(shape, dtype, lm, batch):
@@ -85,6 +126,14 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-kernel", default=None, choices=["qkv", "attention", "wo", "gate_up", "down", "persistent"],
+                    help="kernel whose launches are timed inside the timed region (default: gate_up with per-phase "
+                         "launches, persistent with the persistent kernel)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before the steps, run 3 plain device-to-device copies of this many MiB (a kernel of known "
+                         "traffic for scaling hardware byte counters); 0: none")
+    ap.add_argument("--breakdown-steps", type=int, default=10,
+                    help="steps per extra pass that times each other kernel of the step (0: none)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -103,7 +152,12 @@ def main():
     torch.cuda.set_device(0)
     torch.manual_seed(0)
 
-    n_total = args.warmup + args.steps
+    rk = args.roofline_kernel or ("persistent" if args.exec_mode == 2 else "gate_up")
+    phases = ["persistent"] if args.exec_mode == 2 else ["qkv", "attention", "wo", "gate_up", "down"]
+    if lm:
+        phases.append("lm_head")
+    extra = [k for k in phases if k != rk] if args.breakdown_steps > 0 else []
+    n_total = args.warmup + 2 * args.steps + len(extra) * args.breakdown_steps
     cap = ((shape.kv_len + n_total + 1 + 15) // 16) * 16
     t_gen = time.perf_counter()
     keep = []
@@ -155,6 +209,14 @@ def main():
             events[2].record()
         pos.add_(1)
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -168,16 +230,52 @@ def main():
     total_ms = t0.elapsed_time(t1)
     stack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     lm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if lm else 0.0
-    status = B.read_device_status(ws)
-
     ms_per_step = total_ms / args.steps
     keys_avg = shape.kv_len + args.warmup + (args.steps - 1) / 2.0 + 1
+
+    # The roofline kernel: the same K steps again, every launch of that kernel
+    # carrying a start and a stop HIP event on its own stream (the library
+    # launches it through hipExtLaunchKernel, which stamps them with the
+    # kernel's start and end).  The events slow the step a little, so this is
+    # a second timed region rather than the one `value` comes from.
+    done = args.warmup + args.steps
+    B.launch_timing_start(rk, 65536)
+    t0.record()
+    for i in range(args.steps):
+        step(done + i)
+    t1.record()
+    torch.cuda.synchronize()
+    rk_ms, rk_launches = B.launch_timing_stop()
+    rk_region_ms = t0.elapsed_time(t1) / args.steps
+    rk_keys = keys_avg + args.steps
+    done += args.steps
+
+    def kernel_entry(kind, ms, launches, keys):
+        nbytes = roofline.phase_bytes(shape, kind, batch, keys, wdtype)
+        avg_ms = ms / max(launches, 1)
+        return {"launches": launches, "avg_us": avg_ms * 1e3, "bytes_per_launch": nbytes,
+                "gbps": nbytes / (avg_ms * 1e-3) / 1e9 if launches else None}
+
+    # Extra passes (after the timed region, not part of `value`): each other
+    # kernel of the step timed the same way over a few steps.
+    breakdown = {rk: kernel_entry(rk, rk_ms, rk_launches, rk_keys)}
+    for kind in extra:
+        B.launch_timing_start(kind, 65536)
+        for i in range(args.breakdown_steps):
+            step(done + i)
+        torch.cuda.synchronize()
+        ms, n = B.launch_timing_stop()
+        breakdown[kind] = kernel_entry(kind, ms, n, shape.kv_len + done + (args.breakdown_steps - 1) / 2.0 + 1)
+        done += args.breakdown_steps
+    status = B.read_device_status(ws)
+
     stack_bytes = roofline.step_bytes(shape, batch, keys_avg, wdtype)
     lm_bytes = roofline.lm_head_bytes(shape.vocab, shape.d_model, shape.group) if lm else 0
     step_bytes = stack_bytes + lm_bytes
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     stack_gbps = stack_bytes / (stack_ms * 1e-3) / 1e9
 
+    rk_entry = breakdown[rk]
     result = {
         "metric": METRIC,
         "value": batch * 1000.0 / ms_per_step,
@@ -196,9 +294,14 @@ def main():
         "hbm_gbps": hbm_gbps,
         "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
         "algorithmic_bytes_per_step": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": "i4d_decode_stack (all layers of one step)",
-                     "achieved": stack_gbps, "peak": 8000.0, "unit": "GB/s", "frac": stack_gbps / 8000.0,
-                     "traffic": None, "avg_launch_ms": stack_ms, "bytes_per_launch": stack_bytes},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[rk], "achieved": rk_entry["gbps"], "peak": 8000.0,
+                     "unit": "GB/s", "frac": rk_entry["gbps"] / 8000.0, "traffic": recorded_traffic(KERNEL_NAMES[rk]),
+                     "avg_launch_us": rk_entry["avg_us"], "launches": rk_launches,
+                     "ms_per_step_while_timed": rk_region_ms,
+                     "bytes_per_launch": rk_entry["bytes_per_launch"]},
+        "kernels": breakdown,
+        "stack_ms": stack_ms,
+        "stack_gbps": stack_gbps,
         "lm_head_ms": lm_ms,
         "device_status": status,
         "input_generation_s": round(t_gen, 1),

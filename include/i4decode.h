@@ -187,6 +187,26 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
  * stream's prior work; blocks until it is available.                       */
 int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream);
 
+/* Measurement aid: time every launch of one kernel of the library.
+ * Between i4d_launch_timing_start() and i4d_launch_timing_stop(), each launch
+ * of `kernel` (one of I4D_TIME_*) is bracketed by two HIP events recorded on
+ * the stream that the launch goes to, for at most max_launches launches
+ * (1 <= max_launches <= 65536; later launches are not timed).  stop() waits
+ * for the last event, writes the summed event-to-event time (ms) and the
+ * number of timed launches, and turns timing off.  Process-wide state with
+ * one user at a time: calls from several host threads race.  start() while
+ * timing is on restarts it.  I4D_EINVAL for an unknown kernel or a bad
+ * count, I4D_EHIP if an event cannot be made or read.                      */
+#define I4D_TIME_QKV        1   /* k_gemv_qkv: norm + QKV projection + RoPE + KV append */
+#define I4D_TIME_ATTENTION  2   /* k_attention: split-K decode attention with its merge */
+#define I4D_TIME_WO         3   /* k_gemv_rows on Wo (+ residual) */
+#define I4D_TIME_GATE_UP    4   /* k_gemv_swiglu: norm + gate/up projections + SwiGLU */
+#define I4D_TIME_DOWN       5   /* k_gemv_rows on W_down (+ residual) */
+#define I4D_TIME_LM_HEAD    6   /* k_lm_head: one chunk of the LM head's rows */
+#define I4D_TIME_PERSISTENT 7   /* k_decode_persistent: all layers of one call */
+int i4d_launch_timing_start(int32_t kernel, int32_t max_launches);
+int i4d_launch_timing_stop(float* total_ms, int32_t* launches);
+
 /* Static text for a status code. */
 const char* i4d_status_string(int status);
 

@@ -81,10 +81,13 @@ def lib():
         L.i4d_gemv.argtypes = [ctypes.POINTER(I4dMat), I, P, P, P, Z, P]
         L.i4d_attention.argtypes = [ctypes.POINTER(I4dConfig), I, P, ctypes.POINTER(I4dKv), P, I, P, P, Z, P]
         L.i4d_read_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
+        L.i4d_launch_timing_start.argtypes = [I, I]
+        L.i4d_launch_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
         L.i4d_status_string.argtypes = [ctypes.c_int]
         L.i4d_status_string.restype = ctypes.c_char_p
         for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked",
-                     "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status"):
+                     "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
+                     "i4d_launch_timing_start", "i4d_launch_timing_stop"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,6 +178,21 @@ def gemv(w: I4dMat, batch, x, y, ws=None, stream=None):
 def attention(cfg, batch, q, kv: I4dKv, pos, max_pos, o, ws, stream=None):
     _check(lib().i4d_attention(ctypes.byref(cfg), batch, _ptr(q), ctypes.byref(kv), _ptr(pos), max_pos, _ptr(o),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_attention")
+
+
+# kernels that i4d_launch_timing_start can time (values of I4D_TIME_*)
+TIME_KERNELS = {"qkv": 1, "attention": 2, "wo": 3, "gate_up": 4, "down": 5, "lm_head": 6, "persistent": 7}
+
+
+def launch_timing_start(kernel: str, max_launches: int):
+    _check(lib().i4d_launch_timing_start(TIME_KERNELS[kernel], int(max_launches)), "i4d_launch_timing_start")
+
+
+def launch_timing_stop():
+    """(summed launch time in ms, number of timed launches)."""
+    ms, n = ctypes.c_float(0.0), ctypes.c_int32(0)
+    _check(lib().i4d_launch_timing_stop(ctypes.byref(ms), ctypes.byref(n)), "i4d_launch_timing_stop")
+    return float(ms.value), int(n.value)
 
 
 def read_device_status(ws, stream=None) -> int:

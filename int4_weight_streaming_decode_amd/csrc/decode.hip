@@ -1,5 +1,6 @@
 // libi4decode: kernels and the C ABI of include/i4decode.h (gfx950).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include <algorithm>
@@ -664,8 +665,18 @@ DevMat dev_mat(const i4d_mat& m) {
 
 int pick_fmt(const i4d_mat& m) {
     if (m.dtype == I4D_WEIGHT_INT4)
-        return (m.k % 512 == 0 && is_pow2(m.group) && m.group >= 32) ? FMT_INT4_FAST : FMT_INT4_GEN;
+        return (m.k % 512 == 0 && is_pow2(m.group) && m.group >= 32 && (m.k / m.group) % 2 == 0 && aligned(m.scales, 4))
+                   ? FMT_INT4_FAST : FMT_INT4_GEN;
     return (m.k % 128 == 0) ? FMT_BF16_FAST : FMT_BF16_GEN;
+}
+
+// One format for a task that streams several matrices: the fast int4 path
+// needs every one of them to qualify.
+int pick_fmt(const i4d_mat& a, const i4d_mat& b, const i4d_mat* c = nullptr) {
+    const int f = pick_fmt(a);
+    if (f == FMT_INT4_FAST && (pick_fmt(b) != FMT_INT4_FAST || (c && pick_fmt(*c) != FMT_INT4_FAST)))
+        return FMT_INT4_GEN;
+    return f;
 }
 
 int unit_w(int fmt) {
@@ -750,13 +761,46 @@ constexpr size_t LDS_LIMIT = 160 * 1024;
                                 case 4: CALL(FMT_BF16_GEN, 4); default: CALL(FMT_BF16_GEN, 8); } \
     }
 
+// ---------------------------------------------------------------- launch timing
+// Measurement aid behind i4d_launch_timing_start/stop.  A TimeScope of the
+// selected kind arms the next library kernel launch (launch_k), which then
+// goes out through hipExtLaunchKernel with a start and a stop event: the
+// runtime stamps them with the kernel's own start and end, so no extra
+// packet sits between kernels.
+struct LaunchTiming {
+    int kind = 0, cap = 0, n = 0;
+    bool armed = false;
+    std::vector<hipEvent_t> ev;          // 2 per launch: start, stop
+};
+LaunchTiming g_timing;
+
+struct TimeScope {
+    explicit TimeScope(int kind) { g_timing.armed = (g_timing.kind == kind); }
+    ~TimeScope() { g_timing.armed = false; }
+};
+
+// The timed slot for the launch about to be made (-1: not timed).
+int take_timing_slot() {
+    if (!g_timing.armed || g_timing.n >= g_timing.cap) return -1;
+    g_timing.armed = false;
+    return g_timing.n++;
+}
+
+template <class F, class... A>
+void launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+    const int slot = take_timing_slot();
+    hipEvent_t e0 = slot >= 0 ? g_timing.ev[2 * slot] : nullptr;
+    hipEvent_t e1 = slot >= 0 ? g_timing.ev[2 * slot + 1] : nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0u, args...);
+}
+
 template <int FMT, int NB>
 int launch_rows_t(const GemvTask& t, int nwg, const float* x, int x_stride, int nb, const uint16_t* gain, float eps,
                   float* y, const float* resid, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_rows<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
-    hipLaunchKernelGGL((k_gemv_rows<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, x_stride, nb, gain, eps, y, resid);
+    launch_k(k_gemv_rows<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, x_stride, nb, gain, eps, y, resid);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -765,7 +809,7 @@ int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const ui
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_swiglu<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
-    hipLaunchKernelGGL((k_gemv_swiglu<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, act);
+    launch_k(k_gemv_swiglu<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, act);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -775,7 +819,7 @@ int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint1
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_QKV>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
-    hipLaunchKernelGGL((k_gemv_qkv<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
+    launch_k(k_gemv_qkv<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
                        kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -788,7 +832,7 @@ int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys
         const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k) + (size_t)GEMV_NT * 12;
         if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
         if (set_lds(k_lm_head<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
-        hipLaunchKernelGGL((k_lm_head<FMT, NB>), dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys);
+        launch_k(k_lm_head<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys);
         hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, nb, tok, mx);
         return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
     }
@@ -851,11 +895,11 @@ int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
     if (hd == 128) {
         const size_t lds = attn_lds_bytes<128, ATTN_NT>();
         if (set_lds(k_attention<128>, lds) != hipSuccess) return I4D_EHIP;
-        hipLaunchKernelGGL(k_attention<128>, dim3(items), dim3(ATTN_NT), lds, s, a);
+        launch_k(k_attention<128>, dim3(items), dim3(ATTN_NT), lds, s, a);
     } else {
         const size_t lds = attn_lds_bytes<64, ATTN_NT>();
         if (set_lds(k_attention<64>, lds) != hipSuccess) return I4D_EHIP;
-        hipLaunchKernelGGL(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
+        launch_k(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
     }
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -901,9 +945,14 @@ int launch_persistent_t(PArgs& A, int nwg, size_t lds, hipStream_t s) {
         return I4D_EHIP;
     if (per_cu < 1) return I4D_EUNSUPPORTED;
     void* args[] = {&A};
-    if (hipLaunchCooperativeKernel((const void*)k_decode_persistent<NB>, dim3(nwg), dim3(PERS_NT), args, (unsigned)lds, s) != hipSuccess)
-        return I4D_EHIP;
-    return I4D_OK;
+    // a cooperative launch has no event-carrying form: events are recorded
+    // around it (two packets against a launch of milliseconds)
+    const int slot = take_timing_slot();
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot], s);
+    const hipError_t e = hipLaunchCooperativeKernel((const void*)k_decode_persistent<NB>, dim3(nwg), dim3(PERS_NT), args,
+                                                    (unsigned)lds, s);
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
+    return e == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
 int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* layers, int B, const float* x_in, float* x_out,
@@ -998,26 +1047,42 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
     int rc;
 
     GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
-    const int fq = pick_fmt(L->wq);
+    const int fq = pick_fmt(L->wq, L->wk, &L->wv);
     plan_passes(tq, fq, nb, nwg, 0);
-    if ((rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, kvn, c->n_q_heads,
-                         c->n_kv_heads, c->rope_base, status, s))) return rc;
-
-    if ((rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s))) return rc;
+    {
+        TimeScope ts(I4D_TIME_QKV);
+        rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, kvn, c->n_q_heads,
+                        c->n_kv_heads, c->rope_base, status, s);
+    }
+    if (rc) return rc;
+    {
+        TimeScope ts(I4D_TIME_ATTENTION);
+        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s);
+    }
+    if (rc) return rc;
 
     GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
     const int fo = pick_fmt(L->wo);
     plan_passes(to, fo, nb, nwg, 0);
-    if ((rc = launch_rows(fo, nb, to, nwg, o, c->n_q_heads * hd, B, nullptr, 0.f, y, x_in, s))) return rc;
+    {
+        TimeScope ts(I4D_TIME_WO);
+        rc = launch_rows(fo, nb, to, nwg, o, c->n_q_heads * hd, B, nullptr, 0.f, y, x_in, s);
+    }
+    if (rc) return rc;
 
     GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
-    const int fg = pick_fmt(L->wg);
+    const int fg = pick_fmt(L->wg, L->wu);
     plan_passes(tg, fg, nb, nwg, 0);
-    if ((rc = launch_swiglu(fg, nb, tg, nwg, y, B, L->ffn_norm, c->rms_eps, act, s))) return rc;
+    {
+        TimeScope ts(I4D_TIME_GATE_UP);
+        rc = launch_swiglu(fg, nb, tg, nwg, y, B, L->ffn_norm, c->rms_eps, act, s);
+    }
+    if (rc) return rc;
 
     GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
     const int fd = pick_fmt(L->wd);
     plan_passes(td, fd, nb, nwg, 0);
+    TimeScope ts(I4D_TIME_DOWN);
     return launch_rows(fd, nb, td, nwg, act, c->d_ff, B, nullptr, 0.f, x_out, y, s);
 }
 
@@ -1070,6 +1135,7 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     if (cfg->exec_mode == 2) {
         if (!I4D_ENABLE_PERSISTENT) return I4D_EUNSUPPORTED;
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
+        TimeScope ts(I4D_TIME_PERSISTENT);
         return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
     }
     for (int l = 0; l < n_layers; ++l) {
@@ -1097,6 +1163,7 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
     const int fmt = pick_fmt(*w_lm);
     plan_passes(t, fmt, nb, nwg, (chunk_rows + 1) / 2);
     if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
+    TimeScope ts(I4D_TIME_LM_HEAD);
     return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, (hipStream_t)stream);
 }
 
@@ -1138,6 +1205,40 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
     char* w = (char*)ws;
     return launch_attention(attn_args(cfg, batch, q, kv, nullptr, pos, max_pos, o, w, W, w + W.layer0), cfg->head_dim,
                             (hipStream_t)stream);
+}
+
+int i4d_launch_timing_start(int32_t kernel, int32_t max_launches) {
+    if (kernel < I4D_TIME_QKV || kernel > I4D_TIME_PERSISTENT || max_launches < 1 || max_launches > 65536)
+        return I4D_EINVAL;
+    g_timing.kind = 0;
+    g_timing.n = 0;
+    while ((int)g_timing.ev.size() < 2 * max_launches) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return I4D_EHIP;
+        g_timing.ev.push_back(e);
+    }
+    g_timing.cap = max_launches;
+    g_timing.kind = kernel;
+    return I4D_OK;
+}
+
+int i4d_launch_timing_stop(float* total_ms, int32_t* launches) {
+    if (!total_ms || !launches) return I4D_EINVAL;
+    const int n = g_timing.n;
+    g_timing.kind = 0;
+    g_timing.n = 0;
+    *total_ms = 0.f;
+    *launches = n;
+    if (n == 0) return I4D_OK;
+    double sum = 0.0;
+    for (int i = 0; i < n; ++i) {                  // launches may have gone to several streams
+        float ms = 0.f;
+        if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return I4D_EHIP;
+        if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return I4D_EHIP;
+        sum += ms;
+    }
+    *total_ms = (float)sum;
+    return I4D_OK;
 }
 
 int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream) {

@@ -141,12 +141,18 @@ I4D_DEVINL void load_unit(Unit<FMT>& u, const RowPtrs& rp, int seg, int lane16, 
         if constexpr (FMT == FMT_INT4_FAST) {
             u.a = nt_load((const u32x4*)pa);
             u.b = nt_load((const u32x4*)pb);
+            // The aligned 32-bit word that holds the bf16 scale (on this path
+            // scale rows have an even length and a 4-byte aligned base): the
+            // value of a 16-bit load is re-masked where the loop closes, and
+            // that makes the compiler wait there for every load in flight.
+            u.sa = ld_g((const u32*)((uintptr_t)qa & ~(uintptr_t)3));
+            u.sb = ld_g((const u32*)((uintptr_t)qb & ~(uintptr_t)3));
         } else {
             u.a = nt_load((const u32*)pa);
             u.b = nt_load((const u32*)pb);
+            u.sa = ld_g(qa);
+            u.sb = ld_g(qb);
         }
-        u.sa = ld_g(qa);
-        u.sb = ld_g(qb);
     } else {
         const size_t off = (size_t)k0 * 2;
         const uint8_t* pa = valid ? rp.pa + off : dummy;
@@ -186,7 +192,7 @@ I4D_DEVINL float dot8_int4(u32 w, const h2* act, float acc) {
 }
 
 template <int FMT, int NB, int PREC>
-I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int seg, int lane16,
+I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int log2g, int seg, int lane16,
                              float (&ra)[NB], float (&rb)[NB]) {
     typedef FmtT<FMT> F;
     if constexpr (F::INT4) {
@@ -194,10 +200,18 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
         int c = seg * 16 + lane16;                      // lane chunk index along K
         if (FMT == FMT_INT4_GEN) c = min(c, nchunk - 1);  // masked lanes read a valid chunk, scale 0
         const float* corr = (const float*)(act_lds + NB * PREC * K * 2);
-        // generic path: lanes past the end of K contribute nothing
-        const bool live = (FMT == FMT_INT4_FAST) || (seg * F::UNIT_W + lane16 * F::LANE_W < K);
-        const float sa = live ? bf16_to_f32((uint16_t)u.sa) : 0.f;
-        const float sb = live ? bf16_to_f32((uint16_t)u.sb) : 0.f;
+        float sa, sb;
+        if constexpr (FMT == FMT_INT4_FAST) {
+            // the half of the scale word: the parity of the group index
+            const bool odd = ((c * F::LANE_W) >> log2g) & 1;
+            sa = __uint_as_float(odd ? (u.sa & 0xFFFF0000u) : (u.sa << 16));
+            sb = __uint_as_float(odd ? (u.sb & 0xFFFF0000u) : (u.sb << 16));
+        } else {
+            // generic path: lanes past the end of K contribute nothing
+            const bool live = seg * F::UNIT_W + lane16 * F::LANE_W < K;
+            sa = live ? bf16_to_f32((uint16_t)u.sa) : 0.f;
+            sb = live ? bf16_to_f32((uint16_t)u.sb) : 0.f;
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const float cr = corr[b * nchunk + c];
@@ -553,7 +567,7 @@ I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
 #pragma unroll
             for (int i = 0; i < D; ++i) {
                 if (u < u1) {
-                    consume_unit<FMT, NB, PREC>(P.ring[i], act_lds, t.k, seg, lane16, ra, rb);
+                    consume_unit<FMT, NB, PREC>(P.ring[i], act_lds, t.k, t.log2_group, seg, lane16, ra, rb);
                     ++u;
                     if (++seg == S) {   // this pair's run is complete: park it
                         seg = 0;

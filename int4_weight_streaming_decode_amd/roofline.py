@@ -59,6 +59,31 @@ def step_bytes(shape, batch: int, keys: int, weight_dtype: str = "int4", n_layer
     return total
 
 
+def phase_bytes(shape, phase: str, batch: int, keys: float, weight_dtype: str = "int4") -> float:
+    """Algorithmic HBM bytes of one launch of one kernel of the step:
+    qkv (Wq, Wk, Wv, the attention norm gain, the new K/V), attention (the
+    cache over `keys` keys), wo, gate_up (Wg, Wu, the FFN norm gain), down,
+    lm_head (the whole head: one launch sweeps every chunk) and persistent
+    (the whole stack of one call)."""
+    m = layer_matrices(shape)
+    mb = {n: matrix_bytes(r, c, shape.group, weight_dtype) for n, (r, c) in m.items()}
+    if phase == "qkv":
+        return mb["wq"] + mb["wk"] + mb["wv"] + shape.d_model * 2 + kv_write_bytes(shape, batch)
+    if phase == "attention":
+        return kv_read_bytes(shape, batch, keys)
+    if phase == "wo":
+        return mb["wo"]
+    if phase == "gate_up":
+        return mb["wg"] + mb["wu"] + shape.d_model * 2
+    if phase == "down":
+        return mb["wd"]
+    if phase == "lm_head":
+        return lm_head_bytes(shape.vocab, shape.d_model, shape.group)
+    if phase == "persistent":
+        return step_bytes(shape, batch, keys, weight_dtype)
+    raise ValueError(phase)
+
+
 def step_flops(shape, batch: int, keys: int, n_layers=None, lm_head: bool = False) -> int:
     """2 x multiply-adds of one step over the batch (matrix products and attention)."""
     L = shape.n_layers if n_layers is None else n_layers

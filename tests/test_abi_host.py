@@ -144,3 +144,21 @@ def test_ws_min_bytes_matches_header():
     assert m, "I4D_WS_MIN_BYTES not found"
     a, b, c, d = map(int, m.groups())
     assert B.WS_MIN_BYTES == a + b * c * d
+
+
+def test_launch_timing_validation(lib):
+    ms, n = ctypes.c_float(1.0), ctypes.c_int32(7)
+    assert lib.i4d_launch_timing_start(0, 10) == B.I4D_EINVAL
+    assert lib.i4d_launch_timing_start(8, 10) == B.I4D_EINVAL
+    assert lib.i4d_launch_timing_start(B.TIME_KERNELS["gate_up"], 0) == B.I4D_EINVAL
+    assert lib.i4d_launch_timing_start(B.TIME_KERNELS["gate_up"], 65537) == B.I4D_EINVAL
+    assert lib.i4d_launch_timing_stop(None, ctypes.byref(n)) == B.I4D_EINVAL
+    # nothing was timed: no event is read
+    assert lib.i4d_launch_timing_stop(ctypes.byref(ms), ctypes.byref(n)) == B.I4D_OK
+    assert n.value == 0 and ms.value == 0.0
+
+
+def test_time_kernel_ids_match_header():
+    text = open(HEADER).read()
+    ids = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"#define I4D_TIME_(\w+)\s+(\d+)", text)}
+    assert ids == B.TIME_KERNELS

@@ -61,3 +61,14 @@ def test_int4_bytes_per_weight_and_27b_step():
     assert roofline.step_bytes(s, 1, s.kv_len + 1, "bf16") / 1e9 == pytest.approx(48.454, abs=0.002)
     lm = synth.SHAPES["27b_lm"]
     assert roofline.step_bytes(lm, 1, lm.kv_len + 1, lm_head=True) / 1e9 == pytest.approx(14.489, abs=0.002)
+
+
+def test_phase_bytes_add_up_to_the_step():
+    s = synth.SHAPES["27b_lm"]
+    keys = s.kv_len + 1
+    parts = sum(roofline.phase_bytes(s, p, 1, keys) for p in ("qkv", "attention", "wo", "gate_up", "down"))
+    assert parts * s.n_layers == roofline.step_bytes(s, 1, keys)
+    assert roofline.phase_bytes(s, "persistent", 1, keys) == roofline.step_bytes(s, 1, keys)
+    assert roofline.phase_bytes(s, "lm_head", 1, keys) == roofline.lm_head_bytes(s.vocab, s.d_model, s.group)
+    # gate/up of the 27B shape: two 17408 x 5120 int4 matrices with groups of 128, plus the norm gain
+    assert roofline.phase_bytes(s, "gate_up", 1, keys) == 2 * (17408 * 2560 + 17408 * 40 * 2) + 5120 * 2

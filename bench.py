@@ -81,7 +81,7 @@ def describe(shape, dtype, lm, batch):
          f"{shape.n_q_heads}/{shape.n_kv_heads} heads, head_dim {shape.head_dim}, d_ff {shape.d_ff}, "
          f"group {shape.group}; KV {shape.kv_len} cached tokens; batch {batch}")
     if lm:
-        s += f"; int4 LM head {shape.vocab} x {shape.d_model}, chunks of {shape.lm_chunk} rows, greedy argmax"
+        s += f"; int4 LM head {shape.vocab} x {shape.d_model} with greedy argmax (chunk_rows {shape.lm_chunk} requested)"
     return s
 
 

@@ -157,9 +157,12 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
 
 /* Greedy LM head (Unsloth article 三; Primer 1.2): for each of `batch` hidden
  * states h [B][D] fp32, token_out[b] = lowest v maximising (W_lm h_b)_v and
- * max_logit_out[b] = that logit (fp32).  w_lm is int4 [V][D].  The vocabulary
- * is swept in passes of chunk_rows rows (chunk_rows > 0) with a running
- * argmax; the full logit vector is never stored.  1 <= batch <= 8.
+ * max_logit_out[b] = that logit (fp32).  w_lm is int4 [V][D].  The page's
+ * chunking bounds the logits held at once; here no logit leaves the
+ * registers of the workgroup that computed it (each keeps a running argmax),
+ * so the vocabulary is swept in passes as large as the kernel's per-workgroup
+ * budget allows whatever chunk_rows is (chunk_rows > 0 is still required).
+ * The result does not depend on chunk_rows.  1 <= batch <= 8.
  * ws_bytes >= I4D_WS_MIN_BYTES.                                              */
 int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
                         int32_t* token_out, float* max_logit_out,

@@ -46,12 +46,13 @@ constexpr int GEMV_EXTRA = 64 + MAX_BATCH * 64 * 8;
 // ============================================================== epilogues and staging functors
 
 // Stage `src` (optionally RMS-normalised with `gain`) into LDS.
-template <int FMT, int NB, int PREC>
+template <int FMT, int NB, int PREC, int PC = PRE_CHUNKS>
 struct StageFn {
+    typedef StagePre<FMT, PC> Pre;
     char* act; const float* src; int stride; int K; int nb; const uint16_t* gain; float eps; float* red;
-    I4D_DEVINL void issue(StagePre<FMT>& pre) { stage_issue<FMT, NB, GEMV_NT>(pre, src, stride, K, nb, gain); }
-    I4D_DEVINL void finish(const StagePre<FMT>& pre) {
-        stage_finish<FMT, NB, GEMV_NT, PREC>(pre, act, src, stride, K, nb, gain, eps, red);
+    I4D_DEVINL void issue(Pre& pre) { stage_issue<FMT, NB, GEMV_NT, PC>(pre, src, stride, K, nb, gain); }
+    I4D_DEVINL void finish(const Pre& pre) {
+        stage_finish<FMT, NB, GEMV_NT, PREC, PC>(pre, act, src, stride, K, nb, gain, eps, red);
     }
 };
 
@@ -98,6 +99,28 @@ I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) 
         cs[idx] = float2{(float)cos(phi), (float)sin(phi)};
     }
 }
+
+// Positions of the batch into LDS (an invalid one becomes -1 and raises the
+// status word), then the cos/sin table for them.
+template <int NB>
+struct RopeSetup {
+    const int* pos; int* pos_lds; float2* cs; int* status; int nb, max_pos, cap, hd; double base;
+    I4D_DEVINL void operator()() const {
+        if (i4d_tid() < NB) {
+            int p = -1;
+            if (i4d_tid() < nb) {
+                p = pos[i4d_tid()];
+                if (p < 0 || p > max_pos || p >= cap) {
+                    if (blockIdx.x == 0) raise_status(status, I4D_DEV_BAD_POS);
+                    p = -1;
+                }
+            }
+            pos_lds[i4d_tid()] = p;
+        }
+        __syncthreads();
+        rope_table<NB>(cs, pos_lds, hd, base);
+    }
+};
 
 // RoPE on q and k pairs, q to the fp32 buffer, bf16 k/v appended at slot pos[b].
 struct EpiQKV {
@@ -201,7 +224,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_rows(GemvTask t, const float* 
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, x, x_stride, t.k, nb, gain, eps, L.red};
     EpiRows ep{y, resid, t.a.n, nb};
-    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_ADJ>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
 template <int FMT, int NB>
@@ -210,7 +233,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
     EpiSwiGLU ep{act, t.a.n, nb};
-    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_TWO>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
 template <int FMT, int NB>
@@ -220,23 +243,11 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
     int* pos_lds = (int*)L.extra;
-    if (i4d_tid() < NB) {
-        int p = -1;
-        if (i4d_tid() < nb) {
-            p = pos[i4d_tid()];
-            if (p < 0 || p > max_pos || p >= cap) {
-                if (blockIdx.x == 0) raise_status(status, I4D_DEV_BAD_POS);
-                p = -1;
-            }
-        }
-        pos_lds[i4d_tid()] = p;
-    }
-    __syncthreads();
     float2* cs = (float2*)(L.extra + 64);
-    rope_table<NB>(cs, pos_lds, t.head_dim, base);
+    RopeSetup<NB>{pos, pos_lds, cs, status, nb, max_pos, cap, t.head_dim, base}();
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
     EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
-    gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+    gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_QKV>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
 template <int FMT, int NB>
@@ -245,7 +256,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h,
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, h, t.k, t.k, nb, nullptr, 0.f, L.red};
     EpiArgmax ep{t.a.n, nb, 0ull, -1};
-    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
+    gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_ADJ>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
     // workgroup best per batch slot -> this workgroup's key slots
     u64* kl = (u64*)(L.extra + GEMV_EXTRA);
     int* ks = (int*)(kl + GEMV_NT);
@@ -406,10 +417,10 @@ struct GridSync {
     I4D_DEVINL void wait(int k) const { arrive(k); depart(k); }
 };
 
-template <int NB, class Nx>
+template <int NB, int KND>
 struct PrimeNext {
     GemvPipe<FMT_INT4_FAST, PERS_D>& P; GemvTask t; int w, nwg; bool on;
-    I4D_DEVINL void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, PERS_D>(P, t, w, nwg); }
+    I4D_DEVINL void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, PERS_D, KND>(P, t, w, nwg); }
 };
 
 template <int NB>
@@ -444,7 +455,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
     constexpr int ANSW = AttnNsw<PERS_NT>::v;
 
     GemvPipe<FMT, PERS_D> P;
-    gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.tq, A.layers[0], 0, 1, 2), w0, nwg0);
+    gemv_prime<FMT, PERS_NT, PERS_D, KIND_QKV>(P, task_of(A.tq, A.layers[0], 0, 1, 2), w0, nwg0);
     for (int l = 0; l < A.n_layers; ++l) {
         // per-layer opaque copies of the launch constants: otherwise every
         // phase's schedule arithmetic is hoisted out of the layer loop and
@@ -478,7 +489,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             __syncthreads();
             EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
             NoNext nn;
-            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
+            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ, KIND_QKV>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
         }
         // ---- barrier; the cached history of this workgroup's first attention
         // item streams in while it completes
@@ -489,7 +500,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
         // ---- attention, merged by the last split of each (sequence, KV
         // head); then the Wo weights start streaming
         for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT, ANSW>(a, it, lds, AR, it == w);
-        gemv_prime<FMT, PERS_NT, PERS_D>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
+        gemv_prime<FMT, PERS_NT, PERS_D, KIND_ADJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
         gs.wait(++bar);
         // ---- output projection + residual
         {
@@ -498,8 +509,8 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
             __syncthreads();
             EpiRows ep{y, xin, A.d_model, A.batch};
-            PrimeNext<NB, void> nx{P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg, L.act, L.part, ep, nx);
+            PrimeNext<NB, KIND_TWO> nx{P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg, L.act, L.part, ep, nx);
         }
         gs.wait(++bar);
         // ---- gate/up projection + SwiGLU
@@ -509,8 +520,8 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, y, A.d_model, A.d_model, A.batch, ffn_norm, A.eps, L.red);
             __syncthreads();
             EpiSwiGLU ep{act, A.d_ff, A.batch};
-            PrimeNext<NB, void> nx{P, task_of(A.td, Ly, 6, -1, -1), w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, L.act, L.part, ep, nx);
+            PrimeNext<NB, KIND_ADJ> nx{P, task_of(A.td, Ly, 6, -1, -1), w, nwg, true};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_TWO>(P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, L.act, L.part, ep, nx);
         }
         gs.wait(++bar);
         // ---- down projection + residual (then the next layer's q/k/v weights start streaming)
@@ -521,8 +532,8 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             __syncthreads();
             EpiRows ep{xout, y, A.d_model, A.batch};
             const bool more = l + 1 < A.n_layers;
-            PrimeNext<NB, void> nx{P, task_of(A.tq, more ? A.layers[l + 1] : Ly, 0, 1, 2), w, nwg, more};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ>(P, task_of(A.td, Ly, 6, -1, -1), w, nwg, L.act, L.part, ep, nx);
+            PrimeNext<NB, KIND_QKV> nx{P, task_of(A.tq, more ? A.layers[l + 1] : Ly, 0, 1, 2), w, nwg, more};
+            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.td, Ly, 6, -1, -1), w, nwg, L.act, L.part, ep, nx);
         }
         if (l + 1 < A.n_layers) gs.wait(++bar);
     }
@@ -693,11 +704,14 @@ int maxj_of(int nb) { return nb <= 2 ? MaxJ<1>::v : MaxJ<4>::v; }
 
 // Fill pass geometry: at most `cap_pairs` pairs per pass (0: no cap), and never
 // more pairs per workgroup than keeps every slot within MAXJ runs.
-void plan_passes(GemvTask& t, int fmt, int nb, int nwg, int cap_pairs, int nt = GEMV_NT) {
+// young: the younger waves' share in percent (see wave_cut); the best value
+// was measured per matrix shape.
+void plan_passes(GemvTask& t, int fmt, int nb, int nwg, int cap_pairs, int nt = GEMV_NT, int young = 50) {
     const int S = (t.k + unit_w(fmt) - 1) / unit_w(fmt);
     const int maxj = maxj_of(nb);
+    t.young = young;
     int ppw = (t.total_pairs + nwg - 1) / nwg;
-    while (ppw > 1 && gemv_max_runs(ppw, S, nt / 64) > maxj) --ppw;
+    while (ppw > 1 && gemv_max_runs(ppw, S, nt / 64, young) > maxj) --ppw;
     long long pp = (long long)ppw * nwg;
     if (cap_pairs > 0 && pp > cap_pairs) pp = cap_pairs;
     if (pp > t.total_pairs) pp = t.total_pairs;
@@ -1048,7 +1062,7 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
     const int fq = pick_fmt(L->wq, L->wk, &L->wv);
-    plan_passes(tq, fq, nb, nwg, 0);
+    plan_passes(tq, fq, nb, nwg, 0, GEMV_NT, 36);
     {
         TimeScope ts(I4D_TIME_QKV);
         rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, kvn, c->n_q_heads,
@@ -1063,7 +1077,7 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
     const int fo = pick_fmt(L->wo);
-    plan_passes(to, fo, nb, nwg, 0);
+    plan_passes(to, fo, nb, nwg, 0, GEMV_NT, 40);
     {
         TimeScope ts(I4D_TIME_WO);
         rc = launch_rows(fo, nb, to, nwg, o, c->n_q_heads * hd, B, nullptr, 0.f, y, x_in, s);
@@ -1072,7 +1086,7 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
     const int fg = pick_fmt(L->wg, L->wu);
-    plan_passes(tg, fg, nb, nwg, 0);
+    plan_passes(tg, fg, nb, nwg, 0, GEMV_NT, 36);
     {
         TimeScope ts(I4D_TIME_GATE_UP);
         rc = launch_swiglu(fg, nb, tg, nwg, y, B, L->ffn_norm, c->rms_eps, act, s);
@@ -1081,7 +1095,7 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
     const int fd = pick_fmt(L->wd);
-    plan_passes(td, fd, nb, nwg, 0);
+    plan_passes(td, fd, nb, nwg, 0, GEMV_NT, 40);
     TimeScope ts(I4D_TIME_DOWN);
     return launch_rows(fd, nb, td, nwg, act, c->d_ff, B, nullptr, 0.f, x_out, y, s);
 }
@@ -1161,7 +1175,10 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
     const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
     GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
     const int fmt = pick_fmt(*w_lm);
-    plan_passes(t, fmt, nb, nwg, (chunk_rows + 1) / 2);
+    // Logits only ever exist in registers (each workgroup keeps a running
+    // maximum), so nothing is gained by passes as small as chunk_rows: the
+    // passes are as large as the per-workgroup run budget allows.
+    plan_passes(t, fmt, nb, nwg, 0, GEMV_NT, 34);
     if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
     TimeScope ts(I4D_TIME_LM_HEAD);
     return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, (hipStream_t)stream);
@@ -1188,7 +1205,7 @@ int i4d_gemv(const i4d_mat* wm, int32_t batch, const float* x, float* y, void* w
     const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
     GemvTask t = make_task(KIND_ADJ, wm, nullptr, nullptr, 64);
     const int fmt = pick_fmt(*wm);
-    plan_passes(t, fmt, nb, nwg, 0);
+    plan_passes(t, fmt, nb, nwg, 0, GEMV_NT, 36);
     return launch_rows(fmt, nb, t, nwg, x, wm->k, batch, nullptr, 0.f, y, nullptr, (hipStream_t)stream);
 }
 

@@ -52,6 +52,7 @@ struct GemvTask {
     int total_pairs;
     int pass_pairs;            // pairs per pass (all workgroups together)
     int npasses;
+    int young;                 // share of the younger wave of each SIMD in an 8-wave workgroup, percent
 };
 
 template <int FMT> struct FmtT;
@@ -72,18 +73,21 @@ __host__ __device__ constexpr int act_lds_bytes(int K) {
 // ---------------------------------------------------------------- pair -> rows
 struct RowPtrs { const uint8_t* pa; const uint8_t* pb; const uint16_t* sa; const uint16_t* sb; };
 
-template <int FMT>
+// KND: the task's kind when the kernel knows it at compile time (then only
+// that mapping is compiled), or -1 to read it from the task.
+template <int FMT, int KND = -1>
 I4D_DEVINL RowPtrs resolve_pair(const GemvTask& t, int pair) {
     // select by value (no pointer to a member of the kernel argument, which
     // would push the task into scratch memory)
+    const int kind = KND >= 0 ? KND : t.kind;
     const uint8_t* da = t.a.data; const uint16_t* sa = t.a.scales; int ga = t.a.ngroups;
     const uint8_t* db; const uint16_t* sb; int gb;
     int ra, rb;
-    if (t.kind == KIND_ADJ) {
+    if (kind == KIND_ADJ) {
         ra = 2 * pair;
         rb = min(2 * pair + 1, t.a.n - 1);
         db = da; sb = sa; gb = ga;
-    } else if (t.kind == KIND_TWO) {
+    } else if (kind == KIND_TWO) {
         ra = pair; rb = pair;
         db = t.b.data; sb = t.b.scales; gb = t.b.ngroups;
     } else {
@@ -95,7 +99,7 @@ I4D_DEVINL RowPtrs resolve_pair(const GemvTask& t, int pair) {
             if (lp >= npk) { lp -= npk; da = t.c.data; sa = t.c.scales; ga = t.c.ngroups; }
             else { da = t.b.data; sa = t.b.scales; ga = t.b.ngroups; }
         }
-        const int head = lp / half, i = lp - head * half;
+        const int head = lp >> __builtin_ctz(half), i = lp & (half - 1);     // head_dim is 64 or 128
         ra = head * t.head_dim + i;
         rb = ra + half;
         db = da; sb = sa; gb = ga;
@@ -281,11 +285,14 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
 // rest.  `red` is NT/64*NB floats of LDS.
 constexpr int PRE_CHUNKS = 1;
 
-template <int FMT>
+// PC: chunks per thread loaded up front (the rest are loaded, and waited
+// for, while staging).
+template <int FMT, int PC = PRE_CHUNKS>
 struct StagePre {
     static constexpr int NV = FmtT<FMT>::INT4 ? FmtT<FMT>::LANE_W / 4 : 2;   // float4 loads per chunk
-    f4 x[PRE_CHUNKS][NV];
-    u32x4 g[PRE_CHUNKS][FmtT<FMT>::INT4 ? NV / 2 : 1];
+    static constexpr int CH = PC;
+    f4 x[PC][NV];
+    u32x4 g[PC][FmtT<FMT>::INT4 ? NV / 2 : 1];
 };
 
 // chunk geometry: int4 chunks are LANE_W inputs; bf16 chunks are 8 inputs
@@ -312,11 +319,11 @@ I4D_DEVINL void stage_load_chunk(f4 (&xv)[StagePre<FMT>::NV], u32x4 (&gv)[FmtT<F
     }
 }
 
-template <int FMT, int NB, int NT>
-I4D_DEVINL void stage_issue(StagePre<FMT>& pre, const float* src, int src_stride, int K, int nb, const uint16_t* gain) {
+template <int FMT, int NB, int NT, int PC = PRE_CHUNKS>
+I4D_DEVINL void stage_issue(StagePre<FMT, PC>& pre, const float* src, int src_stride, int K, int nb, const uint16_t* gain) {
     const int nidx = NB * (K / stage_chunk_w<FMT>());
 #pragma unroll
-    for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+    for (int pc = 0; pc < PC; ++pc) {
         const int idx = min(i4d_tid() + pc * NT, nidx - 1);     // clamped: loads are unconditional
         stage_load_chunk<FMT, NB, NT>(pre.x[pc], pre.g[pc], src, src_stride, K, nb, gain, idx);
     }
@@ -385,8 +392,8 @@ I4D_DEVINL void stage_write_chunk(char* act_lds, const f4 (&xv)[StagePre<FMT>::N
     }
 }
 
-template <int FMT, int NB, int NT, int PREC>
-I4D_DEVINL void stage_finish(const StagePre<FMT>& pre, char* act_lds, const float* src, int src_stride, int K, int nb,
+template <int FMT, int NB, int NT, int PREC, int PC = PRE_CHUNKS>
+I4D_DEVINL void stage_finish(const StagePre<FMT, PC>& pre, char* act_lds, const float* src, int src_stride, int K, int nb,
                              const uint16_t* gain, float eps, float* red) {
     const int tid = i4d_tid();
     const int nidx = NB * (K / stage_chunk_w<FMT>());
@@ -400,7 +407,7 @@ I4D_DEVINL void stage_finish(const StagePre<FMT>& pre, char* act_lds, const floa
         for (int b = 0; b < NB; ++b) ss[b] = 0.f;
         const int nchunk = K / stage_chunk_w<FMT>();
 #pragma unroll
-        for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+        for (int pc = 0; pc < PC; ++pc) {
             const int idx = tid + pc * NT;
             if (idx < nidx) {
                 f4 acc = f4{0.f, 0.f, 0.f, 0.f};
@@ -411,7 +418,7 @@ I4D_DEVINL void stage_finish(const StagePre<FMT>& pre, char* act_lds, const floa
                 for (int b = 0; b < NB; ++b) if (b == idx / nchunk) ss[b] += v;
             }
         }
-        for (int idx = tid + PRE_CHUNKS * NT; idx < nidx; idx += NT) {
+        for (int idx = tid + PC * NT; idx < nidx; idx += NT) {
             f4 xv[StagePre<FMT>::NV];
             u32x4 gv[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1];
             stage_load_chunk<FMT, NB, NT>(xv, gv, src, src_stride, K, nb, nullptr, idx);
@@ -440,11 +447,11 @@ I4D_DEVINL void stage_finish(const StagePre<FMT>& pre, char* act_lds, const floa
         __syncthreads();   // red may be reused by the caller
     }
 #pragma unroll
-    for (int pc = 0; pc < PRE_CHUNKS; ++pc) {
+    for (int pc = 0; pc < PC; ++pc) {
         const int idx = tid + pc * NT;
         if (idx < nidx) stage_write_chunk<FMT, NB, PREC>(act_lds, pre.x[pc], pre.g[pc], K, nb, gain != nullptr, rs, idx);
     }
-    for (int idx = tid + PRE_CHUNKS * NT; idx < nidx; idx += NT) {
+    for (int idx = tid + PC * NT; idx < nidx; idx += NT) {
         f4 xv[StagePre<FMT>::NV];
         u32x4 gv[FmtT<FMT>::INT4 ? StagePre<FMT>::NV / 2 : 1];
         stage_load_chunk<FMT, NB, NT>(xv, gv, src, src_stride, K, nb, gain, idx);
@@ -461,12 +468,27 @@ I4D_DEVINL void pass_pairs_of(const GemvTask& t, int pass, int w, int nwg, int& 
     q1 = pb + ((w + 1) * np) / nwg;
 }
 
+// First unit of wave w when U units are split over NW waves.  With two
+// waves per SIMD (8-wave workgroups) the sequencer issues from the older wave
+// first: given equal shares, waves 0-3 finish about 1.4x sooner than waves
+// 4-7.  So each younger wave gets `young` percent of its SIMD's share (the
+// task's young; 50 = an even split).
+template <int NW>
+__host__ __device__ inline int wave_cut(int U, int w, int young) {
+    if constexpr (NW == 8) {
+        const int c = w <= 4 ? w * (100 - young) : 4 * (100 - young) + (w - 4) * young;
+        return (int)(((long long)U * c) / 400);
+    } else {
+        return (w * U) / NW;
+    }
+}
+
 // Unit range of 16-lane slot s (wave s/4, slot s%4) among U units of a workgroup;
 // n_it = iterations every slot of that wave runs (the longest slot's count).
 template <int NW>
-I4D_DEVINL void slot_range(int U, int s, int& u0, int& u1, int& n_it) {
+I4D_DEVINL void slot_range(int U, int s, int young, int& u0, int& u1, int& n_it) {
     const int w = s >> 2, t = s & 3;
-    const int wu0 = (w * U) / NW, wu1 = ((w + 1) * U) / NW;
+    const int wu0 = wave_cut<NW>(U, w, young), wu1 = wave_cut<NW>(U, w + 1, young);
     const int n = wu1 - wu0;
     u0 = wu0 + (t * n) / 4;
     u1 = wu0 + ((t + 1) * n) / 4;
@@ -480,17 +502,17 @@ struct LoadCursor {
     RowPtrs rp;
 };
 
-template <int FMT>
+template <int FMT, int KND = -1>
 I4D_DEVINL void cursor_begin(LoadCursor& lc, const GemvTask& t, int q0, int u0, int u1, int S) {
     lc.u = u0; lc.u1 = u1;
     const int ql = u0 / S;
     lc.pair = q0 + ql;
     lc.seg = u0 - ql * S;
-    lc.rp = resolve_pair<FMT>(t, u0 < u1 ? lc.pair : 0);
+    lc.rp = resolve_pair<FMT, KND>(t, u0 < u1 ? lc.pair : 0);
 }
 
 // Load the slot's next unit into dst (if any) and advance.
-template <int FMT>
+template <int FMT, int KND = -1>
 I4D_DEVINL void cursor_load(LoadCursor& lc, Unit<FMT>& dst, const GemvTask& t, int S, int lane16) {
     const bool valid = lc.u < lc.u1;
     load_unit<FMT>(dst, lc.rp, lc.seg, lane16, t.k, t.log2_group, t.a.group, valid, t.a.data, t.a.scales);
@@ -499,7 +521,7 @@ I4D_DEVINL void cursor_load(LoadCursor& lc, Unit<FMT>& dst, const GemvTask& t, i
         if (++lc.seg == S) {
             lc.seg = 0;
             ++lc.pair;
-            if (lc.u < lc.u1) lc.rp = resolve_pair<FMT>(t, lc.pair);
+            if (lc.u < lc.u1) lc.rp = resolve_pair<FMT, KND>(t, lc.pair);
         }
     }
 }
@@ -517,16 +539,16 @@ struct GemvPipe {
 };
 
 // Issue the first D units of pass 0 of task t into the ring.
-template <int FMT, int NT, int D>
+template <int FMT, int NT, int D, int KND = -1>
 I4D_DEVINL void gemv_prime(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg) {
     constexpr int NW = NT / 64;
     const int slot = i4d_tid() >> 4, lane16 = i4d_tid() & 15;
     const int S = (t.k + FmtT<FMT>::UNIT_W - 1) / FmtT<FMT>::UNIT_W;
     pass_pairs_of(t, 0, w, nwg, P.q0, P.q1);
-    slot_range<NW>((P.q1 - P.q0) * S, slot, P.u0, P.u1, P.n_it);
-    cursor_begin<FMT>(P.lc, t, P.q0, P.u0, P.u1, S);
+    slot_range<NW>((P.q1 - P.q0) * S, slot, t.young, P.u0, P.u1, P.n_it);
+    cursor_begin<FMT, KND>(P.lc, t, P.q0, P.u0, P.u1, S);
 #pragma unroll
-    for (int i = 0; i < D; ++i) cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+    for (int i = 0; i < D; ++i) cursor_load<FMT, KND>(P.lc, P.ring[i], t, S, lane16);
 }
 
 struct NoNext { I4D_DEVINL void operator()() {} };
@@ -538,7 +560,7 @@ struct NoNext { I4D_DEVINL void operator()() {} };
 // After the last pass's loads are consumed, next() may prime the ring for the
 // following phase; its loads are then in flight during this epilogue.
 // LDS: act_lds (staged activations), part_lds (NS*MAXJ*NB*2 floats + 2*NS ints).
-template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Epi, class Next>
+template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, int KND = -1, class Epi, class Next>
 I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int nwg, const char* act_lds, float* part_lds,
                             Epi& epi, Next& next) {
     constexpr int NW = NT / 64, NS = NT / 16;
@@ -581,7 +603,7 @@ I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
                         ++run;
                     }
                 }
-                cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+                cursor_load<FMT, KND>(P.lc, P.ring[i], t, S, lane16);
                 // keep each unit's LDS reads next to their use: hoisting the
                 // activation reads of later units costs registers, not time
                 __builtin_amdgcn_sched_barrier(0);
@@ -599,10 +621,10 @@ I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
         // next pass (or next phase): its first D units fly during this epilogue
         if (pass + 1 < t.npasses) {
             pass_pairs_of(t, pass + 1, w, nwg, P.q0, P.q1);
-            slot_range<NW>((P.q1 - P.q0) * S, slot, P.u0, P.u1, P.n_it);
-            cursor_begin<FMT>(P.lc, t, P.q0, P.u0, P.u1, S);
+            slot_range<NW>((P.q1 - P.q0) * S, slot, t.young, P.u0, P.u1, P.n_it);
+            cursor_begin<FMT, KND>(P.lc, t, P.q0, P.u0, P.u1, S);
 #pragma unroll
-            for (int i = 0; i < D; ++i) cursor_load<FMT>(P.lc, P.ring[i], t, S, lane16);
+            for (int i = 0; i < D; ++i) cursor_load<FMT, KND>(P.lc, P.ring[i], t, S, lane16);
         } else {
             next();
         }
@@ -649,23 +671,24 @@ I4D_DEVINL void gemv_passes(GemvPipe<FMT, D>& P, const GemvTask& t, int w, int n
 // One whole phase in a single kernel: activation loads are issued first, then
 // the weight ring, then the activations are staged (waiting only for their own
 // loads), then every pass runs.
-template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, class Stage, class Epi>
+template <int FMT, int NB, int PREC, int NT, int D, int MAXJ, int KND, class Stage, class Epi>
 I4D_DEVINL void gemv_run(const GemvTask& t, int w, int nwg, char* act_lds, float* part_lds, Stage& stage, Epi& epi) {
-    StagePre<FMT> pre;
+    typename Stage::Pre pre;
     stage.issue(pre);
     GemvPipe<FMT, D> P;
-    gemv_prime<FMT, NT, D>(P, t, w, nwg);
+    gemv_prime<FMT, NT, D, KND>(P, t, w, nwg);
     stage.finish(pre);
     __syncthreads();
     NoNext nn;
-    gemv_passes<FMT, NB, PREC, NT, D, MAXJ>(P, t, w, nwg, act_lds, part_lds, epi, nn);
+    gemv_passes<FMT, NB, PREC, NT, D, MAXJ, KND>(P, t, w, nwg, act_lds, part_lds, epi, nn);
 }
 
 // Largest number of runs any slot can see in a pass of `pairs_per_wg` pairs
 // with S units per pair (host-side sizing of passes).
-__host__ inline int gemv_max_runs(int pairs_per_wg, int S, int nw) {
+__host__ inline int gemv_max_runs(int pairs_per_wg, int S, int nw, int young) {
     const long long U = (long long)pairs_per_wg * S;
-    const long long wave_units = (U + nw - 1) / nw;
+    long long wave_units = (U + nw - 1) / nw;
+    if (nw == 8) wave_units = (U * (100 - std::min(young, 50)) + 399) / 400 + 1;
     const long long slot_units = (wave_units + 3) / 4;
     return (int)((slot_units + S - 1) / S) + 1;
 }

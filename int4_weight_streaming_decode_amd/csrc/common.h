@@ -82,6 +82,13 @@ I4D_DEVINL void st_dev(float* p, float v) { st_dev_t(p, v); }
 I4D_DEVINL void st_dev(int* p, int v) { st_dev_t(p, v); }
 I4D_DEVINL void st_dev(uint16_t* p, uint16_t v) { st_dev_t(p, v); }
 I4D_DEVINL void st_dev(u64* p, u64 v) { st_dev_t(p, v); }
+// An output store: write-through (st_dev) when workgroups of the same launch
+// read it, a plain global store when only a later launch does (the kernel
+// boundary makes it visible).
+template <bool WT, class T> I4D_DEVINL void st_out(T* p, T v) {
+    if constexpr (WT) st_dev_t(p, v);
+    else *(I4D_GLOBAL T*)p = v;
+}
 I4D_DEVINL float ld_dev(const float* p) { return ld_dev_t(p); }
 I4D_DEVINL int ld_dev(const int* p) { return ld_dev_t(p); }
 I4D_DEVINL u64 ld_dev(const u64* p) { return ld_dev_t(p); }

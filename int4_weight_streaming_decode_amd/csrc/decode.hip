@@ -62,6 +62,9 @@ struct StageFn {
 constexpr int PREC_STD = 1, PREC_QKV = 2;
 
 // y[b][row] = (resid ? resid[b][row] : 0) + W x   for rows 2p, 2p+1
+// WT: outputs are read by other workgroups of the same launch (persistent
+// kernel) and are written through; one launch per phase stores plainly.
+template <bool WT = true>
 struct EpiRows {
     float* y; const float* resid; int n; int nb;
     I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
@@ -69,18 +72,19 @@ struct EpiRows {
         const int r = 2 * pair;
         float* yr = y + (size_t)b * n;
         const float* rr = resid ? resid + (size_t)b * n : nullptr;
-        st_dev(yr + r, (rr ? rr[r] : 0.f) + va);
-        if (r + 1 < n) st_dev(yr + r + 1, (rr ? rr[r + 1] : 0.f) + vb);
+        st_out<WT>(yr + r, (rr ? rr[r] : 0.f) + va);
+        if (r + 1 < n) st_out<WT>(yr + r + 1, (rr ? rr[r + 1] : 0.f) + vb);
     }
     I4D_DEVINL void end_pass(int, int, int) {}
 };
 
 // act[b][i] = SiLU(gate_i) * up_i
+template <bool WT = true>
 struct EpiSwiGLU {
     float* act; int F; int nb;
     I4D_DEVINL void operator()(int, int pair, int b, float g, float u) {
         if (b >= nb) return;
-        st_dev(act + (size_t)b * F + pair, g / (1.0f + expf(-g)) * u);
+        st_out<WT>(act + (size_t)b * F + pair, g / (1.0f + expf(-g)) * u);
     }
     I4D_DEVINL void end_pass(int, int, int) {}
 };
@@ -123,6 +127,7 @@ struct RopeSetup {
 };
 
 // RoPE on q and k pairs, q to the fp32 buffer, bf16 k/v appended at slot pos[b].
+template <bool WT = true>
 struct EpiQKV {
     float* q; uint16_t* kc; uint16_t* vc; uint16_t* kvn; const int* pos_lds; const float2* cs;
     int cap, hq, hkv, hd, nb;
@@ -142,22 +147,22 @@ struct EpiQKV {
         }
         if (mat == 0) {
             float* qr = q + ((size_t)b * hq + head) * hd;
-            st_dev(qr + i, ra); st_dev(qr + i + half, rb);
+            st_out<WT>(qr + i, ra); st_out<WT>(qr + i + half, rb);
         } else if (p >= 0) {
             const uint16_t ba = f32_to_bf16(ra), bb = f32_to_bf16(rb);
             uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
-            st_dev(nr + i, ba); st_dev(nr + i + half, bb);
+            st_out<WT>(nr + i, ba); st_out<WT>(nr + i + half, bb);
             // 16-position tiles: K [hd/32][16][32], V [hd][16]
             const size_t tile = ((size_t)b * hkv + head) * cap * hd + (size_t)(p >> 4) * 16 * hd;
             const int tp = p & 15;
             if (mat == 1) {
                 uint16_t* kt = kc + tile;
-                st_dev(kt + (i >> 5) * 512 + tp * 32 + (i & 31), ba);
-                st_dev(kt + ((i + half) >> 5) * 512 + tp * 32 + ((i + half) & 31), bb);
+                st_out<WT>(kt + (i >> 5) * 512 + tp * 32 + (i & 31), ba);
+                st_out<WT>(kt + ((i + half) >> 5) * 512 + tp * 32 + ((i + half) & 31), bb);
             } else {
                 uint16_t* vt = vc + tile;
-                st_dev(vt + (size_t)i * 16 + tp, ba);
-                st_dev(vt + (size_t)(i + half) * 16 + tp, bb);
+                st_out<WT>(vt + (size_t)i * 16 + tp, ba);
+                st_out<WT>(vt + (size_t)(i + half) * 16 + tp, bb);
             }
         }
     }
@@ -223,7 +228,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_rows(GemvTask t, const float* 
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, x, x_stride, t.k, nb, gain, eps, L.red};
-    EpiRows ep{y, resid, t.a.n, nb};
+    EpiRows<false> ep{y, resid, t.a.n, nb};
     gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_ADJ>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -232,7 +237,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiSwiGLU ep{act, t.a.n, nb};
+    EpiSwiGLU<false> ep{act, t.a.n, nb};
     gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_TWO>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -246,7 +251,7 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
     float2* cs = (float2*)(L.extra + 64);
     RopeSetup<NB>{pos, pos_lds, cs, status, nb, max_pos, cap, t.head_dim, base}();
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
+    EpiQKV<false> ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
     gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_QKV>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -487,7 +492,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, attn_norm);
             stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, attn_norm, A.eps, L.red);
             __syncthreads();
-            EpiQKV ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
+            EpiQKV<true> ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
             NoNext nn;
             gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ, KIND_QKV>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
         }
@@ -508,7 +513,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_issue<FMT, NB, PERS_NT>(pre, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr);
             stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
             __syncthreads();
-            EpiRows ep{y, xin, A.d_model, A.batch};
+            EpiRows<true> ep{y, xin, A.d_model, A.batch};
             PrimeNext<NB, KIND_TWO> nx{P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, true};
             gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg, L.act, L.part, ep, nx);
         }
@@ -519,7 +524,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_issue<FMT, NB, PERS_NT>(pre, y, A.d_model, A.d_model, A.batch, ffn_norm);
             stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, y, A.d_model, A.d_model, A.batch, ffn_norm, A.eps, L.red);
             __syncthreads();
-            EpiSwiGLU ep{act, A.d_ff, A.batch};
+            EpiSwiGLU<true> ep{act, A.d_ff, A.batch};
             PrimeNext<NB, KIND_ADJ> nx{P, task_of(A.td, Ly, 6, -1, -1), w, nwg, true};
             gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_TWO>(P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, L.act, L.part, ep, nx);
         }
@@ -530,7 +535,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_issue<FMT, NB, PERS_NT>(pre, act, A.d_ff, A.d_ff, A.batch, nullptr);
             stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, act, A.d_ff, A.d_ff, A.batch, nullptr, 0.f, L.red);
             __syncthreads();
-            EpiRows ep{xout, y, A.d_model, A.batch};
+            EpiRows<true> ep{xout, y, A.d_model, A.batch};
             const bool more = l + 1 < A.n_layers;
             PrimeNext<NB, KIND_QKV> nx{P, task_of(A.tq, more ? A.layers[l + 1] : Ly, 0, 1, 2), w, nwg, more};
             gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.td, Ly, 6, -1, -1), w, nwg, L.act, L.part, ep, nx);
@@ -729,6 +734,7 @@ GemvTask make_task(int kind, const i4d_mat* a, const i4d_mat* b, const i4d_mat* 
     t.b = b ? dev_mat(*b) : t.a;
     t.c = c ? dev_mat(*c) : t.a;
     t.k = a->k;
+    t.pitch_k = a->k;
     t.log2_group = (a->dtype == I4D_WEIGHT_INT4) ? ilog2(a->group) : 0;
     t.head_dim = head_dim;
     if (kind == KIND_ADJ) t.total_pairs = (a->n + 1) / 2;
@@ -858,6 +864,68 @@ int launch_rows(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int
     I4D_DISPATCH(fmt, nb, CALL)
 #undef CALL
 }
+size_t rows_lds_bytes(int fmt, int nb, int K) {
+#define CALL(F, N) return gemv_lds_bytes<F, N, PREC_STD>(K)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+
+// y = resid + W x through k_gemv_rows, in `c` equal K-chunks when the staged
+// activations of the whole row would not fit in LDS (large K with several
+// sequences): chunk 0 adds resid, every later chunk adds onto y in place (the
+// same thread reads and writes each element), so the sum order is fixed.
+int chunk_count(int fmt, int nb, int K, int group) {
+    if (rows_lds_bytes(fmt, nb, K) <= LDS_LIMIT) return 1;
+    if (fmt != FMT_INT4_FAST && fmt != FMT_BF16_FAST) return 0;
+    for (int c = 2; c <= 16; ++c) {
+        if (K % c) continue;
+        const int kc = K / c;
+        if (kc % unit_w(fmt)) continue;
+        if (fmt == FMT_INT4_FAST && (kc % group || (kc / group) % 2)) continue;
+        if (rows_lds_bytes(fmt, nb, kc) <= LDS_LIMIT) return c;
+    }
+    return 0;
+}
+
+size_t qkv_lds_bytes(int fmt, int nb, int K) {
+#define CALL(F, N) return gemv_lds_bytes<F, N, PREC_QKV>(K)
+    I4D_DISPATCH(fmt, nb, CALL)
+#undef CALL
+}
+
+// Host check, before anything is enqueued, that every phase of a layer fits
+// the per-workgroup LDS at this batch (the row GEMVs may split K).
+int phases_fit(const i4d_layer* L, int batch) {
+    const int nb = nb_slot(batch);
+    if (qkv_lds_bytes(pick_fmt(L->wq, L->wk, &L->wv), nb, L->wq.k) > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (rows_lds_bytes(pick_fmt(L->wg, L->wu), nb, L->wg.k) > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (chunk_count(pick_fmt(L->wo), nb, L->wo.k, L->wo.group) == 0) return I4D_EUNSUPPORTED;
+    if (chunk_count(pick_fmt(L->wd), nb, L->wd.k, L->wd.group) == 0) return I4D_EUNSUPPORTED;
+    return I4D_OK;
+}
+
+int launch_rows_chunked(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int x_stride, int bn, float* y,
+                        const float* resid, int young, hipStream_t s) {
+    const int c = chunk_count(fmt, nb, t.k, t.a.group);
+    if (c == 0) return I4D_EUNSUPPORTED;
+    const int kc = t.k / c;
+    for (int i = 0; i < c; ++i) {
+        GemvTask tc = t;
+        tc.k = kc;
+        if (fmt == FMT_INT4_FAST) {
+            tc.a.data += (size_t)i * (kc >> 1);
+            tc.a.scales += (size_t)i * (kc / t.a.group);
+        } else if (fmt == FMT_BF16_FAST) {
+            tc.a.data += (size_t)i * kc * 2;
+        }
+        tc.b = tc.a; tc.c = tc.a;
+        plan_passes(tc, fmt, nb, nwg, 0, GEMV_NT, young);
+        const int rc = launch_rows(fmt, nb, tc, nwg, x + (size_t)i * kc, x_stride, bn, nullptr, 0.f, y, i == 0 ? resid : y, s);
+        if (rc) return rc;
+    }
+    return I4D_OK;
+}
+
 int launch_swiglu(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int bn, const uint16_t* gain, float eps, float* act,
                   hipStream_t s) {
 #define CALL(F, N) return launch_swiglu_t<F, N>(t, nwg, x, bn, gain, eps, act, s)
@@ -1077,10 +1145,9 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
     const int fo = pick_fmt(L->wo);
-    plan_passes(to, fo, nb, nwg, 0, GEMV_NT, 40);
     {
         TimeScope ts(I4D_TIME_WO);
-        rc = launch_rows(fo, nb, to, nwg, o, c->n_q_heads * hd, B, nullptr, 0.f, y, x_in, s);
+        rc = launch_rows_chunked(fo, nb, to, nwg, o, c->n_q_heads * hd, B, y, x_in, 40, s);
     }
     if (rc) return rc;
 
@@ -1095,9 +1162,8 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 
     GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
     const int fd = pick_fmt(L->wd);
-    plan_passes(td, fd, nb, nwg, 0, GEMV_NT, 40);
     TimeScope ts(I4D_TIME_DOWN);
-    return launch_rows(fd, nb, td, nwg, act, c->d_ff, B, nullptr, 0.f, x_out, y, s);
+    return launch_rows_chunked(fd, nb, td, nwg, act, c->d_ff, B, x_out, y, 40, s);
 }
 
 }  // namespace
@@ -1140,6 +1206,7 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if ((rc = validate_layer(cfg, &layers[l]))) return rc;
         if (layers[l].wq.dtype != layers[0].wq.dtype) return I4D_EINVAL;
         if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
+        if (cfg->exec_mode != 2 && (rc = phases_fit(&layers[l], batch))) return rc;
     }
     if (batch * cfg->n_kv_heads > WS_MAX_CNT) return I4D_EUNSUPPORTED;
     const WsLayout W = ws_layout(cfg, n_layers, batch);

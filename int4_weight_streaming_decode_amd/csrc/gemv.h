@@ -47,6 +47,7 @@ struct GemvTask {
     int kind;                  // KIND_*
     DevMat a, b, c;            // ADJ: a.  TWO: rows of a paired with rows of b.  QKV: q, k, v.
     int k;                     // inputs per row (all matrices of the task)
+    int pitch_k;               // inputs per row in memory (k, or more when the task covers a K-chunk)
     int log2_group;            // fast int4 path: group = 1 << log2_group
     int head_dim;              // QKV pairing
     int total_pairs;
@@ -104,7 +105,7 @@ I4D_DEVINL RowPtrs resolve_pair(const GemvTask& t, int pair) {
         rb = ra + half;
         db = da; sb = sa; gb = ga;
     }
-    const size_t row_bytes = FmtT<FMT>::INT4 ? (size_t)(t.k >> 1) : (size_t)t.k * 2;
+    const size_t row_bytes = FmtT<FMT>::INT4 ? (size_t)(t.pitch_k >> 1) : (size_t)t.pitch_k * 2;
     RowPtrs r;
     r.pa = da + (size_t)ra * row_bytes;
     r.pb = db + (size_t)rb * row_bytes;

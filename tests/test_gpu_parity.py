@@ -156,6 +156,29 @@ def test_decode_layer_matches_oracle(name, batch, pos, dtype):
     assert B.read_device_status(ws) == 0
 
 
+def test_decode_layer_splits_wide_rows_over_k():
+    """Batch 4 at the 70B FFN width (d_ff 28672): the staged activations of
+    W_down (4 x 28672 inputs) exceed one workgroup's LDS, so W_down runs in
+    K-chunks that add onto the output in a fixed order."""
+    _print_case("decode_layer wide ffn")
+    shape = synth.SHAPES["tiny"].with_(name="wide_ffn", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                                       d_ff=28672, group=128, rope_base=5e5)
+    pos = [300, 17, 299, 128]
+    batch = len(pos)
+    layers, caches, x = _layer_case(shape, 131, batch, pos)
+    ref = oracle.decode_layer(shape, layers[0], x.astype(np.float64), caches[0][0], caches[0][1], pos)
+    L = DevLayer(layers[0])
+    kvd = DevKV(*caches[0])
+    cfg = config_of(shape)
+    ws = workspace(cfg, batch, max(pos))
+    out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+    B.decode_layer(cfg, L.layer, batch, dev(x), out, kvd.kv, dev(np.array(pos, dtype=np.int32)), max(pos), ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref["z"], what="wide-ffn layer output")
+    _check_kv(kvd, caches[0], (ref["k_cache"], ref["v_cache"]), pos, "wide-ffn layer")
+    assert B.read_device_status(ws) == 0
+
+
 def test_decode_stack_matches_oracle_and_is_deterministic():
     shape = synth.SHAPES["tiny"].with_(n_layers=3)
     pos = [127]

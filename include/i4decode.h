@@ -61,8 +61,9 @@ extern "C" {
 #define I4D_EHIP         -5   /* a HIP launch failed (hipGetLastError) */
 #define I4D_EUNSUPPORTED -6   /* valid request this build does not implement */
 
-/* smallest workspace any entry point accepts (header + LM-head argmax keys) */
-#define I4D_WS_MIN_BYTES (8192 + 4096 * 8 * 8)
+/* smallest workspace any entry point accepts (header + LM-head argmax keys);
+ * batches above 8 need more (i4d_workspace_size) */
+#define I4D_WS_MIN_BYTES (16384 + 4096 * 32 * 8)
 
 /* device status word bits (i4d_read_device_status) */
 #define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
@@ -134,7 +135,15 @@ size_t i4d_workspace_size(const i4d_config* cfg, int32_t n_layers, int32_t batch
  * hipMemset).  Needed once per workspace.                                   */
 int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
-/* One decoder layer for `batch` sequences (1 <= batch <= 8).
+/* One decoder layer for `batch` sequences (1 <= batch <= 32).
+ * Batches of 1..8 stream the weights through the vector-ALU matrix-vector
+ * core.  Batches of 9..32 run each projection as an int4 dequant-GEMM on the
+ * matrix cores (the roofline reply, 二-三: batching raises the arithmetic
+ * intensity past what the vector units sustain); that path needs int4
+ * weights with a power-of-two group >= 128, an even number of groups per
+ * row, 4-byte aligned scales, and d_model, d_ff and n_q_heads*head_dim
+ * multiples of 128 (I4D_EUNSUPPORTED otherwise, before anything is
+ * enqueued).
  *   x_in  [B][D] fp32: hidden state of each sequence's new token.
  *   x_out [B][D] fp32: layer output z; must not alias x_in.
  *   pos   [B] int32 (device): number of cached tokens = position of the new
@@ -162,8 +171,10 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
  * registers of the workgroup that computed it (each keeps a running argmax),
  * so the vocabulary is swept in passes as large as the kernel's per-workgroup
  * budget allows whatever chunk_rows is (chunk_rows > 0 is still required).
- * The result does not depend on chunk_rows.  1 <= batch <= 8.
- * ws_bytes >= I4D_WS_MIN_BYTES.                                              */
+ * The result does not depend on chunk_rows.  1 <= batch <= 32; batches above
+ * 8 run on the matrix cores (same weight conditions as i4d_decode_layer) and
+ * need ws_bytes >= i4d_workspace_size(cfg, 1, batch, 0, V) for D = k;
+ * otherwise ws_bytes >= I4D_WS_MIN_BYTES.                                    */
 int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
                         int32_t* token_out, float* max_logit_out,
                         void* ws, size_t ws_bytes, void* stream);
@@ -172,9 +183,11 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
  * (Unsloth article 二.3).  A test hook for the int4 format.                 */
 int i4d_dequant_int4(const i4d_mat* w, float* out, void* stream);
 
-/* Plain y[b] = W x[b] through the streaming matrix-vector core (x [B][k],
- * y [B][n] fp32, 1 <= batch <= 8).  A test hook for the core every
- * projection of the layer uses.                                             */
+/* Plain y[b] = W x[b] through the core every projection of the layer uses
+ * (x [B][k], y [B][n] fp32, 1 <= batch <= 32).  A test hook.  Batches of 1..8
+ * take the matrix-vector core and ignore ws; batches of 9..32 take the
+ * matrix-core GEMM (conditions as for i4d_decode_layer) and need an
+ * initialised workspace of at least 2 MiB + 128 * k * (1 + n / 64) bytes.    */
 int i4d_gemv(const i4d_mat* w, int32_t batch, const float* x, float* y,
              void* ws, size_t ws_bytes, void* stream);
 

@@ -20,7 +20,7 @@ I4D_EWORKSPACE = -3
 I4D_ERANGE = -4
 I4D_EHIP = -5
 I4D_EUNSUPPORTED = -6
-WS_MIN_BYTES = 8192 + 4096 * 8 * 8    # I4D_WS_MIN_BYTES
+WS_MIN_BYTES = 16384 + 4096 * 32 * 8    # I4D_WS_MIN_BYTES
 I4D_DEV_BAD_POS = 1
 I4D_DEV_BARRIER_TIMEOUT = 2
 

@@ -11,6 +11,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemv.h"
+#include "mfma.h"
 
 namespace {
 
@@ -34,7 +35,8 @@ constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
 constexpr int ATTN_NT = I4D_ATTN_NT;       // threads per attention workgroup
 constexpr int WG_PER_CU = I4D_WG_PER_CU;   // GEMV workgroups per compute unit
 constexpr int NSPLIT_MAX = 128;    // key-axis splits per (sequence, KV head)
-constexpr int MAX_BATCH = 8;
+constexpr int MAX_BATCH = 8;          // matrix-vector (VALU) path
+constexpr int MAX_BATCH_ALL = 32;     // batches above MAX_BATCH take the MFMA path
 
 template <int NB> struct MaxJ { static constexpr int v = NB <= 2 ? 8 : 4; };
 
@@ -277,12 +279,12 @@ __global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h,
 }
 
 // Reduce the per-workgroup argmax keys: token = lowest id of the largest logit.
-__global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg, int nb, int32_t* token_out, float* max_out) {
+__global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg, int kstride, int nb, int32_t* token_out, float* max_out) {
     __shared__ u64 red[256];
     for (int b = 0; b < nb; ++b) {
         u64 best = 0;
         for (int w = i4d_tid(); w < nwg; w += 256) {
-            const u64 k = wg_keys[(size_t)w * MAX_BATCH + b];
+            const u64 k = wg_keys[(size_t)w * kstride + b];
             best = k > best ? k : best;
         }
         red[i4d_tid()] = best;
@@ -309,6 +311,38 @@ __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
     for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW>(a, it, lds, R, false);
 }
 
+// ---------------------------------------------------------------- batched (MFMA) phases
+template <int NB>
+__global__ void __launch_bounds__(512) k_mfma_rows(MfmaTask m, float* y, const float* resid) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiRows<false> ep{y, resid, m.t.a.n, m.nb};
+    mfma_gemm<KIND_ADJ, NB, 1, MEPI_FN>(m, lds, ep, nullptr);
+}
+
+template <int NB>
+__global__ void __launch_bounds__(512) k_mfma_swiglu(MfmaTask m, float* act) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiSwiGLU<false> ep{act, m.t.a.n, m.nb};
+    mfma_gemm<KIND_TWO, NB, 1, MEPI_FN>(m, lds, ep, nullptr);
+}
+
+// q/k/v with RoPE and the KV append; positions (validated, -1 = skipped) and
+// the cos/sin table come from the staging kernel
+template <int NB>
+__global__ void __launch_bounds__(512) k_mfma_qkv(MfmaTask m, float* q, uint16_t* kc, uint16_t* vc, uint16_t* kvn,
+                                                  const int* posv, const float2* cs, int cap, int hq, int hkv) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiQKV<false> ep{q, kc, vc, kvn, posv, cs, cap, hq, hkv, m.t.head_dim, m.nb};
+    mfma_gemm<KIND_QKV, NB, 2, MEPI_FN>(m, lds, ep, nullptr);
+}
+
+template <int NB>
+__global__ void __launch_bounds__(512) k_mfma_lm(MfmaTask m, u64* wg_keys) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    NoNext none;
+    mfma_gemm<KIND_ADJ, NB, 1, MEPI_ARGMAX>(m, lds, none, wg_keys);
+}
+
 // Workspace: an 8 KB header (status word, grid-barrier epoch, the attention
 // arrival counters, barrier flags), the persistent kernel's layer table, then
 // one region of buffers per layer.  The LM head uses the bytes after the header
@@ -316,12 +350,14 @@ __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
 // buffers: calls on one stream never use both at once.  The counters sit in
 // the header because they must read zero at the start of every attention
 // phase (each merge resets its own).
-constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_CNT = 1024, WS_FLAGS = 4096, WS_HEADER = 8192;
+constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_CNT = 1024, WS_FLAGS = 4096, WS_MCNT = 8192, WS_HEADER = 16384;
 constexpr int WS_MAX_CNT = (int)((WS_FLAGS - WS_CNT) / 4);     // B * Hkv arrival counters
+constexpr int WS_MAX_MCNT = (int)((WS_HEADER - WS_MCNT) / 4);  // row-block arrival counters of the batched GEMM
 constexpr int PERS_MAX_WG = 1024;                    // flags: one int per workgroup of the persistent kernel
 constexpr int PERS_MAX_LAYERS = 256;
 constexpr int LM_MAX_WG = 4096;
-constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH * 8;
+constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH_ALL * 8;
+constexpr size_t WS_LM_END = WS_LM_KEYS + WS_LM_BYTES;   // batched-GEMM scratch of the LM head and the GEMV hook
 
 // ============================================================== persistent decode kernel
 // One cooperative launch runs every layer of the step: 256 workgroups (one per
@@ -565,11 +601,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
     size_t table;
+    size_t mfma;                          // scratch of the batched (MFMA) phases, batches above MAX_BATCH
     size_t layer0, layer_stride;          // per-layer regions
     size_t q, o, y, act, x, kvn, pm, pl, po;   // offsets inside a layer region
     int pstride;                          // attention partials per head (>= splits, multiple of 32)
     size_t total;
 };
+
+int nb_mfma(int batch);
+size_t layer_scratch_bytes(const i4d_config* c, int nb);
 
 // Most key-axis splits plan_attention picks for this shape and batch.
 int attn_splits_max(const i4d_config* c, int B) {
@@ -604,7 +644,13 @@ WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     w.layer_stride = lo;
     w.layer0 = off;
     off += (size_t)std::max(n_layers, 1) * lo;
-    w.total = std::max(off, WS_LM_KEYS + WS_LM_BYTES);
+    w.mfma = 0;
+    if (B > MAX_BATCH) {                  // after the LM head's keys, which overlay the layer regions
+        off = std::max(off, WS_LM_END);
+        w.mfma = off;
+        off += layer_scratch_bytes(c, nb_mfma(B));
+    }
+    w.total = std::max(off, WS_LM_END);
     return w;
 }
 
@@ -853,7 +899,7 @@ int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys
         if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
         if (set_lds(k_lm_head<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
         launch_k(k_lm_head<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys);
-        hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, nb, tok, mx);
+        hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, MAX_BATCH, nb, tok, mx);
         return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
     }
 }
@@ -984,6 +1030,180 @@ int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
         launch_k(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
     }
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// ---------------------------------------------------------------- batched (MFMA) path
+// Batches of 9..32 sequences (padded to 16 or 32 MFMA columns).  Each
+// projection is a staging launch (norm, fp16 conversion)
+// followed by the MFMA GEMM with the same epilogue as the matrix-vector path.
+bool mfma_mat_ok(const i4d_mat& m) {
+    return m.dtype == I4D_WEIGHT_INT4 && m.k % 128 == 0 && is_pow2(m.group) && m.group >= 128 && (m.k / m.group) % 2 == 0 &&
+           aligned(m.scales, 4) && aligned(m.data, 16);
+}
+int nb_mfma(int batch) { return batch <= 16 ? 16 : 32; }
+
+struct MfmaPlan { int tiles, rbs, kb, spb, nsteps, nwg; };
+
+// Row blocks of 8*RT tiles; the K axis is split over workgroups (at least two
+// LDS chunks per block) until the grid covers every compute unit.
+MfmaPlan mfma_plan(int total_pairs, int K, int nb, int prec, bool split) {
+    MfmaPlan p;
+    const int tb = nb == 32 ? MfmaGeo<32, 1>::TB : MfmaGeo<16, 1>::TB;
+    const int sc = (nb == 16 && prec == 1) ? MfmaGeo<16, 1>::SC : MfmaGeo<32, 1>::SC;
+    p.tiles = (total_pairs + 7) / 8;
+    p.rbs = (p.tiles + tb - 1) / tb;
+    p.nsteps = K / 128;
+    int kb = 1;
+    if (split && p.rbs < num_cus()) {
+        kb = (num_cus() + p.rbs - 1) / p.rbs;
+        kb = std::min(kb, std::max(1, p.nsteps / (2 * sc)));
+    }
+    p.spb = (p.nsteps + kb - 1) / kb;
+    p.kb = (p.nsteps + p.spb - 1) / p.spb;
+    p.nwg = p.rbs * p.kb;
+    return p;
+}
+size_t mfma_part_bytes(const MfmaPlan& p, int nb) { return p.kb > 1 ? (size_t)p.tiles * p.kb * nb * 16 * 4 : 0; }
+
+// Scratch of one batched phase: staged activations (up to two planes),
+// partial sums, validated positions and the RoPE table.
+struct MfmaScratch { size_t xs, part, posv, cs, total; };
+MfmaScratch mfma_scratch(int kmax, int nb, size_t part_bytes, int hd) {
+    MfmaScratch m;
+    size_t off = 0;
+    auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+    m.xs = take((size_t)2 * nb * kmax * 2);
+    m.part = take(part_bytes);
+    m.posv = take((size_t)nb * 4);
+    m.cs = take((size_t)nb * (hd / 2) * 8);
+    m.total = off;
+    return m;
+}
+MfmaScratch layer_scratch(const i4d_config* c, int nb) {
+    const int D = c->d_model, qw = c->n_q_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim, F = c->d_ff;
+    size_t part = 0;
+    part = std::max(part, mfma_part_bytes(mfma_plan((qw + 2 * kvw) / 2, D, nb, 2, true), nb));
+    part = std::max(part, mfma_part_bytes(mfma_plan((D + 1) / 2, qw, nb, 1, true), nb));
+    part = std::max(part, mfma_part_bytes(mfma_plan(F, D, nb, 1, true), nb));
+    part = std::max(part, mfma_part_bytes(mfma_plan((D + 1) / 2, F, nb, 1, true), nb));
+    return mfma_scratch(std::max(std::max(D, qw), F), nb, part, c->head_dim);
+}
+
+size_t layer_scratch_bytes(const i4d_config* c, int nb) { return layer_scratch(c, nb).total; }
+
+MfmaTask mfma_task(const GemvTask& t, const MfmaPlan& p, char* base, const MfmaScratch& S, int* cnt, int batch, int group) {
+    MfmaTask m;
+    memset(&m, 0, sizeof(m));
+    m.t = t;
+    m.xs = (const uint32_t*)(base + S.xs);
+    m.part = (float*)(base + S.part);
+    m.cnt = cnt;
+    m.tiles = p.tiles; m.kb = p.kb; m.spb = p.spb; m.nsteps = p.nsteps;
+    m.gshift = ilog2(group) - 7;
+    m.nb = batch;
+    return m;
+}
+
+int mfma_stage(int prec, int nb, const float* x, int stride, int batch, int K, const uint16_t* gain, float eps, char* base,
+               const MfmaScratch& S, const int* pos, int max_pos, int cap, int hd, double rope_base, bool rope, int* status,
+               hipStream_t s) {
+    uint32_t* xs = (uint32_t*)(base + S.xs);
+    int* posv = rope ? (int*)(base + S.posv) : nullptr;
+    float2* cs = rope ? (float2*)(base + S.cs) : nullptr;
+    if (prec == 2)
+        hipLaunchKernelGGL(k_mfma_stage<2>, dim3(nb), dim3(256), 0, s, x, stride, batch, nb, K, gain, eps, xs, pos, max_pos,
+                           cap, hd, rope_base, posv, cs, status);
+    else
+        hipLaunchKernelGGL(k_mfma_stage<1>, dim3(nb), dim3(256), 0, s, x, stride, batch, nb, K, gain, eps, xs, pos, max_pos,
+                           cap, hd, rope_base, posv, cs, status);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+template <class Kern, class... A>
+int launch_mfma(Kern kernel, size_t lds, const MfmaPlan& p, hipStream_t s, A... args) {
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (p.kb > 1 && p.rbs > WS_MAX_MCNT) return I4D_EUNSUPPORTED;
+    if (set_lds(kernel, lds) != hipSuccess) return I4D_EHIP;
+    launch_k(kernel, dim3(p.nwg), dim3(MfmaGeo<16, 1>::NT), lds, s, args...);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int mfma_rows(int nb, const MfmaTask& m, const MfmaPlan& p, float* y, const float* resid, hipStream_t s) {
+    return nb == 16 ? launch_mfma(k_mfma_rows<16>, MfmaGeo<16, 1>::LDS_B, p, s, m, y, resid)
+                    : launch_mfma(k_mfma_rows<32>, MfmaGeo<32, 1>::LDS_B, p, s, m, y, resid);
+}
+
+bool mfma_layer_ok(const i4d_config* c, const i4d_layer* L) {
+    const i4d_mat* m[7] = {&L->wq, &L->wk, &L->wv, &L->wo, &L->wg, &L->wu, &L->wd};
+    for (int i = 0; i < 7; ++i)
+        if (!mfma_mat_ok(*m[i])) return false;
+    return c->d_model % 128 == 0 && c->d_ff % 128 == 0 && (c->n_q_heads * c->head_dim) % 128 == 0;
+}
+
+// One layer for 9..32 sequences: staging + MFMA GEMM per projection, the
+// split-K attention in between (which handles any batch).
+int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
+                   const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s) {
+    const int nb = nb_mfma(B), hd = c->head_dim;
+    const int D = c->d_model, qw = c->n_q_heads * hd, F = c->d_ff, g = L->wq.group;
+    int* status = (int*)(ws + WS_STATUS);
+    int* cnt = (int*)(ws + WS_MCNT);
+    char* base = ws + W.mfma;
+    const MfmaScratch S = layer_scratch(c, nb);
+    uint16_t* kvn = (uint16_t*)(R + W.kvn);
+    float* q = (float*)(R + W.q);
+    float* o = (float*)(R + W.o);
+    float* y = (float*)(R + W.y);
+    float* act = (float*)(R + W.act);
+    int rc;
+
+    if ((rc = mfma_stage(2, nb, x_in, D, B, D, L->attn_norm, c->rms_eps, base, S, pos, max_pos, kv->capacity, hd, c->rope_base,
+                         true, status, s)))
+        return rc;
+    const GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
+    const MfmaPlan pq = mfma_plan(tq.total_pairs, D, nb, 2, true);
+    const MfmaTask mq = mfma_task(tq, pq, base, S, cnt, B, g);
+    const int* posv = (const int*)(base + S.posv);
+    const float2* cs = (const float2*)(base + S.cs);
+    {
+        TimeScope ts(I4D_TIME_QKV);
+        rc = nb == 16 ? launch_mfma(k_mfma_qkv<16>, MfmaGeo<16, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
+                                    c->n_q_heads, c->n_kv_heads)
+                      : launch_mfma(k_mfma_qkv<32>, MfmaGeo<32, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
+                                    c->n_q_heads, c->n_kv_heads);
+    }
+    if (rc) return rc;
+    {
+        TimeScope ts(I4D_TIME_ATTENTION);
+        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s);
+    }
+    if (rc) return rc;
+
+    if ((rc = mfma_stage(1, nb, o, qw, B, qw, nullptr, 0.f, base, S, nullptr, 0, 0, hd, 0.0, false, status, s))) return rc;
+    const GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
+    const MfmaPlan po = mfma_plan(to.total_pairs, qw, nb, 1, true);
+    {
+        TimeScope ts(I4D_TIME_WO);
+        rc = mfma_rows(nb, mfma_task(to, po, base, S, cnt, B, g), po, y, x_in, s);
+    }
+    if (rc) return rc;
+
+    if ((rc = mfma_stage(1, nb, y, D, B, D, L->ffn_norm, c->rms_eps, base, S, nullptr, 0, 0, hd, 0.0, false, status, s))) return rc;
+    const GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
+    const MfmaPlan pg = mfma_plan(tg.total_pairs, D, nb, 1, true);
+    const MfmaTask mg = mfma_task(tg, pg, base, S, cnt, B, g);
+    {
+        TimeScope ts(I4D_TIME_GATE_UP);
+        rc = nb == 16 ? launch_mfma(k_mfma_swiglu<16>, MfmaGeo<16, 1>::LDS_B, pg, s, mg, act)
+                      : launch_mfma(k_mfma_swiglu<32>, MfmaGeo<32, 1>::LDS_B, pg, s, mg, act);
+    }
+    if (rc) return rc;
+
+    if ((rc = mfma_stage(1, nb, act, F, B, F, nullptr, 0.f, base, S, nullptr, 0, 0, hd, 0.0, false, status, s))) return rc;
+    const GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
+    const MfmaPlan pd = mfma_plan(td.total_pairs, F, nb, 1, true);
+    TimeScope ts(I4D_TIME_DOWN);
+    return mfma_rows(nb, mfma_task(td, pd, base, S, cnt, B, g), pd, x_out, y, s);
 }
 
 // ---------------------------------------------------------------- persistent launch
@@ -1172,10 +1392,12 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
 extern "C" {
 
 size_t i4d_workspace_size(const i4d_config* cfg, int32_t n_layers, int32_t batch, int32_t max_pos, int32_t vocab) {
-    if (validate_cfg(cfg) || n_layers < 1 || batch < 1 || batch > MAX_BATCH || max_pos < 0) return 0;
+    if (validate_cfg(cfg) || n_layers < 1 || batch < 1 || batch > MAX_BATCH_ALL || max_pos < 0 || vocab < 0) return 0;
     if (batch * cfg->n_kv_heads > WS_MAX_CNT) return 0;
-    (void)vocab;
-    return ws_layout(cfg, n_layers, batch).total;
+    size_t total = ws_layout(cfg, n_layers, batch).total;
+    if (batch > MAX_BATCH && vocab > 0)
+        total = std::max(total, WS_LM_END + mfma_scratch(cfg->d_model, nb_mfma(batch), 0, 64).total);
+    return total;
 }
 
 int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -1198,7 +1420,7 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
     if (n_layers < 1 || !layers || !kv) return I4D_EINVAL;
-    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (batch < 1 || batch > MAX_BATCH_ALL) return I4D_ERANGE;
     if (!x_in || !x_out || !pos || x_in == x_out) return I4D_EINVAL;
     if (!aligned(x_in, 16) || !aligned(x_out, 16) || !aligned(pos, 4)) return I4D_EALIGN;
     if (cfg->d_model % 8 != 0 || cfg->d_ff % 8 != 0) return I4D_EINVAL;
@@ -1206,7 +1428,11 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if ((rc = validate_layer(cfg, &layers[l]))) return rc;
         if (layers[l].wq.dtype != layers[0].wq.dtype) return I4D_EINVAL;
         if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
-        if (cfg->exec_mode != 2 && (rc = phases_fit(&layers[l], batch))) return rc;
+        if (batch > MAX_BATCH) {
+            if (!mfma_layer_ok(cfg, &layers[l])) return I4D_EUNSUPPORTED;
+        } else if (cfg->exec_mode != 2 && (rc = phases_fit(&layers[l], batch))) {
+            return rc;
+        }
     }
     if (batch * cfg->n_kv_heads > WS_MAX_CNT) return I4D_EUNSUPPORTED;
     const WsLayout W = ws_layout(cfg, n_layers, batch);
@@ -1223,7 +1449,9 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         char* R = w + W.layer0 + (size_t)l * W.layer_stride;
         const float* in = (l == 0) ? x_in : (const float*)(R - W.layer_stride + W.x);
         float* out = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
-        if ((rc = run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s))) return rc;
+        rc = batch > MAX_BATCH ? run_layer_mfma(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s)
+                               : run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s);
+        if (rc) return rc;
     }
     return I4D_OK;
 }
@@ -1234,11 +1462,36 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
     int rc;
     if ((rc = validate_mat(w_lm, w_lm->n, w_lm->k, I4D_WEIGHT_INT4, w_lm->group))) return rc;
     if (w_lm->n < 1 || w_lm->k < 8) return I4D_EINVAL;
-    if (batch < 1 || batch > MAX_BATCH || chunk_rows <= 0) return I4D_ERANGE;
+    if (batch < 1 || batch > MAX_BATCH_ALL || chunk_rows <= 0) return I4D_ERANGE;
     if (!h || !token_out || !max_logit_out) return I4D_EINVAL;
     if (!aligned(h, 16)) return I4D_EALIGN;
     if ((rc = validate_ws(ws, ws_bytes, WS_LM_KEYS + WS_LM_BYTES))) return rc;
     char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    if (batch > MAX_BATCH) {
+        // batched: staging + MFMA GEMM with per-lane argmax keys (the K axis is not split)
+        if (!mfma_mat_ok(*w_lm)) return I4D_EUNSUPPORTED;
+        const int nb = nb_mfma(batch);
+        const MfmaScratch S = mfma_scratch(w_lm->k, nb, 0, 64);
+        if ((rc = validate_ws(ws, ws_bytes, WS_LM_END + S.total))) return rc;
+        const GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
+        const MfmaPlan p = mfma_plan(t.total_pairs, w_lm->k, nb, 1, false);
+        if (p.nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
+        char* base = w + WS_LM_END;
+        if ((rc = mfma_stage(1, nb, h, w_lm->k, batch, w_lm->k, nullptr, 0.f, base, S, nullptr, 0, 0, 64, 0.0, false,
+                             (int*)(w + WS_STATUS), s)))
+            return rc;
+        const MfmaTask m = mfma_task(t, p, base, S, nullptr, batch, w_lm->group);
+        u64* keys = (u64*)(w + WS_LM_KEYS);
+        {
+            TimeScope ts(I4D_TIME_LM_HEAD);
+            rc = nb == 16 ? launch_mfma(k_mfma_lm<16>, MfmaGeo<16, 1>::LDS_B, p, s, m, keys)
+                          : launch_mfma(k_mfma_lm<32>, MfmaGeo<32, 1>::LDS_B, p, s, m, keys);
+        }
+        if (rc) return rc;
+        hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)keys, p.nwg, nb, batch, token_out, max_logit_out);
+        return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+    }
     const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
     GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
     const int fmt = pick_fmt(*w_lm);
@@ -1248,7 +1501,7 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
     plan_passes(t, fmt, nb, nwg, 0, GEMV_NT, 34);
     if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
     TimeScope ts(I4D_TIME_LM_HEAD);
-    return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, (hipStream_t)stream);
+    return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, s);
 }
 
 int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {
@@ -1266,9 +1519,24 @@ int i4d_gemv(const i4d_mat* wm, int32_t batch, const float* x, float* y, void* w
     int rc;
     if ((rc = validate_mat(wm, wm->n, wm->k, wm->dtype, wm->group))) return rc;
     if (wm->n < 1) return I4D_EINVAL;
-    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (batch < 1 || batch > MAX_BATCH_ALL) return I4D_ERANGE;
     if (!aligned(x, 16) || !aligned(y, 4)) return I4D_EALIGN;
-    (void)ws; (void)ws_bytes;
+    if (batch > MAX_BATCH) {
+        // batched: staging + MFMA GEMM; scratch after the workspace's LM-head keys
+        if (!mfma_mat_ok(*wm)) return I4D_EUNSUPPORTED;
+        const int nb = nb_mfma(batch);
+        const GemvTask t = make_task(KIND_ADJ, wm, nullptr, nullptr, 64);
+        const MfmaPlan p = mfma_plan(t.total_pairs, wm->k, nb, 1, true);
+        const MfmaScratch S = mfma_scratch(wm->k, nb, mfma_part_bytes(p, nb), 64);
+        if ((rc = validate_ws(ws, ws_bytes, WS_LM_END + S.total))) return rc;
+        char* w = (char*)ws;
+        char* base = w + WS_LM_END;
+        hipStream_t s = (hipStream_t)stream;
+        if ((rc = mfma_stage(1, nb, x, wm->k, batch, wm->k, nullptr, 0.f, base, S, nullptr, 0, 0, 64, 0.0, false,
+                             (int*)(w + WS_STATUS), s)))
+            return rc;
+        return mfma_rows(nb, mfma_task(t, p, base, S, (int*)(w + WS_MCNT), batch, wm->group), p, y, nullptr, s);
+    }
     const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
     GemvTask t = make_task(KIND_ADJ, wm, nullptr, nullptr, 64);
     const int fmt = pick_fmt(*wm);
@@ -1280,7 +1548,7 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
                   float* o, void* ws, size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
-    if (batch < 1 || batch > MAX_BATCH) return I4D_ERANGE;
+    if (batch < 1 || batch > MAX_BATCH_ALL) return I4D_ERANGE;
     if (!q || !o || !pos) return I4D_EINVAL;
     if ((rc = validate_kv(cfg, kv, max_pos))) return rc;
     const WsLayout W = ws_layout(cfg, 1, batch);

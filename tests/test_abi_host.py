@@ -51,12 +51,14 @@ def _cfg(**kw):
 
 def test_workspace_size_is_pure_and_validates(lib):
     assert B.workspace_size(_cfg(), 1, 1, 127) > 0
-    assert B.workspace_size(_cfg(), 1, 8, 32767) > B.workspace_size(_cfg(), 1, 1, 32767)
+    assert B.workspace_size(_cfg(), 64, 8, 32767) > B.workspace_size(_cfg(), 64, 1, 32767)
     assert B.workspace_size(_cfg(), 64, 1, 127) > B.workspace_size(_cfg(), 1, 1, 127)
     assert B.workspace_size(_cfg(), 1, 1, 127) >= B.WS_MIN_BYTES
     assert B.workspace_size(_cfg(head_dim=96), 1, 1, 127) == 0          # unsupported head_dim
     assert B.workspace_size(_cfg(n_q_heads=6, n_kv_heads=4), 1, 1, 127) == 0  # Hq % Hkv != 0
-    assert B.workspace_size(_cfg(), 1, 9, 127) == 0                     # batch > 8
+    assert B.workspace_size(_cfg(), 1, 33, 127) == 0                    # batch > 32
+    assert B.workspace_size(_cfg(), 1, 16, 127) > B.workspace_size(_cfg(), 1, 8, 127)   # matrix-core scratch
+    assert B.workspace_size(_cfg(), 1, 16, 127, 1000) >= B.workspace_size(_cfg(), 1, 16, 127)
     assert B.workspace_size(_cfg(), 1, 0, 127) == 0
     assert B.workspace_size(_cfg(), 0, 1, 127) == 0                     # no layers
 
@@ -101,7 +103,8 @@ def test_decode_layer_argument_validation(lib):
     L = _layer(cfg)
     assert lib.i4d_decode_layer(None, ctypes.byref(L), 1, None, None, None, None, 0, None, 0, None) == B.I4D_EINVAL
     assert _call_layer(cfg, L, batch=0) == B.I4D_ERANGE
-    assert _call_layer(cfg, L, batch=9) == B.I4D_ERANGE
+    assert _call_layer(cfg, L, batch=33) == B.I4D_ERANGE
+    assert _call_layer(cfg, L, batch=16) == B.I4D_EUNSUPPORTED          # K = 688, group 64: not on the MFMA path
     assert _call_layer(cfg, L, x_out=0x100000) == B.I4D_EINVAL           # x_out aliases x_in
     assert _call_layer(cfg, L, x_in=0x100004) == B.I4D_EALIGN
     assert _call_layer(cfg, L, max_pos=256) == B.I4D_ERANGE                # max_pos >= capacity
@@ -128,7 +131,11 @@ def test_lm_head_and_gemv_validation(lib):
     wb = _mat(1000, 256, dtype=B.WEIGHT_BF16)
     assert lib.i4d_lm_head_chunked(ctypes.byref(wb), 1, h, 64, out, out, ws, 1 << 20, None) == B.I4D_EINVAL
     assert lib.i4d_gemv(ctypes.byref(_mat(10, 12)), 1, h, out, None, 0, None) == B.I4D_EINVAL   # k % 8 != 0
-    assert lib.i4d_gemv(ctypes.byref(w), 9, h, out, None, 0, None) == B.I4D_ERANGE
+    assert lib.i4d_gemv(ctypes.byref(w), 33, h, out, None, 0, None) == B.I4D_ERANGE
+    assert lib.i4d_gemv(ctypes.byref(w), 16, h, out, None, 0, None) == B.I4D_EUNSUPPORTED      # group 64
+    w128 = _mat(1000, 256, group=128)
+    assert lib.i4d_gemv(ctypes.byref(w128), 16, h, out, None, 0, None) == B.I4D_EWORKSPACE
+    assert lib.i4d_lm_head_chunked(ctypes.byref(w128), 16, h, 64, out, out, ws, 1 << 20, None) == B.I4D_EWORKSPACE
     assert lib.i4d_dequant_int4(None, out, None) == B.I4D_EINVAL
 
 

@@ -1,0 +1,179 @@
+"""Parity of the batched path (9..32 sequences: int4 dequant-GEMM on the matrix
+cores) with the CPU oracle, through the C ABI.
+
+Same bars as the matrix-vector path: float outputs relative L2 <= 1e-3 and
+max |err| <= 5e-3 * RMS(reference); appended KV slots within one bf16 rounding
+step; argmax token ids exact (unless the oracle's top-2 gap is a near-tie);
+every untouched KV slot bit-identical.  Shapes are small enough for the oracle
+yet span several row tiles, ragged tiles, and a K axis split over workgroups.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from int4_weight_streaming_decode_amd import binding as B
+from tests.gpu_util import DevKV, DevLayer, DevMat, assert_close, config_of, dev, rel_l2, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _scratch_ws(nbytes=64 << 20):
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    return ws
+
+
+# ------------------------------------------------------------------ GEMM core (test hook)
+
+@pytest.mark.parametrize("n,k,g,batch", [
+    (1001, 1024, 128, 16),     # odd row count: ragged last tile and pair
+    (700, 4096, 128, 32),      # two N-tiles, K split over workgroups
+    (256, 8192, 128, 9),       # few rows, long K: deep K split, padded batch
+    (4096, 512, 128, 20),      # many rows, one LDS chunk pair
+    (300, 2048, 256, 16),      # group of 256: two steps per scale
+])
+def test_batched_gemm_matches_oracle(n, k, g, batch):
+    _print_case("batched gemm", n, k, g, batch)
+    rng = np.random.default_rng(n + 3 * k + batch)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    codes, scales = synth.quantize_int4(w, g)
+    mat = {"codes": codes, "scales": scales, "n": n, "k": k, "group": g}
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    m = DevMat(mat)
+    ws = _scratch_ws()
+    ref = oracle.matvec(mat, x.astype(np.float64))
+    for rep in range(2):                      # the arrival counters must come back to zero
+        y = torch.full((batch, n), float("nan"), dtype=torch.float32, device="cuda")
+        B.gemv(m.mat, batch, dev(x), y, ws)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), ref, what=f"batched gemm rep {rep}")
+
+
+def test_batched_gemm_rejects_unsupported_layouts():
+    rng = np.random.default_rng(1)
+    w = (rng.standard_normal((64, 640)) * 0.02).astype(np.float32)
+    codes, scales = synth.quantize_int4(w, 64)          # group 64: not on the matrix-core path
+    m = DevMat({"codes": codes, "scales": scales, "n": 64, "k": 640, "group": 64})
+    y = torch.empty((16, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(B.I4DError) as e:
+        B.gemv(m.mat, 16, dev(np.zeros((16, 640), np.float32)), y, _scratch_ws())
+    assert e.value.code == B.I4D_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ decode layer
+
+BATCH_SHAPE = synth.SHAPES["tiny"].with_(name="batched", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                                         d_ff=1024, group=128, rope_base=1e6)
+BATCH_SHAPE_HD64 = synth.SHAPES["tiny"].with_(name="batched_hd64", d_model=768, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                              d_ff=1536, group=128, rope_base=1e4)
+WIDE_FFN_SHAPE = synth.SHAPES["tiny"].with_(name="batched_wide", d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                            d_ff=28672, group=128, rope_base=5e5)
+
+
+def _check_kv_batched(kvd, before, after_ref, pos, what):
+    k_gpu, v_gpu = kvd.host()
+    kc0, vc0 = before
+    kref, vref = after_ref
+    for b, p in enumerate(pos):
+        for name, g_, r_ in (("K", k_gpu, kref), ("V", v_gpu, vref)):
+            gv = synth.bf16_value(g_[b, :, p]).astype(np.float64)
+            rv = synth.bf16_value(r_[b, :, p]).astype(np.float64)
+            ulp = np.ldexp(1.0, np.frexp(np.abs(rv))[1] - 8)
+            rms = np.sqrt(np.mean(rv * rv))
+            assert rel_l2(gv, rv) <= 1e-3, f"{what}: {name} slot {p} of b={b}"
+            assert np.all(np.abs(gv - rv) <= np.maximum(5e-3 * rms, ulp)), f"{what}: {name} slot {p} of b={b}"
+        mask = np.ones(kc0.shape[2], dtype=bool)
+        mask[p] = False
+        assert np.array_equal(k_gpu[b][:, mask], kc0[b][:, mask]), f"{what}: K slots other than {p} changed (b={b})"
+        assert np.array_equal(v_gpu[b][:, mask], vc0[b][:, mask]), f"{what}: V slots other than {p} changed (b={b})"
+
+
+@pytest.mark.parametrize("shape,batch", [(BATCH_SHAPE, 16), (BATCH_SHAPE, 11), (BATCH_SHAPE_HD64, 32), (WIDE_FFN_SHAPE, 16)])
+def test_batched_decode_layer_matches_oracle(shape, batch):
+    rng = np.random.default_rng(batch)
+    pos = [int(p) for p in rng.integers(0, 300, size=batch)]
+    pos[0] = 300
+    _print_case("batched decode_layer", shape.name, batch, pos)
+    cap = 320
+    layer = synth.make_layer(shape, 40 + batch, 0)
+    kc, vc = synth.make_kv(shape, 40 + batch, 0, batch, pos, cap)
+    x = synth.make_x(shape, 40 + batch, batch)
+    ref = oracle.decode_layer(shape, layer, x.astype(np.float64), kc, vc, pos)
+    L, kvd = DevLayer(layer), DevKV(kc, vc)
+    cfg = config_of(shape)
+    ws = workspace(cfg, batch, max(pos))
+    out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+    B.decode_layer(cfg, L.layer, batch, dev(x), out, kvd.kv, dev(np.array(pos, dtype=np.int32)), max(pos), ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(batch):
+        assert_close(got[b], ref["z"][b], what=f"batched layer b={b}")
+    _check_kv_batched(kvd, (kc, vc), (ref["k_cache"], ref["v_cache"]), pos, "batched layer")
+    assert B.read_device_status(ws) == 0
+
+
+def test_batched_stack_is_deterministic_and_matches_oracle():
+    """Three layers, two steps, batch 16: every split-K merge adds its K blocks
+    in block order, so two runs give the same bits."""
+    shape = BATCH_SHAPE
+    batch, n_layers, pos0, steps = 16, 3, 200, 2
+    _print_case("batched stack", batch, n_layers, steps)
+    cap = 224
+    layers = [synth.make_layer(shape, 61, l) for l in range(n_layers)]
+    caches = [synth.make_kv(shape, 61, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    xs = [synth.make_x(shape, 61, batch, step=s) for s in range(steps)]
+    Ls = [DevLayer(l) for l in layers]
+    cfg = config_of(shape)
+    runs = []
+    for rep in range(2):
+        kvs = [DevKV(*c) for c in caches]
+        ws = workspace(cfg, batch, cap - 1, n_layers=n_layers)
+        outs = []
+        for s in range(steps):
+            out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+            pos = dev(np.full(batch, pos0 + s, dtype=np.int32))
+            B.decode_stack(cfg, [l.layer for l in Ls], batch, dev(xs[s]), out, [k.kv for k in kvs], pos, pos0 + s, ws)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert B.read_device_status(ws) == 0
+        runs.append(outs)
+    ref_caches = caches
+    for s in range(steps):
+        r = oracle.decode_stack(shape, layers, xs[s].astype(np.float64), ref_caches, [pos0 + s] * batch)
+        ref_caches = r["caches"]
+        assert_close(runs[0][s], r["z"], what=f"batched stack step {s}")
+        assert np.array_equal(runs[0][s].view(np.uint32), runs[1][s].view(np.uint32)), f"step {s}: runs differ"
+
+
+# ------------------------------------------------------------------ LM head
+
+@pytest.mark.parametrize("vocab,d,batch", [(20001, 512, 16), (9000, 1024, 32), (3000, 5120, 12)])
+def test_batched_lm_head_matches_oracle(vocab, d, batch):
+    _print_case("batched lm_head", vocab, d, batch)
+    lm = synth.make_lm_head(vocab, d, 128, seed=vocab + batch)
+    h = synth.make_hidden(d, seed=vocab + 2, batch=batch)
+    tok_ref, mx_ref, logits = oracle.lm_head_argmax(lm, h.astype(np.float64))
+    m = DevMat(lm)
+    cfg = B.make_config(d, 4, 2, 128, 128 * 8, 1e-6, 1e4)
+    ws = workspace(cfg, batch, 0, vocab=vocab)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    mx = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    for rep in range(2):
+        B.lm_head_chunked(m.mat, batch, dev(h), 8192, tok, mx, ws)
+        torch.cuda.synchronize()
+        t = tok.cpu().numpy()
+        for b in range(batch):
+            srt = np.sort(logits[b])
+            rms = np.sqrt(np.mean(logits[b] ** 2))
+            if srt[-1] - srt[-2] > 1e-3 * rms:
+                assert t[b] == tok_ref[b], f"b={b}: token {t[b]} != {tok_ref[b]}"
+            else:
+                assert logits[b][t[b]] >= srt[-1] - 1e-3 * rms
+        assert_close(mx.cpu().numpy(), mx_ref, what=f"batched max logit rep {rep}")

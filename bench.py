@@ -11,8 +11,13 @@ steps whose launches of that kernel carry HIP events, a per-kernel breakdown
 from a few more steps per kernel, and the CPU oracle's rate on a bounded
 sample.
 
+Batches of 9..32 run the matrix-core (MFMA) GEMM path.  --layers N runs the
+first N layers of a stack at its full shape (for a batch whose whole stack
+does not fit in HBM, e.g. the 70B shape at batch 32) and adds the per-step
+figures scaled to the full depth, labelled as extrapolated.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--batch B] [--exec-mode M] [--roofline-kernel K]
+                       [--batch B] [--layers N] [--exec-mode M] [--roofline-kernel K]
                        [--breakdown-steps N] [--calibrate-copy-mib MIB] [--no-cpu-baseline]
 """
 
@@ -40,10 +45,13 @@ WORKLOADS = {
 }
 
 
-# library kernel behind each timed phase
+# library kernel behind each timed phase (batches of 1..8: matrix-vector
+# kernels; 9..32: the matrix-core GEMM kernels)
 KERNEL_NAMES = {"qkv": "k_gemv_qkv", "attention": "k_attention<128>", "wo": "k_gemv_rows (Wo)",
                 "gate_up": "k_gemv_swiglu", "down": "k_gemv_rows (W_down)", "lm_head": "k_lm_head",
                 "persistent": "k_decode_persistent"}
+KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128>", "wo": "k_mfma_rows (Wo)",
+                        "gate_up": "k_mfma_swiglu", "down": "k_mfma_rows (W_down)", "lm_head": "k_mfma_lm"}
 
 
 # HBM traffic of the roofline kernel as hardware counters saw it, recorded in
@@ -124,6 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="27b_lm", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="run only the first N layers of the stack (0: all); figures for the full depth are then "
+                         "reported as extrapolated")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-kernel", default=None, choices=["qkv", "attention", "wo", "gate_up", "down", "persistent"],
@@ -148,7 +159,11 @@ def main():
 
     shape_name, wdtype, lm = WORKLOADS[args.workload]
     shape = synth.SHAPES[shape_name]
+    full_layers = shape.n_layers
+    if 0 < args.layers < full_layers:
+        shape = shape.with_(n_layers=args.layers)
     batch = args.batch
+    names = KERNEL_NAMES_BATCHED if batch > 8 else KERNEL_NAMES
     torch.cuda.set_device(0)
     torch.manual_seed(0)
 
@@ -175,6 +190,8 @@ def main():
         k, v = G.make_kv_gpu(shape, 1, l, batch, cap)
         kvs.append(B.make_kv(k, v, cap))
         keep.append((p, k, v))
+        if (l + 1) % 8 == 0 or l + 1 == shape.n_layers:
+            print(f"[bench] inputs: layer {l + 1}/{shape.n_layers} on the device", file=sys.stderr, flush=True)
     lm_mat = None
     if lm:
         W = G.make_lm_head_gpu(shape.vocab, shape.d_model, shape.group, 2)
@@ -287,15 +304,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights, f16 x f16 -> f32 dot; bf16 MFMA attention" if wdtype == "int4" else "bf16 weights, f32 FMA",
+        "dtype": ("bf16 weights, f32 FMA" if wdtype != "int4" else
+                  "int4 weights, f16 x f16 -> f32 MFMA GEMM; bf16 MFMA attention" if batch > 8 else
+                  "int4 weights, f16 x f16 -> f32 dot; bf16 MFMA attention"),
         "data": "synthetic",
         "config": {"workload": describe(shape, wdtype, lm, batch), "batch": batch, "kv_len": shape.kv_len,
                    "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode},
         "hbm_gbps": hbm_gbps,
         "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
         "algorithmic_bytes_per_step": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[rk], "achieved": rk_entry["gbps"], "peak": 8000.0,
-                     "unit": "GB/s", "frac": rk_entry["gbps"] / 8000.0, "traffic": recorded_traffic(KERNEL_NAMES[rk]),
+        "roofline": {"bound": "hbm", "kernel": names[rk], "achieved": rk_entry["gbps"], "peak": 8000.0,
+                     "unit": "GB/s", "frac": rk_entry["gbps"] / 8000.0, "traffic": recorded_traffic(names[rk]),
                      "avg_launch_us": rk_entry["avg_us"], "launches": rk_launches,
                      "ms_per_step_while_timed": rk_region_ms,
                      "bytes_per_launch": rk_entry["bytes_per_launch"]},
@@ -306,6 +325,14 @@ def main():
         "device_status": status,
         "input_generation_s": round(t_gen, 1),
     }
+    if shape.n_layers < full_layers:
+        scale = full_layers / shape.n_layers
+        full_ms = stack_ms * scale + lm_ms
+        result["extrapolated"] = {
+            "layers": full_layers, "ms_per_step": full_ms, "tokens_per_s": batch * 1000.0 / full_ms,
+            "hbm_gbps": (stack_bytes * scale + lm_bytes) / (full_ms * 1e-3) / 1e9,
+            "how": f"the first {shape.n_layers} layers at the full shape, timed; their stack time scaled by "
+                   f"{full_layers}/{shape.n_layers}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, wdtype, lm)
     print(json.dumps(result), flush=True)

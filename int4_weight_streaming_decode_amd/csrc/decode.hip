@@ -645,7 +645,7 @@ WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     w.layer0 = off;
     off += (size_t)std::max(n_layers, 1) * lo;
     w.mfma = 0;
-    if (B > MAX_BATCH) {                  // after the LM head's keys, which overlay the layer regions
+    if (B > MAX_BATCH / 2) {              // after the LM head's keys, which overlay the layer regions
         off = std::max(off, WS_LM_END);
         w.mfma = off;
         off += layer_scratch_bytes(c, nb_mfma(B));
@@ -1430,8 +1430,9 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         if ((rc = validate_kv(cfg, &kv[l], max_pos))) return rc;
         if (batch > MAX_BATCH) {
             if (!mfma_layer_ok(cfg, &layers[l])) return I4D_EUNSUPPORTED;
-        } else if (cfg->exec_mode != 2 && (rc = phases_fit(&layers[l], batch))) {
-            return rc;
+        } else if (cfg->exec_mode != 2 && phases_fit(&layers[l], batch) != I4D_OK) {
+            // 5..8 sequences whose staged activations overflow LDS: the batched path
+            if (batch <= MAX_BATCH / 2 || !mfma_layer_ok(cfg, &layers[l])) return I4D_EUNSUPPORTED;
         }
     }
     if (batch * cfg->n_kv_heads > WS_MAX_CNT) return I4D_EUNSUPPORTED;
@@ -1449,8 +1450,9 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
         char* R = w + W.layer0 + (size_t)l * W.layer_stride;
         const float* in = (l == 0) ? x_in : (const float*)(R - W.layer_stride + W.x);
         float* out = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
-        rc = batch > MAX_BATCH ? run_layer_mfma(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s)
-                               : run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s);
+        const bool batched = batch > MAX_BATCH || phases_fit(&layers[l], batch) != I4D_OK;
+        rc = batched ? run_layer_mfma(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s)
+                     : run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s);
         if (rc) return rc;
     }
     return I4D_OK;

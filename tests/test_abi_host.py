@@ -57,7 +57,7 @@ def test_workspace_size_is_pure_and_validates(lib):
     assert B.workspace_size(_cfg(head_dim=96), 1, 1, 127) == 0          # unsupported head_dim
     assert B.workspace_size(_cfg(n_q_heads=6, n_kv_heads=4), 1, 1, 127) == 0  # Hq % Hkv != 0
     assert B.workspace_size(_cfg(), 1, 33, 127) == 0                    # batch > 32
-    assert B.workspace_size(_cfg(), 1, 16, 127) > B.workspace_size(_cfg(), 1, 8, 127)   # matrix-core scratch
+    assert B.workspace_size(_cfg(), 1, 16, 127) > B.workspace_size(_cfg(), 1, 4, 127)   # matrix-core scratch
     assert B.workspace_size(_cfg(), 1, 16, 127, 1000) >= B.workspace_size(_cfg(), 1, 16, 127)
     assert B.workspace_size(_cfg(), 1, 0, 127) == 0
     assert B.workspace_size(_cfg(), 0, 1, 127) == 0                     # no layers

@@ -73,6 +73,10 @@ BATCH_SHAPE = synth.SHAPES["tiny"].with_(name="batched", d_model=512, n_q_heads=
                                          d_ff=1024, group=128, rope_base=1e6)
 BATCH_SHAPE_HD64 = synth.SHAPES["tiny"].with_(name="batched_hd64", d_model=768, n_q_heads=8, n_kv_heads=2, head_dim=64,
                                               d_ff=1536, group=128, rope_base=1e4)
+# D = 5120 at batch 8: the matrix-vector path's two-plane q/k/v staging
+# (8 x 5120 inputs) overflows LDS, so the layer takes the batched path
+WIDE_D_SHAPE = synth.SHAPES["tiny"].with_(name="batched_wide_d", d_model=5120, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                          d_ff=1024, group=128, rope_base=1e6)
 WIDE_FFN_SHAPE = synth.SHAPES["tiny"].with_(name="batched_wide", d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                             d_ff=28672, group=128, rope_base=5e5)
 
@@ -95,7 +99,8 @@ def _check_kv_batched(kvd, before, after_ref, pos, what):
         assert np.array_equal(v_gpu[b][:, mask], vc0[b][:, mask]), f"{what}: V slots other than {p} changed (b={b})"
 
 
-@pytest.mark.parametrize("shape,batch", [(BATCH_SHAPE, 16), (BATCH_SHAPE, 11), (BATCH_SHAPE_HD64, 32), (WIDE_FFN_SHAPE, 16)])
+@pytest.mark.parametrize("shape,batch", [(BATCH_SHAPE, 16), (BATCH_SHAPE, 11), (BATCH_SHAPE_HD64, 32), (WIDE_FFN_SHAPE, 16),
+                                         (WIDE_D_SHAPE, 8)])
 def test_batched_decode_layer_matches_oracle(shape, batch):
     rng = np.random.default_rng(batch)
     pos = [int(p) for p in rng.integers(0, 300, size=batch)]

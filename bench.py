@@ -136,6 +136,9 @@ def main():
                     help="run only the first N layers of the stack (0: all); figures for the full depth are then "
                          "reported as extrapolated")
     ap.add_argument("--exec-mode", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one whole step (stack, LM head, position advance) in a HIP graph and replay it in "
+                         "the timed region; the attention split is then planned for the cache capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-kernel", default=None, choices=["qkv", "attention", "wo", "gate_up", "down", "persistent"],
                     help="kernel whose launches are timed inside the timed region (default: gate_up with per-phase "
@@ -237,16 +240,35 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            B.decode_stack(cfg, layers, batch, x, out, kvs, pos, cap - 1, ws)
+            if lm:
+                B.lm_head_chunked(lm_mat, batch, out, shape.lm_chunk, tok, mx, ws)
+            pos.add_(1)
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step(args.warmup + i, ev[i])
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    stack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    lm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if lm else 0.0
+    if graph is None:
+        stack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        lm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if lm else 0.0
+    else:                                   # no per-step events inside a replay
+        stack_ms = None
+        lm_ms = None
     ms_per_step = total_ms / args.steps
     keys_avg = shape.kv_len + args.warmup + (args.steps - 1) / 2.0 + 1
 
@@ -290,7 +312,7 @@ def main():
     lm_bytes = roofline.lm_head_bytes(shape.vocab, shape.d_model, shape.group) if lm else 0
     step_bytes = stack_bytes + lm_bytes
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    stack_gbps = stack_bytes / (stack_ms * 1e-3) / 1e9
+    stack_gbps = stack_bytes / (stack_ms * 1e-3) / 1e9 if stack_ms else None
 
     rk_entry = breakdown[rk]
     result = {
@@ -309,7 +331,8 @@ def main():
                   "int4 weights, f16 x f16 -> f32 dot; bf16 MFMA attention"),
         "data": "synthetic",
         "config": {"workload": describe(shape, wdtype, lm, batch), "batch": batch, "kv_len": shape.kv_len,
-                   "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode},
+                   "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode,
+                   "graph": bool(args.graph)},
         "hbm_gbps": hbm_gbps,
         "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
         "algorithmic_bytes_per_step": step_bytes,
@@ -325,7 +348,7 @@ def main():
         "device_status": status,
         "input_generation_s": round(t_gen, 1),
     }
-    if shape.n_layers < full_layers:
+    if shape.n_layers < full_layers and stack_ms:
         scale = full_layers / shape.n_layers
         full_ms = stack_ms * scale + lm_ms
         result["extrapolated"] = {

@@ -140,10 +140,9 @@ int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * core.  Batches of 9..32 run each projection as an int4 dequant-GEMM on the
  * matrix cores (the roofline reply, 二-三: batching raises the arithmetic
  * intensity past what the vector units sustain); that path needs int4
- * weights with a power-of-two group >= 128, an even number of groups per
- * row, 4-byte aligned scales, and d_model, d_ff and n_q_heads*head_dim
- * multiples of 128 (I4D_EUNSUPPORTED otherwise, before anything is
- * enqueued).
+ * weights with groups of 128 or 256, an even number of groups per row,
+ * 4-byte aligned scales, and d_model, d_ff and n_q_heads*head_dim multiples
+ * of 256 (I4D_EUNSUPPORTED otherwise, before anything is enqueued).
  *   x_in  [B][D] fp32: hidden state of each sequence's new token.
  *   x_out [B][D] fp32: layer output z; must not alias x_in.
  *   pos   [B] int32 (device): number of cached tokens = position of the new

@@ -1037,7 +1037,7 @@ int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
 // projection is a staging launch (norm, fp16 conversion)
 // followed by the MFMA GEMM with the same epilogue as the matrix-vector path.
 bool mfma_mat_ok(const i4d_mat& m) {
-    return m.dtype == I4D_WEIGHT_INT4 && m.k % 128 == 0 && is_pow2(m.group) && m.group >= 128 && (m.k / m.group) % 2 == 0 &&
+    return m.dtype == I4D_WEIGHT_INT4 && m.k % 256 == 0 && (m.group == 128 || m.group == 256) && (m.k / m.group) % 2 == 0 &&
            aligned(m.scales, 4) && aligned(m.data, 16);
 }
 int nb_mfma(int batch) { return batch <= 16 ? 16 : 32; }
@@ -1045,20 +1045,25 @@ int nb_mfma(int batch) { return batch <= 16 ? 16 : 32; }
 struct MfmaPlan { int tiles, rbs, kb, spb, nsteps, nwg; };
 
 // Row blocks of 8*RT tiles; the K axis is split over workgroups (at least two
-// LDS chunks per block) until the grid covers every compute unit.
+// LDS chunks per block) as far as one round of workgroups on the compute
+// units allows.
 MfmaPlan mfma_plan(int total_pairs, int K, int nb, int prec, bool split) {
     MfmaPlan p;
-    const int tb = nb == 32 ? MfmaGeo<32, 1>::TB : MfmaGeo<16, 1>::TB;
-    const int sc = (nb == 16 && prec == 1) ? MfmaGeo<16, 1>::SC : MfmaGeo<32, 1>::SC;
+    // the kernel's own geometry for this column count and activation precision
+    const int tb = nb == 16 ? (prec == 1 ? MfmaGeo<16, 1>::TB : MfmaGeo<16, 2>::TB)
+                            : (prec == 1 ? MfmaGeo<32, 1>::TB : MfmaGeo<32, 2>::TB);
+    const int sc = nb == 16 ? (prec == 1 ? MfmaGeo<16, 1>::SC : MfmaGeo<16, 2>::SC)
+                            : (prec == 1 ? MfmaGeo<32, 1>::SC : MfmaGeo<32, 2>::SC);
     p.tiles = (total_pairs + 7) / 8;
     p.rbs = (p.tiles + tb - 1) / tb;
     p.nsteps = K / 128;
     int kb = 1;
     if (split && p.rbs < num_cus()) {
-        kb = (num_cus() + p.rbs - 1) / p.rbs;
+        kb = std::max(1, num_cus() / p.rbs);      // within one round of workgroups
         kb = std::min(kb, std::max(1, p.nsteps / (2 * sc)));
     }
     p.spb = (p.nsteps + kb - 1) / kb;
+    p.spb = (p.spb + sc - 1) / sc * sc;             // K blocks start on a chunk (an even step, an even group)
     p.kb = (p.nsteps + p.spb - 1) / p.spb;
     p.nwg = p.rbs * p.kb;
     return p;
@@ -1137,7 +1142,7 @@ bool mfma_layer_ok(const i4d_config* c, const i4d_layer* L) {
     const i4d_mat* m[7] = {&L->wq, &L->wk, &L->wv, &L->wo, &L->wg, &L->wu, &L->wd};
     for (int i = 0; i < 7; ++i)
         if (!mfma_mat_ok(*m[i])) return false;
-    return c->d_model % 128 == 0 && c->d_ff % 128 == 0 && (c->n_q_heads * c->head_dim) % 128 == 0;
+    return c->d_model % 256 == 0 && c->d_ff % 256 == 0 && (c->n_q_heads * c->head_dim) % 256 == 0;
 }
 
 // One layer for 9..32 sequences: staging + MFMA GEMM per projection, the

@@ -22,8 +22,11 @@
 // epilogue finds the two rows of a pair in lanes r and r ^ 8.
 //
 // Step.  One step covers 128 inputs of every row of a tile: lane group q
-// loads the 16 bytes (32 inputs) at byte 64 s + 16 q of its row, and dword j
-// of that load is the B operand of MFMA j (j = 0..3).  With groups of 128
+// takes the 16 bytes (32 inputs) at byte 64 s + 16 q of its row, and dword j
+// of them is the B operand of MFMA j (j = 0..3).  The bytes are loaded two
+// steps at a time as whole 128-byte lines (eight rows per load instruction)
+// and rearranged through LDS; the scales of a chunk's groups are loaded once
+// per chunk and passed between lanes.  With groups of 128
 // inputs (or a power-of-two multiple) a step lies inside one group, so the
 // four MFMAs of a step accumulate into a fresh tile that is then scaled by
 // the lane's own row scale and added to the running sum:
@@ -52,16 +55,19 @@ template <int NB, int PREC>
 struct MfmaGeo {
     static constexpr int NT = 512;                                   // threads per workgroup
     static constexpr int NTL = NB / 16;                              // 16-sequence N-tiles
-    static constexpr int RT = NB == 32 ? 2 : 1;                      // row tiles per wave
+    static constexpr int RT = (NB == 32 && PREC == 1) ? 2 : 1;       // row tiles per wave
     static constexpr int TB = 8 * RT;                                // row tiles per workgroup
     static constexpr int SC = (NB == 16 && PREC == 1) ? 8 : 4;       // steps per LDS chunk
-    static constexpr int D = 4;                                      // steps of weight loads in flight
+    static constexpr int D = 2;                                      // step pairs of weight loads in flight
     static constexpr int ROW_B = SC * 256 + 16;                      // LDS pitch of one staged row (padded)
     static constexpr int ACT_B = PREC * NB * ROW_B;                  // one chunk buffer
     static constexpr int CHUNK_LOADS = PREC * NB * SC * 16;          // 16-byte pieces per chunk
     static constexpr int LPT = (CHUNK_LOADS + NT - 1) / NT;          // pieces per thread
-    static constexpr int LDS_B = 2 * ACT_B + (NT / 64) * NB * 8 + 64;
-    static_assert(SC % D == 0, "chunk length must be a multiple of the ring depth");
+    static constexpr int WROW_B = 144;                               // one tile row of a step pair in LDS (padded)
+    static constexpr int WT_B = 16 * WROW_B;                         // one tile's step pair
+    static constexpr int WAVE_W_B = RT * WT_B;                       // a wave's weight transpose area
+    static constexpr int LDS_B = 2 * ACT_B + (NT / 64) * WAVE_W_B + (NT / 64) * NB * 8 + 64;
+    static_assert((SC / 2) % D == 0, "chunk length must be a multiple of the ring depth");
 };
 
 // One batched GEMM phase.
@@ -184,10 +190,14 @@ I4D_DEVINL h8 unpack_b(u32 w) {
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// A step pair of one tile is loaded as two fully used cache lines per row:
+// instruction h (0, 1) gives lane l the 16 bytes at 16 (l & 7) of the 128-byte
+// step pair of tile row 8 h + (l >> 3), i.e. eight rows of 128 bytes per
+// instruction.  The wave then passes the bytes through its own LDS area into
+// the MFMA layout (lane (r, q) of step s: row r, bytes 64 s + 16 q).
 template <int NB, int PREC>
 struct MfmaRing {
-    u32x4 w[MfmaGeo<NB, PREC>::D][MfmaGeo<NB, PREC>::RT];
-    u32 s[MfmaGeo<NB, PREC>::D][MfmaGeo<NB, PREC>::RT];
+    u32x4 w[MfmaGeo<NB, PREC>::D][MfmaGeo<NB, PREC>::RT][2];
 };
 
 // Epilogue kinds of the batched path: per (pair, sequence) results go to one
@@ -207,36 +217,49 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
     const int K = m.t.k;
 
     char* act_buf = lds;                                         // [2][ACT_B]
-    u64* key_lds = (u64*)(lds + 2 * G::ACT_B);                   // [NT/64][NB]
+    u64* key_lds = (u64*)(lds + 2 * G::ACT_B + (G::NT / 64) * G::WAVE_W_B);   // [NT/64][NB]
     int* flag = (int*)(key_lds + (G::NT / 64) * NB);
 
-    // rows streamed by this lane
-    const uint8_t* rowp[RT];
-    const uint32_t* rows[RT];
+    char* wlds = lds + 2 * G::ACT_B + wave * G::WAVE_W_B;       // this wave's weight transpose area
+
+    // rows streamed by this lane: whole-line loads (tile row 8h + lane / 8)
+    // and, in the MFMA layout, the scale row of tile row r
+    const uint8_t* wrow[RT][2];
+    const uint32_t* srow[RT];
     int tile[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         tile[i] = rb * G::TB + wave + 8 * i;
-        const int pair = min(8 * tile[i] + (r & 7), m.t.total_pairs - 1);
-        const RowPtrs rp = resolve_pair<FMT_INT4_FAST, KND>(m.t, pair);
-        rowp[i] = (r < 8 ? rp.pa : rp.pb) + 16 * q;
-        rows[i] = (const uint32_t*)(r < 8 ? rp.sa : rp.sb);     // 4-byte aligned rows (even group count)
+        const RowPtrs lp = resolve_pair<FMT_INT4_FAST, KND>(m.t, min(8 * tile[i] + (lane >> 3), m.t.total_pairs - 1));
+        wrow[i][0] = lp.pa + 16 * (lane & 7);
+        wrow[i][1] = lp.pb + 16 * (lane & 7);
+        const RowPtrs rp = resolve_pair<FMT_INT4_FAST, KND>(m.t, min(8 * tile[i] + (r & 7), m.t.total_pairs - 1));
+        srow[i] = (const uint32_t*)(r < 8 ? rp.sa : rp.sb);     // 4-byte aligned rows (even group count)
     }
 
-    // one step of weight loads (clamped into the K block: a step past the end
+    // step pair dp of the K block (clamped into it: a pair past the end
     // reloads the last one, whose values are never used)
-    auto load_step = [&](MfmaRing<NB, PREC>& R, int slot, int ls) {
-        const int gs = s0 + min(ls, nst - 1);
-        const int g = gs >> m.gshift;
+    const int npairs = nst >> 1;                                  // K blocks hold an even number of steps
+    auto load_pair = [&](MfmaRing<NB, PREC>& R, int slot, int dp) {
+        const size_t off = (size_t)s0 * 64 + (size_t)min(dp, npairs - 1) * 128;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            R.w[slot][i] = ld_g_nt((const u32x4*)(rowp[i] + (size_t)gs * 64));
-            R.s[slot][i] = ld_g(rows[i] + (g >> 1));
+            R.w[slot][i][0] = ld_g_nt((const u32x4*)(wrow[i][0] + off));
+            R.w[slot][i][1] = ld_g_nt((const u32x4*)(wrow[i][1] + off));
         }
+    };
+    // scales of chunk c: lane (r, q) holds dword q of the chunk's groups of
+    // row r (chunks start on an even group)
+    const int ngd = m.nsteps >> (m.gshift + 1);                  // scale dwords per row
+    auto load_scales = [&](u32 (&sv)[RT], int c) {
+        const int d0 = ((s0 + c * SC) >> m.gshift) >> 1;
+#pragma unroll
+        for (int i = 0; i < RT; ++i) sv[i] = ld_g(srow[i] + min(d0 + q, ngd - 1));
     };
 
     // staged-activation chunk c of this K block: pieces into registers, then to LDS
     u32x4 pre[G::LPT];
+    u32 scn[RT], scc[RT];
     auto chunk_issue = [&](int c) {
 #pragma unroll
         for (int i = 0; i < G::LPT; ++i) {
@@ -245,6 +268,7 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
             const int st = min(s0 + c * SC + (piece >> 4), m.nsteps - 1);
             pre[i] = ld_g((const u32x4*)(m.xs + (size_t)row * (K >> 1) + (size_t)st * 64) + (piece & 15));
         }
+        load_scales(scn, c);
     };
     auto chunk_write = [&](int buf) {
 #pragma unroll
@@ -255,6 +279,8 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
                 *(u32x4*)(act_buf + buf * G::ACT_B + row * G::ROW_B + piece * 16) = pre[i];
             }
         }
+#pragma unroll
+        for (int i = 0; i < RT; ++i) scc[i] = scn[i];
     };
 
     f4 acc[RT][NTL];
@@ -266,7 +292,7 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
     MfmaRing<NB, PREC> R;
     chunk_issue(0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_step(R, d, d);
+    for (int d = 0; d < D; ++d) load_pair(R, d, d);
     chunk_write(0);
     __syncthreads();
 
@@ -275,46 +301,58 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
         if (c + 1 < nch) chunk_issue(c + 1);
         const char* ab = act_buf + buf * G::ACT_B;
 #pragma unroll
-        for (int i = 0; i < SC; ++i) {
-            const int ls = c * SC + i;
-            const int slot = i % D;
-            if (ls < nst) {
-                const int g = (s0 + ls) >> m.gshift;
-                float sc[RT];
-                h8 bw[RT][4];
+        for (int k = 0; k < SC / 2; ++k) {
+            const int dp = c * (SC / 2) + k;
+            const int slot = k % D;
+            // the step pair's bytes into the MFMA layout
 #pragma unroll
-                for (int t = 0; t < RT; ++t) {
-                    const u32 sw = R.s[slot][t];
-                    sc[t] = __uint_as_float((g & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
-                    bw[t][0] = unpack_b(R.w[slot][t].x);
-                    bw[t][1] = unpack_b(R.w[slot][t].y);
-                    bw[t][2] = unpack_b(R.w[slot][t].z);
-                    bw[t][3] = unpack_b(R.w[slot][t].w);
-                }
+            for (int t = 0; t < RT; ++t)
 #pragma unroll
-                for (int n = 0; n < NTL; ++n) {
-                    f4 cg[RT];
+                for (int h = 0; h < 2; ++h)
+                    *(u32x4*)(wlds + t * G::WT_B + (8 * h + (lane >> 3)) * G::WROW_B + (lane & 7) * 16) = R.w[slot][t][h];
 #pragma unroll
-                    for (int t = 0; t < RT; ++t) cg[t] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                        for (int p = 0; p < PREC; ++p) {
-                            const h8 a = *(const h8*)(ab + (p * NB + n * 16 + r) * G::ROW_B + (i * 128 + 32 * q + 8 * j) * 2);
-#pragma unroll
-                            for (int t = 0; t < RT; ++t) cg[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[t][j], cg[t], 0, 0, 0);
-                        }
-                    }
+            for (int s = 0; s < 2; ++s) {
+                const int i = 2 * k + s;                      // step within the chunk
+                if (c * SC + i < nst) {
+                    const int rel = i >> m.gshift;            // group within the chunk
+                    const int src = r + 16 * (rel >> 1);
+                    float sc[RT];
+                    h8 bw[RT][4];
 #pragma unroll
                     for (int t = 0; t < RT; ++t) {
-                        acc[t][n].x = fmaf(sc[t], cg[t].x, acc[t][n].x);
-                        acc[t][n].y = fmaf(sc[t], cg[t].y, acc[t][n].y);
-                        acc[t][n].z = fmaf(sc[t], cg[t].z, acc[t][n].z);
-                        acc[t][n].w = fmaf(sc[t], cg[t].w, acc[t][n].w);
+                        const u32 sw = (u32)__shfl((int)scc[t], src, 64);
+                        sc[t] = __uint_as_float((rel & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+                        const u32x4 wv = *(const u32x4*)(wlds + t * G::WT_B + r * G::WROW_B + (4 * s + q) * 16);
+                        bw[t][0] = unpack_b(wv.x);
+                        bw[t][1] = unpack_b(wv.y);
+                        bw[t][2] = unpack_b(wv.z);
+                        bw[t][3] = unpack_b(wv.w);
+                    }
+#pragma unroll
+                    for (int n = 0; n < NTL; ++n) {
+                        f4 cg[RT];
+#pragma unroll
+                        for (int t = 0; t < RT; ++t) cg[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                            for (int p = 0; p < PREC; ++p) {
+                                const h8 a = *(const h8*)(ab + (p * NB + n * 16 + r) * G::ROW_B + (i * 128 + 32 * q + 8 * j) * 2);
+#pragma unroll
+                                for (int t = 0; t < RT; ++t) cg[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[t][j], cg[t], 0, 0, 0);
+                            }
+                        }
+#pragma unroll
+                        for (int t = 0; t < RT; ++t) {
+                            acc[t][n].x = fmaf(sc[t], cg[t].x, acc[t][n].x);
+                            acc[t][n].y = fmaf(sc[t], cg[t].y, acc[t][n].y);
+                            acc[t][n].z = fmaf(sc[t], cg[t].z, acc[t][n].z);
+                            acc[t][n].w = fmaf(sc[t], cg[t].w, acc[t][n].w);
+                        }
                     }
                 }
             }
-            load_step(R, slot, ls + D);
+            load_pair(R, slot, dp + D);
         }
         if (c + 1 < nch) chunk_write(buf ^ 1);
         __syncthreads();

@@ -1045,8 +1045,9 @@ int nb_mfma(int batch) { return batch <= 16 ? 16 : 32; }
 struct MfmaPlan { int tiles, rbs, kb, spb, nsteps, nwg; };
 
 // Row blocks of 8*RT tiles; the K axis is split over workgroups (at least two
-// LDS chunks per block) as far as one round of workgroups on the compute
-// units allows.
+// LDS chunks per block) up to one workgroup per compute unit.  (Where the LDS
+// lets two workgroups share a CU, grids with more row blocks than CUs run in
+// one round; splitting K further costs more in partial sums than it gains.)
 MfmaPlan mfma_plan(int total_pairs, int K, int nb, int prec, bool split) {
     MfmaPlan p;
     // the kernel's own geometry for this column count and activation precision
@@ -1054,12 +1055,13 @@ MfmaPlan mfma_plan(int total_pairs, int K, int nb, int prec, bool split) {
                             : (prec == 1 ? MfmaGeo<32, 1>::TB : MfmaGeo<32, 2>::TB);
     const int sc = nb == 16 ? (prec == 1 ? MfmaGeo<16, 1>::SC : MfmaGeo<16, 2>::SC)
                             : (prec == 1 ? MfmaGeo<32, 1>::SC : MfmaGeo<32, 2>::SC);
+    const int slots = num_cus();
     p.tiles = (total_pairs + 7) / 8;
     p.rbs = (p.tiles + tb - 1) / tb;
     p.nsteps = K / 128;
     int kb = 1;
-    if (split && p.rbs < num_cus()) {
-        kb = std::max(1, num_cus() / p.rbs);      // within one round of workgroups
+    if (split && p.rbs < slots) {
+        kb = std::max(1, slots / p.rbs);          // within one round of workgroups
         kb = std::min(kb, std::max(1, p.nsteps / (2 * sc)));
     }
     p.spb = (p.nsteps + kb - 1) / kb;

@@ -57,7 +57,7 @@ struct MfmaGeo {
     static constexpr int NTL = NB / 16;                              // 16-sequence N-tiles
     static constexpr int RT = (NB == 32 && PREC == 1) ? 2 : 1;       // row tiles per wave
     static constexpr int TB = 8 * RT;                                // row tiles per workgroup
-    static constexpr int SC = (NB == 16 && PREC == 1) ? 8 : 4;       // steps per LDS chunk
+    static constexpr int SC = 4;                                     // steps per LDS chunk
     static constexpr int D = 2;                                      // step pairs of weight loads in flight
     static constexpr int ROW_B = SC * 256 + 16;                      // LDS pitch of one staged row (padded)
     static constexpr int ACT_B = PREC * NB * ROW_B;                  // one chunk buffer

@@ -68,6 +68,7 @@ extern "C" {
 /* device status word bits (i4d_read_device_status) */
 #define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
 #define I4D_DEV_BARRIER_TIMEOUT 2 /* a grid barrier of the persistent kernel gave up waiting */
+#define I4D_DEV_BAD_TOKEN     4   /* a token id outside the embedding table: that row became zeros */
 
 /* ---- weight matrices ---- */
 #define I4D_WEIGHT_INT4 0
@@ -177,6 +178,33 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
 int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
                         int32_t* token_out, float* max_logit_out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* Embedding lookup (Primer 1.2: the decode loop starts from the embedding of
+ * the last token): x_out[b] = fp32 of row tokens[b] of the bf16 table
+ * [vocab][d_model] (row-major).  tokens [B] int32 (device); an id outside
+ * 0..vocab-1 gives a zero row and sets I4D_DEV_BAD_TOKEN in the workspace
+ * status word.  1 <= batch <= 32; ws is an initialised workspace (only its
+ * status word is used, ws_bytes >= 16384).                                  */
+int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t batch, const int32_t* tokens,
+              float* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* One whole greedy decode step (Primer 1.2's loop: embed the last token, run
+ * every layer while appending its K/V, logits, pick the next token), all on
+ * the device and in stream order, so a caller can capture it in a graph and
+ * replay it per token:
+ *   x      = i4d_embed(embed, tokens)          embed: bf16 [V][D], V = w_lm->n
+ *   z      = i4d_decode_stack(x)               same contract as i4d_decode_stack
+ *   tokens = argmax of w_lm z                  written IN PLACE over the input
+ *                                              ids; max_logit_out [B] as in
+ *                                              i4d_lm_head_chunked
+ *   pos[b] += 1                                (device), after the step
+ * x_buf: device scratch of 2 * batch * d_model fp32 (16-byte aligned) holding
+ * x and z; z (the last hidden state) is left in its second half.  max_pos is
+ * the host bound of i4d_decode_stack for this step's positions.  Every
+ * argument of the four parts is validated before anything is enqueued.      */
+int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                    const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
+                    int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream);
 
 /* Expand an int4 matrix to fp32 out [n][k]: out = (code - 8) * scale, exact
  * (Unsloth article 二.3).  A test hook for the int4 format.                 */

@@ -23,6 +23,7 @@ I4D_EUNSUPPORTED = -6
 WS_MIN_BYTES = 16384 + 4096 * 32 * 8    # I4D_WS_MIN_BYTES
 I4D_DEV_BAD_POS = 1
 I4D_DEV_BARRIER_TIMEOUT = 2
+I4D_DEV_BAD_TOKEN = 4
 
 WEIGHT_INT4 = 0
 WEIGHT_BF16 = 1
@@ -78,6 +79,9 @@ def lib():
                                        ctypes.POINTER(I4dKv), P, I, P, Z, P]
         L.i4d_lm_head_chunked.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P, Z, P]
         L.i4d_dequant_int4.argtypes = [ctypes.POINTER(I4dMat), P, P]
+        L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
+        L.i4d_decode_step.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P, ctypes.POINTER(I4dMat), I,
+                                      P, P, P, I, P, ctypes.POINTER(I4dKv), P, Z, P]
         L.i4d_gemv.argtypes = [ctypes.POINTER(I4dMat), I, P, P, P, Z, P]
         L.i4d_attention.argtypes = [ctypes.POINTER(I4dConfig), I, P, ctypes.POINTER(I4dKv), P, I, P, P, Z, P]
         L.i4d_read_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
@@ -85,7 +89,8 @@ def lib():
         L.i4d_launch_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
         L.i4d_status_string.argtypes = [ctypes.c_int]
         L.i4d_status_string.restype = ctypes.c_char_p
-        for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked",
+        for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked", "i4d_embed",
+                     "i4d_decode_step",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop"):
             getattr(L, name).restype = ctypes.c_int
@@ -164,6 +169,22 @@ def lm_head_chunked(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out
     _check(lib().i4d_lm_head_chunked(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, _ptr(token_out),
                                      _ptr(max_logit_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "i4d_lm_head_chunked")
+
+
+def embed(table, vocab, d_model, batch, tokens, x_out, ws, stream=None):
+    _check(lib().i4d_embed(_ptr(table), vocab, d_model, batch, _ptr(tokens), _ptr(x_out), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "i4d_embed")
+
+
+def decode_step(cfg, layers, embed_table, w_lm: I4dMat, batch, tokens, max_logit_out, pos, max_pos, x_buf, kvs, ws,
+                stream=None):
+    """One greedy decode step; tokens (device int32 [B]) are replaced by the next tokens and pos advances by one."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_decode_step(ctypes.byref(cfg), n, larr, _ptr(embed_table), ctypes.byref(w_lm), batch, _ptr(tokens),
+                                 _ptr(max_logit_out), _ptr(pos), max_pos, _ptr(x_buf), karr, _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "i4d_decode_step")
 
 
 def dequant_int4(w: I4dMat, out, stream=None):

@@ -311,6 +311,23 @@ __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
     for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW>(a, it, lds, R, false);
 }
 
+// ---------------------------------------------------------------- decode loop glue
+// x[b] = row tokens[b] of the bf16 embedding table (an id outside the table
+// gives a zero row and the status bit).
+__global__ void __launch_bounds__(256) k_embed(const uint16_t* table, int vocab, int D, const int* tokens, float* x, int* status) {
+    const int b = blockIdx.y;
+    const int t = tokens[b];
+    const bool ok = t >= 0 && t < vocab;
+    if (!ok && blockIdx.x == 0 && i4d_tid() == 0) raise_status(status, I4D_DEV_BAD_TOKEN);
+    const uint16_t* row = table + (size_t)(ok ? t : 0) * D;
+    for (int d = blockIdx.x * 256 + i4d_tid(); d < D; d += gridDim.x * 256) x[(size_t)b * D + d] = ok ? bf16_to_f32(row[d]) : 0.f;
+}
+
+// every sequence moves on to its next position
+__global__ void __launch_bounds__(64) k_advance(int* pos, int nb) {
+    if (i4d_tid() < nb) pos[i4d_tid()] += 1;
+}
+
 // ---------------------------------------------------------------- batched (MFMA) phases
 template <int NB>
 __global__ void __launch_bounds__(512) k_mfma_rows(MfmaTask m, float* y, const float* resid) {
@@ -1421,9 +1438,10 @@ int i4d_decode_layer(const i4d_config* cfg, const i4d_layer* layer, int32_t batc
     return i4d_decode_stack(cfg, 1, layer, batch, x_in, x_out, kv, pos, max_pos, ws, ws_bytes, stream);
 }
 
-int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch, const float* x_in,
-                     float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes,
-                     void* stream) {
+// run = false: validate only (nothing is enqueued)
+static int decode_stack_impl(bool run, const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch,
+                             const float* x_in, float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos,
+                             void* ws, size_t ws_bytes, void* stream) {
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
     if (n_layers < 1 || !layers || !kv) return I4D_EINVAL;
@@ -1450,9 +1468,11 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     if (cfg->exec_mode == 2) {
         if (!I4D_ENABLE_PERSISTENT) return I4D_EUNSUPPORTED;
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
+        if (!run) return I4D_OK;
         TimeScope ts(I4D_TIME_PERSISTENT);
         return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
     }
+    if (!run) return I4D_OK;
     for (int l = 0; l < n_layers; ++l) {
         char* R = w + W.layer0 + (size_t)l * W.layer_stride;
         const float* in = (l == 0) ? x_in : (const float*)(R - W.layer_stride + W.x);
@@ -1465,7 +1485,14 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
     return I4D_OK;
 }
 
-int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
+int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch, const float* x_in,
+                     float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes,
+                     void* stream) {
+    return decode_stack_impl(true, cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, ws, ws_bytes, stream);
+}
+
+// run = false: validate only (nothing is enqueued)
+static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
                         float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
     if (!w_lm || w_lm->dtype != I4D_WEIGHT_INT4) return I4D_EINVAL;
     int rc;
@@ -1486,6 +1513,7 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
         const GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
         const MfmaPlan p = mfma_plan(t.total_pairs, w_lm->k, nb, 1, false);
         if (p.nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
+        if (!run) return I4D_OK;
         char* base = w + WS_LM_END;
         if ((rc = mfma_stage(1, nb, h, w_lm->k, batch, w_lm->k, nullptr, 0.f, base, S, nullptr, 0, 0, 64, 0.0, false,
                              (int*)(w + WS_STATUS), s)))
@@ -1509,8 +1537,53 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
     // passes are as large as the per-workgroup run budget allows.
     plan_passes(t, fmt, nb, nwg, 0, GEMV_NT, 34);
     if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
+    if (!run) return I4D_OK;
     TimeScope ts(I4D_TIME_LM_HEAD);
     return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, s);
+}
+
+int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
+                        float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
+    return lm_head_impl(true, w_lm, batch, h, chunk_rows, token_out, max_logit_out, ws, ws_bytes, stream);
+}
+
+int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t batch, const int32_t* tokens, float* x_out,
+              void* ws, size_t ws_bytes, void* stream) {
+    if (!table || !tokens || !x_out || !ws) return I4D_EINVAL;
+    if (vocab < 1 || d_model < 1) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH_ALL) return I4D_ERANGE;
+    if (!aligned(table, 2) || !aligned(tokens, 4) || !aligned(x_out, 4)) return I4D_EALIGN;
+    int rc;
+    if ((rc = validate_ws(ws, ws_bytes, WS_HEADER))) return rc;
+    const dim3 grid((d_model + 255) / 256, batch);
+    hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, (hipStream_t)stream, table, vocab, d_model, tokens, x_out,
+                       (int*)((char*)ws + WS_STATUS));
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                    const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
+                    int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = validate_cfg(cfg))) return rc;
+    if (!embed || !w_lm || !tokens || !pos || !x_buf) return I4D_EINVAL;
+    if (!aligned(embed, 2) || !aligned(tokens, 4)) return I4D_EALIGN;
+    if (w_lm->k != cfg->d_model) return I4D_EINVAL;
+    const size_t plane = (size_t)batch * cfg->d_model;
+    float* x0 = x_buf;
+    float* x1 = x_buf + plane;
+    // every check before anything is enqueued
+    if ((rc = decode_stack_impl(false, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
+    if ((rc = lm_head_impl(false, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((cfg->d_model + 255) / 256, batch);
+    hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, s, embed, w_lm->n, cfg->d_model, (const int*)tokens, x0,
+                       (int*)((char*)ws + WS_STATUS));
+    if (hipGetLastError() != hipSuccess) return I4D_EHIP;
+    if ((rc = decode_stack_impl(true, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
+    if ((rc = lm_head_impl(true, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream))) return rc;
+    hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, s, pos, batch);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
 int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {

@@ -27,7 +27,9 @@ from .decode import (  # noqa: F401
     decode_layer,
     decode_stack,
     dequant_int4,
+    embed_tokens,
     gqa_decode_attention,
+    greedy_decode,
     lm_head_argmax,
     lm_head_chunked_argmax,
     matvec,

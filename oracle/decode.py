@@ -241,3 +241,37 @@ def lm_head_chunked_argmax(w_lm: dict, h: np.ndarray, chunk_rows: int):
         best = np.where(upd, m, best)
         tok = np.where(upd, r0 + i, tok)
     return tok, best
+
+
+# ----------------------------------------------------------------------------- the decode loop
+
+def embed_tokens(table_bits: np.ndarray, tokens) -> np.ndarray:
+    """Hidden state of each sequence's last token: row tokens[b] of the bf16
+    embedding table [V][D] (Primer 1.2: each decode step starts from the
+    embedding of the token generated last).  Ids outside the table raise."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if np.any(tokens < 0) or np.any(tokens >= table_bits.shape[0]):
+        raise IndexError("token id outside the embedding table")
+    return bf16_to_f64(table_bits[tokens])
+
+
+def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, tokens, caches: list, pos, steps: int) -> dict:
+    """`steps` rounds of Primer 1.2's decode loop: embed the last token, run
+    the stack (appending each layer's K/V at pos), take the greedy token of the
+    LM head, advance every position by one.  Returns per-step tokens, maximum
+    logits and logits, the final hidden state and the caches."""
+    tok = np.asarray(tokens, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    out = {"tokens": [], "max_logit": [], "logits": []}
+    for _ in range(steps):
+        r = decode_stack(shape, layers, embed_tokens(table_bits, tok), caches, pos)
+        caches = r["caches"]
+        tok, mx, logits = lm_head_argmax(w_lm, r["z"])
+        out["tokens"].append(tok.copy())
+        out["max_logit"].append(mx)
+        out["logits"].append(logits)
+        out["z"] = r["z"]
+        pos = pos + 1
+    out["caches"] = caches
+    return out
+

@@ -11,6 +11,7 @@ from .inputs import (  # noqa: F401
     TENSOR_IDS,
     bf16_bits,
     bf16_value,
+    make_embedding,
     make_hidden,
     make_kv,
     make_layer,

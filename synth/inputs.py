@@ -24,7 +24,7 @@ import numpy as np
 TENSOR_IDS = {
     "attn_norm": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "ffn_norm": 5,
     "wg": 6, "wu": 7, "wd": 8, "k_cache": 9, "v_cache": 10, "x": 11,
-    "w_lm": 12, "lm_hidden": 13,
+    "w_lm": 12, "lm_hidden": 13, "embed": 14,
 }
 
 BF16_QNAN = np.uint16(0x7FC0)
@@ -138,3 +138,9 @@ def make_lm_head(vocab: int, d_model: int, group: int, seed: int) -> dict:
 def make_hidden(d_model: int, seed: int, batch: int) -> np.ndarray:
     """Final hidden state fed to the LM head: bf16 N(0,1) values as float32 [B][D]."""
     return bf16_value(bf16_bits(rng_for(seed, 0, "lm_hidden").standard_normal((batch, d_model), dtype=np.float32)))
+
+
+def make_embedding(vocab: int, d_model: int, seed: int) -> np.ndarray:
+    """bf16 embedding table [vocab][d_model] (bit patterns), N(0,1) values."""
+    return bf16_bits(rng_for(seed, 0, "embed").standard_normal((vocab, d_model), dtype=np.float32))
+

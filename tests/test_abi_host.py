@@ -169,3 +169,32 @@ def test_time_kernel_ids_match_header():
     text = open(HEADER).read()
     ids = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"#define I4D_TIME_(\w+)\s+(\d+)", text)}
     assert ids == B.TIME_KERNELS
+
+
+def test_embed_and_decode_step_validation(lib):
+    """Every check happens before anything is enqueued (no GPU is touched:
+    each call returns an error code)."""
+    cfg = _cfg()
+    L = _layer(cfg)
+    kv = B.I4dKv(0x500000, 0x600000, 256)
+    lm = _mat(1000, 256)
+    P = ctypes.c_void_p
+    tok, mx, pos, xb, ws, emb = P(0x700000), P(0x710000), P(0x720000), P(0x800000), P(0x400000), P(0x900000)
+
+    def step(cfg=cfg, layer=L, emb=emb, lm=lm, batch=1, tokens=tok, pos=pos, xb=xb, ws_bytes=1 << 30, max_pos=127):
+        return lib.i4d_decode_step(ctypes.byref(cfg), 1, ctypes.byref(layer), emb, ctypes.byref(lm), batch, tokens, mx,
+                                   pos, max_pos, xb, ctypes.byref(kv), ws, ws_bytes, None)
+
+    assert step(emb=None) == B.I4D_EINVAL
+    assert step(tokens=None) == B.I4D_EINVAL
+    assert step(pos=None) == B.I4D_EINVAL
+    assert step(lm=_mat(1000, 128)) == B.I4D_EINVAL             # LM head width != d_model
+    assert step(emb=P(0x900001)) == B.I4D_EALIGN
+    assert step(batch=33) == B.I4D_ERANGE
+    assert step(max_pos=256) == B.I4D_ERANGE                    # max_pos >= capacity
+    assert step(xb=P(0x800004)) == B.I4D_EALIGN
+    assert step(ws_bytes=100) == B.I4D_EWORKSPACE
+    assert lib.i4d_embed(None, 10, 256, 1, tok, xb, ws, 1 << 20, None) == B.I4D_EINVAL
+    assert lib.i4d_embed(emb, 0, 256, 1, tok, xb, ws, 1 << 20, None) == B.I4D_EINVAL
+    assert lib.i4d_embed(emb, 10, 256, 0, tok, xb, ws, 1 << 20, None) == B.I4D_ERANGE
+    assert lib.i4d_embed(emb, 10, 256, 1, tok, xb, ws, 100, None) == B.I4D_EWORKSPACE

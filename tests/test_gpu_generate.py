@@ -1,0 +1,167 @@
+"""The whole greedy decode step through the C ABI (i4d_decode_step): embedding
+lookup of the last token, the layer stack with its K/V appends, the chunked LM
+head writing the next token in place, and the position advance, against the
+oracle's decode loop (Primer 1.2).  Token ids must match exactly unless the
+oracle's top-2 gap is a near-tie; float outputs to the usual bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from int4_weight_streaming_decode_amd import binding as B
+from tests.gpu_util import DevKV, DevLayer, DevMat, assert_close, config_of, dev, workspace
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.SHAPES["tiny"].with_(name="gen", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128, d_ff=1024,
+                                   group=128, rope_base=1e6)
+VOCAB = 3000
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _model(n_layers, batch, pos0, cap, seed):
+    layers = [synth.make_layer(SHAPE, seed, l) for l in range(n_layers)]
+    caches = [synth.make_kv(SHAPE, seed, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    table = synth.make_embedding(VOCAB, SHAPE.d_model, seed)
+    lm = synth.make_lm_head(VOCAB, SHAPE.d_model, SHAPE.group, seed + 1)
+    return layers, caches, table, lm
+
+
+def _check_tokens(got, ref_tokens, ref_logits, what):
+    for b in range(len(got)):
+        srt = np.sort(ref_logits[b])
+        rms = np.sqrt(np.mean(ref_logits[b] ** 2))
+        if srt[-1] - srt[-2] > 1e-3 * rms:
+            assert got[b] == ref_tokens[b], f"{what} b={b}: token {got[b]} != {ref_tokens[b]}"
+        else:                                   # near-tie: a valid maximiser, and the histories may part here
+            assert ref_logits[b][got[b]] >= srt[-1] - 1e-3 * rms
+            pytest.skip(f"{what} b={b}: near-tie, later steps are not comparable")
+
+
+@pytest.mark.parametrize("batch", [2, 16])
+def test_decode_steps_match_the_oracle_loop(batch):
+    n_layers, pos0, steps = 2, 200, 4
+    cap = 224
+    _print_case("decode_step", batch, n_layers, steps)
+    layers, caches, table, lm = _model(n_layers, batch, pos0, cap, 71 + batch)
+    tok0 = np.random.default_rng(batch).integers(0, VOCAB, size=batch).astype(np.int32)
+    Ls = [DevLayer(l) for l in layers]
+    kvs = [DevKV(*c) for c in caches]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+    ws = workspace(cfg, batch, cap - 1, vocab=VOCAB, n_layers=n_layers)
+    tokens = dev(tok0)
+    pos = dev(np.full(batch, pos0, dtype=np.int32))
+    mx = torch.empty(batch, dtype=torch.float32, device="cuda")
+    xbuf = torch.empty((2, batch, SHAPE.d_model), dtype=torch.float32, device="cuda")
+    got = []
+    for s in range(steps):
+        B.decode_step(cfg, [l.layer for l in Ls], emb, W.mat, batch, tokens, mx, pos, pos0 + s, xbuf, [k.kv for k in kvs], ws)
+        torch.cuda.synchronize()
+        got.append((tokens.cpu().numpy().copy(), mx.cpu().numpy().copy()))
+    assert B.read_device_status(ws) == 0
+    assert np.array_equal(pos.cpu().numpy(), np.full(batch, pos0 + steps))
+    ref = oracle.greedy_decode(SHAPE, layers, table, lm, tok0, caches, [pos0] * batch, steps)
+    for s in range(steps):
+        _check_tokens(got[s][0], ref["tokens"][s], ref["logits"][s], f"step {s}")
+        assert_close(got[s][1], ref["max_logit"][s], what=f"step {s} max logit")
+    assert_close(xbuf[1].cpu().numpy(), ref["z"], what="last hidden state")
+
+
+def test_decode_step_follows_a_cyclic_successor_model():
+    """Identity layers (every code 8), one-hot embeddings and an LM head whose
+    row u picks coordinate u - 1: greedy decoding from t must give t+1, t+2, ..."""
+    shape = SHAPE
+    V, D, g = 600, shape.d_model, shape.group
+    _print_case("decode_step successor model")
+    dims = {"wq": (shape.q_width, D), "wk": (shape.kv_width, D), "wv": (shape.kv_width, D), "wo": (D, shape.q_width),
+            "wg": (shape.d_ff, D), "wu": (shape.d_ff, D), "wd": (D, shape.d_ff)}
+    one = synth.bf16_bits(np.ones(D, dtype=np.float32))
+    layer = {"attn_norm": one, "ffn_norm": one}
+    for n, (r, c) in dims.items():
+        layer[n] = {"codes": np.full((r, c // 2), 0x88, dtype=np.uint8),
+                    "scales": synth.bf16_bits(np.full((r, c // g), 0.01, dtype=np.float32)), "n": r, "k": c, "group": g}
+    table = synth.bf16_bits(np.eye(V, D, dtype=np.float32))
+    codes = np.full((V, D), 8, dtype=np.uint8)
+    for u in range(V):
+        codes[u, (u - 1) % D] = 15 if (u - 1) % V < D else 8
+    lm = {"codes": (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8),
+          "scales": synth.bf16_bits(np.full((V, D // g), 0.125, dtype=np.float32)), "n": V, "k": D, "group": g}
+    caches = [synth.make_kv(shape, 3, 0, 2, [40, 41], 64)]
+    L, kv, Wm, emb = DevLayer(layer), DevKV(*caches[0]), DevMat(lm), dev(table)
+    cfg = config_of(shape)
+    ws = workspace(cfg, 2, 63, vocab=V)
+    tokens = dev(np.array([7, 300], dtype=np.int32))
+    pos = dev(np.array([40, 41], dtype=np.int32))
+    mx = torch.empty(2, dtype=torch.float32, device="cuda")
+    xbuf = torch.empty((2, 2, D), dtype=torch.float32, device="cuda")
+    seq = []
+    for s in range(5):
+        B.decode_step(cfg, [L.layer], emb, Wm.mat, 2, tokens, mx, pos, 41 + s, xbuf, [kv.kv], ws)
+        seq.append(tokens.cpu().numpy().tolist())
+    assert seq == [[8, 301], [9, 302], [10, 303], [11, 304], [12, 305]]
+    assert np.allclose(mx.cpu().numpy(), 0.875, rtol=1e-4)     # zero weights reached through fp32 sums
+    assert pos.cpu().numpy().tolist() == [45, 46]
+
+
+def test_decode_step_replays_from_a_graph():
+    """One step captured in a graph and replayed: every replay (with eager work
+    and a synchronisation between replays) gives the tokens of the same step
+    run eagerly on a copy of the state."""
+    batch, n_layers, pos0, steps = 2, 2, 100, 3
+    cap = 128
+    _print_case("decode_step graph", batch, steps)
+    layers, caches, table, lm = _model(n_layers, batch, pos0, cap, 91)
+    tok0 = np.array([17, 2999], dtype=np.int32)
+    Ls = [DevLayer(l) for l in layers]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+
+    def state():
+        return ([DevKV(*c) for c in caches], dev(tok0), dev(np.full(batch, pos0, dtype=np.int32)),
+                torch.empty(batch, dtype=torch.float32, device="cuda"),
+                torch.empty((2, batch, SHAPE.d_model), dtype=torch.float32, device="cuda"),
+                workspace(cfg, batch, cap - 1, vocab=VOCAB, n_layers=n_layers))
+
+    kvs, tokens, pos, mx, xbuf, ws = state()
+    eager = []
+    for s in range(steps):
+        B.decode_step(cfg, [l.layer for l in Ls], emb, W.mat, batch, tokens, mx, pos, cap - 1, xbuf, [k.kv for k in kvs], ws)
+        torch.cuda.synchronize()
+        eager.append(tokens.cpu().numpy().copy())
+
+    kvs2, tokens2, pos2, mx2, xbuf2, ws2 = state()
+    larr = [l.layer for l in Ls]
+    karr = [k.kv for k in kvs2]
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        B.decode_step(cfg, larr, emb, W.mat, batch, tokens2, mx2, pos2, cap - 1, xbuf2, karr, ws2)
+    torch.cuda.current_stream().wait_stream(gs)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1024, device="cuda") * 2).sum().item()      # eager work between replays
+        assert np.array_equal(tokens2.cpu().numpy(), eager[s]), f"replay {s}"
+    assert B.read_device_status(ws2) == 0
+
+
+def test_bad_token_sets_status_and_gives_a_zero_row():
+    D = 256
+    table = synth.make_embedding(100, D, 5)
+    ws = workspace(B.make_config(D, 4, 2, 64, 512, 1e-6, 1e4), 1, 0)
+    x = torch.full((2, D), float("nan"), dtype=torch.float32, device="cuda")
+    B.embed(dev(table), 100, D, 2, dev(np.array([99, 100], dtype=np.int32)), x, ws)
+    torch.cuda.synchronize()
+    xh = x.cpu().numpy()
+    assert np.array_equal(xh[0], synth.bf16_value(table[99]))
+    assert not xh[1].any()
+    assert B.read_device_status(ws) & B.I4D_DEV_BAD_TOKEN

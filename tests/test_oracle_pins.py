@@ -370,3 +370,60 @@ def test_argmax_ties_go_to_lowest_id_across_chunks():
         t, _ = oracle.lm_head_chunked_argmax(lm, h, chunk)
         assert t[0] == 4
     assert oracle.lm_head_argmax(lm, h)[0][0] == 4
+
+
+# ------------------------------------------------------------------ the decode loop (Primer 1.2)
+
+def test_embed_tokens_reads_table_rows():
+    V, D = 9, 12
+    # row v, column d holds (v - 3) / 4 + d / 64: dyadic values, exact in bf16
+    vals = np.array([[(v - 3) / 4 + d / 64 for d in range(D)] for v in range(V)], dtype=np.float32)
+    table = synth.bf16_bits(vals)
+    x = oracle.embed_tokens(table, [5, 0, 8, 5])
+    assert x.dtype == np.float64 and x.shape == (4, D)
+    for i, v in enumerate([5, 0, 8, 5]):
+        assert np.array_equal(x[i], [(v - 3) / 4 + d / 64 for d in range(D)])
+    with pytest.raises(IndexError):
+        oracle.embed_tokens(table, [9])
+    with pytest.raises(IndexError):
+        oracle.embed_tokens(table, [-1])
+
+
+def _identity_layer(shape, g):
+    """Every code 8 (weight 0 whatever the scale): attention and FFN add
+    nothing, so a layer returns its input unchanged."""
+    D, qw, kvw, F = shape.d_model, shape.q_width, shape.kv_width, shape.d_ff
+    dims = {"wq": (qw, D), "wk": (kvw, D), "wv": (kvw, D), "wo": (D, qw), "wg": (F, D), "wu": (F, D), "wd": (D, F)}
+    one = synth.bf16_bits(np.ones(D, dtype=np.float32))
+    layer = {"attn_norm": one, "ffn_norm": one}
+    for n, (r, c) in dims.items():
+        layer[n] = {"codes": np.full((r, c // 2), 0x88, dtype=np.uint8),
+                    "scales": synth.bf16_bits(np.full((r, (c + g - 1) // g), 0.01, dtype=np.float32)),
+                    "n": r, "k": c, "group": g}
+    return layer
+
+
+def test_greedy_decode_follows_a_cyclic_successor_model():
+    """Closed form: with identity layers, one-hot embeddings e_v and an LM
+    head whose row u is 7 * 0.125 * e_{u-1}, the logits of x = e_v peak at
+    u = v + 1 (mod V), so greedy decoding from t yields t+1, t+2, ...; the
+    appended K/V slots are zeros (k = v = 0) and the positions advance."""
+    shape = synth.SHAPES["tiny"].with_(d_model=32, n_q_heads=2, n_kv_heads=1, head_dim=16, d_ff=32, group=16, n_layers=2)
+    V, D, g = 20, 32, 16
+    table = synth.bf16_bits(np.eye(V, D, dtype=np.float32))
+    codes = np.full((V, D), 8, dtype=np.uint8)
+    for u in range(V):
+        codes[u, (u - 1) % V] = 15                        # (15 - 8) * 0.125 = 0.875
+    lm = {"codes": (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8),
+          "scales": synth.bf16_bits(np.full((V, D // g), 0.125, dtype=np.float32)), "n": V, "k": D, "group": g}
+    layers = [_identity_layer(shape, g) for _ in range(2)]
+    caches = [synth.make_kv(shape, 21, l, 2, [5, 9], 16) for l in range(2)]
+    r = oracle.greedy_decode(shape, layers, table, lm, [3, 19], caches, [5, 9], 4)
+    assert [list(t) for t in r["tokens"]] == [[4, 0], [5, 1], [6, 2], [7, 3]]
+    assert np.allclose(r["max_logit"], 0.875)
+    assert np.array_equal(r["z"], oracle.embed_tokens(table, [6, 2]))   # last step's input passes through
+    for l in range(2):
+        kc, vc = r["caches"][l]
+        for b, p0 in enumerate([5, 9]):
+            for s in range(4):                          # slots p0 .. p0+3 hold zeros (RoPE may give -0.0)
+                assert np.all(synth.bf16_value(kc[b, :, p0 + s]) == 0) and np.all(synth.bf16_value(vc[b, :, p0 + s]) == 0)

@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="27b_lm", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--kv-len", type=int, default=0,
+                    help="cached tokens at the first timed step (0: the workload's own, e.g. 8192 for 27B; "
+                         "131072 for a 128k-context decode)")
     ap.add_argument("--layers", type=int, default=0,
                     help="run only the first N layers of the stack (0: all); figures for the full depth are then "
                          "reported as extrapolated")
@@ -165,6 +168,8 @@ def main():
     full_layers = shape.n_layers
     if 0 < args.layers < full_layers:
         shape = shape.with_(n_layers=args.layers)
+    if args.kv_len > 0:
+        shape = shape.with_(kv_len=args.kv_len)
     batch = args.batch
     names = KERNEL_NAMES_BATCHED if batch > 8 else KERNEL_NAMES
     torch.cuda.set_device(0)

@@ -87,6 +87,7 @@ def _attn_case(shape, batch, pos, seed):
 @pytest.mark.parametrize("name,batch,pos", [
     ("tiny", 1, [127]), ("tiny", 2, [0, 37]), ("7b", 1, [4096]), ("27b", 1, [8192]), ("27b", 3, [5, 1000, 2049]),
     ("70b", 1, [32768]),
+    ("27b", 1, [131071]),        # 128k context: 131072 keys attended
 ])
 def test_attention_matches_oracle(name, batch, pos):
     _print_case("attention", name, batch, pos)

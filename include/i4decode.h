@@ -164,6 +164,19 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
                      const int32_t* pos, int32_t max_pos,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* A chunk of n_tokens (1..32) consecutive prompt tokens of ONE sequence
+ * through the stack at once (Primer 1.2: prefill computes, for every prompt
+ * token, what decoding the tokens one after another would).  x_in/x_out
+ * [n_tokens][D]; kv holds that sequence's cache (its batch dimension is 1);
+ * pos [n_tokens] (device) gives each token's position, distinct and normally
+ * consecutive (pos0, pos0+1, ...): token t attends to slots 0..pos[t] and its
+ * K/V are appended at pos[t], so the cache must already hold the tokens before
+ * pos[0].  Same weights, workspace (sized for batch = n_tokens) and
+ * conditions as i4d_decode_stack; exec_mode 2 is not supported here.       */
+int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens,
+                      const float* x_in, float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Greedy LM head (Unsloth article 三; Primer 1.2): for each of `batch` hidden
  * states h [B][D] fp32, token_out[b] = lowest v maximising (W_lm h_b)_v and
  * max_logit_out[b] = that logit (fp32).  w_lm is int4 [V][D].  The page's

@@ -80,6 +80,8 @@ def lib():
         L.i4d_lm_head_chunked.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P, Z, P]
         L.i4d_dequant_int4.argtypes = [ctypes.POINTER(I4dMat), P, P]
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
+        L.i4d_prefill_chunk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
+                                        ctypes.POINTER(I4dKv), P, I, P, Z, P]
         L.i4d_decode_step.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P, ctypes.POINTER(I4dMat), I,
                                       P, P, P, I, P, ctypes.POINTER(I4dKv), P, Z, P]
         L.i4d_gemv.argtypes = [ctypes.POINTER(I4dMat), I, P, P, P, Z, P]
@@ -90,7 +92,7 @@ def lib():
         L.i4d_status_string.argtypes = [ctypes.c_int]
         L.i4d_status_string.restype = ctypes.c_char_p
         for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked", "i4d_embed",
-                     "i4d_decode_step",
+                     "i4d_decode_step", "i4d_prefill_chunk",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop"):
             getattr(L, name).restype = ctypes.c_int
@@ -169,6 +171,15 @@ def lm_head_chunked(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out
     _check(lib().i4d_lm_head_chunked(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, _ptr(token_out),
                                      _ptr(max_logit_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "i4d_lm_head_chunked")
+
+
+def prefill_chunk(cfg, layers, n_tokens, x_in, x_out, kvs, pos, max_pos, ws, stream=None):
+    """n_tokens prompt tokens of one sequence (x [n][D], positions pos [n] on the device) through the stack."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_prefill_chunk(ctypes.byref(cfg), n, larr, n_tokens, _ptr(x_in), _ptr(x_out), karr, _ptr(pos), max_pos,
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_prefill_chunk")
 
 
 def embed(table, vocab, d_model, batch, tokens, x_out, ws, stream=None):

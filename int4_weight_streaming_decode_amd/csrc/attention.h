@@ -48,6 +48,7 @@ struct AttnArgs {
     const uint16_t* kvn;     // [B][Hkv][2][hd]: the new token's bf16 k (row 0) and v (row 1)
     const int* pos;          // [B]
     int cap, hq, hkv, batch, max_pos;
+    int kvb;                 // 1: sequence b has cache b; 0: every entry shares cache 0 (a prompt chunk)
     int nsplit;              // splits per (b, j)
     int T;                   // keys per split (multiple of 16)
     int pstride;             // partial-buffer stride per head (multiple of 32 splits)
@@ -116,8 +117,8 @@ I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool 
                               u32x2 (&vr)[HD / 16]) {
     constexpr int NKB = HD / 16;
     const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
-    const uint16_t* kbase = a.kc + (size_t)(g.b * a.hkv + g.j) * a.cap * HD;
-    const uint16_t* vbase = a.vc + (size_t)(g.b * a.hkv + g.j) * HD * a.cap;
+    const uint16_t* kbase = a.kc + (size_t)(g.b * a.kvb * a.hkv + g.j) * a.cap * HD;
+    const uint16_t* vbase = a.vc + (size_t)(g.b * a.kvb * a.hkv + g.j) * HD * a.cap;
     const size_t tile = (size_t)((g.t_s >> 4) + st) * 16 * HD;     // this subtile's 16-position tile
     // K tile [HD/32][16][32]: block mm of the four lanes of key r is 64 bytes;
     // one instruction reads the 1 KB block [mm][0..15][0..31]

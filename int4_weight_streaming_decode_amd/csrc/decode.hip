@@ -133,6 +133,7 @@ template <bool WT = true>
 struct EpiQKV {
     float* q; uint16_t* kc; uint16_t* vc; uint16_t* kvn; const int* pos_lds; const float2* cs;
     int cap, hq, hkv, hd, nb;
+    int kvb;                   // 1: sequence b appends to cache b; 0: all append to cache 0 (a prompt chunk)
     I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int half = hd >> 1;
@@ -155,7 +156,7 @@ struct EpiQKV {
             uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
             st_out<WT>(nr + i, ba); st_out<WT>(nr + i + half, bb);
             // 16-position tiles: K [hd/32][16][32], V [hd][16]
-            const size_t tile = ((size_t)b * hkv + head) * cap * hd + (size_t)(p >> 4) * 16 * hd;
+            const size_t tile = ((size_t)b * kvb * hkv + head) * cap * hd + (size_t)(p >> 4) * 16 * hd;
             const int tp = p & 15;
             if (mat == 1) {
                 uint16_t* kt = kc + tile;
@@ -246,14 +247,14 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float
 template <int FMT, int NB>
 __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x, int nb, const uint16_t* gain, float eps,
                                                        const int* pos, int max_pos, float* q, uint16_t* kc, uint16_t* vc,
-                                                       uint16_t* kvn, int cap, int hq, int hkv, double base, int* status) {
+                                                       uint16_t* kvn, int cap, int hq, int hkv, double base, int* status, int kvb) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
     int* pos_lds = (int*)L.extra;
     float2* cs = (float2*)(L.extra + 64);
     RopeSetup<NB>{pos, pos_lds, cs, status, nb, max_pos, cap, t.head_dim, base}();
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiQKV<false> ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb};
+    EpiQKV<false> ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb, kvb};
     gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_QKV>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -347,9 +348,9 @@ __global__ void __launch_bounds__(512) k_mfma_swiglu(MfmaTask m, float* act) {
 // the cos/sin table come from the staging kernel
 template <int NB>
 __global__ void __launch_bounds__(512) k_mfma_qkv(MfmaTask m, float* q, uint16_t* kc, uint16_t* vc, uint16_t* kvn,
-                                                  const int* posv, const float2* cs, int cap, int hq, int hkv) {
+                                                  const int* posv, const float2* cs, int cap, int hq, int hkv, int kvb) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    EpiQKV<false> ep{q, kc, vc, kvn, posv, cs, cap, hq, hkv, m.t.head_dim, m.nb};
+    EpiQKV<false> ep{q, kc, vc, kvn, posv, cs, cap, hq, hkv, m.t.head_dim, m.nb, kvb};
     mfma_gemm<KIND_QKV, NB, 2, MEPI_FN>(m, lds, ep, nullptr);
 }
 
@@ -545,7 +546,7 @@ __global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
             stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, attn_norm);
             stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, attn_norm, A.eps, L.red);
             __syncthreads();
-            EpiQKV<true> ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch};
+            EpiQKV<true> ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch, 1};
             NoNext nn;
             gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ, KIND_QKV>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
         }
@@ -898,12 +899,12 @@ int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const ui
 
 template <int FMT, int NB>
 int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, const int* pos, int max_pos,
-                 float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status, hipStream_t s) {
+                 float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status, int kvb, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_QKV>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
     launch_k(k_gemv_qkv<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
-                       kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status);
+                       kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status, kvb);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -997,8 +998,8 @@ int launch_swiglu(int fmt, int nb, const GemvTask& t, int nwg, const float* x, i
 }
 int launch_qkv(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int bn, const uint16_t* gain, float eps,
                const int* pos, int max_pos, float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status,
-               hipStream_t s) {
-#define CALL(F, N) return launch_qkv_t<F, N>(t, nwg, x, bn, gain, eps, pos, max_pos, q, kv, kvn, hq, hkv, base, status, s)
+               int kvb, hipStream_t s) {
+#define CALL(F, N) return launch_qkv_t<F, N>(t, nwg, x, bn, gain, eps, pos, max_pos, q, kv, kvn, hq, hkv, base, status, kvb, s)
     I4D_DISPATCH(fmt, nb, CALL)
 #undef CALL
 }
@@ -1022,8 +1023,9 @@ void plan_attention(const i4d_config* c, int B, int max_pos, int& nsplit, int& T
 // Attention arguments for layer region R (kvn = nullptr: the cache already
 // holds every attended key, as for the attention test hook).
 AttnArgs attn_args(const i4d_config* c, int B, const float* q, const i4d_kv* kv, const uint16_t* kvn, const int* pos,
-                   int max_pos, float* o, char* ws, const WsLayout& W, const char* R) {
+                   int max_pos, float* o, char* ws, const WsLayout& W, const char* R, int kvb = 1) {
     AttnArgs a;
+    a.kvb = kvb;
     a.q = q; a.kc = kv->k; a.vc = kv->v; a.kvn = kvn; a.pos = pos;
     a.cap = kv->capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads; a.batch = B; a.max_pos = max_pos;
     plan_attention(c, B, max_pos, a.nsplit, a.T);
@@ -1167,7 +1169,7 @@ bool mfma_layer_ok(const i4d_config* c, const i4d_layer* L) {
 // One layer for 9..32 sequences: staging + MFMA GEMM per projection, the
 // split-K attention in between (which handles any batch).
 int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
-                   const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s) {
+                   const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s, int kvb) {
     const int nb = nb_mfma(B), hd = c->head_dim;
     const int D = c->d_model, qw = c->n_q_heads * hd, F = c->d_ff, g = L->wq.group;
     int* status = (int*)(ws + WS_STATUS);
@@ -1192,14 +1194,14 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
     {
         TimeScope ts(I4D_TIME_QKV);
         rc = nb == 16 ? launch_mfma(k_mfma_qkv<16>, MfmaGeo<16, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
-                                    c->n_q_heads, c->n_kv_heads)
+                                    c->n_q_heads, c->n_kv_heads, kvb)
                       : launch_mfma(k_mfma_qkv<32>, MfmaGeo<32, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
-                                    c->n_q_heads, c->n_kv_heads);
+                                    c->n_q_heads, c->n_kv_heads, kvb);
     }
     if (rc) return rc;
     {
         TimeScope ts(I4D_TIME_ATTENTION);
-        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s);
+        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R, kvb), hd, s);
     }
     if (rc) return rc;
 
@@ -1361,7 +1363,7 @@ int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* lay
 // One layer as phase launches (q/k/v, attention, Wo, gate/up, down), using
 // the workspace region R.
 int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
-                     const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s) {
+                     const int* pos, int max_pos, char* ws, const WsLayout& W, char* R, hipStream_t s, int kvb) {
     const int nb = nb_slot(B), nwg = num_cus() * WG_PER_CU;
     const int hd = c->head_dim;
     int* status = (int*)(ws + WS_STATUS);
@@ -1378,12 +1380,12 @@ int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float
     {
         TimeScope ts(I4D_TIME_QKV);
         rc = launch_qkv(fq, nb, tq, nwg, x_in, B, L->attn_norm, c->rms_eps, pos, max_pos, q, kv, kvn, c->n_q_heads,
-                        c->n_kv_heads, c->rope_base, status, s);
+                        c->n_kv_heads, c->rope_base, status, kvb, s);
     }
     if (rc) return rc;
     {
         TimeScope ts(I4D_TIME_ATTENTION);
-        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R), hd, s);
+        rc = launch_attention(attn_args(c, B, q, kv, kvn, pos, max_pos, o, ws, W, R, kvb), hd, s);
     }
     if (rc) return rc;
 
@@ -1439,9 +1441,11 @@ int i4d_decode_layer(const i4d_config* cfg, const i4d_layer* layer, int32_t batc
 }
 
 // run = false: validate only (nothing is enqueued)
+// kvb = 1: sequence b uses its own cache (decode); 0: the batch is a chunk of
+// one sequence's tokens sharing cache 0 (prefill)
 static int decode_stack_impl(bool run, const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t batch,
                              const float* x_in, float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             void* ws, size_t ws_bytes, void* stream, int kvb = 1) {
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
     if (n_layers < 1 || !layers || !kv) return I4D_EINVAL;
@@ -1466,7 +1470,7 @@ static int decode_stack_impl(bool run, const i4d_config* cfg, int32_t n_layers, 
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
     if (cfg->exec_mode == 2) {
-        if (!I4D_ENABLE_PERSISTENT) return I4D_EUNSUPPORTED;
+        if (!I4D_ENABLE_PERSISTENT || kvb != 1) return I4D_EUNSUPPORTED;
         if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
         if (!run) return I4D_OK;
         TimeScope ts(I4D_TIME_PERSISTENT);
@@ -1478,8 +1482,8 @@ static int decode_stack_impl(bool run, const i4d_config* cfg, int32_t n_layers, 
         const float* in = (l == 0) ? x_in : (const float*)(R - W.layer_stride + W.x);
         float* out = (l == n_layers - 1) ? x_out : (float*)(R + W.x);
         const bool batched = batch > MAX_BATCH || phases_fit(&layers[l], batch) != I4D_OK;
-        rc = batched ? run_layer_mfma(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s)
-                     : run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s);
+        rc = batched ? run_layer_mfma(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s, kvb)
+                     : run_layer_phases(cfg, &layers[l], batch, in, out, &kv[l], pos, max_pos, w, W, R, s, kvb);
         if (rc) return rc;
     }
     return I4D_OK;
@@ -1545,6 +1549,12 @@ static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const floa
 int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
                         float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
     return lm_head_impl(true, w_lm, batch, h, chunk_rows, token_out, max_logit_out, ws, ws_bytes, stream);
+}
+
+int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens, const float* x_in,
+                      float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return decode_stack_impl(true, cfg, n_layers, layers, n_tokens, x_in, x_out, kv, pos, max_pos, ws, ws_bytes, stream, 0);
 }
 
 int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t batch, const int32_t* tokens, float* x_out,

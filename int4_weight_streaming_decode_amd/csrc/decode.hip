@@ -33,6 +33,9 @@ namespace {
 constexpr int GEMV_NT = I4D_GEMV_NT;       // threads per GEMV workgroup
 constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
 constexpr int ATTN_NT = I4D_ATTN_NT;       // threads per attention workgroup
+// the attention merge gives each (query head, 4 dims) slot its own thread:
+// G <= 16 query heads per KV head at head_dim 128
+static_assert(ATTN_NT >= 16 * 128 / 4, "attention workgroup smaller than its merge");
 constexpr int WG_PER_CU = I4D_WG_PER_CU;   // GEMV workgroups per compute unit
 constexpr int NSPLIT_MAX = 128;    // key-axis splits per (sequence, KV head)
 constexpr int MAX_BATCH = 8;          // matrix-vector (VALU) path
@@ -1247,6 +1250,8 @@ size_t persistent_lds(const i4d_config* c, int nsplit) {
 
 bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int B) {
     if (c->head_dim != 128 || B > 4 || n_layers > PERS_MAX_LAYERS) return false;
+    // the attention merge gives each (query head, 4 dims) slot its own thread
+    if ((c->n_q_heads / c->n_kv_heads) * (c->head_dim / 4) > PERS_NT) return false;
     const int nwg = num_cus();
     if (nwg > PERS_MAX_WG) return false;
     for (int l = 0; l < n_layers; ++l) {

@@ -40,3 +40,4 @@ from .decode import (  # noqa: F401
     swiglu,
     unpack_int4,
 )
+from .sample import gumbel_scores, philox4x32_10, sample_tokens, uniforms  # noqa: F401

@@ -255,11 +255,16 @@ def embed_tokens(table_bits: np.ndarray, tokens) -> np.ndarray:
     return bf16_to_f64(table_bits[tokens])
 
 
-def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, tokens, caches: list, pos, steps: int) -> dict:
+def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, tokens, caches: list, pos, steps: int,
+                  temperature=None, seed: int = 0) -> dict:
     """`steps` rounds of Primer 1.2's decode loop: embed the last token, run
-    the stack (appending each layer's K/V at pos), take the greedy token of the
-    LM head, advance every position by one.  Returns per-step tokens, maximum
-    logits and logits, the final hidden state and the caches."""
+    the stack (appending each layer's K/V at pos), take the LM head's token,
+    advance every position by one.  The token is the greedy one, or with a
+    temperature the Gumbel-max draw of oracle.sample with each sequence's
+    position as its counter word ("max_logit" then holds the winning perturbed
+    score and "logits" the perturbed scores).  Returns per-step tokens, maximum
+    scores and scores, the final hidden state and the caches."""
+    from .sample import sample_tokens
     tok = np.asarray(tokens, dtype=np.int64)
     pos = np.asarray(pos, dtype=np.int64)
     out = {"tokens": [], "max_logit": [], "logits": []}
@@ -267,6 +272,8 @@ def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, token
         r = decode_stack(shape, layers, embed_tokens(table_bits, tok), caches, pos)
         caches = r["caches"]
         tok, mx, logits = lm_head_argmax(w_lm, r["z"])
+        if temperature is not None:
+            tok, mx, logits = sample_tokens(logits, temperature, seed, pos)
         out["tokens"].append(tok.copy())
         out["max_logit"].append(mx)
         out["logits"].append(logits)

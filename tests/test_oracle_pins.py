@@ -427,3 +427,62 @@ def test_greedy_decode_follows_a_cyclic_successor_model():
         for b, p0 in enumerate([5, 9]):
             for s in range(4):                          # slots p0 .. p0+3 hold zeros (RoPE may give -0.0)
                 assert np.all(synth.bf16_value(kc[b, :, p0 + s]) == 0) and np.all(synth.bf16_value(vc[b, :, p0 + s]) == 0)
+
+
+# ----------------------------------------------------------------------------- temperature sampling
+
+def test_philox_matches_the_published_known_answers():
+    """oracle.sample's generator reproduces the Philox4x32-10 known-answer
+    vectors published with the generator (tests/golden/philox4x32_10_kat.json)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for v in kat["vectors"]:
+        c = [int(x, 16) for x in v["ctr"]]
+        k = [int(x, 16) for x in v["key"]]
+        out = oracle.philox4x32_10(*c, *k)
+        assert [int(o) for o in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_uniforms_lie_inside_the_unit_interval_and_are_uniform():
+    u = oracle.uniforms(200_000, 3, 17, 0x1234_5678_9ABC_DEF0)
+    assert u.min() > 0.0 and u.max() < 1.0
+    n = u.size
+    assert abs(u.mean() - 0.5) < 5 * np.sqrt(1 / 12 / n)
+    counts = np.histogram(u, bins=20, range=(0.0, 1.0))[0]
+    chi2 = np.sum((counts - n / 20) ** 2 / (n / 20))
+    assert chi2 < 60.0                       # df 19: p < 1e-5 above this
+    # the counter words and the key all change the stream
+    assert not np.array_equal(u[:64], oracle.uniforms(64, 4, 17, 0x1234_5678_9ABC_DEF0))
+    assert not np.array_equal(u[:64], oracle.uniforms(64, 3, 18, 0x1234_5678_9ABC_DEF0))
+    assert not np.array_equal(u[:64], oracle.uniforms(64, 3, 17, 0x1234_5678_9ABC_DEF1))
+    assert not np.array_equal(u[:64], oracle.uniforms(64, 3, 17, 0x1234_5679_9ABC_DEF0))
+
+
+def test_gumbel_max_draws_follow_the_tempered_softmax():
+    """Many independent draws (one per sequence index) land on each token with
+    the probability softmax(logits / T): a wrong sign, a dropped temperature or
+    a wrong noise law changes these frequencies."""
+    logits = np.array([1.0, 0.5, 0.0, -1.0, 2.0, 0.2, -0.3])
+    T, n = 0.7, 40_000
+    p = softmax(logits / T)
+    tok, score, s = oracle.sample_tokens(np.tile(logits, (n, 1)), T, 99, np.zeros(n, dtype=np.int64))
+    assert np.array_equal(score, s[np.arange(n), tok])
+    freq = np.bincount(tok, minlength=logits.size) / n
+    sigma = np.sqrt(p * (1 - p) / n)
+    assert np.all(np.abs(freq - p) < 5 * sigma), (freq, p)
+    chi2 = np.sum((freq - p) ** 2 / p) * n
+    assert chi2 < 35.0                       # df 6: p < 1e-5 above this
+    # at T = 2 the same logits give a flatter law
+    tok2 = oracle.sample_tokens(np.tile(logits, (n, 1)), 2.0, 5, np.zeros(n, dtype=np.int64))[0]
+    p2 = softmax(logits / 2.0)
+    freq2 = np.bincount(tok2, minlength=logits.size) / n
+    assert np.all(np.abs(freq2 - p2) < 5 * np.sqrt(p2 * (1 - p2) / n))
+
+
+def test_vanishing_temperature_gives_the_greedy_token():
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((4, 1000))
+    tok = oracle.sample_tokens(logits, 1e-9, 7, [0, 1, 2, 3])[0]
+    assert np.array_equal(tok, np.argmax(logits, axis=1))
+    with pytest.raises(ValueError):
+        oracle.sample_tokens(logits, 0.0, 7, [0, 1, 2, 3])

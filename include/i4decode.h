@@ -192,6 +192,23 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
                         int32_t* token_out, float* max_logit_out,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Temperature sampling from the same LM head (Primer 1.2 ends the step by
+ * sampling a token from the logits; the pages name no sampler).  token_out[b]
+ * is a draw from softmax((W_lm h_b) / temperature) by the Gumbel-max method:
+ * the lowest v maximising logit_v / temperature + g_v, with
+ * g_v = -log(-log(u_v)), u_v = (floor(x / 512) + 1/2) / 2^23 and x the first
+ * output word of Philox4x32-10 (Salmon et al., SC'11) at counter
+ * (v, b, counter[b], 0) and key (seed & 0xFFFFFFFF, seed >> 32).  The draw
+ * depends only on those inputs, so any split of the vocabulary gives the same
+ * token.  score_out[b] = the winning perturbed score.  temperature: positive
+ * and finite with a normal fp32 reciprocal (else I4D_EINVAL).  counter: [B]
+ * int32 (device), read by the kernels.  Everything else is as for
+ * i4d_lm_head_chunked.                                                       */
+int i4d_lm_head_sample(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
+                       float temperature, uint64_t seed, const int32_t* counter,
+                       int32_t* token_out, float* score_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Embedding lookup (Primer 1.2: the decode loop starts from the embedding of
  * the last token): x_out[b] = fp32 of row tokens[b] of the bf16 table
  * [vocab][d_model] (row-major).  tokens [B] int32 (device); an id outside
@@ -218,6 +235,16 @@ int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t bat
 int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
                     const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
                     int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream);
+
+/* i4d_decode_step with the token drawn as by i4d_lm_head_sample (Gumbel-max
+ * at `temperature` with `seed`); the counter word of sequence b is pos[b] as
+ * it is before this step's advance, so each step (and each replay of a
+ * captured step) draws fresh noise.  score_out [B]: the winning perturbed
+ * score.                                                                     */
+int i4d_decode_step_sample(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                           const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* score_out, int32_t* pos,
+                           int32_t max_pos, float* x_buf, const i4d_kv* kv, float temperature, uint64_t seed,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Expand an int4 matrix to fp32 out [n][k]: out = (code - 8) * scale, exact
  * (Unsloth article 二.3).  A test hook for the int4 format.                 */

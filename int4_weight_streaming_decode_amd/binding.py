@@ -78,12 +78,16 @@ def lib():
         L.i4d_decode_stack.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                        ctypes.POINTER(I4dKv), P, I, P, Z, P]
         L.i4d_lm_head_chunked.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P, Z, P]
+        L.i4d_lm_head_sample.argtypes = [ctypes.POINTER(I4dMat), I, P, I, ctypes.c_float, ctypes.c_uint64, P, P, P, P, Z, P]
         L.i4d_dequant_int4.argtypes = [ctypes.POINTER(I4dMat), P, P]
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
         L.i4d_prefill_chunk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                         ctypes.POINTER(I4dKv), P, I, P, Z, P]
         L.i4d_decode_step.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P, ctypes.POINTER(I4dMat), I,
                                       P, P, P, I, P, ctypes.POINTER(I4dKv), P, Z, P]
+        L.i4d_decode_step_sample.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P,
+                                             ctypes.POINTER(I4dMat), I, P, P, P, I, P, ctypes.POINTER(I4dKv),
+                                             ctypes.c_float, ctypes.c_uint64, P, Z, P]
         L.i4d_gemv.argtypes = [ctypes.POINTER(I4dMat), I, P, P, P, Z, P]
         L.i4d_attention.argtypes = [ctypes.POINTER(I4dConfig), I, P, ctypes.POINTER(I4dKv), P, I, P, P, Z, P]
         L.i4d_read_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
@@ -92,7 +96,7 @@ def lib():
         L.i4d_status_string.argtypes = [ctypes.c_int]
         L.i4d_status_string.restype = ctypes.c_char_p
         for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked", "i4d_embed",
-                     "i4d_decode_step", "i4d_prefill_chunk",
+                     "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop"):
             getattr(L, name).restype = ctypes.c_int
@@ -173,6 +177,13 @@ def lm_head_chunked(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out
            "i4d_lm_head_chunked")
 
 
+def lm_head_sample(w_lm: I4dMat, batch, h, chunk_rows, temperature, seed, counter, token_out, score_out, ws, stream=None):
+    """Gumbel-max draw from softmax(logits / temperature); counter: device int32 [B]."""
+    _check(lib().i4d_lm_head_sample(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, float(temperature), int(seed),
+                                    _ptr(counter), _ptr(token_out), _ptr(score_out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "i4d_lm_head_sample")
+
+
 def prefill_chunk(cfg, layers, n_tokens, x_in, x_out, kvs, pos, max_pos, ws, stream=None):
     """n_tokens prompt tokens of one sequence (x [n][D], positions pos [n] on the device) through the stack."""
     n = len(layers)
@@ -196,6 +207,18 @@ def decode_step(cfg, layers, embed_table, w_lm: I4dMat, batch, tokens, max_logit
     _check(lib().i4d_decode_step(ctypes.byref(cfg), n, larr, _ptr(embed_table), ctypes.byref(w_lm), batch, _ptr(tokens),
                                  _ptr(max_logit_out), _ptr(pos), max_pos, _ptr(x_buf), karr, _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)), "i4d_decode_step")
+
+
+def decode_step_sample(cfg, layers, embed_table, w_lm: I4dMat, batch, tokens, score_out, pos, max_pos, x_buf, kvs,
+                       temperature, seed, ws, stream=None):
+    """decode_step with the token drawn at `temperature` (counter word: each sequence's position)."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_decode_step_sample(ctypes.byref(cfg), n, larr, _ptr(embed_table), ctypes.byref(w_lm), batch,
+                                        _ptr(tokens), _ptr(score_out), _ptr(pos), max_pos, _ptr(x_buf), karr,
+                                        float(temperature), int(seed), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)), "i4d_decode_step_sample")
 
 
 def dequant_int4(w: I4dMat, out, stream=None):

@@ -68,6 +68,42 @@ I4D_DEVINL float float_from_order_key(u32 k) {
 }
 I4D_DEVINL u64 argmax_key(float logit, u32 idx) { return ((u64)float_order_key(logit) << 32) | (u64)(0xFFFFFFFFu - idx); }
 
+// ---------------------------------------------------------------- temperature sampling
+// First output word of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC'11): ten rounds, each multiplying
+// words 0 and 2 by the round multipliers and mixing the high halves with words
+// 1 and 3 and the round key; the key advances by the Weyl increments between
+// rounds.
+I4D_DEVINL u32 philox4x32_10_x0(u32 c0, u32 c1, u32 c2, u32 c3, u32 k0, u32 k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const u32 lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const u32 lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        c0 = hi1 ^ c1 ^ k0; c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1; c3 = lo0;
+    }
+    return c0;
+}
+
+// The score the LM head's argmax compares.  Greedy (inv_t == 0): the logit.
+// Sampling at temperature T = 1 / inv_t (Gumbel-max): logit / T + g with
+// g = -log(-log(u)), u = (floor(x / 512) + 1/2) / 2^23 (exact in fp32, strictly
+// inside (0, 1)), x = Philox4x32-10 word 0 at counter (row, sequence, ctr[b],
+// 0) and key (k0, k1).  The argmax of these scores is a draw from
+// softmax(logits / T), so the running argmax serves sampling unchanged.
+struct Sampler {
+    float inv_t;             // 0: greedy
+    u32 k0, k1;              // seed, low and high words
+    const int* ctr;          // [B] per-sequence counter word (device memory)
+    I4D_DEVINL float score(float logit, int b, u32 row) const {
+        if (inv_t == 0.f) return logit;
+        const u32 x = philox4x32_10_x0(row, (u32)b, (u32)ctr[b], 0u, k0, k1);
+        const float u = ((float)(x >> 9) + 0.5f) * 1.1920928955078125e-7f;     // 2^-23
+        return logit * inv_t - logf(-logf(u));
+    }
+};
+
 // ---------------------------------------------------------------- device-coherent accesses
 // Values one workgroup writes and another reads within the same kernel (the
 // persistent decode kernel passes activations, q, attention partials and the

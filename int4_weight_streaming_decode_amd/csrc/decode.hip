@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <math.h>
+#include <cmath>
 
 #include <algorithm>
 #include <vector>
@@ -179,12 +180,12 @@ struct EpiQKV {
 // `bslot` (a thread always serves the same slot: the epilogue's thread-to-slot
 // assignment repeats every pass)
 struct EpiArgmax {
-    int n; int nb; u64 best; int bslot;
+    int n; int nb; u64 best; int bslot; Sampler smp;
     I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int r = 2 * pair;
-        u64 k = argmax_key(va, (u32)r);
-        if (r + 1 < n) { const u64 k2 = argmax_key(vb, (u32)(r + 1)); k = k2 > k ? k2 : k; }
+        u64 k = argmax_key(smp.score(va, b, (u32)r), (u32)r);
+        if (r + 1 < n) { const u64 k2 = argmax_key(smp.score(vb, b, (u32)(r + 1)), (u32)(r + 1)); k = k2 > k ? k2 : k; }
         best = k > best ? k : best;
         bslot = b;
     }
@@ -262,11 +263,11 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x
 }
 
 template <int FMT, int NB>
-__global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h, int nb, u64* wg_keys) {
+__global__ void __launch_bounds__(GEMV_NT) k_lm_head(GemvTask t, const float* h, int nb, u64* wg_keys, Sampler smp) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_STD>(lds, t.k);
     StageFn<FMT, NB, PREC_STD> st{L.act, h, t.k, t.k, nb, nullptr, 0.f, L.red};
-    EpiArgmax ep{t.a.n, nb, 0ull, -1};
+    EpiArgmax ep{t.a.n, nb, 0ull, -1, smp};
     gemv_run<FMT, NB, PREC_STD, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_ADJ>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
     // workgroup best per batch slot -> this workgroup's key slots
     u64* kl = (u64*)(L.extra + GEMV_EXTRA);
@@ -358,10 +359,9 @@ __global__ void __launch_bounds__(512) k_mfma_qkv(MfmaTask m, float* q, uint16_t
 }
 
 template <int NB>
-__global__ void __launch_bounds__(512) k_mfma_lm(MfmaTask m, u64* wg_keys) {
+__global__ void __launch_bounds__(512) k_mfma_lm(MfmaTask m, u64* wg_keys, Sampler smp) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    NoNext none;
-    mfma_gemm<KIND_ADJ, NB, 1, MEPI_ARGMAX>(m, lds, none, wg_keys);
+    mfma_gemm<KIND_ADJ, NB, 1, MEPI_ARGMAX>(m, lds, smp, wg_keys);
 }
 
 // Workspace: an 8 KB header (status word, grid-barrier epoch, the attention
@@ -912,14 +912,15 @@ int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint1
 }
 
 template <int FMT, int NB>
-int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys, int32_t* tok, float* mx, hipStream_t s) {
+int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys, int32_t* tok, float* mx, const Sampler& smp,
+                hipStream_t s) {
     if constexpr (!FmtT<FMT>::INT4) {
         return I4D_EUNSUPPORTED;
     } else {
         const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k) + (size_t)GEMV_NT * 12;
         if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
         if (set_lds(k_lm_head<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
-        launch_k(k_lm_head<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys);
+        launch_k(k_lm_head<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys, smp);
         hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, MAX_BATCH, nb, tok, mx);
         return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
     }
@@ -1007,8 +1008,8 @@ int launch_qkv(int fmt, int nb, const GemvTask& t, int nwg, const float* x, int 
 #undef CALL
 }
 int launch_lm(int fmt, int nb, const GemvTask& t, int nwg, const float* h, int bn, u64* keys, int32_t* tok, float* mx,
-              hipStream_t s) {
-#define CALL(F, N) return launch_lm_t<F, N>(t, nwg, h, bn, keys, tok, mx, s)
+              const Sampler& smp, hipStream_t s) {
+#define CALL(F, N) return launch_lm_t<F, N>(t, nwg, h, bn, keys, tok, mx, smp, s)
     I4D_DISPATCH(fmt, nb, CALL)
 #undef CALL
 }
@@ -1502,7 +1503,8 @@ int i4d_decode_stack(const i4d_config* cfg, int32_t n_layers, const i4d_layer* l
 
 // run = false: validate only (nothing is enqueued)
 static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
-                        float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
+                        float* max_logit_out, void* ws, size_t ws_bytes, void* stream,
+                        const Sampler& smp = Sampler{0.f, 0u, 0u, nullptr}) {
     if (!w_lm || w_lm->dtype != I4D_WEIGHT_INT4) return I4D_EINVAL;
     int rc;
     if ((rc = validate_mat(w_lm, w_lm->n, w_lm->k, I4D_WEIGHT_INT4, w_lm->group))) return rc;
@@ -1531,8 +1533,8 @@ static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const floa
         u64* keys = (u64*)(w + WS_LM_KEYS);
         {
             TimeScope ts(I4D_TIME_LM_HEAD);
-            rc = nb == 16 ? launch_mfma(k_mfma_lm<16>, MfmaGeo<16, 1>::LDS_B, p, s, m, keys)
-                          : launch_mfma(k_mfma_lm<32>, MfmaGeo<32, 1>::LDS_B, p, s, m, keys);
+            rc = nb == 16 ? launch_mfma(k_mfma_lm<16>, MfmaGeo<16, 1>::LDS_B, p, s, m, keys, smp)
+                          : launch_mfma(k_mfma_lm<32>, MfmaGeo<32, 1>::LDS_B, p, s, m, keys, smp);
         }
         if (rc) return rc;
         hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)keys, p.nwg, nb, batch, token_out, max_logit_out);
@@ -1548,12 +1550,32 @@ static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const floa
     if (nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
     if (!run) return I4D_OK;
     TimeScope ts(I4D_TIME_LM_HEAD);
-    return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, s);
+    return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, smp, s);
+}
+
+// Host checks of the sampling arguments; the sampler of a valid set.
+static int make_sampler(float temperature, uint64_t seed, const int32_t* counter, Sampler& smp) {
+    if (!counter) return I4D_EINVAL;
+    if (!aligned(counter, 4)) return I4D_EALIGN;
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return I4D_EINVAL;
+    const float inv_t = (float)(1.0 / (double)temperature);
+    if (!std::isfinite(inv_t) || !std::isnormal(inv_t)) return I4D_EINVAL;
+    smp = Sampler{inv_t, (u32)(seed & 0xFFFFFFFFu), (u32)(seed >> 32), counter};
+    return I4D_OK;
 }
 
 int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
                         float* max_logit_out, void* ws, size_t ws_bytes, void* stream) {
     return lm_head_impl(true, w_lm, batch, h, chunk_rows, token_out, max_logit_out, ws, ws_bytes, stream);
+}
+
+int i4d_lm_head_sample(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, float temperature,
+                       uint64_t seed, const int32_t* counter, int32_t* token_out, float* score_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+    Sampler smp;
+    int rc;
+    if ((rc = make_sampler(temperature, seed, counter, smp))) return rc;
+    return lm_head_impl(true, w_lm, batch, h, chunk_rows, token_out, score_out, ws, ws_bytes, stream, smp);
 }
 
 int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens, const float* x_in,
@@ -1576,9 +1598,10 @@ int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t bat
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
-int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
-                    const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
-                    int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                            const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
+                            int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream,
+                            const Sampler& smp) {
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
     if (!embed || !w_lm || !tokens || !pos || !x_buf) return I4D_EINVAL;
@@ -1589,16 +1612,35 @@ int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* la
     float* x1 = x_buf + plane;
     // every check before anything is enqueued
     if ((rc = decode_stack_impl(false, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
-    if ((rc = lm_head_impl(false, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream))) return rc;
+    if ((rc = lm_head_impl(false, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp))) return rc;
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((cfg->d_model + 255) / 256, batch);
     hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, s, embed, w_lm->n, cfg->d_model, (const int*)tokens, x0,
                        (int*)((char*)ws + WS_STATUS));
     if (hipGetLastError() != hipSuccess) return I4D_EHIP;
     if ((rc = decode_stack_impl(true, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
-    if ((rc = lm_head_impl(true, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream))) return rc;
+    if ((rc = lm_head_impl(true, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp))) return rc;
     hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, s, pos, batch);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int i4d_decode_step(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                    const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
+                    int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+    return decode_step_impl(cfg, n_layers, layers, embed, w_lm, batch, tokens, max_logit_out, pos, max_pos, x_buf, kv, ws,
+                            ws_bytes, stream, Sampler{0.f, 0u, 0u, nullptr});
+}
+
+int i4d_decode_step_sample(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                           const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* score_out, int32_t* pos,
+                           int32_t max_pos, float* x_buf, const i4d_kv* kv, float temperature, uint64_t seed, void* ws,
+                           size_t ws_bytes, void* stream) {
+    Sampler smp;
+    int rc;
+    // the counter word of sequence b is its position pos[b] (read before the advance)
+    if ((rc = make_sampler(temperature, seed, pos, smp))) return rc;
+    return decode_step_impl(cfg, n_layers, layers, embed, w_lm, batch, tokens, score_out, pos, max_pos, x_buf, kv, ws,
+                            ws_bytes, stream, smp);
 }
 
 int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {

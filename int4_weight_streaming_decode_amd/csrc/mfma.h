@@ -374,7 +374,8 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
             for (int n = 0; n < NTL; ++n)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const u64 k = ok ? argmax_key(acc[t][n][e], (u32)row) : 0ull;
+                    const int seq = n * 16 + 4 * q + e;      // padded sequences (seq >= nb) keep key 0
+                    const u64 k = (ok && seq < m.nb) ? argmax_key(epi.score(acc[t][n][e], seq, (u32)row), (u32)row) : 0ull;
                     best[n][e] = k > best[n][e] ? k : best[n][e];
                 }
         }

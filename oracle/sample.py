@@ -18,8 +18,8 @@ so that any row of any chunk can draw its own number with no state:
   * counter (v, b, c_b, 0): row v, sequence b, and c_b, a per-sequence counter
     word the caller supplies (the decode loop passes the token's position);
   * key (seed mod 2^32, seed >> 32);
-  * the first output word x gives u = (floor(x / 256) + 1/2) / 2^24, which
-    lies strictly inside (0, 1).
+  * the first output word x gives u = (floor(x / 512) + 1/2) / 2^23, which
+    lies strictly inside (0, 1) and is exact in float32 as well (24 bits).
 
 Parity pins (tests/test_oracle_pins.py): the published Philox4x32-10
 known-answer vectors; the empirical frequencies of many draws against
@@ -57,7 +57,7 @@ def uniforms(n_rows: int, b: int, counter: int, seed: int) -> np.ndarray:
     """u_v for v = 0..n_rows-1 of sequence b (float64, strictly inside (0, 1))."""
     v = np.arange(n_rows, dtype=np.uint64)
     x = philox4x32_10(v, b, counter & 0xFFFFFFFF, 0, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)[0]
-    return ((x >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return ((x >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
 def gumbel_scores(logits: np.ndarray, temperature: float, seed: int, counters) -> np.ndarray:

@@ -198,3 +198,34 @@ def test_embed_and_decode_step_validation(lib):
     assert lib.i4d_embed(emb, 0, 256, 1, tok, xb, ws, 1 << 20, None) == B.I4D_EINVAL
     assert lib.i4d_embed(emb, 10, 256, 0, tok, xb, ws, 1 << 20, None) == B.I4D_ERANGE
     assert lib.i4d_embed(emb, 10, 256, 1, tok, xb, ws, 100, None) == B.I4D_EWORKSPACE
+
+
+def test_sampling_validation(lib):
+    """Temperature and counter checks of the sampling entry points; every call
+    here fails validation before anything is enqueued."""
+    w = _mat(1000, 256)
+    P = ctypes.c_void_p
+    h, out, ws, ctr = P(0x100000), P(0x200000), P(0x400000), P(0x300000)
+
+    def lm(temperature=1.0, counter=ctr, chunk=64, batch=1):
+        return lib.i4d_lm_head_sample(ctypes.byref(w), batch, h, chunk, temperature, 12345, counter, out, out, ws,
+                                      1 << 20, None)
+
+    for t in (0.0, -1.0, float("nan"), float("inf"), 1e-39, 3e38):     # 1e-39: 1/T overflows; 3e38: 1/T subnormal
+        assert lm(temperature=t) == B.I4D_EINVAL, t
+    assert lm(counter=None) == B.I4D_EINVAL
+    assert lm(counter=P(0x300002)) == B.I4D_EALIGN
+    assert lm(chunk=0) == B.I4D_ERANGE                                # valid sampler, then the LM head's own checks
+    assert lm(batch=33) == B.I4D_ERANGE
+    cfg = _cfg()
+    L = _layer(cfg)
+    kv = B.I4dKv(0x500000, 0x600000, 256)
+    tok, pos, xb, emb = P(0x700000), P(0x720000), P(0x800000), P(0x900000)
+
+    def step(temperature=0.8, pos=pos, max_pos=127):
+        return lib.i4d_decode_step_sample(ctypes.byref(cfg), 1, ctypes.byref(L), emb, ctypes.byref(w), 1, tok, out, pos,
+                                          max_pos, xb, ctypes.byref(kv), temperature, 7, ws, 1 << 30, None)
+
+    assert step(pos=None) == B.I4D_EINVAL
+    assert step(temperature=0.0) == B.I4D_EINVAL
+    assert step(max_pos=256) == B.I4D_ERANGE

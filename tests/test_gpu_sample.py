@@ -1,0 +1,149 @@
+"""Temperature sampling through the C ABI (i4d_lm_head_sample,
+i4d_decode_step_sample) against oracle.sample: the same Philox4x32-10
+uniforms and Gumbel-max rule, logits in float64 on the oracle side.  Token
+ids must match exactly unless the oracle's top-2 gap of perturbed scores is a
+near-tie (then the GPU's token must be a valid near-maximiser); the winning
+scores to the usual float bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from int4_weight_streaming_decode_amd import binding as B
+from synth import gpu as G
+from tests.gpu_util import DevLayer, DevKV, DevMat, assert_close, config_of, dev, workspace
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x0123_4567_89AB_CDEF
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _check_draw(got_tok, got_score, ref_tok, ref_scores, tols, what):
+    """Exact ids unless the perturbed top-2 gap is within tols[b], the error
+    the GPU's float32 logits may carry."""
+    for b in range(len(got_tok)):
+        s = ref_scores[b]
+        srt = np.sort(s)
+        tol = tols[b]
+        if srt[-1] - srt[-2] > tol:
+            assert got_tok[b] == ref_tok[b], f"{what} b={b}: token {got_tok[b]} != {ref_tok[b]}"
+        else:
+            assert s[got_tok[b]] >= srt[-1] - tol, f"{what} b={b}: near-tie, token {got_tok[b]} not a near-maximiser"
+    assert_close(np.asarray(got_score, dtype=np.float64), ref_scores[np.arange(len(ref_tok)), ref_tok], what=f"{what} score")
+
+
+def _tols(logits, T):
+    return 1e-3 * np.sqrt(np.mean(logits ** 2, axis=1)) / T + 1e-4
+
+
+@pytest.mark.parametrize("vocab,d,batch,T", [(3000, 512, 1, 0.8), (20001, 1024, 5, 1.3), (9000, 1024, 16, 0.6),
+                                             (4099, 5120, 32, 2.0)])
+def test_lm_head_sample_matches_oracle(vocab, d, batch, T):
+    _print_case("lm_head_sample", vocab, d, batch, T)
+    lm = synth.make_lm_head(vocab, d, 128, seed=vocab + 7 * batch)
+    h = synth.make_hidden(d, seed=vocab + 3, batch=batch)
+    ctr = np.random.default_rng(batch).integers(0, 2 ** 31 - 1, size=batch).astype(np.int32)
+    _, _, logits = oracle.lm_head_argmax(lm, h.astype(np.float64))
+    ref_tok, _, ref_scores = oracle.sample_tokens(logits, T, SEED, ctr)
+    m = DevMat(lm)
+    cfg = B.make_config(d, 4, 2, 128, 128 * 8, 1e-6, 1e4)
+    ws = workspace(cfg, batch, 0, vocab=vocab)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    sc = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    runs = []
+    for rep in range(2):
+        B.lm_head_sample(m.mat, batch, dev(h), 8192, T, SEED, dev(ctr), tok, sc, ws)
+        torch.cuda.synchronize()
+        runs.append((tok.cpu().numpy().copy(), sc.cpu().numpy().copy()))
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1]), "same inputs, different draw"
+    _check_draw(runs[0][0], runs[0][1], ref_tok, ref_scores, _tols(logits, T), "lm_head_sample")
+
+
+def test_lm_head_sample_at_full_size():
+    """152064 x 5120 int4 head from the bench's device generator, batch 2."""
+    shape = synth.SHAPES["27b_lm"]
+    batch, T = 2, 0.9
+    _print_case("lm_head_sample full size", shape.vocab, shape.d_model, batch)
+    W = G.make_lm_head_gpu(shape.vocab, shape.d_model, shape.group, 2)
+    mat = B.make_mat(W["codes"], W["scales"], W["n"], W["k"], W["group"], B.WEIGHT_INT4)
+    h = G.make_x_gpu(shape, 8, batch)
+    ctr = np.array([8192, 70000], dtype=np.int32)
+    ws = workspace(config_of(shape), batch, 0, vocab=shape.vocab)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    sc = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    B.lm_head_sample(mat, batch, h, shape.lm_chunk, T, SEED, dev(ctr), tok, sc, ws)
+    torch.cuda.synchronize()
+    host = {"codes": W["codes"].cpu().numpy(), "scales": W["scales"].cpu().numpy().view(np.uint16),
+            "n": W["n"], "k": W["k"], "group": W["group"]}
+    _, _, logits = oracle.lm_head_argmax(host, h.cpu().numpy().astype(np.float64))
+    ref_tok, _, ref_scores = oracle.sample_tokens(logits, T, SEED, ctr)
+    _check_draw(tok.cpu().numpy(), sc.cpu().numpy(), ref_tok, ref_scores, _tols(logits, T), "full-size sample")
+
+
+def test_low_temperature_sample_is_the_greedy_token():
+    vocab, d, batch = 5000, 512, 3
+    _print_case("lm_head_sample low temperature", vocab, d, batch)
+    lm = synth.make_lm_head(vocab, d, 128, seed=11)
+    h = synth.make_hidden(d, seed=12, batch=batch)
+    m = DevMat(lm)
+    ws = workspace(B.make_config(d, 4, 2, 128, 1024, 1e-6, 1e4), batch, 0, vocab=vocab)
+    tg = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    ts = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    mx = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    B.lm_head_chunked(m.mat, batch, dev(h), 8192, tg, mx, ws)
+    B.lm_head_sample(m.mat, batch, dev(h), 8192, 1e-5, SEED, dev(np.arange(batch, dtype=np.int32)), ts, mx, ws)
+    torch.cuda.synchronize()
+    _, _, logits = oracle.lm_head_argmax(lm, h.astype(np.float64))
+    for b in range(batch):
+        srt = np.sort(logits[b])
+        assert srt[-1] - srt[-2] > 1e-3, "seed gives a near-tie: pick another"
+    assert np.array_equal(tg.cpu().numpy(), ts.cpu().numpy())
+
+
+SHAPE = synth.SHAPES["tiny"].with_(name="gen", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128, d_ff=1024,
+                                   group=128, rope_base=1e6)
+VOCAB = 3000
+
+
+@pytest.mark.parametrize("batch", [2, 16])
+def test_sampled_decode_steps_match_the_oracle_loop(batch):
+    n_layers, pos0, steps, T = 2, 150, 3, 0.7
+    cap = 160
+    _print_case("decode_step_sample", batch, n_layers, steps, T)
+    layers = [synth.make_layer(SHAPE, 81 + batch, l) for l in range(n_layers)]
+    caches = [synth.make_kv(SHAPE, 81 + batch, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    table = synth.make_embedding(VOCAB, SHAPE.d_model, 81 + batch)
+    lm = synth.make_lm_head(VOCAB, SHAPE.d_model, SHAPE.group, 82 + batch)
+    tok0 = np.random.default_rng(batch + 1).integers(0, VOCAB, size=batch).astype(np.int32)
+    Ls = [DevLayer(l) for l in layers]
+    kvs = [DevKV(*c) for c in caches]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+    ws = workspace(cfg, batch, cap - 1, vocab=VOCAB, n_layers=n_layers)
+    tokens = dev(tok0)
+    pos = dev(np.full(batch, pos0, dtype=np.int32))
+    sc = torch.empty(batch, dtype=torch.float32, device="cuda")
+    xbuf = torch.empty((2, batch, SHAPE.d_model), dtype=torch.float32, device="cuda")
+    got = []
+    for s in range(steps):
+        B.decode_step_sample(cfg, [l.layer for l in Ls], emb, W.mat, batch, tokens, sc, pos, pos0 + s, xbuf,
+                             [k.kv for k in kvs], T, SEED, ws)
+        torch.cuda.synchronize()
+        got.append((tokens.cpu().numpy().copy(), sc.cpu().numpy().copy()))
+    assert B.read_device_status(ws) == 0
+    ref = oracle.greedy_decode(SHAPE, layers, table, lm, tok0, caches, [pos0] * batch, steps, temperature=T, seed=SEED)
+    for s in range(steps):
+        scores = ref["logits"][s]                       # the perturbed scores of the oracle's draw
+        tols = 1e-3 * np.sqrt(np.mean(scores ** 2, axis=1)) + 1e-4
+        srt = np.sort(scores, axis=1)
+        tie = any(srt[b, -1] - srt[b, -2] <= tols[b] for b in range(batch))
+        _check_draw(got[s][0], got[s][1], ref["tokens"][s], scores, tols, f"step {s}")
+        if tie:
+            pytest.skip(f"step {s}: near-tie, later steps are not comparable")

@@ -47,10 +47,10 @@ WORKLOADS = {
 
 # library kernel behind each timed phase (batches of 1..8: matrix-vector
 # kernels; 9..32: the matrix-core GEMM kernels)
-KERNEL_NAMES = {"qkv": "k_gemv_qkv", "attention": "k_attention<128>", "wo": "k_gemv_rows (Wo)",
+KERNEL_NAMES = {"qkv": "k_gemv_qkv", "attention": "k_attention<128, false>", "wo": "k_gemv_rows (Wo)",
                 "gate_up": "k_gemv_swiglu", "down": "k_gemv_rows (W_down)", "lm_head": "k_lm_head",
                 "persistent": "k_decode_persistent"}
-KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128>", "wo": "k_mfma_rows (Wo)",
+KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128, false>", "wo": "k_mfma_rows (Wo)",
                         "gate_up": "k_mfma_swiglu", "down": "k_mfma_rows (W_down)", "lm_head": "k_mfma_lm"}
 
 
@@ -143,6 +143,10 @@ def main():
                     help="capture one whole step (stack, LM head, position advance) in a HIP graph and replay it in "
                          "the timed region; the attention split is then planned for the cache capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: the LM head draws the token at this temperature (Gumbel-max) instead of the greedy argmax")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="> 0: paged KV caches (pages of this many positions, shuffled over a pool) instead of contiguous ones")
     ap.add_argument("--roofline-kernel", default=None, choices=["qkv", "attention", "wo", "gate_up", "down", "persistent"],
                     help="kernel whose launches are timed inside the timed region (default: gate_up with per-phase "
                          "launches, persistent with the persistent kernel)")
@@ -182,6 +186,11 @@ def main():
     extra = [k for k in phases if k != rk] if args.breakdown_steps > 0 else []
     n_total = args.warmup + 2 * args.steps + len(extra) * args.breakdown_steps
     cap = ((shape.kv_len + n_total + 1 + 15) // 16) * 16
+    if args.page_size > 0:
+        if args.page_size % 16 or args.exec_mode == 2:
+            sys.exit("--page-size must be a multiple of 16 and cannot be combined with --exec-mode 2")
+        cap = (cap + args.page_size - 1) // args.page_size * args.page_size
+    pgen = torch.Generator(device="cpu").manual_seed(5)
     t_gen = time.perf_counter()
     keep = []
     layers, kvs = [], []
@@ -195,9 +204,17 @@ def main():
             else:
                 mats[n] = B.make_mat(m["bf16"], None, m["n"], m["k"], 0, B.WEIGHT_BF16)
         layers.append(B.make_layer(p["attn_norm"], p["ffn_norm"], mats))
-        k, v = G.make_kv_gpu(shape, 1, l, batch, cap)
-        kvs.append(B.make_kv(k, v, cap))
-        keep.append((p, k, v))
+        if args.page_size > 0:
+            # a pool of batch * cap / P pages, each sequence's pages in shuffled order
+            n_pages = batch * (cap // args.page_size)
+            k, v = G.make_kv_gpu(shape, 1, l, n_pages, args.page_size)
+            table = torch.randperm(n_pages, generator=pgen).to(torch.int32).reshape(batch, -1).cuda()
+            kvs.append(B.make_kv(k, v, cap, table, args.page_size, n_pages))
+            keep.append((p, k, v, table))
+        else:
+            k, v = G.make_kv_gpu(shape, 1, l, batch, cap)
+            kvs.append(B.make_kv(k, v, cap))
+            keep.append((p, k, v))
         if (l + 1) % 8 == 0 or l + 1 == shape.n_layers:
             print(f"[bench] inputs: layer {l + 1}/{shape.n_layers} on the device", file=sys.stderr, flush=True)
     lm_mat = None
@@ -221,6 +238,12 @@ def main():
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
+    def lm_head(h):
+        if args.temperature > 0:
+            B.lm_head_sample(lm_mat, batch, h, shape.lm_chunk, args.temperature, 0x5EED, pos, tok, mx, ws)
+        else:
+            B.lm_head_chunked(lm_mat, batch, h, shape.lm_chunk, tok, mx, ws)
+
     def step(i, events=None):
         max_pos = shape.kv_len + i
         if events:
@@ -229,7 +252,7 @@ def main():
         if events:
             events[1].record()
         if lm:
-            B.lm_head_chunked(lm_mat, batch, out, shape.lm_chunk, tok, mx, ws)
+            lm_head(out)
         if events:
             events[2].record()
         pos.add_(1)
@@ -253,7 +276,7 @@ def main():
         with torch.cuda.graph(graph, stream=gs):
             B.decode_stack(cfg, layers, batch, x, out, kvs, pos, cap - 1, ws)
             if lm:
-                B.lm_head_chunked(lm_mat, batch, out, shape.lm_chunk, tok, mx, ws)
+                lm_head(out)
             pos.add_(1)
         torch.cuda.current_stream().wait_stream(gs)
         torch.cuda.synchronize()
@@ -337,7 +360,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(shape, wdtype, lm, batch), "batch": batch, "kv_len": shape.kv_len,
                    "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode,
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "temperature": args.temperature, "page_size": args.page_size},
         "hbm_gbps": hbm_gbps,
         "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
         "algorithmic_bytes_per_step": step_bytes,

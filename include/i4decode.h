@@ -69,6 +69,7 @@ extern "C" {
 #define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
 #define I4D_DEV_BARRIER_TIMEOUT 2 /* a grid barrier of the persistent kernel gave up waiting */
 #define I4D_DEV_BAD_TOKEN     4   /* a token id outside the embedding table: that row became zeros */
+#define I4D_DEV_BAD_PAGE      8   /* a KV page id outside the pool: read as page 0, append dropped */
 
 /* ---- weight matrices ---- */
 #define I4D_WEIGHT_INT4 0
@@ -115,16 +116,35 @@ typedef struct i4d_config {
 } i4d_config;
 
 /* KV cache of one layer, in tiles of 16 positions (each attention load then
- * reads whole cache lines).  For sequence b, KV head j, position t, dim d:
+ * reads whole cache lines).
+ *
+ * Contiguous (pages == NULL).  For sequence b, KV head j, position t, dim d:
  *   k (after RoPE): bf16 element at [b][j][t / 16][d / 32][t % 16][d % 32]
  *   v:              bf16 element at [b][j][t / 16][d][t % 16]
  * i.e. k is [B][n_kv_heads][capacity/16][head_dim/32][16][32] and v is
  * [B][n_kv_heads][capacity/16][head_dim][16].  capacity % 16 == 0.  Slot t of
- * sequence b holds the token at position t.                                  */
+ * sequence b holds the token at position t.
+ *
+ * Paged (pages != NULL; batches of sequences with their own lengths share one
+ * pool).  k and v are pools of n_pages pages of page_size positions
+ * (page_size % 16 == 0, capacity % page_size == 0), laid out per page as one
+ * sequence's cache of capacity page_size: k [n_pages][n_kv_heads]
+ * [page_size/16][head_dim/32][16][32], v [n_pages][n_kv_heads]
+ * [page_size/16][head_dim][16].  pages is a device int32 table
+ * [B][capacity / page_size]: position t of sequence b lives in page
+ * pages[b * (capacity / page_size) + t / page_size] at offset
+ * t % page_size.  capacity is the longest sequence the table can map.  Page
+ * ids outside 0..n_pages-1 are never dereferenced: attention reads page 0
+ * instead, the append is dropped, and I4D_DEV_BAD_PAGE is set in the
+ * workspace status word.  The persistent kernel (exec_mode 2) does not take
+ * paged caches (I4D_EUNSUPPORTED).                                            */
 typedef struct i4d_kv {
     uint16_t* k;
     uint16_t* v;
     int32_t capacity;
+    const int32_t* pages;    /* NULL: contiguous */
+    int32_t page_size;       /* paged only */
+    int32_t n_pages;         /* paged only */
 } i4d_kv;
 
 /* Bytes of workspace needed to run up to n_layers layers per call for this

@@ -24,6 +24,7 @@ WS_MIN_BYTES = 16384 + 4096 * 32 * 8    # I4D_WS_MIN_BYTES
 I4D_DEV_BAD_POS = 1
 I4D_DEV_BARRIER_TIMEOUT = 2
 I4D_DEV_BAD_TOKEN = 4
+I4D_DEV_BAD_PAGE = 8
 
 WEIGHT_INT4 = 0
 WEIGHT_BF16 = 1
@@ -50,7 +51,8 @@ class I4dConfig(ctypes.Structure):
 
 
 class I4dKv(ctypes.Structure):
-    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("pages", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class I4DError(RuntimeError):
@@ -141,8 +143,10 @@ def make_layer(attn_norm, ffn_norm, mats: dict) -> I4dLayer:
                     ffn_norm.data_ptr(), mats["wg"], mats["wu"], mats["wd"])
 
 
-def make_kv(k_cache, v_cache, capacity) -> I4dKv:
-    return I4dKv(k_cache.data_ptr(), v_cache.data_ptr(), capacity)
+def make_kv(k_cache, v_cache, capacity, pages=None, page_size=0, n_pages=0) -> I4dKv:
+    """Contiguous cache, or (pages: device int32 [B][capacity / page_size]) a paged pool of n_pages pages."""
+    return I4dKv(k_cache.data_ptr(), v_cache.data_ptr(), capacity, pages.data_ptr() if pages is not None else None,
+                 page_size, n_pages)
 
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)

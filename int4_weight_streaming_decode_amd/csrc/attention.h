@@ -41,6 +41,26 @@
 #pragma once
 #include "common.h"
 
+// Where the 16-position tiles of a KV cache live.  pages == nullptr: the
+// contiguous layout [row][Hkv][cap/16] (the caller's cap and Hkv).  Otherwise a
+// pool of pages of `page_tiles` tiles, laid out [page][Hkv][page_tiles], and a
+// table [row][pps] of page ids; an id outside 0..n_pages-1 reads page 0 and
+// raises I4D_DEV_BAD_PAGE in *status.
+struct KvMap {
+    const int* pages;
+    int page_tiles, n_pages, pps;
+};
+
+// Element offset of tile t of (cache row r, KV head j), for tiles of 16 * hd
+// elements.  bad: set when the page id was out of range (page 0 was used).
+I4D_DEVINL size_t kv_tile_off(const KvMap& m, int cap, int hkv, int hd, int r, int j, int t, bool& bad) {
+    if (m.pages == nullptr) return ((size_t)(r * hkv + j) * cap + (size_t)t * 16) * hd;
+    int pg = m.pages[(size_t)r * m.pps + t / m.page_tiles];
+    bad = pg < 0 || pg >= m.n_pages;
+    if (bad) pg = 0;
+    return ((size_t)(pg * hkv + j) * m.page_tiles + t % m.page_tiles) * 16 * hd;
+}
+
 struct AttnArgs {
     const float* q;          // [B][Hq][hd] fp32
     const uint16_t* kc;      // [B][Hkv][cap/16][hd/32][16][32]
@@ -57,6 +77,8 @@ struct AttnArgs {
     float* po;               // [B][Hq][pstride][hd]
     int* cnt;                // [B][Hkv] arrival counters, zero between calls
     float* o;                // [B][Hq][hd] fp32 merged output
+    KvMap pg;                // paged caches (pg.pages == nullptr: contiguous)
+    int* status;             // workspace status word (I4D_DEV_BAD_PAGE)
 };
 
 I4D_DEVINL u32x4 nt_load_k(const u32x4* p) { return ld_g_nt(p); }
@@ -112,14 +134,30 @@ struct AttnRegs {
 // A slot past the item (live = false) reads one 16-byte word of the cache for
 // every lane instead: the loads stay unconditional, so the compiler can count
 // them exactly, but cost one cache line each.
-template <int HD>
+// PAGED: the cache is a page pool (a.pg), compiled separately so that the
+// contiguous kernel keeps its plain address arithmetic.
+template <int HD, bool PAGED>
 I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool live, u32x4 (&kr)[HD / 32],
                               u32x2 (&vr)[HD / 16]) {
     constexpr int NKB = HD / 16;
     const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
-    const uint16_t* kbase = a.kc + (size_t)(g.b * a.kvb * a.hkv + g.j) * a.cap * HD;
-    const uint16_t* vbase = a.vc + (size_t)(g.b * a.kvb * a.hkv + g.j) * HD * a.cap;
-    const size_t tile = (size_t)((g.t_s >> 4) + st) * 16 * HD;     // this subtile's 16-position tile
+    // kbase/vbase + tile: this subtile's 16-position tile (kbase/vbase alone: a
+    // slot past the item reads tile 0 of the row)
+    const uint16_t* kbase;
+    const uint16_t* vbase;
+    size_t tile;
+    if constexpr (PAGED) {
+        bool bad = false;
+        const size_t t0 = kv_tile_off(a.pg, a.cap, a.hkv, HD, g.b * a.kvb, g.j, live ? (g.t_s >> 4) + st : 0, bad);
+        if (bad && lane == 0 && a.status) raise_status(a.status, I4D_DEV_BAD_PAGE);
+        kbase = a.kc + t0;
+        vbase = a.vc + t0;
+        tile = 0;
+    } else {
+        kbase = a.kc + (size_t)(g.b * a.kvb * a.hkv + g.j) * a.cap * HD;
+        vbase = a.vc + (size_t)(g.b * a.kvb * a.hkv + g.j) * HD * a.cap;
+        tile = (size_t)((g.t_s >> 4) + st) * 16 * HD;
+    }
     // K tile [HD/32][16][32]: block mm of the four lanes of key r is 64 bytes;
     // one instruction reads the 1 KB block [mm][0..15][0..31]
     const uint16_t* kp = live ? kbase + tile + r * 32 + 8 * gq : kbase;
@@ -132,14 +170,14 @@ I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool 
 }
 
 // Issue the loads of round r of this wave.
-template <int HD, int NT, int NSW>
+template <int HD, int NT, int NSW, bool PAGED = false>
 I4D_DEVINL void attn_load_round(const AttnArgs& a, const AttnGeo& g, int rnd, AttnRegs<HD, NSW>& R) {
     constexpr int NW = NT / 64;
     const int wave = i4d_tid() >> 6;
 #pragma unroll
     for (int i = 0; i < NSW; ++i) {
         const int st = (rnd * NSW + i) * NW + wave;
-        attn_load_sub<HD>(a, g, st, st < g.nsub, R.k[i], R.v[i]);
+        attn_load_sub<HD, PAGED>(a, g, st, st < g.nsub, R.k[i], R.v[i]);
     }
 }
 
@@ -172,7 +210,7 @@ I4D_DEVINL void attn_patch_new(const AttnArgs& a, const AttnGeo& g, int st, u32x
 
 // The whole item: optional round-0 registers already loaded (pre = true),
 // compute, per-item partial, and the merge by the last split to arrive.
-template <int HD, int NT, int NSW>
+template <int HD, int NT, int NSW, bool PAGED = false>
 I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, NSW>& R, bool pre) {
     constexpr int NW = NT / 64, NKB = HD / 16, DPL = HD / 4;
     const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
@@ -195,7 +233,7 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) qv[kb] = ld_g((const f4*)(qrow + 32 * (kb >> 1) + 4 * (kb & 1)));
     }
-    if (!pre) attn_load_round<HD, NT, NSW>(a, g, 0, R);
+    if (!pre) attn_load_round<HD, NT, NSW, PAGED>(a, g, 0, R);
     s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
     if (wave == 0) {
         const float qs = (r < G) ? a.qscale : 0.f;
@@ -276,7 +314,7 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
     // rounds of NSW subtiles per wave: round 0 is in R already
     const int nround = (nsub + NW * NSW - 1) / (NW * NSW);
     for (int rnd = 0; rnd < nround; ++rnd) {
-        if (rnd > 0) attn_load_round<HD, NT, NSW>(a, g, rnd, R);
+        if (rnd > 0) attn_load_round<HD, NT, NSW, PAGED>(a, g, rnd, R);
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
             const int st = (rnd * NSW + i) * NW + wave;

@@ -138,6 +138,8 @@ struct EpiQKV {
     float* q; uint16_t* kc; uint16_t* vc; uint16_t* kvn; const int* pos_lds; const float2* cs;
     int cap, hq, hkv, hd, nb;
     int kvb;                   // 1: sequence b appends to cache b; 0: all append to cache 0 (a prompt chunk)
+    KvMap pg;                  // paged cache (pg.pages == nullptr: contiguous)
+    int* status;               // I4D_DEV_BAD_PAGE when a page id is out of range (the append is dropped)
     I4D_DEVINL void operator()(int, int pair, int b, float va, float vb) {
         if (b >= nb) return;
         const int half = hd >> 1;
@@ -160,7 +162,12 @@ struct EpiQKV {
             uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
             st_out<WT>(nr + i, ba); st_out<WT>(nr + i + half, bb);
             // 16-position tiles: K [hd/32][16][32], V [hd][16]
-            const size_t tile = ((size_t)b * kvb * hkv + head) * cap * hd + (size_t)(p >> 4) * 16 * hd;
+            bool bad = false;
+            const size_t tile = kv_tile_off(pg, cap, hkv, hd, b * kvb, head, p >> 4, bad);
+            if (bad) {
+                if (status && i == 0) raise_status(status, I4D_DEV_BAD_PAGE);
+                return;
+            }
             const int tp = p & 15;
             if (mat == 1) {
                 uint16_t* kt = kc + tile;
@@ -251,14 +258,15 @@ __global__ void __launch_bounds__(GEMV_NT) k_gemv_swiglu(GemvTask t, const float
 template <int FMT, int NB>
 __global__ void __launch_bounds__(GEMV_NT) k_gemv_qkv(GemvTask t, const float* x, int nb, const uint16_t* gain, float eps,
                                                        const int* pos, int max_pos, float* q, uint16_t* kc, uint16_t* vc,
-                                                       uint16_t* kvn, int cap, int hq, int hkv, double base, int* status, int kvb) {
+                                                       uint16_t* kvn, int cap, int hq, int hkv, double base, int* status, int kvb,
+                                                       KvMap pgm) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     GemvLds L = carve<FMT, NB, PREC_QKV>(lds, t.k);
     int* pos_lds = (int*)L.extra;
     float2* cs = (float2*)(L.extra + 64);
     RopeSetup<NB>{pos, pos_lds, cs, status, nb, max_pos, cap, t.head_dim, base}();
     StageFn<FMT, NB, PREC_QKV> st{L.act, x, t.k, t.k, nb, gain, eps, L.red};
-    EpiQKV<false> ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb, kvb};
+    EpiQKV<false> ep{q, kc, vc, kvn, pos_lds, cs, cap, hq, hkv, t.head_dim, nb, kvb, pgm, status};
     gemv_run<FMT, NB, PREC_QKV, GEMV_NT, GEMV_D, MaxJ<NB>::v, KIND_QKV>(t, blockIdx.x, gridDim.x, L.act, L.part, st, ep);
 }
 
@@ -307,13 +315,13 @@ __global__ void __launch_bounds__(256) k_lm_finalize(const u64* wg_keys, int nwg
     }
 }
 
-template <int HD>
+template <int HD, bool PAGED>
 __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int NSW = AttnNsw<ATTN_NT>::v;
     const int items = a.batch * a.hkv * a.nsplit;
     AttnRegs<HD, NSW> R;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW>(a, it, lds, R, false);
+    for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW, PAGED>(a, it, lds, R, false);
 }
 
 // ---------------------------------------------------------------- decode loop glue
@@ -352,9 +360,10 @@ __global__ void __launch_bounds__(512) k_mfma_swiglu(MfmaTask m, float* act) {
 // the cos/sin table come from the staging kernel
 template <int NB>
 __global__ void __launch_bounds__(512) k_mfma_qkv(MfmaTask m, float* q, uint16_t* kc, uint16_t* vc, uint16_t* kvn,
-                                                  const int* posv, const float2* cs, int cap, int hq, int hkv, int kvb) {
+                                                  const int* posv, const float2* cs, int cap, int hq, int hkv, int kvb,
+                                                  KvMap pgm, int* status) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    EpiQKV<false> ep{q, kc, vc, kvn, posv, cs, cap, hq, hkv, m.t.head_dim, m.nb, kvb};
+    EpiQKV<false> ep{q, kc, vc, kvn, posv, cs, cap, hq, hkv, m.t.head_dim, m.nb, kvb, pgm, status};
     mfma_gemm<KIND_QKV, NB, 2, MEPI_FN>(m, lds, ep, nullptr);
 }
 
@@ -726,6 +735,11 @@ int validate_kv(const i4d_config* c, const i4d_kv* kv, int max_pos) {
     if (!kv || !kv->k || !kv->v) return I4D_EINVAL;
     if (kv->capacity <= 0 || kv->capacity % 16 != 0) return I4D_EINVAL;
     if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return I4D_EALIGN;
+    if (kv->pages) {
+        if (kv->page_size <= 0 || kv->page_size % 16 != 0 || kv->capacity % kv->page_size != 0 || kv->n_pages < 1)
+            return I4D_EINVAL;
+        if (!aligned(kv->pages, 4)) return I4D_EALIGN;
+    }
     if (max_pos < 0 || max_pos >= kv->capacity) return I4D_ERANGE;
     return I4D_OK;
 }
@@ -900,6 +914,12 @@ int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const ui
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
+// page map of a cache (pages == nullptr: contiguous)
+KvMap kv_map(const i4d_kv* kv) {
+    if (!kv->pages) return KvMap{nullptr, 0, 0, 0};
+    return KvMap{kv->pages, kv->page_size / 16, kv->n_pages, kv->capacity / kv->page_size};
+}
+
 template <int FMT, int NB>
 int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, const int* pos, int max_pos,
                  float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status, int kvb, hipStream_t s) {
@@ -907,7 +927,7 @@ int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint1
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
     launch_k(k_gemv_qkv<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
-                       kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status, kvb);
+                       kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status, kvb, kv_map(kv));
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -1038,21 +1058,24 @@ AttnArgs attn_args(const i4d_config* c, int B, const float* q, const i4d_kv* kv,
     a.pm = (float*)(R + W.pm); a.pl = (float*)(R + W.pl); a.po = (float*)(R + W.po);
     a.cnt = (int*)(ws + WS_CNT);
     a.o = o;
+    a.pg = kv_map(kv);
+    a.status = (int*)(ws + WS_STATUS);
     return a;
 }
 
-int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
+template <int HD, bool PAGED>
+int launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const int items = a.batch * a.hkv * a.nsplit;
-    if (hd == 128) {
-        const size_t lds = attn_lds_bytes<128, ATTN_NT>();
-        if (set_lds(k_attention<128>, lds) != hipSuccess) return I4D_EHIP;
-        launch_k(k_attention<128>, dim3(items), dim3(ATTN_NT), lds, s, a);
-    } else {
-        const size_t lds = attn_lds_bytes<64, ATTN_NT>();
-        if (set_lds(k_attention<64>, lds) != hipSuccess) return I4D_EHIP;
-        launch_k(k_attention<64>, dim3(items), dim3(ATTN_NT), lds, s, a);
-    }
+    const size_t lds = attn_lds_bytes<HD, ATTN_NT>();
+    if (set_lds(k_attention<HD, PAGED>, lds) != hipSuccess) return I4D_EHIP;
+    launch_k(k_attention<HD, PAGED>, dim3(items), dim3(ATTN_NT), lds, s, a);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+int launch_attention(const AttnArgs& a, int hd, hipStream_t s) {
+    const bool paged = a.pg.pages != nullptr;
+    if (hd == 128) return paged ? launch_attention_t<128, true>(a, s) : launch_attention_t<128, false>(a, s);
+    return paged ? launch_attention_t<64, true>(a, s) : launch_attention_t<64, false>(a, s);
 }
 
 // ---------------------------------------------------------------- batched (MFMA) path
@@ -1198,9 +1221,9 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
     {
         TimeScope ts(I4D_TIME_QKV);
         rc = nb == 16 ? launch_mfma(k_mfma_qkv<16>, MfmaGeo<16, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
-                                    c->n_q_heads, c->n_kv_heads, kvb)
+                                    c->n_q_heads, c->n_kv_heads, kvb, kv_map(kv), status)
                       : launch_mfma(k_mfma_qkv<32>, MfmaGeo<32, 2>::LDS_B, pq, s, mq, q, kv->k, kv->v, kvn, posv, cs, kv->capacity,
-                                    c->n_q_heads, c->n_kv_heads, kvb);
+                                    c->n_q_heads, c->n_kv_heads, kvb, kv_map(kv), status);
     }
     if (rc) return rc;
     {
@@ -1260,7 +1283,7 @@ bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* la
         const i4d_mat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
         for (int i = 0; i < 7; ++i)
             if (m[i]->dtype != I4D_WEIGHT_INT4 || pick_fmt(*m[i]) != FMT_INT4_FAST || m[i]->group != layers[0].wq.group) return false;
-        if (kv[l].capacity != kv[0].capacity) return false;
+        if (kv[l].capacity != kv[0].capacity || kv[l].pages) return false;
     }
     return true;
 }

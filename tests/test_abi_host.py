@@ -229,3 +229,22 @@ def test_sampling_validation(lib):
     assert step(pos=None) == B.I4D_EINVAL
     assert step(temperature=0.0) == B.I4D_EINVAL
     assert step(max_pos=256) == B.I4D_ERANGE
+
+
+def test_paged_kv_validation(lib):
+    """Page-table fields are checked on the host before anything is enqueued."""
+    cfg = _cfg()
+    layer = _layer(cfg)
+
+    def call(pages=0x300000, page_size=32, n_pages=8, cap=256):
+        kv = B.I4dKv(0x500000, 0x600000, cap, pages, page_size, n_pages)
+        return lib.i4d_decode_layer(ctypes.byref(cfg), ctypes.byref(layer), 1, ctypes.c_void_p(0x100000),
+                                    ctypes.c_void_p(0x200000), ctypes.byref(kv), ctypes.c_void_p(0x700000), 127,
+                                    ctypes.c_void_p(0x400000), 16, None)
+
+    assert call(page_size=24) == B.I4D_EINVAL          # not a multiple of 16
+    assert call(page_size=0) == B.I4D_EINVAL
+    assert call(page_size=96) == B.I4D_EINVAL          # capacity 256 is not a multiple of 96
+    assert call(n_pages=0) == B.I4D_EINVAL
+    assert call(pages=0x300002) == B.I4D_EALIGN
+    assert call() == B.I4D_EWORKSPACE                  # a valid table: the next check (a 16-byte workspace) fails

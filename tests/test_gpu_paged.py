@@ -1,0 +1,166 @@
+"""Paged KV caches (the i4d_kv page table) through the C ABI.
+
+Each sequence's positions live in pages of a shared pool, in a shuffled order
+with unused pages poisoned by NaN.  The layer, the stack and a prompt chunk
+must give bit-identical outputs to the same call on contiguous caches (the
+arithmetic is the same, only the addresses differ).  They must also match the
+oracle to the usual bar, the appended slot must land in its mapped page, and
+every other byte of the pool must stay unchanged.  A page id outside the pool
+is never dereferenced: attention reads page 0, the append is dropped, and the
+status word gets I4D_DEV_BAD_PAGE.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from int4_weight_streaming_decode_amd import binding as B
+from tests.gpu_util import (DevKV, DevLayer, assert_close, config_of, dev, host_u16, k_from_tiles, k_to_tiles,
+                            v_from_tiles, v_to_tiles, workspace)
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.SHAPES["tiny"].with_(name="paged", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128, d_ff=1024,
+                                   group=128, rope_base=1e6)
+SHAPE64 = synth.SHAPES["tiny"].with_(name="paged_hd64", d_model=768, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                     d_ff=1536, group=128, rope_base=1e4)
+NAN16 = np.uint16(0x7FC0)
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+class DevPagedKV:
+    """Contiguous caches [B][Hkv][cap][hd] scattered into a pool of pages of P
+    positions (page order shuffled, `extra` unused pages poisoned)."""
+
+    def __init__(self, kc, vc, P, seed, extra=3):
+        b, h, cap, hd = kc.shape
+        self.P, self.pps, self.shape = P, cap // P, kc.shape
+        self.n_pages = b * self.pps + extra
+        rng = np.random.default_rng(seed)
+        self.table = rng.permutation(self.n_pages)[: b * self.pps].reshape(b, self.pps).astype(np.int32)
+        kp = np.full((self.n_pages, h, P, hd), NAN16, dtype=np.uint16)
+        vp = np.full((self.n_pages, h, P, hd), NAN16, dtype=np.uint16)
+        for s in range(b):
+            for i in range(self.pps):
+                kp[self.table[s, i]] = kc[s, :, i * P:(i + 1) * P]
+                vp[self.table[s, i]] = vc[s, :, i * P:(i + 1) * P]
+        self.k = dev(k_to_tiles(kp))
+        self.v = dev(v_to_tiles(vp))
+        self.pages = dev(self.table)
+        self.kv = B.make_kv(self.k, self.v, cap, self.pages, P, self.n_pages)
+
+    def pools(self):
+        b, h, cap, hd = self.shape
+        ps = (self.n_pages, h, self.P, hd)
+        return k_from_tiles(host_u16(self.k), ps), v_from_tiles(host_u16(self.v), ps)
+
+    def gather(self):
+        """The pool read back as contiguous [B][Hkv][cap][hd] caches."""
+        kp, vp = self.pools()
+        kc = np.concatenate([kp[self.table[:, i]] for i in range(self.pps)], axis=2)
+        vc = np.concatenate([vp[self.table[:, i]] for i in range(self.pps)], axis=2)
+        return kc, vc
+
+
+@pytest.mark.parametrize("shape,batch,P", [(SHAPE, 3, 32), (SHAPE, 16, 64), (SHAPE64, 5, 16), (SHAPE64, 20, 32)])
+def test_paged_layer_equals_contiguous_and_oracle(shape, batch, P):
+    rng = np.random.default_rng(batch * 7 + P)
+    cap = 320
+    pos = [int(p) for p in rng.integers(0, cap - 1, size=batch)]
+    pos[0] = cap - 1
+    _print_case("paged decode_layer", shape.name, batch, P, pos[:4])
+    layer = synth.make_layer(shape, 50 + batch, 0)
+    kc, vc = synth.make_kv(shape, 50 + batch, 0, batch, pos, cap)
+    x = synth.make_x(shape, 50 + batch, batch)
+    L = DevLayer(layer)
+    cfg = config_of(shape)
+    outs = []
+    for paged in (False, True):
+        kvd = DevPagedKV(kc, vc, P, seed=batch) if paged else DevKV(kc, vc)
+        before = kvd.pools() if paged else None
+        ws = workspace(cfg, batch, max(pos))
+        out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+        B.decode_layer(cfg, L.layer, batch, dev(x), out, kvd.kv, dev(np.array(pos, dtype=np.int32)), max(pos), ws)
+        torch.cuda.synchronize()
+        assert B.read_device_status(ws) == 0
+        outs.append((out.cpu().numpy(), kvd.gather() if paged else kvd.host()))
+        if paged:
+            after = kvd.pools()
+            changed = np.zeros(after[0].shape[:1] + after[0].shape[2:3], dtype=bool)     # [page][slot]
+            for b, p in enumerate(pos):
+                changed[kvd.table[b, p // P], p % P] = True
+            for name, a0, a1 in (("K", before[0], after[0]), ("V", before[1], after[1])):
+                diff_slots = np.any(a0 != a1, axis=(1, 3))                           # [page][slot], raw bits
+                assert not np.any(diff_slots & ~changed), f"{name}: pool bytes outside the appended slots changed"
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32)), "paged output differs from contiguous"
+    for c in range(2):
+        assert np.array_equal(outs[0][1][c], outs[1][1][c]), "paged cache differs from contiguous"
+    ref = oracle.decode_layer(shape, layer, x.astype(np.float64), kc, vc, pos)
+    assert_close(outs[1][0], ref["z"], what="paged layer")
+
+
+def test_paged_stack_and_prefill_equal_contiguous():
+    shape, batch, P, cap, n_layers = SHAPE, 4, 48, 240, 2
+    pos = [100, 7, 239, 64]
+    _print_case("paged stack + prefill", batch, P)
+    layers = [synth.make_layer(shape, 70, l) for l in range(n_layers)]
+    caches = [synth.make_kv(shape, 70, l, batch, pos, cap) for l in range(n_layers)]
+    x = synth.make_x(shape, 70, batch)
+    Ls = [DevLayer(l) for l in layers]
+    cfg = config_of(shape)
+    res = []
+    for paged in (False, True):
+        kvs = [DevPagedKV(*c, P, seed=l) if paged else DevKV(*c) for l, c in enumerate(caches)]
+        ws = workspace(cfg, 5, max(pos), n_layers=n_layers)             # 5: the prompt chunk's width
+        out = torch.empty((batch, shape.d_model), dtype=torch.float32, device="cuda")
+        B.decode_stack(cfg, [l.layer for l in Ls], batch, dev(x), out, [k.kv for k in kvs], dev(np.array(pos, dtype=np.int32)),
+                       max(pos), ws)
+        # a prompt chunk of 5 tokens for sequence 1 (positions 8..12) on the updated caches
+        xp = synth.make_x(shape, 71, 5)
+        outp = torch.empty((5, shape.d_model), dtype=torch.float32, device="cuda")
+        if paged:
+            one = [B.make_kv(k.k, k.v, cap, k.pages[1:2], P, k.n_pages) for k in kvs]     # sequence 1's table row
+        else:
+            one = [B.make_kv(k.k[1:2], k.v[1:2], cap) for k in kvs]
+        B.prefill_chunk(cfg, [l.layer for l in Ls], 5, dev(xp), outp, one, dev(np.arange(8, 13, dtype=np.int32)), 12, ws)
+        torch.cuda.synchronize()
+        assert B.read_device_status(ws) == 0
+        res.append((out.cpu().numpy(), outp.cpu().numpy(), [k.gather() if paged else k.host() for k in kvs]))
+    for i in range(2):
+        assert np.array_equal(res[0][i].view(np.uint32), res[1][i].view(np.uint32)), f"output {i} differs"
+    for l in range(n_layers):
+        for c in range(2):
+            assert np.array_equal(res[0][2][l][c], res[1][2][l][c]), f"layer {l} cache {c} differs"
+    ref = oracle.decode_stack(shape, layers, x.astype(np.float64), caches, pos)
+    assert_close(res[1][0], ref["z"], what="paged stack")
+
+
+def test_page_id_outside_the_pool_is_not_dereferenced():
+    """One table entry points past the pool: the kernels read page 0 instead
+    and drop that append; the status word reports it."""
+    shape, batch, P, cap = SHAPE, 2, 32, 128
+    pos = [100, 50]
+    _print_case("paged bad page id", batch, P)
+    layer = synth.make_layer(shape, 90, 0)
+    kc, vc = synth.make_kv(shape, 90, 0, batch, pos, cap)
+    kvd = DevPagedKV(kc, vc, P, seed=9)
+    table = kvd.table.copy()
+    table[0, 100 // P] = kvd.n_pages + 1000          # the page holding sequence 0's new slot
+    kvd.pages.copy_(torch.from_numpy(table).cuda())
+    before = kvd.pools()
+    ws = workspace(config_of(shape), batch, max(pos))
+    out = torch.empty((batch, shape.d_model), dtype=torch.float32, device="cuda")
+    B.decode_layer(config_of(shape), DevLayer(layer).layer, batch, dev(synth.make_x(shape, 90, batch)), out, kvd.kv,
+                   dev(np.array(pos, dtype=np.int32)), max(pos), ws)
+    torch.cuda.synchronize()
+    assert B.read_device_status(ws) & B.I4D_DEV_BAD_PAGE
+    after = kvd.pools()
+    # only sequence 1's appended slot changed anywhere in the pool
+    for a0, a1 in ((before[0], after[0]), (before[1], after[1])):
+        diff = np.argwhere(np.any(a0 != a1, axis=(1, 3)))
+        assert [tuple(d) for d in diff] == [(kvd.table[1, 50 // P], 50 % P)]

@@ -137,7 +137,7 @@ struct AttnRegs {
 // PAGED: the cache is a page pool (a.pg), compiled separately so that the
 // contiguous kernel keeps its plain address arithmetic.
 template <int HD, bool PAGED>
-I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool live, u32x4 (&kr)[HD / 32],
+I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool live, size_t poff, u32x4 (&kr)[HD / 32],
                               u32x2 (&vr)[HD / 16]) {
     constexpr int NKB = HD / 16;
     const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
@@ -147,11 +147,9 @@ I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool 
     const uint16_t* vbase;
     size_t tile;
     if constexpr (PAGED) {
-        bool bad = false;
-        const size_t t0 = kv_tile_off(a.pg, a.cap, a.hkv, HD, g.b * a.kvb, g.j, live ? (g.t_s >> 4) + st : 0, bad);
-        if (bad && lane == 0 && a.status) raise_status(a.status, I4D_DEV_BAD_PAGE);
-        kbase = a.kc + t0;
-        vbase = a.vc + t0;
+        // poff: the tile's offset in the pool, looked up ahead (attn_page_offsets)
+        kbase = a.kc + poff;
+        vbase = a.vc + poff;
         tile = 0;
     } else {
         kbase = a.kc + (size_t)(g.b * a.kvb * a.hkv + g.j) * a.cap * HD;
@@ -169,15 +167,32 @@ I4D_DEVINL void attn_load_sub(const AttnArgs& a, const AttnGeo& g, int st, bool 
     for (int nt = 0; nt < NKB; ++nt) vr[nt] = nt_load_v((const u32x2*)(vp + (live ? 256 * nt : 0)));
 }
 
-// Issue the loads of round r of this wave.
-template <int HD, int NT, int NSW, bool PAGED = false>
-I4D_DEVINL void attn_load_round(const AttnArgs& a, const AttnGeo& g, int rnd, AttnRegs<HD, NSW>& R) {
+// Paged caches: the pool offsets of this wave's subtiles of round rnd (tile 0
+// of the row for slots past the item).  Issued a round ahead, so the page-table
+// reads overlap the previous round instead of preceding every K/V load.
+template <int HD, int NT, int NSW>
+I4D_DEVINL void attn_page_offsets(const AttnArgs& a, const AttnGeo& g, int rnd, size_t (&off)[NSW]) {
     constexpr int NW = NT / 64;
     const int wave = i4d_tid() >> 6;
 #pragma unroll
     for (int i = 0; i < NSW; ++i) {
         const int st = (rnd * NSW + i) * NW + wave;
-        attn_load_sub<HD, PAGED>(a, g, st, st < g.nsub, R.k[i], R.v[i]);
+        bool bad = false;
+        off[i] = kv_tile_off(a.pg, a.cap, a.hkv, HD, g.b * a.kvb, g.j, st < g.nsub ? (g.t_s >> 4) + st : 0, bad);
+        if (bad && (i4d_tid() & 63) == 0 && a.status) raise_status(a.status, I4D_DEV_BAD_PAGE);
+    }
+}
+
+// Issue the loads of round r of this wave (off: the paged offsets of the round).
+template <int HD, int NT, int NSW, bool PAGED = false>
+I4D_DEVINL void attn_load_round(const AttnArgs& a, const AttnGeo& g, int rnd, AttnRegs<HD, NSW>& R,
+                                const size_t* off = nullptr) {
+    constexpr int NW = NT / 64;
+    const int wave = i4d_tid() >> 6;
+#pragma unroll
+    for (int i = 0; i < NSW; ++i) {
+        const int st = (rnd * NSW + i) * NW + wave;
+        attn_load_sub<HD, PAGED>(a, g, st, st < g.nsub, PAGED ? off[i] : 0, R.k[i], R.v[i]);
     }
 }
 
@@ -233,7 +248,13 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) qv[kb] = ld_g((const f4*)(qrow + 32 * (kb >> 1) + 4 * (kb & 1)));
     }
-    if (!pre) attn_load_round<HD, NT, NSW, PAGED>(a, g, 0, R);
+    const int nround = (nsub + NW * NSW - 1) / (NW * NSW);
+    size_t poff[NSW];                                   // paged: pool offsets of the next round's subtiles
+    if constexpr (PAGED) attn_page_offsets<HD, NT, NSW>(a, g, 0, poff);
+    if (!pre) attn_load_round<HD, NT, NSW, PAGED>(a, g, 0, R, poff);
+    if constexpr (PAGED) {
+        if (nround > 1) attn_page_offsets<HD, NT, NSW>(a, g, 1, poff);
+    }
     s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
     if (wave == 0) {
         const float qs = (r < G) ? a.qscale : 0.f;
@@ -312,9 +333,13 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
     };
 
     // rounds of NSW subtiles per wave: round 0 is in R already
-    const int nround = (nsub + NW * NSW - 1) / (NW * NSW);
     for (int rnd = 0; rnd < nround; ++rnd) {
-        if (rnd > 0) attn_load_round<HD, NT, NSW, PAGED>(a, g, rnd, R);
+        if (rnd > 0) {
+            attn_load_round<HD, NT, NSW, PAGED>(a, g, rnd, R, poff);
+            if constexpr (PAGED) {
+                if (rnd + 1 < nround) attn_page_offsets<HD, NT, NSW>(a, g, rnd + 1, poff);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
             const int st = (rnd * NSW + i) * NW + wave;

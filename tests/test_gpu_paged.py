@@ -164,3 +164,32 @@ def test_page_id_outside_the_pool_is_not_dereferenced():
     for a0, a1 in ((before[0], after[0]), (before[1], after[1])):
         diff = np.argwhere(np.any(a0 != a1, axis=(1, 3)))
         assert [tuple(d) for d in diff] == [(kvd.table[1, 50 // P], 50 % P)]
+
+
+@pytest.mark.parametrize("name,pos,P", [("27b", [20000], 256), ("tiny", [16000, 13000, 9000, 15000], 64)])
+def test_paged_attention_over_several_rounds(name, pos, P):
+    """Splits long enough that each wave loads its subtiles in more than one
+    round, so the page ids of every later round come from the read issued a
+    round ahead.  Bit-identical to the contiguous cache and within the bar of
+    the oracle."""
+    from tests.test_gpu_parity import _attn_case
+    shape = synth.SHAPES[name]
+    batch = len(pos)
+    _print_case("paged attention, several rounds", name, pos, P)
+    q, kc, vc = _attn_case(shape, batch, pos, seed=sum(pos))
+    pad = -kc.shape[2] % P                            # capacity to a whole number of pages (poisoned slots)
+    kc = np.pad(kc, ((0, 0), (0, 0), (0, pad), (0, 0)), constant_values=NAN16)
+    vc = np.pad(vc, ((0, 0), (0, 0), (0, pad), (0, 0)), constant_values=NAN16)
+    cfg = config_of(shape)
+    ws = workspace(cfg, batch, max(pos))
+    outs = []
+    for kvd in (DevKV(kc, vc), DevPagedKV(kc, vc, P, seed=3)):
+        o = torch.full((batch, shape.n_q_heads, shape.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        B.attention(cfg, batch, dev(q), kvd.kv, dev(np.array(pos, dtype=np.int32)), max(pos), o, ws)
+        torch.cuda.synchronize()
+        assert B.read_device_status(ws) == 0
+        outs.append(o.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "paged attention differs from contiguous"
+    ref = oracle.gqa_decode_attention(q.astype(np.float64), kc, vc, pos)
+    for b in range(batch):
+        assert_close(outs[1][b], ref[b], what=f"paged attention b={b}")

@@ -147,3 +147,51 @@ def test_sampled_decode_steps_match_the_oracle_loop(batch):
         _check_draw(got[s][0], got[s][1], ref["tokens"][s], scores, tols, f"step {s}")
         if tie:
             pytest.skip(f"step {s}: near-tie, later steps are not comparable")
+
+
+def test_sampled_decode_step_replays_from_a_graph():
+    """One sampled step captured in a graph and replayed: the counter word is
+    the device-side position, so each replay draws new noise.  Every replay
+    equals the same step run eagerly on a copy of the state."""
+    batch, n_layers, pos0, steps, T = 2, 2, 100, 3, 1.1
+    cap = 128
+    _print_case("decode_step_sample graph", batch, steps, T)
+    layers = [synth.make_layer(SHAPE, 93, l) for l in range(n_layers)]
+    caches = [synth.make_kv(SHAPE, 93, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    table = synth.make_embedding(VOCAB, SHAPE.d_model, 93)
+    lm = synth.make_lm_head(VOCAB, SHAPE.d_model, SHAPE.group, 94)
+    tok0 = np.array([5, 2500], dtype=np.int32)
+    Ls = [DevLayer(l) for l in layers]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+    larr = [l.layer for l in Ls]
+
+    def state():
+        return ([DevKV(*c) for c in caches], dev(tok0), dev(np.full(batch, pos0, dtype=np.int32)),
+                torch.empty(batch, dtype=torch.float32, device="cuda"),
+                torch.empty((2, batch, SHAPE.d_model), dtype=torch.float32, device="cuda"),
+                workspace(cfg, batch, cap - 1, vocab=VOCAB, n_layers=n_layers))
+
+    kvs, tokens, pos, sc, xbuf, ws = state()
+    eager = []
+    for s in range(steps):
+        B.decode_step_sample(cfg, larr, emb, W.mat, batch, tokens, sc, pos, cap - 1, xbuf, [k.kv for k in kvs], T, SEED, ws)
+        torch.cuda.synchronize()
+        eager.append((tokens.cpu().numpy().copy(), sc.cpu().numpy().copy()))
+    kvs2, tokens2, pos2, sc2, xbuf2, ws2 = state()
+    karr = [k.kv for k in kvs2]
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        B.decode_step_sample(cfg, larr, emb, W.mat, batch, tokens2, sc2, pos2, cap - 1, xbuf2, karr, T, SEED, ws2)
+    torch.cuda.current_stream().wait_stream(gs)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1024, device="cuda") * 2).sum().item()      # eager work between replays
+        assert np.array_equal(tokens2.cpu().numpy(), eager[s][0]), f"replay {s}"
+        assert np.array_equal(sc2.cpu().numpy(), eager[s][1]), f"replay {s} score"
+    assert B.read_device_status(ws2) == 0
+    assert pos2.cpu().numpy().tolist() == [pos0 + steps] * batch

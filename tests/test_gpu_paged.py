@@ -193,3 +193,35 @@ def test_paged_attention_over_several_rounds(name, pos, P):
     ref = oracle.gqa_decode_attention(q.astype(np.float64), kc, vc, pos)
     for b in range(batch):
         assert_close(outs[1][b], ref[b], what=f"paged attention b={b}")
+
+
+@pytest.mark.parametrize("n_tokens", [24, 32])
+def test_paged_prefill_on_the_matrix_cores_equals_contiguous(n_tokens):
+    """A prompt chunk of 24 or 32 tokens (matrix-core path, every entry sharing
+    one cache) written through a page table: bit-identical to the contiguous
+    cache, and equal to the oracle decoding the tokens one after another."""
+    shape, P, cap, start = SHAPE, 32, 128, 40
+    _print_case("paged prefill", n_tokens, P)
+    layers = [synth.make_layer(shape, 110, 0)]
+    kc, vc = synth.make_kv(shape, 110, 0, 1, [start], cap)
+    x = synth.make_x(shape, 111, n_tokens)
+    pos = np.arange(start, start + n_tokens, dtype=np.int32)
+    L = DevLayer(layers[0])
+    cfg = config_of(shape)
+    res = []
+    for paged in (False, True):
+        kvd = DevPagedKV(kc, vc, P, seed=n_tokens) if paged else DevKV(kc, vc)
+        ws = workspace(cfg, n_tokens, cap - 1)
+        out = torch.empty((n_tokens, shape.d_model), dtype=torch.float32, device="cuda")
+        B.prefill_chunk(cfg, [L.layer], n_tokens, dev(x), out, [kvd.kv], dev(pos), int(pos[-1]), ws)
+        torch.cuda.synchronize()
+        assert B.read_device_status(ws) == 0
+        res.append((out.cpu().numpy(), kvd.gather() if paged else kvd.host()))
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32)), "paged prefill output differs"
+    for c in range(2):
+        assert np.array_equal(res[0][1][c], res[1][1][c]), "paged prefill cache differs"
+    caches = [(kc, vc)]
+    for t in range(n_tokens):
+        r = oracle.decode_stack(shape, layers, x[t:t + 1].astype(np.float64), caches, [int(pos[t])])
+        caches = r["caches"]
+        assert_close(res[1][0][t], r["z"][0], what=f"paged prefill token {t}")

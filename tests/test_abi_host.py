@@ -248,3 +248,19 @@ def test_paged_kv_validation(lib):
     assert call(n_pages=0) == B.I4D_EINVAL
     assert call(pages=0x300002) == B.I4D_EALIGN
     assert call() == B.I4D_EWORKSPACE                  # a valid table: the next check (a 16-byte workspace) fails
+
+
+def test_prefill_chunk_validation(lib):
+    """Chunk width 1..32; the persistent mode does not take prompt chunks.
+    Every call fails validation before anything is enqueued."""
+    P = ctypes.c_void_p
+
+    def call(cfg, n_tokens=8):
+        layer = _layer(cfg)
+        kv = B.I4dKv(0x500000, 0x600000, 256)
+        return lib.i4d_prefill_chunk(ctypes.byref(cfg), 1, ctypes.byref(layer), n_tokens, P(0x100000), P(0x200000),
+                                     ctypes.byref(kv), P(0x700000), 127, P(0x400000), 1 << 30, None)
+
+    assert call(_cfg(), n_tokens=0) == B.I4D_ERANGE
+    assert call(_cfg(), n_tokens=33) == B.I4D_ERANGE
+    assert call(_cfg(exec_mode=2)) == B.I4D_EUNSUPPORTED

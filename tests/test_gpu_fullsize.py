@@ -1,13 +1,23 @@
 """Parity at the full sizes of the timed workloads, through the C ABI.
 
 Inputs come from the seeded device generator (the bench's own), are copied
-to the host, and the CPU oracle recomputes the same step: one 27B-shaped
-layer at 8192 cached tokens (batch 1 on the matrix-vector path, batch 16 on
-the matrix-core path) and the 152064 x 5120 int4 LM head (batch 1 and 16).
+to the host, and the CPU oracle recomputes the same step:
+  * one 27B-shaped layer at 8192 cached tokens: int4 at batch 1 (matrix-vector
+    path) and batch 16 (matrix-core path), bf16 weights at batch 1;
+  * one 70B-shaped layer (D 8192, d_ff 28672, 32768 cached tokens, RoPE base
+    5e5) at batch 1 and at batch 32 (matrix-core path, 32 positions);
+  * two chained 27B-shaped int4 layers over two decode steps (the second step
+    reads the K/V the first one appended);
+  * the 152064 x 5120 int4 LM head (batch 1 and 16).
+Batches are independent sequences, so at batch 32 the oracle recomputes a
+sample of the sequences (first, middle, last) while the GPU runs all of them.
 Same bars as the other parity tests: float outputs relative L2 <= 1e-3 and
-max |err| <= 5e-3 * RMS; the appended K/V slot within one bf16 rounding step;
-token ids exact unless the oracle's top-2 gap is a near-tie.
+max |err| <= 5e-3 * RMS; the appended K/V slot within one bf16 rounding step
+and every other slot bit-identical; token ids exact unless the oracle's top-2
+gap is a near-tie.  Each case prints the oracle's seconds.
 """
+
+import time
 
 import numpy as np
 import pytest
@@ -29,54 +39,142 @@ def _print_case(*a):
 
 
 def _host_mat(m):
-    return {"codes": m["codes"].cpu().numpy(), "scales": m["scales"].cpu().numpy().view(np.uint16),
-            "n": m["n"], "k": m["k"], "group": m["group"]}
+    if "codes" in m:
+        return {"codes": m["codes"].cpu().numpy(), "scales": m["scales"].cpu().numpy().view(np.uint16),
+                "n": m["n"], "k": m["k"], "group": m["group"]}
+    return {"bf16": m["bf16"].cpu().numpy().view(np.uint16), "n": m["n"], "k": m["k"]}
 
 
 def _bits(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("batch", [1, 16])
-def test_27b_layer_at_full_size(batch):
-    shape = synth.SHAPES["27b"]
-    pos0 = shape.kv_len                                   # 8192 cached tokens
-    pos = [pos0 - 37 * b for b in range(batch)]           # batch 16: sequences at different positions
-    cap = ((pos0 + 1 + 15) // 16) * 16
-    _print_case("27b layer full size", batch, pos[:3])
-    p = G.make_layer_gpu(shape, 5, 0)
-    k, v = G.make_kv_gpu(shape, 5, 0, batch, cap)
-    x = G.make_x_gpu(shape, 6, batch)
-    mats = {n: B.make_mat(p[n]["codes"], p[n]["scales"], p[n]["n"], p[n]["k"], p[n]["group"], B.WEIGHT_INT4) for n in MATS}
-    layer = B.make_layer(p["attn_norm"], p["ffn_norm"], mats)
-    kv = B.make_kv(k, v, cap)
-    # the oracle's copies, taken before the call appends slot pos[b]
-    kshape = (batch, shape.n_kv_heads, cap, shape.head_dim)
-    kc = k_from_tiles(_bits(k), kshape)
-    vc = v_from_tiles(_bits(v), kshape)
-    host_layer = {"attn_norm": _bits(p["attn_norm"]), "ffn_norm": _bits(p["ffn_norm"])}
-    host_layer.update({n: _host_mat(p[n]) for n in MATS})
-    cfg = config_of(shape)
-    ws = workspace(cfg, batch, pos0)
-    out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
-    B.decode_layer(cfg, layer, batch, x, out, kv, torch.tensor(pos, dtype=torch.int32, device="cuda"), pos0, ws)
-    torch.cuda.synchronize()
-    assert B.read_device_status(ws) == 0
-    ref = oracle.decode_layer(shape, host_layer, x.cpu().numpy().astype(np.float64), kc, vc, pos)
-    got = out.cpu().numpy()
-    for b in range(batch):
-        assert_close(got[b], ref["z"][b], what=f"27b layer b={b}")
-    kg = k_from_tiles(_bits(k), kshape)
-    vg = v_from_tiles(_bits(v), kshape)
+class _FullLayer:
+    """One layer's device tensors (seeded device generator), its ABI structs and
+    the host copies the oracle reads."""
+
+    def __init__(self, shape, seed, layer, wdtype, batch, cap):
+        self.p = G.make_layer_gpu(shape, seed, layer, wdtype)
+        mats = {}
+        for n in MATS:
+            m = self.p[n]
+            if wdtype == "int4":
+                mats[n] = B.make_mat(m["codes"], m["scales"], m["n"], m["k"], m["group"], B.WEIGHT_INT4)
+            else:
+                mats[n] = B.make_mat(m["bf16"], None, m["n"], m["k"], 0, B.WEIGHT_BF16)
+        self.layer = B.make_layer(self.p["attn_norm"], self.p["ffn_norm"], mats)
+        self.k, self.v = G.make_kv_gpu(shape, seed, layer, batch, cap)
+        self.kv = B.make_kv(self.k, self.v, cap)
+        self.kshape = (batch, shape.n_kv_heads, cap, shape.head_dim)
+        self.host = {"attn_norm": _bits(self.p["attn_norm"]), "ffn_norm": _bits(self.p["ffn_norm"])}
+        self.host.update({n: _host_mat(self.p[n]) for n in MATS})
+
+    def caches(self, sel=None):
+        kc = k_from_tiles(_bits(self.k), self.kshape)
+        vc = v_from_tiles(_bits(self.v), self.kshape)
+        if sel is not None:
+            kc, vc = kc[sel], vc[sel]
+        return kc, vc
+
+
+def _check_slots(kg, vg, kref, vref, k0, v0, pos, what, untouched=None):
+    """Appended slot within one bf16 rounding step (or the float bar); an
+    untouched slot (default: the one before the appended slot) bit-identical to
+    the cache before the call."""
     for b, pb in enumerate(pos):
-        for name, g_, r_ in (("K", kg, ref["k_cache"]), ("V", vg, ref["v_cache"])):
+        for name, g_, r_ in (("K", kg, kref), ("V", vg, vref)):
             gv = synth.bf16_value(g_[b, :, pb]).astype(np.float64)
             rv = synth.bf16_value(r_[b, :, pb]).astype(np.float64)
             ulp = np.ldexp(1.0, np.frexp(np.abs(rv))[1] - 8)
             rms = np.sqrt(np.mean(rv * rv))
-            assert np.all(np.abs(gv - rv) <= np.maximum(5e-3 * rms, ulp)), f"{name} slot {pb} of b={b}"
-        # one untouched slot per sequence, bit-identical
-        assert np.array_equal(kg[b, :, pb - 1], kc[b, :, pb - 1]) and np.array_equal(vg[b, :, pb - 1], vc[b, :, pb - 1])
+            assert np.all(np.abs(gv - rv) <= np.maximum(5e-3 * rms, ulp)), f"{what}: {name} slot {pb} of b={b}"
+        u = pb - 1 if untouched is None else untouched
+        assert np.array_equal(kg[b, :, u], k0[b, :, u]) and np.array_equal(vg[b, :, u], v0[b, :, u]), f"{what}: slot {u}"
+
+
+def _full_layer_case(shape, wdtype, batch, pos, sample=None):
+    pos0 = max(pos)
+    cap = ((pos0 + 1 + 15) // 16) * 16
+    sel = list(range(batch)) if sample is None else sample
+    _print_case(f"{shape.name} {wdtype} layer full size", "batch", batch, "pos", pos[:3], "oracle rows", sel)
+    L = _FullLayer(shape, 5, 0, wdtype, batch, cap)
+    x = G.make_x_gpu(shape, 6, batch)
+    kc, vc = L.caches(sel)                        # the oracle's copies, before slot pos[b] is appended
+    cfg = config_of(shape)
+    ws = workspace(cfg, batch, pos0)
+    out = torch.full((batch, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+    B.decode_layer(cfg, L.layer, batch, x, out, L.kv, torch.tensor(pos, dtype=torch.int32, device="cuda"), pos0, ws)
+    torch.cuda.synchronize()
+    assert B.read_device_status(ws) == 0
+    psel = [pos[b] for b in sel]
+    t0 = time.perf_counter()
+    ref = oracle.decode_layer(shape, L.host, x.cpu().numpy()[sel].astype(np.float64), kc, vc, psel)
+    print(f"oracle: {time.perf_counter() - t0:.1f} s for {len(sel)} sequence(s)", flush=True)
+    got = out.cpu().numpy()[sel]
+    for i, b in enumerate(sel):
+        assert_close(got[i], ref["z"][i], what=f"{shape.name} {wdtype} layer b={b}")
+    kg, vg = L.caches(sel)
+    _check_slots(kg, vg, ref["k_cache"], ref["v_cache"], kc, vc, psel, f"{shape.name} {wdtype}")
+
+
+@pytest.mark.parametrize("batch", [1, 16])
+def test_27b_layer_at_full_size(batch):
+    shape = synth.SHAPES["27b"]
+    _full_layer_case(shape, "int4", batch, [shape.kv_len - 37 * b for b in range(batch)])
+
+
+def test_27b_bf16_layer_at_full_size():
+    shape = synth.SHAPES["27b"]
+    _full_layer_case(shape, "bf16", 1, [shape.kv_len])
+
+
+def test_70b_layer_at_full_size_batch1():
+    shape = synth.SHAPES["70b"]
+    _full_layer_case(shape, "int4", 1, [shape.kv_len])
+
+
+def test_70b_layer_at_full_size_batch32():
+    shape = synth.SHAPES["70b"]
+    # 32 sequences at staggered positions up to 32768 cached tokens (matrix-core path)
+    _full_layer_case(shape, "int4", 32, [shape.kv_len - 211 * b for b in range(32)], sample=[0, 13, 31])
+
+
+def test_27b_two_layers_two_steps():
+    """Two chained full-size layers, two decode steps: step 2 attends over the
+    K/V that step 1 appended in both layers."""
+    shape = synth.SHAPES["27b"]
+    pos0 = shape.kv_len
+    cap = ((pos0 + 2 + 15) // 16) * 16
+    _print_case("27b two layers two steps", pos0)
+    Ls = [_FullLayer(shape, 9, l, "int4", 1, cap) for l in range(2)]
+    caches = [L.caches() for L in Ls]
+    xs = [G.make_x_gpu(shape, 20 + s, 1) for s in range(2)]
+    cfg = config_of(shape)
+    ws = workspace(cfg, 1, pos0 + 1, n_layers=2)
+    larr = [L.layer for L in Ls]
+    karr = [L.kv for L in Ls]
+    outs = []
+    for s in range(2):
+        out = torch.full((1, shape.d_model), float("nan"), dtype=torch.float32, device="cuda")
+        B.decode_stack(cfg, larr, 1, xs[s], out, karr, torch.tensor([pos0 + s], dtype=torch.int32, device="cuda"),
+                       pos0 + s, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert B.read_device_status(ws) == 0
+    t0 = time.perf_counter()
+    ref_caches = caches
+    for s in range(2):
+        r = oracle.decode_stack(shape, [L.host for L in Ls], xs[s].cpu().numpy().astype(np.float64), ref_caches,
+                                [pos0 + s])
+        assert_close(outs[s].cpu().numpy()[0], r["z"][0], what=f"27b 2-layer stack step {s}")
+        ref_caches = r["caches"]
+    print(f"oracle: {time.perf_counter() - t0:.1f} s", flush=True)
+    for l, L in enumerate(Ls):
+        kg, vg = L.caches()
+        kref, vref = ref_caches[l]
+        k0, v0 = caches[l]
+        for s in range(2):
+            _check_slots(kg, vg, kref, vref, k0, v0, [pos0 + s], f"27b stack layer {l} step {s}", untouched=pos0 - 1)
 
 
 @pytest.mark.parametrize("batch", [1, 16])

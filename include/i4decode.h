@@ -67,9 +67,10 @@ extern "C" {
 
 /* device status word bits (i4d_read_device_status) */
 #define I4D_DEV_BAD_POS       1   /* pos[b] < 0, > max_pos or >= capacity: that sequence was skipped */
-#define I4D_DEV_BARRIER_TIMEOUT 2 /* a grid barrier of the persistent kernel gave up waiting */
+#define I4D_DEV_BARRIER_TIMEOUT 2 /* the streaming kernel gave up waiting for another workgroup's values */
 #define I4D_DEV_BAD_TOKEN     4   /* a token id outside the embedding table: that row became zeros */
 #define I4D_DEV_BAD_PAGE      8   /* a KV page id outside the pool: read as page 0, append dropped */
+#define I4D_DEV_NONFINITE    16   /* an activation staged for a weight product was inf or NaN (used as 0) */
 
 /* ---- weight matrices ---- */
 #define I4D_WEIGHT_INT4 0
@@ -103,11 +104,15 @@ typedef struct i4d_layer {
 
 /* Model shape.  head_dim must be 64 or 128; n_q_heads / n_kv_heads <= 16.
  * exec_mode selects how decode_layer/decode_stack run their phases:
- *   0 = auto (currently one launch per phase),
+ *   0 = auto: the streaming kernel (2) when the request qualifies, otherwise
+ *       one launch per phase,
  *   1 = one kernel launch per phase,
- *   2 = one persistent cooperative kernel per call with grid barriers
- *       (int4 weights with one group size, head_dim 128, batch <= 4;
- *       I4D_EUNSUPPORTED otherwise).                                        */
+ *   2 = the streaming kernel: one persistent launch per call runs every
+ *       layer, its workgroups handing values to each other through tagged
+ *       exchange words in the workspace (batch 1, int4 weights with groups of
+ *       128, head_dim 128, d_model, d_ff and n_q_heads*128 multiples of 512,
+ *       d_model and n_q_heads*128 <= 8192, contiguous caches of one capacity, at most 128
+ *       layers; I4D_EUNSUPPORTED otherwise).                                */
 typedef struct i4d_config {
     int32_t d_model, n_q_heads, n_kv_heads, head_dim, d_ff;
     float   rms_eps;
@@ -136,7 +141,7 @@ typedef struct i4d_config {
  * t % page_size.  capacity is the longest sequence the table can map.  Page
  * ids outside 0..n_pages-1 are never dereferenced: attention reads page 0
  * instead, the append is dropped, and I4D_DEV_BAD_PAGE is set in the
- * workspace status word.  The persistent kernel (exec_mode 2) does not take
+ * workspace status word.  The streaming kernel (exec_mode 2) does not take
  * paged caches (I4D_EUNSUPPORTED).                                            */
 typedef struct i4d_kv {
     uint16_t* k;
@@ -306,9 +311,17 @@ int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream);
 #define I4D_TIME_GATE_UP    4   /* k_gemv_swiglu: norm + gate/up projections + SwiGLU */
 #define I4D_TIME_DOWN       5   /* k_gemv_rows on W_down (+ residual) */
 #define I4D_TIME_LM_HEAD    6   /* k_lm_head: one chunk of the LM head's rows */
-#define I4D_TIME_PERSISTENT 7   /* k_decode_persistent: all layers of one call */
+#define I4D_TIME_STREAM     7   /* k_stream_decode: every layer of one call (events around the launch) */
 int i4d_launch_timing_start(int32_t kernel, int32_t max_launches);
 int i4d_launch_timing_stop(float* total_ms, int32_t* launches);
+
+/* Measurement aid (not part of the decode path): read `bytes` of device
+ * memory at buf once with 16-byte nontemporal loads (one 512-thread workgroup
+ * per compute unit, four loads in flight per lane) and XOR every word into
+ * *sink (device uint32, caller-owned).  The achievable streaming-read rate
+ * the decode kernels are measured against.  buf 16-byte aligned, bytes a
+ * multiple of 16 (I4D_EALIGN otherwise), bytes > 0 (I4D_EINVAL).           */
+int i4d_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Static text for a status code. */
 const char* i4d_status_string(int status);

@@ -25,13 +25,14 @@ I4D_DEV_BAD_POS = 1
 I4D_DEV_BARRIER_TIMEOUT = 2
 I4D_DEV_BAD_TOKEN = 4
 I4D_DEV_BAD_PAGE = 8
+I4D_DEV_NONFINITE = 16
 
 WEIGHT_INT4 = 0
 WEIGHT_BF16 = 1
 
 EXEC_AUTO = 0
 EXEC_PHASES = 1
-EXEC_PERSISTENT = 2
+EXEC_STREAM = 2
 
 
 class I4dMat(ctypes.Structure):
@@ -95,12 +96,13 @@ def lib():
         L.i4d_read_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
         L.i4d_launch_timing_start.argtypes = [I, I]
         L.i4d_launch_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
+        L.i4d_read_probe.argtypes = [P, Z, P, P]
         L.i4d_status_string.argtypes = [ctypes.c_int]
         L.i4d_status_string.restype = ctypes.c_char_p
         for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked", "i4d_embed",
                      "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
-                     "i4d_launch_timing_start", "i4d_launch_timing_stop"):
+                     "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -240,7 +242,7 @@ def attention(cfg, batch, q, kv: I4dKv, pos, max_pos, o, ws, stream=None):
 
 
 # kernels that i4d_launch_timing_start can time (values of I4D_TIME_*)
-TIME_KERNELS = {"qkv": 1, "attention": 2, "wo": 3, "gate_up": 4, "down": 5, "lm_head": 6, "persistent": 7}
+TIME_KERNELS = {"qkv": 1, "attention": 2, "wo": 3, "gate_up": 4, "down": 5, "lm_head": 6, "stream": 7}
 
 
 def launch_timing_start(kernel: str, max_launches: int):
@@ -252,6 +254,11 @@ def launch_timing_stop():
     ms, n = ctypes.c_float(0.0), ctypes.c_int32(0)
     _check(lib().i4d_launch_timing_stop(ctypes.byref(ms), ctypes.byref(n)), "i4d_launch_timing_stop")
     return float(ms.value), int(n.value)
+
+
+def read_probe(buf, sink, stream=None):
+    """Measurement aid: read all of `buf` (a device tensor) once into the XOR sink (device int32)."""
+    _check(lib().i4d_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)), "i4d_read_probe")
 
 
 def read_device_status(ws, stream=None) -> int:

@@ -9,12 +9,12 @@
 //
 // Loads.  A wave issues the K/V loads of all its subtiles of a round (up to
 // NSW of them) before computing any, so an item costs about one memory round
-// trip; the persistent kernel issues round 0 before the grid barrier that
-// precedes attention, because the cached history does not depend on the q/k/v
-// phase.  The one key that does -- the new token's, at position pos[b] -- is
-// read from a small side buffer that the q/k/v epilogue writes next to the
-// cache, and patched into the registers after the barrier; cache lines loaded
-// before the barrier may hold the old contents of that slot.
+// trip; the streaming kernel (stream.hip) issues round 0 before it waits for
+// this step's q, k and v, because the cached history does not depend on the
+// q/k/v phase.  The one key that does -- the new token's, at position pos[b] --
+// is read from the exchange vector that the q/k/v epilogue writes, and patched
+// into the registers once it has arrived; cache lines loaded earlier may hold
+// the old contents of that slot.
 //
 // Merge.  Each item leaves a partial (running max m, running sum l,
 // unnormalised O); the last of the nsplit workgroups of (b, j) to finish
@@ -55,7 +55,7 @@ struct KvMap {
 // elements.  bad: set when the page id was out of range (page 0 was used).
 I4D_DEVINL size_t kv_tile_off(const KvMap& m, int cap, int hkv, int hd, int r, int j, int t, bool& bad) {
     if (m.pages == nullptr) return ((size_t)(r * hkv + j) * cap + (size_t)t * 16) * hd;
-    int pg = m.pages[(size_t)r * m.pps + t / m.page_tiles];
+    int pg = ld_g(m.pages + (size_t)r * m.pps + t / m.page_tiles);
     bad = pg < 0 || pg >= m.n_pages;
     if (bad) pg = 0;
     return ((size_t)(pg * hkv + j) * m.page_tiles + t % m.page_tiles) * 16 * hd;
@@ -91,7 +91,7 @@ I4D_DEVINL s4 dwords_to_s4(u32 lo, u32 hi) { return __builtin_bit_cast(s4, u32x2
 
 // Number of keys attended by sequence b (pos + 1), or 0 if pos is invalid.
 I4D_DEVINL int keys_of(const AttnArgs& a, int b) {
-    const int p = a.pos[b];
+    const int p = ld_g(a.pos + b);
     return (p >= 0 && p <= a.max_pos && p < a.cap) ? p + 1 : 0;
 }
 
@@ -223,21 +223,145 @@ I4D_DEVINL void attn_patch_new(const AttnArgs& a, const AttnGeo& g, int st, u32x
     }
 }
 
+// One 16-key subtile st of an item: scores against the q operand (qop, the
+// hi/lo bf16 parts in LDS), online-softmax update of this lane's running max m
+// and sum lsum, and O += P V.  Keys at or past g.t_e are masked.
+template <int HD>
+I4D_DEVINL void attn_sub(const AttnGeo& g, int st, const u32x4 (&kr)[HD / 32], const u32x2 (&vr)[HD / 16], const s4* qop,
+                         float& m, float& lsum, f4 (&O)[HD / 16]) {
+    constexpr int NKB = HD / 16;
+    const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
+    const int t_e = g.t_e;
+    const int t0 = g.t_s + 16 * st;
+    const int tv = t0 + 4 * gq;
+    const bool kvalid = t0 + r < t_e;               // this lane's K row
+    const int vvalid = t_e - tv;                    // keys of this lane's V run in range
+    // scores^T for keys 4gq..4gq+3 of head r
+    f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        u32x4 w = kr[kb >> 1];
+        if (!kvalid) w = u32x4{0, 0, 0, 0};
+        const s4 kop = (kb & 1) ? dwords_to_s4(w.z, w.w) : dwords_to_s4(w.x, w.y);
+        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb) * 64 + lane], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb + 1) * 64 + lane], sc, 0, 0, 0);
+    }
+    float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (tv + i >= t_e) sv[i] = -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mnew = fmaxf(m, mx);                // finite: the subtile has a valid key
+    const float alpha = exp2f(m - mnew);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - mnew);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mnew;
+    // rescale O rows (heads 4gq + i) by their alpha
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ai = shfl_f(alpha, 4 * gq + i);
+#pragma unroll
+        for (int nt = 0; nt < NKB; ++nt) O[nt][i] *= ai;
+    }
+    uint16_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ph[i] = f32_to_bf16(p[i]);
+        pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
+    }
+    const s4 pho = pack_bf16x4(ph[0], ph[1], ph[2], ph[3]);
+    const s4 plo = pack_bf16x4(pl[0], pl[1], pl[2], pl[3]);
+    const u32 vm0 = vvalid >= 2 ? 0xFFFFFFFFu : (vvalid == 1 ? 0x0000FFFFu : 0u);
+    const u32 vm1 = vvalid >= 4 ? 0xFFFFFFFFu : (vvalid == 3 ? 0x0000FFFFu : 0u);
+#pragma unroll
+    for (int nt = 0; nt < NKB; ++nt) {
+        const s4 vop = dwords_to_s4(vr[nt].x & vm0, vr[nt].y & vm1);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pho, vop, O[nt], 0, 0, 0);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop, O[nt], 0, 0, 0);
+    }
+}
+
+// The q^T operand of head r of the item's group (hi and lo bf16 parts, dims in
+// the K-row order of attn_sub), from this lane's 4 x NKB fp32 q values (dims
+// 32(kb/2) + 8gq + 4(kb%2) + i), scaled by qscale (0 for lanes past the group).
+template <int HD>
+I4D_DEVINL void attn_q_operand(const f4 (&qv)[HD / 16], float qs, s4* qop) {
+    constexpr int NKB = HD / 16;
+    const int lane = i4d_tid() & 63;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        uint16_t hv[4], lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = qv[kb][i] * qs;
+            hv[i] = f32_to_bf16(v);
+            lv[i] = f32_to_bf16(v - bf16_to_f32(hv[i]));
+        }
+        qop[(2 * kb) * 64 + lane] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+        qop[(2 * kb + 1) * 64 + lane] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
+    }
+}
+
+// Each wave's running state (m and the row sum per head, O per head and dim)
+// to its LDS area: wm[16], wl[16], wo[16][HD] per wave.
+template <int HD, int NT>
+I4D_DEVINL void attn_waves_to_lds(char* lds, float m, float lsum, const f4 (&O)[HD / 16]) {
+    constexpr int NKB = HD / 16;
+    const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+    float* wbase = (float*)lds + wave * (16 * HD + 32);
+    float lt = lsum;
+    lt += shfl_xor_f(lt, 16);
+    lt += shfl_xor_f(lt, 32);
+    if (gq == 0) { wbase[r] = m; wbase[16 + r] = lt; }
+#pragma unroll
+    for (int nt = 0; nt < NKB; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wbase[32 + (4 * gq + i) * HD + 16 * nt + r] = O[nt][i];
+}
+
+// The waves' states combined per (head h < G, dim d): this split's partial
+// (M, L, unnormalised O).  sink(h, d, M, L, acc) is called once per (h, d).
+template <int HD, int NT, class Sink>
+I4D_DEVINL void attn_combine_waves(const char* lds, int G, Sink& sink) {
+    constexpr int NW = NT / 64;
+    for (int idx = i4d_tid(); idx < G * HD; idx += NT) {
+        const int h = idx / HD, d = idx - h * HD;
+        const float* lw = (const float*)lds;
+        float M = -INFINITY;
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, lw[w * (16 * HD + 32) + h]);
+        float acc = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+            for (int w = 0; w < NW; ++w) {
+                const float* wb = lw + w * (16 * HD + 32);
+                const float e = exp2f(wb[h] - M);
+                acc = fmaf(wb[32 + h * HD + d], e, acc);
+                L = fmaf(wb[16 + h], e, L);
+            }
+        }
+        sink(h, d, M, L, acc);
+    }
+}
+
 // The whole item: optional round-0 registers already loaded (pre = true),
 // compute, per-item partial, and the merge by the last split to arrive.
 template <int HD, int NT, int NSW, bool PAGED = false>
 I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, NSW>& R, bool pre) {
-    constexpr int NW = NT / 64, NKB = HD / 16, DPL = HD / 4;
+    constexpr int NW = NT / 64, NKB = HD / 16;
     const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, gq = lane >> 4;
     const int G = a.hq / a.hkv;
     const AttnGeo g = attn_geo(a, item);
-    const int nsub = g.nsub, t_e = g.t_e;
+    const int nsub = g.nsub;
 
     // the subtile holding the new key gets the side-buffer values just before
     // it is used (in whichever round loads it: a line loaded earlier may be
     // stale); the other subtiles' loads are not waited for by these
-    const int stp = (a.kvn != nullptr && g.kpos >= g.t_s && g.kpos < t_e) ? (g.kpos - g.t_s) / 16 : -1;
+    const int stp = (a.kvn != nullptr && g.kpos >= g.t_s && g.kpos < g.t_e) ? (g.kpos - g.t_s) / 16 : -1;
     // q first: its loads then only wait for themselves, not for the K/V stream
     // issued after them.  q^T operand (hi, lo) for head r of this group, dims
     // in the K-row order above, kept in LDS after the per-wave areas (every
@@ -256,81 +380,13 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
         if (nround > 1) attn_page_offsets<HD, NT, NSW>(a, g, 1, poff);
     }
     s4* qop = (s4*)(lds + NW * (16 * HD + 32) * 4);
-    if (wave == 0) {
-        const float qs = (r < G) ? a.qscale : 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            uint16_t hv[4], lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = qv[kb][i] * qs;
-                hv[i] = f32_to_bf16(v);
-                lv[i] = f32_to_bf16(v - bf16_to_f32(hv[i]));
-            }
-            qop[(2 * kb) * 64 + lane] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-            qop[(2 * kb + 1) * 64 + lane] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
-        }
-    }
+    if (wave == 0) attn_q_operand<HD>(qv, (r < G) ? a.qscale : 0.f, qop);
     __syncthreads();
 
     float m = -INFINITY, lsum = 0.f;
     f4 O[NKB];
 #pragma unroll
     for (int nt = 0; nt < NKB; ++nt) O[nt] = f4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute_sub = [&](int st, const u32x4 (&kr)[NKB / 2], const u32x2 (&vr)[NKB]) {
-        const int t0 = g.t_s + 16 * st;
-        const int tv = t0 + 4 * gq;
-        const bool kvalid = t0 + r < t_e;               // this lane's K row
-        const int vvalid = t_e - tv;                    // keys of this lane's V run in range
-        // scores^T for keys 4gq..4gq+3 of head r
-        f4 sc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            u32x4 w = kr[kb >> 1];
-            if (!kvalid) w = u32x4{0, 0, 0, 0};
-            const s4 kop = (kb & 1) ? dwords_to_s4(w.z, w.w) : dwords_to_s4(w.x, w.y);
-            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb) * 64 + lane], sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb + 1) * 64 + lane], sc, 0, 0, 0);
-        }
-        float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tv + i >= t_e) sv[i] = -INFINITY;
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float mnew = fmaxf(m, mx);                // finite: the subtile has a valid key
-        const float alpha = exp2f(m - mnew);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - mnew);
-        lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m = mnew;
-        // rescale O rows (heads 4gq + i) by their alpha
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = shfl_f(alpha, 4 * gq + i);
-#pragma unroll
-            for (int nt = 0; nt < NKB; ++nt) O[nt][i] *= ai;
-        }
-        uint16_t ph[4], pl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ph[i] = f32_to_bf16(p[i]);
-            pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
-        }
-        const s4 pho = pack_bf16x4(ph[0], ph[1], ph[2], ph[3]);
-        const s4 plo = pack_bf16x4(pl[0], pl[1], pl[2], pl[3]);
-        const u32 vm0 = vvalid >= 2 ? 0xFFFFFFFFu : (vvalid == 1 ? 0x0000FFFFu : 0u);
-        const u32 vm1 = vvalid >= 4 ? 0xFFFFFFFFu : (vvalid == 3 ? 0x0000FFFFu : 0u);
-#pragma unroll
-        for (int nt = 0; nt < NKB; ++nt) {
-            const s4 vop = dwords_to_s4(vr[nt].x & vm0, vr[nt].y & vm1);
-            O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pho, vop, O[nt], 0, 0, 0);
-            O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop, O[nt], 0, 0, 0);
-        }
-    };
 
     // rounds of NSW subtiles per wave: round 0 is in R already
     for (int rnd = 0; rnd < nround; ++rnd) {
@@ -344,42 +400,21 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
         for (int i = 0; i < NSW; ++i) {
             const int st = (rnd * NSW + i) * NW + wave;
             if (st == stp) attn_patch_new<HD>(a, g, st, R.k[i], R.v[i]);
-            if (st < nsub) compute_sub(st, R.k[i], R.v[i]);
+            if (st < nsub) attn_sub<HD>(g, st, R.k[i], R.v[i], qop, m, lsum, O);
         }
     }
 
-    // per-wave state -> LDS: wm[16], wl[16], wo[16][HD] per wave
-    float* wbase = (float*)lds + wave * (16 * HD + 32);
-    float lt = lsum;
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
-    if (gq == 0) { wbase[r] = m; wbase[16 + r] = lt; }
-#pragma unroll
-    for (int nt = 0; nt < NKB; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wbase[32 + (4 * gq + i) * HD + 16 * nt + r] = O[nt][i];
+    attn_waves_to_lds<HD, NT>(lds, m, lsum, O);
     __syncthreads();
 
     // combine the waves; write this split's partial (through to memory)
     const size_t hrow0 = (size_t)(g.b * a.hq + g.j * G);
-    for (int idx = tid; idx < G * HD; idx += NT) {
-        const int h = idx / HD, d = idx - h * HD;
-        const float* lw = (const float*)lds;
-        float M = -INFINITY;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, lw[w * (16 * HD + 32) + h]);
-        float acc = 0.f, L = 0.f;
-        if (M != -INFINITY) {
-            for (int w = 0; w < NW; ++w) {
-                const float* wb = lw + w * (16 * HD + 32);
-                const float e = exp2f(wb[h] - M);
-                acc = fmaf(wb[32 + h * HD + d], e, acc);
-                L = fmaf(wb[16 + h], e, L);
-            }
-        }
+    auto put = [&](int h, int d, float M, float L, float acc) {
         const size_t pidx = (hrow0 + h) * a.pstride + g.s;
         st_dev(a.po + pidx * HD + d, acc);
         if (d == 0) { st_dev(a.pm + pidx, M); st_dev(a.pl + pidx, L); }
-    }
+    };
+    attn_combine_waves<HD, NT>(lds, G, put);
     wait_stores();
     __syncthreads();
 

@@ -28,7 +28,9 @@ I4D_DEVINL int i4d_tid() {
 // count against the LDS wait counter: every LDS wait would then wait for the
 // weight stream as well.
 #define I4D_GLOBAL __attribute__((address_space(1)))
+#define I4D_CONST __attribute__((address_space(4)))
 template <class T> I4D_DEVINL T ld_g(const T* p) { return *(const I4D_GLOBAL T*)p; }
+template <class T> I4D_DEVINL void st_g(T* p, T v) { *(I4D_GLOBAL T*)p = v; }
 template <class T> I4D_DEVINL T ld_g_nt(const T* p) { return __builtin_nontemporal_load((const I4D_GLOBAL T*)p); }
 
 // ---------------------------------------------------------------- bf16

@@ -13,6 +13,7 @@
 #include "common.h"
 #include "gemv.h"
 #include "mfma.h"
+#include "stream.h"
 
 namespace {
 
@@ -27,9 +28,6 @@ namespace {
 #endif
 #ifndef I4D_WG_PER_CU
 #define I4D_WG_PER_CU 1
-#endif
-#ifndef I4D_ENABLE_PERSISTENT
-#define I4D_ENABLE_PERSISTENT 1
 #endif
 constexpr int GEMV_NT = I4D_GEMV_NT;       // threads per GEMV workgroup
 constexpr int GEMV_D = I4D_GEMV_D;         // units in flight per lane
@@ -324,6 +322,26 @@ __global__ void __launch_bounds__(ATTN_NT) k_attention(AttnArgs a) {
     for (int it = blockIdx.x; it < items; it += gridDim.x) attn_item<HD, ATTN_NT, NSW, PAGED>(a, it, lds, R, false);
 }
 
+// ---------------------------------------------------------------- streaming-read probe
+// Each lane keeps four 16-byte nontemporal loads in flight over a grid-stride
+// sweep; the words are XOR-folded so the loads cannot be dropped.
+__global__ void __launch_bounds__(512) k_read_probe(const u32x4* src, size_t n16, u32* sink) {
+    const size_t nthr = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + i4d_tid();
+    u32 acc = 0;
+    for (; i + 3 * nthr < n16; i += 4 * nthr) {
+        const u32x4 a = ld_g_nt(src + i), b = ld_g_nt(src + i + nthr), c = ld_g_nt(src + i + 2 * nthr),
+                    d = ld_g_nt(src + i + 3 * nthr);
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n16; i += nthr) {
+        const u32x4 a = ld_g_nt(src + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int m = 32; m >= 1; m >>= 1) acc ^= (u32)__shfl_xor((int)acc, m, 64);
+    if ((i4d_tid() & 63) == 0) atomicXor(sink, acc);
+}
+
 // ---------------------------------------------------------------- decode loop glue
 // x[b] = row tokens[b] of the bf16 embedding table (an id outside the table
 // gives a zero row and the status bit).
@@ -373,245 +391,20 @@ __global__ void __launch_bounds__(512) k_mfma_lm(MfmaTask m, u64* wg_keys, Sampl
     mfma_gemm<KIND_ADJ, NB, 1, MEPI_ARGMAX>(m, lds, smp, wg_keys);
 }
 
-// Workspace: an 8 KB header (status word, grid-barrier epoch, the attention
-// arrival counters, barrier flags), the persistent kernel's layer table, then
-// one region of buffers per layer.  The LM head uses the bytes after the header
-// for its per-workgroup argmax keys (WS_LM_BYTES), overlapping the layer
-// buffers: calls on one stream never use both at once.  The counters sit in
-// the header because they must read zero at the start of every attention
-// phase (each merge resets its own).
-constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_CNT = 1024, WS_FLAGS = 4096, WS_MCNT = 8192, WS_HEADER = 16384;
-constexpr int WS_MAX_CNT = (int)((WS_FLAGS - WS_CNT) / 4);     // B * Hkv arrival counters
+// Workspace: a 16 KB header (status word, the streaming kernel's launch epoch,
+// the attention arrival counters, the batched GEMM's row-block counters),
+// then one region of buffers per layer, then (batch 1) the streaming kernel's
+// region.  The LM head uses the bytes after the header for its per-workgroup
+// argmax keys (WS_LM_BYTES), overlapping the layer buffers: calls on one
+// stream never use both at once.  The counters sit in the header because
+// they must read zero at the start of every attention phase (each merge
+// resets its own).
+constexpr size_t WS_STATUS = 0, WS_EPOCH = 64, WS_CNT = 1024, WS_CNT_END = 4096, WS_MCNT = 8192, WS_HEADER = 16384;
+constexpr int WS_MAX_CNT = (int)((WS_CNT_END - WS_CNT) / 4);   // B * Hkv arrival counters
 constexpr int WS_MAX_MCNT = (int)((WS_HEADER - WS_MCNT) / 4);  // row-block arrival counters of the batched GEMM
-constexpr int PERS_MAX_WG = 1024;                    // flags: one int per workgroup of the persistent kernel
-constexpr int PERS_MAX_LAYERS = 256;
 constexpr int LM_MAX_WG = 4096;
 constexpr size_t WS_LM_KEYS = WS_HEADER, WS_LM_BYTES = (size_t)LM_MAX_WG * MAX_BATCH_ALL * 8;
 constexpr size_t WS_LM_END = WS_LM_KEYS + WS_LM_BYTES;   // batched-GEMM scratch of the LM head and the GEMV hook
-
-// ============================================================== persistent decode kernel
-// One cooperative launch runs every layer of the step: 256 workgroups (one per
-// compute unit) walk through the six phases of each layer, separated by grid
-// barriers.  Before a barrier each workgroup already issues the weight loads
-// of the next matrix-vector phase (weights do not depend on activations), so
-// HBM keeps streaming while the barrier completes.
-
-// Per-layer device pointers: the only per-layer data the kernel reads (the
-// schedules of the four matrix-vector phases are the same for every layer and
-// travel in the kernel arguments as templates).
-struct PDesc {
-    const uint8_t* d[7];          // codes of wq wk wv wo wg wu wd
-    const uint16_t* sc[7];        // their bf16 scales
-    const uint16_t* attn_norm;
-    const uint16_t* ffn_norm;
-    uint16_t* kc;
-    uint16_t* vc;
-};
-constexpr size_t PERS_TABLE_BYTES = (size_t)PERS_MAX_LAYERS * sizeof(PDesc);
-
-struct PArgs {
-    const PDesc* layers;
-    int n_layers, batch;
-    const float* x_in;
-    float* x_out;                // output of the last layer
-    GemvTask tq, to, tg, td;     // schedules of q/k/v, Wo, gate/up, down (pointers filled per layer)
-    char* lbase;                 // per-layer workspace regions: lbase + l * lstride
-    size_t lstride, off_q, off_o, off_y, off_act, off_x, off_kvn, off_pm, off_pl, off_po;
-    AttnArgs attn;               // per-layer q, o, kc, vc filled in by the kernel
-    const int* pos;
-    int max_pos, cap, hq, hkv, hd, d_model, d_ff;
-    double base;
-    float eps;
-    int act_bytes;               // LDS bytes reserved for staged activations
-    int pos_off;                 // LDS offset of the per-sequence positions (past every phase's use)
-    int* status; int* flags; int* epoch;
-};
-
-// A phase's task: the template with layer L's matrices i0 (and i1, i2).
-I4D_DEVINL GemvTask task_of(GemvTask t, const PDesc& L, int i0, int i1, int i2) {
-    t.a.data = L.d[i0]; t.a.scales = L.sc[i0];
-    if (i1 >= 0) { t.b.data = L.d[i1]; t.b.scales = L.sc[i1]; } else { t.b.data = t.a.data; t.b.scales = t.a.scales; }
-    if (i2 >= 0) { t.c.data = L.d[i2]; t.c.scales = L.sc[i2]; } else { t.c.data = t.a.data; t.c.scales = t.a.scales; }
-    return t;
-}
-
-// Copy a chunk of layer descriptors (passed by value) into the workspace
-// table; a few of these replace a host-to-device copy of the table.
-constexpr int PDESC_PER_FILL = 24;
-struct PDescChunk { PDesc e[PDESC_PER_FILL]; PDesc* dst; int count; };
-__global__ void __launch_bounds__(64) k_fill_table(PDescChunk c) {
-    const int words = c.count * (int)(sizeof(PDesc) / 8);
-    for (int i = i4d_tid(); i < words; i += 64) ((u64*)c.dst)[i] = ((const u64*)c.e)[i];
-}
-
-// One wave per SIMD: the fused kernel's live state needs more than the 256
-// registers a wave gets at two waves per SIMD; at one wave it can also use
-// the accumulation registers and needs no scratch memory.  A deeper load ring
-// keeps as many bytes in flight per compute unit as two waves would.
-constexpr int PERS_NT = 256;
-constexpr int PERS_D = 10;
-constexpr long long BAR_SPIN_LIMIT = 1 << 20;
-
-// Grid barrier on per-workgroup epoch flags.  A workgroup publishes epoch
-// base + k once every thread's stores have completed, then one wave polls all
-// flags with device-scope loads.  The spin is bounded: on timeout the status
-// word gets I4D_DEV_BARRIER_TIMEOUT and, that bit being sticky, no later
-// barrier of any workgroup waits again -- every wave always reaches the end.
-struct GridSync {
-    int* flags; int* status; int base; int nwg;
-    // publish arrival k once every store of this workgroup has completed
-    I4D_DEVINL void arrive(int k) const {
-        wait_stores();
-        __syncthreads();
-        if (i4d_tid() == 0) st_dev(flags + blockIdx.x, base + k);
-    }
-    // wait until every workgroup has arrived at k (bounded spin)
-    I4D_DEVINL void depart(int k) const {
-        const int target = base + k;
-        if (i4d_tid() < 64) {
-            if ((ld_dev(status) & I4D_DEV_BARRIER_TIMEOUT) == 0) {
-                long long spins = 0;
-                for (;;) {
-                    bool ok = true;
-                    for (int i = i4d_tid(); i < nwg; i += 64) ok = ok && (ld_dev(flags + i) - target >= 0);
-                    if (__all(ok)) break;
-                    if (++spins > BAR_SPIN_LIMIT) {
-                        if (i4d_tid() == 0) raise_status(status, I4D_DEV_BARRIER_TIMEOUT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    I4D_DEVINL void wait(int k) const { arrive(k); depart(k); }
-};
-
-template <int NB, int KND>
-struct PrimeNext {
-    GemvPipe<FMT_INT4_FAST, PERS_D>& P; GemvTask t; int w, nwg; bool on;
-    I4D_DEVINL void operator()() { if (on) gemv_prime<FMT_INT4_FAST, PERS_NT, PERS_D, KND>(P, t, w, nwg); }
-};
-
-template <int NB>
-__global__ void __launch_bounds__(PERS_NT) k_decode_persistent(PArgs A) {
-    constexpr int FMT = FMT_INT4_FAST;
-    constexpr int MJ = MaxJ<NB>::v;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int w0 = blockIdx.x, nwg0 = gridDim.x;
-    GemvLds L;
-    L.act = lds;
-    L.part = (float*)(lds + A.act_bytes);
-    L.red = L.part + gemv_part_bytes<FMT, NB, PERS_NT>() / 4;
-    L.extra = (char*)(L.red + (PERS_NT / 64) * NB);
-    int* pos_lds = (int*)(lds + A.pos_off);
-    float2* cs = (float2*)(lds + A.pos_off + 64);
-    if (i4d_tid() < NB) {
-        int p = -1;
-        if (i4d_tid() < A.batch) {
-            p = A.pos[i4d_tid()];
-            if (p < 0 || p > A.max_pos || p >= A.cap) {
-                if (w0 == 0) raise_status(A.status, I4D_DEV_BAD_POS);
-                p = -1;
-            }
-        }
-        pos_lds[i4d_tid()] = p;
-    }
-    __syncthreads();
-    rope_table<NB>(cs, pos_lds, A.hd, A.base);
-    GridSync gs{A.flags, A.status, ld_dev(A.epoch), nwg0};
-    int bar = 0;
-    const int items = A.batch * A.hkv * A.attn.nsplit;
-    constexpr int ANSW = AttnNsw<PERS_NT>::v;
-
-    GemvPipe<FMT, PERS_D> P;
-    gemv_prime<FMT, PERS_NT, PERS_D, KIND_QKV>(P, task_of(A.tq, A.layers[0], 0, 1, 2), w0, nwg0);
-    for (int l = 0; l < A.n_layers; ++l) {
-        // per-layer opaque copies of the launch constants: otherwise every
-        // phase's schedule arithmetic is hoisted out of the layer loop and
-        // stays live in registers across all phases
-        int w = w0, nwg = nwg0;
-        asm volatile("" : "+s"(w), "+s"(nwg));
-        const PDesc& Ly = A.layers[l];
-        const uint16_t* attn_norm = Ly.attn_norm;
-        const uint16_t* ffn_norm = Ly.ffn_norm;
-        uint16_t* kc = Ly.kc;
-        uint16_t* vc = Ly.vc;
-        char* R = A.lbase + (size_t)l * A.lstride;
-        float* q = (float*)(R + A.off_q);
-        float* o = (float*)(R + A.off_o);
-        float* y = (float*)(R + A.off_y);
-        float* act = (float*)(R + A.off_act);
-        const float* xin = (l == 0) ? A.x_in : (const float*)(R - A.lstride + A.off_x);
-        float* xout = (l + 1 == A.n_layers) ? A.x_out : (float*)(R + A.off_x);
-
-        uint16_t* kvn = (uint16_t*)(R + A.off_kvn);
-        AttnArgs a = A.attn;
-        asm volatile("" : "+s"(a.nsplit), "+s"(a.T), "+s"(a.hq), "+s"(a.hkv), "+s"(a.cap));
-        a.kc = kc; a.vc = vc; a.q = q; a.kvn = kvn; a.o = o;
-        a.pm = (float*)(R + A.off_pm); a.pl = (float*)(R + A.off_pl); a.po = (float*)(R + A.off_po);
-
-        // ---- q/k/v projection, RoPE, KV append
-        {
-            StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, xin, A.d_model, A.d_model, A.batch, attn_norm);
-            stage_finish<FMT, NB, PERS_NT, PREC_QKV>(pre, L.act, xin, A.d_model, A.d_model, A.batch, attn_norm, A.eps, L.red);
-            __syncthreads();
-            EpiQKV<true> ep{q, kc, vc, kvn, pos_lds, cs, A.cap, A.hq, A.hkv, A.hd, A.batch, 1};
-            NoNext nn;
-            gemv_passes<FMT, NB, PREC_QKV, PERS_NT, PERS_D, MJ, KIND_QKV>(P, task_of(A.tq, Ly, 0, 1, 2), w, nwg, L.act, L.part, ep, nn);
-        }
-        // ---- barrier; the cached history of this workgroup's first attention
-        // item streams in while it completes
-        AttnRegs<128, ANSW> AR;
-        gs.arrive(++bar);
-        if (w < items) attn_load_round<128, PERS_NT, ANSW>(a, attn_geo(a, w), 0, AR);
-        gs.depart(bar);
-        // ---- attention, merged by the last split of each (sequence, KV
-        // head); then the Wo weights start streaming
-        for (int it = w; it < items; it += nwg) attn_item<128, PERS_NT, ANSW>(a, it, lds, AR, it == w);
-        gemv_prime<FMT, PERS_NT, PERS_D, KIND_ADJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg);
-        gs.wait(++bar);
-        // ---- output projection + residual
-        {
-            StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, o, A.hq * A.hd, A.hq * A.hd, A.batch, nullptr, 0.f, L.red);
-            __syncthreads();
-            EpiRows<true> ep{y, xin, A.d_model, A.batch};
-            PrimeNext<NB, KIND_TWO> nx{P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.to, Ly, 3, -1, -1), w, nwg, L.act, L.part, ep, nx);
-        }
-        gs.wait(++bar);
-        // ---- gate/up projection + SwiGLU
-        {
-            StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, y, A.d_model, A.d_model, A.batch, ffn_norm);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, y, A.d_model, A.d_model, A.batch, ffn_norm, A.eps, L.red);
-            __syncthreads();
-            EpiSwiGLU<true> ep{act, A.d_ff, A.batch};
-            PrimeNext<NB, KIND_ADJ> nx{P, task_of(A.td, Ly, 6, -1, -1), w, nwg, true};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_TWO>(P, task_of(A.tg, Ly, 4, 5, -1), w, nwg, L.act, L.part, ep, nx);
-        }
-        gs.wait(++bar);
-        // ---- down projection + residual (then the next layer's q/k/v weights start streaming)
-        {
-            StagePre<FMT> pre;
-            stage_issue<FMT, NB, PERS_NT>(pre, act, A.d_ff, A.d_ff, A.batch, nullptr);
-            stage_finish<FMT, NB, PERS_NT, PREC_STD>(pre, L.act, act, A.d_ff, A.d_ff, A.batch, nullptr, 0.f, L.red);
-            __syncthreads();
-            EpiRows<true> ep{xout, y, A.d_model, A.batch};
-            const bool more = l + 1 < A.n_layers;
-            PrimeNext<NB, KIND_QKV> nx{P, task_of(A.tq, more ? A.layers[l + 1] : Ly, 0, 1, 2), w, nwg, more};
-            gemv_passes<FMT, NB, PREC_STD, PERS_NT, PERS_D, MJ, KIND_ADJ>(P, task_of(A.td, Ly, 6, -1, -1), w, nwg, L.act, L.part, ep, nx);
-        }
-        if (l + 1 < A.n_layers) gs.wait(++bar);
-    }
-    // every workgroup read the epoch at its start before any passed the first
-    // barrier, so the next launch's epoch can be published now
-    if (w0 == 0 && i4d_tid() == 0) st_dev(A.epoch, gs.base + bar);
-}
 
 // ============================================================== host helpers
 int g_num_cus[64];
@@ -630,7 +423,7 @@ int num_cus() {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t table;
+    size_t stream;                        // the streaming kernel's region (batch 1), 0 if none
     size_t mfma;                          // scratch of the batched (MFMA) phases, batches above MAX_BATCH
     size_t layer0, layer_stride;          // per-layer regions
     size_t q, o, y, act, x, kvn, pm, pl, po;   // offsets inside a layer region
@@ -649,15 +442,12 @@ int attn_splits_max(const i4d_config* c, int B) {
 
 // Layer l's region holds its q, merged attention output o, residual y, SwiGLU
 // activations, output x, the new token's k/v side copy and the attention
-// partials.  Per-phase launches use region 0 only; the persistent kernel gives
-// every layer its own region so that no buffer is read in a launch before it
-// has been written there.  Partial rows are padded to 128-byte lines so the
-// partials of different (sequence, KV head) groups never share a cache line.
+// partials.  Partial rows are padded to 128-byte lines so the partials of
+// different (sequence, KV head) groups never share a cache line.  The
+// streaming kernel's region comes after everything the LM head may overlay.
 WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
     WsLayout w;
     size_t off = WS_HEADER;
-    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    w.table = take(PERS_TABLE_BYTES);
     const size_t hq = c->n_q_heads, hkv = c->n_kv_heads, hd = c->head_dim;
     w.pstride = (attn_splits_max(c, B) + 31) / 32 * 32;
     size_t lo = 0;
@@ -680,7 +470,13 @@ WsLayout ws_layout(const i4d_config* c, int n_layers, int B) {
         w.mfma = off;
         off += layer_scratch_bytes(c, nb_mfma(B));
     }
-    w.total = std::max(off, WS_LM_END);
+    off = std::max(off, WS_LM_END);
+    w.stream = 0;
+    if (B == 1 && c->head_dim == 128) {
+        w.stream = align256(off);
+        off = w.stream + i4d_stream::region_bytes(c, std::max(n_layers, 1), num_cus());
+    }
+    w.total = off;
     return w;
 }
 
@@ -1259,136 +1055,6 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
     return mfma_rows(nb, mfma_task(td, pd, base, S, cnt, B, g), pd, x_out, y, s);
 }
 
-// ---------------------------------------------------------------- persistent launch
-template <int NB>
-size_t persistent_lds(const i4d_config* c, int nsplit) {
-    constexpr int FMT = FMT_INT4_FAST;
-    const int D = c->d_model, qw = c->n_q_heads * c->head_dim, F = c->d_ff;
-    const int act = std::max(std::max(act_lds_bytes<FMT, NB, PREC_QKV>(D), act_lds_bytes<FMT, NB, PREC_STD>(qw)),
-                             act_lds_bytes<FMT, NB, PREC_STD>(F));
-    const size_t gemv = (size_t)act + gemv_part_bytes<FMT, NB, PERS_NT>() + (PERS_NT / 64) * NB * 4 + 256;
-    const size_t attn = attn_lds_bytes<128, PERS_NT>();
-    (void)nsplit;
-    return align256(std::max(gemv, attn)) + GEMV_EXTRA;
-}
-
-bool persistent_supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int B) {
-    if (c->head_dim != 128 || B > 4 || n_layers > PERS_MAX_LAYERS) return false;
-    // the attention merge gives each (query head, 4 dims) slot its own thread
-    if ((c->n_q_heads / c->n_kv_heads) * (c->head_dim / 4) > PERS_NT) return false;
-    const int nwg = num_cus();
-    if (nwg > PERS_MAX_WG) return false;
-    for (int l = 0; l < n_layers; ++l) {
-        const i4d_layer& L = layers[l];
-        const i4d_mat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
-        for (int i = 0; i < 7; ++i)
-            if (m[i]->dtype != I4D_WEIGHT_INT4 || pick_fmt(*m[i]) != FMT_INT4_FAST || m[i]->group != layers[0].wq.group) return false;
-        if (kv[l].capacity != kv[0].capacity || kv[l].pages) return false;
-    }
-    return true;
-}
-
-template <int NB>
-int launch_persistent_t(PArgs& A, int nwg, size_t lds, hipStream_t s) {
-    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
-    if (set_lds(k_decode_persistent<NB>, lds) != hipSuccess) return I4D_EHIP;
-    // The cooperative kernel must run entirely in registers and LDS: a build
-    // that gives it a private (scratch) segment is not launched.
-    hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, (const void*)k_decode_persistent<NB>) != hipSuccess) return I4D_EHIP;
-    if (fa.localSizeBytes != 0) return I4D_EUNSUPPORTED;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_persistent<NB>, PERS_NT, lds) != hipSuccess)
-        return I4D_EHIP;
-    if (per_cu < 1) return I4D_EUNSUPPORTED;
-    void* args[] = {&A};
-    // a cooperative launch has no event-carrying form: events are recorded
-    // around it (two packets against a launch of milliseconds)
-    const int slot = take_timing_slot();
-    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot], s);
-    const hipError_t e = hipLaunchCooperativeKernel((const void*)k_decode_persistent<NB>, dim3(nwg), dim3(PERS_NT), args,
-                                                    (unsigned)lds, s);
-    if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
-    return e == hipSuccess ? I4D_OK : I4D_EHIP;
-}
-
-int run_stack_persistent(const i4d_config* c, int n_layers, const i4d_layer* layers, int B, const float* x_in, float* x_out,
-                         const i4d_kv* kv, const int* pos, int max_pos, char* ws, const WsLayout& W, hipStream_t s) {
-    const int nb = nb_slot(B), nwg = num_cus();
-    const int hd = c->head_dim;
-    // the layer table goes to the workspace as by-value kernel arguments of a
-    // few copy kernels (no host buffer has to outlive this call)
-    PDesc* table = (PDesc*)(ws + W.table);
-    for (int l0 = 0; l0 < n_layers; l0 += PDESC_PER_FILL) {
-        PDescChunk ch;
-        memset(&ch, 0, sizeof(ch));
-        ch.count = std::min(PDESC_PER_FILL, n_layers - l0);
-        ch.dst = table + l0;
-        for (int i = 0; i < ch.count; ++i) {
-            const i4d_layer& Ls = layers[l0 + i];
-            const i4d_mat* m[7] = {&Ls.wq, &Ls.wk, &Ls.wv, &Ls.wo, &Ls.wg, &Ls.wu, &Ls.wd};
-            PDesc& d = ch.e[i];
-            for (int k = 0; k < 7; ++k) { d.d[k] = (const uint8_t*)m[k]->data; d.sc[k] = (const uint16_t*)m[k]->scales; }
-            d.attn_norm = Ls.attn_norm;
-            d.ffn_norm = Ls.ffn_norm;
-            d.kc = kv[l0 + i].k;
-            d.vc = kv[l0 + i].v;
-        }
-        hipLaunchKernelGGL(k_fill_table, dim3(1), dim3(64), 0, s, ch);
-    }
-
-    PArgs A;
-    memset(&A, 0, sizeof(A));
-    A.layers = table;
-    A.n_layers = n_layers;
-    A.batch = B;
-    A.x_in = x_in;
-    A.x_out = x_out;
-    const i4d_layer& L0 = layers[0];
-    A.tq = make_task(KIND_QKV, &L0.wq, &L0.wk, &L0.wv, hd);
-    A.to = make_task(KIND_ADJ, &L0.wo, nullptr, nullptr, hd);
-    A.tg = make_task(KIND_TWO, &L0.wg, &L0.wu, nullptr, hd);
-    A.td = make_task(KIND_ADJ, &L0.wd, nullptr, nullptr, hd);
-    plan_passes(A.tq, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
-    plan_passes(A.to, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
-    plan_passes(A.tg, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
-    plan_passes(A.td, FMT_INT4_FAST, nb, nwg, 0, PERS_NT);
-    A.lbase = ws + W.layer0;
-    A.lstride = W.layer_stride;
-    A.off_q = W.q; A.off_o = W.o; A.off_y = W.y; A.off_act = W.act; A.off_x = W.x;
-    A.attn = attn_args(c, B, nullptr, &kv[0], nullptr, pos, max_pos, nullptr, ws, W, ws + W.layer0);  // per-layer pointers set in the kernel
-    const AttnArgs& a = A.attn;
-    A.off_kvn = W.kvn; A.off_pm = W.pm; A.off_pl = W.pl; A.off_po = W.po;
-    A.pos = pos; A.max_pos = max_pos; A.cap = kv[0].capacity;
-    A.hq = c->n_q_heads; A.hkv = c->n_kv_heads; A.hd = hd; A.d_model = c->d_model; A.d_ff = c->d_ff;
-    A.base = c->rope_base; A.eps = c->rms_eps;
-    A.status = (int*)(ws + WS_STATUS); A.flags = (int*)(ws + WS_FLAGS); A.epoch = (int*)(ws + WS_EPOCH);
-    const int D = c->d_model, qw = c->n_q_heads * hd, F = c->d_ff;
-    switch (nb) {
-        case 1: {
-            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 1, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 1, PREC_STD>(qw)),
-                                   act_lds_bytes<FMT_INT4_FAST, 1, PREC_STD>(F));
-            const size_t lds = persistent_lds<1>(c, a.nsplit);
-            A.pos_off = (int)lds - GEMV_EXTRA;
-            return launch_persistent_t<1>(A, nwg, lds, s);
-        }
-        case 2: {
-            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 2, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 2, PREC_STD>(qw)),
-                                   act_lds_bytes<FMT_INT4_FAST, 2, PREC_STD>(F));
-            const size_t lds = persistent_lds<2>(c, a.nsplit);
-            A.pos_off = (int)lds - GEMV_EXTRA;
-            return launch_persistent_t<2>(A, nwg, lds, s);
-        }
-        default: {
-            A.act_bytes = std::max(std::max(act_lds_bytes<FMT_INT4_FAST, 4, PREC_QKV>(D), act_lds_bytes<FMT_INT4_FAST, 4, PREC_STD>(qw)),
-                                   act_lds_bytes<FMT_INT4_FAST, 4, PREC_STD>(F));
-            const size_t lds = persistent_lds<4>(c, a.nsplit);
-            A.pos_off = (int)lds - GEMV_EXTRA;
-            return launch_persistent_t<4>(A, nwg, lds, s);
-        }
-    }
-}
-
 // One layer as phase launches (q/k/v, attention, Wo, gate/up, down), using
 // the workspace region R.
 int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
@@ -1498,12 +1164,15 @@ static int decode_stack_impl(bool run, const i4d_config* cfg, int32_t n_layers, 
     if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
-    if (cfg->exec_mode == 2) {
-        if (!I4D_ENABLE_PERSISTENT || kvb != 1) return I4D_EUNSUPPORTED;
-        if (!persistent_supported(cfg, n_layers, layers, kv, batch)) return I4D_EUNSUPPORTED;
+    // the streaming kernel: exec_mode 2, or auto when the request qualifies
+    const bool stream_ok = kvb == 1 && W.stream != 0 && i4d_stream::supported(cfg, n_layers, layers, kv, batch, num_cus());
+    if (cfg->exec_mode == 2 && !stream_ok) return I4D_EUNSUPPORTED;
+    if (stream_ok && cfg->exec_mode != 1) {
         if (!run) return I4D_OK;
-        TimeScope ts(I4D_TIME_PERSISTENT);
-        return run_stack_persistent(cfg, n_layers, layers, batch, x_in, x_out, kv, pos, max_pos, w, W, s);
+        TimeScope ts(I4D_TIME_STREAM);
+        const int slot = take_timing_slot();
+        return i4d_stream::run(cfg, n_layers, layers, x_in, x_out, kv, pos, max_pos, w + W.stream, (int*)(w + WS_STATUS),
+                               (unsigned*)(w + WS_EPOCH), num_cus(), s, slot >= 0 ? &g_timing.ev[2 * slot] : nullptr);
     }
     if (!run) return I4D_OK;
     for (int l = 0; l < n_layers; ++l) {
@@ -1722,7 +1391,7 @@ int i4d_attention(const i4d_config* cfg, int32_t batch, const float* q, const i4
 }
 
 int i4d_launch_timing_start(int32_t kernel, int32_t max_launches) {
-    if (kernel < I4D_TIME_QKV || kernel > I4D_TIME_PERSISTENT || max_launches < 1 || max_launches > 65536)
+    if (kernel < I4D_TIME_QKV || kernel > I4D_TIME_STREAM || max_launches < 1 || max_launches > 65536)
         return I4D_EINVAL;
     g_timing.kind = 0;
     g_timing.n = 0;
@@ -1760,6 +1429,13 @@ int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream) {
     if (hipMemcpyAsync(status_out, ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return I4D_EHIP;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return I4D_EHIP;
     return I4D_OK;
+}
+
+int i4d_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes == 0) return I4D_EINVAL;
+    if (!aligned(buf, 16) || bytes % 16 || !aligned(sink, 4)) return I4D_EALIGN;
+    hipLaunchKernelGGL(k_read_probe, dim3(num_cus()), dim3(512), 0, (hipStream_t)stream, (const u32x4*)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
 const char* i4d_status_string(int status) {

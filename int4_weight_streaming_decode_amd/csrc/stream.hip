@@ -1,0 +1,1077 @@
+// Streaming decode kernel: one persistent launch runs every layer of a
+// batch-1 decode step (gfx950, wave64).
+//
+// Why one launch.  At batch 1 every weight byte is read once per token and the
+// step is bound by HBM (Primer 1.2; Roofline reply 一/二).  Issued as one kernel
+// per phase, each of the five phases of a layer pays its own start-up (the
+// first weight bytes arrive only after the activations are staged) and its own
+// drain; the pages' cure is fusion so that nothing stops the weight stream
+// (Unsloth article 二.1, Roofline reply 三).  Here one workgroup per compute
+// unit walks all phases of all layers, and its weight stream never stops at a
+// phase boundary: each lane keeps RD units of weights in flight, and the loads
+// run ahead into the next phase (weights do not depend on activations) while
+// the workgroup waits for the activations that phase needs.
+//
+// Exchange between workgroups.  Every value one workgroup hands to another
+// (q, the new k/v, attention partials, merged heads, residual stream, SwiGLU
+// activations) is stored as a 64-bit word: the fp32 value and a 32-bit tag
+// that is unique to this launch.  A reader loads the words -- plainly first,
+// so the 32 compute units of an XCD share one fetch through their L2 -- and
+// reloads any word whose tag is stale with device-scope loads until it is
+// current.  There is no grid barrier and no write acknowledgement on the
+// critical path: a value is usable as soon as its own word arrives.  Each
+// layer has its own exchange region, so a plain load never meets a line that
+// was cached earlier in the same launch.
+//
+// The int4 dot product.  Activations are staged in LDS as integers: each run
+// of 32 inputs is scaled by a power of two so that its largest magnitude lies
+// in [2^13, 2^14), rounded to an integer a, and a is written as four balanced
+// base-16 digits d_p in [-8, 7] (a = sum_p d_p 16^p; the nibbles of
+// (a + 0x8888) ^ 0x8888).  Plane p holds digit p of every input, eight inputs
+// per dword in the weight codes' nibble order.  A code dword XOR 0x88888888
+// is the eight signed int4 values c - 8, so v_dot8_i32_i4 against plane p
+// gives sum (c - 8) d_p exactly; the four plane sums are combined by shifts
+// into sum (c - 8) a (exact in int32), converted once, and scaled by the
+// group scale times the run's power of two.  The only rounding is that of the
+// activations to 15 significant bits relative to their run's maximum (23 bits
+// and six digit planes for the q/k/v projection, whose k and v are rounded to
+// bf16 into the cache), and no activation can overflow (the power of two
+// adapts to any finite value).
+// About 0.85 VALU operations per weight.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "stream.h"
+#include "attention.h"
+#include "common.h"
+
+namespace i4d_stream {
+namespace {
+
+constexpr int NT = 512;            // threads per workgroup: 8 waves, two per SIMD
+constexpr int NWAVE = NT / 64;
+constexpr int NSLOT = NT / 16;     // 16-lane slots
+constexpr int RD = 4;              // weight units in flight per lane
+constexpr int HD = 128;
+constexpr int ANSW = 2;            // attention subtiles per wave per load round
+constexpr int PS = 16384;          // LDS bytes per digit plane (K <= 32768)
+constexpr int MAXRUN = 8;          // pair runs per slot per phase
+constexpr int MAX_LAYERS = 128;    // layer table kept in LDS
+constexpr int MAX_RES = 64;        // residual rows per compute unit: pairs of Wo / W_down
+constexpr int KMAX = 2 * PS;       // largest K: 4 bits per input in each digit plane
+constexpr int SPIN_LIMIT = 1 << 17;
+
+enum { K_QKV = 0, K_WO = 1, K_GU = 2, K_DN = 3 };
+
+// ------------------------------------------------------------------ layer table
+struct LPtr {
+    const uint8_t* c[7];          // codes of wq wk wv wo wg wu wd
+    const uint8_t* s[7];          // their bf16 scales (byte pointers)
+    const uint16_t* g1;           // attention norm gain
+    const uint16_t* g2;           // FFN norm gain
+    uint16_t* kc;
+    uint16_t* vc;
+};
+constexpr int LPTR_WORDS = (int)(sizeof(LPtr) / 8);
+
+// ------------------------------------------------------------------ per-kind geometry (same for every layer)
+// A phase streams pairs of rows: q/k/v (i, i + hd/2) of one head of ONE of
+// the three matrices (compute units are split between q, k and v in
+// proportion to their rows); Wo and W_down rows (p, p + D/2); gate row p with
+// up row p.  The pairs of a compute unit are cut into units of 16 lanes x 16
+// bytes per row (512 inputs) and the units into one contiguous range per
+// 16-lane slot; every slot runs n iterations (short ranges load a harmless
+// repeat of their first unit and skip it).
+struct KGeo {
+    int S;                        // units per row (K / 512)
+    int K;
+    int p0, np;                   // this unit's first pair and pair count (within its matrix)
+    int U, n;                     // units, iterations per slot
+    int mia, mib;                 // table index of the matrix of row a, row b
+    int mat;                      // q/k/v: 0, 1, 2
+    unsigned ca_off, cb_off;      // code byte offsets of pair p0's rows a and b
+    unsigned sa_off, sb_off;      // scale byte offsets
+    unsigned jump, jumps;         // q/k/v: extra advance at a head boundary (codes, scales)
+    int jper;                     // units between head boundaries (0: none)
+};
+struct SGeo {                     // per (kind, slot)
+    int len, seg0, cnt0, u0, pair0;   // pair0: local index of the slot's first pair
+    unsigned off0, soff0;         // byte offsets within the unit's code / scale streams (lane 0 of the slot)
+};
+
+struct Args {
+    const LPtr* table;
+    int L;
+    const float* x_in;
+    float* x_out;
+    const int* pos;
+    int max_pos, cap;
+    int D, F, Hq, Hkv;
+    float eps, qscale;
+    double base;
+    int nsplit, T;                 // attention: splits per KV head, keys per split
+    int cq, ck;                    // compute units [0, cq): q rows, [cq, ck): k rows, [ck, nwg): v rows
+    char* lbase;                   // exchange regions: lbase + l * lstride
+    size_t lstride;
+    unsigned ox, oq, okv, opart, oo, oy, oact;   // byte offsets in a region
+    const uint8_t* zero;           // 1 KB of zeros (loads past the last phase)
+    int* status;
+    unsigned* epoch;
+};
+
+// ------------------------------------------------------------------ LDS layout
+constexpr int ATT_LDS = NWAVE * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8;   // attn_lds_bytes<HD, NT>
+constexpr int A_BYTES = ((std::max(4 * PS + KMAX / 32 * 4, ATT_LDS + 2 * HD * 2) + 255) / 256) * 256;
+constexpr int OFF_PART = A_BYTES;                                  // float2 [NSLOT][MAXRUN]
+constexpr int OFF_RES = OFF_PART + NSLOT * MAXRUN * 8;             // float [4][MAX_RES]: x rows a, b; y rows a, b
+constexpr int OFF_ROPE = OFF_RES + 4 * MAX_RES * 4;                // float2 [HD / 2]
+constexpr int OFF_KG = OFF_ROPE + (HD / 2) * 8;                    // KGeo [4]
+constexpr int OFF_SG = OFF_KG + 4 * (int)sizeof(KGeo);             // SGeo [4][NSLOT]
+constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [NWAVE]
+constexpr int OFF_TAB = ((OFF_RED + NWAVE * 4 + 255) / 256) * 256; // LPtr [L]
+constexpr size_t lds_bytes(int L) { return (size_t)OFF_TAB + (size_t)L * sizeof(LPtr); }
+
+// ------------------------------------------------------------------ helpers
+typedef u64 u64x2 __attribute__((ext_vector_type(2)));
+
+template <class T> I4D_DEVINL T* uni(T* p) {        // a pointer every lane holds equally, in scalar registers
+    const u64 v = (u64)p;
+    const u32 lo = __builtin_amdgcn_readfirstlane((u32)v), hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
+    return (T*)(((u64)hi << 32) | lo);
+}
+I4D_DEVINL int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+I4D_DEVINL unsigned uniu(unsigned v) { return (unsigned)__builtin_amdgcn_readfirstlane((int)v); }
+
+// An opaque copy of the pointer to the launch arguments, in the constant
+// address space: fields read through it are re-read (scalar loads) where
+// they are used instead of being hoisted out of the layer loop into registers
+// that would stay live across every phase.
+template <class T> I4D_DEVINL const I4D_CONST T* opaque_ptr(const T* p) {
+    const I4D_CONST T* c = (const I4D_CONST T*)p;
+    asm volatile("" : "+s"(c));
+    return c;
+}
+
+// Base of layer l's exchange region, from an opaque read of the arguments.
+I4D_DEVINL char* layer_region(const struct Args* Ap, int l) {
+    const I4D_CONST Args& a = *opaque_ptr(Ap);
+    return a.lbase + (size_t)l * a.lstride;
+}
+
+I4D_DEVINL void ll_put(u64* p, float v, u32 tag) { st_dev_t(p, ((u64)tag << 32) | (u64)__float_as_uint(v)); }
+
+struct Spin {
+    int* status;
+    bool dead;                   // this thread gave up waiting once: it no longer waits
+};
+
+// N consecutive exchange words from p (16-byte aligned, N even): plain loads,
+// then device-scope reloads of every word whose tag is not `tag` (bounded).
+template <int N>
+I4D_DEVINL void ll_get(const u64* p, u32 tag, float (&v)[N], Spin& sp) {
+    u64 w[N];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const u64x2 t = ld_g((const u64x2*)p + i);
+        w[2 * i] = t.x;
+        w[2 * i + 1] = t.y;
+    }
+    int polls = 0;
+    for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < N; ++i) ok = ok && (u32)(w[i] >> 32) == tag;
+        if (ok || sp.dead) break;
+        if (++polls > SPIN_LIMIT) {
+            sp.dead = true;
+            raise_status(sp.status, I4D_DEV_BARRIER_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((u32)(w[i] >> 32) != tag) w[i] = ld_dev_t(p + i);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __uint_as_float((u32)w[i]);
+}
+
+// The wide activations (o, y, act) travel as packed 32-bit words: the fp32
+// value rounded to 15 mantissa bits (round to nearest even; the staging keeps
+// 15 bits relative to each 32-input run's largest value anyway) in the upper
+// 24 bits, the low 8 bits of the launch tag below (a word left by an earlier
+// launch carries another tag byte).
+I4D_DEVINL u32 pk_word(float v, u32 tag) {
+    u32 u = __float_as_uint(v);
+    u += 0x7Fu + ((u >> 8) & 1u);
+    return (u & 0xFFFFFF00u) | (tag & 0xFFu);
+}
+I4D_DEVINL void pk_put(u32* p, float v, u32 tag) { st_dev_t(p, pk_word(v, tag)); }
+I4D_DEVINL float pk_val(u32 w) { return __uint_as_float(w & 0xFFFFFF00u); }
+
+// This thread's input groups g = tid + r * NT (r < RM; groups past ngr read
+// the last group again) from an exchange vector: all plain loads first (one
+// memory round trip for the lot), then device-scope reloads of the words whose
+// tag is not yet current, until every tag is (bounded).  WIDE: 64-bit words (value, 32-bit
+// tag); otherwise packed 32-bit words.
+template <int RM, bool WIDE>
+I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8], Spin& sp) {
+    const int tid = i4d_tid();
+    if constexpr (WIDE) {
+        const u64* p = (const u64*)src;
+        u64 w[RM][8];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int g = min(tid + r * NT, ngr - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u64x2 t = ld_g((const u64x2*)(p + 8 * (size_t)g) + i);
+                w[r][2 * i] = t.x; w[r][2 * i + 1] = t.y;
+            }
+        }
+        for (int polls = 0;;) {
+            bool ok = true;
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ok = ok && (u32)(w[r][e] >> 32) == tag;
+            if (ok || sp.dead) break;
+            if (++polls > SPIN_LIMIT) { sp.dead = true; raise_status(sp.status, I4D_DEV_BARRIER_TIMEOUT); break; }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int g = min(tid + r * NT, ngr - 1);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((u32)(w[r][e] >> 32) != tag) w[r][e] = ld_dev_t(p + 8 * (size_t)g + e);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[r][e] = __uint_as_float((u32)w[r][e]);
+    } else {
+        const u32* p = (const u32*)src;
+        const u32 t8 = tag & 0xFFu;
+        u32 w[RM][8];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int g = min(tid + r * NT, ngr - 1);
+            const u32x4 a = ld_g((const u32x4*)(p + 8 * (size_t)g)), b = ld_g((const u32x4*)(p + 8 * (size_t)g) + 1);
+            w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+            w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
+        }
+        for (int polls = 0;;) {
+            bool ok = true;
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ok = ok && (w[r][e] & 0xFFu) == t8;
+            if (ok || sp.dead) break;
+            if (++polls > SPIN_LIMIT) { sp.dead = true; raise_status(sp.status, I4D_DEV_BARRIER_TIMEOUT); break; }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int g = min(tid + r * NT, ngr - 1);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2)
+                    if ((w[r][e] & 0xFFu) != t8 || (w[r][e + 1] & 0xFFu) != t8) {
+                        const u64 t = ld_dev_t((const u64*)(p + 8 * (size_t)g + e));
+                        w[r][e] = (u32)t; w[r][e + 1] = (u32)(t >> 32);
+                    }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[r][e] = pk_val(w[r][e]);
+    }
+}
+
+// ------------------------------------------------------------------ weight units
+struct Unit { u32x4 a, b; u32 sa, sb; };
+
+// The lane's stream of weight units over all matrix-vector phases of the
+// step, RD units ahead of the consumer.
+struct Loader {
+    const uint8_t* ca; const uint8_t* cb; const uint8_t* sa; const uint8_t* sb;   // scalar bases
+    unsigned off, soff, jump, jumps;
+    int cnt, jper, len, j, n, ph, nph;
+};
+
+I4D_DEVINL void loader_next(Loader& Ld, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero, int slot) {
+    do { ++Ld.ph; } while (Ld.ph < Ld.nph && kg[Ld.ph & 3].n == 0);
+    if (Ld.ph >= Ld.nph) {       // past the last phase: repeat reads of a zero block, never consumed
+        Ld.ca = Ld.cb = Ld.sa = Ld.sb = uni(zero);
+        Ld.n = 0x7FFFFFFF; Ld.j = 0; Ld.len = 0; Ld.jper = 0; Ld.cnt = 1 << 30;
+        Ld.off = Ld.soff = 0; Ld.jump = Ld.jumps = 0;
+        return;
+    }
+    const int kind = Ld.ph & 3, l = Ld.ph >> 2;
+    const KGeo& k = kg[kind];
+    const LPtr& t = tab[l];
+    Ld.ca = uni(t.c[k.mia] + k.ca_off);
+    Ld.cb = uni(t.c[k.mib] + k.cb_off);
+    Ld.sa = uni(t.s[k.mia] + k.sa_off);
+    Ld.sb = uni(t.s[k.mib] + k.sb_off);
+    Ld.n = uni(k.n); Ld.j = 0;
+    Ld.jump = uniu(k.jump); Ld.jumps = uniu(k.jumps); Ld.jper = uni(k.jper);
+    const SGeo& s = sg[kind * NSLOT + slot];
+    const int lane16 = i4d_tid() & 15;
+    Ld.len = s.len; Ld.cnt = s.cnt0;
+    Ld.off = s.off0 + (unsigned)lane16 * 16u;
+    Ld.soff = s.soff0 + 4u * (unsigned)(lane16 >> 3);
+}
+
+// Issue the loads of the next unit into u (always the same four loads, so
+// the compiler's wait counts stay exact) and advance.
+I4D_DEVINL void loader_load(Loader& Ld, Unit& u, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero, int slot) {
+    if (Ld.j == Ld.n) loader_next(Ld, kg, sg, tab, zero, slot);
+    const bool v = Ld.j < Ld.len;
+    // a skipped unit reads the slot's first 16 bytes and scale word again
+    const unsigned lane16 = (unsigned)i4d_tid() & 15u;
+    const unsigned o = v ? Ld.off : lane16 * 16u;
+    const unsigned so = v ? Ld.soff : 4u * (lane16 >> 3);
+    u.a = ld_g_nt((const u32x4*)(Ld.ca + o));
+    u.b = ld_g_nt((const u32x4*)(Ld.cb + o));
+    u.sa = ld_g((const u32*)(Ld.sa + so));
+    u.sb = ld_g((const u32*)(Ld.sb + so));
+    if (v) {
+        Ld.off += 256u;
+        Ld.soff += 8u;
+        if (--Ld.cnt == 0) { Ld.off += Ld.jump; Ld.soff += Ld.jumps; Ld.cnt = Ld.jper; }
+    }
+    ++Ld.j;
+}
+
+// ------------------------------------------------------------------ the dot product of one unit
+// Digit planes 0..3 at act + p * PS; for the q/k/v projection (six planes,
+// K <= 8192 so each plane fills at most half of its slot) planes 4 and 5 sit
+// in the upper halves of slots 0 and 1.
+constexpr int P4 = PS / 2, P5 = PS + PS / 2;
+
+I4D_DEVINL void dot_unit(const Unit& u, const char* act, unsigned aoff, float cs, int hs, bool six, float& ra, float& rb) {
+    const u32x4 d0 = *(const u32x4*)(act + aoff);
+    const u32x4 d1 = *(const u32x4*)(act + PS + aoff);
+    const u32x4 d2 = *(const u32x4*)(act + 2 * PS + aoff);
+    const u32x4 d3 = *(const u32x4*)(act + 3 * PS + aoff);
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int wa = (int)(u.a[q] ^ 0x88888888u), wb = (int)(u.b[q] ^ 0x88888888u);
+        a0 = __builtin_amdgcn_sdot8(wa, (int)d0[q], a0, false);
+        a1 = __builtin_amdgcn_sdot8(wa, (int)d1[q], a1, false);
+        a2 = __builtin_amdgcn_sdot8(wa, (int)d2[q], a2, false);
+        a3 = __builtin_amdgcn_sdot8(wa, (int)d3[q], a3, false);
+        b0 = __builtin_amdgcn_sdot8(wb, (int)d0[q], b0, false);
+        b1 = __builtin_amdgcn_sdot8(wb, (int)d1[q], b1, false);
+        b2 = __builtin_amdgcn_sdot8(wb, (int)d2[q], b2, false);
+        b3 = __builtin_amdgcn_sdot8(wb, (int)d3[q], b3, false);
+    }
+    int ia = ((a3 * 16 + a2) * 16 + a1) * 16 + a0;
+    int ib = ((b3 * 16 + b2) * 16 + b1) * 16 + b0;
+    if (six) {
+        const u32x4 d4 = *(const u32x4*)(act + P4 + aoff);
+        const u32x4 d5 = *(const u32x4*)(act + P5 + aoff);
+        int a4 = 0, a5 = 0, b4 = 0, b5 = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int wa = (int)(u.a[q] ^ 0x88888888u), wb = (int)(u.b[q] ^ 0x88888888u);
+            a4 = __builtin_amdgcn_sdot8(wa, (int)d4[q], a4, false);
+            a5 = __builtin_amdgcn_sdot8(wa, (int)d5[q], a5, false);
+            b4 = __builtin_amdgcn_sdot8(wb, (int)d4[q], b4, false);
+            b5 = __builtin_amdgcn_sdot8(wb, (int)d5[q], b5, false);
+        }
+        // |sum (c - 8) a| < 32 * 8 * 2^22 = 2^30: exact in int32 (the Horner
+        // steps may wrap, the two's-complement result does not)
+        ia = (int)((u32)(a5 * 16 + a4) * 65536u + (u32)ia);
+        ib = (int)((u32)(b5 * 16 + b4) * 65536u + (u32)ib);
+    }
+    const float sa = __uint_as_float((u.sa << hs) & 0xFFFF0000u);
+    const float sb = __uint_as_float((u.sb << hs) & 0xFFFF0000u);
+    ra = fmaf((float)ia, sa * cs, ra);
+    rb = fmaf((float)ib, sb * cs, rb);
+}
+
+// ------------------------------------------------------------------ activation staging
+// Eight inputs of group g (inputs 8g..8g+7), already normalised: digits into
+// the four planes, the power of two of the 32-input run (a quad of lanes) into
+// cs.  Non-finite inputs become zeros and raise I4D_DEV_NONFINITE.
+I4D_DEVINL void digitize8(char* act, float* cs, int g, float (&v)[8], bool six, int* status) {
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = fmaxf(m, shfl_xor_f(m, 1));
+    m = fmaxf(m, shfl_xor_f(m, 2));
+    if (!(m <= 3.0e38f)) {           // inf or NaN somewhere in the run
+        if ((i4d_tid() & 3) == 0) raise_status(status, I4D_DEV_NONFINITE);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        m = 0.f;
+    }
+    int ex;
+    (void)frexpf(m, &ex);            // m < 2^ex (m = 0: ex = 0)
+    // four planes: |a| <= 2^14, digits of a + 0x8888; six: |a| <= 2^22, of a + 0x888888
+    const int sh = (six ? 22 : 14) - ex;
+    const u32 bias = six ? 0x888888u : 0x8888u;
+    u32 pl[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int a = (int)rintf(ldexpf(v[e], sh));
+        const u32 dg = ((u32)a + bias) ^ bias;                 // digit p in nibble p
+#pragma unroll
+        for (int q = 0; q < 6; ++q) pl[q] |= ((dg >> (4 * q)) & 15u) << (4 * e);
+    }
+    u32* p = (u32*)act + g;
+    p[0] = pl[0];
+    p[PS / 4] = pl[1];
+    p[2 * PS / 4] = pl[2];
+    p[3 * PS / 4] = pl[3];
+    if (six) {
+        p[P4 / 4] = pl[4];
+        p[P5 / 4] = pl[5];
+    }
+    if ((i4d_tid() & 3) == 0) cs[g >> 2] = ldexpf(1.f, -sh);
+}
+
+// Sum of one value over the workgroup (every thread gets it).
+I4D_DEVINL float block_sum(float v, float* red) {
+    for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+    if ((i4d_tid() & 63) == 0) red[i4d_tid() >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) t += red[w];
+    __syncthreads();
+    return t;
+}
+
+// ------------------------------------------------------------------ the kernel
+__global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ Ap) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const I4D_CONST Args& A = *(const I4D_CONST Args*)Ap;
+    const int tid = i4d_tid();
+    const int c = blockIdx.x, nwg = gridDim.x;
+    char* act = lds;                                  // digit planes
+    float* cs = (float*)(lds + 4 * PS);               // run scales
+    float2* part = (float2*)(lds + OFF_PART);
+    float* res = (float*)(lds + OFF_RES);
+    float2* rope = (float2*)(lds + OFF_ROPE);
+    KGeo* kg = (KGeo*)(lds + OFF_KG);
+    SGeo* sg = (SGeo*)(lds + OFF_SG);
+    float* red = (float*)(lds + OFF_RED);
+    LPtr* tab = (LPtr*)(lds + OFF_TAB);
+    Spin sp{A.status, false};
+    const u32 tag = ld_g(A.epoch) + 1u;
+    const int D = A.D, F = A.F, qw = A.Hq * HD, kvw = A.Hkv * HD;
+
+    // ---- set-up: layer table, position and RoPE table, geometry, residual rows
+    for (int i = tid; i < A.L * LPTR_WORDS; i += NT) ((u64*)tab)[i] = ld_g((const u64*)A.table + i);
+    int p = ld_g(A.pos);
+    if (p < 0 || p > A.max_pos || p >= A.cap) {
+        if (c == 0 && tid == 0) raise_status(A.status, I4D_DEV_BAD_POS);
+        p = -1;
+    }
+    if (tid < HD / 2) {
+        const double theta = pow(A.base, -2.0 * (double)tid / (double)HD);
+        const double phi = (double)max(p, 0) * theta;
+        rope[tid] = float2{(float)cos(phi), (float)sin(phi)};
+    }
+    if (tid < 4) {
+        KGeo k;
+        const int kind = tid;
+        int P, ci, nci, rows_half;
+        k.K = kind == K_WO ? qw : kind == K_DN ? F : D;
+        k.mat = 0; k.jump = k.jumps = 0u; k.jper = 0;
+        if (kind == K_QKV) {
+            k.mat = c < A.cq ? 0 : c < A.ck ? 1 : 2;
+            P = (k.mat == 0 ? qw : kvw) / 2;
+            ci = k.mat == 0 ? c : k.mat == 1 ? c - A.cq : c - A.ck;
+            nci = k.mat == 0 ? A.cq : k.mat == 1 ? A.ck - A.cq : nwg - A.ck;
+            k.mia = k.mib = k.mat;
+        } else {
+            P = kind == K_GU ? F : D / 2;
+            ci = c; nci = nwg;
+            k.mia = kind == K_WO ? 3 : kind == K_GU ? 4 : 6;
+            k.mib = kind == K_GU ? 5 : k.mia;
+        }
+        k.S = k.K / 512;
+        k.p0 = (int)(((long long)ci * P) / nci);
+        k.np = (int)(((long long)(ci + 1) * P) / nci) - k.p0;
+        k.U = k.np * k.S;
+        k.n = (k.U + NSLOT - 1) / NSLOT;
+        const unsigned rb = (unsigned)k.K / 2u, srb = (unsigned)k.K / 64u;
+        if (kind == K_QKV) {
+            const int row0 = (k.p0 / (HD / 2)) * HD + k.p0 % (HD / 2);
+            k.ca_off = (unsigned)row0 * rb; k.cb_off = k.ca_off + (unsigned)(HD / 2) * rb;
+            k.sa_off = (unsigned)row0 * srb; k.sb_off = k.sa_off + (unsigned)(HD / 2) * srb;
+            k.jump = (unsigned)(HD / 2) * rb; k.jumps = (unsigned)(HD / 2) * srb;
+            k.jper = (HD / 2) * k.S;
+        } else {
+            rows_half = kind == K_GU ? 0 : D / 2;
+            k.ca_off = (unsigned)k.p0 * rb; k.cb_off = (unsigned)(k.p0 + rows_half) * rb;
+            k.sa_off = (unsigned)k.p0 * srb; k.sb_off = (unsigned)(k.p0 + rows_half) * srb;
+        }
+        kg[kind] = k;
+    }
+    __syncthreads();
+    if (tid < 4 * NSLOT) {
+        const int kind = tid / NSLOT, s = tid % NSLOT;
+        const KGeo& k = kg[kind];
+        SGeo g;
+        g.u0 = (int)(((long long)s * k.U) / NSLOT);
+        g.len = (int)(((long long)(s + 1) * k.U) / NSLOT) - g.u0;
+        const int pl = k.S ? g.u0 / k.S : 0;
+        g.seg0 = g.u0 - pl * k.S;
+        g.pair0 = pl;
+        const unsigned rb = (unsigned)k.K / 2u, srb = (unsigned)k.K / 64u;
+        int drow = pl;                                   // rows between pair p0's row a and this slot's first row a
+        g.cnt0 = 1 << 30;
+        if (kind == K_QKV) {
+            const int pa = k.p0 + pl;
+            drow = ((pa / (HD / 2)) * HD + pa % (HD / 2)) - ((k.p0 / (HD / 2)) * HD + k.p0 % (HD / 2));
+            g.cnt0 = (HD / 2 - pa % (HD / 2)) * k.S - g.seg0;
+        }
+        g.off0 = (unsigned)drow * rb + (unsigned)g.seg0 * 256u;
+        g.soff0 = (unsigned)drow * srb + (unsigned)g.seg0 * 8u;
+        sg[tid] = g;
+    }
+    __syncthreads();
+    {   // residual rows of layer 0 (rows p and p + D/2 of this unit's Wo / W_down pairs)
+        const KGeo& k = kg[K_WO];
+        for (int i = tid; i < k.np; i += NT) {
+            res[i] = ld_g(A.x_in + k.p0 + i);
+            res[MAX_RES + i] = ld_g(A.x_in + k.p0 + i + D / 2);
+        }
+    }
+    __syncthreads();
+
+    // ---- prime the weight ring
+    Loader Ld;
+    Ld.ph = -1; Ld.nph = 4 * A.L; Ld.j = 0; Ld.n = 0;
+    Unit ring[RD];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) loader_load(Ld, ring[i], kg, sg, tab, A.zero, tid >> 4);
+    int rot = 0;                                         // ring rotation owed by the last consumed phase
+
+    for (int ph = 0; ph < 4 * Ap->L; ++ph) {
+        const I4D_CONST Args& A = *opaque_ptr(Ap);
+        const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6, slot = tid >> 4, lane16 = tid & 15;
+        const int kind = ph & 3, l = ph >> 2;
+        const int D = A.D, F = A.F, G = A.Hq / A.Hkv;
+        // Exchange pointers of this layer, re-derived where used (see opaque_ptr)
+#define I4D_RP(T, field) ((T*)(layer_region(Ap, l) + opaque_ptr(Ap)->field))
+
+        if (kind == K_WO) {
+            // ================= attention: item (KV head j, split s) of this unit
+            const int items = A.Hkv * A.nsplit;
+            if (c < items) {
+                AttnArgs a;
+                memset(&a, 0, sizeof(a));
+                a.kc = tab[l].kc; a.vc = tab[l].vc; a.pos = A.pos;
+                a.cap = A.cap; a.hq = A.Hq; a.hkv = A.Hkv; a.batch = 1; a.max_pos = A.max_pos;
+                a.kvb = 1; a.nsplit = A.nsplit; a.T = A.T; a.qscale = A.qscale;
+                const AttnGeo g = attn_geo(a, c);
+                AttnRegs<HD, ANSW> Rg;
+                attn_load_round<HD, NT, ANSW>(a, g, 0, Rg);
+                s4* qop = (s4*)(lds + NWAVE * (16 * HD + 32) * 4);
+                uint16_t* knew = (uint16_t*)(lds + ATT_LDS);
+                uint16_t* vnew = knew + HD;
+                const int r = lane & 15, gq = lane >> 4;
+                if (wave == 0) {
+                    // q^T operand of head r of the group, one 4-dim block at a time (attn_q_operand's layout)
+                    const u64* qrow = I4D_RP(u64, oq) + (size_t)(g.j * G + min(r, G - 1)) * HD + 8 * gq;
+                    const float qs = (r < G) ? A.qscale : 0.f;
+#pragma unroll 1
+                    for (int kb = 0; kb < HD / 16; ++kb) {
+                        float t4[4];
+                        ll_get<4>(qrow + 32 * (kb >> 1) + 4 * (kb & 1), tag, t4, sp);
+                        uint16_t hv[4], lv[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float v = t4[q] * qs;
+                            hv[q] = f32_to_bf16(v);
+                            lv[q] = f32_to_bf16(v - bf16_to_f32(hv[q]));
+                        }
+                        qop[(2 * kb) * 64 + lane] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+                        qop[(2 * kb + 1) * 64 + lane] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
+                    }
+                } else if (wave <= 2) {
+                    float t2[2];
+                    ll_get<2>(I4D_RP(u64, okv) + (size_t)g.j * 2 * HD + (wave - 1) * HD + 2 * lane, tag, t2, sp);
+                    uint16_t* dst = wave == 1 ? knew : vnew;
+                    dst[2 * lane] = f32_to_bf16(t2[0]);          // the values are bf16 already: exact
+                    dst[2 * lane + 1] = f32_to_bf16(t2[1]);
+                }
+                __syncthreads();
+                const int stp = (g.kpos >= g.t_s && g.kpos < g.t_e) ? (g.kpos - g.t_s) / 16 : -1;
+                float m = -INFINITY, lsum = 0.f;
+                f4 O[HD / 16];
+#pragma unroll
+                for (int nt = 0; nt < HD / 16; ++nt) O[nt] = f4{0.f, 0.f, 0.f, 0.f};
+                const int nround = (g.nsub + NWAVE * ANSW - 1) / (NWAVE * ANSW);
+                for (int rnd = 0; rnd < nround; ++rnd) {
+                    if (rnd > 0) attn_load_round<HD, NT, ANSW>(a, g, rnd, Rg);
+#pragma unroll
+                    for (int i = 0; i < ANSW; ++i) {
+                        const int st = (rnd * ANSW + i) * NWAVE + wave;
+                        if (st == stp) {
+                            // the new key: its K row and V column from the exchange, not the cache
+                            const int t0 = g.t_s + 16 * st;
+                            if (t0 + r == g.kpos) {
+#pragma unroll
+                                for (int mm = 0; mm < HD / 32; ++mm) Rg.k[i][mm] = *(const u32x4*)(knew + 32 * mm + 8 * gq);
+                            }
+                            const int e = g.kpos - (t0 + 4 * gq);
+                            if (e >= 0 && e < 4) {
+#pragma unroll
+                                for (int nt = 0; nt < HD / 16; ++nt) {
+                                    const u32 nv = (u32)vnew[16 * nt + r];
+                                    u32 lo = Rg.v[i][nt].x, hi = Rg.v[i][nt].y;
+                                    if (e == 0) lo = (lo & 0xFFFF0000u) | nv;
+                                    else if (e == 1) lo = (lo & 0x0000FFFFu) | (nv << 16);
+                                    else if (e == 2) hi = (hi & 0xFFFF0000u) | nv;
+                                    else hi = (hi & 0x0000FFFFu) | (nv << 16);
+                                    Rg.v[i][nt] = u32x2{lo, hi};
+                                }
+                            }
+                        }
+                        if (st < g.nsub) attn_sub<HD>(g, st, Rg.k[i], Rg.v[i], qop, m, lsum, O);
+                    }
+                }
+                attn_waves_to_lds<HD, NT>(lds, m, lsum, O);
+                __syncthreads();
+                const int ns = A.nsplit, hb = g.j * G;
+                auto put = [&](int h, int d, float M, float Lv, float acc) {
+                    u64* pr = I4D_RP(u64, opart) + ((size_t)(hb + h) * ns + g.s) * (HD + 2);
+                    ll_put(pr + 2 + d, acc, tag);
+                    if (d == 0) { ll_put(pr, M, tag); ll_put(pr + 1, Lv, tag); }
+                };
+                attn_combine_waves<HD, NT>(lds, G, put);
+            }
+            // ================= merge: head h, dims 32 qd .. 32 qd + 31 of this unit
+            for (int it = c; it < A.Hq * 4; it += nwg) {
+                const int h = it >> 2, qd = it & 3, ns = A.nsplit;
+                float* mv = (float*)lds;                        // [ns]
+                float* lv = mv + 64;                            // [ns]
+                float* ov = lv + 64;                            // [ns][32]
+                const u64* hp = I4D_RP(u64, opart) + (size_t)h * ns * (HD + 2);
+                // one round: thread (s, q) fetches dims 2q, 2q + 1 of split s; threads of q = 0 also m and l
+                for (int idx = tid; idx < ns * 16; idx += NT) {
+                    const int s = idx >> 4, q = idx & 15;
+                    float t2[2];
+                    ll_get<2>(hp + (size_t)s * (HD + 2) + 2 + 32 * qd + 2 * q, tag, t2, sp);
+                    ov[s * 32 + 2 * q] = t2[0];
+                    ov[s * 32 + 2 * q + 1] = t2[1];
+                    if (q == 0) {
+                        ll_get<2>(hp + (size_t)s * (HD + 2), tag, t2, sp);
+                        mv[s] = t2[0];
+                        lv[s] = t2[1];
+                    }
+                }
+                __syncthreads();
+                if (tid < 32) {
+                    float M = -INFINITY;
+                    for (int s = 0; s < ns; ++s) M = fmaxf(M, mv[s]);
+                    float Lsum = 0.f, acc = 0.f;
+                    if (M != -INFINITY) {
+                        for (int s = 0; s < ns; ++s) {
+                            const float w = exp2f(mv[s] - M);
+                            Lsum = fmaf(lv[s], w, Lsum);
+                            acc = fmaf(ov[s * 32 + tid], w, acc);
+                        }
+                    }
+                    pk_put((u32*)I4D_RP(u64, oo) + (size_t)h * HD + 32 * qd + tid, Lsum > 0.f ? acc / Lsum : 0.f, tag);
+                }
+                __syncthreads();
+            }
+        }
+
+        // ================= stage this phase's activations (digits in LDS)
+        const KGeo& k = kg[kind];
+        {
+            const int K = k.K, ngr = K / 8;
+            const bool six = kind == K_QKV;
+            // normalised inputs (x, y: K = D <= 8192, two rounds of groups): RMSNorm, then digits
+            auto norm_stage = [&](float (&v)[2][8], const uint16_t* gain) {
+                float ss = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+                    if (rr * NT + tid < ngr)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ss = fmaf(v[rr][e], v[rr][e], ss);
+                const float rs = 1.0f / sqrtf(block_sum(ss, red) / (float)K + A.eps);
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int g = rr * NT + tid;
+                    if (g < ngr) {
+                        const u32x4 gw = ld_g((const u32x4*)(gain + 8 * g));
+                        const u32 gws[4] = {gw.x, gw.y, gw.z, gw.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[rr][e] *= rs * __uint_as_float((e & 1) ? (gws[e >> 1] & 0xFFFF0000u) : (gws[e >> 1] << 16));
+                        digitize8(act, cs, g, v[rr], six, A.status);
+                    }
+                }
+            };
+            if (kind == K_QKV) {
+                float v[2][8];
+                if (l == 0) {                                  // the caller's fp32 input
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const int g = min(rr * NT + tid, ngr - 1);
+                        const f4 a0 = ld_g((const f4*)(A.x_in + 8 * g)), a1 = ld_g((const f4*)(A.x_in + 8 * g + 4));
+                        v[rr][0] = a0.x; v[rr][1] = a0.y; v[rr][2] = a0.z; v[rr][3] = a0.w;
+                        v[rr][4] = a1.x; v[rr][5] = a1.y; v[rr][6] = a1.z; v[rr][7] = a1.w;
+                    }
+                } else {
+                    fetch_groups<2, true>(I4D_RP(u64, ox), ngr, tag, v, sp);
+                }
+                norm_stage(v, tab[l].g1);
+            } else if (kind == K_GU) {
+                float v[2][8];
+                fetch_groups<2, false>(I4D_RP(u64, oy), ngr, tag, v, sp);
+                norm_stage(v, tab[l].g2);
+            } else if (kind == K_WO) {
+                float v[2][8];                                 // q width <= 8192
+                fetch_groups<2, false>(I4D_RP(u64, oo), ngr, tag, v, sp);
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+                    if (rr * NT + tid < ngr) digitize8(act, cs, rr * NT + tid, v[rr], false, A.status);
+            } else {
+                float v[8][8];                                 // d_ff <= 32768
+                fetch_groups<8, false>(I4D_RP(u64, oact), ngr, tag, v, sp);
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr)
+                    if (rr * NT + tid < ngr) digitize8(act, cs, rr * NT + tid, v[rr], false, A.status);
+            }
+        }
+        __syncthreads();
+
+        // ================= stream this phase's weights through the ring
+        {
+            if (rot == 1) { const Unit t = ring[0]; ring[0] = ring[1]; ring[1] = ring[2]; ring[2] = ring[3]; ring[3] = t; }
+            else if (rot == 2) { Unit t = ring[0]; ring[0] = ring[2]; ring[2] = t; t = ring[1]; ring[1] = ring[3]; ring[3] = t; }
+            else if (rot == 3) { const Unit t = ring[3]; ring[3] = ring[2]; ring[2] = ring[1]; ring[1] = ring[0]; ring[0] = t; }
+            const int n = uni(k.n), S = k.S;
+            const SGeo& s = sg[kind * NSLOT + slot];
+            const int len = s.len;
+            int seg = s.seg0, run = 0;
+            unsigned aoff = (unsigned)seg * 256u + (unsigned)lane16 * 16u;
+            const int hs = ((lane16 >> 2) & 1) ? 0 : 16;
+            const bool six = kind == K_QKV;
+            float ra = 0.f, rb = 0.f;
+            auto step = [&](Unit& u, int j) {
+                if (j < len) {
+                    dot_unit(u, act, aoff, cs[aoff >> 4], hs, six, ra, rb);
+                    ++seg;
+                    aoff += 256u;
+                    const bool wrap = seg == S;
+                    if (wrap || j == len - 1) {
+                        const float va = row16_sum(ra), vb = row16_sum(rb);
+                        if (lane16 == 0 && run < MAXRUN) part[slot * MAXRUN + run] = float2{va, vb};
+                        ++run;
+                        ra = 0.f; rb = 0.f;
+                    }
+                    if (wrap) { seg = 0; aoff = (unsigned)lane16 * 16u; }
+                }
+                loader_load(Ld, u, kg, sg, tab, A.zero, slot);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            int j = 0;
+            for (; j + RD <= n; j += RD) {
+#pragma unroll
+                for (int i = 0; i < RD; ++i) step(ring[i], j + i);
+            }
+#pragma unroll
+            for (int i = 0; i < RD; ++i)
+                if (j + i < n) step(ring[i], j + i);
+            rot = n % RD;
+        }
+        __syncthreads();
+
+        // ================= per-pair totals (fixed slot order) and the phase's epilogue
+        for (int pl = tid; pl < k.np; pl += NT) {
+            const int S = k.S, U = k.U;
+            float va = 0.f, vb = 0.f;
+            // the slots whose unit ranges meet this pair's units [pl S, (pl + 1) S), in slot order
+            int s = min(NSLOT - 1, (pl * S * NSLOT) / U);
+            while (s > 0 && sg[kind * NSLOT + s].u0 > pl * S) --s;
+            for (; s < NSLOT; ++s) {
+                const SGeo& q = sg[kind * NSLOT + s];
+                if (q.u0 >= (pl + 1) * S) break;
+                if (q.len == 0 || q.u0 + q.len <= pl * S) continue;     // an empty slot wrote nothing
+                const float2 t = part[s * MAXRUN + (pl - q.pair0)];
+                va += t.x;
+                vb += t.y;
+            }
+            const int pm = k.p0 + pl;                          // pair index within its matrix
+            if (kind == K_QKV) {
+                const int head = pm / (HD / 2), i = pm % (HD / 2);
+                float xa = va, xb = vb;
+                if (k.mat < 2) {
+                    const float2 rc = rope[i];
+                    xa = va * rc.x - vb * rc.y;
+                    xb = va * rc.y + vb * rc.x;
+                }
+                if (k.mat == 0) {
+                    ll_put(I4D_RP(u64, oq) + (size_t)head * HD + i, xa, tag);
+                    ll_put(I4D_RP(u64, oq) + (size_t)head * HD + i + HD / 2, xb, tag);
+                } else {
+                    const uint16_t ba = f32_to_bf16(xa), bb = f32_to_bf16(xb);
+                    u64* nr = I4D_RP(u64, okv) + (size_t)head * 2 * HD + (k.mat - 1) * HD;
+                    ll_put(nr + i, bf16_to_f32(ba), tag);
+                    ll_put(nr + i + HD / 2, bf16_to_f32(bb), tag);
+                    if (p >= 0) {
+                        const size_t tile = ((size_t)head * A.cap + (size_t)(p >> 4) * 16) * HD;
+                        const int tp = p & 15;
+                        if (k.mat == 1) {
+                            uint16_t* kt = tab[l].kc + tile;
+                            st_g(kt + (i >> 5) * 512 + tp * 32 + (i & 31), ba);
+                            st_g(kt + ((i + HD / 2) >> 5) * 512 + tp * 32 + ((i + HD / 2) & 31), bb);
+                        } else {
+                            uint16_t* vt = tab[l].vc + tile;
+                            st_g(vt + (size_t)i * 16 + tp, ba);
+                            st_g(vt + (size_t)(i + HD / 2) * 16 + tp, bb);
+                        }
+                    }
+                }
+            } else if (kind == K_WO) {
+                const float ya = res[pl] + va, yb = res[MAX_RES + pl] + vb;
+                res[2 * MAX_RES + pl] = ya;
+                res[3 * MAX_RES + pl] = yb;
+                pk_put((u32*)I4D_RP(u64, oy) + pm, ya, tag);
+                pk_put((u32*)I4D_RP(u64, oy) + pm + D / 2, yb, tag);
+            } else if (kind == K_GU) {
+                pk_put((u32*)I4D_RP(u64, oact) + pm, va / (1.0f + expf(-va)) * vb, tag);
+            } else {
+                const float za = res[2 * MAX_RES + pl] + va, zb = res[3 * MAX_RES + pl] + vb;
+                res[pl] = za;
+                res[MAX_RES + pl] = zb;
+                if (l + 1 == A.L) {
+                    st_g(A.x_out + pm, za);
+                    st_g(A.x_out + pm + D / 2, zb);
+                } else {
+                    u64* xn = (u64*)(A.lbase + (size_t)(l + 1) * A.lstride + A.ox);
+                    ll_put(xn + pm, za, tag);
+                    ll_put(xn + pm + D / 2, zb, tag);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#undef I4D_RP
+    wait_stores();
+    // every workgroup read the epoch before any of them could finish (each
+    // waits for data from all others), so the next launch's epoch goes out now
+    if (c == 0 && tid == 0) st_dev_t(A.epoch, tag);
+}
+
+// The launch arguments, passed by value, into the workspace (the kernel reads
+// them through a pointer, re-reading fields where they are used).
+__global__ void __launch_bounds__(64) k_fill_args(Args a, Args* dst) {
+    constexpr int W = (int)(sizeof(Args) / 8);
+    for (int i = i4d_tid(); i < W; i += 64) ((u64*)dst)[i] = ((const u64*)&a)[i];
+}
+
+// Copy a chunk of layer-table entries (passed by value) into the workspace.
+constexpr int LPTR_PER_FILL = 24;
+struct LPtrChunk { LPtr e[LPTR_PER_FILL]; LPtr* dst; int count; };
+__global__ void __launch_bounds__(64) k_fill_ltab(LPtrChunk ch) {
+    const int words = ch.count * LPTR_WORDS;
+    for (int i = i4d_tid(); i < words; i += 64) ((u64*)ch.dst)[i] = ((const u64*)ch.e)[i];
+}
+
+// ------------------------------------------------------------------ host side
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Region {
+    size_t args, table, zero, layer0, lstride;
+    size_t ox, oq, okv, opart, oo, oy, oact;
+    size_t total;
+};
+
+// Key-axis splits per KV head: one attention item per compute unit, at most
+// 64 (the merge stages one head's partials of every split in LDS).
+int splits_of(const i4d_config* c, int nwg) { return std::max(1, std::min(64, nwg / c->n_kv_heads)); }
+
+Region region_of(const i4d_config* c, int n_layers, int nwg) {
+    Region r;
+    size_t off = 0;
+    r.args = off; off = a256(off + sizeof(Args));
+    r.table = off; off = a256(off + (size_t)MAX_LAYERS * sizeof(LPtr));
+    r.zero = off; off = a256(off + 1024);
+    r.layer0 = off;
+    const size_t D = c->d_model, F = c->d_ff, qw = (size_t)c->n_q_heads * HD, kvw = (size_t)c->n_kv_heads * HD;
+    const size_t ns = splits_of(c, nwg);
+    size_t lo = 0;
+    auto take = [&](size_t words) { const size_t o = lo; lo = a256(lo + words * 8); return o; };
+    r.ox = take(D);
+    r.oq = take(qw);
+    r.okv = take(2 * kvw);
+    r.opart = take((size_t)c->n_q_heads * ns * (HD + 2));
+    r.oo = take(qw);
+    r.oy = take(D);
+    r.oact = take(F);
+    r.lstride = lo;
+    r.total = off + (size_t)n_layers * lo;
+    return r;
+}
+
+}  // namespace
+
+size_t region_bytes(const i4d_config* c, int n_layers, int nwg) { return region_of(c, n_layers, nwg).total; }
+
+namespace {
+
+// Every host-side decision of one launch, taken before anything is enqueued.
+struct Plan {
+    int cq, ck;          // q/k/v split of the compute units
+    size_t lds;
+};
+
+// q/k/v rows go to compute units in proportion: [0, cq) q, [cq, ck) k, [ck, nwg) v.
+void qkv_split(const i4d_config* c, int nwg, int& cq, int& ck) {
+    const int npq = c->n_q_heads * HD / 2, npk = c->n_kv_heads * HD / 2;
+    int nq = (int)((long long)nwg * npq / (npq + 2 * npk));
+    nq = std::min(std::max(nq, 1), nwg - 2);
+    const int nk = std::max(1, (nwg - nq) / 2);
+    cq = nq;
+    ck = nq + nk;
+}
+
+// Runs per slot of a phase whose compute unit holds np pairs of S units.
+int runs_of(int np, int S) {
+    const int n = (np * S + NSLOT - 1) / NSLOT;
+    return (n + S - 1) / S + 1;
+}
+
+bool make_plan(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int batch, int nwg, Plan& P) {
+    if (batch != 1 || c->head_dim != HD || n_layers < 1 || n_layers > MAX_LAYERS) return false;
+    const int D = c->d_model, F = c->d_ff, qw = c->n_q_heads * HD, kvw = c->n_kv_heads * HD;
+    if (c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads) return false;
+    if (c->n_q_heads / c->n_kv_heads > 16) return false;
+    // every K a whole number of 512-input units and within one digit plane;
+    // D and the q width at most two staging rounds of the workgroup
+    if (D % 512 || F % 512 || qw % 512 || F > KMAX || D > 2 * NT * 8 || qw > 2 * NT * 8) return false;
+    if (nwg < 3 || nwg > 1024) return false;
+    if ((D / 2 + nwg - 1) / nwg > MAX_RES) return false;     // residual rows per compute unit
+    for (int l = 0; l < n_layers; ++l) {
+        const i4d_layer& L = layers[l];
+        const i4d_mat* m[7] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+        for (int i = 0; i < 7; ++i) {
+            if (m[i]->dtype != I4D_WEIGHT_INT4 || m[i]->group != 128) return false;
+            if (((uintptr_t)m[i]->data % 16) || ((uintptr_t)m[i]->scales % 4)) return false;
+        }
+        if (kv[l].pages || kv[l].capacity != kv[0].capacity) return false;
+        if (((uintptr_t)L.attn_norm % 16) || ((uintptr_t)L.ffn_norm % 16)) return false;
+    }
+    // pair runs per slot within MAXRUN in every phase
+    qkv_split(c, nwg, P.cq, P.ck);
+    const int nq = P.cq, nk = P.ck - P.cq, nv = nwg - P.ck;
+    if (nk < 1 || nv < 1) return false;
+    const int pqkv = std::max((qw / 2 + nq - 1) / nq, std::max((kvw / 2 + nk - 1) / nk, (kvw / 2 + nv - 1) / nv));
+    if (runs_of(pqkv, D / 512) > MAXRUN) return false;
+    if (runs_of((D / 2 + nwg - 1) / nwg, qw / 512) > MAXRUN) return false;
+    if (runs_of((F + nwg - 1) / nwg, D / 512) > MAXRUN) return false;
+    if (runs_of((D / 2 + nwg - 1) / nwg, F / 512) > MAXRUN) return false;
+    // LDS, no scratch, one workgroup per compute unit
+    P.lds = lds_bytes(n_layers);
+    if (P.lds > 160 * 1024) return false;
+    static int lds_set[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (lds_set[dev] < (int)P.lds) {
+        if (hipFuncSetAttribute((const void*)k_stream_decode, hipFuncAttributeMaxDynamicSharedMemorySize, (int)P.lds) != hipSuccess)
+            return false;
+        lds_set[dev] = (int)P.lds;
+    }
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, (const void*)k_stream_decode) != hipSuccess || fa.localSizeBytes != 0) return false;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_stream_decode, NT, P.lds) != hipSuccess) return false;
+    return per_cu >= 1;
+}
+
+}  // namespace
+
+bool supported(const i4d_config* c, int n_layers, const i4d_layer* layers, const i4d_kv* kv, int batch, int nwg) {
+    Plan P;
+    return make_plan(c, n_layers, layers, kv, batch, nwg, P);
+}
+
+int run(const i4d_config* c, int n_layers, const i4d_layer* layers, const float* x_in, float* x_out, const i4d_kv* kv,
+        const int* pos, int max_pos, char* region, int* status, unsigned* epoch, int nwg, hipStream_t s,
+        hipEvent_t* timing_ev) {
+    Plan P;
+    if (!make_plan(c, n_layers, layers, kv, 1, nwg, P)) return I4D_EUNSUPPORTED;
+    hipStreamCaptureStatus cap_st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap_st) != hipSuccess) return I4D_EHIP;
+    const Region R = region_of(c, n_layers, nwg);
+
+    LPtr* table = (LPtr*)(region + R.table);
+    for (int l0 = 0; l0 < n_layers; l0 += LPTR_PER_FILL) {
+        LPtrChunk ch;
+        memset(&ch, 0, sizeof(ch));
+        ch.count = std::min(LPTR_PER_FILL, n_layers - l0);
+        ch.dst = table + l0;
+        for (int i = 0; i < ch.count; ++i) {
+            const i4d_layer& Ls = layers[l0 + i];
+            const i4d_mat* m[7] = {&Ls.wq, &Ls.wk, &Ls.wv, &Ls.wo, &Ls.wg, &Ls.wu, &Ls.wd};
+            LPtr& d = ch.e[i];
+            for (int k = 0; k < 7; ++k) { d.c[k] = (const uint8_t*)m[k]->data; d.s[k] = (const uint8_t*)m[k]->scales; }
+            d.g1 = Ls.attn_norm;
+            d.g2 = Ls.ffn_norm;
+            d.kc = kv[l0 + i].k;
+            d.vc = kv[l0 + i].v;
+        }
+        hipLaunchKernelGGL(k_fill_ltab, dim3(1), dim3(64), 0, s, ch);
+    }
+
+    Args A;
+    memset(&A, 0, sizeof(A));
+    A.table = table;
+    A.L = n_layers;
+    A.x_in = x_in;
+    A.x_out = x_out;
+    A.pos = pos;
+    A.max_pos = max_pos;
+    A.cap = kv[0].capacity;
+    A.D = c->d_model; A.F = c->d_ff; A.Hq = c->n_q_heads; A.Hkv = c->n_kv_heads;
+    A.eps = c->rms_eps;
+    A.qscale = (float)(1.4426950408889634 / sqrt((double)HD));
+    A.base = c->rope_base;
+    A.nsplit = splits_of(c, nwg);
+    const int tiles = (max_pos + 1 + 15) / 16;
+    A.T = 16 * ((tiles + A.nsplit - 1) / A.nsplit);
+    A.cq = P.cq; A.ck = P.ck;
+    A.lbase = region + R.layer0;
+    A.lstride = R.lstride;
+    A.ox = (unsigned)R.ox; A.oq = (unsigned)R.oq; A.okv = (unsigned)R.okv; A.opart = (unsigned)R.opart;
+    A.oo = (unsigned)R.oo; A.oy = (unsigned)R.oy; A.oact = (unsigned)R.oact;
+    A.zero = (const uint8_t*)(region + R.zero);
+    A.status = status;
+    A.epoch = epoch;
+    hipLaunchKernelGGL(k_fill_args, dim3(1), dim3(64), 0, s, A, (Args*)(region + R.args));
+
+    if (timing_ev) (void)hipEventRecord(timing_ev[0], s);
+    hipError_t e;
+    const Args* Ad = (const Args*)(region + R.args);
+    if (cap_st == hipStreamCaptureStatusNone) {
+        void* args[] = {&Ad};
+        e = hipLaunchCooperativeKernel((const void*)k_stream_decode, dim3(nwg), dim3(NT), args, (unsigned)P.lds, s);
+    } else {
+        // inside a graph capture: an ordinary launch of one workgroup per compute
+        // unit (a graph replays its kernels one after another, so every workgroup
+        // is resident; a workgroup that waits too long gives up, never hangs)
+        hipLaunchKernelGGL(k_stream_decode, dim3(nwg), dim3(NT), P.lds, s, Ad);
+        e = hipGetLastError();
+    }
+    if (timing_ev) (void)hipEventRecord(timing_ev[1], s);
+    return e == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+}  // namespace i4d_stream

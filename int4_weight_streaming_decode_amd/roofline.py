@@ -63,8 +63,8 @@ def phase_bytes(shape, phase: str, batch: int, keys: float, weight_dtype: str = 
     """Algorithmic HBM bytes of one launch of one kernel of the step:
     qkv (Wq, Wk, Wv, the attention norm gain, the new K/V), attention (the
     cache over `keys` keys), wo, gate_up (Wg, Wu, the FFN norm gain), down,
-    lm_head (the whole head: one launch sweeps every chunk) and persistent
-    (the whole stack of one call)."""
+    lm_head (the whole head: one launch sweeps every chunk) and stream
+    (the streaming kernel: the whole stack of one call)."""
     m = layer_matrices(shape)
     mb = {n: matrix_bytes(r, c, shape.group, weight_dtype) for n, (r, c) in m.items()}
     if phase == "qkv":
@@ -79,7 +79,7 @@ def phase_bytes(shape, phase: str, batch: int, keys: float, weight_dtype: str = 
         return mb["wd"]
     if phase == "lm_head":
         return lm_head_bytes(shape.vocab, shape.d_model, shape.group)
-    if phase == "persistent":
+    if phase == "stream":
         return step_bytes(shape, batch, keys, weight_dtype)
     raise ValueError(phase)
 

@@ -297,7 +297,7 @@ FAST_SHAPE = synth.SHAPES["tiny"].with_(name="fast", d_model=512, n_q_heads=4, n
                                         d_ff=1024, group=128, rope_base=1e6)
 
 
-@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_PERSISTENT])
+@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_STREAM])
 def test_multi_step_decode_matches_oracle(exec_mode):
     _print_case("multi-step decode", exec_mode)
     outs, kv_gpu, ref_outs, ref_caches, status = _multi_step(FAST_SHAPE, 2, 120, 3, exec_mode)
@@ -311,7 +311,7 @@ def test_multi_step_decode_matches_oracle(exec_mode):
                                   what=f"layer {l} {name} slot {120 + s}")
 
 
-@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_PERSISTENT])
+@pytest.mark.parametrize("exec_mode", [B.EXEC_PHASES, B.EXEC_STREAM])
 def test_decode_is_bit_reproducible(exec_mode):
     """Fixed reduction orders: the same inputs give the same bits, run to run
     (position 5000: several 16-key subtiles per attention split)."""
@@ -325,39 +325,33 @@ def test_decode_is_bit_reproducible(exec_mode):
         assert np.array_equal(a[1][l][0], b[1][l][0]) and np.array_equal(a[1][l][1], b[1][l][1])
 
 
-def test_persistent_kernel_agrees_with_phase_launches():
-    """The two execution modes cut the reductions differently (256 vs 512
-    threads per workgroup), so they agree to rounding, and both match the
-    oracle."""
-    _print_case("persistent vs phases")
+def test_stream_kernel_agrees_with_phase_launches():
+    """The phase launches stage activations as fp16, the streaming kernel as
+    16-bit integers per 32-input run: both match the oracle, agree with each
+    other to the float bar, and round each appended K/V element to the same
+    bf16 value or to a neighbouring one."""
+    _print_case("stream vs phases")
     a = _multi_step(FAST_SHAPE, 3, 5000, 2, B.EXEC_PHASES, seed=29)
-    b = _multi_step(FAST_SHAPE, 3, 5000, 2, B.EXEC_PERSISTENT, seed=29)
+    b = _multi_step(FAST_SHAPE, 3, 5000, 2, B.EXEC_STREAM, seed=29)
     assert a[4] == 0 and b[4] == 0
     for s in range(2):
-        assert rel_l2(b[0][s], a[0][s]) <= 1e-5, f"step {s}"
-        assert_close(b[0][s], a[2][s], what=f"persistent step {s} vs oracle")
+        assert_close(b[0][s], a[0][s], what=f"stream vs phases step {s}")
+        assert_close(b[0][s], a[2][s], what=f"stream step {s} vs oracle")
     for l in range(3):
         for k in range(2):
-            # the same slot rounded to bf16 from two fp32 results that differ
-            # in the last bits: one rounding step apart, or (for values near
-            # zero) many ulps for a tiny absolute difference
             ga = synth.bf16_value(a[1][l][k]).astype(np.float64)
             gb = synth.bf16_value(b[1][l][k]).astype(np.float64)
             rms = np.sqrt(np.mean(ga * ga))
             ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ga), np.abs(gb)))[1] - 8)
-            err = np.abs(ga - gb)
-            bad = err > np.maximum(1e-5 * rms, ulp)
-            i = int(np.argmax(err - np.maximum(1e-5 * rms, ulp)))
-            assert not bad.any(), (f"layer {l} {'KV'[k]}: {int(bad.sum())} elements apart; worst "
-                                   f"{ga.ravel()[i]:.6e} vs {gb.ravel()[i]:.6e} (RMS {rms:.3e}, "
-                                   f"{int(bf16_ulp_diff(a[1][l][k], b[1][l][k]).ravel()[i])} ulps)")
+            bad = np.abs(ga - gb) > np.maximum(5e-3 * rms, ulp)
+            assert not bad.any(), f"layer {l} {'KV'[k]}: {int(bad.sum())} elements apart"
 
 
-def test_persistent_mode_rejects_unsupported_shapes():
+def test_stream_mode_rejects_unsupported_shapes():
     shape = synth.SHAPES["tiny"]                       # K = 256, 688: not on the 512-wide fast path
     layers, caches, x = _layer_case(shape, 3, 1, [20], cap=64)
     L, kvd = DevLayer(layers[0]), DevKV(*caches[0])
-    cfg = config_of(shape, B.EXEC_PERSISTENT)
+    cfg = config_of(shape, B.EXEC_STREAM)
     ws = workspace(cfg, 1, 20)
     out = torch.empty((1, shape.d_model), dtype=torch.float32, device="cuda")
     with pytest.raises(B.I4DError) as e:

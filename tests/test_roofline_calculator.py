@@ -68,7 +68,32 @@ def test_phase_bytes_add_up_to_the_step():
     keys = s.kv_len + 1
     parts = sum(roofline.phase_bytes(s, p, 1, keys) for p in ("qkv", "attention", "wo", "gate_up", "down"))
     assert parts * s.n_layers == roofline.step_bytes(s, 1, keys)
-    assert roofline.phase_bytes(s, "persistent", 1, keys) == roofline.step_bytes(s, 1, keys)
+    assert roofline.phase_bytes(s, "stream", 1, keys) == roofline.step_bytes(s, 1, keys)
     assert roofline.phase_bytes(s, "lm_head", 1, keys) == roofline.lm_head_bytes(s.vocab, s.d_model, s.group)
     # gate/up of the 27B shape: two 17408 x 5120 int4 matrices with groups of 128, plus the norm gain
     assert roofline.phase_bytes(s, "gate_up", 1, keys) == 2 * (17408 * 2560 + 17408 * 40 * 2) + 5120 * 2
+
+
+def test_step_flops_is_two_flops_per_parameter_plus_attention():
+    """Roofline reply 二: a decode token costs two FLOPs (one multiply-add) per
+    weight.  The parameters are counted from a layer the input generator
+    actually builds; the attention term is one multiply-add per (query head,
+    key, dim) for the scores and again for the weighted sum of values."""
+    s = synth.SHAPES["tiny"].with_(n_layers=3)
+    layer = synth.make_layer(s, 0, 0)
+    params = sum(layer[n]["codes"].size * 2 for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"))
+    assert roofline.step_flops(s, 1, 0) == 2 * params * s.n_layers
+    keys = 128
+    attn = 2 * (s.n_q_heads * keys * s.head_dim) * 2 * s.n_layers
+    assert roofline.step_flops(s, 1, keys) == 2 * params * s.n_layers + attn
+    assert roofline.step_flops(s, 4, keys) == 4 * roofline.step_flops(s, 1, keys)
+
+
+@pytest.mark.parametrize("batch,intensity", [(1, 4.8), (4, 11.4), (16, 17.2), (32, 18.8)])
+def test_70b_batch_sweep_intensity(batch, intensity):
+    """The 70B-shaped stack's roofline position per batch (FLOP per algorithmic
+    byte of the whole step, KV 32768): the KV read grows with the batch, the
+    weight read does not."""
+    s = synth.SHAPES["70b"]
+    keys = s.kv_len + 1
+    assert roofline.step_flops(s, batch, keys) / roofline.step_bytes(s, batch, keys) == pytest.approx(intensity, abs=0.05)

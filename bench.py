@@ -5,20 +5,26 @@ Default workload (the headline metric): the 27B-shaped int4 decoder stack
 128) plus the 152064 x 5120 int4 LM head swept in chunks of 8192 rows, batch 1,
 8192 cached tokens at the first timed step (the position advances by one per
 step).  Inputs are synthetic (seeded, generated on the GPU, resident in HBM
-before timing).  Prints one JSON line: `value` from K timed steps, the
-roofline of the dominant kernel (k_gemv_swiglu) from a second region of K
-steps whose launches of that kernel carry HIP events, a per-kernel breakdown
-from a few more steps per kernel, and the CPU oracle's rate on a bounded
-sample.
+before timing).  At batch 1 the stack runs as one launch of the streaming
+kernel (k_stream_decode); other batches run one launch per phase (1..8) or the
+matrix-core GEMM path (9..32).
 
-Batches of 9..32 run the matrix-core (MFMA) GEMM path.  --layers N runs the
-first N layers of a stack at its full shape (for a batch whose whole stack
-does not fit in HBM, e.g. the 70B shape at batch 32) and adds the per-step
-figures scaled to the full depth, labelled as extrapolated.
+Prints one JSON line: `value` (tok/s) from K timed steps with no
+instrumentation; `kernels`, every kernel of the step timed by HIP events on
+its own stream over a few more steps, with its algorithmic bytes, GB/s, share
+of the step and fraction of 8 TB/s; `roofline`, the kernel with the largest
+share of the step, timed over K more steps; `step_roofline`, the whole step
+against 8 TB/s and against the measured streaming-read rate of the read probe;
+bytes per token and FLOP per byte of the step; the CPU oracle's rate on a
+bounded sample.
+
+--layers N runs the first N layers of a stack at its full shape (for a batch
+whose whole stack does not fit in HBM, e.g. the 70B shape at batch 32) and
+adds the per-step figures scaled to the full depth, labelled as extrapolated.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--batch B] [--layers N] [--exec-mode M] [--roofline-kernel K]
-                       [--breakdown-steps N] [--calibrate-copy-mib MIB] [--no-cpu-baseline]
+                       [--batch B] [--layers N] [--exec-mode M] [--breakdown-steps N]
+                       [--calibrate-copy-mib MIB] [--no-cpu-baseline] [--no-read-probe]
 """
 
 import argparse
@@ -45,11 +51,11 @@ WORKLOADS = {
 }
 
 
-# library kernel behind each timed phase (batches of 1..8: matrix-vector
-# kernels; 9..32: the matrix-core GEMM kernels)
+# library kernel behind each timed phase (batch 1: the streaming kernel;
+# batches of 2..8: matrix-vector kernels; 9..32: the matrix-core GEMM kernels)
 KERNEL_NAMES = {"qkv": "k_gemv_qkv", "attention": "k_attention<128, false>", "wo": "k_gemv_rows (Wo)",
                 "gate_up": "k_gemv_swiglu", "down": "k_gemv_rows (W_down)", "lm_head": "k_lm_head",
-                "persistent": "k_decode_persistent"}
+                "stream": "k_stream_decode"}
 KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128, false>", "wo": "k_mfma_rows (Wo)",
                         "gate_up": "k_mfma_swiglu", "down": "k_mfma_rows (W_down)", "lm_head": "k_mfma_lm"}
 
@@ -58,7 +64,8 @@ KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128, fals
 # this profile by two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size, with a hash of the kernel sources it was taken
 # on.  Reported only while the sources still hash the same.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_27b_int4_hbm_traffic.md")
+TRAFFIC_RECORDS = [os.path.join(ROOT, "profiles", f) for f in ("stream_decode_27b_int4_hbm_traffic.md",
+                                                                 "gate_up_27b_int4_hbm_traffic.md")]
 
 
 def sources_sha256() -> str:
@@ -72,15 +79,18 @@ def sources_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str):
-    """Bytes per launch from the traffic record, or None if absent or stale."""
-    if not os.path.exists(TRAFFIC_RECORD):
-        return None
+def recorded_traffic(kernel: str, workload: str):
+    """Bytes per launch from a traffic record of this kernel on this workload,
+    or None if absent or taken on other sources."""
     import re
-    for line in open(TRAFFIC_RECORD):
-        m = re.match(r"traffic-record: kernel=(\S+) bytes_per_launch=(\d+) sources_sha256=([0-9a-f]{64})", line.strip())
-        if m and m.group(1) == kernel and m.group(3) == sources_sha256():
-            return int(m.group(2))
+    for path in TRAFFIC_RECORDS:
+        if not os.path.exists(path):
+            continue
+        for line in open(path):
+            m = re.match(r"traffic-record: kernel=(\S+) workload=(\S+) bytes_per_launch=(\d+) sources_sha256=([0-9a-f]{64})",
+                         line.strip())
+            if m and m.group(1) == kernel and m.group(2) == workload and m.group(4) == sources_sha256():
+                return int(m.group(3))
     return None
 
 
@@ -138,23 +148,21 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="run only the first N layers of the stack (0: all); figures for the full depth are then "
                          "reported as extrapolated")
-    ap.add_argument("--exec-mode", type=int, default=0)
+    ap.add_argument("--exec-mode", type=int, default=0, help="0 auto, 1 one launch per phase, 2 streaming kernel")
     ap.add_argument("--graph", action="store_true",
                     help="capture one whole step (stack, LM head, position advance) in a HIP graph and replay it in "
                          "the timed region; the attention split is then planned for the cache capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: the LM head draws the token at this temperature (Gumbel-max) instead of the greedy argmax")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: paged KV caches (pages of this many positions, shuffled over a pool) instead of contiguous ones")
-    ap.add_argument("--roofline-kernel", default=None, choices=["qkv", "attention", "wo", "gate_up", "down", "persistent"],
-                    help="kernel whose launches are timed inside the timed region (default: gate_up with per-phase "
-                         "launches, persistent with the persistent kernel)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the steps, run 3 plain device-to-device copies of this many MiB (a kernel of known "
                          "traffic for scaling hardware byte counters); 0: none")
     ap.add_argument("--breakdown-steps", type=int, default=10,
-                    help="steps per extra pass that times each other kernel of the step (0: none)")
+                    help="steps per extra pass that times one kernel of the step (0: no per-kernel figures)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -175,20 +183,15 @@ def main():
     if args.kv_len > 0:
         shape = shape.with_(kv_len=args.kv_len)
     batch = args.batch
-    names = KERNEL_NAMES_BATCHED if batch > 8 else KERNEL_NAMES
     torch.cuda.set_device(0)
     torch.manual_seed(0)
 
-    rk = args.roofline_kernel or ("persistent" if args.exec_mode == 2 else "gate_up")
-    phases = ["persistent"] if args.exec_mode == 2 else ["qkv", "attention", "wo", "gate_up", "down"]
-    if lm:
-        phases.append("lm_head")
-    extra = [k for k in phases if k != rk] if args.breakdown_steps > 0 else []
-    n_total = args.warmup + 2 * args.steps + len(extra) * args.breakdown_steps
+    n_kinds = 7
+    n_total = args.warmup + 1 + 2 * args.steps + n_kinds * args.breakdown_steps
     cap = ((shape.kv_len + n_total + 1 + 15) // 16) * 16
     if args.page_size > 0:
-        if args.page_size % 16 or args.exec_mode == 2:
-            sys.exit("--page-size must be a multiple of 16 and cannot be combined with --exec-mode 2")
+        if args.page_size % 16:
+            sys.exit("--page-size must be a multiple of 16")
         cap = (cap + args.page_size - 1) // args.page_size * args.page_size
     pgen = torch.Generator(device="cpu").manual_seed(5)
     t_gen = time.perf_counter()
@@ -236,26 +239,21 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-
     def lm_head(h):
         if args.temperature > 0:
             B.lm_head_sample(lm_mat, batch, h, shape.lm_chunk, args.temperature, 0x5EED, pos, tok, mx, ws)
         else:
             B.lm_head_chunked(lm_mat, batch, h, shape.lm_chunk, tok, mx, ws)
 
-    def step(i, events=None):
-        max_pos = shape.kv_len + i
-        if events:
-            events[0].record()
-        B.decode_stack(cfg, layers, batch, x, out, kvs, pos, max_pos, ws)
-        if events:
-            events[1].record()
+    done = 0
+
+    def step():
+        nonlocal done
+        B.decode_stack(cfg, layers, batch, x, out, kvs, pos, shape.kv_len + done, ws)
         if lm:
             lm_head(out)
-        if events:
-            events[2].record()
         pos.add_(1)
+        done += 1
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -265,9 +263,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        step(i)
+    for _ in range(args.warmup):
+        step()
+    # which path runs the stack: one streaming launch, or one launch per phase
+    B.launch_timing_start("stream", 4)
+    step()
     torch.cuda.synchronize()
+    streaming = B.launch_timing_stop()[1] > 0
+    if streaming:
+        kinds = ["stream"]
+        names = KERNEL_NAMES
+    else:
+        kinds = ["qkv", "attention", "wo", "gate_up", "down"]
+        names = KERNEL_NAMES_BATCHED if batch > 8 else KERNEL_NAMES
+    if lm:
+        kinds.append("lm_head")
+    torch.cuda.synchronize()
+
     graph = None
     if args.graph:
         gs = torch.cuda.Stream()
@@ -280,69 +292,85 @@ def main():
             pos.add_(1)
         torch.cuda.current_stream().wait_stream(gs)
         torch.cuda.synchronize()
+
+    # ---- the timed region: K steps, nothing instrumented
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    keys0 = shape.kv_len + done + 1
     t0.record()
-    for i in range(args.steps):
+    for _ in range(args.steps):
         if graph is not None:
             graph.replay()
+            done += 1
         else:
-            step(args.warmup + i, ev[i])
+            step()
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    if graph is None:
-        stack_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-        lm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if lm else 0.0
-    else:                                   # no per-step events inside a replay
-        stack_ms = None
-        lm_ms = None
-    ms_per_step = total_ms / args.steps
-    keys_avg = shape.kv_len + args.warmup + (args.steps - 1) / 2.0 + 1
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    keys_avg = keys0 + (args.steps - 1) / 2.0
 
-    # The roofline kernel: the same K steps again, every launch of that kernel
-    # carrying a start and a stop HIP event on its own stream (the library
-    # launches it through hipExtLaunchKernel, which stamps them with the
-    # kernel's start and end).  The events slow the step a little, so this is
-    # a second timed region rather than the one `value` comes from.
-    done = args.warmup + args.steps
-    B.launch_timing_start(rk, 65536)
-    t0.record()
-    for i in range(args.steps):
-        step(done + i)
-    t1.record()
-    torch.cuda.synchronize()
-    rk_ms, rk_launches = B.launch_timing_stop()
-    rk_region_ms = t0.elapsed_time(t1) / args.steps
-    rk_keys = keys_avg + args.steps
-    done += args.steps
-
-    def kernel_entry(kind, ms, launches, keys):
+    # ---- every kernel of the step, each timed by events on its own stream
+    def kernel_entry(kind, ms, launches, keys, steps):
         nbytes = roofline.phase_bytes(shape, kind, batch, keys, wdtype)
         avg_ms = ms / max(launches, 1)
-        return {"launches": launches, "avg_us": avg_ms * 1e3, "bytes_per_launch": nbytes,
-                "gbps": nbytes / (avg_ms * 1e-3) / 1e9 if launches else None}
+        e = {"kernel": names[kind], "launches_per_step": launches / max(steps, 1), "avg_us": avg_ms * 1e3,
+             "bytes_per_launch": nbytes}
+        if launches:
+            e["gbps"] = nbytes / (avg_ms * 1e-3) / 1e9
+            e["frac_of_8tbps"] = e["gbps"] / 8000.0
+            e["share_of_step"] = (ms / steps) / ms_per_step
+        return e
 
-    # Extra passes (after the timed region, not part of `value`): each other
-    # kernel of the step timed the same way over a few steps.
-    breakdown = {rk: kernel_entry(rk, rk_ms, rk_launches, rk_keys)}
-    for kind in extra:
-        B.launch_timing_start(kind, 65536)
-        for i in range(args.breakdown_steps):
-            step(done + i)
+    breakdown = {}
+    if args.breakdown_steps > 0 and graph is None:
+        for kind in kinds:
+            k0 = shape.kv_len + done + 1
+            B.launch_timing_start(kind, 65536)
+            for _ in range(args.breakdown_steps):
+                step()
+            torch.cuda.synchronize()
+            ms, n = B.launch_timing_stop()
+            breakdown[kind] = kernel_entry(kind, ms, n, k0 + (args.breakdown_steps - 1) / 2.0, args.breakdown_steps)
+    # ---- the roofline kernel: the largest share of the step, timed over K more steps
+    rk = max(breakdown, key=lambda k: breakdown[k].get("share_of_step", 0.0)) if breakdown else kinds[0]
+    rk_entry = None
+    if graph is None:
+        k0 = shape.kv_len + done + 1
+        B.launch_timing_start(rk, 65536)
+        t0.record()
+        for _ in range(args.steps):
+            step()
+        t1.record()
         torch.cuda.synchronize()
-        ms, n = B.launch_timing_stop()
-        breakdown[kind] = kernel_entry(kind, ms, n, shape.kv_len + done + (args.breakdown_steps - 1) / 2.0 + 1)
-        done += args.breakdown_steps
+        rk_ms, rk_launches = B.launch_timing_stop()
+        rk_region_ms = t0.elapsed_time(t1) / args.steps
+        rk_entry = kernel_entry(rk, rk_ms, rk_launches, k0 + (args.steps - 1) / 2.0, args.steps)
     status = B.read_device_status(ws)
+
+    # ---- the measured streaming-read rate (plain 16-byte loads over 4 GiB)
+    probe = None
+    if not args.no_read_probe:
+        buf = torch.ones((1 << 32) // 4, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        B.read_probe(buf, sink)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(5):
+            B.read_probe(buf, sink)
+        t1.record()
+        torch.cuda.synchronize()
+        probe = {"gbps": 5 * buf.numel() * 4 / (t0.elapsed_time(t1) * 1e-3) / 1e9, "bytes": buf.numel() * 4,
+                 "how": "k_read_probe: one 512-thread workgroup per compute unit, 4 nontemporal 16-byte loads in "
+                        "flight per lane, 5 sweeps of 4 GiB"}
+        del buf
 
     stack_bytes = roofline.step_bytes(shape, batch, keys_avg, wdtype)
     lm_bytes = roofline.lm_head_bytes(shape.vocab, shape.d_model, shape.group) if lm else 0
     step_bytes = stack_bytes + lm_bytes
+    step_flops = roofline.step_flops(shape, batch, keys_avg, lm_head=lm)
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    stack_gbps = stack_bytes / (stack_ms * 1e-3) / 1e9 if stack_ms else None
 
-    rk_entry = breakdown[rk]
+    workload_id = f"{args.workload}-b{batch}"
     result = {
         "metric": METRIC,
         "value": batch * 1000.0 / ms_per_step,
@@ -356,34 +384,46 @@ def main():
         "vs_baseline": None,
         "dtype": ("bf16 weights, f32 FMA" if wdtype != "int4" else
                   "int4 weights, f16 x f16 -> f32 MFMA GEMM; bf16 MFMA attention" if batch > 8 else
+                  "int4 weights x int4 digits of 16/24-bit activations -> i32 dot; bf16 MFMA attention" if streaming else
                   "int4 weights, f16 x f16 -> f32 dot; bf16 MFMA attention"),
         "data": "synthetic",
         "config": {"workload": describe(shape, wdtype, lm, batch), "batch": batch, "kv_len": shape.kv_len,
                    "layers": shape.n_layers, "weights": wdtype, "lm_head": lm, "exec_mode": args.exec_mode,
+                   "stack_path": "streaming kernel" if streaming else ("matrix-core GEMM" if batch > 8 else
+                                                                        "one launch per phase"),
                    "graph": bool(args.graph), "temperature": args.temperature, "page_size": args.page_size},
         "hbm_gbps": hbm_gbps,
         "hbm_frac_of_8tbps": hbm_gbps / 8000.0,
         "algorithmic_bytes_per_step": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": names[rk], "achieved": rk_entry["gbps"], "peak": 8000.0,
-                     "unit": "GB/s", "frac": rk_entry["gbps"] / 8000.0, "traffic": recorded_traffic(names[rk]),
-                     "avg_launch_us": rk_entry["avg_us"], "launches": rk_launches,
-                     "ms_per_step_while_timed": rk_region_ms,
-                     "bytes_per_launch": rk_entry["bytes_per_launch"]},
+        "bytes_per_token": step_bytes / batch,
+        "flop_per_token": step_flops / batch,
+        "flop_per_byte": step_flops / step_bytes,
+        "step_roofline": {"bound": "hbm", "achieved": hbm_gbps, "peak": 8000.0, "unit": "GB/s",
+                          "frac": hbm_gbps / 8000.0,
+                          "frac_of_read_probe": hbm_gbps / probe["gbps"] if probe else None},
+        "read_probe": probe,
         "kernels": breakdown,
-        "stack_ms": stack_ms,
-        "stack_gbps": stack_gbps,
-        "lm_head_ms": lm_ms,
         "device_status": status,
         "input_generation_s": round(t_gen, 1),
     }
-    if shape.n_layers < full_layers and stack_ms:
+    if rk_entry is not None:
+        result["roofline"] = {"bound": "hbm", "kernel": names[rk], "achieved": rk_entry.get("gbps"), "peak": 8000.0,
+                              "unit": "GB/s", "frac": rk_entry["gbps"] / 8000.0 if "gbps" in rk_entry else None,
+                              "traffic": recorded_traffic(names[rk], workload_id),
+                              "avg_launch_us": rk_entry["avg_us"], "launches_per_step": rk_entry["launches_per_step"],
+                              "share_of_step": rk_entry.get("share_of_step"),
+                              "ms_per_step_while_timed": rk_region_ms,
+                              "bytes_per_launch": rk_entry["bytes_per_launch"]}
+    if shape.n_layers < full_layers:
         scale = full_layers / shape.n_layers
+        lm_ms = breakdown.get("lm_head", {}).get("avg_us", 0.0) / 1e3 if lm else 0.0
+        stack_ms = ms_per_step - lm_ms
         full_ms = stack_ms * scale + lm_ms
         result["extrapolated"] = {
             "layers": full_layers, "ms_per_step": full_ms, "tokens_per_s": batch * 1000.0 / full_ms,
             "hbm_gbps": (stack_bytes * scale + lm_bytes) / (full_ms * 1e-3) / 1e9,
-            "how": f"the first {shape.n_layers} layers at the full shape, timed; their stack time scaled by "
-                   f"{full_layers}/{shape.n_layers}"}
+            "how": f"the first {shape.n_layers} layers at the full shape, timed; the step time less the LM head "
+                   f"scaled by {full_layers}/{shape.n_layers}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, wdtype, lm)
     print(json.dumps(result), flush=True)

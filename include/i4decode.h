@@ -217,6 +217,18 @@ int i4d_lm_head_chunked(const i4d_mat* w_lm, int32_t batch, const float* h, int3
                         int32_t* token_out, float* max_logit_out,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* i4d_lm_head_chunked without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * i4d_lm_head_chunked for 1 <= batch <= 8 (the matrix-vector path); batch
+ * above 8 returns I4D_ERANGE.  The per-workgroup argmax keys live in a
+ * 256 KiB device array of the library (one per GPU, held until the process
+ * ends); the entry point calls no allocator.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.                               */
+int i4d_lm_head_chunked_noalloc(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows,
+                                int32_t* token_out, float* max_logit_out, void* stream);
+
 /* Temperature sampling from the same LM head (Primer 1.2 ends the step by
  * sampling a token from the logits; the pages name no sampler).  token_out[b]
  * is a draw from softmax((W_lm h_b) / temperature) by the Gumbel-max method:

@@ -81,6 +81,7 @@ def lib():
         L.i4d_decode_stack.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                        ctypes.POINTER(I4dKv), P, I, P, Z, P]
         L.i4d_lm_head_chunked.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P, Z, P]
+        L.i4d_lm_head_chunked_noalloc.argtypes = [ctypes.POINTER(I4dMat), I, P, I, P, P, P]
         L.i4d_lm_head_sample.argtypes = [ctypes.POINTER(I4dMat), I, P, I, ctypes.c_float, ctypes.c_uint64, P, P, P, P, Z, P]
         L.i4d_dequant_int4.argtypes = [ctypes.POINTER(I4dMat), P, P]
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
@@ -102,7 +103,8 @@ def lib():
         for name in ("i4d_workspace_init", "i4d_decode_layer", "i4d_decode_stack", "i4d_lm_head_chunked", "i4d_embed",
                      "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
-                     "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe"):
+                     "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe",
+                     "i4d_lm_head_chunked_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -181,6 +183,12 @@ def lm_head_chunked(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out
     _check(lib().i4d_lm_head_chunked(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, _ptr(token_out),
                                      _ptr(max_logit_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "i4d_lm_head_chunked")
+
+
+def lm_head_chunked_noalloc(w_lm: I4dMat, batch, h, chunk_rows, token_out, max_logit_out, stream=None):
+    """Greedy LM head (batch <= 8) with the library's own device scratch: no workspace argument."""
+    _check(lib().i4d_lm_head_chunked_noalloc(ctypes.byref(w_lm), batch, _ptr(h), chunk_rows, _ptr(token_out),
+                                             _ptr(max_logit_out), _stream(stream)), "i4d_lm_head_chunked_noalloc")
 
 
 def lm_head_sample(w_lm: I4dMat, batch, h, chunk_rows, temperature, seed, counter, token_out, score_out, ws, stream=None):

@@ -5,6 +5,7 @@
 #include <cmath>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 #include <string.h>
 
@@ -1243,6 +1244,53 @@ static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const floa
     if (!run) return I4D_OK;
     TimeScope ts(I4D_TIME_LM_HEAD);
     return launch_lm(fmt, nb, t, nwg, h, batch, (u64*)(w + WS_LM_KEYS), token_out, max_logit_out, smp, s);
+}
+
+// ---- greedy LM head without a workspace
+// The matrix-vector LM head's only scratch is the per-workgroup argmax keys
+// (every workgroup writes its own before the finalising kernel reads them, so
+// nothing needs clearing).  This variant keeps them in a file-scope device
+// array instead of the caller's workspace.  Host code must not pass the
+// array's name to a kernel: the name is a host-side stand-in; the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current (each GPU holds its own copy of the array).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)LM_MAX_WG * MAX_BATCH * sizeof(u64);   // 256 KiB
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static int scratch_device_ptr(u64** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return I4D_EHIP;
+    static std::mutex mu;
+    static void* ptrs[NOALLOC_MAX_DEVICES] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return I4D_EHIP;
+        ptrs[dev] = ptr;
+    }
+    *out = (u64*)ptrs[dev];
+    return I4D_OK;
+}
+
+int i4d_lm_head_chunked_noalloc(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t chunk_rows, int32_t* token_out,
+                                float* max_logit_out, void* stream) {
+    if (!w_lm || w_lm->dtype != I4D_WEIGHT_INT4) return I4D_EINVAL;
+    int rc;
+    if ((rc = validate_mat(w_lm, w_lm->n, w_lm->k, I4D_WEIGHT_INT4, w_lm->group))) return rc;
+    if (w_lm->n < 1 || w_lm->k < 8) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH || chunk_rows <= 0) return I4D_ERANGE;
+    if (!h || !token_out || !max_logit_out) return I4D_EINVAL;
+    if (!aligned(h, 16)) return I4D_EALIGN;
+    const int nb = nb_slot(batch), nwg = num_cus() * WG_PER_CU;
+    GemvTask t = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
+    const int fmt = pick_fmt(*w_lm);
+    plan_passes(t, fmt, nb, nwg, 0, GEMV_NT, 34);
+    if ((size_t)nwg * MAX_BATCH * sizeof(u64) > NOALLOC_SCRATCH_BYTES) return I4D_ERANGE;
+    u64* keys = nullptr;
+    if ((rc = scratch_device_ptr(&keys))) return rc;
+    return launch_lm(fmt, nb, t, nwg, h, batch, keys, token_out, max_logit_out, Sampler{0.f, 0u, 0u, nullptr},
+                     (hipStream_t)stream);
 }
 
 // Host checks of the sampling arguments; the sampler of a valid set.

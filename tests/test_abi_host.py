@@ -139,6 +139,22 @@ def test_lm_head_and_gemv_validation(lib):
     assert lib.i4d_dequant_int4(None, out, None) == B.I4D_EINVAL
 
 
+def test_lm_head_noalloc_validation(lib):
+    """The workspace-free LM head checks its arguments before any device call:
+    it takes the matrix-vector path only (batch 1..8)."""
+    w = _mat(1000, 256)
+    h = ctypes.c_void_p(0x100000)
+    out = ctypes.c_void_p(0x200000)
+    f = lib.i4d_lm_head_chunked_noalloc
+    assert f(ctypes.byref(w), 9, h, 64, out, out, None) == B.I4D_ERANGE      # batch above 8: no scratch for the MFMA path
+    assert f(ctypes.byref(w), 0, h, 64, out, out, None) == B.I4D_ERANGE
+    assert f(ctypes.byref(w), 1, h, 0, out, out, None) == B.I4D_ERANGE       # chunk_rows must be positive
+    assert f(ctypes.byref(w), 1, None, 64, out, out, None) == B.I4D_EINVAL
+    assert f(ctypes.byref(w), 1, ctypes.c_void_p(0x100004), 64, out, out, None) == B.I4D_EALIGN
+    assert f(ctypes.byref(_mat(1000, 256, dtype=B.WEIGHT_BF16)), 1, h, 64, out, out, None) == B.I4D_EINVAL
+    assert f(None, 1, h, 64, out, out, None) == B.I4D_EINVAL
+
+
 def test_binding_raises_with_status():
     with pytest.raises(B.I4DError) as e:
         B._check(B.I4D_EALIGN, "x")

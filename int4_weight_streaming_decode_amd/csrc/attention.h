@@ -107,17 +107,20 @@ struct AttnGeo {
     int b, j, s, t_s, t_e, nsub, kpos;     // kpos: the new key's position, -1 if none
 };
 
-I4D_DEVINL AttnGeo attn_geo(const AttnArgs& a, int item) {
+// nk: keys of the item's sequence (keys_of), when the caller already knows it
+I4D_DEVINL AttnGeo attn_geo_nk(const AttnArgs& a, int item, int nk) {
     AttnGeo g;
     g.s = item % a.nsplit;
     g.j = (item / a.nsplit) % a.hkv;
     g.b = item / (a.nsplit * a.hkv);
-    const int nk = keys_of(a, g.b);
     g.t_s = g.s * a.T;
     g.t_e = min(g.t_s + a.T, nk);
     g.nsub = (g.t_e > g.t_s) ? (g.t_e - g.t_s + 15) / 16 : 0;
     g.kpos = nk - 1;
     return g;
+}
+I4D_DEVINL AttnGeo attn_geo(const AttnArgs& a, int item) {
+    return attn_geo_nk(a, item, keys_of(a, item / (a.nsplit * a.hkv)));
 }
 
 template <int HD, int NSW>

@@ -54,7 +54,7 @@ namespace {
 constexpr int NT = 512;            // threads per workgroup: 8 waves, two per SIMD
 constexpr int NWAVE = NT / 64;
 constexpr int NSLOT = NT / 16;     // 16-lane slots
-constexpr int RD = 4;              // weight units in flight per lane
+constexpr int RD = 6;              // weight units in flight per lane
 constexpr int HD = 128;
 constexpr int ANSW = 2;            // attention subtiles per wave per load round
 constexpr int PS = 16384;          // LDS bytes per digit plane (K <= 32768)
@@ -131,7 +131,10 @@ constexpr int OFF_ROPE = OFF_RES + 4 * MAX_RES * 4;                // float2 [HD
 constexpr int OFF_KG = OFF_ROPE + (HD / 2) * 8;                    // KGeo [4]
 constexpr int OFF_SG = OFF_KG + 4 * (int)sizeof(KGeo);             // SGeo [4][NSLOT]
 constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [NWAVE]
-constexpr int OFF_TAB = ((OFF_RED + NWAVE * 4 + 255) / 256) * 256; // LPtr [L]
+constexpr int MAXNP = (MAXRUN - 1) * NSLOT;                        // pairs per unit and phase (runs_of() <= MAXRUN)
+constexpr int OFF_PINFO = OFF_RED + NWAVE * 4;                     // u32 [4][MAXNP]: first entry << 8 | count
+constexpr int OFF_PLIST = OFF_PINFO + 4 * MAXNP * 4;               // u8 [4][NSLOT * MAXRUN]: part indices, pair-major
+constexpr int OFF_TAB = ((OFF_PLIST + 4 * NSLOT * MAXRUN + 255) / 256) * 256; // LPtr [L]
 constexpr size_t lds_bytes(int L) { return (size_t)OFF_TAB + (size_t)L * sizeof(LPtr); }
 
 // ------------------------------------------------------------------ helpers
@@ -502,7 +505,11 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         k.p0 = (int)(((long long)ci * P) / nci);
         k.np = (int)(((long long)(ci + 1) * P) / nci) - k.p0;
         k.U = k.np * k.S;
-        k.n = (k.U + NSLOT - 1) / NSLOT;
+        // steps per slot, a whole number of ring turns: the steps past a
+        // slot's units only issue loads (re-reads of cached words), and every
+        // phase leaves the ring in the same order, the next phase's first RD
+        // units in flight
+        k.n = ((k.U + NSLOT - 1) / NSLOT + RD - 1) / RD * RD;
         const unsigned rb = (unsigned)k.K / 2u, srb = (unsigned)k.K / 64u;
         if (kind == K_QKV) {
             const int row0 = (k.p0 / (HD / 2)) * HD + k.p0 % (HD / 2);
@@ -540,6 +547,34 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         sg[tid] = g;
     }
     __syncthreads();
+    // Per pair: the partial sums of the slots that met it, as indices into
+    // part[slot][run] in slot order, so that an epilogue thread reads its
+    // pair's few partials with independent loads.  Slot s touches pairs
+    // pair0 .. pair0 + nr - 1 (run r is pair pair0 + r).
+    {
+        u32* pinfo = (u32*)(lds + OFF_PINFO);
+        uint8_t* plist = (uint8_t*)(lds + OFF_PLIST);
+        for (int i = tid; i < 4 * MAXNP; i += NT) {
+            const int kind = i / MAXNP, pl = i % MAXNP;
+            const KGeo& k = kg[kind];
+            if (pl >= k.np) continue;
+            int base = 0, cnt = 0;
+#pragma unroll 4
+            for (int s = 0; s < NSLOT; ++s) {
+                const SGeo& q = sg[kind * NSLOT + s];
+                const int nr = q.len > 0 ? (q.u0 + q.len - 1) / k.S - q.pair0 + 1 : 0;
+                base += min(max(pl - q.pair0, 0), nr);              // entries of earlier pairs
+                if (pl >= q.pair0 && pl < q.pair0 + nr) ++cnt;
+            }
+            pinfo[kind * MAXNP + pl] = ((u32)base << 8) | (u32)cnt;
+            int e = base;
+            for (int s = 0; s < NSLOT; ++s) {
+                const SGeo& q = sg[kind * NSLOT + s];
+                const int nr = q.len > 0 ? (q.u0 + q.len - 1) / k.S - q.pair0 + 1 : 0;
+                if (pl >= q.pair0 && pl < q.pair0 + nr) plist[kind * NSLOT * MAXRUN + e++] = (uint8_t)(s * MAXRUN + (pl - q.pair0));
+            }
+        }
+    }
     {   // residual rows of layer 0 (rows p and p + D/2 of this unit's Wo / W_down pairs)
         const KGeo& k = kg[K_WO];
         for (int i = tid; i < k.np; i += NT) {
@@ -555,7 +590,6 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
     Unit ring[RD];
 #pragma unroll
     for (int i = 0; i < RD; ++i) loader_load(Ld, ring[i], kg, sg, tab, A.zero, tid >> 4);
-    int rot = 0;                                         // ring rotation owed by the last consumed phase
 
     for (int ph = 0; ph < 4 * Ap->L; ++ph) {
         const I4D_CONST Args& A = *opaque_ptr(Ap);
@@ -574,7 +608,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 a.kc = tab[l].kc; a.vc = tab[l].vc; a.pos = A.pos;
                 a.cap = A.cap; a.hq = A.Hq; a.hkv = A.Hkv; a.batch = 1; a.max_pos = A.max_pos;
                 a.kvb = 1; a.nsplit = A.nsplit; a.T = A.T; a.qscale = A.qscale;
-                const AttnGeo g = attn_geo(a, c);
+                const AttnGeo g = attn_geo_nk(a, c, p + 1);     // p: this launch's position (-1 if invalid)
                 AttnRegs<HD, ANSW> Rg;
                 attn_load_round<HD, NT, ANSW>(a, g, 0, Rg);
                 s4* qop = (s4*)(lds + NWAVE * (16 * HD + 32) * 4);
@@ -673,18 +707,28 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                     }
                 }
                 __syncthreads();
-                if (tid < 32) {
-                    float M = -INFINITY;
-                    for (int s = 0; s < ns; ++s) M = fmaxf(M, mv[s]);
-                    float Lsum = 0.f, acc = 0.f;
+                {
+                    // every wave: the largest running max over the splits (ns <= 64, one per lane)
+                    float M = (lane < ns) ? mv[lane] : -INFINITY;
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+                    // thread (d, k): dim 32 qd + d, splits k, k + 16, ...; then a sum over the 16 k-lanes
+                    const int d = tid >> 4, kk = tid & 15;
+                    float acc = 0.f, Lsum = 0.f;
                     if (M != -INFINITY) {
-                        for (int s = 0; s < ns; ++s) {
+                        for (int s = kk; s < ns; s += 16) {
                             const float w = exp2f(mv[s] - M);
+                            acc = fmaf(ov[s * 32 + d], w, acc);
                             Lsum = fmaf(lv[s], w, Lsum);
-                            acc = fmaf(ov[s * 32 + tid], w, acc);
                         }
                     }
-                    pk_put((u32*)I4D_RP(u64, oo) + (size_t)h * HD + 32 * qd + tid, Lsum > 0.f ? acc / Lsum : 0.f, tag);
+#pragma unroll
+                    for (int o = 8; o >= 1; o >>= 1) {
+                        acc += __shfl_xor(acc, o);
+                        Lsum += __shfl_xor(Lsum, o);
+                    }
+                    if (kk == 0)
+                        pk_put((u32*)I4D_RP(u64, oo) + (size_t)h * HD + 32 * qd + d, Lsum > 0.f ? acc / Lsum : 0.f, tag);
                 }
                 __syncthreads();
             }
@@ -696,7 +740,13 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             const int K = k.K, ngr = K / 8;
             const bool six = kind == K_QKV;
             // normalised inputs (x, y: K = D <= 8192, two rounds of groups): RMSNorm, then digits
-            auto norm_stage = [&](float (&v)[2][8], const uint16_t* gain) {
+            // the gain words of this thread's groups, loaded before the exchange
+            // fetch so that their latency hides under it
+            auto load_gain = [&](const uint16_t* gain, u32x4 (&gw)[2]) {
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) gw[rr] = ld_g((const u32x4*)(gain + 8 * min(rr * NT + tid, ngr - 1)));
+            };
+            auto norm_stage = [&](float (&v)[2][8], const u32x4 (&gw)[2]) {
                 float ss = 0.f;
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
@@ -708,8 +758,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 for (int rr = 0; rr < 2; ++rr) {
                     const int g = rr * NT + tid;
                     if (g < ngr) {
-                        const u32x4 gw = ld_g((const u32x4*)(gain + 8 * g));
-                        const u32 gws[4] = {gw.x, gw.y, gw.z, gw.w};
+                        const u32 gws[4] = {gw[rr].x, gw[rr].y, gw[rr].z, gw[rr].w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             v[rr][e] *= rs * __uint_as_float((e & 1) ? (gws[e >> 1] & 0xFFFF0000u) : (gws[e >> 1] << 16));
@@ -719,6 +768,8 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             };
             if (kind == K_QKV) {
                 float v[2][8];
+                u32x4 gw[2];
+                load_gain(tab[l].g1, gw);
                 if (l == 0) {                                  // the caller's fp32 input
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr) {
@@ -730,11 +781,13 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 } else {
                     fetch_groups<2, true>(I4D_RP(u64, ox), ngr, tag, v, sp);
                 }
-                norm_stage(v, tab[l].g1);
+                norm_stage(v, gw);
             } else if (kind == K_GU) {
                 float v[2][8];
+                u32x4 gw[2];
+                load_gain(tab[l].g2, gw);
                 fetch_groups<2, false>(I4D_RP(u64, oy), ngr, tag, v, sp);
-                norm_stage(v, tab[l].g2);
+                norm_stage(v, gw);
             } else if (kind == K_WO) {
                 float v[2][8];                                 // q width <= 8192
                 fetch_groups<2, false>(I4D_RP(u64, oo), ngr, tag, v, sp);
@@ -753,9 +806,6 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
 
         // ================= stream this phase's weights through the ring
         {
-            if (rot == 1) { const Unit t = ring[0]; ring[0] = ring[1]; ring[1] = ring[2]; ring[2] = ring[3]; ring[3] = t; }
-            else if (rot == 2) { Unit t = ring[0]; ring[0] = ring[2]; ring[2] = t; t = ring[1]; ring[1] = ring[3]; ring[3] = t; }
-            else if (rot == 3) { const Unit t = ring[3]; ring[3] = ring[2]; ring[2] = ring[1]; ring[1] = ring[0]; ring[0] = t; }
             const int n = uni(k.n), S = k.S;
             const SGeo& s = sg[kind * NSLOT + slot];
             const int len = s.len;
@@ -781,32 +831,31 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 loader_load(Ld, u, kg, sg, tab, A.zero, slot);
                 __builtin_amdgcn_sched_barrier(0);
             };
-            int j = 0;
-            for (; j + RD <= n; j += RD) {
+            for (int j = 0; j < n; j += RD) {                  // n: a multiple of RD
 #pragma unroll
                 for (int i = 0; i < RD; ++i) step(ring[i], j + i);
             }
-#pragma unroll
-            for (int i = 0; i < RD; ++i)
-                if (j + i < n) step(ring[i], j + i);
-            rot = n % RD;
         }
         __syncthreads();
 
         // ================= per-pair totals (fixed slot order) and the phase's epilogue
-        for (int pl = tid; pl < k.np; pl += NT) {
-            const int S = k.S, U = k.U;
+        // One thread per pair (np < NT: see below).  Not a loop: a loop that
+        // stores without loading makes the compiler wait for every load in
+        // flight -- here the next phase's weight ring -- before entering it.
+        static_assert((MAXRUN - 1) * NSLOT < NT, "runs_of() <= MAXRUN bounds the pairs per unit below NT");
+        if (tid < k.np) {
+            const int pl = tid;
             float va = 0.f, vb = 0.f;
-            // the slots whose unit ranges meet this pair's units [pl S, (pl + 1) S), in slot order
-            int s = min(NSLOT - 1, (pl * S * NSLOT) / U);
-            while (s > 0 && sg[kind * NSLOT + s].u0 > pl * S) --s;
-            for (; s < NSLOT; ++s) {
-                const SGeo& q = sg[kind * NSLOT + s];
-                if (q.u0 >= (pl + 1) * S) break;
-                if (q.len == 0 || q.u0 + q.len <= pl * S) continue;     // an empty slot wrote nothing
-                const float2 t = part[s * MAXRUN + (pl - q.pair0)];
-                va += t.x;
-                vb += t.y;
+            {   // the partials of the slots that met this pair, in slot order
+                const u32 pi = ((const u32*)(lds + OFF_PINFO))[kind * MAXNP + pl];
+                const uint8_t* pe = (const uint8_t*)(lds + OFF_PLIST) + kind * NSLOT * MAXRUN + (pi >> 8);
+                const int cnt = (int)(pi & 255u);
+#pragma unroll 4
+                for (int e = 0; e < cnt; ++e) {
+                    const float2 t = part[pe[e]];
+                    va += t.x;
+                    vb += t.y;
+                }
             }
             const int pm = k.p0 + pl;                          // pair index within its matrix
             if (kind == K_QKV) {

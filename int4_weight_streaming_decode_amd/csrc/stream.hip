@@ -54,7 +54,9 @@ namespace {
 constexpr int NT = 512;            // threads per workgroup: 8 waves, two per SIMD
 constexpr int NWAVE = NT / 64;
 constexpr int NSLOT = NT / 16;     // 16-lane slots
-constexpr int RD = 6;              // weight units in flight per lane
+constexpr int RD = 2;              // weight units in flight per lane: two keep a lane's HBM stream
+                                   // busy; deeper rings measured slower (the prefetch burst at each
+                                   // phase boundary delays the exchange loads queued behind it)
 constexpr int HD = 128;
 constexpr int ANSW = 2;            // attention subtiles per wave per load round
 constexpr int PS = 16384;          // LDS bytes per digit plane (K <= 32768)

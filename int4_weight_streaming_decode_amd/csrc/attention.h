@@ -239,17 +239,21 @@ I4D_DEVINL void attn_sub(const AttnGeo& g, int st, const u32x4 (&kr)[HD / 32], c
     const int tv = t0 + 4 * gq;
     const bool kvalid = t0 + r < t_e;               // this lane's K row
     const int vvalid = t_e - tv;                    // keys of this lane's V run in range
-    // scores^T for keys 4gq..4gq+3 of head r
-    f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+    // scores^T for keys 4gq..4gq+3 of head r: four independent accumulators
+    // (q's high and low parts, even and odd dimension blocks) so that the
+    // matrix-core instructions do not wait on each other's results
+    f4 sc[4] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         u32x4 w = kr[kb >> 1];
         if (!kvalid) w = u32x4{0, 0, 0, 0};
         const s4 kop = (kb & 1) ? dwords_to_s4(w.z, w.w) : dwords_to_s4(w.x, w.y);
-        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb) * 64 + lane], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb + 1) * 64 + lane], sc, 0, 0, 0);
+        sc[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb) * 64 + lane], sc[kb & 1], 0, 0, 0);
+        sc[2 + (kb & 1)] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kop, qop[(2 * kb + 1) * 64 + lane], sc[2 + (kb & 1)], 0, 0, 0);
     }
-    float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (sc[0][i] + sc[1][i]) + (sc[2][i] + sc[3][i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (tv + i >= t_e) sv[i] = -INFINITY;

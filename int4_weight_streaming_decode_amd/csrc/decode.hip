@@ -105,7 +105,9 @@ I4D_DEVINL void rope_table(float2* cs, const int* pos_lds, int hd, double base) 
         const int b = idx / half, i = idx - b * half;
         const double theta = pow(base, -2.0 * (double)i / (double)hd);
         const double phi = (double)max(pos_lds[b], 0) * theta;
-        cs[idx] = float2{(float)cos(phi), (float)sin(phi)};
+        double sn, cn;
+        sincos(phi, &sn, &cn);             // one argument reduction for both
+        cs[idx] = float2{(float)cn, (float)sn};
     }
 }
 
@@ -621,27 +623,47 @@ GemvTask make_task(int kind, const i4d_mat* a, const i4d_mat* b, const i4d_mat* 
     return t;
 }
 
-// Raise a kernel's dynamic-LDS limit once per process and device (a host-side
-// cache keyed by the kernel; the attribute only ever grows).
-struct LdsAttr { const void* fn; int dev; size_t bytes; };
-LdsAttr g_lds_attr[256];
-int g_lds_attr_n = 0;
+// Every kernel is launched only if it runs without scratch memory: a
+// private segment would mean the compiler put registers or arrays in slow
+// per-lane memory (and that the dispatch must provide it).  The build checks
+// every kernel's code object for one; this is the run-time check of the
+// same, once per kernel and device (a host-side cache).
+struct KernAttr { const void* fn; int dev; size_t lds; bool scratch_free; };
+KernAttr g_kern_attr[512];
+int g_kern_attr_n = 0;
 
-template <class K>
-hipError_t set_lds(K kernel, size_t bytes) {
+KernAttr* kern_attr(const void* fn) {
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const void* fn = (const void*)kernel;
-    for (int i = 0; i < g_lds_attr_n; ++i)
-        if (g_lds_attr[i].fn == fn && g_lds_attr[i].dev == dev) {
-            if (g_lds_attr[i].bytes >= bytes) return hipSuccess;
-            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-            if (e == hipSuccess) g_lds_attr[i].bytes = bytes;
-            return e;
-        }
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess && g_lds_attr_n < 256) g_lds_attr[g_lds_attr_n++] = LdsAttr{fn, dev, bytes};
-    return e;
+    for (int i = 0; i < g_kern_attr_n; ++i)
+        if (g_kern_attr[i].fn == fn && g_kern_attr[i].dev == dev) return &g_kern_attr[i];
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, fn) != hipSuccess) return nullptr;
+    if (g_kern_attr_n >= 512) return nullptr;
+    g_kern_attr[g_kern_attr_n] = KernAttr{fn, dev, 0, fa.localSizeBytes == 0};
+    return &g_kern_attr[g_kern_attr_n++];
+}
+
+// I4D_OK, or I4D_EUNSUPPORTED for a kernel that needs scratch, or I4D_EHIP.
+template <class K>
+int scratch_free(K kernel) {
+    const KernAttr* a = kern_attr((const void*)kernel);
+    if (!a) return I4D_EHIP;
+    return a->scratch_free ? I4D_OK : I4D_EUNSUPPORTED;
+}
+
+// The scratch check, then the kernel's dynamic-LDS limit raised to `bytes`
+// (the attribute only ever grows).
+template <class K>
+int set_lds(K kernel, size_t bytes) {
+    KernAttr* a = kern_attr((const void*)kernel);
+    if (!a) return I4D_EHIP;
+    if (!a->scratch_free) return I4D_EUNSUPPORTED;
+    if (a->lds >= bytes) return I4D_OK;
+    if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+        return I4D_EHIP;
+    a->lds = bytes;
+    return I4D_OK;
 }
 
 constexpr size_t LDS_LIMIT = 160 * 1024;
@@ -697,7 +719,7 @@ int launch_rows_t(const GemvTask& t, int nwg, const float* x, int x_stride, int 
                   float* y, const float* resid, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
-    if (set_lds(k_gemv_rows<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    if (const int rc_ = set_lds(k_gemv_rows<FMT, NB>, lds)) return rc_;
     launch_k(k_gemv_rows<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, x_stride, nb, gain, eps, y, resid);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -706,7 +728,7 @@ template <int FMT, int NB>
 int launch_swiglu_t(const GemvTask& t, int nwg, const float* x, int nb, const uint16_t* gain, float eps, float* act, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
-    if (set_lds(k_gemv_swiglu<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    if (const int rc_ = set_lds(k_gemv_swiglu<FMT, NB>, lds)) return rc_;
     launch_k(k_gemv_swiglu<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, act);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -722,7 +744,7 @@ int launch_qkv_t(const GemvTask& t, int nwg, const float* x, int nb, const uint1
                  float* q, const i4d_kv* kv, uint16_t* kvn, int hq, int hkv, double base, int* status, int kvb, hipStream_t s) {
     const size_t lds = gemv_lds_bytes<FMT, NB, PREC_QKV>(t.k);
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
-    if (set_lds(k_gemv_qkv<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+    if (const int rc_ = set_lds(k_gemv_qkv<FMT, NB>, lds)) return rc_;
     launch_k(k_gemv_qkv<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, x, nb, gain, eps, pos, max_pos, q,
                        kv->k, kv->v, kvn, kv->capacity, hq, hkv, base, status, kvb, kv_map(kv));
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
@@ -736,7 +758,8 @@ int launch_lm_t(const GemvTask& t, int nwg, const float* h, int nb, u64* wg_keys
     } else {
         const size_t lds = gemv_lds_bytes<FMT, NB, PREC_STD>(t.k) + (size_t)GEMV_NT * 12;
         if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
-        if (set_lds(k_lm_head<FMT, NB>, lds) != hipSuccess) return I4D_EHIP;
+        if (const int rc_ = set_lds(k_lm_head<FMT, NB>, lds)) return rc_;
+        if (const int rc_ = scratch_free(k_lm_finalize)) return rc_;
         launch_k(k_lm_head<FMT, NB>, dim3(nwg), dim3(GEMV_NT), lds, s, t, h, nb, wg_keys, smp);
         hipLaunchKernelGGL(k_lm_finalize, dim3(1), dim3(256), 0, s, (const u64*)wg_keys, nwg, MAX_BATCH, nb, tok, mx);
         return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
@@ -864,7 +887,7 @@ template <int HD, bool PAGED>
 int launch_attention_t(const AttnArgs& a, hipStream_t s) {
     const int items = a.batch * a.hkv * a.nsplit;
     const size_t lds = attn_lds_bytes<HD, ATTN_NT>();
-    if (set_lds(k_attention<HD, PAGED>, lds) != hipSuccess) return I4D_EHIP;
+    if (const int rc_ = set_lds(k_attention<HD, PAGED>, lds)) return rc_;
     launch_k(k_attention<HD, PAGED>, dim3(items), dim3(ATTN_NT), lds, s, a);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -917,7 +940,7 @@ size_t mfma_part_bytes(const MfmaPlan& p, int nb) { return p.kb > 1 ? (size_t)p.
 
 // Scratch of one batched phase: staged activations (up to two planes),
 // partial sums, validated positions and the RoPE table.
-struct MfmaScratch { size_t xs, part, posv, cs, total; };
+struct MfmaScratch { size_t xs, part, posv, cs, xsc, total; };
 MfmaScratch mfma_scratch(int kmax, int nb, size_t part_bytes, int hd) {
     MfmaScratch m;
     size_t off = 0;
@@ -926,6 +949,7 @@ MfmaScratch mfma_scratch(int kmax, int nb, size_t part_bytes, int hd) {
     m.part = take(part_bytes);
     m.posv = take((size_t)nb * 4);
     m.cs = take((size_t)nb * (hd / 2) * 8);
+    m.xsc = take((size_t)nb * 4);
     m.total = off;
     return m;
 }
@@ -946,6 +970,7 @@ MfmaTask mfma_task(const GemvTask& t, const MfmaPlan& p, char* base, const MfmaS
     memset(&m, 0, sizeof(m));
     m.t = t;
     m.xs = (const uint32_t*)(base + S.xs);
+    m.xscale = (const float*)(base + S.xsc);
     m.part = (float*)(base + S.part);
     m.cnt = cnt;
     m.tiles = p.tiles; m.kb = p.kb; m.spb = p.spb; m.nsteps = p.nsteps;
@@ -960,12 +985,14 @@ int mfma_stage(int prec, int nb, const float* x, int stride, int batch, int K, c
     uint32_t* xs = (uint32_t*)(base + S.xs);
     int* posv = rope ? (int*)(base + S.posv) : nullptr;
     float2* cs = rope ? (float2*)(base + S.cs) : nullptr;
+    float* xsc = (float*)(base + S.xsc);
+    if (const int rc_ = scratch_free(prec == 2 ? k_mfma_stage<2> : k_mfma_stage<1>)) return rc_;
     if (prec == 2)
         hipLaunchKernelGGL(k_mfma_stage<2>, dim3(nb), dim3(256), 0, s, x, stride, batch, nb, K, gain, eps, xs, pos, max_pos,
-                           cap, hd, rope_base, posv, cs, status);
+                           cap, hd, rope_base, posv, cs, status, xsc);
     else
         hipLaunchKernelGGL(k_mfma_stage<1>, dim3(nb), dim3(256), 0, s, x, stride, batch, nb, K, gain, eps, xs, pos, max_pos,
-                           cap, hd, rope_base, posv, cs, status);
+                           cap, hd, rope_base, posv, cs, status, xsc);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
 
@@ -973,7 +1000,7 @@ template <class Kern, class... A>
 int launch_mfma(Kern kernel, size_t lds, const MfmaPlan& p, hipStream_t s, A... args) {
     if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
     if (p.kb > 1 && p.rbs > WS_MAX_MCNT) return I4D_EUNSUPPORTED;
-    if (set_lds(kernel, lds) != hipSuccess) return I4D_EHIP;
+    if (const int rc_ = set_lds(kernel, lds)) return rc_;
     launch_k(kernel, dim3(p.nwg), dim3(MfmaGeo<16, 1>::NT), lds, s, args...);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -1127,6 +1154,7 @@ int i4d_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     if (!aligned(ws, 256)) return I4D_EALIGN;
     if (ws_bytes < WS_HEADER) return I4D_EWORKSPACE;
     // the status word lives in the header; zero the whole workspace
+    if (const int rc_ = scratch_free(k_fill_zero)) return rc_;
     hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(256), 0, (hipStream_t)stream, (int*)ws, ws_bytes / 4);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -1218,6 +1246,7 @@ static int lm_head_impl(bool run, const i4d_mat* w_lm, int32_t batch, const floa
         const MfmaPlan p = mfma_plan(t.total_pairs, w_lm->k, nb, 1, false);
         if (p.nwg > LM_MAX_WG) return I4D_EUNSUPPORTED;
         if (!run) return I4D_OK;
+        if ((rc = scratch_free(k_lm_finalize))) return rc;
         char* base = w + WS_LM_END;
         if ((rc = mfma_stage(1, nb, h, w_lm->k, batch, w_lm->k, nullptr, 0.f, base, S, nullptr, 0, 0, 64, 0.0, false,
                              (int*)(w + WS_STATUS), s)))
@@ -1333,6 +1362,7 @@ int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t bat
     int rc;
     if ((rc = validate_ws(ws, ws_bytes, WS_HEADER))) return rc;
     const dim3 grid((d_model + 255) / 256, batch);
+    if (const int rc_ = scratch_free(k_embed)) return rc_;
     hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, (hipStream_t)stream, table, vocab, d_model, tokens, x_out,
                        (int*)((char*)ws + WS_STATUS));
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
@@ -1355,6 +1385,8 @@ static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_l
     if ((rc = lm_head_impl(false, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp))) return rc;
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((cfg->d_model + 255) / 256, batch);
+    if (const int rc_ = scratch_free(k_embed)) return rc_;
+    if (const int rc_ = scratch_free(k_advance)) return rc_;
     hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, s, embed, w_lm->n, cfg->d_model, (const int*)tokens, x0,
                        (int*)((char*)ws + WS_STATUS));
     if (hipGetLastError() != hipSuccess) return I4D_EHIP;
@@ -1388,6 +1420,7 @@ int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {
     int rc;
     if ((rc = validate_mat(wm, wm->n, wm->k, I4D_WEIGHT_INT4, wm->group))) return rc;
     const int ng = (wm->k + wm->group - 1) / wm->group;
+    if (const int rc_ = scratch_free(k_dequant)) return rc_;
     hipLaunchKernelGGL(k_dequant, dim3(1024), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)wm->data,
                        (const uint16_t*)wm->scales, wm->n, wm->k, wm->group, ng, out);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
@@ -1482,6 +1515,7 @@ int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream) {
 int i4d_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     if (!buf || !sink || bytes == 0) return I4D_EINVAL;
     if (!aligned(buf, 16) || bytes % 16 || !aligned(sink, 4)) return I4D_EALIGN;
+    if (const int rc_ = scratch_free(k_read_probe)) return rc_;
     hipLaunchKernelGGL(k_read_probe, dim3(num_cus()), dim3(512), 0, (hipStream_t)stream, (const u32x4*)buf, bytes / 16, sink);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }

@@ -30,6 +30,10 @@
 //   sum (c - 8) x = acc - (1032 * sum x_even + 1152 * sum a_odd)
 // (a_odd = the stored x_odd / 16).  The bf16 group scale multiplies the unit's
 // partial sum once.  This costs about 1.2 VALU operations per weight.
+// fp16 range: each staged chunk is multiplied by a power of two 2^-e (e = 0
+// unless its largest staged magnitude reaches 2^15), so every staged value is
+// a finite fp16 whatever the activations' range; 2^e is stored beside the
+// chunk's correction and multiplies the group scale (both exact).
 #pragma once
 #include "common.h"
 
@@ -64,11 +68,11 @@ template <> struct FmtT<FMT_BF16_GEN>  { static constexpr int LANE_B = 4,  LANE_
 
 // ---------------------------------------------------------------- LDS footprint of a staged activation
 // int4: PREC planes of fp16 pairs [NB][K/2] (4 B each; plane 0 the fp16 value,
-// plane 1 the fp16 of the remainder) + corrections [NB][K/LANE_W] fp32.
+// plane 1 the fp16 of the remainder) + per chunk {correction, 2^e} [NB][K/LANE_W] fp32 pairs.
 // bf16: fp32 [NB][K].
 template <int FMT, int NB, int PREC>
 __host__ __device__ constexpr int act_lds_bytes(int K) {
-    return FmtT<FMT>::INT4 ? NB * (PREC * K * 2 + (K / FmtT<FMT>::LANE_W) * 4) : NB * K * 4;
+    return FmtT<FMT>::INT4 ? NB * (PREC * K * 2 + (K / FmtT<FMT>::LANE_W) * 8) : NB * K * 4;
 }
 
 // ---------------------------------------------------------------- pair -> rows
@@ -204,7 +208,7 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
         const int nchunk = K / F::LANE_W;
         int c = seg * 16 + lane16;                      // lane chunk index along K
         if (FMT == FMT_INT4_GEN) c = min(c, nchunk - 1);  // masked lanes read a valid chunk, scale 0
-        const float* corr = (const float*)(act_lds + NB * PREC * K * 2);
+        const float2* corr = (const float2*)(act_lds + NB * PREC * K * 2);
         float sa, sb;
         if constexpr (FMT == FMT_INT4_FAST) {
             // the half of the scale word: the parity of the group index
@@ -219,8 +223,8 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const float cr = corr[b * nchunk + c];
-            float acca = -cr, accb = -cr;
+            const float2 cr = corr[b * nchunk + c];         // {correction, 2^e of the chunk}
+            float acca = -cr.x, accb = -cr.x;
 #pragma unroll
             for (int pl = 0; pl < PREC; ++pl) {
                 const h2* act = (const h2*)act_lds + (size_t)(pl * NB + b) * (K >> 1);
@@ -240,8 +244,8 @@ I4D_DEVINL void consume_unit(const Unit<FMT>& u, const char* act_lds, int K, int
                     accb = dot8_int4(u.b, xa, accb);
                 }
             }
-            ra[b] = fmaf(sa, acca, ra[b]);
-            rb[b] = fmaf(sb, accb, rb[b]);
+            ra[b] = fmaf(sa * cr.y, acca, ra[b]);
+            rb[b] = fmaf(sb * cr.y, accb, rb[b]);
         }
     } else {
         const float* act = (const float*)act_lds;
@@ -345,22 +349,33 @@ I4D_DEVINL void stage_write_chunk(char* act_lds, const f4 (&xv)[StagePre<FMT>::N
     for (int bb = 0; bb < NB; ++bb) if (bb == b && b < nb) scale = rs[bb];
     if constexpr (F::INT4) {
         h2* act = (h2*)act_lds;
-        float* corr = (float*)(act_lds + NB * PREC * K * 2);
+        float2* corr = (float2*)(act_lds + NB * PREC * K * 2);
+        // staged values a (odd positions pre-divided by 16, exact), then the
+        // chunk's power of two: largest |a| below 2^15 after it
+        float av[F::LANE_W];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < F::LANE_W; ++q) {
+            float v = xv[q >> 2][q & 3] * scale;
+            if (has_gain) {
+                const u32 gw = gv[q >> 3][(q >> 1) & 3];
+                v *= __uint_as_float((q & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+            }
+            av[q] = (q & 1) ? v * 0.0625f : v;
+            amax = fmaxf(amax, fabsf(av[q]));
+        }
+        int ex = 0;
+        (void)frexpf(amax, &ex);                      // amax < 2^ex (0 for amax = 0; inf/NaN stay as they are)
+        const int sh = max(ex - 15, 0);
+        const float down = ldexpf(1.f, -sh);
         double ce = 0.0;
 #pragma unroll
         for (int d = 0; d < F::LANE_W / 8; ++d) {
-            // a[e]: staged value (odd positions pre-divided by 16, exact);
             // hi = fp16(a), lo = fp16(a - hi) when two planes are used
             _Float16 hi[8], lo[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int q = d * 8 + e;
-                float v = xv[q >> 2][q & 3] * scale;
-                if (has_gain) {
-                    const u32 gw = gv[q >> 3][(q >> 1) & 3];
-                    v *= __uint_as_float((q & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
-                }
-                const float a = (e & 1) ? v * 0.0625f : v;
+                const float a = av[d * 8 + e] * down;
                 hi[e] = (_Float16)a;
                 lo[e] = (_Float16)(a - (float)hi[e]);
                 const double w = (e & 1) ? 1152.0 : 1032.0;
@@ -379,7 +394,7 @@ I4D_DEVINL void stage_write_chunk(char* act_lds, const f4 (&xv)[StagePre<FMT>::N
                 dl[3] = h2{lo[3], lo[7]};
             }
         }
-        corr[b * nchunk + c] = (float)ce;
+        corr[b * nchunk + c] = float2{(float)ce, ldexpf(1.f, sh)};
     } else {
         float* act = (float*)act_lds + (size_t)b * K + k0;
         const u32x4 gw = gv[0];

@@ -74,6 +74,7 @@ struct MfmaGeo {
 struct MfmaTask {
     GemvTask t;                // matrices and pair mapping (int4, fast layout)
     const uint32_t* xs;        // staged activations: fp16 pairs [PREC][NB][K/2] (uint32 = two halves)
+    const float* xscale;       // [NB] power of two that multiplies sequence b's results (its row was staged times its inverse)
     float* part;               // partial sums [tiles][kb][NB][16] (K split only)
     int* cnt;                  // arrival counters, one per row block (K split only)
     int tiles;                 // ceil(total_pairs / 8)
@@ -89,7 +90,9 @@ struct MfmaTask {
 // x is RMS-normalised with `gain` when one is given (h = x / sqrt(mean x^2 +
 // eps) * gain), converted to fp16 in the unpack's order ((0,4), (1,5), (2,6),
 // (3,7) of every 8 inputs, odd ones divided by 16), optionally with a second
-// plane holding the fp16 of the remainder.
+// plane holding the fp16 of the remainder.  fp16 range: the row is staged
+// times 2^-e, e = 0 unless its largest staged magnitude reaches 2^15, and
+// xscale[b] = 2^e multiplies the sequence's results (both exact).
 // RoPE set-up rides along for the q/k/v phase: slot b validates pos[b]
 // (pos_out[b] = -1 and the status bit when out of range) and writes the
 // float64-derived cos/sin of its angles, cs[b][i] for i < hd/2.
@@ -97,8 +100,9 @@ template <int PREC>
 __global__ void __launch_bounds__(256) k_mfma_stage(const float* x, int x_stride, int nb, int NBP, int K, const uint16_t* gain,
                                                     float eps, uint32_t* xs,
                                                     const int* pos, int max_pos, int cap, int hd, double base,
-                                                    int* pos_out, float2* cs, int* status) {
+                                                    int* pos_out, float2* cs, int* status, float* xscale) {
     __shared__ float red[4];
+    __shared__ float redm[4];
     const int b = blockIdx.x, tid = i4d_tid();
     const int nsteps = K >> 7;
     const bool live = b < nb;
@@ -132,30 +136,54 @@ __global__ void __launch_bounds__(256) k_mfma_stage(const float* x, int x_stride
         rs = 1.0f / sqrtf((((red[0] + red[1]) + red[2]) + red[3]) / (float)K + eps);
     }
 
-    // 8-input chunks, one per thread per round
-    for (int c = tid; c < nsteps * 16; c += 256) {
+    // the staged values of 8-input chunk c (odd ones divided by 16)
+    auto staged = [&](int c, float (&a)[8]) {
         const int k0 = c * 8;
-        float v[8];
         if (live) {
             const f4 a0 = ld_g((const f4*)(xb + k0)), a1 = ld_g((const f4*)(xb + k0 + 4));
-            v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w; v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+            a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
             if (gain != nullptr) {
                 const u32x4 gw = ld_g((const u32x4*)(gain + k0));
                 const u32 g4[4] = {gw.x, gw.y, gw.z, gw.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const u32 w = g4[e >> 1];
-                    v[e] = v[e] * rs * __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    a[e] = a[e] * rs * __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
                 }
             }
+#pragma unroll
+            for (int e = 1; e < 8; e += 2) a[e] *= 0.0625f;
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            for (int e = 0; e < 8; ++e) a[e] = 0.f;
         }
+    };
+    // the row's power of two: largest staged |a| below 2^15 after it
+    float amax = 0.f;
+    for (int c = tid; c < nsteps * 16; c += 256) {
+        float a[8];
+        staged(c, a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
+    }
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
+    if ((tid & 63) == 0) redm[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+    int ex = 0;
+    (void)frexpf(amax, &ex);                          // amax < 2^ex (0 for amax = 0)
+    const int sh = max(ex - 15, 0);
+    const float down = ldexpf(1.f, -sh);
+    if (tid == 0) xscale[b] = ldexpf(1.f, sh);
+
+    // 8-input chunks, one per thread per round
+    for (int c = tid; c < nsteps * 16; c += 256) {
+        float v[8];
+        staged(c, v);
         _Float16 hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float a = (e & 1) ? v[e] * 0.0625f : v[e];
+            const float a = v[e] * down;
             hi[e] = (_Float16)a;
             lo[e] = (_Float16)(a - (float)hi[e]);
         }
@@ -375,7 +403,9 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int seq = n * 16 + 4 * q + e;      // padded sequences (seq >= nb) keep key 0
-                    const u64 k = (ok && seq < m.nb) ? argmax_key(epi.score(acc[t][n][e], seq, (u32)row), (u32)row) : 0ull;
+                    const u64 k = (ok && seq < m.nb)
+                                      ? argmax_key(epi.score(acc[t][n][e] * ld_g(m.xscale + seq), seq, (u32)row), (u32)row)
+                                      : 0ull;
                     best[n][e] = k > best[n][e] ? k : best[n][e];
                 }
         }
@@ -411,7 +441,10 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
                     const float o = shfl_xor_f(v, 8);
                     const int pair = 8 * tile[t] + r;
                     const int b = n * 16 + 4 * q + e;
-                    if (r < 8 && pair < m.t.total_pairs && b < m.nb) epi(0, pair, b, v, o);
+                    if (r < 8 && pair < m.t.total_pairs && b < m.nb) {
+                        const float xsc = ld_g(m.xscale + b);
+                        epi(0, pair, b, v * xsc, o * xsc);
+                    }
                 }
     } else {
         // K split: partials through to memory, the last workgroup of the row
@@ -448,7 +481,8 @@ I4D_DEVINL void mfma_gemm(const MfmaTask& m, char* lds, Epi& epi, u64* wg_keys) 
                     va += ld_g(pp + (size_t)k * NB * 16);
                     vb += ld_g(pp + (size_t)k * NB * 16 + 8);
                 }
-                if (pair < m.t.total_pairs) epi(0, pair, b, va, vb);
+                const float xsc = ld_g(m.xscale + b);
+                if (pair < m.t.total_pairs) epi(0, pair, b, va * xsc, vb * xsc);
             }
         }
     }

@@ -422,13 +422,26 @@ I4D_DEVINL void digitize8(char* act, float* cs, int g, float (&v)[8], bool six, 
     // four planes: |a| <= 2^14, digits of a + 0x8888; six: |a| <= 2^22, of a + 0x888888
     const int sh = (six ? 22 : 14) - ex;
     const u32 bias = six ? 0x888888u : 0x8888u;
-    u32 pl[6] = {0, 0, 0, 0, 0, 0};
+    u32 dg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int a = (int)rintf(ldexpf(v[e], sh));
-        const u32 dg = ((u32)a + bias) ^ bias;                 // digit p in nibble p
+        dg[e] = ((u32)a + bias) ^ bias;                        // digit p in nibble p
+    }
+    // plane q = nibble q of dg[0..7] in nibbles 0..7: gather byte b of the even
+    // and of the odd inputs into two words; the low nibbles of those bytes are
+    // plane 2b, the high nibbles plane 2b + 1, interleaved even/odd
+    u32 pl[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int q = 0; q < 6; ++q) pl[q] |= ((dg >> (4 * q)) & 15u) << (4 * e);
+    for (int b = 0; b < 3; ++b) {
+        if (b == 2 && !six) break;
+        const int sb = 8 * b;
+        const u32 ev = ((dg[0] >> sb) & 0xFFu) | (((dg[2] >> sb) & 0xFFu) << 8) | (((dg[4] >> sb) & 0xFFu) << 16) |
+                       (((dg[6] >> sb) & 0xFFu) << 24);
+        const u32 od = ((dg[1] >> sb) & 0xFFu) | (((dg[3] >> sb) & 0xFFu) << 8) | (((dg[5] >> sb) & 0xFFu) << 16) |
+                       (((dg[7] >> sb) & 0xFFu) << 24);
+        pl[2 * b] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+        pl[2 * b + 1] = ((ev >> 4) & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
     }
     u32* p = (u32*)act + g;
     p[0] = pl[0];
@@ -483,7 +496,9 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
     if (tid < HD / 2) {
         const double theta = pow(A.base, -2.0 * (double)tid / (double)HD);
         const double phi = (double)max(p, 0) * theta;
-        rope[tid] = float2{(float)cos(phi), (float)sin(phi)};
+        double sn, cn;
+        sincos(phi, &sn, &cn);
+        rope[tid] = float2{(float)cn, (float)sn};
     }
     if (tid < 4) {
         KGeo k;

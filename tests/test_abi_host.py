@@ -37,6 +37,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, s), s
 
 
+def test_no_kernel_of_the_library_needs_scratch(lib):
+    """Every kernel in the built library's gfx950 code object declares a
+    private segment of 0 bytes (no register spills or arrays in per-lane
+    scratch memory); the launchers also refuse such a kernel at run time."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import __graft_entry__ as g
+    assert g.kernels_with_scratch(B.LIB_PATH) == []
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(code)

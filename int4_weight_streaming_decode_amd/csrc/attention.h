@@ -292,6 +292,97 @@ I4D_DEVINL void attn_sub(const AttnGeo& g, int st, const u32x4 (&kr)[HD / 32], c
     }
 }
 
+// Two subtiles st0 and st1 (st1 may lie past the item: all its keys masked) in
+// one online-softmax step, on gfx950's 16x16x32 bf16 matrix instruction.  The
+// instruction pairs A and B by (lane group, element), so each operand only has
+// to list the K axis in the same order on both sides:
+//   scores^T[key][head]: A = the K row (lane (r, g): key r, the 8 dims of its
+//     16-byte load), B = q^T (lane (r, g): head r, the same 8 dims), one
+//     instruction per 32-dim block and per q part (high, low);
+//   O[head][dim] += P V: element j of lane group g is key 4g + j of subtile
+//     st0 for j < 4, key 4g + j - 4 of st1 otherwise: A = P (lane (r, g): head
+//     r), B = V (lane (r, g): dim 16 nt + r), so both subtiles take two
+//     instructions per 16-dim tile (P high, P low).
+// q32: the q operand in LDS, q32[(2 mm + p) * 64 + lane] = part p (0 high, 1
+// low bf16) of dims 32 mm + 8 g .. + 7 of head r.  Same arithmetic per key as
+// attn_sub, up to summation order.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+I4D_DEVINL bf16x8 as_bf16x8(u32 a, u32 b, u32 c, u32 d) { return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d}); }
+
+template <int HD>
+I4D_DEVINL void attn_sub2(const AttnGeo& g, int st0, int st1, const u32x4 (&kr0)[HD / 32], const u32x2 (&vr0)[HD / 16],
+                          const u32x4 (&kr1)[HD / 32], const u32x2 (&vr1)[HD / 16], const u32x4* q32,
+                          float& m, float& lsum, f4 (&O)[HD / 16]) {
+    constexpr int NKB = HD / 16, NMM = HD / 32;
+    const int lane = i4d_tid() & 63, r = lane & 15, gq = lane >> 4;
+    const int t_e = g.t_e;
+    const int t00 = g.t_s + 16 * st0, t01 = g.t_s + 16 * st1;
+    const int tv0 = t00 + 4 * gq, tv1 = t01 + 4 * gq;
+    const bool kv0 = t00 + r < t_e, kv1 = t01 + r < t_e;
+    f4 s0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    f4 s1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mm = 0; mm < NMM; ++mm) {
+        const bf16x8 qh = __builtin_bit_cast(bf16x8, q32[(2 * mm) * 64 + lane]);
+        const bf16x8 ql = __builtin_bit_cast(bf16x8, q32[(2 * mm + 1) * 64 + lane]);
+        const u32x4 w0 = kv0 ? kr0[mm] : u32x4{0, 0, 0, 0};
+        const u32x4 w1 = kv1 ? kr1[mm] : u32x4{0, 0, 0, 0};
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, w0), k1 = __builtin_bit_cast(bf16x8, w1);
+        s0[mm & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh, s0[mm & 1], 0, 0, 0);
+        s1[mm & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh, s1[mm & 1], 0, 0, 0);
+        s0[mm & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, ql, s0[mm & 1], 0, 0, 0);
+        s1[mm & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, ql, s1[mm & 1], 0, 0, 0);
+    }
+    float sv0[4], sv1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv0[i] = (tv0 + i < t_e) ? s0[0][i] + s0[1][i] : -INFINITY;
+        sv1[i] = (tv1 + i < t_e) ? s1[0][i] + s1[1][i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv0[0], sv0[1]), fmaxf(sv0[2], sv0[3])), fmaxf(fmaxf(sv1[0], sv1[1]), fmaxf(sv1[2], sv1[3])));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mnew = fmaxf(m, mx);                // finite: subtile st0 has a valid key
+    const float alpha = exp2f(m - mnew);
+    float p0[4], p1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p0[i] = exp2f(sv0[i] - mnew);
+        p1[i] = exp2f(sv1[i] - mnew);
+    }
+    lsum = lsum * alpha + (((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3])));
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ai = shfl_f(alpha, 4 * gq + i);
+#pragma unroll
+        for (int nt = 0; nt < NKB; ++nt) O[nt][i] *= ai;
+    }
+    uint16_t ph0[4], pl0[4], ph1[4], pl1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ph0[i] = f32_to_bf16(p0[i]);
+        pl0[i] = f32_to_bf16(p0[i] - bf16_to_f32(ph0[i]));
+        ph1[i] = f32_to_bf16(p1[i]);
+        pl1[i] = f32_to_bf16(p1[i] - bf16_to_f32(ph1[i]));
+    }
+    auto pk2 = [](uint16_t a, uint16_t b) { return (u32)a | ((u32)b << 16); };
+    const bf16x8 ph = as_bf16x8(pk2(ph0[0], ph0[1]), pk2(ph0[2], ph0[3]), pk2(ph1[0], ph1[1]), pk2(ph1[2], ph1[3]));
+    const bf16x8 pl = as_bf16x8(pk2(pl0[0], pl0[1]), pk2(pl0[2], pl0[3]), pk2(pl1[0], pl1[1]), pk2(pl1[2], pl1[3]));
+    const int vv0 = t_e - tv0, vv1 = t_e - tv1;
+    const u32 m00 = vv0 >= 2 ? 0xFFFFFFFFu : (vv0 == 1 ? 0x0000FFFFu : 0u);
+    const u32 m01 = vv0 >= 4 ? 0xFFFFFFFFu : (vv0 == 3 ? 0x0000FFFFu : 0u);
+    const u32 m10 = vv1 >= 2 ? 0xFFFFFFFFu : (vv1 == 1 ? 0x0000FFFFu : 0u);
+    const u32 m11 = vv1 >= 4 ? 0xFFFFFFFFu : (vv1 == 3 ? 0x0000FFFFu : 0u);
+#pragma unroll
+    for (int nt = 0; nt < NKB; ++nt) {
+        const bf16x8 v = as_bf16x8(vr0[nt].x & m00, vr0[nt].y & m01, vr1[nt].x & m10, vr1[nt].y & m11);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, v, O[nt], 0, 0, 0);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, O[nt], 0, 0, 0);
+    }
+}
+
 // The q^T operand of head r of the item's group (hi and lo bf16 parts, dims in
 // the K-row order of attn_sub), from this lane's 4 x NKB fp32 q values (dims
 // 32(kb/2) + 8gq + 4(kb%2) + i), scaled by qscale (0 for lanes past the group).

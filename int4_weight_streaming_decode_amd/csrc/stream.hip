@@ -218,13 +218,33 @@ I4D_DEVINL void pk_put(u32* p, float v, u32 tag) { st_dev_t(p, pk_word(v, tag));
 I4D_DEVINL float pk_val(u32 w) { return __uint_as_float(w & 0xFFFFFF00u); }
 
 // This thread's input groups g = tid + r * NT (r < RM; groups past ngr read
-// the last group again) from an exchange vector: all plain loads first (one
-// memory round trip for the lot), then device-scope reloads of the words whose
-// tag is not yet current, until every tag is (bounded).  WIDE: 64-bit words (value, 32-bit
-// tag); otherwise packed 32-bit words.
+// the last group again) from an exchange vector: first a device-scope wait
+// for the last word of the thread's last group, then plain loads of all its
+// groups (one memory round trip for the lot), then device-scope reloads of
+// the words whose tag is not yet current, until every tag is (bounded).
+// The first wait keeps the plain loads from running ahead of most producers:
+// a plain load of a line not yet written leaves that stale line in the L2,
+// where the other compute units of the XCD then find it and must reload.
+// WIDE: 64-bit words (value, 32-bit tag); otherwise packed 32-bit words.
 template <int RM, bool WIDE>
 I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8], Spin& sp) {
     const int tid = i4d_tid();
+    {
+        const int gl = min(tid + (RM - 1) * NT, ngr - 1);
+        int polls = 0;
+        while (!sp.dead) {
+            bool ok;
+            if constexpr (WIDE) ok = (u32)(ld_dev_t((const u64*)src + 8 * (size_t)gl + 7) >> 32) == tag;
+            else ok = (ld_dev_t((const u32*)src + 8 * (size_t)gl + 7) & 0xFFu) == (tag & 0xFFu);
+            if (ok) break;
+            if (++polls > SPIN_LIMIT) {
+                sp.dead = true;
+                raise_status(sp.status, I4D_DEV_BARRIER_TIMEOUT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
     if constexpr (WIDE) {
         const u64* p = (const u64*)src;
         u64 w[RM][8];
@@ -628,27 +648,29 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 const AttnGeo g = attn_geo_nk(a, c, p + 1);     // p: this launch's position (-1 if invalid)
                 AttnRegs<HD, ANSW> Rg;
                 attn_load_round<HD, NT, ANSW>(a, g, 0, Rg);
-                s4* qop = (s4*)(lds + NWAVE * (16 * HD + 32) * 4);
+                u32x4* q32 = (u32x4*)(lds + NWAVE * (16 * HD + 32) * 4);   // [HD / 32][2][64]
                 uint16_t* knew = (uint16_t*)(lds + ATT_LDS);
                 uint16_t* vnew = knew + HD;
                 const int r = lane & 15, gq = lane >> 4;
                 if (wave == 0) {
-                    // q^T operand of head r of the group, one 4-dim block at a time (attn_q_operand's layout)
+                    // q^T operand of head r of the group for the 16x16x32 instruction: per
+                    // 32-dim block mm, the 8 dims 32 mm + 8 gq .. + 7 as bf16 high and low parts
                     const u64* qrow = I4D_RP(u64, oq) + (size_t)(g.j * G + min(r, G - 1)) * HD + 8 * gq;
                     const float qs = (r < G) ? A.qscale : 0.f;
 #pragma unroll 1
-                    for (int kb = 0; kb < HD / 16; ++kb) {
-                        float t4[4];
-                        ll_get<4>(qrow + 32 * (kb >> 1) + 4 * (kb & 1), tag, t4, sp);
-                        uint16_t hv[4], lv[4];
+                    for (int mm = 0; mm < HD / 32; ++mm) {
+                        float t8[8];
+                        ll_get<8>(qrow + 32 * mm, tag, t8, sp);
+                        u32 hv[4], lv[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const float v = t4[q] * qs;
-                            hv[q] = f32_to_bf16(v);
-                            lv[q] = f32_to_bf16(v - bf16_to_f32(hv[q]));
+                            const float v0 = t8[2 * q] * qs, v1 = t8[2 * q + 1] * qs;
+                            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+                            hv[q] = (u32)h0 | ((u32)h1 << 16);
+                            lv[q] = (u32)f32_to_bf16(v0 - bf16_to_f32(h0)) | ((u32)f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
                         }
-                        qop[(2 * kb) * 64 + lane] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-                        qop[(2 * kb + 1) * 64 + lane] = pack_bf16x4(lv[0], lv[1], lv[2], lv[3]);
+                        q32[(2 * mm) * 64 + lane] = u32x4{hv[0], hv[1], hv[2], hv[3]};
+                        q32[(2 * mm + 1) * 64 + lane] = u32x4{lv[0], lv[1], lv[2], lv[3]};
                     }
                 } else if (wave <= 2) {
                     float t2[2];
@@ -690,7 +712,16 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                                 }
                             }
                         }
-                        if (st < g.nsub) attn_sub<HD>(g, st, Rg.k[i], Rg.v[i], qop, m, lsum, O);
+                    }
+                    // the round's subtiles two at a time (an odd last one with a masked partner)
+#pragma unroll
+                    for (int i = 0; i < ANSW; i += 2) {
+                        const int st0 = (rnd * ANSW + i) * NWAVE + wave;
+                        if (st0 >= g.nsub) continue;
+                        if (i + 1 < ANSW)
+                            attn_sub2<HD>(g, st0, st0 + NWAVE, Rg.k[i], Rg.v[i], Rg.k[i + 1], Rg.v[i + 1], q32, m, lsum, O);
+                        else
+                            attn_sub2<HD>(g, st0, g.nsub, Rg.k[i], Rg.v[i], Rg.k[i], Rg.v[i], q32, m, lsum, O);
                     }
                 }
                 attn_waves_to_lds<HD, NT>(lds, m, lsum, O);

@@ -644,8 +644,18 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 memset(&a, 0, sizeof(a));
                 a.kc = tab[l].kc; a.vc = tab[l].vc; a.pos = A.pos;
                 a.cap = A.cap; a.hq = A.Hq; a.hkv = A.Hkv; a.batch = 1; a.max_pos = A.max_pos;
-                a.kvb = 1; a.nsplit = A.nsplit; a.T = A.T; a.qscale = A.qscale;
-                const AttnGeo g = attn_geo_nk(a, c, p + 1);     // p: this launch's position (-1 if invalid)
+                a.kvb = 1; a.nsplit = A.nsplit; a.qscale = A.qscale;
+                // Splits of this launch's cached keys 0 .. p - 1 (whole 16-key tiles); the
+                // new key p joins the split that holds it, or the last one when p falls
+                // just past them (p a multiple of nsplit * 16): its K and V come from the
+                // exchange, so that extra subtile needs no load (see the rounds below).
+                const int ns = A.nsplit;
+                a.T = 16 * max(1, ((max(p, 0) + 15) / 16 + ns - 1) / ns);
+                AttnGeo g = attn_geo_nk(a, c, p + 1);           // p: this launch's position (-1 if invalid)
+                if (g.s == ns - 1 && g.t_s < p + 1) {
+                    g.t_e = p + 1;
+                    g.nsub = (g.t_e - g.t_s + 15) / 16;
+                }
                 AttnRegs<HD, ANSW> Rg;
                 attn_load_round<HD, NT, ANSW>(a, g, 0, Rg);
                 u32x4* q32 = (u32x4*)(lds + NWAVE * (16 * HD + 32) * 4);   // [HD / 32][2][64]
@@ -687,7 +697,16 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 for (int nt = 0; nt < HD / 16; ++nt) O[nt] = f4{0.f, 0.f, 0.f, 0.f};
                 const int nround = (g.nsub + NWAVE * ANSW - 1) / (NWAVE * ANSW);
                 for (int rnd = 0; rnd < nround; ++rnd) {
-                    if (rnd > 0) attn_load_round<HD, NT, ANSW>(a, g, rnd, Rg);
+                    if (rnd > 0) {
+                        // no load for a round whose only subtile of this wave is the new key alone
+                        bool need = false;
+#pragma unroll
+                        for (int i = 0; i < ANSW; ++i) {
+                            const int st = (rnd * ANSW + i) * NWAVE + wave;
+                            need = need || (st < g.nsub && !(g.t_s + 16 * st == g.kpos && g.kpos == g.t_e - 1));
+                        }
+                        if (need) attn_load_round<HD, NT, ANSW>(a, g, rnd, Rg);
+                    }
 #pragma unroll
                     for (int i = 0; i < ANSW; ++i) {
                         const int st = (rnd * ANSW + i) * NWAVE + wave;
@@ -726,7 +745,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 }
                 attn_waves_to_lds<HD, NT>(lds, m, lsum, O);
                 __syncthreads();
-                const int ns = A.nsplit, hb = g.j * G;
+                const int hb = g.j * G;
                 auto put = [&](int h, int d, float M, float Lv, float acc) {
                     u64* pr = I4D_RP(u64, opart) + ((size_t)(hb + h) * ns + g.s) * (HD + 2);
                     ll_put(pr + 2 + d, acc, tag);

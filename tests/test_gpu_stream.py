@@ -61,6 +61,8 @@ def _check_caches(got, before, ref, pos, what):
     ("s512", 1, 127),         # one attention subtile per split
     ("s512", 3, 5000),        # three chained layers, several subtiles per split
     ("s512", 1, 40000),       # splits of more than one load round
+    ("s512", 1, 1024),        # p = splits * 16: the new key extends the last split by one subtile
+    ("s512", 1, 16384),       # ... which is then a second round holding the new key alone
     ("g7", 2, 2049),          # 7 query heads per KV head, q/k/v split over 28 + 4 + 4 heads
 ])
 def test_stream_stack_matches_oracle(name, n_layers, pos):

@@ -64,8 +64,8 @@ KERNEL_NAMES_BATCHED = {"qkv": "k_mfma_qkv", "attention": "k_attention<128, fals
 # this profile by two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size, with a hash of the kernel sources it was taken
 # on.  Reported only while the sources still hash the same.
-TRAFFIC_RECORDS = [os.path.join(ROOT, "profiles", f) for f in ("stream_decode_27b_int4_hbm_traffic.md",
-                                                                 "gate_up_27b_int4_hbm_traffic.md")]
+TRAFFIC_RECORDS = [os.path.join(ROOT, "profiles", f) for f in ("k_stream_decode_27b_lm_b1_hbm_traffic.md",
+                                                                 "phase_launches_gate_up_27b_int4_hbm_traffic.md")]
 
 
 def sources_sha256() -> str:

@@ -550,6 +550,12 @@ I4D_DEVINL void attn_item(const AttnArgs& a, int item, char* lds, AttnRegs<HD, N
         const f4* src = (const f4*)(a.po + (hrow0 + h) * a.pstride * HD) + d4;
         const int per = (ns + chunks - 1) / chunks;
         const int s_lo = min(chunk * per, ns), s_hi = min(ns, s_lo + per);
+        // Plain loads of the other splits' partials are safe only because no
+        // workgroup reads these lines earlier in this launch, so the XCD's L2
+        // cannot hold a stale copy: the writers stored them through to memory
+        // and raised the counter after the stores completed.  Any read of
+        // a.pm / a.pl / a.po before this point would break that and must then
+        // use device-scope loads (ld_dev).
         f4 pv[MB];
 #pragma unroll
         for (int u = 0; u < MB; ++u) pv[u] = ld_g(src + (size_t)min(s_lo + u, ns - 1) * (HD / 4));

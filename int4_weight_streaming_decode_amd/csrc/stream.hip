@@ -8,9 +8,17 @@
 // drain; the pages' cure is fusion so that nothing stops the weight stream
 // (Unsloth article 二.1, Roofline reply 三).  Here one workgroup per compute
 // unit walks all phases of all layers, and its weight stream never stops at a
-// phase boundary: each lane keeps RD units of weights in flight, and the loads
-// run ahead into the next phase (weights do not depend on activations) while
-// the workgroup waits for the activations that phase needs.
+// phase boundary (weights do not depend on activations).
+//
+// Two roles per workgroup.  Two of its ten waves only move weights: they
+// walk the units of every phase of every layer in order and copy them into a
+// ring in LDS, as far ahead as the ring allows.  The other eight waves stage
+// the activations, take the exchange waits, form the dot products from the
+// ring and run attention and the epilogues.  A wave's vector-memory loads
+// complete in issue order, so a wave that both prefetched weights and waited
+// for an exchange value would wait for its prefetch as well; with the roles
+// in different waves, the weight stream runs on through every exchange wait,
+// staging and epilogue until the ring is full.
 //
 // Exchange between workgroups.  Every value one workgroup hands to another
 // (q, the new k/v, attention partials, merged heads, residual stream, SwiGLU
@@ -51,20 +59,31 @@
 namespace i4d_stream {
 namespace {
 
-constexpr int NT = 512;            // threads per workgroup: 8 waves, two per SIMD
+constexpr int NT = 640;            // threads per workgroup: 10 waves, eight consumers (two per SIMD) and two loaders
 constexpr int NWAVE = NT / 64;
-constexpr int NSLOT = NT / 16;     // 16-lane slots
-constexpr int RD = 2;              // weight units in flight per lane: two keep a lane's HBM stream
-                                   // busy; deeper rings measured slower (the prefetch burst at each
-                                   // phase boundary delays the exchange loads queued behind it)
+constexpr int NLW = 2;             // loader waves: they only copy weights from HBM into the LDS ring
+constexpr int NCW = NWAVE - NLW;   // consumer waves: staging, exchange, dot products, attention, epilogues
+constexpr int NCT = NCW * 64;      // consumer threads (thread ids 0 .. NCT - 1)
+constexpr int CPL = NCW / NLW;     // consumer waves fed by one loader wave
+constexpr int NSLOT = NCT / 16;    // 16-lane slots of the consumers
+constexpr int SPL = NSLOT / NLW;   // slots fed by one loader wave
+static_assert(SPL == 4 * CPL && NLW * CPL == NCW, "a loader wave feeds whole consumer waves");
+// One step of one loader's half of the ring: for each of its consumer waves,
+// 1 KB of row-a codes and 1 KB of row-b codes (16 bytes per consumer lane),
+// then the two scale words of each row of each of its slots.
+constexpr int HSTEP = CPL * 2 * 1024 + SPL * 16;
+constexpr int LDEPTH = 3;          // steps a loader wave keeps in flight (registers)
+constexpr int NBMAX = 16;          // ring steps at most
 constexpr int HD = 128;
 constexpr int ANSW = 2;            // attention subtiles per wave per load round
-constexpr int PS = 16384;          // LDS bytes per digit plane (K <= 32768)
 constexpr int MAXRUN = 8;          // pair runs per slot per phase
 constexpr int MAX_LAYERS = 128;    // layer table kept in LDS
 constexpr int MAX_RES = 64;        // residual rows per compute unit: pairs of Wo / W_down
-constexpr int KMAX = 2 * PS;       // largest K: 4 bits per input in each digit plane
-constexpr int SPIN_LIMIT = 1 << 17;
+constexpr int KMAX = 32768;        // largest K
+constexpr int RMN = 2;             // staging rounds of NCT groups of 8 for K <= 8192 (d_model, q width)
+constexpr int RMD = 5;             // staging rounds per pass for W_down's input (d_ff <= 20480: one pass)
+constexpr int SPIN_LIMIT = 1 << 17;   // polls of an exchange word
+constexpr int WAIT_LIMIT = 1 << 23;   // polls of a wait between the waves of one workgroup
 
 enum { K_QKV = 0, K_WO = 1, K_GU = 2, K_DN = 3 };
 
@@ -85,23 +104,24 @@ constexpr int LPTR_WORDS = (int)(sizeof(LPtr) / 8);
 // proportion to their rows); Wo and W_down rows (p, p + D/2); gate row p with
 // up row p.  The pairs of a compute unit are cut into units of 16 lanes x 16
 // bytes per row (512 inputs) and the units into one contiguous range per
-// 16-lane slot; every slot runs n iterations (short ranges load a harmless
-// repeat of their first unit and skip it).
+// 16-lane slot; every slot runs n steps (a short range skips its last ones).
 struct KGeo {
     int S;                        // units per row (K / 512)
     int K;
     int p0, np;                   // this unit's first pair and pair count (within its matrix)
-    int U, n;                     // units, iterations per slot
+    int U, n;                     // units, steps per slot
     int mia, mib;                 // table index of the matrix of row a, row b
     int mat;                      // q/k/v: 0, 1, 2
     unsigned ca_off, cb_off;      // code byte offsets of pair p0's rows a and b
     unsigned sa_off, sb_off;      // scale byte offsets
-    unsigned jump, jumps;         // q/k/v: extra advance at a head boundary (codes, scales)
+    unsigned jump;                // q/k/v: extra code advance at a head boundary
     int jper;                     // units between head boundaries (0: none)
 };
+// The scale byte offset of a unit is its code byte offset / 32 (two bytes of
+// scale per 64 bytes of codes), so the loader only tracks the latter.
 struct SGeo {                     // per (kind, slot)
     int len, seg0, cnt0, u0, pair0;   // pair0: local index of the slot's first pair
-    unsigned off0, soff0;         // byte offsets within the unit's code / scale streams (lane 0 of the slot)
+    unsigned off0;                // byte offset of the slot's first unit in its code stream (lane 0)
 };
 
 struct Args {
@@ -114,8 +134,10 @@ struct Args {
     int D, F, Hq, Hkv;
     float eps, qscale;
     double base;
-    int nsplit, T;                 // attention: splits per KV head, keys per split
+    int nsplit;                    // attention: splits per KV head
     int cq, ck;                    // compute units [0, cq): q rows, [cq, ck): k rows, [ck, nwg): v rows
+    int ps, nb;                    // LDS bytes per digit plane; ring steps
+    unsigned off_act, off_ring;    // LDS offsets of the staging / attention area and of the ring
     char* lbase;                   // exchange regions: lbase + l * lstride
     size_t lstride;
     unsigned ox, oq, okv, opart, oo, oy, oact;   // byte offsets in a region
@@ -125,19 +147,27 @@ struct Args {
 };
 
 // ------------------------------------------------------------------ LDS layout
-constexpr int ATT_LDS = NWAVE * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8;   // attn_lds_bytes<HD, NT>
-constexpr int A_BYTES = ((std::max(4 * PS + KMAX / 32 * 4, ATT_LDS + 2 * HD * 2) + 255) / 256) * 256;
-constexpr int OFF_PART = A_BYTES;                                  // float2 [NSLOT][MAXRUN]
+// Fixed part first; then the layer table; then (offsets per launch, from the
+// shapes) the staging area -- digit planes and run scales, or attention's and
+// the merge's working set -- and the weight ring, NLW halves of nb steps.
+constexpr int ATT_LDS = NCW * (16 * HD + 32) * 4 + (HD / 16) * 2 * 64 * 8;   // attn_lds_bytes<HD, NCT>
+constexpr int MERGE_LDS = (64 + 64 + 64 * 32) * 4;
+constexpr int OFF_PART = 0;                                        // float2 [NSLOT][MAXRUN]
 constexpr int OFF_RES = OFF_PART + NSLOT * MAXRUN * 8;             // float [4][MAX_RES]: x rows a, b; y rows a, b
 constexpr int OFF_ROPE = OFF_RES + 4 * MAX_RES * 4;                // float2 [HD / 2]
 constexpr int OFF_KG = OFF_ROPE + (HD / 2) * 8;                    // KGeo [4]
 constexpr int OFF_SG = OFF_KG + 4 * (int)sizeof(KGeo);             // SGeo [4][NSLOT]
-constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [NWAVE]
+constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [2][NCW]
 constexpr int MAXNP = (MAXRUN - 1) * NSLOT;                        // pairs per unit and phase (runs_of() <= MAXRUN)
-constexpr int OFF_PINFO = OFF_RED + NWAVE * 4;                     // u32 [4][MAXNP]: first entry << 8 | count
+constexpr int OFF_PINFO = OFF_RED + 2 * NCW * 4;                   // u32 [4][MAXNP]: first entry << 8 | count
 constexpr int OFF_PLIST = OFF_PINFO + 4 * MAXNP * 4;               // u8 [4][NSLOT * MAXRUN]: part indices, pair-major
-constexpr int OFF_TAB = ((OFF_PLIST + 4 * NSLOT * MAXRUN + 255) / 256) * 256; // LPtr [L]
-constexpr size_t lds_bytes(int L) { return (size_t)OFF_TAB + (size_t)L * sizeof(LPtr); }
+constexpr int OFF_SYNC = ((OFF_PLIST + 4 * NSLOT * MAXRUN + 15) / 16) * 16;   // u32 [16], see below
+constexpr int OFF_TAB = ((OFF_SYNC + 64 + 255) / 256) * 256;       // LPtr [L]
+// words of the sync block
+constexpr int SY_READY = 0;        // [NLW]: steps the loader wave has written into its half
+constexpr int SY_CONS = 4;         // [NCW]: steps the consumer wave has read
+constexpr int SY_BAR = 12;         // arrivals at the consumers' barriers
+constexpr int SY_ABORT = 13;       // set by a wave that gave up an intra-workgroup wait
 
 // ------------------------------------------------------------------ helpers
 typedef u64 u64x2 __attribute__((ext_vector_type(2)));
@@ -217,20 +247,21 @@ I4D_DEVINL u32 pk_word(float v, u32 tag) {
 I4D_DEVINL void pk_put(u32* p, float v, u32 tag) { st_dev_t(p, pk_word(v, tag)); }
 I4D_DEVINL float pk_val(u32 w) { return __uint_as_float(w & 0xFFFFFF00u); }
 
-// This thread's input groups g = tid + r * NT (r < RM; groups past ngr read
-// the last group again) from an exchange vector: first a device-scope wait
-// for the last word of the thread's last group, then plain loads of all its
-// groups (one memory round trip for the lot), then device-scope reloads of
-// the words whose tag is not yet current, until every tag is (bounded).
-// The first wait keeps the plain loads from running ahead of most producers:
-// a plain load of a line not yet written leaves that stale line in the L2,
-// where the other compute units of the XCD then find it and must reload.
+// This consumer thread's input groups g = g0 + tid + r * NCT (r < RM; groups
+// past ngr read the last group again) from an exchange vector: first a
+// device-scope wait for the last word of the thread's last group, then plain
+// loads of all its groups (one memory round trip for the lot), then
+// device-scope reloads of the words whose tag is not yet current, until every
+// tag is (bounded).  The first wait keeps the plain loads from running ahead
+// of most producers: a plain load of a line not yet written leaves that stale
+// line in the L2, where the other compute units of the XCD then find it and
+// must reload.
 // WIDE: 64-bit words (value, 32-bit tag); otherwise packed 32-bit words.
 template <int RM, bool WIDE>
-I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8], Spin& sp) {
+I4D_DEVINL void fetch_groups(const void* src, int g0, int ngr, u32 tag, float (&v)[RM][8], Spin& sp) {
     const int tid = i4d_tid();
     {
-        const int gl = min(tid + (RM - 1) * NT, ngr - 1);
+        const int gl = min(g0 + tid + (RM - 1) * NCT, ngr - 1);
         int polls = 0;
         while (!sp.dead) {
             bool ok;
@@ -250,7 +281,7 @@ I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8
         u64 w[RM][8];
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
-            const int g = min(tid + r * NT, ngr - 1);
+            const int g = min(g0 + tid + r * NCT, ngr - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u64x2 t = ld_g((const u64x2*)(p + 8 * (size_t)g) + i);
@@ -268,7 +299,7 @@ I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const int g = min(tid + r * NT, ngr - 1);
+                const int g = min(g0 + tid + r * NCT, ngr - 1);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     if ((u32)(w[r][e] >> 32) != tag) w[r][e] = ld_dev_t(p + 8 * (size_t)g + e);
@@ -284,7 +315,7 @@ I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8
         u32 w[RM][8];
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
-            const int g = min(tid + r * NT, ngr - 1);
+            const int g = min(g0 + tid + r * NCT, ngr - 1);
             const u32x4 a = ld_g((const u32x4*)(p + 8 * (size_t)g)), b = ld_g((const u32x4*)(p + 8 * (size_t)g) + 1);
             w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
             w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
@@ -300,7 +331,7 @@ I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
-                const int g = min(tid + r * NT, ngr - 1);
+                const int g = min(g0 + tid + r * NCT, ngr - 1);
 #pragma unroll
                 for (int e = 0; e < 8; e += 2)
                     if ((w[r][e] & 0xFFu) != t8 || (w[r][e + 1] & 0xFFu) != t8) {
@@ -316,73 +347,189 @@ I4D_DEVINL void fetch_groups(const void* src, int ngr, u32 tag, float (&v)[RM][8
     }
 }
 
-// ------------------------------------------------------------------ weight units
-struct Unit { u32x4 a, b; u32 sa, sb; };
+// ------------------------------------------------------------------ waits between the waves of one workgroup
+// LDS words written by one wave and polled by another.  LDS executes the
+// operations of one wave in issue order, so a word written after some data is
+// seen only after that data; the signal fences keep the compiler from moving
+// memory operations across the hand-off.  Every wait is bounded: a wave that
+// gives up raises I4D_DEV_BARRIER_TIMEOUT and sets the abort word, after
+// which no wave of the workgroup waits any more (results are then wrong, but
+// the launch ends).
+#define I4D_LDS __attribute__((address_space(3)))
+I4D_DEVINL u32 lds_get(const u32* p) { return uniu(*(const volatile I4D_LDS u32*)p); }
+I4D_DEVINL void lds_put(u32* p, u32 v) { *(volatile I4D_LDS u32*)p = v; }
 
-// The lane's stream of weight units over all matrix-vector phases of the
-// step, RD units ahead of the consumer.
-struct Loader {
-    const uint8_t* ca; const uint8_t* cb; const uint8_t* sa; const uint8_t* sb;   // scalar bases
-    unsigned off, soff, jump, jumps;
-    int cnt, jper, len, j, n, ph, nph;
+// Wait until f() (a re-read of some LDS words) reaches `need`; returns the last value read.
+template <class F>
+I4D_DEVINL u32 lds_wait(F f, u32 need, u32* sync, int* status) {
+    u32 v = f();
+    for (int polls = 0; (int)(v - need) < 0; ) {
+        if (lds_get(sync + SY_ABORT)) break;
+        if (++polls > WAIT_LIMIT) {
+            lds_put(sync + SY_ABORT, 1u);
+            if ((i4d_tid() & 63) == 0) raise_status(status, I4D_DEV_BARRIER_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = f();
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return v;
+}
+
+// A barrier of the NCW consumer waves only (the loader waves never stop for
+// one): each wave adds one arrival and waits for all arrivals of this barrier.
+struct CBar {
+    u32* sync;
+    int* status;
+    u32 target;                  // arrivals that complete this wave's next barrier
 };
+I4D_DEVINL void cbar(CBar& b) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes have landed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if ((i4d_tid() & 63) == 0)
+        __hip_atomic_fetch_add((I4D_LDS u32*)(b.sync + SY_BAR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    b.target += NCW;
+    u32* s = b.sync;
+    (void)lds_wait([&] { return lds_get(s + SY_BAR); }, b.target, s, b.status);
+}
 
-I4D_DEVINL void loader_next(Loader& Ld, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero, int slot) {
+// ------------------------------------------------------------------ the loader waves
+// One loader lane copies, per step, the 16 bytes of row a and of row b that
+// consumer lane `lane` of each of its CPL consumer waves will use, and one
+// scale word (lanes < 4 * SPL).  Loads go through buffer descriptors built
+// once per phase (scalar base, 32-bit lane offset), and a slot's offset at
+// step j is computed from j alone: its first unit's offset, 256 bytes per
+// unit, and the q/k/v head jump once j reaches the slot's head boundary (a
+// slot holds at most MAXRUN * S units, fewer than a head's 64 * S, so it
+// crosses at most one).  A step past the slot's range reads the phase's first
+// bytes again.
+struct LSlot { unsigned off0; int len, jat; };     // jat: first step past the head boundary
+struct Loader {
+    __amdgpu_buffer_rsrc_t ca, cb;
+    const uint8_t* sa; const uint8_t* sb;      // scale rows (a lane picks one: a plain global load)
+    unsigned jump;
+    int j, n, ph, nph;
+    LSlot cs[CPL], ss;
+};
+struct Stage { u32x4 a[CPL], b[CPL]; u32 s; };
+
+I4D_DEVINL __amdgpu_buffer_rsrc_t rsrc_of(const uint8_t* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)uni(p), (short)0, -1, 0x00020000);
+}
+
+I4D_DEVINL void loader_next(Loader& Ld, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero, int lw) {
     do { ++Ld.ph; } while (Ld.ph < Ld.nph && kg[Ld.ph & 3].n == 0);
-    if (Ld.ph >= Ld.nph) {       // past the last phase: repeat reads of a zero block, never consumed
-        Ld.ca = Ld.cb = Ld.sa = Ld.sb = uni(zero);
-        Ld.n = 0x7FFFFFFF; Ld.j = 0; Ld.len = 0; Ld.jper = 0; Ld.cnt = 1 << 30;
-        Ld.off = Ld.soff = 0; Ld.jump = Ld.jumps = 0;
+    if (Ld.ph >= Ld.nph) {       // past the last phase: reads of a zero block, never consumed
+        Ld.ca = Ld.cb = rsrc_of(zero);
+        Ld.sa = Ld.sb = uni(zero);
+        Ld.n = 0x7FFFFFFF; Ld.j = 0; Ld.jump = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) Ld.cs[i] = LSlot{0u, 0, 1 << 30};
+        Ld.ss = LSlot{0u, 0, 1 << 30};
         return;
     }
     const int kind = Ld.ph & 3, l = Ld.ph >> 2;
     const KGeo& k = kg[kind];
     const LPtr& t = tab[l];
-    Ld.ca = uni(t.c[k.mia] + k.ca_off);
-    Ld.cb = uni(t.c[k.mib] + k.cb_off);
+    Ld.ca = rsrc_of(t.c[k.mia] + k.ca_off);
+    Ld.cb = rsrc_of(t.c[k.mib] + k.cb_off);
     Ld.sa = uni(t.s[k.mia] + k.sa_off);
     Ld.sb = uni(t.s[k.mib] + k.sb_off);
     Ld.n = uni(k.n); Ld.j = 0;
-    Ld.jump = uniu(k.jump); Ld.jumps = uniu(k.jumps); Ld.jper = uni(k.jper);
-    const SGeo& s = sg[kind * NSLOT + slot];
-    const int lane16 = i4d_tid() & 15;
-    Ld.len = s.len; Ld.cnt = s.cnt0;
-    Ld.off = s.off0 + (unsigned)lane16 * 16u;
-    Ld.soff = s.soff0 + 4u * (unsigned)(lane16 >> 3);
+    Ld.jump = uniu(k.jump);
+    const int lane = i4d_tid() & 63;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const SGeo& s = sg[kind * NSLOT + SPL * lw + 4 * i + (lane >> 4)];
+        Ld.cs[i] = LSlot{s.off0 + (unsigned)(lane & 15) * 16u, s.len, s.cnt0};
+    }
+    const SGeo& s = sg[kind * NSLOT + SPL * lw + min(lane >> 2, SPL - 1)];
+    Ld.ss = LSlot{s.off0, s.len, s.cnt0};
 }
 
-// Issue the loads of the next unit into u (always the same four loads, so
-// the compiler's wait counts stay exact) and advance.
-I4D_DEVINL void loader_load(Loader& Ld, Unit& u, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero, int slot) {
-    if (Ld.j == Ld.n) loader_next(Ld, kg, sg, tab, zero, slot);
-    const bool v = Ld.j < Ld.len;
-    // a skipped unit reads the slot's first 16 bytes and scale word again
-    const unsigned lane16 = (unsigned)i4d_tid() & 15u;
-    const unsigned o = v ? Ld.off : lane16 * 16u;
-    const unsigned so = v ? Ld.soff : 4u * (lane16 >> 3);
-    u.a = ld_g_nt((const u32x4*)(Ld.ca + o));
-    u.b = ld_g_nt((const u32x4*)(Ld.cb + o));
-    u.sa = ld_g((const u32*)(Ld.sa + so));
-    u.sb = ld_g((const u32*)(Ld.sb + so));
-    if (v) {
-        Ld.off += 256u;
-        Ld.soff += 8u;
-        if (--Ld.cnt == 0) { Ld.off += Ld.jump; Ld.soff += Ld.jumps; Ld.cnt = Ld.jper; }
+// Issue the loads of the next step into st (always the same 2 CPL + 1 loads,
+// so that the compiler's wait counts stay exact) and advance.
+I4D_DEVINL void loader_issue(Loader& Ld, Stage& st, const KGeo* kg, const SGeo* sg, const LPtr* tab, const uint8_t* zero,
+                             int lw) {
+    if (Ld.j == Ld.n) loader_next(Ld, kg, sg, tab, zero, lw);
+    const int lane = i4d_tid() & 63, j = Ld.j;
+    const unsigned jo = (unsigned)j << 8;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const LSlot& q = Ld.cs[i];
+        const unsigned o = j < q.len ? q.off0 + jo + (j >= q.jat ? Ld.jump : 0u) : (unsigned)(lane & 15) * 16u;
+        st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(Ld.ca, (int)o, 0, 2);     // nontemporal
+        st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(Ld.cb, (int)o, 0, 2);
+    }
+    {
+        const LSlot& q = Ld.ss;
+        const unsigned so = (j < q.len ? (q.off0 + jo + (j >= q.jat ? Ld.jump : 0u)) >> 5 : 0u) + 4u * (unsigned)(lane & 1);
+        const size_t ds = ((lane >> 1) & 1) ? (size_t)((uintptr_t)Ld.sb - (uintptr_t)Ld.sa) : 0u;
+        st.s = ld_g((const u32*)(Ld.sa + ds + so));
     }
     ++Ld.j;
 }
 
-// ------------------------------------------------------------------ the dot product of one unit
-// Digit planes 0..3 at act + p * PS; for the q/k/v projection (six planes,
-// K <= 8192 so each plane fills at most half of its slot) planes 4 and 5 sit
-// in the upper halves of slots 0 and 1.
-constexpr int P4 = PS / 2, P5 = PS + PS / 2;
+// Loader wave lw: every step of every phase of every layer, LDEPTH steps in
+// flight in registers; step t goes into ring entry t mod nb of its half once
+// every consumer wave of the half has read the step that entry held.
+I4D_DEVINL void loader_main(const I4D_CONST Args& A, const KGeo* kg, const SGeo* sg, const LPtr* tab, char* ring,
+                            u32* sync, int lw) {
+    const int lane = i4d_tid() & 63;
+    const int nb = uni(A.nb);
+    char* half = ring + (size_t)lw * nb * HSTEP;
+    u32* ready = sync + SY_READY + lw;
+    const u32* cons = sync + SY_CONS + CPL * lw;
+    const int T = uni(A.L * (kg[0].n + kg[1].n + kg[2].n + kg[3].n));
+    Loader Ld;
+    Ld.ph = -1; Ld.nph = 4 * A.L; Ld.j = 0; Ld.n = 0;
+    Stage st[LDEPTH];
+#pragma unroll
+    for (int i = 0; i < LDEPTH; ++i) loader_issue(Ld, st[i], kg, sg, tab, A.zero, lw);
+    auto cmin = [&] {
+        u32 m = lds_get(cons);
+#pragma unroll
+        for (int i = 1; i < CPL; ++i) m = min(m, lds_get(cons + i));
+        return m;
+    };
+    u32 freed = 0;                  // steps every consumer wave of the half has read (last seen)
+    int slot = 0;
+    for (int t0 = 0; t0 < T; t0 += LDEPTH) {
+#pragma unroll
+        for (int i = 0; i < LDEPTH; ++i) {
+            const int t = t0 + i;
+            if (t < T) {
+                if ((int)freed < t - nb + 1) freed = lds_wait(cmin, (u32)(t - nb + 1), sync, A.status);
+                char* dst = half + slot * HSTEP;
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    *(u32x4*)(dst + (2 * q) * 1024 + lane * 16) = st[i].a[q];
+                    *(u32x4*)(dst + (2 * q + 1) * 1024 + lane * 16) = st[i].b[q];
+                }
+                if (lane < 4 * SPL) *(u32*)(dst + CPL * 2048 + lane * 4) = st[i].s;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                if (lane == 0) lds_put(ready, (u32)(t + 1));
+                slot = slot + 1 == nb ? 0 : slot + 1;
+            }
+            loader_issue(Ld, st[i], kg, sg, tab, A.zero, lw);
+        }
+    }
+}
 
-I4D_DEVINL void dot_unit(const Unit& u, const char* act, unsigned aoff, float cs, int hs, bool six, float& ra, float& rb) {
-    const u32x4 d0 = *(const u32x4*)(act + aoff);
-    const u32x4 d1 = *(const u32x4*)(act + PS + aoff);
-    const u32x4 d2 = *(const u32x4*)(act + 2 * PS + aoff);
-    const u32x4 d3 = *(const u32x4*)(act + 3 * PS + aoff);
+// ------------------------------------------------------------------ the dot product of one unit
+// Digit planes 0..3 at act + p * ps; for the q/k/v projection (six planes,
+// K = d_model <= ps, so each plane fills at most half of its slot) planes 4
+// and 5 sit in the upper halves of slots 0 and 1.
+struct Unit { u32x4 a, b; u32 sa, sb; };
+
+I4D_DEVINL void dot_unit(const Unit& u, const char* act, int ps, unsigned aoff, float cs, int hs, bool six, float& ra,
+                         float& rb) {
+    const char* ap = act + aoff;
+    const u32x4 d0 = *(const u32x4*)(ap);
+    const u32x4 d1 = *(const u32x4*)(ap + ps);
+    const u32x4 d2 = *(const u32x4*)(ap + 2 * ps);
+    const u32x4 d3 = *(const u32x4*)(ap + 3 * ps);
     int a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -399,8 +546,8 @@ I4D_DEVINL void dot_unit(const Unit& u, const char* act, unsigned aoff, float cs
     int ia = ((a3 * 16 + a2) * 16 + a1) * 16 + a0;
     int ib = ((b3 * 16 + b2) * 16 + b1) * 16 + b0;
     if (six) {
-        const u32x4 d4 = *(const u32x4*)(act + P4 + aoff);
-        const u32x4 d5 = *(const u32x4*)(act + P5 + aoff);
+        const u32x4 d4 = *(const u32x4*)(ap + ps / 2);
+        const u32x4 d5 = *(const u32x4*)(ap + ps + ps / 2);
         int a4 = 0, a5 = 0, b4 = 0, b5 = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -425,7 +572,7 @@ I4D_DEVINL void dot_unit(const Unit& u, const char* act, unsigned aoff, float cs
 // Eight inputs of group g (inputs 8g..8g+7), already normalised: digits into
 // the four planes, the power of two of the 32-input run (a quad of lanes) into
 // cs.  Non-finite inputs become zeros and raise I4D_DEV_NONFINITE.
-I4D_DEVINL void digitize8(char* act, float* cs, int g, float (&v)[8], bool six, int* status) {
+I4D_DEVINL void digitize8(char* act, int ps, float* cs, int g, float (&v)[8], bool six, int* status) {
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
@@ -463,28 +610,50 @@ I4D_DEVINL void digitize8(char* act, float* cs, int g, float (&v)[8], bool six, 
         pl[2 * b] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
         pl[2 * b + 1] = ((ev >> 4) & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
     }
-    u32* p = (u32*)act + g;
-    p[0] = pl[0];
-    p[PS / 4] = pl[1];
-    p[2 * PS / 4] = pl[2];
-    p[3 * PS / 4] = pl[3];
+    char* p = act + 4 * g;
+    *(u32*)(p) = pl[0];
+    *(u32*)(p + ps) = pl[1];
+    *(u32*)(p + 2 * ps) = pl[2];
+    *(u32*)(p + 3 * ps) = pl[3];
     if (six) {
-        p[P4 / 4] = pl[4];
-        p[P5 / 4] = pl[5];
+        *(u32*)(p + ps / 2) = pl[4];
+        *(u32*)(p + ps + ps / 2) = pl[5];
     }
     if ((i4d_tid() & 3) == 0) cs[g >> 2] = ldexpf(1.f, -sh);
 }
 
-// Sum of one value over the workgroup (every thread gets it).
-I4D_DEVINL float block_sum(float v, float* red) {
+// Sum of one value over the consumer waves (every consumer thread gets it).
+// red holds two sets of NCW slots, used in turn, so one barrier suffices.
+I4D_DEVINL float block_sum(float v, float* red, u32& par, CBar& cb) {
     for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
-    if ((i4d_tid() & 63) == 0) red[i4d_tid() >> 6] = v;
-    __syncthreads();
+    float* r = red + par * NCW;
+    par ^= 1u;
+    if ((i4d_tid() & 63) == 0) r[i4d_tid() >> 6] = v;
+    cbar(cb);
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) t += red[w];
-    __syncthreads();
+    for (int w = 0; w < NCW; ++w) t += r[w];
     return t;
+}
+
+// ------------------------------------------------------------------ attention item of a compute unit
+// Item c = (KV head j, split s) of layer l at this launch's position p (-1 if
+// invalid).  Splits hold whole 16-key tiles of the cached keys 0 .. p - 1; the
+// new key p joins the split that holds it, or the last one when p falls just
+// past them (p a multiple of nsplit * 16): its K and V come from the exchange,
+// so that extra subtile needs no load.
+I4D_DEVINL void attn_setup(const I4D_CONST Args& A, const LPtr* tab, int l, int c, int p, AttnArgs& a, AttnGeo& g) {
+    memset(&a, 0, sizeof(a));
+    a.kc = tab[l].kc; a.vc = tab[l].vc; a.pos = A.pos;
+    a.cap = A.cap; a.hq = A.Hq; a.hkv = A.Hkv; a.batch = 1; a.max_pos = A.max_pos;
+    a.kvb = 1; a.nsplit = A.nsplit; a.qscale = A.qscale;
+    const int ns = A.nsplit;
+    a.T = 16 * max(1, ((max(p, 0) + 15) / 16 + ns - 1) / ns);
+    g = attn_geo_nk(a, c, p + 1);
+    if (g.s == ns - 1 && g.t_s < p + 1) {
+        g.t_e = p + 1;
+        g.nsub = (g.t_e - g.t_s + 15) / 16;
+    }
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -493,21 +662,20 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
     const I4D_CONST Args& A = *(const I4D_CONST Args*)Ap;
     const int tid = i4d_tid();
     const int c = blockIdx.x, nwg = gridDim.x;
-    char* act = lds;                                  // digit planes
-    float* cs = (float*)(lds + 4 * PS);               // run scales
     float2* part = (float2*)(lds + OFF_PART);
     float* res = (float*)(lds + OFF_RES);
     float2* rope = (float2*)(lds + OFF_ROPE);
     KGeo* kg = (KGeo*)(lds + OFF_KG);
     SGeo* sg = (SGeo*)(lds + OFF_SG);
     float* red = (float*)(lds + OFF_RED);
+    u32* sync = (u32*)(lds + OFF_SYNC);
     LPtr* tab = (LPtr*)(lds + OFF_TAB);
-    Spin sp{A.status, false};
-    const u32 tag = ld_g(A.epoch) + 1u;
     const int D = A.D, F = A.F, qw = A.Hq * HD, kvw = A.Hkv * HD;
 
-    // ---- set-up: layer table, position and RoPE table, geometry, residual rows
+    // ---- set-up (all eight waves): layer table, position and RoPE table,
+    // geometry, residual rows, sync words
     for (int i = tid; i < A.L * LPTR_WORDS; i += NT) ((u64*)tab)[i] = ld_g((const u64*)A.table + i);
+    if (tid < 16) sync[tid] = 0u;
     int p = ld_g(A.pos);
     if (p < 0 || p > A.max_pos || p >= A.cap) {
         if (c == 0 && tid == 0) raise_status(A.status, I4D_DEV_BAD_POS);
@@ -525,7 +693,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         const int kind = tid;
         int P, ci, nci, rows_half;
         k.K = kind == K_WO ? qw : kind == K_DN ? F : D;
-        k.mat = 0; k.jump = k.jumps = 0u; k.jper = 0;
+        k.mat = 0; k.jump = 0u; k.jper = 0;
         if (kind == K_QKV) {
             k.mat = c < A.cq ? 0 : c < A.ck ? 1 : 2;
             P = (k.mat == 0 ? qw : kvw) / 2;
@@ -542,17 +710,13 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         k.p0 = (int)(((long long)ci * P) / nci);
         k.np = (int)(((long long)(ci + 1) * P) / nci) - k.p0;
         k.U = k.np * k.S;
-        // steps per slot, a whole number of ring turns: the steps past a
-        // slot's units only issue loads (re-reads of cached words), and every
-        // phase leaves the ring in the same order, the next phase's first RD
-        // units in flight
-        k.n = ((k.U + NSLOT - 1) / NSLOT + RD - 1) / RD * RD;
+        k.n = (k.U + NSLOT - 1) / NSLOT;
         const unsigned rb = (unsigned)k.K / 2u, srb = (unsigned)k.K / 64u;
         if (kind == K_QKV) {
             const int row0 = (k.p0 / (HD / 2)) * HD + k.p0 % (HD / 2);
             k.ca_off = (unsigned)row0 * rb; k.cb_off = k.ca_off + (unsigned)(HD / 2) * rb;
             k.sa_off = (unsigned)row0 * srb; k.sb_off = k.sa_off + (unsigned)(HD / 2) * srb;
-            k.jump = (unsigned)(HD / 2) * rb; k.jumps = (unsigned)(HD / 2) * srb;
+            k.jump = (unsigned)(HD / 2) * rb;
             k.jper = (HD / 2) * k.S;
         } else {
             rows_half = kind == K_GU ? 0 : D / 2;
@@ -571,7 +735,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         const int pl = k.S ? g.u0 / k.S : 0;
         g.seg0 = g.u0 - pl * k.S;
         g.pair0 = pl;
-        const unsigned rb = (unsigned)k.K / 2u, srb = (unsigned)k.K / 64u;
+        const unsigned rb = (unsigned)k.K / 2u;
         int drow = pl;                                   // rows between pair p0's row a and this slot's first row a
         g.cnt0 = 1 << 30;
         if (kind == K_QKV) {
@@ -580,7 +744,6 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             g.cnt0 = (HD / 2 - pa % (HD / 2)) * k.S - g.seg0;
         }
         g.off0 = (unsigned)drow * rb + (unsigned)g.seg0 * 256u;
-        g.soff0 = (unsigned)drow * srb + (unsigned)g.seg0 * 8u;
         sg[tid] = g;
     }
     __syncthreads();
@@ -621,18 +784,28 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
     }
     __syncthreads();
 
-    // ---- prime the weight ring
-    Loader Ld;
-    Ld.ph = -1; Ld.nph = 4 * A.L; Ld.j = 0; Ld.n = 0;
-    Unit ring[RD];
-#pragma unroll
-    for (int i = 0; i < RD; ++i) loader_load(Ld, ring[i], kg, sg, tab, A.zero, tid >> 4);
+    // ---- the loader waves: the weight stream, and nothing else
+    if (tid >= NCT) {
+        loader_main(A, kg, sg, tab, lds + A.off_ring, sync, (tid >> 6) - NCW);
+        return;
+    }
+
+    // ---- the consumer waves: every phase of every layer
+    Spin sp{A.status, false};
+    CBar cb{sync, A.status, 0u};
+    u32 rpar = 0u;                                    // block_sum's set of slots
+    const u32 tag = ld_g(A.epoch) + 1u;
+    int t = 0, rslot = 0;                             // global step, its ring entry
+    u32 rdy = 0u;                                     // steps the loader of this wave's half has written (last seen)
+    AttnRegs<HD, ANSW> Rg;                            // K/V of the attention item's first round
 
     for (int ph = 0; ph < 4 * Ap->L; ++ph) {
         const I4D_CONST Args& A = *opaque_ptr(Ap);
         const int tid = i4d_tid(), lane = tid & 63, wave = tid >> 6, slot = tid >> 4, lane16 = tid & 15;
         const int kind = ph & 3, l = ph >> 2;
-        const int D = A.D, F = A.F, G = A.Hq / A.Hkv;
+        const int D = A.D, F = A.F, G = A.Hq / A.Hkv, ps = A.ps;
+        char* act = lds + A.off_act;                  // digit planes, then run scales (float)
+        float* cs = (float*)(act + 4 * ps);
         // Exchange pointers of this layer, re-derived where used (see opaque_ptr)
 #define I4D_RP(T, field) ((T*)(layer_region(Ap, l) + opaque_ptr(Ap)->field))
 
@@ -641,25 +814,12 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             const int items = A.Hkv * A.nsplit;
             if (c < items) {
                 AttnArgs a;
-                memset(&a, 0, sizeof(a));
-                a.kc = tab[l].kc; a.vc = tab[l].vc; a.pos = A.pos;
-                a.cap = A.cap; a.hq = A.Hq; a.hkv = A.Hkv; a.batch = 1; a.max_pos = A.max_pos;
-                a.kvb = 1; a.nsplit = A.nsplit; a.qscale = A.qscale;
-                // Splits of this launch's cached keys 0 .. p - 1 (whole 16-key tiles); the
-                // new key p joins the split that holds it, or the last one when p falls
-                // just past them (p a multiple of nsplit * 16): its K and V come from the
-                // exchange, so that extra subtile needs no load (see the rounds below).
+                AttnGeo g;
+                attn_setup(A, tab, l, c, p, a, g);
                 const int ns = A.nsplit;
-                a.T = 16 * max(1, ((max(p, 0) + 15) / 16 + ns - 1) / ns);
-                AttnGeo g = attn_geo_nk(a, c, p + 1);           // p: this launch's position (-1 if invalid)
-                if (g.s == ns - 1 && g.t_s < p + 1) {
-                    g.t_e = p + 1;
-                    g.nsub = (g.t_e - g.t_s + 15) / 16;
-                }
-                AttnRegs<HD, ANSW> Rg;
-                attn_load_round<HD, NT, ANSW>(a, g, 0, Rg);
-                u32x4* q32 = (u32x4*)(lds + NWAVE * (16 * HD + 32) * 4);   // [HD / 32][2][64]
-                uint16_t* knew = (uint16_t*)(lds + ATT_LDS);
+                // round 0 of the K/V loads went out during the q/k/v phase (Rg)
+                u32x4* q32 = (u32x4*)(act + NCW * (16 * HD + 32) * 4);   // [HD / 32][2][64]
+                uint16_t* knew = (uint16_t*)(act + ATT_LDS);
                 uint16_t* vnew = knew + HD;
                 const int r = lane & 15, gq = lane >> 4;
                 if (wave == 0) {
@@ -689,27 +849,27 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                     dst[2 * lane] = f32_to_bf16(t2[0]);          // the values are bf16 already: exact
                     dst[2 * lane + 1] = f32_to_bf16(t2[1]);
                 }
-                __syncthreads();
+                cbar(cb);
                 const int stp = (g.kpos >= g.t_s && g.kpos < g.t_e) ? (g.kpos - g.t_s) / 16 : -1;
                 float m = -INFINITY, lsum = 0.f;
                 f4 O[HD / 16];
 #pragma unroll
                 for (int nt = 0; nt < HD / 16; ++nt) O[nt] = f4{0.f, 0.f, 0.f, 0.f};
-                const int nround = (g.nsub + NWAVE * ANSW - 1) / (NWAVE * ANSW);
+                const int nround = (g.nsub + NCW * ANSW - 1) / (NCW * ANSW);
                 for (int rnd = 0; rnd < nround; ++rnd) {
                     if (rnd > 0) {
                         // no load for a round whose only subtile of this wave is the new key alone
                         bool need = false;
 #pragma unroll
                         for (int i = 0; i < ANSW; ++i) {
-                            const int st = (rnd * ANSW + i) * NWAVE + wave;
+                            const int st = (rnd * ANSW + i) * NCW + wave;
                             need = need || (st < g.nsub && !(g.t_s + 16 * st == g.kpos && g.kpos == g.t_e - 1));
                         }
-                        if (need) attn_load_round<HD, NT, ANSW>(a, g, rnd, Rg);
+                        if (need) attn_load_round<HD, NCT, ANSW>(a, g, rnd, Rg);
                     }
 #pragma unroll
                     for (int i = 0; i < ANSW; ++i) {
-                        const int st = (rnd * ANSW + i) * NWAVE + wave;
+                        const int st = (rnd * ANSW + i) * NCW + wave;
                         if (st == stp) {
                             // the new key: its K row and V column from the exchange, not the cache
                             const int t0 = g.t_s + 16 * st;
@@ -735,33 +895,34 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                     // the round's subtiles two at a time (an odd last one with a masked partner)
 #pragma unroll
                     for (int i = 0; i < ANSW; i += 2) {
-                        const int st0 = (rnd * ANSW + i) * NWAVE + wave;
+                        const int st0 = (rnd * ANSW + i) * NCW + wave;
                         if (st0 >= g.nsub) continue;
                         if (i + 1 < ANSW)
-                            attn_sub2<HD>(g, st0, st0 + NWAVE, Rg.k[i], Rg.v[i], Rg.k[i + 1], Rg.v[i + 1], q32, m, lsum, O);
+                            attn_sub2<HD>(g, st0, st0 + NCW, Rg.k[i], Rg.v[i], Rg.k[i + 1], Rg.v[i + 1], q32, m, lsum, O);
                         else
                             attn_sub2<HD>(g, st0, g.nsub, Rg.k[i], Rg.v[i], Rg.k[i], Rg.v[i], q32, m, lsum, O);
                     }
                 }
-                attn_waves_to_lds<HD, NT>(lds, m, lsum, O);
-                __syncthreads();
+                attn_waves_to_lds<HD, NCT>(act, m, lsum, O);
+                cbar(cb);
                 const int hb = g.j * G;
                 auto put = [&](int h, int d, float M, float Lv, float acc) {
                     u64* pr = I4D_RP(u64, opart) + ((size_t)(hb + h) * ns + g.s) * (HD + 2);
                     ll_put(pr + 2 + d, acc, tag);
                     if (d == 0) { ll_put(pr, M, tag); ll_put(pr + 1, Lv, tag); }
                 };
-                attn_combine_waves<HD, NT>(lds, G, put);
+                attn_combine_waves<HD, NCT>(act, G, put);
             }
             // ================= merge: head h, dims 32 qd .. 32 qd + 31 of this unit
             for (int it = c; it < A.Hq * 4; it += nwg) {
                 const int h = it >> 2, qd = it & 3, ns = A.nsplit;
-                float* mv = (float*)lds;                        // [ns]
+                cbar(cb);                                       // the attention's LDS is free again
+                float* mv = (float*)act;                        // [ns]
                 float* lv = mv + 64;                            // [ns]
                 float* ov = lv + 64;                            // [ns][32]
                 const u64* hp = I4D_RP(u64, opart) + (size_t)h * ns * (HD + 2);
                 // one round: thread (s, q) fetches dims 2q, 2q + 1 of split s; threads of q = 0 also m and l
-                for (int idx = tid; idx < ns * 16; idx += NT) {
+                for (int idx = tid; idx < ns * 16; idx += NCT) {
                     const int s = idx >> 4, q = idx & 15;
                     float t2[2];
                     ll_get<2>(hp + (size_t)s * (HD + 2) + 2 + 32 * qd + 2 * q, tag, t2, sp);
@@ -773,32 +934,32 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                         lv[s] = t2[1];
                     }
                 }
-                __syncthreads();
-                {
+                cbar(cb);
+                if (tid < 32 * 8) {
                     // every wave: the largest running max over the splits (ns <= 64, one per lane)
                     float M = (lane < ns) ? mv[lane] : -INFINITY;
 #pragma unroll
                     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-                    // thread (d, k): dim 32 qd + d, splits k, k + 16, ...; then a sum over the 16 k-lanes
-                    const int d = tid >> 4, kk = tid & 15;
+                    // thread (d, k): dim 32 qd + d, splits k, k + 8, ...; then a sum over the 8 k-lanes
+                    const int d = tid >> 3, kk = tid & 7;
                     float acc = 0.f, Lsum = 0.f;
                     if (M != -INFINITY) {
-                        for (int s = kk; s < ns; s += 16) {
+                        for (int s = kk; s < ns; s += 8) {
                             const float w = exp2f(mv[s] - M);
                             acc = fmaf(ov[s * 32 + d], w, acc);
                             Lsum = fmaf(lv[s], w, Lsum);
                         }
                     }
 #pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1) {
+                    for (int o = 4; o >= 1; o >>= 1) {
                         acc += __shfl_xor(acc, o);
                         Lsum += __shfl_xor(Lsum, o);
                     }
                     if (kk == 0)
                         pk_put((u32*)I4D_RP(u64, oo) + (size_t)h * HD + 32 * qd + d, Lsum > 0.f ? acc / Lsum : 0.f, tag);
                 }
-                __syncthreads();
             }
+            cbar(cb);                                           // before the staging reuses the LDS
         }
 
         // ================= stage this phase's activations (digits in LDS)
@@ -806,72 +967,84 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         {
             const int K = k.K, ngr = K / 8;
             const bool six = kind == K_QKV;
-            // normalised inputs (x, y: K = D <= 8192, two rounds of groups): RMSNorm, then digits
+            // normalised inputs (x, y: K = D <= 8192, RMN rounds of groups): RMSNorm, then digits
             // the gain words of this thread's groups, loaded before the exchange
             // fetch so that their latency hides under it
-            auto load_gain = [&](const uint16_t* gain, u32x4 (&gw)[2]) {
+            auto load_gain = [&](const uint16_t* gain, u32x4 (&gw)[RMN]) {
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) gw[rr] = ld_g((const u32x4*)(gain + 8 * min(rr * NT + tid, ngr - 1)));
+                for (int rr = 0; rr < RMN; ++rr) gw[rr] = ld_g((const u32x4*)(gain + 8 * min(rr * NCT + tid, ngr - 1)));
             };
-            auto norm_stage = [&](float (&v)[2][8], const u32x4 (&gw)[2]) {
+            auto norm_stage = [&](float (&v)[RMN][8], const u32x4 (&gw)[RMN]) {
                 float ss = 0.f;
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr)
-                    if (rr * NT + tid < ngr)
+                for (int rr = 0; rr < RMN; ++rr)
+                    if (rr * NCT + tid < ngr)
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ss = fmaf(v[rr][e], v[rr][e], ss);
-                const float rs = 1.0f / sqrtf(block_sum(ss, red) / (float)K + A.eps);
+                const float rs = 1.0f / sqrtf(block_sum(ss, red, rpar, cb) / (float)K + A.eps);
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int g = rr * NT + tid;
+                for (int rr = 0; rr < RMN; ++rr) {
+                    const int g = rr * NCT + tid;
                     if (g < ngr) {
                         const u32 gws[4] = {gw[rr].x, gw[rr].y, gw[rr].z, gw[rr].w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             v[rr][e] *= rs * __uint_as_float((e & 1) ? (gws[e >> 1] & 0xFFFF0000u) : (gws[e >> 1] << 16));
-                        digitize8(act, cs, g, v[rr], six, A.status);
+                        digitize8(act, ps, cs, g, v[rr], six, A.status);
                     }
                 }
             };
             if (kind == K_QKV) {
-                float v[2][8];
-                u32x4 gw[2];
+                float v[RMN][8];
+                u32x4 gw[RMN];
                 load_gain(tab[l].g1, gw);
                 if (l == 0) {                                  // the caller's fp32 input
 #pragma unroll
-                    for (int rr = 0; rr < 2; ++rr) {
-                        const int g = min(rr * NT + tid, ngr - 1);
+                    for (int rr = 0; rr < RMN; ++rr) {
+                        const int g = min(rr * NCT + tid, ngr - 1);
                         const f4 a0 = ld_g((const f4*)(A.x_in + 8 * g)), a1 = ld_g((const f4*)(A.x_in + 8 * g + 4));
                         v[rr][0] = a0.x; v[rr][1] = a0.y; v[rr][2] = a0.z; v[rr][3] = a0.w;
                         v[rr][4] = a1.x; v[rr][5] = a1.y; v[rr][6] = a1.z; v[rr][7] = a1.w;
                     }
                 } else {
-                    fetch_groups<2, true>(I4D_RP(u64, ox), ngr, tag, v, sp);
+                    fetch_groups<RMN, true>(I4D_RP(u64, ox), 0, ngr, tag, v, sp);
                 }
                 norm_stage(v, gw);
             } else if (kind == K_GU) {
-                float v[2][8];
-                u32x4 gw[2];
+                float v[RMN][8];
+                u32x4 gw[RMN];
                 load_gain(tab[l].g2, gw);
-                fetch_groups<2, false>(I4D_RP(u64, oy), ngr, tag, v, sp);
+                fetch_groups<RMN, false>(I4D_RP(u64, oy), 0, ngr, tag, v, sp);
                 norm_stage(v, gw);
             } else if (kind == K_WO) {
-                float v[2][8];                                 // q width <= 8192
-                fetch_groups<2, false>(I4D_RP(u64, oo), ngr, tag, v, sp);
+                float v[RMN][8];                               // q width <= 8192
+                fetch_groups<RMN, false>(I4D_RP(u64, oo), 0, ngr, tag, v, sp);
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr)
-                    if (rr * NT + tid < ngr) digitize8(act, cs, rr * NT + tid, v[rr], false, A.status);
+                for (int rr = 0; rr < RMN; ++rr)
+                    if (rr * NCT + tid < ngr) digitize8(act, ps, cs, rr * NCT + tid, v[rr], false, A.status);
             } else {
-                float v[8][8];                                 // d_ff <= 32768
-                fetch_groups<8, false>(I4D_RP(u64, oact), ngr, tag, v, sp);
+                for (int g0 = 0; g0 < ngr; g0 += RMD * NCT) {  // d_ff <= 32768: passes of RMD rounds
+                    float v[RMD][8];
+                    fetch_groups<RMD, false>(I4D_RP(u64, oact), g0, ngr, tag, v, sp);
 #pragma unroll
-                for (int rr = 0; rr < 8; ++rr)
-                    if (rr * NT + tid < ngr) digitize8(act, cs, rr * NT + tid, v[rr], false, A.status);
+                    for (int rr = 0; rr < RMD; ++rr)
+                        if (g0 + rr * NCT + tid < ngr) digitize8(act, ps, cs, g0 + rr * NCT + tid, v[rr], false, A.status);
+                }
             }
         }
-        __syncthreads();
+        cbar(cb);
+        if (kind == K_QKV && c < A.Hkv * A.nsplit) {
+            // The cached keys of this layer's attention item do not depend on this
+            // step: their first round of loads goes out now and lands while the
+            // weights stream (the staging above had to wait for its exchange
+            // loads alone; nothing waits on vector memory until the attention).
+            AttnArgs a;
+            AttnGeo g;
+            attn_setup(A, tab, l, c, p, a, g);
+            attn_load_round<HD, NCT, ANSW>(a, g, 0, Rg);
+        }
 
-        // ================= stream this phase's weights through the ring
+        // ================= this phase's weight units, from the ring
         {
             const int n = uni(k.n), S = k.S;
             const SGeo& s = sg[kind * NSLOT + slot];
@@ -880,10 +1053,25 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             unsigned aoff = (unsigned)seg * 256u + (unsigned)lane16 * 16u;
             const int hs = ((lane16 >> 2) & 1) ? 0 : 16;
             const bool six = kind == K_QKV;
+            // this wave's place in the ring: its loader's half, its 2 KB of codes, its slots' scale words
+            const int lw = wave / CPL, cw = wave - CPL * lw;
+            const char* half = lds + A.off_ring + (size_t)lw * A.nb * HSTEP;
+            const unsigned uoff = (unsigned)(cw * 2048 + lane * 16);
+            const unsigned soff = (unsigned)(CPL * 2048 + (4 * (4 * cw + (lane >> 4)) + (lane16 >> 3)) * 4);
+            const u32* ready = sync + SY_READY + lw;
+            u32* cons = sync + SY_CONS + wave;
+            const int nb = A.nb;
             float ra = 0.f, rb = 0.f;
-            auto step = [&](Unit& u, int j) {
+            for (int j = 0; j < n; ++j) {
+                if ((int)rdy < t + 1) rdy = lds_wait([&] { return lds_get(ready); }, (u32)(t + 1), sync, A.status);
                 if (j < len) {
-                    dot_unit(u, act, aoff, cs[aoff >> 4], hs, six, ra, rb);
+                    const char* e = half + rslot * HSTEP;
+                    Unit u;
+                    u.a = *(const u32x4*)(e + uoff);
+                    u.b = *(const u32x4*)(e + uoff + 1024);
+                    u.sa = *(const u32*)(e + soff);
+                    u.sb = *(const u32*)(e + soff + 8);
+                    dot_unit(u, act, ps, aoff, cs[aoff >> 4], hs, six, ra, rb);
                     ++seg;
                     aoff += 256u;
                     const bool wrap = seg == S;
@@ -895,21 +1083,17 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                     }
                     if (wrap) { seg = 0; aoff = (unsigned)lane16 * 16u; }
                 }
-                loader_load(Ld, u, kg, sg, tab, A.zero, slot);
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            for (int j = 0; j < n; j += RD) {                  // n: a multiple of RD
-#pragma unroll
-                for (int i = 0; i < RD; ++i) step(ring[i], j + i);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                if (lane == 0) lds_put(cons, (u32)(t + 1));  // after this wave's reads of entry rslot
+                ++t;
+                rslot = rslot + 1 == nb ? 0 : rslot + 1;
             }
         }
-        __syncthreads();
+        cbar(cb);
 
         // ================= per-pair totals (fixed slot order) and the phase's epilogue
-        // One thread per pair (np < NT: see below).  Not a loop: a loop that
-        // stores without loading makes the compiler wait for every load in
-        // flight -- here the next phase's weight ring -- before entering it.
-        static_assert((MAXRUN - 1) * NSLOT < NT, "runs_of() <= MAXRUN bounds the pairs per unit below NT");
+        // One thread per pair (np < NCT: see below).
+        static_assert(MAXNP < NCT, "runs_of() <= MAXRUN bounds the pairs per unit below NCT");
         if (tid < k.np) {
             const int pl = tid;
             float va = 0.f, vb = 0.f;
@@ -977,13 +1161,16 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 }
             }
         }
-        __syncthreads();
+        // No barrier here: the next writes of part[] (the next stream) and of
+        // the staging area come after the next phase's staging barrier, which
+        // every wave reaches only after its epilogue; res[] rows are read and
+        // written by the same thread.
     }
 #undef I4D_RP
     wait_stores();
     // every workgroup read the epoch before any of them could finish (each
     // waits for data from all others), so the next launch's epoch goes out now
-    if (c == 0 && tid == 0) st_dev_t(A.epoch, tag);
+    if (blockIdx.x == 0 && i4d_tid() == 0) st_dev_t(opaque_ptr(Ap)->epoch, tag);
 }
 
 // The launch arguments, passed by value, into the workspace (the kernel reads
@@ -1046,8 +1233,28 @@ namespace {
 // Every host-side decision of one launch, taken before anything is enqueued.
 struct Plan {
     int cq, ck;          // q/k/v split of the compute units
+    int ps, nb;          // LDS bytes per digit plane; ring steps
+    unsigned off_act, off_ring;
     size_t lds;
 };
+
+constexpr int LDS_MAX = 160 * 1024;
+
+// LDS of one launch: the fixed part and the layer table, the staging area
+// (four digit planes of ps bytes and the run scales, or attention's working
+// set), then as many ring steps as fit (at most NBMAX).
+void lds_plan(const i4d_config* c, int n_layers, Plan& P) {
+    const int D = c->d_model, F = c->d_ff, qw = c->n_q_heads * HD;
+    const int kmax = std::max(D, std::max(qw, F));
+    P.ps = (int)a256((size_t)std::max(kmax / 2, D));        // six planes for q/k/v need d_model <= ps
+    const size_t stage = (size_t)4 * P.ps + (size_t)P.ps / 4;
+    const size_t att = (size_t)ATT_LDS + 2 * HD * 2;
+    P.off_act = (unsigned)a256((size_t)OFF_TAB + (size_t)n_layers * sizeof(LPtr));
+    P.off_ring = P.off_act + (unsigned)a256(std::max(stage, std::max(att, (size_t)MERGE_LDS)));
+    const long room = (long)LDS_MAX - (long)P.off_ring;
+    P.nb = room > 0 ? (int)std::min<long>(NBMAX, room / (NLW * HSTEP)) : 0;
+    P.lds = (size_t)P.off_ring + (size_t)NLW * std::max(P.nb, 0) * HSTEP;
+}
 
 // q/k/v rows go to compute units in proportion: [0, cq) q, [cq, ck) k, [ck, nwg) v.
 void qkv_split(const i4d_config* c, int nwg, int& cq, int& ck) {
@@ -1072,7 +1279,8 @@ bool make_plan(const i4d_config* c, int n_layers, const i4d_layer* layers, const
     if (c->n_q_heads / c->n_kv_heads > 16) return false;
     // every K a whole number of 512-input units and within one digit plane;
     // D and the q width at most two staging rounds of the workgroup
-    if (D % 512 || F % 512 || qw % 512 || F > KMAX || D > 2 * NT * 8 || qw > 2 * NT * 8) return false;
+    if (D % 512 || F % 512 || qw % 512 || F > KMAX || D > 8192 || qw > 8192) return false;
+    static_assert(RMN * NCT * 8 >= 8192, "d_model and the q width within RMN staging rounds");
     if (nwg < 3 || nwg > 1024) return false;
     if ((D / 2 + nwg - 1) / nwg > MAX_RES) return false;     // residual rows per compute unit
     for (int l = 0; l < n_layers; ++l) {
@@ -1095,8 +1303,8 @@ bool make_plan(const i4d_config* c, int n_layers, const i4d_layer* layers, const
     if (runs_of((F + nwg - 1) / nwg, D / 512) > MAXRUN) return false;
     if (runs_of((D / 2 + nwg - 1) / nwg, F / 512) > MAXRUN) return false;
     // LDS, no scratch, one workgroup per compute unit
-    P.lds = lds_bytes(n_layers);
-    if (P.lds > 160 * 1024) return false;
+    lds_plan(c, n_layers, P);
+    if (P.nb < 2 || P.lds > (size_t)LDS_MAX) return false;
     static int lds_set[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -1161,9 +1369,9 @@ int run(const i4d_config* c, int n_layers, const i4d_layer* layers, const float*
     A.qscale = (float)(1.4426950408889634 / sqrt((double)HD));
     A.base = c->rope_base;
     A.nsplit = splits_of(c, nwg);
-    const int tiles = (max_pos + 1 + 15) / 16;
-    A.T = 16 * ((tiles + A.nsplit - 1) / A.nsplit);
     A.cq = P.cq; A.ck = P.ck;
+    A.ps = P.ps; A.nb = P.nb;
+    A.off_act = P.off_act; A.off_ring = P.off_ring;
     A.lbase = region + R.layer0;
     A.lstride = R.lstride;
     A.ox = (unsigned)R.ox; A.oq = (unsigned)R.oq; A.okv = (unsigned)R.okv; A.opart = (unsigned)R.opart;

@@ -518,6 +518,15 @@ I4D_DEVINL void loader_main(const I4D_CONST Args& A, const KGeo* kg, const SGeo*
 }
 
 // ------------------------------------------------------------------ the dot product of one unit
+// sum of the eight signed 4-bit products of w and d, starting from zero: the
+// three-operand form takes the zero as an inline constant (the compiler would
+// otherwise zero a register for the two-operand form that accumulates in place)
+I4D_DEVINL int dot8_first(int w, int d) {
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(w), "v"(d));
+    return r;
+}
+
 // Digit planes 0..3 at act + p * ps; for the q/k/v projection (six planes,
 // K = d_model <= ps, so each plane fills at most half of its slot) planes 4
 // and 5 sit in the upper halves of slots 0 and 1.
@@ -530,9 +539,16 @@ I4D_DEVINL void dot_unit(const Unit& u, const char* act, int ps, unsigned aoff, 
     const u32x4 d1 = *(const u32x4*)(ap + ps);
     const u32x4 d2 = *(const u32x4*)(ap + 2 * ps);
     const u32x4 d3 = *(const u32x4*)(ap + 3 * ps);
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+    int a0, a1, a2, a3, b0, b1, b2, b3;
+    {
+        const int wa = (int)(u.a[0] ^ 0x88888888u), wb = (int)(u.b[0] ^ 0x88888888u);
+        a0 = dot8_first(wa, (int)d0[0]); a1 = dot8_first(wa, (int)d1[0]);
+        a2 = dot8_first(wa, (int)d2[0]); a3 = dot8_first(wa, (int)d3[0]);
+        b0 = dot8_first(wb, (int)d0[0]); b1 = dot8_first(wb, (int)d1[0]);
+        b2 = dot8_first(wb, (int)d2[0]); b3 = dot8_first(wb, (int)d3[0]);
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 1; q < 4; ++q) {
         const int wa = (int)(u.a[q] ^ 0x88888888u), wb = (int)(u.b[q] ^ 0x88888888u);
         a0 = __builtin_amdgcn_sdot8(wa, (int)d0[q], a0, false);
         a1 = __builtin_amdgcn_sdot8(wa, (int)d1[q], a1, false);
@@ -548,9 +564,14 @@ I4D_DEVINL void dot_unit(const Unit& u, const char* act, int ps, unsigned aoff, 
     if (six) {
         const u32x4 d4 = *(const u32x4*)(ap + ps / 2);
         const u32x4 d5 = *(const u32x4*)(ap + ps + ps / 2);
-        int a4 = 0, a5 = 0, b4 = 0, b5 = 0;
+        int a4, a5, b4, b5;
+        {
+            const int wa = (int)(u.a[0] ^ 0x88888888u), wb = (int)(u.b[0] ^ 0x88888888u);
+            a4 = dot8_first(wa, (int)d4[0]); a5 = dot8_first(wa, (int)d5[0]);
+            b4 = dot8_first(wb, (int)d4[0]); b5 = dot8_first(wb, (int)d5[0]);
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 1; q < 4; ++q) {
             const int wa = (int)(u.a[q] ^ 0x88888888u), wb = (int)(u.b[q] ^ 0x88888888u);
             a4 = __builtin_amdgcn_sdot8(wa, (int)d4[q], a4, false);
             a5 = __builtin_amdgcn_sdot8(wa, (int)d5[q], a5, false);
@@ -822,30 +843,31 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 uint16_t* knew = (uint16_t*)(act + ATT_LDS);
                 uint16_t* vnew = knew + HD;
                 const int r = lane & 15, gq = lane >> 4;
-                if (wave == 0) {
-                    // q^T operand of head r of the group for the 16x16x32 instruction: per
-                    // 32-dim block mm, the 8 dims 32 mm + 8 gq .. + 7 as bf16 high and low parts
+                static_assert(HD / 32 + 2 <= NCW, "one wave per 32-dim block of q, one each for the new k and v");
+                if (wave < HD / 32) {
+                    // q^T operand of head r of the group for the 16x16x32 instruction: wave mm
+                    // takes 32-dim block mm, the 8 dims 32 mm + 8 gq .. + 7 as bf16 high and
+                    // low parts (the blocks' exchange reads overlap instead of following each other)
+                    const int mm = wave;
                     const u64* qrow = I4D_RP(u64, oq) + (size_t)(g.j * G + min(r, G - 1)) * HD + 8 * gq;
                     const float qs = (r < G) ? A.qscale : 0.f;
-#pragma unroll 1
-                    for (int mm = 0; mm < HD / 32; ++mm) {
-                        float t8[8];
-                        ll_get<8>(qrow + 32 * mm, tag, t8, sp);
-                        u32 hv[4], lv[4];
+                    float t8[8];
+                    ll_get<8>(qrow + 32 * mm, tag, t8, sp);
+                    u32 hv[4], lv[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float v0 = t8[2 * q] * qs, v1 = t8[2 * q + 1] * qs;
-                            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-                            hv[q] = (u32)h0 | ((u32)h1 << 16);
-                            lv[q] = (u32)f32_to_bf16(v0 - bf16_to_f32(h0)) | ((u32)f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
-                        }
-                        q32[(2 * mm) * 64 + lane] = u32x4{hv[0], hv[1], hv[2], hv[3]};
-                        q32[(2 * mm + 1) * 64 + lane] = u32x4{lv[0], lv[1], lv[2], lv[3]};
+                    for (int q = 0; q < 4; ++q) {
+                        const float v0 = t8[2 * q] * qs, v1 = t8[2 * q + 1] * qs;
+                        const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+                        hv[q] = (u32)h0 | ((u32)h1 << 16);
+                        lv[q] = (u32)f32_to_bf16(v0 - bf16_to_f32(h0)) | ((u32)f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
                     }
-                } else if (wave <= 2) {
+                    q32[(2 * mm) * 64 + lane] = u32x4{hv[0], hv[1], hv[2], hv[3]};
+                    q32[(2 * mm + 1) * 64 + lane] = u32x4{lv[0], lv[1], lv[2], lv[3]};
+                } else if (wave < HD / 32 + 2) {
+                    const int kv = wave - HD / 32;              // 0: the new k, 1: the new v
                     float t2[2];
-                    ll_get<2>(I4D_RP(u64, okv) + (size_t)g.j * 2 * HD + (wave - 1) * HD + 2 * lane, tag, t2, sp);
-                    uint16_t* dst = wave == 1 ? knew : vnew;
+                    ll_get<2>(I4D_RP(u64, okv) + (size_t)g.j * 2 * HD + kv * HD + 2 * lane, tag, t2, sp);
+                    uint16_t* dst = kv == 0 ? knew : vnew;
                     dst[2 * lane] = f32_to_bf16(t2[0]);          // the values are bf16 already: exact
                     dst[2 * lane + 1] = f32_to_bf16(t2[1]);
                 }
@@ -924,14 +946,19 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 // one round: thread (s, q) fetches dims 2q, 2q + 1 of split s; threads of q = 0 also m and l
                 for (int idx = tid; idx < ns * 16; idx += NCT) {
                     const int s = idx >> 4, q = idx & 15;
+                    const u64* ps = hp + (size_t)s * (HD + 2);
+                    // the split's (m, l) words are read together with its O words (one
+                    // round trip); only a stale pair is fetched again
+                    const u64x2 mlw = ld_g((const u64x2*)ps);
                     float t2[2];
-                    ll_get<2>(hp + (size_t)s * (HD + 2) + 2 + 32 * qd + 2 * q, tag, t2, sp);
+                    ll_get<2>(ps + 2 + 32 * qd + 2 * q, tag, t2, sp);
                     ov[s * 32 + 2 * q] = t2[0];
                     ov[s * 32 + 2 * q + 1] = t2[1];
                     if (q == 0) {
-                        ll_get<2>(hp + (size_t)s * (HD + 2), tag, t2, sp);
-                        mv[s] = t2[0];
-                        lv[s] = t2[1];
+                        float ml[2] = {__uint_as_float((u32)mlw.x), __uint_as_float((u32)mlw.y)};
+                        if ((u32)(mlw.x >> 32) != tag || (u32)(mlw.y >> 32) != tag) ll_get<2>(ps, tag, ml, sp);
+                        mv[s] = ml[0];
+                        lv[s] = ml[1];
                     }
                 }
                 cbar(cb);

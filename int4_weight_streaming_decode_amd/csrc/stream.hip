@@ -610,26 +610,38 @@ I4D_DEVINL void digitize8(char* act, int ps, float* cs, int g, float (&v)[8], bo
     // four planes: |a| <= 2^14, digits of a + 0x8888; six: |a| <= 2^22, of a + 0x888888
     const int sh = (six ? 22 : 14) - ex;
     const u32 bias = six ? 0x888888u : 0x8888u;
+    // a = round-to-nearest-even(v 2^sh), |v 2^sh| < 2^22: adding 1.5 * 2^23 leaves
+    // a in the low bits of the sum's encoding (at a = +-2^22 the sum is 2^24 or
+    // 2^23, whose encodings still differ from that of 1.5 * 2^23 by exactly a)
     u32 dg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int a = (int)rintf(ldexpf(v[e], sh));
-        dg[e] = ((u32)a + bias) ^ bias;                        // digit p in nibble p
+        const u32 r = __float_as_uint(ldexpf(v[e], sh) + 12582912.0f);
+        dg[e] = (r + (bias - 0x4B400000u)) ^ bias;             // (a + bias) ^ bias: digit p in nibble p
     }
-    // plane q = nibble q of dg[0..7] in nibbles 0..7: gather byte b of the even
-    // and of the odd inputs into two words; the low nibbles of those bytes are
-    // plane 2b, the high nibbles plane 2b + 1, interleaved even/odd
-    u32 pl[6] = {0, 0, 0, 0, 0, 0};
+    // plane q = nibble q of dg[0..7] in nibbles 0..7: byte b of the even and of
+    // the odd inputs gathered into two words (byte permutes); the low nibbles
+    // of those bytes are plane 2b, the high nibbles plane 2b + 1, even/odd
+    // interleaved.  perm(x, y, s): result byte k = byte s_k of (x:y), 0-3 from y.
+    auto gather = [&](u32 d0, u32 d2, u32 d4, u32 d6, u32 (&w)[3]) {
+        const u32 lo02 = __builtin_amdgcn_perm(d2, d0, 0x05010400u), lo46 = __builtin_amdgcn_perm(d6, d4, 0x05010400u);
+        w[0] = __builtin_amdgcn_perm(lo46, lo02, 0x05040100u);        // byte 0 of d0 d2 d4 d6
+        w[1] = __builtin_amdgcn_perm(lo46, lo02, 0x07060302u);        // byte 1
+        if (six) {
+            const u32 hi02 = __builtin_amdgcn_perm(d2, d0, 0x07030602u), hi46 = __builtin_amdgcn_perm(d6, d4, 0x07030602u);
+            w[2] = __builtin_amdgcn_perm(hi46, hi02, 0x05040100u);    // byte 2
+        } else {
+            w[2] = 0u;
+        }
+    };
+    u32 ev[3], od[3];
+    gather(dg[0], dg[2], dg[4], dg[6], ev);
+    gather(dg[1], dg[3], dg[5], dg[7], od);
+    u32 pl[6];
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
-        if (b == 2 && !six) break;
-        const int sb = 8 * b;
-        const u32 ev = ((dg[0] >> sb) & 0xFFu) | (((dg[2] >> sb) & 0xFFu) << 8) | (((dg[4] >> sb) & 0xFFu) << 16) |
-                       (((dg[6] >> sb) & 0xFFu) << 24);
-        const u32 od = ((dg[1] >> sb) & 0xFFu) | (((dg[3] >> sb) & 0xFFu) << 8) | (((dg[5] >> sb) & 0xFFu) << 16) |
-                       (((dg[7] >> sb) & 0xFFu) << 24);
-        pl[2 * b] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
-        pl[2 * b + 1] = ((ev >> 4) & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
+        pl[2 * b] = (ev[b] & 0x0F0F0F0Fu) | ((od[b] << 4) & 0xF0F0F0F0u);
+        pl[2 * b + 1] = ((ev[b] >> 4) & 0x0F0F0F0Fu) | (od[b] & 0xF0F0F0F0u);
     }
     char* p = act + 4 * g;
     *(u32*)(p) = pl[0];

@@ -202,6 +202,33 @@ int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* 
                       const float* x_in, float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Prefill of a whole prompt (Primer 1.2: prefill computes, for every prompt
+ * token, what decoding the tokens one after another would): n_tokens
+ * consecutive tokens of ONE sequence, at positions pos0 .. pos0+n_tokens-1,
+ * through the n_layers layers at once.  The int4 projections run as GEMMs
+ * with the prompt as the wide dimension (weights read once per 64-token
+ * tile, not once per token), and attention is a causal attention tiled over
+ * the prompt (Roofline reply 四): token t attends slots 0..pos0+t, where
+ * slots below pos0 hold the sequence's earlier tokens and the prompt's own
+ * K/V (bf16, RoPE applied to K) are appended at pos0+t.
+ * x_in / x_out: [n_tokens][d_model] fp32 device, 16-byte aligned; x_out may
+ * be x_in.  layers, kv: HOST arrays of n_layers entries; each kv is the
+ * sequence's cache (batch dimension 1, contiguous or paged, row 0 of the page
+ * table) and needs capacity > pos0+n_tokens-1.  Weights: int4, groups of 128
+ * or 256 (one group size for all layers), every K a multiple of 256, d_model,
+ * d_ff and Hq*head_dim multiples of 256; otherwise I4D_EUNSUPPORTED.
+ * 1 <= n_tokens <= I4D_PREFILL_MAX_TOKENS.  ws: ws_bytes >=
+ * i4d_prefill_workspace_size(cfg, n_tokens), 256-byte aligned, status word
+ * as for the decode calls.  Numerics: activations enter the projections as
+ * fp16 (q/k/v: fp16 + fp16 remainder) times a power of two per token,
+ * accumulated in fp32 -- the batched decode path's arithmetic.  Enqueued on
+ * `stream`; returns after enqueueing.                                      */
+#define I4D_PREFILL_MAX_TOKENS 65536
+size_t i4d_prefill_workspace_size(const i4d_config* cfg, int32_t n_tokens);
+int i4d_prefill(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens,
+                const float* x_in, float* x_out, const i4d_kv* kv, int32_t pos0,
+                void* ws, size_t ws_bytes, void* stream);
+
 /* Greedy LM head (Unsloth article 三; Primer 1.2): for each of `batch` hidden
  * states h [B][D] fp32, token_out[b] = lowest v maximising (W_lm h_b)_v and
  * max_logit_out[b] = that logit (fp32).  w_lm is int4 [V][D].  The page's

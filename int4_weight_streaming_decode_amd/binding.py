@@ -87,6 +87,10 @@ def lib():
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
         L.i4d_prefill_chunk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                         ctypes.POINTER(I4dKv), P, I, P, Z, P]
+        L.i4d_prefill_workspace_size.argtypes = [ctypes.POINTER(I4dConfig), I]
+        L.i4d_prefill_workspace_size.restype = Z
+        L.i4d_prefill.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P, ctypes.POINTER(I4dKv), I,
+                                  P, Z, P]
         L.i4d_decode_step.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P, ctypes.POINTER(I4dMat), I,
                                       P, P, P, I, P, ctypes.POINTER(I4dKv), P, Z, P]
         L.i4d_decode_step_sample.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P,
@@ -104,7 +108,7 @@ def lib():
                      "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe",
-                     "i4d_lm_head_chunked_noalloc"):
+                     "i4d_lm_head_chunked_noalloc", "i4d_prefill"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +209,19 @@ def prefill_chunk(cfg, layers, n_tokens, x_in, x_out, kvs, pos, max_pos, ws, str
     karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
     _check(lib().i4d_prefill_chunk(ctypes.byref(cfg), n, larr, n_tokens, _ptr(x_in), _ptr(x_out), karr, _ptr(pos), max_pos,
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_prefill_chunk")
+
+
+def prefill_workspace_size(cfg: I4dConfig, n_tokens: int) -> int:
+    return int(lib().i4d_prefill_workspace_size(ctypes.byref(cfg), n_tokens))
+
+
+def prefill(cfg, layers, n_tokens, x_in, x_out, kvs, pos0, ws, stream=None):
+    """A whole prompt of one sequence (x [n][D] at positions pos0 .. pos0 + n - 1) through the stack."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_prefill(ctypes.byref(cfg), n, larr, n_tokens, _ptr(x_in), _ptr(x_out), karr, int(pos0), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "i4d_prefill")
 
 
 def embed(table, vocab, d_model, batch, tokens, x_out, ws, stream=None):

@@ -14,6 +14,7 @@
 #include "common.h"
 #include "gemv.h"
 #include "mfma.h"
+#include "prefill.h"
 #include "stream.h"
 
 namespace {
@@ -160,8 +161,10 @@ struct EpiQKV {
             st_out<WT>(qr + i, ra); st_out<WT>(qr + i + half, rb);
         } else if (p >= 0) {
             const uint16_t ba = f32_to_bf16(ra), bb = f32_to_bf16(rb);
-            uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;   // side copy for this step's attention
-            st_out<WT>(nr + i, ba); st_out<WT>(nr + i + half, bb);
+            if (kvn != nullptr) {                      // side copy for this step's attention (none for a prompt)
+                uint16_t* nr = kvn + (((size_t)b * hkv + head) * 2 + (mat - 1)) * hd;
+                st_out<WT>(nr + i, ba); st_out<WT>(nr + i + half, bb);
+            }
             // 16-position tiles: K [hd/32][16][32], V [hd][16]
             bool bad = false;
             const size_t tile = kv_tile_off(pg, cap, hkv, hd, b * kvb, head, p >> 4, bad);
@@ -1083,6 +1086,202 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
     return mfma_rows(nb, mfma_task(td, pd, base, S, cnt, B, g), pd, x_out, y, s);
 }
 
+// ---------------------------------------------------------------- prompt prefill
+// GEMM kernels of the prefill path (prefill.h), one per epilogue.
+__global__ void __launch_bounds__(PF_NT) k_pf_rows(PfTask g, float* y, const float* resid) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiRows<false> ep{y, resid, g.t.a.n, g.ntok};
+    pf_gemm<KIND_ADJ, 1>(g, lds, ep);
+}
+
+__global__ void __launch_bounds__(PF_NT) k_pf_swiglu(PfTask g, float* act) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiSwiGLU<false> ep{act, g.t.a.n, g.ntok};
+    pf_gemm<KIND_TWO, 1>(g, lds, ep);
+}
+
+// q (fp32, RoPE applied) to its buffer, bf16 k/v appended at each token's slot
+__global__ void __launch_bounds__(PF_NT) k_pf_qkv(PfTask g, float* q, uint16_t* kc, uint16_t* vc, const int* posv,
+                                                  const float2* cs, int cap, int hq, int hkv, KvMap pgm, int* status) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    EpiQKV<false> ep{q, kc, vc, nullptr, posv, cs, cap, hq, hkv, g.t.head_dim, g.ntok, 0, pgm, status};
+    pf_gemm<KIND_QKV, 2>(g, lds, ep);
+}
+
+// Tiles of one prefill GEMM; the K axis is split (adjacent-row tasks only)
+// while the tiles fill fewer than two workgroups per compute unit, keeping at
+// least 8 steps per split.
+struct PfPlan { int mtiles, ntiles, ks, spk, nsteps, nwg; };
+PfPlan pf_plan(int total_pairs, int K, int ntok, bool split) {
+    PfPlan p;
+    p.mtiles = (ntok + PF_BM - 1) / PF_BM;
+    p.ntiles = (total_pairs + PF_PAIRS - 1) / PF_PAIRS;
+    p.nsteps = K / 128;
+    const int slots = 2 * num_cus();
+    const int base = p.mtiles * p.ntiles;
+    int ks = 1;
+    if (split && base < slots) ks = std::max(1, std::min(slots / base, p.nsteps / 8));
+    p.spk = (p.nsteps + ks - 1) / ks;
+    p.ks = (p.nsteps + p.spk - 1) / p.spk;
+    p.nwg = base * p.ks;
+    return p;
+}
+
+// Workspace of i4d_prefill: the status header, then per prompt of T tokens
+// (sp = T rounded up to 64) the staged activations (two planes), their
+// per-token powers of two, positions and RoPE table, q and the attention
+// output, the residual stream, the SwiGLU activations, two layer outputs and
+// the split-K partial sums.
+struct PfWs { size_t xs, xsc, posv, pos, cs, q, o, y, act, xa, xb, part, total; };
+PfWs pf_ws(const i4d_config* c, int T) {
+    const size_t sp = (size_t)(T + PF_BM - 1) / PF_BM * PF_BM;
+    const size_t D = c->d_model, qw = (size_t)c->n_q_heads * c->head_dim, F = c->d_ff;
+    const size_t kmax = std::max(std::max(D, qw), F);
+    PfWs w;
+    size_t off = WS_HEADER;
+    auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+    w.xs = take(2 * sp * kmax * 2);
+    w.xsc = take(sp * 4);
+    w.posv = take(sp * 4);
+    w.pos = take(sp * 4);
+    w.cs = take(sp * (c->head_dim / 2) * 8);
+    w.q = take((size_t)T * qw * 4);
+    w.o = take((size_t)T * qw * 4);
+    w.y = take((size_t)T * D * 4);
+    w.act = take((size_t)T * F * 4);
+    w.xa = take((size_t)T * D * 4);
+    w.xb = take((size_t)T * D * 4);
+    size_t part = 0;
+    for (int kk = 0; kk < 2; ++kk) {          // the two adjacent-row GEMMs (Wo: K = qw, down: K = F), N = D
+        const PfPlan pp = pf_plan((int)((D + 1) / 2), kk == 0 ? (int)qw : (int)F, T, true);
+        if (pp.ks > 1) part = std::max(part, (size_t)pp.ks * T * D * 4);
+    }
+    w.part = take(part);
+    w.total = off;
+    return w;
+}
+
+PfTask pf_task(const GemvTask& t, const PfPlan& p, char* ws, const PfWs& W, int T, int group, int rows) {
+    PfTask g;
+    memset(&g, 0, sizeof(g));
+    g.t = t;
+    g.xs = (const uint32_t*)(ws + W.xs);
+    g.xscale = (const float*)(ws + W.xsc);
+    g.part = (float*)(ws + W.part);
+    g.sp = (T + PF_BM - 1) / PF_BM * PF_BM;
+    g.ntok = T;
+    g.nsteps = p.nsteps;
+    g.gshift = ilog2(group) - 7;
+    g.mtiles = p.mtiles; g.ntiles = p.ntiles; g.ks = p.ks; g.spk = p.spk;
+    g.rows = rows;
+    return g;
+}
+
+template <class Kern, class... A>
+int launch_pf(Kern kernel, size_t lds, const PfPlan& p, hipStream_t s, A... args) {
+    if (lds > LDS_LIMIT) return I4D_EUNSUPPORTED;
+    if (const int rc_ = set_lds(kernel, lds)) return rc_;
+    launch_k(kernel, dim3(p.nwg), dim3(PF_NT), lds, s, args...);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// Adjacent-row GEMM + residual, with the split-K reduction when planned.
+int pf_rows(const PfTask& g, const PfPlan& p, float* y, const float* resid, hipStream_t s) {
+    int rc;
+    if ((rc = launch_pf(k_pf_rows, pf_lds_bytes<1>(), p, s, g, y, resid))) return rc;
+    if (p.ks == 1) return I4D_OK;
+    if ((rc = scratch_free(k_pf_reduce))) return rc;
+    const size_t n = (size_t)g.ntok * g.rows;
+    const int nblk = (int)std::min<size_t>((n + 255) / 256, (size_t)num_cus() * 8);
+    hipLaunchKernelGGL(k_pf_reduce, dim3(nblk), dim3(256), 0, s, (const float*)g.part, p.ks, g.ntok, g.rows, g.xscale, resid, y);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// Staging of T token rows into the prefill workspace (k_mfma_stage, one
+// workgroup per staged row; rows past T are zero-filled).
+int pf_stage(int prec, const float* x, int stride, int T, int K, const uint16_t* gain, float eps, char* ws, const PfWs& W,
+             int max_pos, int cap, int hd, double rope_base, bool rope, hipStream_t s) {
+    const int sp = (T + PF_BM - 1) / PF_BM * PF_BM;
+    uint32_t* xs = (uint32_t*)(ws + W.xs);
+    int* status = (int*)(ws + WS_STATUS);
+    const int* pos = rope ? (const int*)(ws + W.pos) : nullptr;
+    int* posv = rope ? (int*)(ws + W.posv) : nullptr;
+    float2* cs = rope ? (float2*)(ws + W.cs) : nullptr;
+    float* xsc = (float*)(ws + W.xsc);
+    if (const int rc_ = scratch_free(prec == 2 ? k_mfma_stage<2> : k_mfma_stage<1>)) return rc_;
+    if (prec == 2)
+        hipLaunchKernelGGL(k_mfma_stage<2>, dim3(sp), dim3(256), 0, s, x, stride, T, sp, K, gain, eps, xs, pos, max_pos, cap,
+                           hd, rope_base, posv, cs, status, xsc);
+    else
+        hipLaunchKernelGGL(k_mfma_stage<1>, dim3(sp), dim3(256), 0, s, x, stride, T, sp, K, gain, eps, xs, pos, max_pos, cap,
+                           hd, rope_base, posv, cs, status, xsc);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// One layer of a prompt of T tokens at positions pos0 .. pos0 + T - 1.
+int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const float* x_in, float* x_out, const i4d_kv* kv,
+                      int pos0, char* ws, const PfWs& W, hipStream_t s) {
+    const int hd = c->head_dim, D = c->d_model, qw = c->n_q_heads * hd, F = c->d_ff, g = L->wq.group;
+    const int max_pos = pos0 + T - 1;
+    int* status = (int*)(ws + WS_STATUS);
+    float* q = (float*)(ws + W.q);
+    float* o = (float*)(ws + W.o);
+    float* y = (float*)(ws + W.y);
+    float* act = (float*)(ws + W.act);
+    int rc;
+
+    if ((rc = pf_stage(2, x_in, D, T, D, L->attn_norm, c->rms_eps, ws, W, max_pos, kv->capacity, hd, c->rope_base, true, s)))
+        return rc;
+    const GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
+    const PfPlan pq = pf_plan(tq.total_pairs, D, T, false);
+    {
+        TimeScope ts(I4D_TIME_QKV);
+        rc = launch_pf(k_pf_qkv, pf_lds_bytes<2>(), pq, s, pf_task(tq, pq, ws, W, T, g, 0), q, kv->k, kv->v,
+                       (const int*)(ws + W.posv), (const float2*)(ws + W.cs), kv->capacity, c->n_q_heads, c->n_kv_heads,
+                       kv_map(kv), status);
+    }
+    if (rc) return rc;
+    {
+        PfAttnArgs a;
+        a.q = q; a.kc = kv->k; a.vc = kv->v; a.o = o;
+        a.ntok = T; a.pos0 = pos0; a.cap = kv->capacity; a.hq = c->n_q_heads; a.hkv = c->n_kv_heads;
+        a.nqb = (T + 15) / 16;
+        a.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+        a.pg = kv_map(kv);
+        a.status = status;
+        const int nwg = (a.hq * a.nqb + 3) / 4;
+        auto kern = hd == 128 ? k_pf_attn<128> : k_pf_attn<64>;
+        if ((rc = scratch_free(kern))) return rc;
+        TimeScope ts(I4D_TIME_ATTENTION);
+        launch_k(kern, dim3(nwg), dim3(256), 0, s, a);
+        if (hipGetLastError() != hipSuccess) return I4D_EHIP;
+    }
+
+    if ((rc = pf_stage(1, o, qw, T, qw, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
+    const GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
+    const PfPlan po = pf_plan(to.total_pairs, qw, T, true);
+    {
+        TimeScope ts(I4D_TIME_WO);
+        rc = pf_rows(pf_task(to, po, ws, W, T, g, D), po, y, x_in, s);
+    }
+    if (rc) return rc;
+
+    if ((rc = pf_stage(1, y, D, T, D, L->ffn_norm, c->rms_eps, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
+    const GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
+    const PfPlan pg = pf_plan(tg.total_pairs, D, T, false);
+    {
+        TimeScope ts(I4D_TIME_GATE_UP);
+        rc = launch_pf(k_pf_swiglu, pf_lds_bytes<1>(), pg, s, pf_task(tg, pg, ws, W, T, g, 0), act);
+    }
+    if (rc) return rc;
+
+    if ((rc = pf_stage(1, act, F, T, F, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
+    const GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
+    const PfPlan pd = pf_plan(td.total_pairs, F, T, true);
+    TimeScope ts(I4D_TIME_DOWN);
+    return pf_rows(pf_task(td, pd, ws, W, T, g, D), pd, x_out, y, s);
+}
+
 // One layer as phase launches (q/k/v, attention, Wo, gate/up, down), using
 // the workspace region R.
 int run_layer_phases(const i4d_config* c, const i4d_layer* L, int B, const float* x_in, float* x_out, const i4d_kv* kv,
@@ -1351,6 +1550,42 @@ int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* 
                       float* x_out, const i4d_kv* kv, const int32_t* pos, int32_t max_pos, void* ws, size_t ws_bytes,
                       void* stream) {
     return decode_stack_impl(true, cfg, n_layers, layers, n_tokens, x_in, x_out, kv, pos, max_pos, ws, ws_bytes, stream, 0);
+}
+
+size_t i4d_prefill_workspace_size(const i4d_config* cfg, int32_t n_tokens) {
+    if (validate_cfg(cfg) || n_tokens < 1 || n_tokens > I4D_PREFILL_MAX_TOKENS) return 0;
+    return pf_ws(cfg, n_tokens).total;
+}
+
+int i4d_prefill(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens, const float* x_in,
+                float* x_out, const i4d_kv* kv, int32_t pos0, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = validate_cfg(cfg))) return rc;
+    if (n_layers < 1 || !layers || !kv || !x_in || !x_out) return I4D_EINVAL;
+    if (n_tokens < 1 || n_tokens > I4D_PREFILL_MAX_TOKENS || pos0 < 0) return I4D_ERANGE;
+    if (!aligned(x_in, 16) || !aligned(x_out, 16)) return I4D_EALIGN;
+    const PfWs W = pf_ws(cfg, n_tokens);
+    if ((rc = validate_ws(ws, ws_bytes, W.total))) return rc;
+    const long long last = (long long)pos0 + n_tokens - 1;
+    if (last > INT32_MAX) return I4D_ERANGE;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((rc = validate_layer(cfg, &layers[l]))) return rc;
+        if ((rc = validate_kv(cfg, &kv[l], (int)last))) return rc;
+        if (layers[l].wq.dtype != I4D_WEIGHT_INT4 || !mfma_layer_ok(cfg, &layers[l])) return I4D_EUNSUPPORTED;
+        if (layers[l].wq.group != layers[0].wq.group) return I4D_EUNSUPPORTED;
+    }
+    char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = scratch_free(k_pf_positions))) return rc;
+    hipLaunchKernelGGL(k_pf_positions, dim3((n_tokens + 255) / 256), dim3(256), 0, s, (int*)(w + W.pos), n_tokens, pos0);
+    if (hipGetLastError() != hipSuccess) return I4D_EHIP;
+    const float* in = x_in;
+    for (int l = 0; l < n_layers; ++l) {
+        float* out = (l == n_layers - 1) ? x_out : (float*)(w + ((l & 1) ? W.xb : W.xa));
+        if ((rc = run_layer_prefill(cfg, &layers[l], n_tokens, in, out, &kv[l], pos0, w, W, s))) return rc;
+        in = out;
+    }
+    return I4D_OK;
 }
 
 int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t batch, const int32_t* tokens, float* x_out,

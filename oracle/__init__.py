@@ -26,6 +26,7 @@ from .decode import (  # noqa: F401
     bf16_to_f64,
     decode_layer,
     decode_stack,
+    prefill,
     dequant_int4,
     embed_tokens,
     gqa_decode_attention,

@@ -11,7 +11,9 @@ Each function is the plain definition of one step, written from the pages:
   * Primer 1.2: at decode one token enters, every layer reads all cached K/V
     of its layer and appends the new token's K/V; the last hidden state times
     the embedding matrix gives the vocabulary logits, from which a token is
-    sampled (greedy here).
+    sampled (greedy here).  Prefill runs the prompt's tokens through the same
+    computation; each prompt token gets what decoding it after the tokens
+    before it would give (prefill()).
   * Unsloth article 二.1: the feed-forward network is SwiGLU, SiLU of the gate
     projection times the up projection, then the down projection.
   * Unsloth article 二.2: grouped-query attention -- each KV head serves a
@@ -77,10 +79,27 @@ def dequant_int4(codes: np.ndarray, scales: np.ndarray, k: int, group: int) -> n
     return (c - 8.0) * s[:, np.arange(k) // group]
 
 
+# Recently expanded small matrices, kept so that a long sequence of decode
+# steps over the same weights does not expand them again at every step (the
+# values are the same either way).  Each entry holds the code and scale arrays
+# it was made from, so an entry is only reused for those very arrays.
+_DENSE_MEMO = []
+_DENSE_MEMO_MAX, _DENSE_MEMO_ELEMS = 16, 1 << 22
+
+
 def _dense(mat: dict, r0: int = 0, r1=None) -> np.ndarray:
     r1 = mat["n"] if r1 is None else r1
     if "codes" in mat:
-        return dequant_int4(mat["codes"][r0:r1], mat["scales"][r0:r1], mat["k"], mat["group"])
+        small = (r1 - r0) * mat["k"] <= _DENSE_MEMO_ELEMS
+        if small:
+            for codes, scales, a, b, w in _DENSE_MEMO:
+                if codes is mat["codes"] and scales is mat["scales"] and a == r0 and b == r1:
+                    return w
+        w = dequant_int4(mat["codes"][r0:r1], mat["scales"][r0:r1], mat["k"], mat["group"])
+        if small:
+            _DENSE_MEMO.append((mat["codes"], mat["scales"], r0, r1, w))
+            del _DENSE_MEMO[:-_DENSE_MEMO_MAX]
+        return w
     return bf16_to_f64(mat["bf16"][r0:r1])
 
 
@@ -211,6 +230,21 @@ def decode_stack(shape, layers: list, x: np.ndarray, caches: list, pos) -> dict:
         z = r["z"]
         new_caches.append((r["k_cache"], r["v_cache"]))
     return {"z": z, "caches": new_caches}
+
+
+def prefill(shape, layers: list, x: np.ndarray, caches: list, pos0: int) -> dict:
+    """Prefill of a prompt by its definition (Primer 1.2, prefill vs decode):
+    every prompt token gets what decoding it at position pos0 + t, after the
+    tokens before it, gives.  x [T][D]; caches hold the sequence's earlier
+    tokens below pos0 (batch dimension 1).  Returns each token's output
+    z [T][D] and the caches with the T prompt tokens' K/V appended."""
+    x = np.asarray(x, dtype=np.float64)
+    zs = []
+    for t in range(x.shape[0]):
+        r = decode_stack(shape, layers, x[t:t + 1], caches, [pos0 + t])
+        caches = r["caches"]
+        zs.append(r["z"][0])
+    return {"z": np.stack(zs), "caches": caches}
 
 
 # ----------------------------------------------------------------------------- LM head

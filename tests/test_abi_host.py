@@ -290,3 +290,31 @@ def test_prefill_chunk_validation(lib):
     assert call(_cfg(), n_tokens=0) == B.I4D_ERANGE
     assert call(_cfg(), n_tokens=33) == B.I4D_ERANGE
     assert call(_cfg(exec_mode=2)) == B.I4D_EUNSUPPORTED
+
+
+def test_prefill_validation(lib):
+    """Whole-prompt prefill: token count, first position, alignment, cache
+    capacity, workspace size and the matrix-core weight conditions are all
+    checked before anything is enqueued."""
+    P = ctypes.c_void_p
+    cfg_ok = _cfg(d_model=512, d_ff=1024, head_dim=128, n_q_heads=4, n_kv_heads=2)
+
+    def call(cfg, n_tokens=64, pos0=0, cap=256, x_in=0x100000, ws_bytes=1 << 40, group=128):
+        layer = _layer(cfg, group=group)
+        kv = B.I4dKv(0x500000, 0x600000, cap)
+        return lib.i4d_prefill(ctypes.byref(cfg), 1, ctypes.byref(layer), n_tokens, P(x_in), P(0x200000),
+                               ctypes.byref(kv), pos0, P(0x400000), ws_bytes, None)
+
+    assert call(cfg_ok, n_tokens=0) == B.I4D_ERANGE
+    assert call(cfg_ok, n_tokens=65537) == B.I4D_ERANGE
+    assert call(cfg_ok, pos0=-1) == B.I4D_ERANGE
+    assert call(cfg_ok, x_in=0x100004) == B.I4D_EALIGN
+    assert call(cfg_ok, ws_bytes=16) == B.I4D_EWORKSPACE
+    assert call(cfg_ok, n_tokens=200, pos0=100, cap=288) == B.I4D_ERANGE      # last position 299 >= capacity
+    assert call(_cfg()) == B.I4D_EUNSUPPORTED                                  # d_ff 688: not a multiple of 256
+    assert call(cfg_ok, group=64) == B.I4D_EUNSUPPORTED                        # groups of 64
+    assert call(_cfg(head_dim=96)) == B.I4D_EINVAL
+    n1 = B.prefill_workspace_size(cfg_ok, 1)
+    assert 0 < n1 < B.prefill_workspace_size(cfg_ok, 512) < B.prefill_workspace_size(cfg_ok, 4096)
+    assert B.prefill_workspace_size(cfg_ok, 0) == 0
+    assert B.prefill_workspace_size(cfg_ok, 65537) == 0

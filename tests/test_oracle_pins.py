@@ -333,6 +333,39 @@ def test_decode_stack_is_layer_composition():
     assert np.array_equal(r["z"], z)
 
 
+def test_prefill_equals_sequence_form_on_every_row():
+    """The oracle's prefill (token after token) against the causal-mask
+    sequence form over the whole prompt: every row, and every appended slot."""
+    shape = synth.SHAPES["tiny"].with_(d_model=64, n_q_heads=4, n_kv_heads=2, head_dim=16, d_ff=96, group=16)
+    layer = synth.make_layer(shape, seed=21, layer=0)
+    S, cap = 11, 16
+    X = np.random.default_rng(22).standard_normal((S, shape.d_model))
+    Z, kc, vc = _sequence_layer(shape, layer, X)
+    poison = np.full((1, shape.n_kv_heads, cap, shape.head_dim), 0x7FC0, dtype=np.uint16)
+    r = oracle.prefill(shape, [layer], X, [(poison, poison.copy())], 0)
+    assert np.allclose(r["z"], Z, rtol=1e-12, atol=1e-12)
+    k_out, v_out = r["caches"][0]
+    assert np.array_equal(k_out[0, :, :S], kc) and np.array_equal(v_out[0, :, :S], vc)
+    assert np.array_equal(k_out[0, :, S:], poison[0, :, S:])
+
+
+def test_prefill_after_a_history_equals_the_tail_of_one_long_prefill():
+    """A prompt split in two (the second part after the first's cache) gives
+    the same rows as one prefill over the whole prompt."""
+    shape = synth.SHAPES["tiny"].with_(d_model=32, n_q_heads=2, n_kv_heads=1, head_dim=16, d_ff=48, group=16, n_layers=2)
+    layers = [synth.make_layer(shape, 23, l) for l in range(2)]
+    cap = 16
+    empty = [(np.zeros((1, 1, cap, 16), dtype=np.uint16), np.zeros((1, 1, cap, 16), dtype=np.uint16)) for _ in range(2)]
+    X = np.random.default_rng(24).standard_normal((9, shape.d_model))
+    whole = oracle.prefill(shape, layers, X, empty, 0)
+    head = oracle.prefill(shape, layers, X[:4], empty, 0)
+    tail = oracle.prefill(shape, layers, X[4:], head["caches"], 4)
+    assert np.array_equal(tail["z"], whole["z"][4:])
+    for l in range(2):
+        for i in range(2):
+            assert np.array_equal(tail["caches"][l][i], whole["caches"][l][i])
+
+
 # ------------------------------------------------------------------ LM head
 
 def _tiny_lm(V, D, g, seed):

@@ -22,7 +22,12 @@ bounded sample.
 whose whole stack does not fit in HBM, e.g. the 70B shape at batch 32) and
 adds the per-step figures scaled to the full depth, labelled as extrapolated.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+--prefill N measures prefill instead (one JSON line of its own): one step is
+i4d_prefill of one N-token prompt through the stack (int4 MFMA GEMMs over the
+prompt, causal prompt attention); `value` is prompt tokens/s, `roofline` the
+gate/up GEMM against the 2.5 PFLOP/s dense fp16 matrix-core peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--prefill N]
                        [--batch B] [--layers N] [--exec-mode M] [--breakdown-steps N]
                        [--calibrate-copy-mib MIB] [--no-cpu-baseline] [--no-read-probe]
 """
@@ -135,6 +140,145 @@ def cpu_baseline(shape, dtype, lm):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+PREFILL_KERNELS = {"qkv": "k_pf_qkv", "attention": "k_pf_attn<128>", "wo": "k_pf_rows (Wo)",
+                   "gate_up": "k_pf_swiglu", "down": "k_pf_rows (W_down)"}
+MFMA_F16_PEAK_TFLOPS = 2500.0        # dense fp16 matrix-core peak of the chip
+
+
+def prefill_cpu_baseline(shape, n_sample=2):
+    """The CPU oracle's prefill (token after token) of a short prompt through
+    one layer of the workload's shape, scaled to the whole stack."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cap = ((n_sample + 15) // 16) * 16
+    layer = synth.make_layer(shape, 17, 0, "int4")
+    kc, vc = synth.make_kv(shape, 17, 0, 1, [0], cap)
+    x = np.stack([synth.make_x(shape, 17, 1, step=t)[0] for t in range(n_sample)]).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.prefill(shape, [layer], x, [(kc, vc)], 0)
+    t = time.perf_counter() - t0
+    return {"value": n_sample / (t * shape.n_layers), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_sample} prompt tokens through 1 of {shape.n_layers} layers ({t:.2f} s), scaled to the stack",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def prefill_main(args):
+    """One step = i4d_prefill of one prompt of args.prefill tokens (positions
+    0 .. n-1) through the whole int4 stack; the same prompt every step (each
+    step rewrites the same cache slots)."""
+    import torch
+
+    from int4_weight_streaming_decode_amd import binding as B
+    from synth import gpu as G
+
+    shape_name, wdtype, _ = WORKLOADS[args.workload]
+    if wdtype != "int4":
+        sys.exit("prefill runs on int4 weights")
+    shape = synth.SHAPES[shape_name]
+    full_layers = shape.n_layers
+    if 0 < args.layers < full_layers:
+        shape = shape.with_(n_layers=args.layers)
+    n = args.prefill
+    torch.cuda.set_device(0)
+    cap = ((n + 15) // 16 + 1) * 16
+    t_gen = time.perf_counter()
+    keep, layers, kvs = [], [], []
+    for l in range(shape.n_layers):
+        p = G.make_layer_gpu(shape, 1, l, "int4")
+        mats = {k: B.make_mat(p[k]["codes"], p[k]["scales"], p[k]["n"], p[k]["k"], p[k]["group"], B.WEIGHT_INT4)
+                for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")}
+        layers.append(B.make_layer(p["attn_norm"], p["ffn_norm"], mats))
+        k, v = G.make_kv_gpu(shape, 1, l, 1, cap)
+        kvs.append(B.make_kv(k, v, cap))
+        keep.append((p, k, v))
+        if (l + 1) % 8 == 0 or l + 1 == shape.n_layers:
+            print(f"[bench] inputs: layer {l + 1}/{shape.n_layers} on the device", file=sys.stderr, flush=True)
+    layers = (B.I4dLayer * len(layers))(*layers)
+    kvs = (B.I4dKv * len(kvs))(*kvs)
+    x = G.make_x_gpu(shape, 3, n)
+    out = torch.empty_like(x)
+    cfg = B.make_config(shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
+                        shape.rms_eps, shape.rope_base, 0)
+    ws = torch.zeros(B.prefill_workspace_size(cfg, n), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    def step():
+        B.prefill(cfg, layers, n, x, out, kvs, 0, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    fl = roofline.prefill_flops(shape, n, 0)
+    breakdown = {}
+    nb = max(1, args.breakdown_steps)
+    for kind in ("qkv", "attention", "wo", "gate_up", "down"):
+        B.launch_timing_start(kind, 65536)
+        for _ in range(nb):
+            step()
+        torch.cuda.synchronize()
+        ms, launches = B.launch_timing_stop()
+        avg_ms = ms / max(launches, 1)
+        f = fl["per_layer"][kind]
+        breakdown[kind] = {"kernel": PREFILL_KERNELS[kind], "launches_per_step": launches / nb, "avg_us": avg_ms * 1e3,
+                           "flop_per_launch": f, "tflops": f / (avg_ms * 1e-3) / 1e12 if launches else None,
+                           "share_of_step": (ms / nb) / ms_per_step}
+    status = B.read_device_status(ws)
+    rk = "gate_up"
+    rk_e = breakdown[rk]
+    tflops = fl["total"] / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": f"prefill tokens/s of one {n}-token prompt, {shape.name}-shaped int4 stack",
+        "value": n * 1000.0 / ms_per_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights, f16 x f16 -> f32 MFMA GEMM (q/k/v: f16 + f16 remainder); bf16 MFMA attention",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}-prefill{n}: {shape.n_layers} layers, D={shape.d_model}, "
+                               f"{shape.n_q_heads}/{shape.n_kv_heads} heads, head_dim {shape.head_dim}, d_ff {shape.d_ff}, "
+                               f"group {shape.group}; one prompt of {n} tokens at positions 0..{n - 1}",
+                   "prompt_tokens": n, "layers": shape.n_layers, "weights": "int4"},
+        "roofline": {"bound": "mfma", "kernel": rk_e["kernel"], "achieved": rk_e["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": (rk_e["tflops"] or 0.0) / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "avg_launch_us": rk_e["avg_us"], "flop_per_launch": rk_e["flop_per_launch"]},
+        "step_roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tflops / MFMA_F16_PEAK_TFLOPS},
+        "flop_per_step": fl["total"],
+        "kernels": breakdown,
+        "device_status": status,
+        "input_generation_s": round(t_gen, 1),
+    }
+    if shape.n_layers < full_layers:
+        full_ms = ms_per_step * full_layers / shape.n_layers
+        result["extrapolated"] = {"layers": full_layers, "ms_per_step": full_ms, "tokens_per_s": n * 1000.0 / full_ms,
+                                  "how": f"the first {shape.n_layers} layers timed, scaled by {full_layers}/{shape.n_layers}"}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(shape)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,12 +307,17 @@ def main():
                          "traffic for scaling hardware byte counters); 0: none")
     ap.add_argument("--breakdown-steps", type=int, default=10,
                     help="steps per extra pass that times one kernel of the step (0: no per-kernel figures)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="measure prefill instead: one prompt of this many tokens through the stack per step")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design note, "
               "not a measured path", file=sys.stderr)
         sys.exit(2)
+    if args.prefill > 0:
+        prefill_main(args)
+        return
 
     import torch
 

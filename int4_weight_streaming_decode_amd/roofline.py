@@ -95,6 +95,21 @@ def step_flops(shape, batch: int, keys: int, n_layers=None, lm_head: bool = Fals
     return total
 
 
+def prefill_flops(shape, n_tokens: int, pos0: int = 0, n_layers=None) -> dict:
+    """2 x multiply-adds of a prefill of n_tokens prompt tokens at positions
+    pos0 .. pos0 + n_tokens - 1 (token t attends pos0 + t + 1 keys), per
+    projection of one layer and in total."""
+    L = shape.n_layers if n_layers is None else n_layers
+    m = layer_matrices(shape)
+    per = {"qkv": 2 * n_tokens * (m["wq"][0] + m["wk"][0] + m["wv"][0]) * shape.d_model,
+           "wo": 2 * n_tokens * m["wo"][0] * m["wo"][1],
+           "gate_up": 2 * n_tokens * (m["wg"][0] + m["wu"][0]) * m["wg"][1],
+           "down": 2 * n_tokens * m["wd"][0] * m["wd"][1]}
+    keys = n_tokens * pos0 + n_tokens * (n_tokens + 1) // 2
+    per["attention"] = 4 * shape.n_q_heads * shape.head_dim * keys      # q.k and p.v per key
+    return {"per_layer": per, "total": L * sum(per.values())}
+
+
 def decode_latency_bound_s(weight_bytes: float, bandwidth: float) -> float:
     """Lower bound of one decode step: every weight read once (Primer 1.2)."""
     return weight_bytes / bandwidth

@@ -97,3 +97,14 @@ def test_70b_batch_sweep_intensity(batch, intensity):
     s = synth.SHAPES["70b"]
     keys = s.kv_len + 1
     assert roofline.step_flops(s, batch, keys) / roofline.step_bytes(s, batch, keys) == pytest.approx(intensity, abs=0.05)
+
+
+def test_prefill_flops_is_the_sum_of_per_token_decode_flops():
+    """A prompt of n tokens from position p0 costs what n decode steps at
+    positions p0 .. p0 + n - 1 (keys p0 + t + 1) cost together."""
+    s = synth.SHAPES["27b"]
+    for n, p0 in ((1, 0), (512, 0), (77, 300)):
+        total = roofline.prefill_flops(s, n, p0)["total"]
+        assert total == sum(roofline.step_flops(s, 1, p0 + t + 1) for t in range(n))
+    per = roofline.prefill_flops(s, 512, 0)["per_layer"]
+    assert per["gate_up"] == 2 * 512 * 2 * s.d_ff * s.d_model

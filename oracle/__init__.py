@@ -41,4 +41,4 @@ from .decode import (  # noqa: F401
     swiglu,
     unpack_int4,
 )
-from .sample import gumbel_scores, philox4x32_10, sample_tokens, uniforms  # noqa: F401
+from .sample import gumbel_scores, philox4x32_10, sample_tokens, sample_tokens_topk, top_k_rows, uniforms  # noqa: F401

@@ -21,9 +21,17 @@ so that any row of any chunk can draw its own number with no state:
   * the first output word x gives u = (floor(x / 512) + 1/2) / 2^23, which
     lies strictly inside (0, 1) and is exact in float32 as well (24 bits).
 
+Top-k sampling (the "optional temperature/top-k" of the decode loop's
+sample step): the draw from softmax(logits / T) restricted to the k largest
+logits (equal logits ranked by lower id), renormalised over them.  With the
+same Gumbel noise it is the argmax of the perturbed scores over those k rows
+only, so k = V is plain temperature sampling and k = 1 the greedy token.
+
 Parity pins (tests/test_oracle_pins.py): the published Philox4x32-10
 known-answer vectors; the empirical frequencies of many draws against
-softmax(logits / T); a vanishing temperature giving the greedy token.
+softmax(logits / T), and against the renormalised softmax over the top k; a
+vanishing temperature, and k = 1, giving the greedy token; k = V giving the
+plain draw; equal logits at the cut kept by lower id.
 """
 
 import numpy as np
@@ -78,3 +86,28 @@ def sample_tokens(logits: np.ndarray, temperature: float, seed: int, counters):
     s = gumbel_scores(logits, temperature, seed, counters)
     tok = np.argmax(s, axis=1)
     return tok, s[np.arange(s.shape[0]), tok], s
+
+
+def top_k_rows(logits_row: np.ndarray, top_k: int) -> np.ndarray:
+    """Ids of the top_k largest logits of one row, larger logit first, equal
+    logits by lower id."""
+    v = np.asarray(logits_row, dtype=np.float64)
+    order = np.lexsort((np.arange(v.size), -v))
+    return order[:top_k]
+
+
+def sample_tokens_topk(logits: np.ndarray, temperature: float, top_k: int, seed: int, counters):
+    """Top-k sampling: token = lowest id attaining the largest perturbed score
+    logit_v / T + g_v among the top_k rows of each sequence (same noise as
+    sample_tokens).  Returns (tokens [B], that score [B], the scores [B][V]
+    with rows outside the top k set to -inf)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    if not 1 <= top_k <= logits.shape[1]:
+        raise ValueError("top_k must lie in 1..V")
+    _, _, s = sample_tokens(logits, temperature, seed, counters)
+    masked = np.full_like(s, -np.inf)
+    for b in range(s.shape[0]):
+        keep = top_k_rows(logits[b], top_k)
+        masked[b, keep] = s[b, keep]
+    tok = np.argmax(masked, axis=1)
+    return tok, masked[np.arange(s.shape[0]), tok], masked

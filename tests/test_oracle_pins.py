@@ -519,3 +519,43 @@ def test_vanishing_temperature_gives_the_greedy_token():
     assert np.array_equal(tok, np.argmax(logits, axis=1))
     with pytest.raises(ValueError):
         oracle.sample_tokens(logits, 0.0, 7, [0, 1, 2, 3])
+
+
+# ----------------------------------------------------------------------------- top-k sampling
+
+def test_topk_draws_follow_the_renormalised_softmax_over_the_top_k():
+    """Frequencies of many top-k draws: softmax(logits / T) over the k largest
+    logits, renormalised, and never a row outside them."""
+    logits = np.array([1.0, 0.5, 0.0, -1.0, 2.0, 0.2, -0.3])
+    T, n, k = 0.9, 40_000, 3
+    keep = np.array([4, 0, 1])                            # 2.0, 1.0, 0.5
+    p = np.zeros(logits.size)
+    p[keep] = softmax(logits[keep] / T)
+    tok = oracle.sample_tokens_topk(np.tile(logits, (n, 1)), T, k, 31, np.zeros(n, dtype=np.int64))[0]
+    freq = np.bincount(tok, minlength=logits.size) / n
+    assert np.all(freq[p == 0] == 0)
+    sigma = np.sqrt(p[keep] * (1 - p[keep]) / n)
+    assert np.all(np.abs(freq[keep] - p[keep]) < 5 * sigma), (freq, p)
+
+
+def test_topk_one_is_greedy_and_topk_v_is_the_plain_draw():
+    rng = np.random.default_rng(6)
+    logits = rng.standard_normal((5, 800))
+    ctr = [3, 1, 4, 1, 5]
+    t1 = oracle.sample_tokens_topk(logits, 1.7, 1, 11, ctr)[0]
+    assert np.array_equal(t1, np.argmax(logits, axis=1))
+    tv, sv, _ = oracle.sample_tokens_topk(logits, 1.7, 800, 11, ctr)
+    t0, s0, _ = oracle.sample_tokens(logits, 1.7, 11, ctr)
+    assert np.array_equal(tv, t0) and np.array_equal(sv, s0)
+    with pytest.raises(ValueError):
+        oracle.sample_tokens_topk(logits, 1.0, 0, 11, ctr)
+
+
+def test_topk_cut_keeps_equal_logits_by_lower_id():
+    v = np.array([0.5, 2.0, 1.0, 1.0, 1.0, -3.0])
+    assert list(oracle.top_k_rows(v, 3)) == [1, 2, 3]
+    assert list(oracle.top_k_rows(v, 1)) == [1]
+    # a draw at k = 3 never lands on row 4 although its logit equals row 3's
+    n = 5000
+    tok = oracle.sample_tokens_topk(np.tile(v, (n, 1)), 1.0, 3, 2, np.zeros(n, dtype=np.int64))[0]
+    assert set(np.unique(tok)) <= {1, 2, 3}

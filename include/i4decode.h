@@ -273,6 +273,25 @@ int i4d_lm_head_sample(const i4d_mat* w_lm, int32_t batch, const float* h, int32
                        int32_t* token_out, float* score_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Top-k sampling (the decode loop's sample step of Primer 1.2 with the
+ * optional top-k restriction): token_out[b] is a draw from
+ * softmax(logits / temperature) renormalised over the top_k largest logits of
+ * sequence b (equal logits ranked by lower id), i.e. the lowest v maximising
+ * the perturbed score of i4d_lm_head_sample (same noise, same counter words)
+ * among those top_k rows only.  top_k = V gives i4d_lm_head_sample's token,
+ * top_k = 1 the greedy token.  score_out[b] = the winning perturbed score.
+ * 1 <= top_k <= min(64, V), ceil(V / 1024) * top_k <= 16384 (else
+ * I4D_ERANGE / I4D_EUNSUPPORTED).  Unlike the greedy and temperature heads,
+ * the step's logits [B][V] (fp32) are written to the workspace, whose size
+ * must be at least i4d_topk_workspace_size(w_lm, batch, top_k) (initialised
+ * as for the decode calls).  Other arguments and conditions as for
+ * i4d_lm_head_sample.                                                        */
+size_t i4d_topk_workspace_size(const i4d_mat* w_lm, int32_t batch, int32_t top_k);
+int i4d_lm_head_sample_topk(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t top_k,
+                            float temperature, uint64_t seed, const int32_t* counter,
+                            int32_t* token_out, float* score_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Embedding lookup (Primer 1.2: the decode loop starts from the embedding of
  * the last token): x_out[b] = fp32 of row tokens[b] of the bf16 table
  * [vocab][d_model] (row-major).  tokens [B] int32 (device); an id outside

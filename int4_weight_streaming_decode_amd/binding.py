@@ -87,6 +87,10 @@ def lib():
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
         L.i4d_prefill_chunk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                         ctypes.POINTER(I4dKv), P, I, P, Z, P]
+        L.i4d_topk_workspace_size.argtypes = [ctypes.POINTER(I4dMat), I, I]
+        L.i4d_topk_workspace_size.restype = Z
+        L.i4d_lm_head_sample_topk.argtypes = [ctypes.POINTER(I4dMat), I, P, I, ctypes.c_float, ctypes.c_uint64, P, P, P, P,
+                                              Z, P]
         L.i4d_prefill_workspace_size.argtypes = [ctypes.POINTER(I4dConfig), I]
         L.i4d_prefill_workspace_size.restype = Z
         L.i4d_prefill.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P, ctypes.POINTER(I4dKv), I,
@@ -108,7 +112,7 @@ def lib():
                      "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe",
-                     "i4d_lm_head_chunked_noalloc", "i4d_prefill"):
+                     "i4d_lm_head_chunked_noalloc", "i4d_prefill", "i4d_lm_head_sample_topk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -209,6 +213,18 @@ def prefill_chunk(cfg, layers, n_tokens, x_in, x_out, kvs, pos, max_pos, ws, str
     karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
     _check(lib().i4d_prefill_chunk(ctypes.byref(cfg), n, larr, n_tokens, _ptr(x_in), _ptr(x_out), karr, _ptr(pos), max_pos,
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "i4d_prefill_chunk")
+
+
+def topk_workspace_size(w_lm: I4dMat, batch: int, top_k: int) -> int:
+    return int(lib().i4d_topk_workspace_size(ctypes.byref(w_lm), batch, top_k))
+
+
+def lm_head_sample_topk(w_lm: I4dMat, batch, h, top_k, temperature, seed, counter, token_out, score_out, ws,
+                        stream=None):
+    _check(lib().i4d_lm_head_sample_topk(ctypes.byref(w_lm), batch, _ptr(h), int(top_k), float(temperature),
+                                         int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(counter), _ptr(token_out),
+                                         _ptr(score_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "i4d_lm_head_sample_topk")
 
 
 def prefill_workspace_size(cfg: I4dConfig, n_tokens: int) -> int:

@@ -365,6 +365,77 @@ __global__ void __launch_bounds__(64) k_advance(int* pos, int nb) {
     if (i4d_tid() < nb) pos[i4d_tid()] += 1;
 }
 
+// ---------------------------------------------------------------- top-k sampling
+// Top-k sampling (the decode loop's sample step restricted to the k largest
+// logits, renormalised): the logits of a step are written by the LM head's
+// GEMV, every 1024-row slice keeps its k largest ordered keys (logit, then
+// lower id: argmax_key), one workgroup per sequence merges the slices' lists
+// into the global k largest, and the token is the Gumbel-max over those k
+// rows (the noise of Sampler::score, so k = V gives the temperature draw and
+// k = 1 the greedy token).
+constexpr int TOPK_MAX = 64, TOPK_SLICE = 1024, TOPK_MERGE_MAX = 16384;
+
+// Bitonic sort of n (a power of two) keys in LDS into descending order.
+I4D_DEVINL void bitonic_desc(u64* key, int n) {
+    for (int size = 2; size <= n; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = threadIdx.x; t < (n >> 1); t += blockDim.x) {
+                const int i = 2 * t - (t & (stride - 1)), j = i + stride;
+                const bool desc = (i & size) == 0;
+                const u64 a = key[i], c = key[j];
+                if ((a < c) == desc) { key[i] = c; key[j] = a; }
+            }
+            __syncthreads();
+        }
+}
+
+// grid (slices, B): the k largest keys of rows [1024 s, 1024 s + 1024) of
+// sequence b's logits into cand[b][s][0..k) (key 0 pads past the vocabulary)
+__global__ void __launch_bounds__(512) k_topk_slice(const float* logits, int V, int k, u64* cand) {
+    __shared__ u64 key[TOPK_SLICE];
+    const int sl = blockIdx.x, b = blockIdx.y, nsl = gridDim.x;
+    for (int i = threadIdx.x; i < TOPK_SLICE; i += blockDim.x) {
+        const int row = sl * TOPK_SLICE + i;
+        key[i] = row < V ? argmax_key(ld_g(logits + (size_t)b * V + row), (u32)row) : 0ull;
+    }
+    __syncthreads();
+    bitonic_desc(key, TOPK_SLICE);
+    for (int i = threadIdx.x; i < k; i += blockDim.x) cand[((size_t)b * nsl + sl) * k + i] = key[i];
+}
+
+// grid (B): merge sequence b's n = slices * k candidate keys (n padded to the
+// power of two np2 in LDS), keep the k largest, and draw among them
+__global__ void __launch_bounds__(1024) k_topk_sample(const u64* cand, int n, int np2, int k, Sampler smp, int32_t* token_out,
+                                                      float* score_out) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    u64* key = (u64*)lds;
+    __shared__ u64 wbest[16];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    for (int i = tid; i < np2; i += blockDim.x) key[i] = i < n ? ld_g(cand + (size_t)b * n + i) : 0ull;
+    __syncthreads();
+    bitonic_desc(key, np2);
+    u64 best = 0;
+    if (tid < k && key[tid] != 0ull) {
+        const u64 kk = key[tid];
+        const u32 row = 0xFFFFFFFFu - (u32)kk;
+        const float logit = float_from_order_key((u32)(kk >> 32));
+        best = argmax_key(smp.score(logit, b, row), row);
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        const u32 lo = __shfl_xor((u32)best, o, 64), hi = __shfl_xor((u32)(best >> 32), o, 64);
+        const u64 other = ((u64)hi << 32) | lo;
+        best = other > best ? other : best;
+    }
+    if ((tid & 63) == 0) wbest[tid >> 6] = best;
+    __syncthreads();
+    if (tid == 0) {
+        u64 m = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = wbest[w] > m ? wbest[w] : m;
+        token_out[b] = (int32_t)(0xFFFFFFFFu - (u32)m);
+        score_out[b] = float_from_order_key((u32)(m >> 32));
+    }
+}
+
 // ---------------------------------------------------------------- batched (MFMA) phases
 template <int NB>
 __global__ void __launch_bounds__(512) k_mfma_rows(MfmaTask m, float* y, const float* resid) {
@@ -1601,6 +1672,77 @@ int i4d_embed(const uint16_t* table, int32_t vocab, int32_t d_model, int32_t bat
     hipLaunchKernelGGL(k_embed, grid, dim3(256), 0, (hipStream_t)stream, table, vocab, d_model, tokens, x_out,
                        (int*)((char*)ws + WS_STATUS));
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+// Workspace of top-k sampling: the LM head GEMV's own scratch (batches above
+// 8), then the logits [B][V] fp32 and the slices' candidate keys [B][slices][k].
+struct TopkWs { size_t logits, cand, total; int slices; };
+static int topk_ws(const i4d_mat* w_lm, int batch, int top_k, TopkWs& t) {
+    size_t off = WS_HEADER;
+    if (batch > MAX_BATCH) {
+        if (!mfma_mat_ok(*w_lm)) return I4D_EUNSUPPORTED;
+        const int nb = nb_mfma(batch);
+        const GemvTask tk = make_task(KIND_ADJ, w_lm, nullptr, nullptr, 64);
+        const MfmaPlan p = mfma_plan(tk.total_pairs, w_lm->k, nb, 1, true);
+        off = WS_LM_END + mfma_scratch(w_lm->k, nb, mfma_part_bytes(p, nb), 64).total;
+    }
+    t.slices = (w_lm->n + TOPK_SLICE - 1) / TOPK_SLICE;
+    if ((long long)t.slices * top_k > TOPK_MERGE_MAX) return I4D_EUNSUPPORTED;
+    t.logits = align256(off);
+    t.cand = align256(t.logits + (size_t)batch * w_lm->n * 4);
+    t.total = t.cand + (size_t)batch * t.slices * top_k * 8;
+    return I4D_OK;
+}
+
+static int lm_head_topk_impl(bool run, const i4d_mat* w_lm, int32_t batch, const float* h, int32_t top_k, float temperature,
+                             uint64_t seed, const int32_t* counter, int32_t* token_out, float* score_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    if (!w_lm || w_lm->dtype != I4D_WEIGHT_INT4) return I4D_EINVAL;
+    int rc;
+    if ((rc = validate_mat(w_lm, w_lm->n, w_lm->k, I4D_WEIGHT_INT4, w_lm->group))) return rc;
+    if (w_lm->n < 1 || w_lm->k < 8) return I4D_EINVAL;
+    if (batch < 1 || batch > MAX_BATCH_ALL) return I4D_ERANGE;
+    if (top_k < 1 || top_k > TOPK_MAX || top_k > w_lm->n) return I4D_ERANGE;
+    if (!h || !token_out || !score_out || !counter) return I4D_EINVAL;
+    if (!aligned(h, 16) || !aligned(counter, 4)) return I4D_EALIGN;
+    Sampler smp;
+    if ((rc = make_sampler(temperature, seed, counter, smp))) return rc;
+    TopkWs T;
+    if ((rc = topk_ws(w_lm, batch, top_k, T))) return rc;
+    if ((rc = validate_ws(ws, ws_bytes, T.total))) return rc;
+    if (!run) return I4D_OK;
+    char* w = (char*)ws;
+    float* logits = (float*)(w + T.logits);
+    u64* cand = (u64*)(w + T.cand);
+    hipStream_t s = (hipStream_t)stream;
+    {
+        TimeScope ts(I4D_TIME_LM_HEAD);
+        if ((rc = i4d_gemv(w_lm, batch, h, logits, ws, ws_bytes, stream))) return rc;
+    }
+    if ((rc = scratch_free(k_topk_slice)) || (rc = scratch_free(k_topk_sample))) return rc;
+    hipLaunchKernelGGL(k_topk_slice, dim3(T.slices, batch), dim3(512), 0, s, (const float*)logits, w_lm->n, top_k, cand);
+    if (hipGetLastError() != hipSuccess) return I4D_EHIP;
+    const int n = T.slices * top_k;
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    if ((rc = set_lds(k_topk_sample, (size_t)np2 * 8))) return rc;
+    hipLaunchKernelGGL(k_topk_sample, dim3(batch), dim3(1024), (size_t)np2 * 8, s, (const u64*)cand, n, np2, top_k, smp,
+                       token_out, score_out);
+    return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
+}
+
+size_t i4d_topk_workspace_size(const i4d_mat* w_lm, int32_t batch, int32_t top_k) {
+    if (!w_lm || w_lm->n < 1 || batch < 1 || batch > MAX_BATCH_ALL || top_k < 1 || top_k > TOPK_MAX) return 0;
+    TopkWs T;
+    if (topk_ws(w_lm, batch, top_k, T)) return 0;
+    return T.total;
+}
+
+int i4d_lm_head_sample_topk(const i4d_mat* w_lm, int32_t batch, const float* h, int32_t top_k, float temperature,
+                            uint64_t seed, const int32_t* counter, int32_t* token_out, float* score_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    return lm_head_topk_impl(true, w_lm, batch, h, top_k, temperature, seed, counter, token_out, score_out, ws, ws_bytes,
+                             stream);
 }
 
 static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,

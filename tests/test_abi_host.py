@@ -318,3 +318,26 @@ def test_prefill_validation(lib):
     assert 0 < n1 < B.prefill_workspace_size(cfg_ok, 512) < B.prefill_workspace_size(cfg_ok, 4096)
     assert B.prefill_workspace_size(cfg_ok, 0) == 0
     assert B.prefill_workspace_size(cfg_ok, 65537) == 0
+
+
+def test_topk_sampling_validation(lib):
+    """Top-k sampling: k range, temperature, the merge bound and the workspace
+    size are checked before anything is enqueued."""
+    P = ctypes.c_void_p
+    w = _mat(151936, 512, 128)
+
+    def call(top_k=40, T=0.8, batch=1, ws_bytes=1 << 40, mat=w):
+        return lib.i4d_lm_head_sample_topk(ctypes.byref(mat), batch, P(0x100000), top_k, ctypes.c_float(T),
+                                           ctypes.c_uint64(7), P(0x300000), P(0x200000), P(0x210000), P(0x400000),
+                                           ws_bytes, None)
+
+    assert call(top_k=0) == B.I4D_ERANGE
+    assert call(top_k=65) == B.I4D_ERANGE
+    assert call(T=0.0) == B.I4D_EINVAL
+    assert call(T=float("inf")) == B.I4D_EINVAL
+    assert call(batch=33) == B.I4D_ERANGE
+    assert call(ws_bytes=16) == B.I4D_EWORKSPACE
+    assert call(mat=_mat(300000, 512, 128), top_k=64) == B.I4D_EUNSUPPORTED    # 293 slices x 64 > 16384
+    n1 = B.topk_workspace_size(w, 1, 40)
+    assert n1 >= 151936 * 4 and B.topk_workspace_size(w, 4, 40) > n1
+    assert B.topk_workspace_size(w, 1, 0) == 0 and B.topk_workspace_size(w, 1, 65) == 0

@@ -1,0 +1,108 @@
+"""Top-k sampling through the C ABI (i4d_lm_head_sample_topk) against
+oracle.sample_tokens_topk: the k largest logits (equal ones by lower id), then
+the Gumbel-max draw of temperature sampling over those rows only, logits in
+float64 on the oracle side.  Token ids must match exactly unless the oracle's
+cut (k-th against (k+1)-th logit) or its top-2 gap of perturbed scores is a
+near-tie within the float32 logits' error; then the GPU's token must be a valid
+near-choice.  Winning scores to the usual float bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from int4_weight_streaming_decode_amd import binding as B
+from synth import gpu as G
+from tests.gpu_util import DevMat, assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x0FED_CBA9_8765_4321
+
+
+def _check(got_tok, got_score, logits, T, k, ctr, what):
+    ref_tok, _, masked = oracle.sample_tokens_topk(logits, T, k, SEED, ctr)
+    full = oracle.gumbel_scores(logits, T, SEED, ctr)
+    for b in range(len(got_tok)):
+        tol_l = 1e-3 * np.sqrt(np.mean(logits[b] ** 2)) + 1e-4     # float32 logit error
+        tol_s = tol_l / T
+        order = oracle.top_k_rows(logits[b], logits.shape[1])
+        lk = logits[b, order[k - 1]]
+        cut_clear = k == logits.shape[1] or lk - logits[b, order[k]] > 2 * tol_l
+        s = np.sort(masked[b][np.isfinite(masked[b])])
+        draw_clear = s.size < 2 or s[-1] - s[-2] > 2 * tol_s
+        g = int(got_tok[b])
+        if cut_clear and draw_clear:
+            assert g == ref_tok[b], f"{what} b={b}: token {g} != {ref_tok[b]}"
+        else:
+            assert logits[b, g] >= lk - 2 * tol_l, f"{what} b={b}: token {g} outside the near-top-{k}"
+            assert full[b, g] >= s[-1] - 2 * tol_s, f"{what} b={b}: token {g} not a near-maximiser"
+    assert_close(np.asarray(got_score, dtype=np.float64), full[np.arange(len(got_tok)), got_tok.astype(np.int64)],
+                 what=f"{what} score")
+
+
+@pytest.mark.parametrize("vocab,d,batch,T,k", [(3000, 512, 1, 0.8, 1), (3000, 512, 1, 0.8, 5), (20001, 1024, 5, 1.3, 40),
+                                               (9000, 1024, 16, 0.6, 64), (4099, 5120, 32, 2.0, 17), (64, 512, 3, 1.0, 64)])
+def test_lm_head_sample_topk_matches_oracle(vocab, d, batch, T, k):
+    print("CASE topk", vocab, d, batch, T, k, flush=True)
+    lm = synth.make_lm_head(vocab, d, 128, seed=vocab + 11 * batch)
+    h = synth.make_hidden(d, seed=vocab + 5, batch=batch)
+    ctr = np.random.default_rng(batch + k).integers(0, 2 ** 31 - 1, size=batch).astype(np.int32)
+    _, _, logits = oracle.lm_head_argmax(lm, h.astype(np.float64))
+    m = DevMat(lm)
+    n = B.topk_workspace_size(m.mat, batch, k)
+    assert n > 0
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    sc = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    runs = []
+    for rep in range(2):
+        B.lm_head_sample_topk(m.mat, batch, dev(h), k, T, SEED, dev(ctr), tok, sc, ws)
+        torch.cuda.synchronize()
+        runs.append((tok.cpu().numpy().copy(), sc.cpu().numpy().copy()))
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1]), "same inputs, different draw"
+    assert B.read_device_status(ws) == 0
+    _check(runs[0][0], runs[0][1], logits, T, k, ctr, f"topk V={vocab} B={batch} k={k}")
+
+
+def test_topk_one_gives_the_greedy_token():
+    vocab, d, batch = 5000, 1024, 4
+    lm = synth.make_lm_head(vocab, d, 128, seed=3)
+    h = synth.make_hidden(d, seed=4, batch=batch)
+    tok_ref, _, logits = oracle.lm_head_argmax(lm, h.astype(np.float64))
+    m = DevMat(lm)
+    ws = torch.zeros(B.topk_workspace_size(m.mat, batch, 1), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    sc = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    B.lm_head_sample_topk(m.mat, batch, dev(h), 1, 0.7, SEED, dev(np.arange(batch, dtype=np.int32)), tok, sc, ws)
+    torch.cuda.synchronize()
+    got = tok.cpu().numpy()
+    srt = np.sort(logits, axis=1)
+    for b in range(batch):
+        if srt[b, -1] - srt[b, -2] > 1e-3 * np.sqrt(np.mean(logits[b] ** 2)):
+            assert got[b] == tok_ref[b]
+
+
+def test_lm_head_sample_topk_at_full_size():
+    """152064 x 5120 int4 head from the bench's device generator, batch 2, k = 50."""
+    shape = synth.SHAPES["27b_lm"]
+    batch, T, k = 2, 0.9, 50
+    print("CASE topk full size", shape.vocab, shape.d_model, batch, k, flush=True)
+    W = G.make_lm_head_gpu(shape.vocab, shape.d_model, shape.group, 2)
+    mat = B.make_mat(W["codes"], W["scales"], W["n"], W["k"], W["group"], B.WEIGHT_INT4)
+    h = G.make_x_gpu(shape, 8, batch)
+    ctr = np.array([8192, 70000], dtype=np.int32)
+    ws = torch.zeros(B.topk_workspace_size(mat, batch, k), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    sc = torch.empty((batch,), dtype=torch.float32, device="cuda")
+    B.lm_head_sample_topk(mat, batch, h, k, T, SEED, dev(ctr), tok, sc, ws)
+    torch.cuda.synchronize()
+    lm = {"codes": W["codes"].cpu().numpy().view(np.uint8), "scales": W["scales"].cpu().numpy().view(np.uint16),
+          "n": W["n"], "k": W["k"], "group": W["group"]}
+    _, _, logits = oracle.lm_head_argmax(lm, h.cpu().numpy().astype(np.float64))
+    _check(tok.cpu().numpy(), sc.cpu().numpy(), logits, T, k, ctr, "topk full size")

@@ -329,6 +329,18 @@ int i4d_decode_step_sample(const i4d_config* cfg, int32_t n_layers, const i4d_la
                            int32_t max_pos, float* x_buf, const i4d_kv* kv, float temperature, uint64_t seed,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* i4d_decode_step with the token drawn by top-k sampling
+ * (i4d_lm_head_sample_topk at top_k, temperature and seed; counter word of
+ * sequence b = pos[b] before this step's advance).  ws_bytes must be at least
+ * both i4d_workspace_size(cfg, n_layers, batch, max_pos, V) and
+ * i4d_topk_workspace_size(w_lm, batch, top_k); at batch 1 the sampling
+ * scratch must also end before the streaming kernel's region (true for
+ * vocabularies up to about 200k), else I4D_EUNSUPPORTED.                     */
+int i4d_decode_step_sample_topk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                                const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* score_out, int32_t* pos,
+                                int32_t max_pos, float* x_buf, const i4d_kv* kv, int32_t top_k, float temperature,
+                                uint64_t seed, void* ws, size_t ws_bytes, void* stream);
+
 /* Expand an int4 matrix to fp32 out [n][k]: out = (code - 8) * scale, exact
  * (Unsloth article 二.3).  A test hook for the int4 format.                 */
 int i4d_dequant_int4(const i4d_mat* w, float* out, void* stream);

@@ -87,6 +87,9 @@ def lib():
         L.i4d_embed.argtypes = [P, I, I, I, P, P, P, Z, P]
         L.i4d_prefill_chunk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), I, P, P,
                                         ctypes.POINTER(I4dKv), P, I, P, Z, P]
+        L.i4d_decode_step_sample_topk.argtypes = [ctypes.POINTER(I4dConfig), I, ctypes.POINTER(I4dLayer), P,
+                                                  ctypes.POINTER(I4dMat), I, P, P, P, I, P, ctypes.POINTER(I4dKv), I,
+                                                  ctypes.c_float, ctypes.c_uint64, P, Z, P]
         L.i4d_topk_workspace_size.argtypes = [ctypes.POINTER(I4dMat), I, I]
         L.i4d_topk_workspace_size.restype = Z
         L.i4d_lm_head_sample_topk.argtypes = [ctypes.POINTER(I4dMat), I, P, I, ctypes.c_float, ctypes.c_uint64, P, P, P, P,
@@ -112,7 +115,8 @@ def lib():
                      "i4d_decode_step", "i4d_prefill_chunk", "i4d_lm_head_sample", "i4d_decode_step_sample",
                      "i4d_dequant_int4", "i4d_gemv", "i4d_attention", "i4d_read_device_status",
                      "i4d_launch_timing_start", "i4d_launch_timing_stop", "i4d_read_probe",
-                     "i4d_lm_head_chunked_noalloc", "i4d_prefill", "i4d_lm_head_sample_topk"):
+                     "i4d_lm_head_chunked_noalloc", "i4d_prefill", "i4d_lm_head_sample_topk",
+                     "i4d_decode_step_sample_topk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,6 +270,19 @@ def decode_step_sample(cfg, layers, embed_table, w_lm: I4dMat, batch, tokens, sc
                                         _ptr(tokens), _ptr(score_out), _ptr(pos), max_pos, _ptr(x_buf), karr,
                                         float(temperature), int(seed), _ptr(ws), ws.numel() * ws.element_size(),
                                         _stream(stream)), "i4d_decode_step_sample")
+
+
+def decode_step_sample_topk(cfg, layers, embed_table, w_lm: I4dMat, batch, tokens, score_out, pos, max_pos, x_buf,
+                            kvs, top_k, temperature, seed, ws, stream=None):
+    """decode_step with the token drawn by top-k sampling (counter word: each sequence's position)."""
+    n = len(layers)
+    larr = layers if isinstance(layers, ctypes.Array) else (I4dLayer * n)(*layers)
+    karr = kvs if isinstance(kvs, ctypes.Array) else (I4dKv * n)(*kvs)
+    _check(lib().i4d_decode_step_sample_topk(ctypes.byref(cfg), n, larr, _ptr(embed_table), ctypes.byref(w_lm), batch,
+                                             _ptr(tokens), _ptr(score_out), _ptr(pos), max_pos, _ptr(x_buf), karr,
+                                             int(top_k), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)),
+           "i4d_decode_step_sample_topk")
 
 
 def dequant_int4(w: I4dMat, out, stream=None):

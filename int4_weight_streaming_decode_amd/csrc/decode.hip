@@ -1745,10 +1745,11 @@ int i4d_lm_head_sample_topk(const i4d_mat* w_lm, int32_t batch, const float* h, 
                              stream);
 }
 
+// top_k > 0: the token is drawn by top-k sampling at (temperature, seed)
 static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
                             const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* max_logit_out, int32_t* pos,
                             int32_t max_pos, float* x_buf, const i4d_kv* kv, void* ws, size_t ws_bytes, void* stream,
-                            const Sampler& smp) {
+                            const Sampler& smp, int top_k = 0, float temperature = 0.f, uint64_t seed = 0) {
     int rc;
     if ((rc = validate_cfg(cfg))) return rc;
     if (!embed || !w_lm || !tokens || !pos || !x_buf) return I4D_EINVAL;
@@ -1759,7 +1760,20 @@ static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_l
     float* x1 = x_buf + plane;
     // every check before anything is enqueued
     if ((rc = decode_stack_impl(false, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
-    if ((rc = lm_head_impl(false, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp))) return rc;
+    auto head = [&](bool run) {
+        return top_k > 0 ? lm_head_topk_impl(run, w_lm, batch, x1, top_k, temperature, seed, pos, tokens, max_logit_out, ws,
+                                             ws_bytes, stream)
+                         : lm_head_impl(run, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp);
+    };
+    if ((rc = head(false))) return rc;
+    if (top_k > 0) {
+        // the sampling scratch must not reach the streaming kernel's region,
+        // whose exchange words carry over from step to step
+        TopkWs T;
+        if ((rc = topk_ws(w_lm, batch, top_k, T))) return rc;
+        const WsLayout W = ws_layout(cfg, n_layers, batch);
+        if (W.stream != 0 && T.total > W.stream) return I4D_EUNSUPPORTED;
+    }
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((cfg->d_model + 255) / 256, batch);
     if (const int rc_ = scratch_free(k_embed)) return rc_;
@@ -1768,7 +1782,7 @@ static int decode_step_impl(const i4d_config* cfg, int32_t n_layers, const i4d_l
                        (int*)((char*)ws + WS_STATUS));
     if (hipGetLastError() != hipSuccess) return I4D_EHIP;
     if ((rc = decode_stack_impl(true, cfg, n_layers, layers, batch, x0, x1, kv, pos, max_pos, ws, ws_bytes, stream))) return rc;
-    if ((rc = lm_head_impl(true, w_lm, batch, x1, 8192, tokens, max_logit_out, ws, ws_bytes, stream, smp))) return rc;
+    if ((rc = head(true))) return rc;
     hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, s, pos, batch);
     return hipGetLastError() == hipSuccess ? I4D_OK : I4D_EHIP;
 }
@@ -1790,6 +1804,16 @@ int i4d_decode_step_sample(const i4d_config* cfg, int32_t n_layers, const i4d_la
     if ((rc = make_sampler(temperature, seed, pos, smp))) return rc;
     return decode_step_impl(cfg, n_layers, layers, embed, w_lm, batch, tokens, score_out, pos, max_pos, x_buf, kv, ws,
                             ws_bytes, stream, smp);
+}
+
+int i4d_decode_step_sample_topk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, const uint16_t* embed,
+                                const i4d_mat* w_lm, int32_t batch, int32_t* tokens, float* score_out, int32_t* pos,
+                                int32_t max_pos, float* x_buf, const i4d_kv* kv, int32_t top_k, float temperature,
+                                uint64_t seed, void* ws, size_t ws_bytes, void* stream) {
+    if (top_k < 1) return I4D_ERANGE;
+    // the counter word of sequence b is its position pos[b] (read before the advance)
+    return decode_step_impl(cfg, n_layers, layers, embed, w_lm, batch, tokens, score_out, pos, max_pos, x_buf, kv, ws,
+                            ws_bytes, stream, Sampler{0.f, 0u, 0u, nullptr}, top_k, temperature, seed);
 }
 
 int i4d_dequant_int4(const i4d_mat* wm, float* out, void* stream) {

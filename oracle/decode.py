@@ -290,15 +290,18 @@ def embed_tokens(table_bits: np.ndarray, tokens) -> np.ndarray:
 
 
 def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, tokens, caches: list, pos, steps: int,
-                  temperature=None, seed: int = 0) -> dict:
+                  temperature=None, seed: int = 0, top_k: int = 0) -> dict:
     """`steps` rounds of Primer 1.2's decode loop: embed the last token, run
     the stack (appending each layer's K/V at pos), take the LM head's token,
     advance every position by one.  The token is the greedy one, or with a
     temperature the Gumbel-max draw of oracle.sample with each sequence's
     position as its counter word ("max_logit" then holds the winning perturbed
-    score and "logits" the perturbed scores).  Returns per-step tokens, maximum
-    scores and scores, the final hidden state and the caches."""
-    from .sample import sample_tokens
+    score and "logits" the perturbed scores); with top_k > 0 as well, the draw
+    is restricted to the top_k largest logits (oracle.sample_tokens_topk; the
+    scores of the other rows are -inf, and "raw" holds the step's logits).
+    Returns per-step tokens, maximum scores and scores, the final hidden state
+    and the caches."""
+    from .sample import sample_tokens, sample_tokens_topk
     tok = np.asarray(tokens, dtype=np.int64)
     pos = np.asarray(pos, dtype=np.int64)
     out = {"tokens": [], "max_logit": [], "logits": []}
@@ -306,7 +309,10 @@ def greedy_decode(shape, layers: list, table_bits: np.ndarray, w_lm: dict, token
         r = decode_stack(shape, layers, embed_tokens(table_bits, tok), caches, pos)
         caches = r["caches"]
         tok, mx, logits = lm_head_argmax(w_lm, r["z"])
-        if temperature is not None:
+        out.setdefault("raw", []).append(logits)
+        if temperature is not None and top_k > 0:
+            tok, mx, logits = sample_tokens_topk(logits, temperature, top_k, seed, pos)
+        elif temperature is not None:
             tok, mx, logits = sample_tokens(logits, temperature, seed, pos)
         out["tokens"].append(tok.copy())
         out["max_logit"].append(mx)

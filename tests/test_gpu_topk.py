@@ -106,3 +106,50 @@ def test_lm_head_sample_topk_at_full_size():
           "n": W["n"], "k": W["k"], "group": W["group"]}
     _, _, logits = oracle.lm_head_argmax(lm, h.cpu().numpy().astype(np.float64))
     _check(tok.cpu().numpy(), sc.cpu().numpy(), logits, T, k, ctr, "topk full size")
+
+
+SHAPE = synth.SHAPES["tiny"].with_(name="gen", d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128, d_ff=1024,
+                                   group=128, rope_base=1e6)
+VOCAB = 3000
+
+
+@pytest.mark.parametrize("batch,k", [(1, 20), (4, 5), (16, 64)])
+def test_topk_decode_steps_match_the_oracle_loop(batch, k):
+    """Whole decode steps (embed, stack, top-k draw, advance) against the
+    oracle's loop with the same top-k rule; batch 1 runs the streaming kernel."""
+    from tests.gpu_util import DevKV, DevLayer, config_of
+    n_layers, pos0, steps, T = 2, 150, 3, 0.9
+    cap = 160
+    print("CASE decode_step_sample_topk", batch, k, flush=True)
+    layers = [synth.make_layer(SHAPE, 71 + batch, l) for l in range(n_layers)]
+    caches = [synth.make_kv(SHAPE, 71 + batch, l, batch, [pos0] * batch, cap) for l in range(n_layers)]
+    table = synth.make_embedding(VOCAB, SHAPE.d_model, 71 + batch)
+    lm = synth.make_lm_head(VOCAB, SHAPE.d_model, SHAPE.group, 72 + batch)
+    tok0 = np.random.default_rng(batch + 3).integers(0, VOCAB, size=batch).astype(np.int32)
+    Ls = [DevLayer(l) for l in layers]
+    kvs = [DevKV(*c) for c in caches]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+    n = max(B.workspace_size(cfg, n_layers, batch, cap - 1, VOCAB), B.topk_workspace_size(W.mat, batch, k))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    tokens = dev(tok0)
+    pos = dev(np.full(batch, pos0, dtype=np.int32))
+    sc = torch.empty(batch, dtype=torch.float32, device="cuda")
+    xbuf = torch.empty((2, batch, SHAPE.d_model), dtype=torch.float32, device="cuda")
+    got = []
+    for s in range(steps):
+        B.decode_step_sample_topk(cfg, [l.layer for l in Ls], emb, W.mat, batch, tokens, sc, pos, pos0 + s, xbuf,
+                                  [kv.kv for kv in kvs], k, T, SEED, ws)
+        torch.cuda.synchronize()
+        got.append((tokens.cpu().numpy().copy(), sc.cpu().numpy().copy()))
+    assert B.read_device_status(ws) == 0
+    assert np.array_equal(pos.cpu().numpy(), np.full(batch, pos0 + steps))
+    ref = oracle.greedy_decode(SHAPE, layers, table, lm, tok0, caches, [pos0] * batch, steps, temperature=T, seed=SEED,
+                               top_k=k)
+    for s in range(steps):
+        logits = ref["raw"][s]
+        ctr = np.full(batch, pos0 + s)
+        _check(got[s][0], got[s][1], logits, T, k, ctr, f"step {s}")
+        if not np.array_equal(got[s][0], ref["tokens"][s]):
+            pytest.skip(f"step {s}: a near-tie chose another valid token; later steps are not comparable")

@@ -8,7 +8,10 @@ to the host, and the CPU oracle recomputes the same step:
     5e5) at batch 1 and at batch 32 (matrix-core path, 32 positions);
   * two chained 27B-shaped int4 layers over two decode steps (the second step
     reads the K/V the first one appended);
-  * the 152064 x 5120 int4 LM head (batch 1 and 16).
+  * the 152064 x 5120 int4 LM head (batch 1 and 16);
+  * one 27B-shaped layer prefilled with a 512-token prompt (i4d_prefill, the
+    launch configuration of bench.py --prefill 512): sampled tokens recomputed
+    one by one, each against the cache the GPU built for the tokens before it.
 Batches are independent sequences, so at batch 32 the oracle recomputes a
 sample of the sequences (first, middle, last) while the GPU runs all of them.
 Same bars as the other parity tests: float outputs relative L2 <= 1e-3 and
@@ -201,3 +204,41 @@ def test_lm_head_at_full_size(batch):
         else:
             assert logits[b][t[b]] >= srt[-1] - 1e-3 * rms
     assert_close(mx.cpu().numpy(), mx_ref, what="full LM head max logit")
+
+
+def test_prefill_27b_layer_512_tokens_sampled(monkeypatch):
+    """i4d_prefill of a 512-token prompt (positions 0..511) through one
+    27B-shaped int4 layer.  For sampled tokens t the oracle decodes token t
+    against the GPU's cache slots 0..t-1 (the slots from t on poisoned): the
+    output row to the float bar and the K/V it appends at slot t within one
+    bf16 rounding step of the GPU's slot t.  Slots past the prompt untouched."""
+    shape = synth.SHAPES["27b"].with_(n_layers=1)
+    n = 512
+    cap = n + 16
+    _print_case("prefill 27b layer full size", n, "tokens")
+    L = _FullLayer(shape, 9, 0, "int4", 1, cap)
+    k0, v0 = L.caches()
+    x = G.make_x_gpu(shape, 10, n)
+    cfg = config_of(shape)
+    ws = torch.zeros(B.prefill_workspace_size(cfg, n), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    out = torch.full_like(x, float("nan"))
+    B.prefill(cfg, [L.layer], n, x, out, [L.kv], 0, ws)
+    torch.cuda.synchronize()
+    assert B.read_device_status(ws) == 0
+    kc, vc = L.caches()
+    got = out.cpu().numpy()
+    xh = x.cpu().numpy().astype(np.float64)
+    assert np.array_equal(kc[:, :, n:], k0[:, :, n:]) and np.array_equal(vc[:, :, n:], v0[:, :, n:])
+    # expand the layer's matrices once for all sampled tokens (same values)
+    monkeypatch.setattr(oracle.decode, "_DENSE_MEMO_ELEMS", 1 << 27)
+    monkeypatch.setattr(oracle.decode, "_DENSE_MEMO", [])
+    t0 = time.time()
+    for t in (0, 1, 63, 64, 255, 300, 511):
+        kt, vt = kc.copy(), vc.copy()
+        kt[:, :, t:] = 0x7FC0
+        vt[:, :, t:] = 0x7FC0
+        r = oracle.decode_layer(shape, L.host, xh[t:t + 1], kt, vt, [t])
+        assert_close(got[t], r["z"][0], what=f"prefill token {t}")
+        _check_slots(kc, vc, r["k_cache"], r["v_cache"], kc, vc, [t], f"prefill token {t}")
+    print(f"oracle {time.time() - t0:.1f} s", flush=True)

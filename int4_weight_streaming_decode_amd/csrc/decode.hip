@@ -1158,17 +1158,20 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
 }
 
 // ---------------------------------------------------------------- prompt prefill
-// GEMM kernels of the prefill path (prefill.h), one per epilogue.
-__global__ void __launch_bounds__(PF_NT) k_pf_rows(PfTask g, float* y, const float* resid) {
+// GEMM kernels of the prefill path (prefill.h), one per epilogue.  The
+// wide-tile ones are built for the waves per SIMD their tile size runs at.
+__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(PF_BM_WIDE == 128 ? 1 : 2, PF_BM_WIDE == 128 ? 1 : 2)))
+k_pf_rows(PfTask g, float* y, const float* resid) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     EpiRows<false> ep{y, resid, g.t.a.n, g.ntok};
-    pf_gemm<KIND_ADJ, 1>(g, lds, ep);
+    pf_gemm<KIND_ADJ, 1, PF_BM_WIDE>(g, lds, ep);
 }
 
-__global__ void __launch_bounds__(PF_NT) k_pf_swiglu(PfTask g, float* act) {
+__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(PF_BM_WIDE == 128 ? 1 : 2, PF_BM_WIDE == 128 ? 1 : 2)))
+k_pf_swiglu(PfTask g, float* act) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     EpiSwiGLU<false> ep{act, g.t.a.n, g.ntok};
-    pf_gemm<KIND_TWO, 1>(g, lds, ep);
+    pf_gemm<KIND_TWO, 1, PF_BM_WIDE>(g, lds, ep);
 }
 
 // q (fp32, RoPE applied) to its buffer, bf16 k/v appended at each token's slot
@@ -1176,19 +1179,19 @@ __global__ void __launch_bounds__(PF_NT) k_pf_qkv(PfTask g, float* q, uint16_t* 
                                                   const float2* cs, int cap, int hq, int hkv, KvMap pgm, int* status) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     EpiQKV<false> ep{q, kc, vc, nullptr, posv, cs, cap, hq, hkv, g.t.head_dim, g.ntok, 0, pgm, status};
-    pf_gemm<KIND_QKV, 2>(g, lds, ep);
+    pf_gemm<KIND_QKV, 2, PF_BM_QKV>(g, lds, ep);
 }
 
 // Tiles of one prefill GEMM; the K axis is split (adjacent-row tasks only)
 // while the tiles fill fewer than two workgroups per compute unit, keeping at
 // least 8 steps per split.
 struct PfPlan { int mtiles, ntiles, ks, spk, nsteps, nwg; };
-PfPlan pf_plan(int total_pairs, int K, int ntok, bool split) {
+PfPlan pf_plan(int total_pairs, int K, int ntok, bool split, int bm) {
     PfPlan p;
-    p.mtiles = (ntok + PF_BM - 1) / PF_BM;
+    p.mtiles = (ntok + bm - 1) / bm;
     p.ntiles = (total_pairs + PF_PAIRS - 1) / PF_PAIRS;
     p.nsteps = K / 128;
-    const int slots = 2 * num_cus();
+    const int slots = (bm == 128 ? 1 : 2) * num_cus();   // resident workgroups per CU
     const int base = p.mtiles * p.ntiles;
     int ks = 1;
     if (split && base < slots) ks = std::max(1, std::min(slots / base, p.nsteps / 8));
@@ -1205,7 +1208,7 @@ PfPlan pf_plan(int total_pairs, int K, int ntok, bool split) {
 // the split-K partial sums.
 struct PfWs { size_t xs, xsc, posv, pos, cs, q, o, y, act, xa, xb, part, total; };
 PfWs pf_ws(const i4d_config* c, int T) {
-    const size_t sp = (size_t)(T + PF_BM - 1) / PF_BM * PF_BM;
+    const size_t sp = (size_t)(T + PF_BM_MAX - 1) / PF_BM_MAX * PF_BM_MAX;
     const size_t D = c->d_model, qw = (size_t)c->n_q_heads * c->head_dim, F = c->d_ff;
     const size_t kmax = std::max(std::max(D, qw), F);
     PfWs w;
@@ -1224,7 +1227,7 @@ PfWs pf_ws(const i4d_config* c, int T) {
     w.xb = take((size_t)T * D * 4);
     size_t part = 0;
     for (int kk = 0; kk < 2; ++kk) {          // the two adjacent-row GEMMs (Wo: K = qw, down: K = F), N = D
-        const PfPlan pp = pf_plan((int)((D + 1) / 2), kk == 0 ? (int)qw : (int)F, T, true);
+        const PfPlan pp = pf_plan((int)((D + 1) / 2), kk == 0 ? (int)qw : (int)F, T, true, PF_BM_WIDE);
         if (pp.ks > 1) part = std::max(part, (size_t)pp.ks * T * D * 4);
     }
     w.part = take(part);
@@ -1239,7 +1242,7 @@ PfTask pf_task(const GemvTask& t, const PfPlan& p, char* ws, const PfWs& W, int 
     g.xs = (const uint32_t*)(ws + W.xs);
     g.xscale = (const float*)(ws + W.xsc);
     g.part = (float*)(ws + W.part);
-    g.sp = (T + PF_BM - 1) / PF_BM * PF_BM;
+    g.sp = (T + PF_BM_MAX - 1) / PF_BM_MAX * PF_BM_MAX;
     g.ntok = T;
     g.nsteps = p.nsteps;
     g.gshift = ilog2(group) - 7;
@@ -1259,7 +1262,7 @@ int launch_pf(Kern kernel, size_t lds, const PfPlan& p, hipStream_t s, A... args
 // Adjacent-row GEMM + residual, with the split-K reduction when planned.
 int pf_rows(const PfTask& g, const PfPlan& p, float* y, const float* resid, hipStream_t s) {
     int rc;
-    if ((rc = launch_pf(k_pf_rows, pf_lds_bytes<1>(), p, s, g, y, resid))) return rc;
+    if ((rc = launch_pf(k_pf_rows, pf_lds_bytes<1, PF_BM_WIDE>(), p, s, g, y, resid))) return rc;
     if (p.ks == 1) return I4D_OK;
     if ((rc = scratch_free(k_pf_reduce))) return rc;
     const size_t n = (size_t)g.ntok * g.rows;
@@ -1272,7 +1275,7 @@ int pf_rows(const PfTask& g, const PfPlan& p, float* y, const float* resid, hipS
 // workgroup per staged row; rows past T are zero-filled).
 int pf_stage(int prec, const float* x, int stride, int T, int K, const uint16_t* gain, float eps, char* ws, const PfWs& W,
              int max_pos, int cap, int hd, double rope_base, bool rope, hipStream_t s) {
-    const int sp = (T + PF_BM - 1) / PF_BM * PF_BM;
+    const int sp = (T + PF_BM_MAX - 1) / PF_BM_MAX * PF_BM_MAX;
     uint32_t* xs = (uint32_t*)(ws + W.xs);
     int* status = (int*)(ws + WS_STATUS);
     const int* pos = rope ? (const int*)(ws + W.pos) : nullptr;
@@ -1304,10 +1307,10 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
     if ((rc = pf_stage(2, x_in, D, T, D, L->attn_norm, c->rms_eps, ws, W, max_pos, kv->capacity, hd, c->rope_base, true, s)))
         return rc;
     const GemvTask tq = make_task(KIND_QKV, &L->wq, &L->wk, &L->wv, hd);
-    const PfPlan pq = pf_plan(tq.total_pairs, D, T, false);
+    const PfPlan pq = pf_plan(tq.total_pairs, D, T, false, PF_BM_QKV);
     {
         TimeScope ts(I4D_TIME_QKV);
-        rc = launch_pf(k_pf_qkv, pf_lds_bytes<2>(), pq, s, pf_task(tq, pq, ws, W, T, g, 0), q, kv->k, kv->v,
+        rc = launch_pf(k_pf_qkv, pf_lds_bytes<2, PF_BM_QKV>(), pq, s, pf_task(tq, pq, ws, W, T, g, 0), q, kv->k, kv->v,
                        (const int*)(ws + W.posv), (const float2*)(ws + W.cs), kv->capacity, c->n_q_heads, c->n_kv_heads,
                        kv_map(kv), status);
     }
@@ -1330,7 +1333,7 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
 
     if ((rc = pf_stage(1, o, qw, T, qw, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
     const GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
-    const PfPlan po = pf_plan(to.total_pairs, qw, T, true);
+    const PfPlan po = pf_plan(to.total_pairs, qw, T, true, PF_BM_WIDE);
     {
         TimeScope ts(I4D_TIME_WO);
         rc = pf_rows(pf_task(to, po, ws, W, T, g, D), po, y, x_in, s);
@@ -1339,16 +1342,16 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
 
     if ((rc = pf_stage(1, y, D, T, D, L->ffn_norm, c->rms_eps, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
     const GemvTask tg = make_task(KIND_TWO, &L->wg, &L->wu, nullptr, hd);
-    const PfPlan pg = pf_plan(tg.total_pairs, D, T, false);
+    const PfPlan pg = pf_plan(tg.total_pairs, D, T, false, PF_BM_WIDE);
     {
         TimeScope ts(I4D_TIME_GATE_UP);
-        rc = launch_pf(k_pf_swiglu, pf_lds_bytes<1>(), pg, s, pf_task(tg, pg, ws, W, T, g, 0), act);
+        rc = launch_pf(k_pf_swiglu, pf_lds_bytes<1, PF_BM_WIDE>(), pg, s, pf_task(tg, pg, ws, W, T, g, 0), act);
     }
     if (rc) return rc;
 
     if ((rc = pf_stage(1, act, F, T, F, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
     const GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
-    const PfPlan pd = pf_plan(td.total_pairs, F, T, true);
+    const PfPlan pd = pf_plan(td.total_pairs, F, T, true, PF_BM_WIDE);
     TimeScope ts(I4D_TIME_DOWN);
     return pf_rows(pf_task(td, pd, ws, W, T, g, D), pd, x_out, y, s);
 }

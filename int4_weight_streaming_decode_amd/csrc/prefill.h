@@ -15,10 +15,13 @@
 // inputs pre-divided by 16, one power of two per token for fp16 range), so
 // the integer unpack and the group-scale handling are the ones of that path.
 //
-// Tile.  A workgroup (4 waves) owns 64 tokens x 256 weight rows; each wave
+// Tile.  A workgroup (4 waves) owns BM tokens x 256 weight rows; each wave
 // owns 4 row tiles of 16 (the pair mapping of the decode kernels: lanes r and
-// r ^ 8 of a tile hold the two rows of a pair) for all 64 tokens, i.e. 16
-// accumulator tiles.  The K axis is walked in steps of 128 inputs (one group
+// r ^ 8 of a tile hold the two rows of a pair) for all BM tokens, i.e. 4 BM / 16
+// accumulator tiles.  BM = 64, two waves per SIMD (the kernels are built
+// for that register budget).  BM = 128 at one wave per SIMD, where each
+// expanded weight feeds twice the MFMAs, measured slower: the second wave's
+// latency hiding is worth more than the halved expansion.  The K axis is walked in steps of 128 inputs (one group
 // of 128 or half a group of 256): per step a wave expands its 4 x 64 bytes of
 // codes per lane-row into B operands once and runs 4 (tokens) x 4 (rows) x 4
 // (32-input slices) MFMAs per activation plane; each (token tile, row tile)
@@ -57,19 +60,25 @@
 #include "mfma.h"
 
 constexpr int PF_NT = 256;                          // threads per GEMM workgroup
-constexpr int PF_BM = 64;                           // tokens per workgroup tile
+#ifndef I4D_PF_BM_WIDE
+#define I4D_PF_BM_WIDE 64
+#endif
+constexpr int PF_BM_MAX = 128;                      // staged rows are padded to a multiple of this
+constexpr int PF_BM_QKV = 64;                       // tokens per workgroup tile: q/k/v (two activation planes)
+constexpr int PF_BM_WIDE = I4D_PF_BM_WIDE;          // the other projections
 constexpr int PF_WT = 4;                            // 16-row tiles per wave
 constexpr int PF_BN = (PF_NT / 64) * PF_WT * 16;    // weight rows per workgroup (256)
 constexpr int PF_PAIRS = PF_BN / 2;                 // pairs per workgroup
-constexpr int PF_PLANE_B = PF_BM * 256;             // one step of one activation plane in LDS
-template <int PREC> __host__ __device__ constexpr int pf_lds_bytes() { return 2 * PREC * PF_PLANE_B; }
+// one step of one activation plane in LDS, and the two buffers of all planes
+template <int BM> __host__ __device__ constexpr int pf_plane_bytes() { return BM * 256; }
+template <int PREC, int BM> __host__ __device__ constexpr int pf_lds_bytes() { return 2 * PREC * pf_plane_bytes<BM>(); }
 
 struct PfTask {
     GemvTask t;              // matrices and pair mapping (int4, groups of 128 or 256)
     const uint32_t* xs;      // staged activations [PREC][sp][K/2] (uint32 = two fp16)
     const float* xscale;     // [sp] power of two that multiplies token t's results
     float* part;             // K split: partial sums [ks][ntok][rows]
-    int sp;                  // staged rows per plane (tokens rounded up to 64)
+    int sp;                  // staged rows per plane (tokens rounded up to PF_BM_MAX)
     int ntok;                // prompt tokens
     int nsteps;              // K / 128
     int gshift;              // log2(group / 128)
@@ -97,12 +106,14 @@ typedef __attribute__((address_space(3))) void* lds_vptr;
 // this wave, then the workgroup barrier
 I4D_DEVINL void pf_sync() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int KND, int PREC, class Epi>
+// BM tokens per workgroup tile (BM / 16 token tiles per wave)
+template <int KND, int PREC, int BM, class Epi>
 I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
+    constexpr int MT = BM / 16, RPW = BM / (PF_NT / 64), PLANE_B = pf_plane_bytes<BM>();
     int mt, nt, kss;
     pf_tile(g, mt, nt, kss);
     const int tid = i4d_tid(), wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
-    const int tok0 = mt * PF_BM;
+    const int tok0 = mt * BM;
     const int s0 = kss * g.spk, s1 = min(g.nsteps, s0 + g.spk);
     const size_t K2 = (size_t)(g.t.k >> 1);           // uint32 per staged row
 
@@ -118,18 +129,18 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
         sp[i] = r < 8 ? rp.sa : rp.sb;
     }
 
-    // step s of the 64 token rows into LDS buffer b: wave w fills rows
-    // 16 w .. 16 w + 15, four rows (1 KB) per instruction; lane l writes piece
-    // l & 15 of its row, which holds the row's piece (l & 15) ^ (row & 15)
+    // step s of the BM token rows into LDS buffer b: wave w fills rows
+    // RPW w .. RPW w + RPW - 1, four rows (1 KB) per instruction; lane l writes
+    // piece l & 15 of its row, which holds the row's piece (l & 15) ^ (row & 15)
     auto load_a = [&](int b, int s) {
 #pragma unroll
         for (int p = 0; p < PREC; ++p)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RPW / 4; ++i) {
                 const int rl = 4 * i + (lane >> 4);
-                const uint32_t* src = g.xs + ((size_t)p * g.sp + tok0 + 16 * wave + rl) * K2 + (size_t)s * 64 +
-                                      (((lane & 15) ^ rl) << 2);
-                char* dst = lds + (b * PREC + p) * PF_PLANE_B + (16 * wave + 4 * i) * 256;
+                const uint32_t* src = g.xs + ((size_t)p * g.sp + tok0 + RPW * wave + rl) * K2 + (size_t)s * 64 +
+                                      (((lane & 15) ^ (rl & 15)) << 2);
+                char* dst = lds + (b * PREC + p) * PLANE_B + (RPW * wave + 4 * i) * 256;
                 __builtin_amdgcn_global_load_lds((const I4D_GLOBAL void*)src, (lds_vptr)dst, 16, 0, 0);
             }
     };
@@ -143,9 +154,9 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
         }
     };
 
-    f4 acc[4][PF_WT];
+    f4 acc[MT][PF_WT];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < PF_WT; ++i) acc[m][i] = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -169,9 +180,9 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
             load_a(b ^ 1, s + 1);
             load_w(s + 1);
         }
-        const char* ab = lds + b * PREC * PF_PLANE_B;
+        const char* ab = lds + b * PREC * PLANE_B;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < MT; ++m) {
             f4 cg[PF_WT];
 #pragma unroll
             for (int i = 0; i < PF_WT; ++i) cg[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -179,7 +190,7 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int p = 0; p < PREC; ++p) {
-                    const h8 a = *(const h8*)(ab + p * PF_PLANE_B + (16 * m + r) * 256 + (((4 * q + j) ^ r) << 4));
+                    const h8 a = *(const h8*)(ab + p * PLANE_B + (16 * m + r) * 256 + (((4 * q + j) ^ r) << 4));
 #pragma unroll
                     for (int i = 0; i < PF_WT; ++i) cg[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[i][j], cg[i], 0, 0, 0);
                 }
@@ -201,7 +212,7 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
         for (int i = 0; i < PF_WT; ++i) {
             const int pair = 8 * (nt * (PF_BN / 16) + wave * PF_WT + i) + r;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float v = acc[m][i][e];
@@ -219,7 +230,7 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
         for (int i = 0; i < PF_WT; ++i) {
             const int row = 2 * (8 * (nt * (PF_BN / 16) + wave * PF_WT + i) + (r & 7)) + (r >> 3);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = tok0 + 16 * m + 4 * q + e;

@@ -225,3 +225,43 @@ def test_paged_prefill_on_the_matrix_cores_equals_contiguous(n_tokens):
         r = oracle.decode_stack(shape, layers, x[t:t + 1].astype(np.float64), caches, [int(pos[t])])
         caches = r["caches"]
         assert_close(res[1][0][t], r["z"][0], what=f"paged prefill token {t}")
+
+
+@pytest.mark.parametrize("n_tokens,pos0,P", [(200, 40, 32), (333, 0, 64)])
+def test_paged_whole_prompt_prefill_equals_contiguous(n_tokens, pos0, P):
+    """i4d_prefill (GEMMs over the prompt, causal prompt attention) on a paged
+    cache: outputs and caches bit-identical to the contiguous call, outputs to
+    the oracle's bar, and unused pages untouched."""
+    shape = SHAPE
+    cap = ((pos0 + n_tokens + P - 1) // P + 1) * P
+    _print_case("paged whole-prompt prefill", n_tokens, pos0, P)
+    layers = [synth.make_layer(shape, 97, l) for l in range(2)]
+    caches = [synth.make_kv(shape, 97, l, 1, [pos0], cap) for l in range(2)]
+    x = np.stack([synth.make_x(shape, 97, 1, step=t)[0] for t in range(n_tokens)])
+    Ls = [DevLayer(l) for l in layers]
+    cfg = config_of(shape)
+    res = []
+    for paged in (False, True):
+        kvs = [DevPagedKV(kc, vc, P, seed=n_tokens + l) if paged else DevKV(kc, vc) for l, (kc, vc) in enumerate(caches)]
+        before = [k.pools() for k in kvs] if paged else None
+        ws = torch.zeros(B.prefill_workspace_size(cfg, n_tokens), dtype=torch.uint8, device="cuda")
+        B.workspace_init(ws)
+        out = torch.empty((n_tokens, shape.d_model), dtype=torch.float32, device="cuda")
+        B.prefill(cfg, [l.layer for l in Ls], n_tokens, dev(x), out, [k.kv for k in kvs], pos0, ws)
+        torch.cuda.synchronize()
+        assert B.read_device_status(ws) == 0
+        res.append((out.cpu().numpy(), [k.gather() if paged else k.host() for k in kvs]))
+        if paged:
+            for k, (kb, vb) in zip(kvs, before):
+                used = set(k.table.ravel().tolist())
+                ka, va = k.pools()
+                for pg in range(k.n_pages):
+                    if pg not in used:
+                        assert np.array_equal(ka[pg], kb[pg]) and np.array_equal(va[pg], vb[pg]), f"unused page {pg}"
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32)), "paged prefill output differs"
+    for l in range(2):
+        for c in range(2):
+            assert np.array_equal(res[0][1][l][c], res[1][1][l][c]), f"layer {l} cache {c} differs"
+    ref = oracle.prefill(shape, layers, x.astype(np.float64), caches, pos0)
+    for t in range(0, n_tokens, 37):
+        assert_close(res[1][0][t], ref["z"][t], what=f"paged prefill token {t}")

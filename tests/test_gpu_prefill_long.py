@@ -60,7 +60,7 @@ def check(shape, n_tokens, pos0):
             assert np.array_equal(g_[0][:, mask], c0[0][:, mask]), f"layer {l} {name}: other slots changed"
 
 
-@pytest.mark.parametrize("n_tokens,pos0", [(128, 0), (512, 0), (77, 40), (1, 63), (200, 300)])
+@pytest.mark.parametrize("n_tokens,pos0", [(128, 0), (512, 0), (77, 40), (1, 63), (200, 300), (2048, 5)])
 def test_prefill_equals_sequential_decode(n_tokens, pos0):
     check(SHAPE_A, n_tokens, pos0)
 

@@ -42,9 +42,9 @@
 // into sum (c - 8) a (exact in int32), converted once, and scaled by the
 // group scale times the run's power of two.  The only rounding is that of the
 // activations to 15 significant bits relative to their run's maximum (23 bits
-// and six digit planes for the q/k/v projection, whose k and v are rounded to
-// bf16 into the cache), and no activation can overflow (the power of two
-// adapts to any finite value).
+// and six digit planes for the k and v rows, which are rounded to bf16 into
+// the cache), and no activation can overflow (the power of two adapts to any
+// finite value).
 // About 0.85 VALU operations per weight.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -1015,7 +1015,10 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
         const KGeo& k = kg[kind];
         {
             const int K = k.K, ngr = K / 8;
-            const bool six = kind == K_QKV;
+            // six digit planes (23 bits) for the k and v rows, which are rounded to
+            // bf16 into the cache; four (15 bits) for q, which attention splits into
+            // bf16 high and low parts (16 bits) anyway, and for the other phases
+            const bool six = kind == K_QKV && kg[K_QKV].mat != 0;
             // normalised inputs (x, y: K = D <= 8192, RMN rounds of groups): RMSNorm, then digits
             // the gain words of this thread's groups, loaded before the exchange
             // fetch so that their latency hides under it
@@ -1101,7 +1104,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
             int seg = s.seg0, run = 0;
             unsigned aoff = (unsigned)seg * 256u + (unsigned)lane16 * 16u;
             const int hs = ((lane16 >> 2) & 1) ? 0 : 16;
-            const bool six = kind == K_QKV;
+            const bool six = kind == K_QKV && k.mat != 0;
             // this wave's place in the ring: its loader's half, its 2 KB of codes, its slots' scale words
             const int lw = wave / CPL, cw = wave - CPL * lw;
             const char* half = lds + A.off_ring + (size_t)lw * A.nb * HSTEP;
@@ -1308,7 +1311,8 @@ void lds_plan(const i4d_config* c, int n_layers, Plan& P) {
 // q/k/v rows go to compute units in proportion: [0, cq) q, [cq, ck) k, [ck, nwg) v.
 void qkv_split(const i4d_config* c, int nwg, int& cq, int& ck) {
     const int npq = c->n_q_heads * HD / 2, npk = c->n_kv_heads * HD / 2;
-    int nq = (int)((long long)nwg * npq / (npq + 2 * npk));
+    // q rows cost about 10 units per step, k and v rows 14 (six digit planes against four)
+    int nq = (int)((long long)nwg * npq * 10 / (npq * 10 + 2 * npk * 14));
     nq = std::min(std::max(nq, 1), nwg - 2);
     const int nk = std::max(1, (nwg - nq) / 2);
     cq = nq;

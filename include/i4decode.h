@@ -375,12 +375,16 @@ int i4d_read_device_status(const void* ws, int32_t* status_out, void* stream);
  * one user at a time: calls from several host threads race.  start() while
  * timing is on restarts it.  I4D_EINVAL for an unknown kernel or a bad
  * count, I4D_EHIP if an event cannot be made or read.                      */
-#define I4D_TIME_QKV        1   /* k_gemv_qkv: norm + QKV projection + RoPE + KV append */
-#define I4D_TIME_ATTENTION  2   /* k_attention: split-K decode attention with its merge */
-#define I4D_TIME_WO         3   /* k_gemv_rows on Wo (+ residual) */
-#define I4D_TIME_GATE_UP    4   /* k_gemv_swiglu: norm + gate/up projections + SwiGLU */
-#define I4D_TIME_DOWN       5   /* k_gemv_rows on W_down (+ residual) */
-#define I4D_TIME_LM_HEAD    6   /* k_lm_head: one chunk of the LM head's rows */
+/* Each kind names one phase of a layer; the kernel timed is the one that
+ * phase runs on the path taken (phase launches, the batched matrix-core path,
+ * or i4d_prefill's GEMMs and prompt attention).                            */
+#define I4D_TIME_QKV        1   /* k_gemv_qkv / k_mfma_qkv / k_pf_qkv: QKV projection + RoPE + KV append */
+#define I4D_TIME_ATTENTION  2   /* k_attention (split-K decode attention with its merge) / k_pf_attn */
+#define I4D_TIME_WO         3   /* k_gemv_rows / k_mfma_rows / k_pf_rows on Wo (+ residual) */
+#define I4D_TIME_GATE_UP    4   /* k_gemv_swiglu / k_mfma_swiglu / k_pf_swiglu: gate/up + SwiGLU */
+#define I4D_TIME_DOWN       5   /* k_gemv_rows / k_mfma_rows / k_pf_rows on W_down (+ residual) */
+#define I4D_TIME_LM_HEAD    6   /* k_lm_head / k_mfma_lm (one chunk of the LM head's rows), or the
+                                   logits GEMV of top-k sampling */
 #define I4D_TIME_STREAM     7   /* k_stream_decode: every layer of one call (events around the launch) */
 int i4d_launch_timing_start(int32_t kernel, int32_t max_launches);
 int i4d_launch_timing_stop(float* total_ms, int32_t* launches);

@@ -165,3 +165,51 @@ def test_bad_token_sets_status_and_gives_a_zero_row():
     assert np.array_equal(xh[0], synth.bf16_value(table[99]))
     assert not xh[1].any()
     assert B.read_device_status(ws) & B.I4D_DEV_BAD_TOKEN
+
+
+def test_generation_after_a_prefilled_prompt():
+    """Primer 1.2's two phases in order: a prompt through i4d_prefill, its last
+    row through the LM head for the first new token, then greedy decode steps
+    at batch 1 (the streaming kernel, reading the cache the prefill wrote).
+    The oracle does the same: prefill (token by token), LM head, decode loop."""
+    n_layers, n, steps = 2, 150, 4
+    cap = 176
+    _print_case("generation after prefill", n, steps)
+    layers = [synth.make_layer(SHAPE, 61, l) for l in range(n_layers)]
+    caches = [synth.make_kv(SHAPE, 61, l, 1, [0], cap) for l in range(n_layers)]   # no history; slots poisoned
+    table = synth.make_embedding(VOCAB, SHAPE.d_model, 61)
+    lm = synth.make_lm_head(VOCAB, SHAPE.d_model, SHAPE.group, 62)
+    prompt = np.random.default_rng(61).integers(0, VOCAB, size=n)
+    x = synth.bf16_value(table[prompt]).astype(np.float32)          # the prompt's embedding rows
+    Ls = [DevLayer(l) for l in layers]
+    kvs = [DevKV(*c) for c in caches]
+    W, emb = DevMat(lm), dev(table)
+    cfg = config_of(SHAPE)
+    wsp = torch.zeros(B.prefill_workspace_size(cfg, n), dtype=torch.uint8, device="cuda")
+    B.workspace_init(wsp)
+    out = torch.empty((n, SHAPE.d_model), dtype=torch.float32, device="cuda")
+    B.prefill(cfg, [l.layer for l in Ls], n, dev(x), out, [k.kv for k in kvs], 0, wsp)
+    ws = workspace(cfg, 1, cap - 1, vocab=VOCAB, n_layers=n_layers)
+    tokens = torch.empty(1, dtype=torch.int32, device="cuda")
+    mx = torch.empty(1, dtype=torch.float32, device="cuda")
+    B.lm_head_chunked(W.mat, 1, out[n - 1:n].contiguous(), 8192, tokens, mx, ws)
+    torch.cuda.synchronize()
+    assert B.read_device_status(wsp) == 0
+    got = [(tokens.cpu().numpy().copy(), mx.cpu().numpy().copy())]
+    pos = dev(np.array([n], dtype=np.int32))
+    xbuf = torch.empty((2, 1, SHAPE.d_model), dtype=torch.float32, device="cuda")
+    for s in range(steps):
+        B.decode_step(cfg, [l.layer for l in Ls], emb, W.mat, 1, tokens, mx, pos, n + s, xbuf, [k.kv for k in kvs], ws)
+        torch.cuda.synchronize()
+        got.append((tokens.cpu().numpy().copy(), mx.cpu().numpy().copy()))
+    assert B.read_device_status(ws) == 0
+
+    ref = oracle.prefill(SHAPE, layers, x.astype(np.float64), caches, 0)
+    assert_close(out.cpu().numpy(), ref["z"], what="prefill outputs")
+    t0, m0, lg0 = oracle.lm_head_argmax(lm, ref["z"][n - 1:n])
+    _check_tokens(got[0][0], t0, lg0, "first token")
+    assert_close(got[0][1], m0, what="first token max logit")
+    r = oracle.greedy_decode(SHAPE, layers, table, lm, t0, ref["caches"], [n], steps)
+    for s in range(steps):
+        _check_tokens(got[s + 1][0], r["tokens"][s], r["logits"][s], f"step {s}")
+        assert_close(got[s + 1][1], r["max_logit"][s], what=f"step {s} max logit")

@@ -1160,11 +1160,11 @@ int run_layer_mfma(const i4d_config* c, const i4d_layer* L, int B, const float* 
 // ---------------------------------------------------------------- prompt prefill
 // GEMM kernels of the prefill path (prefill.h), one per epilogue.  The
 // wide-tile ones are built for the waves per SIMD their tile size runs at.
-__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(PF_BM_WIDE == 128 ? 1 : 2, PF_BM_WIDE == 128 ? 1 : 2)))
+__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(PF_BM_ROWS == 128 ? 1 : 2, PF_BM_ROWS == 128 ? 1 : 2)))
 k_pf_rows(PfTask g, float* y, const float* resid) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     EpiRows<false> ep{y, resid, g.t.a.n, g.ntok};
-    pf_gemm<KIND_ADJ, 1, PF_BM_WIDE>(g, lds, ep);
+    pf_gemm<KIND_ADJ, 1, PF_BM_ROWS>(g, lds, ep);
 }
 
 __global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(PF_BM_WIDE == 128 ? 1 : 2, PF_BM_WIDE == 128 ? 1 : 2)))
@@ -1227,7 +1227,7 @@ PfWs pf_ws(const i4d_config* c, int T) {
     w.xb = take((size_t)T * D * 4);
     size_t part = 0;
     for (int kk = 0; kk < 2; ++kk) {          // the two adjacent-row GEMMs (Wo: K = qw, down: K = F), N = D
-        const PfPlan pp = pf_plan((int)((D + 1) / 2), kk == 0 ? (int)qw : (int)F, T, true, PF_BM_WIDE);
+        const PfPlan pp = pf_plan((int)((D + 1) / 2), kk == 0 ? (int)qw : (int)F, T, true, PF_BM_ROWS);
         if (pp.ks > 1) part = std::max(part, (size_t)pp.ks * T * D * 4);
     }
     w.part = take(part);
@@ -1262,7 +1262,7 @@ int launch_pf(Kern kernel, size_t lds, const PfPlan& p, hipStream_t s, A... args
 // Adjacent-row GEMM + residual, with the split-K reduction when planned.
 int pf_rows(const PfTask& g, const PfPlan& p, float* y, const float* resid, hipStream_t s) {
     int rc;
-    if ((rc = launch_pf(k_pf_rows, pf_lds_bytes<1, PF_BM_WIDE>(), p, s, g, y, resid))) return rc;
+    if ((rc = launch_pf(k_pf_rows, pf_lds_bytes<1, PF_BM_ROWS>(), p, s, g, y, resid))) return rc;
     if (p.ks == 1) return I4D_OK;
     if ((rc = scratch_free(k_pf_reduce))) return rc;
     const size_t n = (size_t)g.ntok * g.rows;
@@ -1333,7 +1333,7 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
 
     if ((rc = pf_stage(1, o, qw, T, qw, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
     const GemvTask to = make_task(KIND_ADJ, &L->wo, nullptr, nullptr, hd);
-    const PfPlan po = pf_plan(to.total_pairs, qw, T, true, PF_BM_WIDE);
+    const PfPlan po = pf_plan(to.total_pairs, qw, T, true, PF_BM_ROWS);
     {
         TimeScope ts(I4D_TIME_WO);
         rc = pf_rows(pf_task(to, po, ws, W, T, g, D), po, y, x_in, s);
@@ -1351,7 +1351,7 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
 
     if ((rc = pf_stage(1, act, F, T, F, nullptr, 0.f, ws, W, 0, 0, hd, 0.0, false, s))) return rc;
     const GemvTask td = make_task(KIND_ADJ, &L->wd, nullptr, nullptr, hd);
-    const PfPlan pd = pf_plan(td.total_pairs, F, T, true, PF_BM_WIDE);
+    const PfPlan pd = pf_plan(td.total_pairs, F, T, true, PF_BM_ROWS);
     TimeScope ts(I4D_TIME_DOWN);
     return pf_rows(pf_task(td, pd, ws, W, T, g, D), pd, x_out, y, s);
 }

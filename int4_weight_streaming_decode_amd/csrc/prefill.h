@@ -65,7 +65,11 @@ constexpr int PF_NT = 256;                          // threads per GEMM workgrou
 #endif
 constexpr int PF_BM_MAX = 128;                      // staged rows are padded to a multiple of this
 constexpr int PF_BM_QKV = 64;                       // tokens per workgroup tile: q/k/v (two activation planes)
-constexpr int PF_BM_WIDE = I4D_PF_BM_WIDE;          // the other projections
+constexpr int PF_BM_WIDE = I4D_PF_BM_WIDE;          // gate/up
+#ifndef I4D_PF_BM_ROWS
+#define I4D_PF_BM_ROWS 64
+#endif
+constexpr int PF_BM_ROWS = I4D_PF_BM_ROWS;          // Wo and W_down (adjacent-row GEMMs + residual)
 constexpr int PF_WT = 4;                            // 16-row tiles per wave
 constexpr int PF_BN = (PF_NT / 64) * PF_WT * 16;    // weight rows per workgroup (256)
 constexpr int PF_PAIRS = PF_BN / 2;                 // pairs per workgroup
@@ -138,8 +142,9 @@ I4D_DEVINL void pf_gemm(const PfTask& g, char* lds, Epi& epi) {
 #pragma unroll
             for (int i = 0; i < RPW / 4; ++i) {
                 const int rl = 4 * i + (lane >> 4);
-                const uint32_t* src = g.xs + ((size_t)p * g.sp + tok0 + RPW * wave + rl) * K2 + (size_t)s * 64 +
-                                      (((lane & 15) ^ (rl & 15)) << 2);
+                const int row = RPW * wave + rl;               // the read side swizzles by row & 15
+                const uint32_t* src = g.xs + ((size_t)p * g.sp + tok0 + row) * K2 + (size_t)s * 64 +
+                                      (((lane & 15) ^ (row & 15)) << 2);
                 char* dst = lds + (b * PREC + p) * PLANE_B + (RPW * wave + 4 * i) * 256;
                 __builtin_amdgcn_global_load_lds((const I4D_GLOBAL void*)src, (lds_vptr)dst, 16, 0, 0);
             }

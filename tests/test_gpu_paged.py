@@ -265,3 +265,36 @@ def test_paged_whole_prompt_prefill_equals_contiguous(n_tokens, pos0, P):
     ref = oracle.prefill(shape, layers, x.astype(np.float64), caches, pos0)
     for t in range(0, n_tokens, 37):
         assert_close(res[1][0][t], ref["z"][t], what=f"paged prefill token {t}")
+
+
+def test_prefill_with_a_page_id_outside_the_pool():
+    """A prompt prefill whose table points one page past the pool: the GEMM
+    epilogue drops the appends into that page, the prompt attention reads page
+    0 in its place (so the outputs are not meaningful), the status word
+    reports it, and no page changes except at the slots the prompt appends
+    into valid pages."""
+    shape, P, n, pos0 = SHAPE, 32, 80, 20
+    cap = 128
+    _print_case("paged prefill bad page id", n, pos0, P)
+    layer = synth.make_layer(shape, 91, 0)
+    kc, vc = synth.make_kv(shape, 91, 0, 1, [pos0], cap)
+    kvd = DevPagedKV(kc, vc, P, seed=19)
+    table = kvd.table.copy()
+    bad = 64 // P                                    # logical page 2: slots 64..95, inside the prompt
+    table[0, bad] = kvd.n_pages + 1000
+    kvd.pages.copy_(torch.from_numpy(table).cuda())
+    before = kvd.pools()
+    x = np.stack([synth.make_x(shape, 91, 1, step=t)[0] for t in range(n)])
+    cfg = config_of(shape)
+    ws = torch.zeros(B.prefill_workspace_size(cfg, n), dtype=torch.uint8, device="cuda")
+    B.workspace_init(ws)
+    out = torch.empty((n, shape.d_model), dtype=torch.float32, device="cuda")
+    B.prefill(cfg, [DevLayer(layer).layer], n, dev(x), out, [kvd.kv], pos0, ws)
+    torch.cuda.synchronize()
+    assert B.read_device_status(ws) & B.I4D_DEV_BAD_PAGE      # the outputs are not meaningful then
+    after = kvd.pools()
+    # changed (page, slot) pairs: exactly the prompt's slots that map to valid pages
+    want = sorted((int(kvd.table[0, s // P]), s % P) for s in range(pos0, pos0 + n) if s // P != bad)
+    for a0, a1 in ((before[0], after[0]), (before[1], after[1])):
+        diff = sorted(tuple(int(v) for v in d) for d in np.argwhere(np.any(a0 != a1, axis=(1, 3))))
+        assert diff == want

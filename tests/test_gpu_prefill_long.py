@@ -104,3 +104,48 @@ def test_prefill_in_two_calls_equals_one_call():
     for a, b in zip(one, two):
         for u, v in zip(a.host(), b.host()):
             assert np.array_equal(u, v)
+
+
+def test_prefill_replays_from_a_graph():
+    """i4d_prefill captured in a graph (it enqueues kernels only: no memset, no
+    allocation) and replayed three times, with eager work, a synchronisation
+    and the output poisoned between replays: every replay gives the eager
+    call's outputs and cache, bit for bit."""
+    shape, n, pos0, cap = SHAPE_A, 200, 30, 240
+    print("CASE prefill graph", n, pos0, flush=True)
+    layers = [synth.make_layer(shape, 47, l) for l in range(2)]
+    caches = [synth.make_kv(shape, 47, l, 1, [pos0], cap) for l in range(2)]
+    x = dev(np.stack([synth.make_x(shape, 47, 1, step=t)[0] for t in range(n)]))
+    Ls = [DevLayer(l) for l in layers]
+    cfg = config_of(shape)
+
+    def state():
+        kvs = [DevKV(*c) for c in caches]
+        ws = torch.zeros(B.prefill_workspace_size(cfg, n), dtype=torch.uint8, device="cuda")
+        B.workspace_init(ws)
+        return kvs, ws, torch.empty((n, shape.d_model), dtype=torch.float32, device="cuda")
+
+    kvs, ws, out = state()
+    B.prefill(cfg, [l.layer for l in Ls], n, x, out, [k.kv for k in kvs], pos0, ws)
+    torch.cuda.synchronize()
+    ref_out, ref_kv = out.cpu().numpy(), [k.host() for k in kvs]
+
+    kvs2, ws2, out2 = state()
+    larr, karr = [l.layer for l in Ls], [k.kv for k in kvs2]
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        B.prefill(cfg, larr, n, x, out2, karr, pos0, ws2)
+    torch.cuda.current_stream().wait_stream(gs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1024, device="cuda") * 2).sum().item()      # eager work between replays
+        assert np.array_equal(out2.cpu().numpy().view(np.uint32), ref_out.view(np.uint32)), f"replay {rep}"
+        for a, b in zip([k.host() for k in kvs2], ref_kv):
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"replay {rep}: cache"
+    assert B.read_device_status(ws2) == 0

@@ -254,7 +254,7 @@ def prefill_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights, f16 x f16 -> f32 MFMA GEMM (q/k/v: f16 + f16 remainder); bf16 MFMA attention",
+        "dtype": "int4 weights, f16 x f16 -> f32 MFMA GEMM (k/v rows: f16 + f16 remainder); bf16 MFMA attention",
         "data": "synthetic",
         "config": {"workload": f"{shape.name}-prefill{n}: {shape.n_layers} layers, D={shape.d_model}, "
                                f"{shape.n_q_heads}/{shape.n_kv_heads} heads, head_dim {shape.head_dim}, d_ff {shape.d_ff}, "

@@ -1179,7 +1179,13 @@ __global__ void __launch_bounds__(PF_NT) k_pf_qkv(PfTask g, float* q, uint16_t* 
                                                   const float2* cs, int cap, int hq, int hkv, KvMap pgm, int* status) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     EpiQKV<false> ep{q, kc, vc, nullptr, posv, cs, cap, hq, hkv, g.t.head_dim, g.ntok, 0, pgm, status};
-    pf_gemm<KIND_QKV, 2, PF_BM_QKV>(g, lds, ep);
+    int mt, nt, kss;
+    pf_tile(g, mt, nt, kss);
+    // q rows from the fp16 value plane alone (q enters attention as bf16
+    // high + low parts); k and v rows, rounded to bf16 into the cache, also
+    // take the remainder plane
+    if (nt < g.nlo) pf_gemm<KIND_QKV, 1, PF_BM_QKV>(g, lds, ep);
+    else pf_gemm<KIND_QKV, 2, PF_BM_QKV>(g, lds, ep);
 }
 
 // Tiles of one prefill GEMM; the K axis is split (adjacent-row tasks only)
@@ -1310,7 +1316,9 @@ int run_layer_prefill(const i4d_config* c, const i4d_layer* L, int T, const floa
     const PfPlan pq = pf_plan(tq.total_pairs, D, T, false, PF_BM_QKV);
     {
         TimeScope ts(I4D_TIME_QKV);
-        rc = launch_pf(k_pf_qkv, pf_lds_bytes<2, PF_BM_QKV>(), pq, s, pf_task(tq, pq, ws, W, T, g, 0), q, kv->k, kv->v,
+        PfTask gq = pf_task(tq, pq, ws, W, T, g, 0);
+        gq.nlo = std::min(pq.ntiles, (tq.a.n >> 1) / PF_PAIRS);      // row blocks holding q pairs only
+        rc = launch_pf(k_pf_qkv, pf_lds_bytes<2, PF_BM_QKV>(), pq, s, gq, q, kv->k, kv->v,
                        (const int*)(ws + W.posv), (const float2*)(ws + W.cs), kv->capacity, c->n_q_heads, c->n_kv_heads,
                        kv_map(kv), status);
     }

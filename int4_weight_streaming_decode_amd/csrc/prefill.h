@@ -89,6 +89,7 @@ struct PfTask {
     int mtiles, ntiles;      // token tiles, row blocks
     int ks, spk;             // K splits, steps per split
     int rows;                // output rows of the partial sums (K split)
+    int nlo;                 // row blocks 0 .. nlo - 1 run on the value plane alone (q/k/v: the q rows); 0: none
 };
 
 // Tile of this workgroup: the hardware sends workgroup i to XCD i % 8, so
@@ -100,8 +101,16 @@ I4D_DEVINL void pf_tile(const PfTask& g, int& mt, int& nt, int& kss) {
     const int w = x * per + min(x, rem) + local;
     mt = w % g.mtiles;
     const int rest = w / g.mtiles;
-    nt = rest % g.ntiles;
+    const int u = rest % g.ntiles, N = g.ntiles, nh = N - g.nlo;
     kss = rest / g.ntiles;
+    nt = u;
+    if (g.nlo > 0 && nh > 0) {
+        // one-plane blocks cost about half a two-plane block: deal the nh
+        // two-plane blocks evenly over the block order, each first in its
+        // run, so that every XCD gets its share and starts them first
+        const int c0 = (u * nh + N - 1) / N, c1 = ((u + 1) * nh + N - 1) / N;
+        nt = c0 < c1 ? g.nlo + c0 : u - c0;
+    }
 }
 
 typedef __attribute__((address_space(3))) void* lds_vptr;

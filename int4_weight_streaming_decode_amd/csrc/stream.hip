@@ -157,7 +157,7 @@ constexpr int OFF_RES = OFF_PART + NSLOT * MAXRUN * 8;             // float [4][
 constexpr int OFF_ROPE = OFF_RES + 4 * MAX_RES * 4;                // float2 [HD / 2]
 constexpr int OFF_KG = OFF_ROPE + (HD / 2) * 8;                    // KGeo [4]
 constexpr int OFF_SG = OFF_KG + 4 * (int)sizeof(KGeo);             // SGeo [4][NSLOT]
-constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [2][NCW]
+constexpr int OFF_RED = OFF_SG + 4 * NSLOT * (int)sizeof(SGeo);    // float [NCW] (+ NCW unused)
 constexpr int MAXNP = (MAXRUN - 1) * NSLOT;                        // pairs per unit and phase (runs_of() <= MAXRUN)
 constexpr int OFF_PINFO = OFF_RED + 2 * NCW * 4;                   // u32 [4][MAXNP]: first entry << 8 | count
 constexpr int OFF_PLIST = OFF_PINFO + 4 * MAXNP * 4;               // u8 [4][NSLOT * MAXRUN]: part indices, pair-major
@@ -665,18 +665,14 @@ I4D_DEVINL void digitize8(char* act, int ps, float* cs, int g, float (&v)[8], bo
     if ((i4d_tid() & 3) == 0) cs[g >> 2] = ldexpf(1.f, -sh);
 }
 
-// Sum of one value over the consumer waves (every consumer thread gets it).
-// red holds two sets of NCW slots, used in turn, so one barrier suffices.
-I4D_DEVINL float block_sum(float v, float* red, u32& par, CBar& cb) {
+// This consumer wave's sum of v into red[wave]; the reader waits for a
+// consumer barrier first.  red[] is written by the two normalised stagings of
+// a layer (q/k/v, gate/up) and read by the same phase's epilogue; between a
+// phase's epilogue and the next staging that writes red[] lies at least one
+// consumer barrier that every wave reaches only after its epilogue.
+I4D_DEVINL void wave_share(float v, float* red) {
     for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
-    float* r = red + par * NCW;
-    par ^= 1u;
-    if ((i4d_tid() & 63) == 0) r[i4d_tid() >> 6] = v;
-    cbar(cb);
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < NCW; ++w) t += r[w];
-    return t;
+    if ((i4d_tid() & 63) == 0) red[i4d_tid() >> 6] = v;
 }
 
 // ------------------------------------------------------------------ attention item of a compute unit
@@ -836,7 +832,6 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
     // ---- the consumer waves: every phase of every layer
     Spin sp{A.status, false};
     CBar cb{sync, A.status, 0u};
-    u32 rpar = 0u;                                    // block_sum's set of slots
     const u32 tag = ld_g(A.epoch) + 1u;
     int t = 0, rslot = 0;                             // global step, its ring entry
     u32 rdy = 0u;                                     // steps the loader of this wave's half has written (last seen)
@@ -1026,6 +1021,12 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
 #pragma unroll
                 for (int rr = 0; rr < RMN; ++rr) gw[rr] = ld_g((const u32x4*)(gain + 8 * min(rr * NCT + tid, ngr - 1)));
             };
+            // RMSNorm's 1/rms is one factor per token, so it multiplies the
+            // pair sums in the epilogue instead: the digits are those of
+            // gain * x (each run takes its own power of two, so the scale of
+            // the run does not matter), and the sum of squares needs no
+            // barrier of its own -- each wave leaves its share in red[] before
+            // the barrier that ends the staging
             auto norm_stage = [&](float (&v)[RMN][8], const u32x4 (&gw)[RMN]) {
                 float ss = 0.f;
 #pragma unroll
@@ -1033,7 +1034,6 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                     if (rr * NCT + tid < ngr)
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ss = fmaf(v[rr][e], v[rr][e], ss);
-                const float rs = 1.0f / sqrtf(block_sum(ss, red, rpar, cb) / (float)K + A.eps);
 #pragma unroll
                 for (int rr = 0; rr < RMN; ++rr) {
                     const int g = rr * NCT + tid;
@@ -1041,10 +1041,11 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                         const u32 gws[4] = {gw[rr].x, gw[rr].y, gw[rr].z, gw[rr].w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            v[rr][e] *= rs * __uint_as_float((e & 1) ? (gws[e >> 1] & 0xFFFF0000u) : (gws[e >> 1] << 16));
+                            v[rr][e] *= __uint_as_float((e & 1) ? (gws[e >> 1] & 0xFFFF0000u) : (gws[e >> 1] << 16));
                         digitize8(act, ps, cs, g, v[rr], six, A.status);
                     }
                 }
+                wave_share(ss, red);
             };
             if (kind == K_QKV) {
                 float v[RMN][8];
@@ -1161,6 +1162,14 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
                 }
             }
             const int pm = k.p0 + pl;                          // pair index within its matrix
+            if (kind == K_QKV || kind == K_GU) {               // RMSNorm's 1/rms (see the staging)
+                float ssq = 0.f;
+#pragma unroll
+                for (int w = 0; w < NCW; ++w) ssq += red[w];
+                const float rs = 1.0f / sqrtf(ssq / (float)k.K + A.eps);
+                va *= rs;
+                vb *= rs;
+            }
             if (kind == K_QKV) {
                 const int head = pm / (HD / 2), i = pm % (HD / 2);
                 float xa = va, xb = vb;

@@ -1236,17 +1236,24 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
 
 // The launch arguments, passed by value, into the workspace (the kernel reads
 // them through a pointer, re-reading fields where they are used).
-__global__ void __launch_bounds__(64) k_fill_args(Args a, Args* dst) {
+// One word per thread, so that every thread's load of the argument is in
+// flight at once (a loop of dependent load/store rounds costs one argument
+// read latency per round).
+constexpr int FILL_NT = 512;
+static_assert(sizeof(Args) % 8 == 0 && sizeof(Args) / 8 <= FILL_NT, "one word of Args per thread");
+__global__ void __launch_bounds__(FILL_NT) k_fill_args(Args a, Args* dst) {
     constexpr int W = (int)(sizeof(Args) / 8);
-    for (int i = i4d_tid(); i < W; i += 64) ((u64*)dst)[i] = ((const u64*)&a)[i];
+    const int i = i4d_tid();
+    if (i < W) ((u64*)dst)[i] = ((const u64*)&a)[i];
 }
 
 // Copy a chunk of layer-table entries (passed by value) into the workspace.
 constexpr int LPTR_PER_FILL = 24;
+static_assert(LPTR_PER_FILL * LPTR_WORDS <= FILL_NT, "one table word per thread");
 struct LPtrChunk { LPtr e[LPTR_PER_FILL]; LPtr* dst; int count; };
-__global__ void __launch_bounds__(64) k_fill_ltab(LPtrChunk ch) {
-    const int words = ch.count * LPTR_WORDS;
-    for (int i = i4d_tid(); i < words; i += 64) ((u64*)ch.dst)[i] = ((const u64*)ch.e)[i];
+__global__ void __launch_bounds__(FILL_NT) k_fill_ltab(LPtrChunk ch) {
+    const int i = i4d_tid();
+    if (i < ch.count * LPTR_WORDS) ((u64*)ch.dst)[i] = ((const u64*)ch.e)[i];
 }
 
 // ------------------------------------------------------------------ host side
@@ -1414,7 +1421,7 @@ int run(const i4d_config* c, int n_layers, const i4d_layer* layers, const float*
             d.kc = kv[l0 + i].k;
             d.vc = kv[l0 + i].v;
         }
-        hipLaunchKernelGGL(k_fill_ltab, dim3(1), dim3(64), 0, s, ch);
+        hipLaunchKernelGGL(k_fill_ltab, dim3(1), dim3(FILL_NT), 0, s, ch);
     }
 
     Args A;
@@ -1441,7 +1448,7 @@ int run(const i4d_config* c, int n_layers, const i4d_layer* layers, const float*
     A.zero = (const uint8_t*)(region + R.zero);
     A.status = status;
     A.epoch = epoch;
-    hipLaunchKernelGGL(k_fill_args, dim3(1), dim3(64), 0, s, A, (Args*)(region + R.args));
+    hipLaunchKernelGGL(k_fill_args, dim3(1), dim3(FILL_NT), 0, s, A, (Args*)(region + R.args));
 
     if (timing_ev) (void)hipEventRecord(timing_ev[0], s);
     hipError_t e;

@@ -1236,9 +1236,7 @@ __global__ void __launch_bounds__(NT) k_stream_decode(const Args* __restrict__ A
 
 // The launch arguments, passed by value, into the workspace (the kernel reads
 // them through a pointer, re-reading fields where they are used).
-// One word per thread, so that every thread's load of the argument is in
-// flight at once (a loop of dependent load/store rounds costs one argument
-// read latency per round).
+// One word per thread: every read of the argument is issued at once.
 constexpr int FILL_NT = 512;
 static_assert(sizeof(Args) % 8 == 0 && sizeof(Args) / 8 <= FILL_NT, "one word of Args per thread");
 __global__ void __launch_bounds__(FILL_NT) k_fill_args(Args a, Args* dst) {

@@ -222,7 +222,8 @@ int i4d_prefill_chunk(const i4d_config* cfg, int32_t n_layers, const i4d_layer* 
  * as for the decode calls.  Enqueues kernels only (no memset, no
  * allocation), so the call can be captured in a graph.  Numerics:
  * activations enter the projections as fp16 (k and v rows: fp16 + fp16
- * remainder) times a power of two per token, accumulated in fp32.  Enqueued on `stream`; returns after enqueueing.      */
+ * remainder) times a power of two per token, accumulated in fp32.
+ * Enqueued on `stream`; returns after enqueueing.                         */
 #define I4D_PREFILL_MAX_TOKENS 65536
 size_t i4d_prefill_workspace_size(const i4d_config* cfg, int32_t n_tokens);
 int i4d_prefill(const i4d_config* cfg, int32_t n_layers, const i4d_layer* layers, int32_t n_tokens,

@@ -206,16 +206,18 @@ def test_lm_head_at_full_size(batch):
     assert_close(mx.cpu().numpy(), mx_ref, what="full LM head max logit")
 
 
-def test_prefill_27b_layer_512_tokens_sampled(monkeypatch):
+@pytest.mark.parametrize("name,sample", [("27b", (0, 1, 63, 64, 255, 300, 511)), ("70b", (0, 63, 300, 511))])
+def test_prefill_layer_512_tokens_sampled(monkeypatch, name, sample):
     """i4d_prefill of a 512-token prompt (positions 0..511) through one
-    27B-shaped int4 layer.  For sampled tokens t the oracle decodes token t
-    against the GPU's cache slots 0..t-1 (the slots from t on poisoned): the
-    output row to the float bar and the K/V it appends at slot t within one
-    bf16 rounding step of the GPU's slot t.  Slots past the prompt untouched."""
-    shape = synth.SHAPES["27b"].with_(n_layers=1)
+    27B- or 70B-shaped int4 layer (70B: D 8192, 64/8 heads, d_ff 28672).  For
+    sampled tokens t the oracle decodes token t against the GPU's cache slots
+    0..t-1 (the slots from t on poisoned): the output row to the float bar and
+    the K/V it appends at slot t within one bf16 rounding step of the GPU's
+    slot t.  Slots past the prompt untouched."""
+    shape = synth.SHAPES[name].with_(n_layers=1)
     n = 512
     cap = n + 16
-    _print_case("prefill 27b layer full size", n, "tokens")
+    _print_case(f"prefill {name} layer full size", n, "tokens")
     L = _FullLayer(shape, 9, 0, "int4", 1, cap)
     k0, v0 = L.caches()
     x = G.make_x_gpu(shape, 10, n)
@@ -231,10 +233,10 @@ def test_prefill_27b_layer_512_tokens_sampled(monkeypatch):
     xh = x.cpu().numpy().astype(np.float64)
     assert np.array_equal(kc[:, :, n:], k0[:, :, n:]) and np.array_equal(vc[:, :, n:], v0[:, :, n:])
     # expand the layer's matrices once for all sampled tokens (same values)
-    monkeypatch.setattr(oracle.decode, "_DENSE_MEMO_ELEMS", 1 << 27)
+    monkeypatch.setattr(oracle.decode, "_DENSE_MEMO_ELEMS", 1 << 28)
     monkeypatch.setattr(oracle.decode, "_DENSE_MEMO", [])
     t0 = time.time()
-    for t in (0, 1, 63, 64, 255, 300, 511):
+    for t in sample:
         kt, vt = kc.copy(), vc.copy()
         kt[:, :, t:] = 0x7FC0
         vt[:, :, t:] = 0x7FC0
